@@ -1,0 +1,266 @@
+"""FP64 CPU oracle for fused linear cross-entropy (FLCE), standalone
+cross-entropy (CE) and per-shard vocabulary statistics.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module. The HIP library never
+calls it, and it shares no code with the HIP library: it is plain NumPy in
+float64, written from the definitions, so a reader can check it by eye.
+
+Sources (web pages in the reference set):
+  * "liger-kernel 0.0.1 -> 0.1.1" package diff, README section "Kernels":
+    CrossEntropy is PyTorch's CrossEntropyLoss (linked there as the definition),
+    computed together with its gradient; FusedLinearCrossEntropy fuses the model
+    head with that loss and chunks the input rows; "Key Features": the
+    computation is exact, with no approximation.
+  * "Peak performance, minimized memory" (torchtune + Liger blog), text under
+    Figure 1 "Fused Linear Cross Entropy": flatten [B, S, H] to [B*S, H], apply
+    the head on row chunks, take each chunk's loss and logits gradient, then
+    derive the hidden-state gradient and accumulate the head gradient.
+  * DeepSpeed PR "opt-in Liger vocab-parallel CE backend", sections "Changes"
+    and "Real-device validation": reductions none/sum/mean, ignored targets,
+    vocabulary shards across tensor-parallel ranks.
+
+Readings where the pages say nothing (each is also listed in the design notes):
+  * loss_n = logsumexp(z_n) - z_n[y_n]; a row is ignored iff y_n == ignore_index;
+    a row whose target is not ignored but lies outside [0, V) is "bad": it is
+    treated as ignored and reported.
+  * mean divides by the number of rows that are neither ignored nor bad; with
+    no such row the loss and every gradient are 0 (PyTorch would give NaN).
+  * reduction "none" returns per-row losses; its gradients are those of their
+    sum (an all-ones upstream gradient).
+  * the optional head bias b enters as z = x W^T + b; its gradient is the
+    column sum of dZ.
+  * shard statistics are taken relative to the shard's own maximum; the target
+    logit is 0 when the target is outside the shard or the row is ignored.
+
+Every function here evaluates the plain definition. The only partition is the
+row blocking of `flce`, which the FLCE description itself prescribes (rows are
+independent, so blocking changes nothing but the order of the grad_W sum); for
+inputs of at most `row_block` rows there is no blocking at all.
+"""
+
+import numpy as np
+
+REDUCTIONS = ("none", "sum", "mean")
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def target_masks(targets, V, ignore_index):
+    """Row classification for targets y (any integer array).
+
+    valid[n]: y_n != ignore_index and 0 <= y_n < V (the row contributes).
+    bad[n]:   y_n != ignore_index and y_n outside [0, V) (reported, then
+              treated like an ignored row).
+    """
+    y = np.asarray(targets).astype(np.int64)
+    not_ignored = y != int(ignore_index)
+    in_range = (y >= 0) & (y < V)
+    return not_ignored & in_range, not_ignored & ~in_range
+
+
+def reduction_scale(n_valid, reduction):
+    """Factor applied to each row's loss gradient: 1/N_valid for mean (0 when
+    N_valid is 0), else 1 (sum, and none whose gradient is that of the sum)."""
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    if reduction == "mean":
+        return 1.0 / n_valid if n_valid > 0 else 0.0
+    return 1.0
+
+
+def logsumexp_rows(Z):
+    """lse_n = M_n + ln sum_v exp(Z[n, v] - M_n) with M_n = max_v Z[n, v]."""
+    Z = _f64(Z)
+    M = Z.max(axis=1)
+    return M + np.log(np.exp(Z - M[:, None]).sum(axis=1))
+
+
+def _rows_loss_and_dlogits(Z, y, valid, scale):
+    """Per-row CE loss and the gradient of scale * sum(loss) w.r.t. Z.
+
+    loss_n = lse_n - Z[n, y_n] for valid rows, 0 otherwise;
+    dZ[n, :] = scale * (softmax(Z[n, :]) - onehot(y_n)) for valid rows, 0 otherwise.
+    """
+    Z = _f64(Z)
+    n_rows = Z.shape[0]
+    lse = logsumexp_rows(Z)
+    rows = np.arange(n_rows)
+    ysafe = np.where(valid, y, 0)
+    z_target = Z[rows, ysafe]
+    loss = np.where(valid, lse - z_target, 0.0)
+    P = np.exp(Z - lse[:, None])
+    P[rows[valid], ysafe[valid]] -= 1.0
+    dZ = scale * P * valid[:, None]
+    return loss, dZ
+
+
+def _reduce(loss_rows, n_valid, reduction):
+    if reduction == "none":
+        return loss_rows.copy()
+    total = float(loss_rows.sum())
+    if reduction == "sum":
+        return total
+    return total / n_valid if n_valid > 0 else 0.0
+
+
+def cross_entropy(logits, targets, ignore_index=-100, reduction="mean"):
+    """Cross-entropy over given logits [N, V] and its gradient.
+
+    Returns (loss, grad_logits, info): loss is a float (sum/mean) or an [N]
+    array (none); grad_logits is [N, V] float64; info holds n_valid, n_bad and
+    the per-row losses.
+    """
+    Z = _f64(logits)
+    N, V = Z.shape
+    y = np.asarray(targets).astype(np.int64)
+    valid, bad = target_masks(y, V, ignore_index)
+    n_valid = int(valid.sum())
+    scale = reduction_scale(n_valid, reduction)
+    loss_rows, dZ = _rows_loss_and_dlogits(Z, y, valid, scale)
+    info = {"n_valid": n_valid, "n_bad": int(bad.sum()), "loss_rows": loss_rows}
+    return _reduce(loss_rows, n_valid, reduction), dZ, info
+
+
+def flce(X, W, targets, bias=None, ignore_index=-100, reduction="mean",
+         row_block=1024, want_grads=True):
+    """Fused linear cross-entropy: loss of CE(X W^T + b, y) and its gradients.
+
+    X [N, H], W [V, H] (lm_head weight, nn.Linear layout), bias [V] or None,
+    targets [N]. Logits are materialised one row block at a time, in float64.
+    Returns (loss, grads, info) with grads = {"X": [N, H], "W": [V, H],
+    "bias": [V] or None} (None entries when want_grads is False).
+    """
+    X = _f64(X)
+    W = _f64(W)
+    N, H = X.shape
+    V = W.shape[0]
+    if W.shape[1] != H:
+        raise ValueError("X and W disagree on H")
+    b = None if bias is None else _f64(bias)
+    y = np.asarray(targets).astype(np.int64)
+    valid, bad = target_masks(y, V, ignore_index)
+    n_valid = int(valid.sum())
+    scale = reduction_scale(n_valid, reduction)
+
+    loss_rows = np.zeros(N)
+    gX = np.zeros((N, H)) if want_grads else None
+    gW = np.zeros((V, H)) if want_grads else None
+    gb = (np.zeros(V) if b is not None else None) if want_grads else None
+    for r0 in range(0, N, max(1, int(row_block))):
+        r1 = min(N, r0 + int(row_block))
+        Xb = X[r0:r1]
+        Z = Xb @ W.T
+        if b is not None:
+            Z = Z + b[None, :]
+        lr, dZ = _rows_loss_and_dlogits(Z, y[r0:r1], valid[r0:r1], scale)
+        loss_rows[r0:r1] = lr
+        if want_grads:
+            gX[r0:r1] = dZ @ W
+            gW += dZ.T @ Xb
+            if gb is not None:
+                gb += dZ.sum(axis=0)
+    info = {"n_valid": n_valid, "n_bad": int(bad.sum()), "loss_rows": loss_rows}
+    return _reduce(loss_rows, n_valid, reduction), {"X": gX, "W": gW, "bias": gb}, info
+
+
+def flce_rows(X, W, targets, rows, bias=None, ignore_index=-100, reduction="mean"):
+    """Loss and grad_X for selected rows only (grad_X of a row needs only that
+    row), with the reduction scale of the whole batch. Used to check sampled
+    rows of large problems. Returns (loss_rows [R], grad_X [R, H])."""
+    X = _f64(X)
+    W = _f64(W)
+    V = W.shape[0]
+    y = np.asarray(targets).astype(np.int64)
+    valid, _ = target_masks(y, V, ignore_index)
+    scale = reduction_scale(int(valid.sum()), reduction)
+    rows = np.asarray(rows, dtype=np.int64)
+    Z = X[rows] @ W.T
+    if bias is not None:
+        Z = Z + _f64(bias)[None, :]
+    lr, dZ = _rows_loss_and_dlogits(Z, y[rows], valid[rows], scale)
+    return lr, dZ @ W
+
+
+def flce_grad_w_rows(X, W, targets, vocab_rows, bias=None, ignore_index=-100,
+                     reduction="mean", row_block=1024):
+    """grad_W[v, :] and grad_bias[v] for selected vocabulary rows v, summed over
+    every token row (dZ[:, v] needs each token row's full logsumexp). Returns
+    (grad_W_rows [R, H], grad_bias_rows [R])."""
+    X = _f64(X)
+    W = _f64(W)
+    N, H = X.shape
+    V = W.shape[0]
+    y = np.asarray(targets).astype(np.int64)
+    valid, _ = target_masks(y, V, ignore_index)
+    scale = reduction_scale(int(valid.sum()), reduction)
+    vr = np.asarray(vocab_rows, dtype=np.int64)
+    b = None if bias is None else _f64(bias)
+    gW = np.zeros((len(vr), H))
+    gb = np.zeros(len(vr))
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        Z = X[r0:r1] @ W.T
+        if b is not None:
+            Z = Z + b[None, :]
+        _, dZ = _rows_loss_and_dlogits(Z, y[r0:r1], valid[r0:r1], scale)
+        gW += dZ[:, vr].T @ X[r0:r1]
+        gb += dZ[:, vr].sum(axis=0)
+    return gW, gb
+
+
+def shard_stats(logits_shard, targets, vocab_start, V_global, ignore_index=-100):
+    """Per-row statistics of one vocabulary shard [N, V_local] covering global
+    ids [vocab_start, vocab_start + V_local).
+
+    m_n = max over the shard; s_n = sum over the shard of exp(z - m_n);
+    t_n = z[n, y_n - vocab_start] if row n is valid (w.r.t. V_global) and its
+    target falls in the shard, else 0.
+    """
+    Z = _f64(logits_shard)
+    N, Vl = Z.shape
+    y = np.asarray(targets).astype(np.int64)
+    valid, _ = target_masks(y, V_global, ignore_index)
+    m = Z.max(axis=1)
+    s = np.exp(Z - m[:, None]).sum(axis=1)
+    local = y - int(vocab_start)
+    here = valid & (local >= 0) & (local < Vl)
+    t = np.where(here, Z[np.arange(N), np.where(here, local, 0)], 0.0)
+    return m, s, t
+
+
+def combine_shard_stats(stats):
+    """Combine per-shard (m, s, t) into (lse, target logit) per row:
+    M = max_k m_k, S = sum_k s_k exp(m_k - M), lse = M + ln S, z_y = sum_k t_k."""
+    ms = np.stack([_f64(st[0]) for st in stats])
+    ss = np.stack([_f64(st[1]) for st in stats])
+    ts = np.stack([_f64(st[2]) for st in stats])
+    M = ms.max(axis=0)
+    S = (ss * np.exp(ms - M[None, :])).sum(axis=0)
+    return M + np.log(S), ts.sum(axis=0)
+
+
+def flce_shard_stats(X, W_shard, targets, vocab_start, V_global, bias_shard=None,
+                     ignore_index=-100, row_block=1024):
+    """Shard statistics of the logits X W_shard^T (+ bias_shard), materialised
+    one row block at a time."""
+    X = _f64(X)
+    Ws = _f64(W_shard)
+    y = np.asarray(targets).astype(np.int64)
+    N = X.shape[0]
+    out = [np.zeros(N), np.zeros(N), np.zeros(N)]
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        Z = X[r0:r1] @ Ws.T
+        if bias_shard is not None:
+            Z = Z + _f64(bias_shard)[None, :]
+        m, s, t = shard_stats(Z, y[r0:r1], vocab_start, V_global, ignore_index)
+        out[0][r0:r1], out[1][r0:r1], out[2][r0:r1] = m, s, t
+    return tuple(out)
+
+
+def materialised_logits_bytes(n_tokens, vocab, elem_bytes):
+    """Bytes of a full [tokens, vocab] logits tensor: what FLCE avoids holding."""
+    return int(n_tokens) * int(vocab) * int(elem_bytes)

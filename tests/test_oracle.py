@@ -1,0 +1,356 @@
+"""Pins for the FP64 oracle, independent of the oracle's own formulas.
+
+Each test checks the oracle against something it does not compute itself:
+closed forms of special cases, hand-worked values, central finite differences,
+a brute-force pure-Python evaluation, PyTorch's CPU cross-entropy (the pages
+define CE by PyTorch's CrossEntropyLoss), invariants that any correct result
+satisfies, and the one number the pages print for this path (16.8 GB of logits).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import flce_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_problem(rng, N=7, H=5, V=9, bias=True, n_ignored=2, ignore_index=-100):
+    X = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H)) * 0.7
+    b = rng.standard_normal(V) * 0.3 if bias else None
+    y = rng.integers(0, V, size=N)
+    if n_ignored:
+        y[rng.choice(N, n_ignored, replace=False)] = ignore_index
+    return X, W, b, y
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_zero_weight_gives_log_vocab(reduction):
+    rng = np.random.default_rng(1)
+    N, H, V = 11, 6, 13
+    X = rng.standard_normal((N, H))
+    W = np.zeros((V, H))
+    y = rng.integers(0, V, size=N)
+    y[[2, 5]] = -100
+    valid = y != -100
+    nv = int(valid.sum())
+    loss, g, info = O.flce(X, W, y, reduction=reduction)
+    lnV = math.log(V)
+    if reduction == "none":
+        np.testing.assert_allclose(loss, np.where(valid, lnV, 0.0), rtol=0, atol=1e-14)
+    elif reduction == "sum":
+        assert abs(loss - nv * lnV) < 1e-12
+    else:
+        assert abs(loss - lnV) < 1e-14
+    s = 1.0 / nv if reduction == "mean" else 1.0
+    # With W = 0 every softmax is uniform: dZ[n] = s (1/V - e_{y_n}) for valid n.
+    assert np.all(g["X"] == 0.0)
+    expect_gW = np.zeros((V, H))
+    for n in range(N):
+        if valid[n]:
+            expect_gW += s * X[n][None, :] / V
+            expect_gW[y[n]] -= s * X[n]
+    np.testing.assert_allclose(g["W"], expect_gW, rtol=0, atol=1e-13)
+
+
+def test_zero_input_reduces_to_bias_softmax():
+    """X = 0 makes every logit row equal to the bias: loss_n = lse(b) - b_y,
+    grad_W = 0, grad_bias = s (N_valid softmax(b) - counts), grad_X_n =
+    s (softmax(b) - e_y) W. softmax / logsumexp come from scipy here."""
+    from scipy.special import logsumexp, softmax
+
+    rng = np.random.default_rng(2)
+    N, H, V = 9, 4, 17
+    X = np.zeros((N, H))
+    W = rng.standard_normal((V, H))
+    b = rng.standard_normal(V) * 2
+    y = rng.integers(0, V, size=N)
+    y[3] = -100
+    valid = y != -100
+    nv = int(valid.sum())
+    loss, g, _ = O.flce(X, W, y, bias=b, reduction="mean")
+    lse = logsumexp(b)
+    assert abs(loss - np.mean(lse - b[y[valid]])) < 1e-13
+    assert np.all(g["W"] == 0.0)
+    counts = np.bincount(y[valid], minlength=V)
+    p = softmax(b)
+    np.testing.assert_allclose(g["bias"], (nv * p - counts) / nv, atol=1e-14)
+    for n in range(N):
+        e = np.zeros(V)
+        if valid[n]:
+            e[y[n]] = 1.0
+            np.testing.assert_allclose(g["X"][n], (p - e) @ W / nv, atol=1e-14)
+        else:
+            assert np.all(g["X"][n] == 0.0)
+
+
+def test_two_classes_is_softplus():
+    """With V = 2 the loss is softplus(z_other - z_target) and its gradient
+    w.r.t. z_target is -sigmoid(z_other - z_target)."""
+    rng = np.random.default_rng(3)
+    Z = rng.standard_normal((20, 2)) * 3
+    y = rng.integers(0, 2, size=20)
+    loss, dZ, _ = O.cross_entropy(Z, y, reduction="none")
+    d = Z[np.arange(20), 1 - y] - Z[np.arange(20), y]
+    np.testing.assert_allclose(loss, np.logaddexp(0.0, d), rtol=1e-11, atol=1e-15)
+    sig = 1.0 / (1.0 + np.exp(-d))
+    np.testing.assert_allclose(dZ[np.arange(20), y], -sig, rtol=1e-11, atol=1e-15)
+    np.testing.assert_allclose(dZ[np.arange(20), 1 - y], sig, rtol=1e-11, atol=1e-15)
+
+
+def test_hand_worked_examples():
+    with open(os.path.join(GOLDEN, "ce_hand_example.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        z = np.array([c["logits"]])
+        loss, dZ, _ = O.cross_entropy(z, [c["target"]], reduction="sum")
+        assert abs(loss - c["loss"]) < 1e-14
+        np.testing.assert_allclose(dZ[0], c["grad"], atol=1e-15)
+
+
+def test_materialised_logits_bytes_matches_page():
+    with open(os.path.join(GOLDEN, "logits_bytes.json")) as f:
+        g = json.load(f)
+    nbytes = O.materialised_logits_bytes(g["batch"] * g["seq"], g["vocab"], g["elem_bytes"])
+    assert round(nbytes / 1e9, 1) == g["printed_gb"]
+
+
+# ------------------------------------------------------- independent evaluators
+
+def _brute_force_ce(Z, y, ignore_index, reduction):
+    """Pure-Python loops with math.exp / math.log, no max subtraction."""
+    total = 0.0
+    rows = []
+    nv = 0
+    for n in range(len(Z)):
+        if y[n] == ignore_index:
+            rows.append(0.0)
+            continue
+        nv += 1
+        s = 0.0
+        for z in Z[n]:
+            s += math.exp(z)
+        li = math.log(s) - Z[n][y[n]]
+        rows.append(li)
+        total += li
+    if reduction == "none":
+        return rows
+    if reduction == "sum":
+        return total
+    return total / nv
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_brute_force_tiny(reduction):
+    rng = np.random.default_rng(4)
+    X, W, b, y = _rand_problem(rng, N=6, H=3, V=5)
+    loss, _, _ = O.flce(X, W, y, bias=b, reduction=reduction)
+    Z = [[sum(X[n][h] * W[v][h] for h in range(3)) + b[v] for v in range(5)] for n in range(6)]
+    ref = _brute_force_ce(Z, list(y), -100, reduction)
+    np.testing.assert_allclose(loss, ref, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_finite_differences(reduction):
+    """Central differences of the scalar objective (sum of per-row losses for
+    'none') agree with the oracle's analytic gradients."""
+    rng = np.random.default_rng(5)
+    X, W, b, y = _rand_problem(rng, N=6, H=4, V=7)
+
+    def obj(X_, W_, b_):
+        loss, _, _ = O.flce(X_, W_, y, bias=b_, reduction=reduction, want_grads=False)
+        return float(np.sum(loss))
+
+    _, g, _ = O.flce(X, W, y, bias=b, reduction=reduction)
+    eps = 1e-6
+    for name, arr, grad in (("X", X, g["X"]), ("W", W, g["W"]), ("bias", b, g["bias"])):
+        num = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = arr[idx]
+            arr[idx] = old + eps
+            fp = obj(X, W, b)
+            arr[idx] = old - eps
+            fm = obj(X, W, b)
+            arr[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        scale = max(1.0, float(np.abs(grad).max()))
+        assert np.abs(num - grad).max() <= 1e-7 * scale, name
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_against_torch_cpu_float64(reduction):
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    rng = np.random.default_rng(6)
+    X, W, b, y = _rand_problem(rng, N=40, H=16, V=33, n_ignored=5)
+    loss, g, _ = O.flce(X, W, y, bias=b, reduction=reduction, row_block=7)
+    tX = torch.tensor(X, requires_grad=True)
+    tW = torch.tensor(W, requires_grad=True)
+    tb = torch.tensor(b, requires_grad=True)
+    ty = torch.tensor(y)
+    tl = F.cross_entropy(F.linear(tX, tW, tb), ty, ignore_index=-100, reduction=reduction)
+    tl.sum().backward()
+    np.testing.assert_allclose(loss, tl.detach().numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g["X"], tX.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(g["W"], tW.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(g["bias"], tb.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_ce_against_torch_cpu_float64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    Z = rng.standard_normal((30, 50)) * 4
+    y = rng.integers(0, 50, size=30)
+    y[[0, 7, 9]] = -100
+    for red in ("none", "sum", "mean"):
+        loss, dZ, _ = O.cross_entropy(Z, y, reduction=red)
+        tZ = torch.tensor(Z, requires_grad=True)
+        tl = torch.nn.functional.cross_entropy(tZ, torch.tensor(y), reduction=red)
+        tl.sum().backward()
+        np.testing.assert_allclose(loss, tl.detach().numpy(), rtol=1e-12)
+        np.testing.assert_allclose(dZ, tZ.grad.numpy(), rtol=1e-11, atol=1e-15)
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_reduction_identities():
+    rng = np.random.default_rng(8)
+    X, W, b, y = _rand_problem(rng, N=25, H=6, V=11, n_ignored=4)
+    ln, gn, info = O.flce(X, W, y, bias=b, reduction="none")
+    ls, gs, _ = O.flce(X, W, y, bias=b, reduction="sum")
+    lm, gm, _ = O.flce(X, W, y, bias=b, reduction="mean")
+    nv = info["n_valid"]
+    assert nv == 21
+    assert abs(ls - ln.sum()) < 1e-12
+    assert abs(lm - ls / nv) < 1e-13
+    for k in ("X", "W", "bias"):
+        np.testing.assert_allclose(gn[k], gs[k], atol=0)
+        np.testing.assert_allclose(gm[k], gs[k] / nv, rtol=1e-13, atol=1e-16)
+
+
+def test_gradient_row_sums_vanish():
+    rng = np.random.default_rng(9)
+    X, W, b, y = _rand_problem(rng, N=20, H=5, V=12)
+    _, dZ, _ = O.cross_entropy(X @ W.T + b, y, reduction="sum")
+    np.testing.assert_allclose(dZ.sum(axis=1), 0.0, atol=1e-14)
+    _, g, _ = O.flce(X, W, y, bias=b, reduction="sum")
+    np.testing.assert_allclose(g["W"].sum(axis=0), 0.0, atol=1e-12)
+    assert abs(g["bias"].sum()) < 1e-12
+
+
+def test_bias_shift_invariance():
+    rng = np.random.default_rng(10)
+    X, W, b, y = _rand_problem(rng, N=15, H=5, V=8)
+    l1, g1, _ = O.flce(X, W, y, bias=b, reduction="mean")
+    l2, g2, _ = O.flce(X, W, y, bias=b + 3.25, reduction="mean")
+    assert abs(l1 - l2) < 1e-13
+    for k in ("X", "W", "bias"):
+        np.testing.assert_allclose(g1[k], g2[k], atol=1e-14)
+
+
+def test_row_permutation_equivariance():
+    rng = np.random.default_rng(11)
+    X, W, b, y = _rand_problem(rng, N=18, H=5, V=8)
+    perm = rng.permutation(18)
+    ln, g, _ = O.flce(X, W, y, bias=b, reduction="none")
+    lp, gp, _ = O.flce(X[perm], W, y[perm], bias=b, reduction="none")
+    np.testing.assert_allclose(lp, ln[perm], atol=1e-15)
+    np.testing.assert_allclose(gp["X"], g["X"][perm], atol=1e-15)
+    np.testing.assert_allclose(gp["W"], g["W"], atol=1e-13)
+
+
+def test_row_blocking_does_not_change_results():
+    rng = np.random.default_rng(12)
+    X, W, b, y = _rand_problem(rng, N=23, H=6, V=10)
+    l1, g1, _ = O.flce(X, W, y, bias=b, reduction="mean", row_block=1024)
+    l2, g2, _ = O.flce(X, W, y, bias=b, reduction="mean", row_block=4)
+    assert abs(l1 - l2) < 1e-14
+    for k in ("X", "W", "bias"):
+        np.testing.assert_allclose(g1[k], g2[k], atol=1e-14)
+
+
+def test_ignored_and_bad_rows_are_exact_zeros():
+    rng = np.random.default_rng(13)
+    X, W, b, y = _rand_problem(rng, N=12, H=4, V=6, n_ignored=3)
+    y[0] = 6      # out of range -> bad
+    y[1] = -7     # negative, not the ignore index -> bad
+    loss, g, info = O.flce(X, W, y, bias=b, reduction="none")
+    assert info["n_bad"] == 2
+    dead = (y == -100) | (y == 6) | (y == -7)
+    assert np.all(loss[dead] == 0.0)
+    assert np.all(g["X"][dead] == 0.0)
+    assert np.all(loss[~dead] > 0.0)
+
+
+def test_mean_with_no_valid_rows_is_zero():
+    X = np.ones((4, 3))
+    W = np.ones((5, 3))
+    y = np.full(4, -100)
+    loss, g, info = O.flce(X, W, y, reduction="mean")
+    assert loss == 0.0 and info["n_valid"] == 0
+    assert np.all(g["X"] == 0) and np.all(g["W"] == 0)
+
+
+def test_ignore_index_inside_vocab_range():
+    """A row is ignored iff its target equals ignore_index, even when that value
+    is a legal class id."""
+    rng = np.random.default_rng(14)
+    Z = rng.standard_normal((6, 5))
+    y = np.array([0, 1, 2, 3, 4, 2])
+    loss, dZ, info = O.cross_entropy(Z, y, ignore_index=2, reduction="none")
+    assert info["n_valid"] == 4
+    assert loss[2] == 0.0 and loss[5] == 0.0
+    assert np.all(dZ[[2, 5]] == 0.0)
+
+
+# ----------------------------------------------------------------- shard stats
+
+def test_shard_stats_combine_to_full_vocab():
+    rng = np.random.default_rng(15)
+    N, V = 64, 96
+    Z = rng.standard_normal((N, V)) * 2
+    y = rng.integers(0, V, size=N)
+    y[[1, 4, 9]] = -100
+    parts = [O.shard_stats(Z[:, a:a + 32], y, a, V) for a in (0, 32, 64)]
+    lse, zt = O.combine_shard_stats(parts)
+    full_lse = np.array([math.log(sum(math.exp(v) for v in row)) for row in Z])
+    np.testing.assert_allclose(lse, full_lse, rtol=1e-14)
+    valid = y != -100
+    np.testing.assert_allclose(zt[valid], Z[np.arange(N)[valid], y[valid]], rtol=0, atol=0)
+    assert np.all(zt[~valid] == 0.0)
+    for m, s, t in parts:
+        assert np.all(s >= 1.0)   # the shard maximum contributes exp(0) = 1
+
+
+def test_flce_shard_stats_matches_materialised():
+    rng = np.random.default_rng(16)
+    X, W, b, y = _rand_problem(rng, N=30, H=6, V=20)
+    Ws, bs = W[8:15], b[8:15]
+    m, s, t = O.flce_shard_stats(X, Ws, y, 8, 20, bias_shard=bs, row_block=7)
+    m2, s2, t2 = O.shard_stats(X @ Ws.T + bs, y, 8, 20)
+    np.testing.assert_allclose(m, m2, atol=1e-15)
+    np.testing.assert_allclose(s, s2, rtol=1e-14)
+    np.testing.assert_allclose(t, t2, atol=1e-15)
+
+
+def test_sampled_helpers_agree_with_full():
+    rng = np.random.default_rng(17)
+    X, W, b, y = _rand_problem(rng, N=26, H=5, V=14, n_ignored=3)
+    loss, g, info = O.flce(X, W, y, bias=b, reduction="mean")
+    rows = np.array([0, 5, 25, 11])
+    lr, gx = O.flce_rows(X, W, y, rows, bias=b, reduction="mean")
+    np.testing.assert_allclose(lr, info["loss_rows"][rows], atol=1e-15)
+    np.testing.assert_allclose(gx, g["X"][rows], atol=1e-15)
+    vr = np.array([13, 0, 7])
+    gw, gb = O.flce_grad_w_rows(X, W, y, vr, bias=b, reduction="mean", row_block=5)
+    np.testing.assert_allclose(gw, g["W"][vr], atol=1e-14)
+    np.testing.assert_allclose(gb, g["bias"][vr], atol=1e-14)
