@@ -1,0 +1,183 @@
+/*
+ * flce.h -- C ABI of liblce03.so: fused linear cross-entropy (FLCE),
+ * standalone cross-entropy (CE) and vocabulary-shard statistics on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (sources: the liger-kernel 0.1.1 README, "Kernels"
+ * section, for CrossEntropy and FusedLinearCrossEntropy; the torchtune + Liger
+ * blog "Peak performance, minimized memory", text under Figure 1, for the
+ * chunked FLCE steps; the DeepSpeed vocab-parallel CE pull request, "Changes"
+ * and "Real-device validation", for reductions, ignored targets and shards):
+ *
+ *   z_n      = x_n W^T (+ b)                        logits of row n, [V]
+ *   lse_n    = ln sum_v exp(z_n[v])
+ *   loss_n   = lse_n - z_n[y_n]   (0 for ignored rows)
+ *   none -> [loss_n];  sum -> sum_n loss_n;  mean -> sum_n loss_n / N_valid
+ *   dz_n     = s * (softmax(z_n) - onehot(y_n))    s = 1/N_valid (mean), else 1
+ *   grad_X   = dZ W,  grad_W = dZ^T X,  grad_bias = sum_n dz_n
+ *
+ * FLCE never holds the [N, V] logits: it processes `chunk_rows` rows at a
+ * time, turning each chunk's logits in place into dlogits.
+ *
+ * Conventions shared by every entry point
+ *   - Array pointers are DEVICE pointers owned by the caller; arrays are dense
+ *     and row-major (the last index is contiguous). Base pointers must be
+ *     16-byte aligned. The library never allocates or frees device memory:
+ *     scratch space is the caller's `workspace`.
+ *   - Element type of X, W, bias and logits: FLCE_F32 (float) or FLCE_BF16
+ *     (bfloat16 bit patterns, uint16). All of a call's floating inputs share
+ *     one type. Losses, statistics and FLCE gradients are float32.
+ *   - Targets are int32 class ids. A row is ignored iff its target equals
+ *     ignore_index. A target that is not ignore_index and lies outside
+ *     [0, V) is a device-detected error: the row is treated as ignored (zero
+ *     loss and gradient), and flce_check_device_error() reports FLCE_E_TARGET.
+ *   - mean with no valid row returns loss 0 and zero gradients.
+ *   - For reduction NONE the gradients are those of the sum of row losses.
+ *   - Gradient outputs are overwritten, never accumulated into.
+ *   - Every call is asynchronous: work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the default stream) and the call returns without waiting. The
+ *     library keeps no state between calls, so concurrent calls on different
+ *     streams are safe as long as their workspaces and outputs do not overlap.
+ *   - Errors are returned as flce_status; host-detectable errors are returned
+ *     before anything is enqueued. No exception crosses the ABI.
+ */
+#ifndef LCE03_FLCE_H
+#define LCE03_FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_E_INVALID_ARG = 1, /* null pointer, non-positive size, bad enum, shape mismatch */
+  FLCE_E_WORKSPACE = 2,   /* workspace null or smaller than the *_workspace_bytes query */
+  FLCE_E_UNSUPPORTED = 3, /* misaligned pointer, bf16 with H % 8 != 0, size over limits */
+  FLCE_E_TARGET = 4,      /* (device) a target outside [0, V) that is not ignore_index */
+  FLCE_E_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} flce_status;
+
+typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1 } flce_dtype;
+
+typedef enum {
+  FLCE_REDUCTION_NONE = 0,
+  FLCE_REDUCTION_SUM = 1,
+  FLCE_REDUCTION_MEAN = 2
+} flce_reduction;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* flce_status_string(int status);
+
+/*
+ * Bytes of workspace flce_forward_backward / flce_shard_stats need for this
+ * problem and chunk size (chunk_rows 0 = the planner's choice). Pure host
+ * computation; returns 0 for invalid sizes.
+ */
+size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows);
+
+/*
+ * The chunk planner's decision (pure host computation): rows per chunk and the
+ * number of K-splits used for the grad_X product. Either output may be NULL.
+ * Returns FLCE_OK or FLCE_E_INVALID_ARG.
+ */
+int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
+              int64_t* chunk_rows_out, int32_t* dx_splits_out);
+
+/*
+ * Fused linear cross-entropy, forward and backward in one call (the liger
+ * README's FusedLinearCrossEntropy; the steps of the torchtune blog, Figure 1).
+ *
+ *   X        [N, H]  hidden states (the flattened [batch*seq, H])
+ *   W        [V, H]  lm_head weight (nn.Linear(H, V).weight layout)
+ *   bias     [V] or NULL
+ *   targets  [N] int32
+ *   loss     [1] float32, or [N] for FLCE_REDUCTION_NONE
+ *   grad_X   [N, H] float32 or NULL (NULL skips the grad_X product)
+ *   grad_W   [V, H] float32 or NULL (NULL skips the grad_W product)
+ *   grad_bias[V] float32 or NULL (must be NULL when bias is NULL)
+ *   workspace of at least flce_workspace_bytes(N, H, V, dtype, chunk_rows)
+ *   chunk_rows: rows per chunk, 0 = planner's choice; peak scratch is about
+ *   chunk_rows * V elements of the input type.
+ * Results do not depend on chunk_rows except for the rounding order of grad_W
+ * and grad_bias; the loss is bitwise independent of it.
+ */
+int flce_forward_backward(const void* X, const void* W, const void* bias,
+                          const int32_t* targets, int64_t N, int64_t H, int64_t V,
+                          int dtype, int32_t ignore_index, int reduction,
+                          float* loss, float* grad_X, float* grad_W, float* grad_bias,
+                          void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                          void* stream);
+
+/* Bytes of workspace ce_forward_backward / ce_shard_stats need. */
+size_t ce_workspace_bytes(int64_t N, int64_t V);
+
+/*
+ * Cross-entropy over given logits, loss and gradient together (the liger
+ * README's CrossEntropy: the gradient may overwrite the input logits).
+ *
+ *   logits      [N, V] (dtype)
+ *   grad_logits [N, V] (same dtype), or == logits (in place), or NULL (loss only)
+ *   targets     [N] int32;  loss [1] or [N] (NONE) float32
+ * When grad_logits is neither NULL nor logits, logits is not modified.
+ */
+int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* targets,
+                        int64_t N, int64_t V, int dtype, int32_t ignore_index,
+                        int reduction, float* loss, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Statistics of one vocabulary shard (the per-rank part of vocab-parallel CE in
+ * the DeepSpeed and Megatron pages), for logits columns covering global ids
+ * [vocab_start, vocab_start + V_local) of V_global. For each row n:
+ *   row_max[n]          = max over the shard
+ *   row_sumexp[n]       = sum over the shard of exp(z - row_max[n])
+ *   row_target_logit[n] = z[n, y_n - vocab_start] when y_n is a valid global
+ *                         target inside the shard, else 0
+ * Combining shards k: M = max m_k, lse = M + ln sum_k s_k exp(m_k - M),
+ * z_y = sum_k t_k. No collective is performed. Targets are global ids checked
+ * against [0, V_global).
+ */
+int ce_shard_stats(const void* logits_shard, const int32_t* targets, int64_t N,
+                   int64_t V_local, int64_t vocab_start, int64_t V_global, int dtype,
+                   int32_t ignore_index, float* row_max, float* row_sumexp,
+                   float* row_target_logit, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * Shard statistics of the logits X W_shard^T (+ bias_shard), computed chunk by
+ * chunk without holding [N, V_local]; W_shard is [V_local, H]. Workspace:
+ * flce_workspace_bytes(N, H, V_local, dtype, chunk_rows).
+ */
+int flce_shard_stats(const void* X, const void* W_shard, const void* bias_shard,
+                     const int32_t* targets, int64_t N, int64_t H, int64_t V_local,
+                     int64_t vocab_start, int64_t V_global, int dtype,
+                     int32_t ignore_index, float* row_max, float* row_sumexp,
+                     float* row_target_logit, void* workspace, size_t workspace_bytes,
+                     int64_t chunk_rows, void* stream);
+
+/*
+ * Waits for `stream`, then reports whether the last call that used this
+ * workspace met an out-of-range target: FLCE_OK, FLCE_E_TARGET or FLCE_E_HIP.
+ */
+int flce_check_device_error(const void* workspace, void* stream);
+
+/*
+ * Kernel timing for measurement. While enabled, the library brackets each
+ * kernel it launches with HIP events on that kernel's stream. flce_timing_read
+ * waits for the recorded events, returns for kernel class `kind` (0 logits
+ * GEMM, 1 row CE, 2 grad_X GEMM, 3 grad_W GEMM, 4 other) the summed duration
+ * in milliseconds and the number of launches since the last reset, and
+ * flce_timing_reset clears the tallies. Not thread-safe; off by default.
+ */
+int flce_timing_enable(int enable);
+int flce_timing_read(int kind, double* total_ms, int64_t* launches);
+int flce_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE03_FLCE_H */

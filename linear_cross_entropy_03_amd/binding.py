@@ -1,0 +1,271 @@
+"""ctypes binding of liblce03.so (include/flce.h), same function names.
+
+Argument marshalling only: torch tensors are checked for device, dtype and
+contiguity, turned into raw pointers and handed to the C ABI together with the
+current HIP stream. Every computation happens in the library's HIP kernels.
+PyTorch is used to allocate device memory (outputs and workspace, when the
+caller does not pass them) and to name the stream. A non-OK status raises
+FlceError. The library is loaded on first use; if it has not been built the
+import fails loudly (there is no fallback).
+"""
+
+import ctypes
+import os
+import re
+
+import torch  # loads the HIP runtime that the library then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblce03.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "flce.h")
+
+F32, BF16 = 0, 1
+REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
+OK, E_INVALID_ARG, E_WORKSPACE, E_UNSUPPORTED, E_TARGET, E_HIP = range(6)
+TIMING_KINDS = {"logits_gemm": 0, "row_ce": 1, "grad_x_gemm": 2, "grad_w_gemm": 3, "other": 4}
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_int = ctypes.c_int
+
+_SIGNATURES = {
+    "flce_status_string": (ctypes.c_char_p, [_int]),
+    "flce_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _i64]),
+    "flce_plan": (_int, [_i64, _i64, _i64, _int, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
+    "flce_forward_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _i32, _int,
+                                     _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
+    "ce_workspace_bytes": (_sz, [_i64, _i64]),
+    "ce_forward_backward": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _i32, _int, _vp, _vp, _sz, _vp]),
+    "ce_shard_stats": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _int, _i32, _vp, _vp, _vp, _vp,
+                              _sz, _vp]),
+    "flce_shard_stats": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i32,
+                                _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
+    "flce_check_device_error": (_int, [_vp, _vp]),
+    "flce_timing_enable": (_int, [_int]),
+    "flce_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    "flce_timing_reset": (_int, []),
+}
+
+_lib = None
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_text(status)})")
+
+
+def header_functions():
+    """Names of the functions include/flce.h declares."""
+    with open(HEADER_PATH) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+
+
+def lib():
+    """The loaded library (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m linear_cross_entropy_03_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_text(status):
+    return lib().flce_status_string(int(status)).decode()
+
+
+flce_status_string = status_text
+
+
+def _check(status, where):
+    if status != OK:
+        raise FlceError(status, where)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _red(reduction):
+    try:
+        return REDUCTIONS[reduction]
+    except KeyError:
+        raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}") from None
+
+
+def flce_workspace_bytes(N, H, V, dtype=BF16, chunk_rows=0):
+    return int(lib().flce_workspace_bytes(N, H, V, dtype, chunk_rows))
+
+
+def ce_workspace_bytes(N, V):
+    return int(lib().ce_workspace_bytes(N, V))
+
+
+def flce_plan(N, H, V, dtype=BF16, chunk_rows=0):
+    """(rows per chunk, grad_X K-splits) the planner picks."""
+    c = _i64()
+    s = _i32()
+    _check(lib().flce_plan(N, H, V, dtype, chunk_rows, ctypes.byref(c), ctypes.byref(s)), "flce_plan")
+    return int(c.value), int(s.value)
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def flce_forward_backward(X, W, targets, bias=None, ignore_index=-100, reduction="mean",
+                          grad_X=True, grad_W=True, grad_bias=None, loss=None, workspace=None,
+                          chunk_rows=0, stream=None):
+    """Fused linear cross-entropy forward + backward.
+
+    X [N, H] and W [V, H] (and bias [V]) share one dtype (float32 or bfloat16);
+    targets is int32 [N]. grad_X / grad_W / grad_bias: a preallocated float32
+    tensor, True (allocate), or False/None (skip; grad_bias defaults to
+    bias is not None). Returns (loss, grad_X, grad_W, grad_bias).
+    """
+    N, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    dt = _dtype_code(X)
+    if grad_bias is None:
+        grad_bias = bias is not None
+    outs = []
+    for want, shape in ((grad_X, (N, H)), (grad_W, (V, H)), (grad_bias, (V,))):
+        if isinstance(want, torch.Tensor):
+            outs.append(want)
+        elif want:
+            outs.append(_empty(shape, torch.float32, dev))
+        else:
+            outs.append(None)
+    gX, gW, gb = outs
+    if loss is None:
+        loss = _empty((N,) if reduction == "none" else (1,), torch.float32, dev)
+    if workspace is None:
+        workspace = _empty((max(1, flce_workspace_bytes(N, H, V, dt, chunk_rows)),), torch.uint8, dev)
+    st = lib().flce_forward_backward(
+        _ptr(X, "X"), _ptr(W, "W", X.dtype), _ptr(bias, "bias", X.dtype),
+        _ptr(targets, "targets", torch.int32), N, H, V, dt, ignore_index, _red(reduction),
+        _ptr(loss, "loss", torch.float32), _ptr(gX, "grad_X", torch.float32),
+        _ptr(gW, "grad_W", torch.float32), _ptr(gb, "grad_bias", torch.float32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
+        _stream(stream))
+    _check(st, "flce_forward_backward")
+    return loss, gX, gW, gb
+
+
+def ce_forward_backward(logits, targets, ignore_index=-100, reduction="mean", grad_logits=True,
+                        loss=None, workspace=None, stream=None):
+    """Cross-entropy over given logits [N, V] with its gradient.
+
+    grad_logits: a tensor (may be `logits` itself for in-place), True
+    (allocate), or False/None (loss only). Returns (loss, grad_logits).
+    """
+    N, V = logits.shape
+    dev = logits.device
+    dt = _dtype_code(logits)
+    if isinstance(grad_logits, torch.Tensor):
+        g = grad_logits
+    elif grad_logits:
+        g = torch.empty_like(logits)
+    else:
+        g = None
+    if loss is None:
+        loss = _empty((N,) if reduction == "none" else (1,), torch.float32, dev)
+    if workspace is None:
+        workspace = _empty((max(1, ce_workspace_bytes(N, V)),), torch.uint8, dev)
+    st = lib().ce_forward_backward(
+        _ptr(logits, "logits"), _ptr(g, "grad_logits", logits.dtype),
+        _ptr(targets, "targets", torch.int32), N, V, dt, ignore_index, _red(reduction),
+        _ptr(loss, "loss", torch.float32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "ce_forward_backward")
+    return loss, g
+
+
+def ce_shard_stats(logits_shard, targets, vocab_start, V_global, ignore_index=-100,
+                   out=None, workspace=None, stream=None):
+    """Per-row (max, sumexp, target logit) of one vocabulary shard."""
+    N, Vl = logits_shard.shape
+    dev = logits_shard.device
+    m, s, t = out if out is not None else tuple(_empty((N,), torch.float32, dev) for _ in range(3))
+    if workspace is None:
+        workspace = _empty((max(1, ce_workspace_bytes(N, V_global)),), torch.uint8, dev)
+    st = lib().ce_shard_stats(
+        _ptr(logits_shard, "logits_shard"), _ptr(targets, "targets", torch.int32), N, Vl,
+        vocab_start, V_global, _dtype_code(logits_shard), ignore_index,
+        _ptr(m, "row_max", torch.float32), _ptr(s, "row_sumexp", torch.float32),
+        _ptr(t, "row_target_logit", torch.float32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "ce_shard_stats")
+    return m, s, t
+
+
+def flce_shard_stats(X, W_shard, targets, vocab_start, V_global, bias_shard=None,
+                     ignore_index=-100, out=None, workspace=None, chunk_rows=0, stream=None):
+    """Shard statistics of X W_shard^T (+ bias_shard) without holding the logits."""
+    N, H = X.shape
+    Vl = W_shard.shape[0]
+    dev = X.device
+    dt = _dtype_code(X)
+    m, s, t = out if out is not None else tuple(_empty((N,), torch.float32, dev) for _ in range(3))
+    if workspace is None:
+        workspace = _empty((max(1, flce_workspace_bytes(N, H, Vl, dt, chunk_rows)),), torch.uint8, dev)
+    st = lib().flce_shard_stats(
+        _ptr(X, "X"), _ptr(W_shard, "W_shard", X.dtype), _ptr(bias_shard, "bias_shard", X.dtype),
+        _ptr(targets, "targets", torch.int32), N, H, Vl, vocab_start, V_global, dt, ignore_index,
+        _ptr(m, "row_max", torch.float32), _ptr(s, "row_sumexp", torch.float32),
+        _ptr(t, "row_target_logit", torch.float32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), chunk_rows, _stream(stream))
+    _check(st, "flce_shard_stats")
+    return m, s, t
+
+
+def flce_check_device_error(workspace, stream=None):
+    """Status of the last call that used `workspace` (waits for the stream)."""
+    return int(lib().flce_check_device_error(_ptr(workspace, "workspace"), _stream(stream)))
+
+
+def flce_timing_enable(enable=True):
+    _check(lib().flce_timing_enable(1 if enable else 0), "flce_timing_enable")
+
+
+def flce_timing_read(kind):
+    ms = ctypes.c_double()
+    n = _i64()
+    _check(lib().flce_timing_read(TIMING_KINDS.get(kind, kind), ctypes.byref(ms), ctypes.byref(n)),
+           "flce_timing_read")
+    return float(ms.value), int(n.value)
+
+
+def flce_timing_reset():
+    _check(lib().flce_timing_reset(), "flce_timing_reset")

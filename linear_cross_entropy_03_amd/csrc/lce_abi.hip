@@ -1,0 +1,447 @@
+// C entry points of liblce03 (declared in include/flce.h): argument
+// validation, the chunk planner, workspace carving and the launch sequence.
+//
+// FLCE (torchtune + Liger blog, Figure 1 text; liger-kernel README,
+// FusedLinearCrossEntropy): for each chunk of rows,
+//   1. logits GEMM     Z_c = X_c W^T (+ b)        -> workspace chunk buffer
+//   2. row CE          loss rows; Z_c := dZ_c in place
+//   3. bias colsum     grad_bias (+)= column sums of dZ_c
+//   4. grad_X GEMM     grad_X[c rows] = dZ_c W
+//   5. grad_W GEMM     grad_W (+)= dZ_c^T X_c
+// followed by one deterministic loss reduction. Everything is enqueued on the
+// caller's stream; nothing is allocated.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <vector>
+
+#include "../../include/flce.h"
+#include "lce_common.h"
+
+using namespace lce;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline size_t elem_bytes(int dtype) { return dtype == FLCE_BF16 ? 2 : 4; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxRows = int64_t(1) << 31;     // grid.x of the row kernels
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+// Default byte budget of one chunk's logits (the planner's only memory knob).
+constexpr double kChunkBudget = 2.4e9;
+constexpr int64_t kRowQuantum = 256;  // GEMM tile rows
+
+struct Plan {
+  int64_t chunk;    // rows per chunk
+  int64_t ldz;      // row stride of the chunk buffer (elements)
+  int dx_splits;    // K-splits of the grad_X GEMM
+  size_t off_rows;  // per-row losses [N] float
+  size_t off_chunk; // chunk buffer [chunk, ldz]
+  size_t off_split; // split-K partials [dx_splits, chunk, H] float (dx_splits > 1)
+  size_t total;
+};
+
+// Choose the K-split count of grad_X = dZ_c W (M = chunk, N = H, K = V) that
+// best fills whole waves of 256 workgroups (one 256x256 tile per CU).
+int choose_dx_splits(int64_t chunk, int64_t H, int64_t V) {
+  const int64_t tiles = ((chunk + 255) / 256) * ((H + 255) / 256);
+  auto fill = [&](int s) {
+    const int64_t units = tiles * s;
+    const int64_t waves = (units + 255) / 256;
+    return static_cast<double>(units) / static_cast<double>(waves * 256);
+  };
+  // A split must keep at least 2048 of K and must raise the fill by > 2%.
+  int best = 1;
+  double best_eff = fill(1);
+  for (int s = 2; s <= 8; s *= 2) {
+    if (V / s < 2048) break;
+    const double eff = fill(s);
+    if (eff > best_eff + 0.02) { best_eff = eff; best = s; }
+  }
+  return best;
+}
+
+bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, Plan* p) {
+  if (N < 0 || H <= 0 || V <= 0 || N >= kMaxRows || H >= kMaxDim || V >= kMaxDim) return false;
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return false;
+  if (chunk_rows < 0) return false;
+  const size_t e = elem_bytes(dtype);
+  const int64_t ldz = round_up(V, 8);
+  int64_t chunk;
+  if (chunk_rows > 0) {
+    chunk = std::min(chunk_rows, std::max<int64_t>(N, 1));
+  } else {
+    // Largest multiple of 256 rows under the budget, then evened out over
+    // the chunks; never one chunk holding every row of a multi-tile batch,
+    // so the [N, V] logits are never materialised.
+    int64_t cmax = static_cast<int64_t>(kChunkBudget / (static_cast<double>(ldz) * e));
+    cmax = std::max<int64_t>(kRowQuantum, cmax / kRowQuantum * kRowQuantum);
+    if (N > 2 * kRowQuantum) cmax = std::min(cmax, round_up((N + 1) / 2, kRowQuantum));
+    const int64_t n1 = std::max<int64_t>(N, 1);
+    if (cmax >= n1) {
+      chunk = n1;
+    } else {
+      const int64_t nchunks = (n1 + cmax - 1) / cmax;
+      chunk = std::min(round_up((n1 + nchunks - 1) / nchunks, kRowQuantum), cmax);
+    }
+  }
+  p->chunk = chunk;
+  p->ldz = ldz;
+  p->dx_splits = dtype == FLCE_BF16 ? choose_dx_splits(chunk, H, V) : 1;
+  size_t off = align_up(sizeof(WsHeader));
+  p->off_rows = off;
+  off += align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float));
+  p->off_chunk = off;
+  off += align_up(static_cast<size_t>(chunk) * static_cast<size_t>(ldz) * e);
+  p->off_split = off;
+  if (p->dx_splits > 1)
+    off += align_up(static_cast<size_t>(p->dx_splits) * static_cast<size_t>(chunk) *
+                    static_cast<size_t>(H) * sizeof(float));
+  p->total = off;
+  return true;
+}
+
+size_t ce_ws_bytes(int64_t N) {
+  return align_up(sizeof(WsHeader)) + align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float));
+}
+
+// ------------------------------------------------------------- timing
+
+struct TimedLaunch {
+  int kind;
+  hipEvent_t start, stop;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_records;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` on stream s, bracketed by events when timing is on.
+template <typename F>
+hipError_t timed(int kind, hipStream_t s, F&& launch) {
+  if (!g_timing) return launch();
+  TimedLaunch r{kind, take_event(), take_event()};
+  if (r.start == nullptr || r.stop == nullptr) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(r.start, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(r.stop, s);
+  if (e != hipSuccess) return e;
+  g_records.push_back(r);
+  return hipSuccess;
+}
+
+enum Kind { kKindLogits = 0, kKindRowCE = 1, kKindGradX = 2, kKindGradW = 3, kKindOther = 4 };
+
+#define LCE_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return FLCE_E_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* flce_status_string(int status) {
+  switch (status) {
+    case FLCE_OK: return "ok";
+    case FLCE_E_INVALID_ARG: return "invalid argument (null pointer, size, enum or shape)";
+    case FLCE_E_WORKSPACE: return "workspace missing or smaller than required";
+    case FLCE_E_UNSUPPORTED: return "unsupported layout (pointer not 16-byte aligned, bf16 H not a multiple of 8, or size limit)";
+    case FLCE_E_TARGET: return "a target outside [0, V) that is not ignore_index";
+    case FLCE_E_HIP: return "HIP runtime or kernel launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows) {
+  Plan p;
+  if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return 0;
+  return p.total;
+}
+
+int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, int64_t* chunk_rows_out,
+              int32_t* dx_splits_out) {
+  Plan p;
+  if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
+  if (chunk_rows_out) *chunk_rows_out = p.chunk;
+  if (dx_splits_out) *dx_splits_out = p.dx_splits;
+  return FLCE_OK;
+}
+
+size_t ce_workspace_bytes(int64_t N, int64_t V) {
+  if (N < 0 || V <= 0 || N >= kMaxRows || V >= kMaxDim) return 0;
+  return ce_ws_bytes(N);
+}
+
+static int validate_common(int dtype, int reduction) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_E_INVALID_ARG;
+  if (reduction < FLCE_REDUCTION_NONE || reduction > FLCE_REDUCTION_MEAN) return FLCE_E_INVALID_ARG;
+  return FLCE_OK;
+}
+
+int flce_forward_backward(const void* X, const void* W, const void* bias, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int dtype, int32_t ignore_index,
+                          int reduction, float* loss, float* grad_X, float* grad_W,
+                          float* grad_bias, void* workspace, size_t workspace_bytes,
+                          int64_t chunk_rows, void* stream) {
+  int st = validate_common(dtype, reduction);
+  if (st != FLCE_OK) return st;
+  if (N < 0 || H <= 0 || V <= 0 || chunk_rows < 0) return FLCE_E_INVALID_ARG;
+  if (W == nullptr || loss == nullptr) return FLCE_E_INVALID_ARG;
+  if (N > 0 && (X == nullptr || targets == nullptr)) return FLCE_E_INVALID_ARG;
+  if (grad_bias != nullptr && bias == nullptr) return FLCE_E_INVALID_ARG;
+  if (N >= kMaxRows || H >= kMaxDim || V >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  const void* ptrs[] = {X, W, bias, targets, loss, grad_X, grad_W, grad_bias, workspace};
+  for (const void* q : ptrs)
+    if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
+  if (dtype == FLCE_BF16 && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  Plan p;
+  if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  float* loss_rows = reduction == FLCE_REDUCTION_NONE ? loss : reinterpret_cast<float*>(ws + p.off_rows);
+  void* zbuf = ws + p.off_chunk;
+  float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
+  const size_t e = elem_bytes(dtype);
+  const bool need_grad = grad_X != nullptr || grad_W != nullptr || grad_bias != nullptr;
+  auto gemm = dtype == FLCE_BF16 ? launch_gemm_bf16 : launch_gemm_f32;
+
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
+  }));
+  if (N == 0) {
+    if (grad_W) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W, V * H, 0.0f, s); }));
+    if (grad_bias) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_bias, V, 0.0f, s); }));
+  }
+
+  for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
+    const int64_t rows = std::min(p.chunk, N - r0);
+    const bool first = r0 == 0;
+    const char* Xc = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+
+    GemmDesc g1{};
+    g1.A = Xc; g1.lda = H; g1.a_kmajor = true;
+    g1.B = W; g1.ldb = H; g1.b_kmajor = true;
+    g1.C = zbuf; g1.ldc = p.ldz; g1.bias = bias;
+    g1.M = rows; g1.N = V; g1.K = H;
+    g1.epilogue = kEpiLogits; g1.k_splits = 1;
+    LCE_TRY(timed(kKindLogits, s, [&] { return gemm(g1, s); }));
+
+    LCE_TRY(timed(kKindRowCE, s, [&] {
+      return launch_row_ce(dtype, zbuf, p.ldz, need_grad ? zbuf : nullptr, p.ldz, rows, V,
+                           p.ldz - V, targets + r0, ignore_index, hdr, loss_rows + r0, s);
+    }));
+    if (!need_grad) continue;
+
+    if (grad_bias)
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_colsum(dtype, zbuf, p.ldz, rows, V, grad_bias, !first, s);
+      }));
+
+    if (grad_X) {
+      GemmDesc g2{};
+      g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
+      g2.B = W; g2.ldb = H; g2.b_kmajor = false;
+      g2.M = rows; g2.N = H; g2.K = V;
+      g2.epilogue = kEpiStoreF32;
+      float* out = grad_X + static_cast<size_t>(r0) * H;
+      if (p.dx_splits > 1) {
+        g2.C = split_buf; g2.ldc = H;
+        g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
+        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+        LCE_TRY(timed(kKindOther, s, [&] {
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, s);
+        }));
+      } else {
+        g2.C = out; g2.ldc = H; g2.k_splits = 1;
+        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+      }
+    }
+
+    if (grad_W) {
+      GemmDesc g3{};
+      g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
+      g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
+      g3.C = grad_W; g3.ldc = H;
+      g3.M = V; g3.N = H; g3.K = rows;
+      g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32;
+      g3.k_splits = 1;
+      LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
+    }
+  }
+
+  if (reduction != FLCE_REDUCTION_NONE)
+    LCE_TRY(timed(kKindOther, s, [&] {
+      return launch_reduce_loss(loss_rows, N, hdr, reduction, loss, s);
+    }));
+  return FLCE_OK;
+}
+
+int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* targets, int64_t N,
+                        int64_t V, int dtype, int32_t ignore_index, int reduction, float* loss,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate_common(dtype, reduction);
+  if (st != FLCE_OK) return st;
+  if (N < 0 || V <= 0 || loss == nullptr) return FLCE_E_INVALID_ARG;
+  if (N > 0 && (logits == nullptr || targets == nullptr)) return FLCE_E_INVALID_ARG;
+  if (N >= kMaxRows || V >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  const void* ptrs[] = {logits, grad_logits, targets, loss, workspace};
+  for (const void* q : ptrs)
+    if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < ce_ws_bytes(N)) return FLCE_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  float* loss_rows = reduction == FLCE_REDUCTION_NONE ? loss : reinterpret_cast<float*>(ws + align_up(sizeof(WsHeader)));
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
+  }));
+  LCE_TRY(timed(kKindRowCE, s, [&] {
+    return launch_row_ce(dtype, logits, V, grad_logits, V, N, V, 0, targets, ignore_index, hdr,
+                         loss_rows, s);
+  }));
+  if (reduction != FLCE_REDUCTION_NONE)
+    LCE_TRY(timed(kKindOther, s, [&] {
+      return launch_reduce_loss(loss_rows, N, hdr, reduction, loss, s);
+    }));
+  return FLCE_OK;
+}
+
+int ce_shard_stats(const void* logits_shard, const int32_t* targets, int64_t N, int64_t V_local,
+                   int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
+                   float* row_max, float* row_sumexp, float* row_target_logit, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_E_INVALID_ARG;
+  if (N < 0 || V_local <= 0 || vocab_start < 0 || V_global < vocab_start + V_local)
+    return FLCE_E_INVALID_ARG;
+  if (N > 0 && (logits_shard == nullptr || targets == nullptr || row_max == nullptr ||
+                row_sumexp == nullptr || row_target_logit == nullptr))
+    return FLCE_E_INVALID_ARG;
+  if (N >= kMaxRows || V_global >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  const void* ptrs[] = {logits_shard, targets, row_max, row_sumexp, row_target_logit, workspace};
+  for (const void* q : ptrs)
+    if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < ce_ws_bytes(N)) return FLCE_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  WsHeader* hdr = static_cast<WsHeader*>(workspace);
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, N, V_global, ignore_index, FLCE_REDUCTION_SUM, hdr, s);
+  }));
+  LCE_TRY(timed(kKindRowCE, s, [&] {
+    return launch_shard_stats(dtype, logits_shard, V_local, N, V_local, vocab_start, V_global,
+                              targets, ignore_index, row_max, row_sumexp, row_target_logit, s);
+  }));
+  return FLCE_OK;
+}
+
+int flce_shard_stats(const void* X, const void* W_shard, const void* bias_shard,
+                     const int32_t* targets, int64_t N, int64_t H, int64_t V_local,
+                     int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
+                     float* row_max, float* row_sumexp, float* row_target_logit, void* workspace,
+                     size_t workspace_bytes, int64_t chunk_rows, void* stream) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_E_INVALID_ARG;
+  if (N < 0 || H <= 0 || V_local <= 0 || vocab_start < 0 || V_global < vocab_start + V_local ||
+      chunk_rows < 0)
+    return FLCE_E_INVALID_ARG;
+  if (W_shard == nullptr) return FLCE_E_INVALID_ARG;
+  if (N > 0 && (X == nullptr || targets == nullptr || row_max == nullptr || row_sumexp == nullptr ||
+                row_target_logit == nullptr))
+    return FLCE_E_INVALID_ARG;
+  if (N >= kMaxRows || H >= kMaxDim || V_global >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  const void* ptrs[] = {X, W_shard, bias_shard, targets, row_max, row_sumexp, row_target_logit, workspace};
+  for (const void* q : ptrs)
+    if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
+  if (dtype == FLCE_BF16 && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  Plan p;
+  if (!make_plan(N, H, V_local, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  void* zbuf = ws + p.off_chunk;
+  const size_t e = elem_bytes(dtype);
+  auto gemm = dtype == FLCE_BF16 ? launch_gemm_bf16 : launch_gemm_f32;
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, N, V_global, ignore_index, FLCE_REDUCTION_SUM, hdr, s);
+  }));
+  for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
+    const int64_t rows = std::min(p.chunk, N - r0);
+    GemmDesc g1{};
+    g1.A = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+    g1.lda = H; g1.a_kmajor = true;
+    g1.B = W_shard; g1.ldb = H; g1.b_kmajor = true;
+    g1.C = zbuf; g1.ldc = p.ldz; g1.bias = bias_shard;
+    g1.M = rows; g1.N = V_local; g1.K = H;
+    g1.epilogue = kEpiLogits; g1.k_splits = 1;
+    LCE_TRY(timed(kKindLogits, s, [&] { return gemm(g1, s); }));
+    LCE_TRY(timed(kKindRowCE, s, [&] {
+      return launch_shard_stats(dtype, zbuf, p.ldz, rows, V_local, vocab_start, V_global,
+                                targets + r0, ignore_index, row_max + r0, row_sumexp + r0,
+                                row_target_logit + r0, s);
+    }));
+  }
+  return FLCE_OK;
+}
+
+int flce_check_device_error(const void* workspace, void* stream) {
+  if (workspace == nullptr) return FLCE_E_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return FLCE_E_HIP;
+  int32_t n_bad = 0;
+  if (hipMemcpy(&n_bad, workspace, sizeof(n_bad), hipMemcpyDeviceToHost) != hipSuccess) return FLCE_E_HIP;
+  return n_bad != 0 ? FLCE_E_TARGET : FLCE_OK;
+}
+
+int flce_timing_enable(int enable) {
+  g_timing = enable != 0;
+  return FLCE_OK;
+}
+
+int flce_timing_read(int kind, double* total_ms, int64_t* launches) {
+  double ms = 0.0;
+  int64_t count = 0;
+  for (const TimedLaunch& r : g_records) {
+    if (r.kind != kind) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return FLCE_E_HIP;
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return FLCE_E_HIP;
+    ms += t;
+    ++count;
+  }
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = count;
+  return FLCE_OK;
+}
+
+int flce_timing_reset(void) {
+  for (const TimedLaunch& r : g_records) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return FLCE_E_HIP;
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_records.clear();
+  return FLCE_OK;
+}
+
+}  // extern "C"

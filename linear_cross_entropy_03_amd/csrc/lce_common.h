@@ -1,0 +1,191 @@
+// Shared device helpers and the internal launch interface of liblce03.
+//
+// Everything here is gfx950 (CDNA4) code: wave64, DPP and ds_swizzle
+// cross-lane moves, v_cvt_pk_bf16_f32 rounding, v_exp_f32 / v_log_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Workspace header written by the target-count kernel at the start of every
+// call and read by the kernels after it.
+struct WsHeader {
+  int32_t n_bad;    // targets neither ignore_index nor inside [0, V)
+  int32_t n_valid;  // rows that contribute to the loss
+  float scale;      // gradient factor: 1/n_valid (mean, 0 if none), else 1
+  int32_t pad[61];
+};
+static_assert(sizeof(WsHeader) == 256, "header is one 256-byte slot");
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xFFFFu);
+}
+
+// Element access for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static void store(float* p, float v) { *p = v; }
+  __device__ static void unpack(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                      __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ static void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+  __device__ static void unpack(const uint4& u, float* f) {
+    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+  }
+};
+
+// ------------------------------------------------------- wave64 reductions
+// Butterfly within rows of 16 lanes with DPP, across the two rows of each
+// 32-lane half with ds_swizzle, across the halves with readlane. Every lane
+// returns the same value; the combination order is fixed, so results are
+// deterministic.
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swz_xor16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+  v = fmaxf(v, swz_xor16(v));
+  return fmaxf(lane_f32(v, 0), lane_f32(v, 32));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  v += swz_xor16(v);
+  return lane_f32(v, 0) + lane_f32(v, 32);
+}
+
+// Block-wide reductions; `scratch` holds one float per wave and must not be
+// reused by the caller before the next __syncthreads().
+template <int kThreads>
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+  constexpr int kWaves = kThreads / 64;
+  v = wave_max(v);
+  if (kWaves == 1) return v;
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, scratch[w]);
+  return r;
+}
+template <int kThreads>
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+  constexpr int kWaves = kThreads / 64;
+  v = wave_sum(v);
+  if (kWaves == 1) return v;
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r += scratch[w];
+  return r;
+}
+
+// ------------------------------------------------- internal launch interface
+// Host-side launchers; each returns hipSuccess or the launch error.
+
+enum Epilogue : int {
+  kEpiLogits = 0,   // C (input dtype) = acc (+ bias[n]); C is [M, ldc]
+  kEpiStoreF32 = 1, // C (float) = acc
+  kEpiAccumF32 = 2  // C (float) += acc
+};
+
+struct GemmDesc {
+  const void* A;   // A[m, k] = a_kmajor ? A[m*lda + k] : A[k*lda + m]
+  const void* B;   // B[k, n] = b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
+  void* C;         // C[m, n] at C[m*ldc + n]
+  const void* bias;  // kEpiLogits only, [N] or null
+  int64_t lda, ldb, ldc;
+  int64_t M, N, K;
+  bool a_kmajor, b_kmajor;
+  int epilogue;
+  int k_splits;        // >1: split K; split s writes C + s*split_stride (kEpiStoreF32 only)
+  int64_t split_stride;
+};
+
+hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s);
+
+hipError_t launch_count_targets(const int32_t* targets, int64_t n, int64_t V,
+                                int32_t ignore_index, int reduction, WsHeader* hdr,
+                                hipStream_t s);
+
+// Row CE over `rows` rows of Z (row stride ldz). Row r uses target
+// targets[r]; its loss goes to loss_rows[r]. When grad != null, grad row r
+// (stride ldg; may alias Z) receives scale * (softmax - onehot), and columns
+// [V, V + pad_cols) of it are set to zero.
+hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* grad, int64_t ldg,
+                         int64_t rows, int64_t V, int64_t pad_cols, const int32_t* targets,
+                         int32_t ignore_index, const WsHeader* hdr, float* loss_rows,
+                         hipStream_t s);
+
+hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t rows,
+                              int64_t V_local, int64_t vocab_start, int64_t V_global,
+                              const int32_t* targets, int32_t ignore_index, float* row_max,
+                              float* row_sumexp, float* row_target, hipStream_t s);
+
+hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader* hdr,
+                              int reduction, float* loss, hipStream_t s);
+
+hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V,
+                         float* out, bool accumulate, hipStream_t s);
+
+hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride,
+                                int64_t rows, int64_t cols, int64_t ld_out, float* out,
+                                hipStream_t s);
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+}  // namespace lce

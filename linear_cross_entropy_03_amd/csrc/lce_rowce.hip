@@ -1,0 +1,418 @@
+// Row kernels of the FLCE / CE path (HBM-bound, no MFMA):
+//   * target counting (valid rows, bad targets, reduction scale),
+//   * the fused row cross-entropy: logsumexp, target logit, loss and the
+//     in-place softmax-minus-one-hot gradient (liger-kernel README, "Kernels":
+//     CrossEntropy computes loss and gradient in one pass and may replace the
+//     input logits with the gradient; torchtune + Liger blog, Figure 1 text:
+//     each chunk's loss and logits gradient come from that CE kernel),
+//   * per-shard statistics (DeepSpeed vocab-parallel CE page),
+//   * the deterministic loss reduction, bias-gradient column sums, split-K
+//     reduction and a fill kernel.
+//
+// One workgroup owns one row. Rows are streamed with 16-byte loads; when a row
+// fits in the workgroup's registers (up to 16 vectors per lane) it is read
+// from HBM once and the gradient is computed from the registers, so the row
+// costs one read and one write.
+#include "lce_common.h"
+
+namespace lce {
+
+// ------------------------------------------------------------ target count
+
+__global__ __launch_bounds__(1024) void k_count_targets(const int32_t* __restrict__ t, int64_t n,
+                                                        int64_t V, int32_t ign, int reduction,
+                                                        WsHeader* __restrict__ hdr) {
+  __shared__ int s_valid, s_bad;
+  if (threadIdx.x == 0) { s_valid = 0; s_bad = 0; }
+  __syncthreads();
+  int valid = 0, bad = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) {
+    const int32_t y = t[i];
+    if (y == ign) continue;
+    if (y >= 0 && static_cast<int64_t>(y) < V) ++valid; else ++bad;
+  }
+  atomicAdd(&s_valid, valid);  // integer sums: exact in any order
+  atomicAdd(&s_bad, bad);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    hdr->n_bad = s_bad;
+    hdr->n_valid = s_valid;
+    // reduction: 0 none, 1 sum, 2 mean
+    hdr->scale = (reduction == 2) ? (s_valid > 0 ? 1.0f / static_cast<float>(s_valid) : 0.0f) : 1.0f;
+  }
+}
+
+hipError_t launch_count_targets(const int32_t* targets, int64_t n, int64_t V, int32_t ignore_index,
+                                int reduction, WsHeader* hdr, hipStream_t s) {
+  hipLaunchKernelGGL(k_count_targets, dim3(1), dim3(1024), 0, s, targets, n, V, ignore_index,
+                     reduction, hdr);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ row CE
+
+// Row geometry: `head` scalar elements up to 16-byte alignment, `nvec`
+// 16-byte vectors, then the scalar tail [tail0, V).
+struct RowSplit {
+  int64_t head, nvec, tail0;
+};
+template <typename T>
+__device__ __forceinline__ RowSplit split_row(const T* z, int64_t V) {
+  constexpr int kVec = Elem<T>::kVec;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(z);
+  int64_t head = static_cast<int64_t>(((16u - (a & 15u)) & 15u) / sizeof(T));
+  if (head > V) head = V;
+  const int64_t nvec = (V - head) / kVec;
+  return {head, nvec, head + nvec * kVec};
+}
+
+// Fold x into a running (max, sum of exp(x - max)) pair.
+__device__ __forceinline__ void online_push(float& m, float& s, float x) {
+  const float mn = fmaxf(m, x);
+  s = s * __builtin_amdgcn_exp2f((m - mn) * kLog2e) + __builtin_amdgcn_exp2f((x - mn) * kLog2e);
+  m = mn;
+}
+template <int kN>
+__device__ __forceinline__ void online_push_vec(float& m, float& s, const float* f) {
+  float vm = f[0];
+#pragma unroll
+  for (int i = 1; i < kN; ++i) vm = fmaxf(vm, f[i]);
+  const float mn = fmaxf(m, vm);
+  float acc = s * __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+#pragma unroll
+  for (int i = 0; i < kN; ++i) acc += __builtin_amdgcn_exp2f((f[i] - mn) * kLog2e);
+  s = acc;
+  m = mn;
+}
+
+// Block-wide (max, sumexp) from per-lane online pairs.
+template <int kThreads>
+__device__ __forceinline__ void block_lse_parts(float m, float s, float* red0, float* red1,
+                                                float& M, float& S) {
+  M = block_max<kThreads>(m, red0);
+  const float mine = (m == -INFINITY) ? 0.0f : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+  S = block_sum<kThreads>(mine, red1);
+}
+
+// kRes > 0: the row's vectors stay in registers (kRes per lane); kRes == 0:
+// two streaming passes over the row. Z and G may be the same rows (in-place),
+// so neither is declared __restrict__.
+template <typename T, int kThreads, int kRes>
+__global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T* G,
+                                                     int64_t ldg, int64_t V, int64_t pad_cols,
+                                                     const int32_t* __restrict__ targets,
+                                                     int32_t ign, const WsHeader* __restrict__ hdr,
+                                                     float* __restrict__ loss_rows) {
+  using E = Elem<T>;
+  constexpr int kVec = E::kVec;
+  __shared__ float red0[kThreads / 64], red1[kThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const T* z = Z + row * ldz;
+  const int32_t y = targets[row];
+  const bool valid = (y != ign) && y >= 0 && static_cast<int64_t>(y) < V;
+  const RowSplit rs = split_row(z, V);
+  const uint4* zv = reinterpret_cast<const uint4*>(z + rs.head);
+
+  // The target logit is read before any lane can overwrite the row.
+  float zt = 0.0f;
+  if (tid == 0 && valid) zt = E::load(z + y);
+
+  float m = -INFINITY, s = 0.0f;
+  uint4 buf[kRes > 0 ? kRes : 1];
+  if constexpr (kRes > 0) {
+#pragma unroll
+    for (int j = 0; j < kRes; ++j) {
+      const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
+      buf[j] = vi < rs.nvec ? zv[vi] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // max first, then one exp per element against the lane maximum.
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRes; ++j) {
+      const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
+      if (vi < rs.nvec) {
+        float f[kVec];
+        E::unpack(buf[j], f);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) lm = fmaxf(lm, f[i]);
+      }
+    }
+    if (tid < rs.head) lm = fmaxf(lm, E::load(z + tid));
+    if (tid < V - rs.tail0) lm = fmaxf(lm, E::load(z + rs.tail0 + tid));
+    float ls = 0.0f;
+    if (lm != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kRes; ++j) {
+        const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
+        if (vi < rs.nvec) {
+          float f[kVec];
+          E::unpack(buf[j], f);
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) ls += __builtin_amdgcn_exp2f((f[i] - lm) * kLog2e);
+        }
+      }
+      if (tid < rs.head) ls += __builtin_amdgcn_exp2f((E::load(z + tid) - lm) * kLog2e);
+      if (tid < V - rs.tail0) ls += __builtin_amdgcn_exp2f((E::load(z + rs.tail0 + tid) - lm) * kLog2e);
+    }
+    m = lm;
+    s = ls;
+  } else {
+    for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+      float f[kVec];
+      E::unpack(zv[vi], f);
+      online_push_vec<kVec>(m, s, f);
+    }
+    if (tid < rs.head) online_push(m, s, E::load(z + tid));
+    if (tid < V - rs.tail0) online_push(m, s, E::load(z + rs.tail0 + tid));
+  }
+
+  float M, S;
+  block_lse_parts<kThreads>(m, s, red0, red1, M, S);
+  const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
+  if (tid == 0) loss_rows[row] = valid ? (lse - zt) : 0.0f;
+  if (G == nullptr) return;
+
+  const float c = valid ? hdr->scale : 0.0f;
+  T* g = G + row * ldg;
+  uint4* gv = reinterpret_cast<uint4*>(g + rs.head);
+  auto grad_of = [&](float x, int64_t v) -> float {
+    if (!valid) return 0.0f;
+    const float p = __builtin_amdgcn_exp2f((x - lse) * kLog2e);
+    return c * (v == y ? p - 1.0f : p);
+  };
+  if constexpr (kRes > 0) {
+#pragma unroll
+    for (int j = 0; j < kRes; ++j) {
+      const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
+      if (vi < rs.nvec) {
+        float f[kVec];
+        E::unpack(buf[j], f);
+        const int64_t v0 = rs.head + vi * kVec;
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
+        gv[vi] = E::pack(f);
+      }
+    }
+  } else {
+    for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+      float f[kVec];
+      E::unpack(zv[vi], f);
+      const int64_t v0 = rs.head + vi * kVec;
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
+      gv[vi] = E::pack(f);
+    }
+  }
+  if (tid < rs.head) E::store(g + tid, grad_of(E::load(z + tid), tid));
+  if (tid < V - rs.tail0) {
+    const int64_t v = rs.tail0 + tid;
+    E::store(g + v, grad_of(E::load(z + v), v));
+  }
+  if (tid < pad_cols) E::store(g + V + tid, 0.0f);
+}
+
+template <typename T, int kThreads>
+static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
+                                  int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
+                                  const WsHeader* hdr, float* loss_rows, hipStream_t s) {
+  constexpr int kVec = Elem<T>::kVec;
+  const int64_t nvec_max = (V + kVec - 1) / kVec;
+  const T* z = static_cast<const T*>(Z);
+  T* g = static_cast<T*>(G);
+  const dim3 grid(static_cast<unsigned>(rows)), block(kThreads);
+#define LCE_ROW_CE(R)                                                                           \
+  hipLaunchKernelGGL((k_row_ce<T, kThreads, R>), grid, block, 0, s, z, ldz, g, ldg, V, pad_cols, \
+                     targets, ign, hdr, loss_rows)
+  if (nvec_max <= 1 * kThreads) LCE_ROW_CE(1);
+  else if (nvec_max <= 2 * kThreads) LCE_ROW_CE(2);
+  else if (nvec_max <= 4 * kThreads) LCE_ROW_CE(4);
+  else if (nvec_max <= 8 * kThreads) LCE_ROW_CE(8);
+  else if (nvec_max <= 16 * kThreads) LCE_ROW_CE(16);
+  else LCE_ROW_CE(0);
+#undef LCE_ROW_CE
+  return hipGetLastError();
+}
+
+hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
+                         int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
+                         const WsHeader* hdr, float* loss_rows, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const bool big = V >= 16384;
+  if (dtype == 1) {
+    return big ? row_ce_dispatch<uint16_t, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign,
+                                                 hdr, loss_rows, s)
+               : row_ce_dispatch<uint16_t, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign,
+                                                hdr, loss_rows, s);
+  }
+  return big ? row_ce_dispatch<float, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
+                                            loss_rows, s)
+             : row_ce_dispatch<float, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
+                                           loss_rows, s);
+}
+
+// ------------------------------------------------------------ shard stats
+
+template <typename T, int kThreads>
+__global__ __launch_bounds__(kThreads) void k_shard_stats(const T* __restrict__ Z, int64_t ldz,
+                                                          int64_t Vl, int64_t v0, int64_t Vg,
+                                                          const int32_t* __restrict__ targets,
+                                                          int32_t ign, float* __restrict__ rmax,
+                                                          float* __restrict__ rsum,
+                                                          float* __restrict__ rtgt) {
+  using E = Elem<T>;
+  constexpr int kVec = E::kVec;
+  __shared__ float red0[kThreads / 64], red1[kThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const T* z = Z + row * ldz;
+  const RowSplit rs = split_row(z, Vl);
+  const uint4* zv = reinterpret_cast<const uint4*>(z + rs.head);
+  float m = -INFINITY, s = 0.0f;
+  for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+    float f[kVec];
+    E::unpack(zv[vi], f);
+    online_push_vec<kVec>(m, s, f);
+  }
+  if (tid < rs.head) online_push(m, s, E::load(z + tid));
+  if (tid < Vl - rs.tail0) online_push(m, s, E::load(z + rs.tail0 + tid));
+  float M, S;
+  block_lse_parts<kThreads>(m, s, red0, red1, M, S);
+  if (tid == 0) {
+    const int32_t y = targets[row];
+    const int64_t local = static_cast<int64_t>(y) - v0;
+    const bool here = (y != ign) && y >= 0 && static_cast<int64_t>(y) < Vg && local >= 0 && local < Vl;
+    rmax[row] = M;
+    rsum[row] = S;
+    rtgt[row] = here ? E::load(z + local) : 0.0f;
+  }
+}
+
+hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V_local,
+                              int64_t vocab_start, int64_t V_global, const int32_t* targets,
+                              int32_t ign, float* row_max, float* row_sumexp, float* row_target,
+                              hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(rows));
+  if (dtype == 1)
+    hipLaunchKernelGGL((k_shard_stats<uint16_t, 1024>), grid, dim3(1024), 0, s,
+                       static_cast<const uint16_t*>(Z), ldz, V_local, vocab_start, V_global, targets,
+                       ign, row_max, row_sumexp, row_target);
+  else
+    hipLaunchKernelGGL((k_shard_stats<float, 1024>), grid, dim3(1024), 0, s,
+                       static_cast<const float*>(Z), ldz, V_local, vocab_start, V_global, targets,
+                       ign, row_max, row_sumexp, row_target);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ loss reduce
+
+// Sum of per-row losses in float64, in a fixed order independent of how the
+// rows were chunked; mean divides by the valid-row count.
+__global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ rows, int64_t n,
+                                                      const WsHeader* __restrict__ hdr,
+                                                      int reduction, float* __restrict__ out) {
+  __shared__ double part[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) acc += static_cast<double>(rows[i]);
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double total = part[0];
+    if (reduction == 2) total = hdr->n_valid > 0 ? total / static_cast<double>(hdr->n_valid) : 0.0;
+    out[0] = static_cast<float>(total);
+  }
+}
+
+hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader* hdr, int reduction,
+                              float* loss, hipStream_t s) {
+  hipLaunchKernelGGL(k_reduce_loss, dim3(1), dim3(1024), 0, s, loss_rows, n, hdr, reduction, loss);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------- bias-gradient colsum
+
+// out[v] (+)= sum over rows of Z[r, v]; each lane owns two adjacent columns
+// and walks the rows in order (deterministic).
+template <typename T>
+__global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ Z, int64_t ldz, int64_t rows,
+                                                int64_t V, float* __restrict__ out, int accumulate) {
+  const int64_t v = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 2;
+  if (v >= V) return;
+  const bool two = v + 1 < V;
+  float a0 = 0.0f, a1 = 0.0f;
+  const T* p = Z + v;
+  int64_t r = 0;
+  for (; r + 4 <= rows; r += 4) {
+    float x[4], w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[u] = Elem<T>::load(p + (r + u) * ldz);
+      w[u] = two ? Elem<T>::load(p + (r + u) * ldz + 1) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { a0 += x[u]; a1 += w[u]; }
+  }
+  for (; r < rows; ++r) {
+    a0 += Elem<T>::load(p + r * ldz);
+    if (two) a1 += Elem<T>::load(p + r * ldz + 1);
+  }
+  if (accumulate) { a0 += out[v]; if (two) a1 += out[v + 1]; }
+  out[v] = a0;
+  if (two) out[v + 1] = a1;
+}
+
+hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V, float* out,
+                         bool accumulate, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((V + 511) / 512));
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_colsum<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(Z),
+                       ldz, rows, V, out, accumulate ? 1 : 0);
+  else
+    hipLaunchKernelGGL(k_colsum<float>, grid, dim3(256), 0, s, static_cast<const float*>(Z), ldz,
+                       rows, V, out, accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------- split-K reduce
+
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ parts, int splits,
+                                                       int64_t stride, int64_t rows, int64_t cols,
+                                                       int64_t ld_out, float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows * cols) return;
+  const int64_t r = i / cols, c = i - r * cols;
+  float acc = parts[r * cols + c];
+  for (int sp = 1; sp < splits; ++sp) acc += parts[sp * stride + r * cols + c];
+  out[r * ld_out + c] = acc;
+}
+
+hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride, int64_t rows,
+                                int64_t cols, int64_t ld_out, float* out, hipStream_t s) {
+  const int64_t n = rows * cols;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                     parts, splits, split_stride, rows, cols, ld_out, out);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------------- fill
+
+__global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_fill_f32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace lce

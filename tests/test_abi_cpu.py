@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/flce.h declares, and rejects bad arguments before touching the GPU.
+No kernel is launched here."""
+
+import ctypes
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB_PATH = os.path.join(ROOT, "linear_cross_entropy_03_amd", "liblce03.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH),
+                                reason="liblce03.so not built (run __graft_entry__.build())")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from linear_cross_entropy_03_amd import binding
+    binding.lib()
+    return binding
+
+
+def test_exports_every_declared_function(B):
+    names = B.header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(B.lib(), n), n
+        assert n in B._SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings(B):
+    for code in range(6):
+        assert B.status_text(code)
+    assert B.status_text(99) == "unknown status"
+
+
+def test_workspace_queries_and_plan(B):
+    assert B.flce_workspace_bytes(0, 64, 1024, B.F32) > 0
+    assert B.flce_workspace_bytes(10, 0, 1024, B.F32) == 0
+    assert B.flce_workspace_bytes(10, 64, 1024, 7) == 0
+    small = B.flce_workspace_bytes(32768, 4096, 128256, B.BF16, 1024)
+    big = B.flce_workspace_bytes(32768, 4096, 128256, B.BF16, 4096)
+    assert big > small >= 1024 * 128256 * 2
+    # The automatic chunk never holds all rows of a multi-chunk batch.
+    for N, H, V in ((8192, 2048, 128256), (32768, 4096, 128256), (32768, 4096, 256000)):
+        c, s = B.flce_plan(N, H, V, B.BF16)
+        assert c % 256 == 0 and c < N
+        assert c * ((V + 7) // 8 * 8) * 2 <= 2.5e9
+        assert s in (1, 2, 4, 8)
+    assert B.flce_plan(256, 64, 1024, B.F32) == (256, 1)
+    assert B.flce_plan(300, 64, 1000, B.F32, 64)[0] == 64
+    assert B.ce_workspace_bytes(1024, 32768) >= 1024 * 4
+    assert B.ce_workspace_bytes(-1, 5) == 0
+
+
+def _fb(B, **kw):
+    args = dict(X=16, W=16, bias=None, targets=16, N=4, H=8, V=10, dtype=B.BF16, ign=-100, red=2,
+                loss=16, gX=16, gW=16, gb=None, ws=16, wsb=1 << 30, chunk=0, stream=None)
+    args.update(kw)
+    return B.lib().flce_forward_backward(
+        args["X"], args["W"], args["bias"], args["targets"], args["N"], args["H"], args["V"],
+        args["dtype"], args["ign"], args["red"], args["loss"], args["gX"], args["gW"], args["gb"],
+        args["ws"], args["wsb"], args["chunk"], args["stream"])
+
+
+def test_flce_argument_errors(B):
+    # Pointers here are fake (aligned integers): every call must fail in
+    # validation, before anything is enqueued.
+    assert _fb(B, W=None) == B.E_INVALID_ARG
+    assert _fb(B, loss=None) == B.E_INVALID_ARG
+    assert _fb(B, X=None) == B.E_INVALID_ARG
+    assert _fb(B, targets=None) == B.E_INVALID_ARG
+    assert _fb(B, N=-1) == B.E_INVALID_ARG
+    assert _fb(B, H=0) == B.E_INVALID_ARG
+    assert _fb(B, V=0) == B.E_INVALID_ARG
+    assert _fb(B, dtype=5) == B.E_INVALID_ARG
+    assert _fb(B, red=3) == B.E_INVALID_ARG
+    assert _fb(B, gb=16) == B.E_INVALID_ARG          # grad_bias without bias
+    assert _fb(B, chunk=-2) == B.E_INVALID_ARG
+    assert _fb(B, X=24) == B.E_UNSUPPORTED           # misaligned
+    assert _fb(B, H=12) == B.E_UNSUPPORTED           # bf16 needs H % 8 == 0
+    assert _fb(B, ws=None) == B.E_WORKSPACE
+    assert _fb(B, wsb=64) == B.E_WORKSPACE
+
+
+def test_ce_and_shard_argument_errors(B):
+    L = B.lib()
+    assert L.ce_forward_backward(16, 16, 16, 4, 10, B.BF16, -100, 9, 16, 16, 1 << 20, None) == B.E_INVALID_ARG
+    assert L.ce_forward_backward(16, 16, 16, 4, 0, B.BF16, -100, 1, 16, 16, 1 << 20, None) == B.E_INVALID_ARG
+    assert L.ce_forward_backward(16, 16, 16, 4, 10, B.BF16, -100, 1, 16, 16, 8, None) == B.E_WORKSPACE
+    assert L.ce_forward_backward(16, 40, 16, 4, 10, B.BF16, -100, 1, 16, 16, 1 << 20, None) == B.E_UNSUPPORTED
+    # shard must fit inside the global vocabulary
+    assert L.ce_shard_stats(16, 16, 4, 10, 5, 12, B.BF16, -100, 16, 16, 16, 16, 1 << 20, None) == B.E_INVALID_ARG
+    assert L.flce_shard_stats(16, 16, None, 16, 4, 8, 10, 0, 10, B.BF16, -100, 16, 16, 16, 16, 8, 0,
+                              None) == B.E_WORKSPACE
+    assert L.flce_check_device_error(None, None) == B.E_INVALID_ARG

@@ -1,0 +1,214 @@
+"""GPU parity: fused linear cross-entropy (through the C ABI) against the FP64
+oracle, element by element at sizes the oracle finishes in seconds (several
+tiles, several chunks, ragged tails), plus invariants."""
+
+import numpy as np
+import pytest
+
+from gpu_util import (TOL, check_max_rel, check_scalar, oracle_inputs, say, to_dev, to_host,
+                      torch_or_skip)
+from linear_cross_entropy_03_amd import synth
+from oracle import flce_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    torch_or_skip()
+    from linear_cross_entropy_03_amd import binding
+    binding.lib()
+    return binding
+
+
+def run_flce(B, inp, reduction, chunk_rows=0, want=("X", "W", "bias")):
+    import torch
+    dt = inp["dtype"]
+    X, W = to_dev(inp["X"], dt), to_dev(inp["W"], dt)
+    b = to_dev(inp["bias"], dt)
+    y = to_dev(inp["targets"], "i32")
+    loss, gX, gW, gb = B.flce_forward_backward(
+        X, W, y, bias=b, reduction=reduction, chunk_rows=chunk_rows,
+        grad_X="X" in want, grad_W="W" in want, grad_bias=(b is not None and "bias" in want))
+    torch.cuda.synchronize()
+    return to_host(loss), to_host(gX), to_host(gW), to_host(gb)
+
+
+def check_against_oracle(inp, reduction, got, want=("X", "W", "bias")):
+    X, W, b, y = oracle_inputs(inp)
+    ref_loss, ref_g, info = O.flce(X, W, y, bias=b, reduction=reduction)
+    t = TOL[inp["dtype"]]
+    loss, gX, gW, gb = got
+    if reduction == "none":
+        check_max_rel(loss, ref_loss, t["loss"], "loss rows")
+        assert np.all(loss[y == -100] == 0.0), "ignored rows must have exact zero loss"
+    else:
+        check_scalar(loss, ref_loss, t["loss"])
+    if "X" in want:
+        check_max_rel(gX, ref_g["X"], t["grad"], "grad_X")
+        assert np.all(gX[y == -100] == 0.0), "ignored rows must have exact zero grad_X"
+    if "W" in want:
+        check_max_rel(gW, ref_g["W"], t["grad"], "grad_W")
+    if b is not None and "bias" in want:
+        check_max_rel(gb, ref_g["bias"], t["grad"], "grad_bias")
+    return ref_loss, ref_g
+
+
+@pytest.mark.parametrize("reduction", ["mean", "none", "sum"])
+def test_tiny_f32(B, reduction):
+    """N 256, H 64, V 1024, fp32, 10% ignored."""
+    inp = synth.make_flce_inputs(256, 64, 1024, "f32", ignore_frac=0.1)
+    say("flce tiny f32", reduction)
+    check_against_oracle(inp, reduction, run_flce(B, inp, reduction))
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 0])
+def test_tiny_f32_forced_chunks(B, chunk):
+    inp = synth.make_flce_inputs(256, 64, 1024, "f32", ignore_frac=0.1)
+    say("flce tiny f32 chunk", chunk)
+    check_against_oracle(inp, "mean", run_flce(B, inp, "mean", chunk_rows=chunk))
+
+
+def test_f32_ragged_with_bias(B):
+    inp = synth.make_flce_inputs(300, 72, 1000, "f32", bias_std=0.5, ignore_frac=0.15, seed=5)
+    say("flce f32 ragged bias")
+    check_against_oracle(inp, "sum", run_flce(B, inp, "sum", chunk_rows=128))
+
+
+@pytest.mark.parametrize("chunk", [0, 256, 160])
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_bf16_ragged_tiles(B, reduction, chunk):
+    """bf16, N 600 (3 row tiles), H 136 (K tail), V 1000 (V % 8 != 0), bias."""
+    inp = synth.make_flce_inputs(600, 136, 1000, "bf16", bias_std=0.1, ignore_frac=0.1, seed=11)
+    say("flce bf16 ragged", reduction, chunk)
+    check_against_oracle(inp, reduction, run_flce(B, inp, reduction, chunk_rows=chunk))
+
+
+def test_bf16_multi_chunk_mid(B):
+    """N 1024 in 4 chunks, H 512, V 4099: the grad_W read-modify-write path."""
+    inp = synth.make_flce_inputs(1024, 512, 4099, "bf16", ignore_frac=0.1, seed=12)
+    say("flce bf16 mid 4 chunks")
+    check_against_oracle(inp, "mean", run_flce(B, inp, "mean", chunk_rows=256))
+
+
+def test_bf16_split_k_grad_x(B):
+    """N 512, H 2048, V 16384: the planner splits grad_X's K over V."""
+    c, s = B.flce_plan(512, 2048, 16384, B.BF16)
+    assert s > 1
+    inp = synth.make_flce_inputs(512, 2048, 16384, "bf16", ignore_frac=0.1, seed=13)
+    say("flce bf16 split-K", c, s)
+    check_against_oracle(inp, "mean", run_flce(B, inp, "mean"))
+
+
+def test_bf16_zipf_targets_with_skipped_grads(B):
+    inp = synth.make_flce_inputs(768, 256, 3000, "bf16", target_dist="zipf", seed=14)
+    say("flce bf16 zipf, grad_X only")
+    got = run_flce(B, inp, "mean", chunk_rows=256, want=("X",))
+    assert got[2] is None
+    check_against_oracle(inp, "mean", got, want=("X",))
+    say("flce bf16 zipf, grad_W only")
+    got = run_flce(B, inp, "mean", chunk_rows=256, want=("W",))
+    check_against_oracle(inp, "mean", got, want=("W",))
+    say("flce bf16 zipf, loss only")
+    got = run_flce(B, inp, "mean", want=())
+    check_against_oracle(inp, "mean", got, want=())
+
+
+def test_loss_bitwise_independent_of_chunking_and_deterministic(B):
+    """Per-row losses (hence the loss) are bitwise independent of the chunk
+    size; grad_X is bitwise equal whenever the grad_X K-split is the same (a
+    different split only changes its rounding order); repeated calls are
+    bitwise identical."""
+    inp = synth.make_flce_inputs(1000, 256, 5000, "bf16", bias_std=0.02, seed=15)
+    say("flce chunk independence")
+    chunks = (0, 256, 512, 1000)
+    runs = {c: run_flce(B, inp, "none", chunk_rows=c) for c in chunks}
+    splits = {c: B.flce_plan(1000, 256, 5000, B.BF16, c)[1] for c in chunks}
+    base = runs[1000]
+    for c, r in runs.items():
+        assert np.array_equal(r[0], base[0]), f"loss rows differ at chunk {c}"
+        if splits[c] == splits[1000]:
+            assert np.array_equal(r[1], base[1]), f"grad_X differs at chunk {c}"
+        else:
+            check_max_rel(r[1], base[1], 1e-5, f"grad_X chunk {c} vs 1000")
+        check_max_rel(r[2], base[2], 1e-5, f"grad_W chunk {c} vs 1000")
+        check_max_rel(r[3], base[3], 1e-5, f"grad_bias chunk {c} vs 1000")
+    again = run_flce(B, inp, "none", chunk_rows=256)
+    for a, b in zip(again, runs[256]):
+        assert np.array_equal(a, b), "two identical calls differ"
+
+
+def test_gradient_invariants_f32(B):
+    """Each dlogits row sums to zero, so sum_v grad_W[v, :] = 0 and
+    sum_v grad_bias[v] = 0 (fp32: up to fp32 rounding)."""
+    inp = synth.make_flce_inputs(512, 128, 2048, "f32", bias_std=0.05, seed=16)
+    say("flce invariants f32")
+    loss, gX, gW, gb = run_flce(B, inp, "sum")
+    assert np.abs(gW.sum(axis=0)).max() <= 1e-5 * np.abs(gW).max() * 2048 ** 0.5
+    assert abs(gb.sum()) <= 1e-5 * np.abs(gb).max() * 2048 ** 0.5
+
+
+def test_gradient_invariants_bf16(B):
+    """With dlogits stored in bf16 each row sum is off by at most the rounding
+    of its entries: at most 2**-9 for the target entry (|p - 1| < 1) plus
+    2**-9 * sum_v p_v for the rest, i.e. 2**-8 per valid row in total."""
+    inp = synth.make_flce_inputs(512, 128, 2048, "bf16", bias_std=0.05, seed=16)
+    say("flce invariants bf16")
+    loss, gX, gW, gb = run_flce(B, inp, "sum")
+    n_valid = int((inp["targets"] != -100).sum())
+    assert abs(gb.sum()) <= n_valid * 2.0 ** -8
+    xmax = np.abs(np.asarray(inp["X_f32"], dtype=np.float64)).max()
+    assert np.abs(gW.sum(axis=0)).max() <= n_valid * 2.0 ** -8 * xmax
+
+
+def test_all_ignored_and_empty(B):
+    import torch
+    inp = synth.make_flce_inputs(64, 32, 100, "f32", ignore_frac=1.0)
+    say("flce all ignored")
+    loss, gX, gW, _ = run_flce(B, inp, "mean")
+    assert float(loss[0]) == 0.0 and np.all(gX == 0) and np.all(gW == 0)
+    X = torch.empty((0, 32), dtype=torch.float32, device="cuda")
+    W = torch.randn((100, 32), dtype=torch.float32, device="cuda")
+    y = torch.empty((0,), dtype=torch.int32, device="cuda")
+    gW0 = torch.full((100, 32), 7.0, device="cuda")
+    say("flce empty batch")
+    l0, _, gW0, _ = B.flce_forward_backward(X, W, y, reduction="sum", grad_X=False, grad_W=gW0)
+    torch.cuda.synchronize()
+    assert float(l0.item()) == 0.0 and bool((gW0 == 0).all())
+
+
+def test_bad_target_reported(B):
+    import torch
+    inp = synth.make_flce_inputs(40, 16, 50, "f32", ignore_frac=0.0, seed=17)
+    y = inp["targets"].copy()
+    y[5] = 77
+    inp2 = dict(inp, targets=y)
+    ws = torch.zeros(B.flce_workspace_bytes(40, 16, 50, B.F32), dtype=torch.uint8, device="cuda")
+    say("flce bad target")
+    loss, gX, gW, _ = B.flce_forward_backward(
+        to_dev(inp["X"], "f32"), to_dev(inp["W"], "f32"), to_dev(y, "i32"), reduction="none",
+        workspace=ws)
+    assert B.flce_check_device_error(ws) == B.E_TARGET
+    check_against_oracle(inp2, "none", (to_host(loss), to_host(gX), to_host(gW), None))
+
+
+def test_shard_stats_of_projection(B):
+    """flce_shard_stats on W[v0:v0+Vl] equals the oracle's statistics of the
+    materialised shard logits."""
+    import torch
+    inp = synth.make_flce_inputs(700, 256, 3000, "bf16", bias_std=0.1, seed=18)
+    X, W, b, y = oracle_inputs(inp)
+    v0, Vl = 1000, 1200
+    say("flce shard stats")
+    m, s, t = B.flce_shard_stats(to_dev(inp["X"], "bf16"),
+                                 to_dev(np.ascontiguousarray(inp["W"][v0:v0 + Vl]), "bf16"),
+                                 to_dev(inp["targets"], "i32"), v0, 3000,
+                                 bias_shard=to_dev(np.ascontiguousarray(inp["bias"][v0:v0 + Vl]), "bf16"),
+                                 chunk_rows=256)
+    torch.cuda.synchronize()
+    rm, rs, rt = O.flce_shard_stats(X, W[v0:v0 + Vl], y, v0, 3000, bias_shard=b[v0:v0 + Vl])
+    # logits are rounded to bf16 before the statistics: compare at bf16 tolerance
+    check_max_rel(to_host(m), rm, 1e-2, "row max")
+    check_max_rel(to_host(s), rs, 2e-2, "row sumexp")
+    check_max_rel(to_host(t), rt, 1e-2, "target logit")
+    assert np.all(to_host(t)[(inp["targets"] < v0) | (inp["targets"] >= v0 + Vl)] == 0.0)
