@@ -23,6 +23,7 @@ HIPCC_FLAGS = [
     # Keep the compiler from forming packed-fp32 VALU instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    "-Wno-inline-asm",
 ]
 
 

@@ -16,6 +16,8 @@
 // the transposing stores and the MFMA operand reads are bank-conflict free.
 //
 // fp32 path: a plain LDS-tiled VALU kernel (used for fp32 inputs).
+#include <cstdlib>
+
 #include "lce_common.h"
 
 namespace lce {
@@ -267,8 +269,333 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmDesc d, int64_t tiles_
 
 }  // namespace mfma
 
+// ---------------------------------------------------------------------------
+// v2: 4-stage pipeline with direct HBM->LDS loads.
+//
+// K advances 32 at a time through 4 LDS stages of 32 KiB (A 16 KiB + B
+// 16 KiB). Each stage is filled by buffer_load_dwordx4 ... lds: the data never
+// passes through registers, and rows past the operand's end and K-tails read
+// as zero through the buffer descriptor's range check instead of branches.
+// Loads run three stages ahead of the MFMAs. The LDS-DMA loads are issued
+// from inline assembly and their completion is tracked here with explicit
+// vmcnt waits (the compiler would otherwise wait for every load in flight
+// before each LDS read). One barrier per stage sits between the stage's two
+// 16-wide k steps, so the next stage's first fragments are read from LDS while
+// the current stage's second k step is on the MFMA pipe.
+//
+// Operands that are k-contiguous in HBM are stored [row][k] and read with
+// ds_read_b128; m/n-contiguous operands are stored [k][mn] as loaded and read
+// with ds_read_b64_tr_b16, which hands each lane four consecutive k of one
+// column. Both layouts XOR-swizzle their 16-byte slots so the MFMA operand
+// reads are bank-conflict free.
+namespace mfma2 {
+
+constexpr int kBM = 256, kBK = 32, kStages = 4, kThreads = 256;
+constexpr int kOpElems = kBM * kBK;           // one operand, one stage: 8192 bf16
+constexpr int kStageElems = 2 * kOpElems;     // A then B
+constexpr int kLoadsPerStage = 8;             // DMA instructions per wave per stage
+constexpr int kOOB = 0x7FFFFFF0;              // buffer offset that reads as zero
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4_t lds_v4;
+
+// Wave index as a scalar (the compiler cannot see that threadIdx.x >> 6 is
+// uniform across a wave).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ int kswz(int row) {
+  return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
+}
+__device__ __forceinline__ int mswz(int k) {
+  const int i = k & 3;
+  return ((i & 1) << 1) | ((i & 2) << 1) | ((i & 1) << 3);
+}
+// Element offset of (row, 8-wide k chunk kc) in a k-major stage tile [256][32].
+__device__ __forceinline__ int koff(int row, int kc) { return row * kBK + ((kc ^ kswz(row)) << 3); }
+// Element offset of (k, mn) in an mn-major stage tile [32][256].
+__device__ __forceinline__ int moff(int k, int mn) {
+  return k * kBM + (((mn >> 3) ^ mswz(k)) << 3) + (mn & 7);
+}
+
+// Raw buffer descriptor over [base, base + bytes) in scalar registers; reads
+// past the end return zero.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : static_cast<int>(bytes));
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)) & 0xFFFF;  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(n);
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(p)));
+}
+
+// 16 bytes per lane from buffer offset voff to LDS dst + 16 * lane.
+__device__ __forceinline__ void dma16(const i32x4_t& r, uint32_t dst, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(dst), "v"(voff), "s"(r)
+               : "memory");
+}
+
+template <int kN>
+__device__ __forceinline__ void wait_vmcnt() {
+  // vmcnt = kN; expcnt and lgkmcnt at their maxima (not waited on).
+  __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+__device__ __forceinline__ void wait_stage_loads(int ahead) {
+  if (ahead >= 3) wait_vmcnt<3 * kLoadsPerStage>();
+  else if (ahead == 2) wait_vmcnt<2 * kLoadsPerStage>();
+  else if (ahead == 1) wait_vmcnt<kLoadsPerStage>();
+  else wait_vmcnt<0>();
+}
+__device__ __forceinline__ void block_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One operand of the GEMM: issues a stage's direct loads and reads MFMA
+// fragments. `rows` is the extent along m (A) or n (B); ld its row stride.
+template <bool kKMajor>
+struct Operand {
+  const uint16_t* P;
+  int64_t ld, rows, r0;   // r0: first m/n row of this tile
+  i32x4_t tile_rsrc;      // k-major: the tile's rows
+  int voff0[4];           // k-major: per-lane byte offset of (row, chunk) at k = 0
+  int kc8[4];             // k-major: per-lane chunk start (elements)
+  int moff0[4];           // mn-major: per-lane byte offset inside a stage
+
+  __device__ __forceinline__ void init(const uint16_t* P_, int64_t ld_, int64_t rows_, int64_t r0_) {
+    P = P_; ld = ld_; rows = rows_; r0 = r0_;
+    const int lane = threadIdx.x & 63, w = wave_id();
+    if constexpr (kKMajor) {
+      int64_t nrows = rows - r0;
+      if (nrows > kBM) nrows = kBM;
+      tile_rsrc = make_rsrc(P + r0 * ld, nrows * ld * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = w * 64 + j * 16 + (lane >> 2);
+        const int kc = (lane & 3) ^ kswz(row);
+        kc8[j] = kc * 8;
+        voff0[j] = static_cast<int>(row * ld * 2) + kc * 16;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = w * 8 + j * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ mswz(k);
+        moff0[j] = static_cast<int>(k * ld * 2) + c * 16;
+      }
+    }
+  }
+
+  // Direct load number t (0..3) of K range [k0, k0 + 32) (clipped to kend)
+  // into the stage tile `dst`; four of them fill this wave's share.
+  __device__ __forceinline__ void issue_one(uint16_t* dst, int64_t k0, int64_t kend, int t) const {
+    const int w = wave_id();
+    if constexpr (kKMajor) {
+      const int64_t klim = kend - k0;  // chunks with kc8 >= klim are K-tail
+      const int voff = kc8[t] < klim ? voff0[t] + static_cast<int>(k0 * 2) : kOOB;
+      dma16(tile_rsrc, lds_addr(dst + (w * 64 + t * 16) * kBK), voff);
+    } else {
+      int64_t nk = kend - k0;
+      if (nk > kBK) nk = kBK;
+      // From (k0, r0) to the end of row k0 + nk - 1.
+      const i32x4_t r = make_rsrc(P + k0 * ld + r0, (nk * ld - r0) * 2);
+      dma16(r, lds_addr(dst + (w * 8 + t * 2) * kBM), moff0[t]);
+    }
+  }
+
+  __device__ __forceinline__ void issue(uint16_t* dst, int64_t k0, int64_t kend) const {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) issue_one(dst, k0, kend, t);
+  }
+
+  // Fragment for MFMA rows base..base+31 (lane%32) and k-half lane/32 of the
+  // 16-wide k step kk: 8 consecutive k values.
+  __device__ __forceinline__ bf16x8_t frag(const uint16_t* src, int base, int kk) const {
+    const int lane = threadIdx.x & 63;
+    if constexpr (kKMajor) {
+      const int row = base + (lane & 31);
+      return *reinterpret_cast<const bf16x8_t*>(src + koff(row, kk * 2 + (lane >> 5)));
+    } else {
+      const int i = (lane & 15) >> 2, q = lane & 3;
+      const int k = kk * 16 + (lane >> 5) * 8 + i;
+      const int mn = base + ((lane >> 4) & 1) * 16 + q * 4;
+      uint16_t* s = const_cast<uint16_t*>(src);
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s + moff(k, mn)));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s + moff(k + 4, mn)));
+      const short __attribute__((ext_vector_type(8))) v =
+          __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+};
+
+struct Frags {
+  bf16x8_t a[4], b[4];
+};
+
+template <bool kAK, bool kBKm>
+__device__ __forceinline__ void load_frags(Frags& f, const Operand<kAK>& A, const Operand<kBKm>& B,
+                                           const uint16_t* stage, int wm, int wn, int kk) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = A.frag(stage, wm * 128 + i * 32, kk);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b[j] = B.frag(stage + kOpElems, wn * 128 + j * 32, kk);
+}
+
+// One 16-wide k step: read the next fragments `nf` from LDS and run the 16
+// MFMAs on `f`; the scheduler is told to interleave the LDS reads one per
+// MFMA so neither pipe waits on a burst of the other.
+template <bool kAK, bool kBKm>
+__device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][4], const Frags& f, Frags& nf,
+                                         const Operand<kAK>& A, const Operand<kBKm>& B,
+                                         const uint16_t* src, int wm, int wn, int kk) {
+  load_frags(nf, A, B, src, wm, wn, kk);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      // B first: each 32x32 result block is C^T, so a lane holds 4 consecutive n.
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  constexpr int kReads = (kAK ? 4 : 8) + (kBKm ? 4 : 8);  // LDS read instructions per step
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if (t < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+}
+
 template <bool kAK, bool kBKm, int kEpi>
-static hipError_t launch_mfma(const GemmDesc& d, hipStream_t s) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
+  extern __shared__ __align__(16) uint16_t smem[];
+
+  int64_t tm, tn;
+  int sp;
+  mfma::tile_of(blockIdx.x, tiles_m, tiles_n, d.k_splits, tm, tn, sp);
+  const int64_t m0 = tm * kBM, n0 = tn * kBM;
+  const int64_t kbeg = static_cast<int64_t>(sp) * k_per_split;
+  int64_t kend = kbeg + k_per_split;
+  if (kend > d.K) kend = d.K;
+  const int ksteps = kend > kbeg ? static_cast<int>((kend - kbeg + kBK - 1) / kBK) : 0;
+
+  Operand<kAK> opA;
+  Operand<kBKm> opB;
+  opA.init(static_cast<const uint16_t*>(d.A), d.lda, d.M, m0);
+  opB.init(static_cast<const uint16_t*>(d.B), d.ldb, d.N, n0);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Pipeline: stage s lives in buffer s % 4. Stages 0..2 are loaded up front;
+  // during stage s the loads of stage s + 3 go into buffer (s + 3) % 4, whose
+  // last reader (stage s - 1) finished before the previous barrier. The
+  // barrier of stage s (between its two k steps) waits for stage s + 1.
+  if (ksteps > 0) {
+    const int pre = ksteps < kStages - 1 ? ksteps : kStages - 1;
+    for (int s = 0; s < pre; ++s) {
+      uint16_t* st = smem + s * kStageElems;
+      opA.issue(st, kbeg + static_cast<int64_t>(s) * kBK, kend);
+      opB.issue(st + kOpElems, kbeg + static_cast<int64_t>(s) * kBK, kend);
+    }
+    wait_stage_loads(pre - 1);
+    block_sync();
+    Frags f0, f1;
+    load_frags(f0, opA, opB, smem, wm, wn, 0);
+    for (int s = 0; s < ksteps; ++s) {
+      const uint16_t* cur = smem + (s % kStages) * kStageElems;
+      if (s + kStages - 1 < ksteps) {
+        uint16_t* st = smem + ((s + kStages - 1) % kStages) * kStageElems;
+        const int64_t k0 = kbeg + static_cast<int64_t>(s + kStages - 1) * kBK;
+        opA.issue(st, k0, kend);
+        opB.issue(st + kOpElems, k0, kend);
+      }
+      mma_step(acc, f0, f1, opA, opB, cur, wm, wn, 1);
+      // Stage s + 1 must have landed; loads up to min(s + 3, ksteps - 1) were issued.
+      const int last_issued = (s + kStages - 1 < ksteps - 1) ? s + kStages - 1 : ksteps - 1;
+      wait_stage_loads(last_issued - (s + 1));
+      block_sync();
+      // On the last stage this reads a stale (in-bounds) buffer; never used.
+      mma_step(acc, f1, f0, opA, opB, smem + ((s + 1) % kStages) * kStageElems, wm, wn, 0);
+    }
+  }
+
+  const int l32 = lane & 31, lhi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 128 + i * 32 + l32;
+    if (m >= d.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + wn * 128 + j * 32 + q * 8 + lhi * 4;
+        if (n >= d.N) continue;
+        float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
+                      acc[i][j][q * 4 + 3]};
+        const bool full = n + 3 < d.N;
+        if constexpr (kEpi == kEpiLogits) {
+          if (d.bias != nullptr) {
+            const uint16_t* b = static_cast<const uint16_t*>(d.bias);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < d.N) v[e] += bf16_to_f32(b[n + e]);
+          }
+          uint16_t* c = static_cast<uint16_t*>(d.C) + m * d.ldc + n;
+          if (full) {
+            *reinterpret_cast<uint2*>(c) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < d.N) c[e] = f32_to_bf16(v[e]);
+          }
+        } else {
+          float* c = static_cast<float*>(d.C) + static_cast<int64_t>(sp) * d.split_stride +
+                     m * d.ldc + n;
+          if (full) {
+            float4 o = make_float4(v[0], v[1], v[2], v[3]);
+            if constexpr (kEpi == kEpiAccumF32) {
+              const float4 old = *reinterpret_cast<const float4*>(c);
+              o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+            }
+            *reinterpret_cast<float4*>(c) = o;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < d.N) c[e] = (kEpi == kEpiAccumF32) ? c[e] + v[e] : v[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace mfma2
+
+template <bool kAK, bool kBKm, int kEpi>
+static hipError_t launch_mfma_v1(const GemmDesc& d, hipStream_t s) {
   using namespace mfma;
   const int64_t tiles_m = (d.M + kBM - 1) / kBM, tiles_n = (d.N + kBN - 1) / kBN;
   const int splits = d.k_splits > 1 ? d.k_splits : 1;
@@ -290,6 +617,40 @@ static hipError_t launch_mfma(const GemmDesc& d, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), lds, s, dd, tiles_m,
                      tiles_n, k_per);
   return hipGetLastError();
+}
+
+template <bool kAK, bool kBKm, int kEpi>
+static hipError_t launch_mfma_v2(const GemmDesc& d, hipStream_t s) {
+  using namespace mfma2;
+  const int64_t tiles_m = (d.M + kBM - 1) / kBM, tiles_n = (d.N + kBM - 1) / kBM;
+  const int splits = d.k_splits > 1 ? d.k_splits : 1;
+  int64_t k_per = (d.K + splits - 1) / splits;
+  k_per = (k_per + kBK - 1) / kBK * kBK;
+  const int64_t blocks = tiles_m * tiles_n * splits;
+  const size_t lds = static_cast<size_t>(kStages) * kStageElems * sizeof(uint16_t);  // 128 KiB
+  auto kern = k_gemm2<kAK, kBKm, kEpi>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  GemmDesc dd = d;
+  dd.k_splits = splits;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), lds, s, dd, tiles_m,
+                     tiles_n, k_per);
+  return hipGetLastError();
+}
+
+template <bool kAK, bool kBKm, int kEpi>
+static hipError_t launch_mfma(const GemmDesc& d, hipStream_t s) {
+  static const int variant = [] {
+    const char* e = getenv("LCE03_GEMM_VARIANT");
+    return e ? atoi(e) : 2;
+  }();
+  return variant == 1 ? launch_mfma_v1<kAK, kBKm, kEpi>(d, s) : launch_mfma_v2<kAK, kBKm, kEpi>(d, s);
 }
 
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
