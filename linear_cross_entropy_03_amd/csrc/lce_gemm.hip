@@ -283,6 +283,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmDesc d, int64_t tiles_
 // 16-wide k steps, so the next stage's first fragments are read from LDS while
 // the current stage's second k step is on the MFMA pipe.
 //
+// The 256x256 tile is split over kWM x kWN waves. With 2 x 4 waves (two per
+// SIMD, 128x64 each) one wave keeps the MFMA pipe busy while the other is
+// held at a DMA issue (the texture unit accepts about 64 bytes per clock, so
+// a stage's 32 KiB of DMA keeps it busy for ~512 cycles); with 2 x 2 waves
+// (128x128 each) there is no such cover.
+//
 // Operands that are k-contiguous in HBM are stored [row][k] and read with
 // ds_read_b128; m/n-contiguous operands are stored [k][mn] as loaded and read
 // with ds_read_b64_tr_b16, which hands each lane four consecutive k of one
@@ -290,10 +296,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmDesc d, int64_t tiles_
 // reads are bank-conflict free.
 namespace mfma2 {
 
-constexpr int kBM = 256, kBK = 32, kStages = 4, kThreads = 256;
+constexpr int kBM = 256, kBK = 32, kStages = 4;
+constexpr int kWM = 2;                        // waves along M (each 128 rows)
 constexpr int kOpElems = kBM * kBK;           // one operand, one stage: 8192 bf16
 constexpr int kStageElems = 2 * kOpElems;     // A then B
-constexpr int kLoadsPerStage = 8;             // DMA instructions per wave per stage
 constexpr int kOOB = 0x7FFFFFF0;              // buffer offset that reads as zero
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -352,10 +358,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
+// Wait until at most `ahead` stages of loads (kPer instructions each) are in flight.
+template <int kPer>
 __device__ __forceinline__ void wait_stage_loads(int ahead) {
-  if (ahead >= 3) wait_vmcnt<3 * kLoadsPerStage>();
-  else if (ahead == 2) wait_vmcnt<2 * kLoadsPerStage>();
-  else if (ahead == 1) wait_vmcnt<kLoadsPerStage>();
+  if (ahead >= 3) wait_vmcnt<3 * kPer>();
+  else if (ahead == 2) wait_vmcnt<2 * kPer>();
+  else if (ahead == 1) wait_vmcnt<kPer>();
   else wait_vmcnt<0>();
 }
 __device__ __forceinline__ void block_sync() {
@@ -365,16 +373,26 @@ __device__ __forceinline__ void block_sync() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One operand of the GEMM: issues a stage's direct loads and reads MFMA
-// fragments. `rows` is the extent along m (A) or n (B); ld its row stride.
-template <bool kKMajor>
+// One operand of the GEMM: issues this wave's share of a stage's direct loads
+// and reads MFMA fragments. `rows` is the extent along m (A) or n (B); ld
+// its row stride. kWaves waves share each stage's loads.
+template <bool kKMajor, int kWaves>
 struct Operand {
+  // k-major: 16 rows per instruction; mn-major: 2 k-rows per instruction.
+  static constexpr int kInstr = kKMajor ? kBM / 16 / kWaves : kBK / 2 / kWaves;
   const uint16_t* P;
-  int64_t ld, rows, r0;   // r0: first m/n row of this tile
-  i32x4_t tile_rsrc;      // k-major: the tile's rows
-  int voff0[4];           // k-major: per-lane byte offset of (row, chunk) at k = 0
-  int kc8[4];             // k-major: per-lane chunk start (elements)
-  int moff0[4];           // mn-major: per-lane byte offset inside a stage
+  int64_t ld, rows, r0;     // r0: first m/n row of this tile
+  i32x4_t tile_rsrc;        // k-major: the tile's rows
+  int voff0[kInstr];        // k-major: per-lane byte offset of (row, chunk) at k = 0
+  int kc8[kInstr];          // k-major: per-lane chunk start (elements)
+  int moff0[kInstr];        // mn-major: per-lane byte offset inside a stage
+
+  __device__ __forceinline__ int first_row(int w, int t) const {   // k-major LDS row
+    return (w * kInstr + t) * 16;
+  }
+  __device__ __forceinline__ int first_k(int w, int t) const {     // mn-major LDS k-row
+    return (w * kInstr + t) * 2;
+  }
 
   __device__ __forceinline__ void init(const uint16_t* P_, int64_t ld_, int64_t rows_, int64_t r0_) {
     P = P_; ld = ld_; rows = rows_; r0 = r0_;
@@ -384,42 +402,41 @@ struct Operand {
       if (nrows > kBM) nrows = kBM;
       tile_rsrc = make_rsrc(P + r0 * ld, nrows * ld * 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = w * 64 + j * 16 + (lane >> 2);
+      for (int t = 0; t < kInstr; ++t) {
+        const int row = first_row(w, t) + (lane >> 2);
         const int kc = (lane & 3) ^ kswz(row);
-        kc8[j] = kc * 8;
-        voff0[j] = static_cast<int>(row * ld * 2) + kc * 16;
+        kc8[t] = kc * 8;
+        voff0[t] = static_cast<int>(row * ld * 2) + kc * 16;
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = w * 8 + j * 2 + (lane >> 5);
+      for (int t = 0; t < kInstr; ++t) {
+        const int k = first_k(w, t) + (lane >> 5);
         const int c = (lane & 31) ^ mswz(k);
-        moff0[j] = static_cast<int>(k * ld * 2) + c * 16;
+        moff0[t] = static_cast<int>(k * ld * 2) + c * 16;
       }
     }
   }
 
-  // Direct load number t (0..3) of K range [k0, k0 + 32) (clipped to kend)
-  // into the stage tile `dst`; four of them fill this wave's share.
-  __device__ __forceinline__ void issue_one(uint16_t* dst, int64_t k0, int64_t kend, int t) const {
+  // This wave's direct loads of K range [k0, k0 + 32) (clipped to kend) into
+  // the stage tile `dst`.
+  __device__ __forceinline__ void issue(uint16_t* dst, int64_t k0, int64_t kend) const {
     const int w = wave_id();
     if constexpr (kKMajor) {
       const int64_t klim = kend - k0;  // chunks with kc8 >= klim are K-tail
-      const int voff = kc8[t] < klim ? voff0[t] + static_cast<int>(k0 * 2) : kOOB;
-      dma16(tile_rsrc, lds_addr(dst + (w * 64 + t * 16) * kBK), voff);
+#pragma unroll
+      for (int t = 0; t < kInstr; ++t) {
+        const int voff = kc8[t] < klim ? voff0[t] + static_cast<int>(k0 * 2) : kOOB;
+        dma16(tile_rsrc, lds_addr(dst + first_row(w, t) * kBK), voff);
+      }
     } else {
       int64_t nk = kend - k0;
       if (nk > kBK) nk = kBK;
       // From (k0, r0) to the end of row k0 + nk - 1.
       const i32x4_t r = make_rsrc(P + k0 * ld + r0, (nk * ld - r0) * 2);
-      dma16(r, lds_addr(dst + (w * 8 + t * 2) * kBM), moff0[t]);
-    }
-  }
-
-  __device__ __forceinline__ void issue(uint16_t* dst, int64_t k0, int64_t kend) const {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) issue_one(dst, k0, kend, t);
+      for (int t = 0; t < kInstr; ++t) dma16(r, lds_addr(dst + first_k(w, t) * kBM), moff0[t]);
+    }
   }
 
   // Fragment for MFMA rows base..base+31 (lane%32) and k-half lane/32 of the
@@ -443,44 +460,53 @@ struct Operand {
   }
 };
 
+// A wave's fragments for one 16-wide k step: 4 blocks of 32 rows of A and
+// kFJ blocks of 32 columns of B.
+template <int kFJ>
 struct Frags {
-  bf16x8_t a[4], b[4];
+  bf16x8_t a[4], b[kFJ];
 };
 
-template <bool kAK, bool kBKm>
-__device__ __forceinline__ void load_frags(Frags& f, const Operand<kAK>& A, const Operand<kBKm>& B,
-                                           const uint16_t* stage, int wm, int wn, int kk) {
+template <int kFJ, bool kAK, bool kBKm, int kW>
+__device__ __forceinline__ void load_frags(Frags<kFJ>& f, const Operand<kAK, kW>& A,
+                                           const Operand<kBKm, kW>& B, const uint16_t* stage,
+                                           int row0, int col0, int kk) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = A.frag(stage, wm * 128 + i * 32, kk);
+  for (int i = 0; i < 4; ++i) f.a[i] = A.frag(stage, row0 + i * 32, kk);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = B.frag(stage + kOpElems, wn * 128 + j * 32, kk);
+  for (int j = 0; j < kFJ; ++j) f.b[j] = B.frag(stage + kOpElems, col0 + j * 32, kk);
 }
 
-// One 16-wide k step: read the next fragments `nf` from LDS and run the 16
-// MFMAs on `f`; the scheduler is told to interleave the LDS reads one per
-// MFMA so neither pipe waits on a burst of the other.
-template <bool kAK, bool kBKm>
-__device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][4], const Frags& f, Frags& nf,
-                                         const Operand<kAK>& A, const Operand<kBKm>& B,
-                                         const uint16_t* src, int wm, int wn, int kk) {
-  load_frags(nf, A, B, src, wm, wn, kk);
+// One 16-wide k step: read the next fragments `nf` from LDS and run the
+// 4 x kFJ MFMAs on `f`; the scheduler is told to interleave the LDS reads one
+// per MFMA so neither pipe waits on a burst of the other.
+template <int kFJ, bool kAK, bool kBKm, int kW>
+__device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][kFJ], const Frags<kFJ>& f,
+                                         Frags<kFJ>& nf, const Operand<kAK, kW>& A,
+                                         const Operand<kBKm, kW>& B, const uint16_t* src,
+                                         int row0, int col0, int kk) {
+  load_frags(nf, A, B, src, row0, col0, kk);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kFJ; ++j)
       // B first: each 32x32 result block is C^T, so a lane holds 4 consecutive n.
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-  constexpr int kReads = (kAK ? 4 : 8) + (kBKm ? 4 : 8);  // LDS read instructions per step
+  constexpr int kReads = (kAK ? 4 : 8) + (kBKm ? kFJ : 2 * kFJ);  // LDS reads per step
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
+  for (int t = 0; t < 4 * kFJ; ++t) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     if (t < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
+  if constexpr (kReads > 4 * kFJ) __builtin_amdgcn_sched_group_barrier(0x100, kReads - 4 * kFJ, 0);
 }
 
-template <bool kAK, bool kBKm, int kEpi>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <bool kAK, bool kBKm, int kEpi, int kWN>
+__global__ __launch_bounds__(64 * kWM * kWN) __attribute__((amdgpu_waves_per_eu(kWN / 2, kWN / 2)))
 void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
+  constexpr int kWaves = kWM * kWN;
+  constexpr int kFJ = kBM / kWN / 32;  // 32-column MFMA blocks per wave
+  constexpr int kPer = Operand<kAK, kWaves>::kInstr + Operand<kBKm, kWaves>::kInstr;
   extern __shared__ __align__(16) uint16_t smem[];
 
   int64_t tm, tn;
@@ -492,20 +518,21 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
   if (kend > d.K) kend = d.K;
   const int ksteps = kend > kbeg ? static_cast<int>((kend - kbeg + kBK - 1) / kBK) : 0;
 
-  Operand<kAK> opA;
-  Operand<kBKm> opB;
+  Operand<kAK, kWaves> opA;
+  Operand<kBKm, kWaves> opB;
   opA.init(static_cast<const uint16_t*>(d.A), d.lda, d.M, m0);
   opB.init(static_cast<const uint16_t*>(d.B), d.ldb, d.N, n0);
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int row0 = wm * (kBM / kWM), col0 = wn * (kBM / kWN);
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][kFJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kFJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -520,10 +547,10 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
       opA.issue(st, kbeg + static_cast<int64_t>(s) * kBK, kend);
       opB.issue(st + kOpElems, kbeg + static_cast<int64_t>(s) * kBK, kend);
     }
-    wait_stage_loads(pre - 1);
+    wait_stage_loads<kPer>(pre - 1);
     block_sync();
-    Frags f0, f1;
-    load_frags(f0, opA, opB, smem, wm, wn, 0);
+    Frags<kFJ> f0, f1;
+    load_frags(f0, opA, opB, smem, row0, col0, 0);
     for (int s = 0; s < ksteps; ++s) {
       const uint16_t* cur = smem + (s % kStages) * kStageElems;
       if (s + kStages - 1 < ksteps) {
@@ -532,26 +559,26 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
         opA.issue(st, k0, kend);
         opB.issue(st + kOpElems, k0, kend);
       }
-      mma_step(acc, f0, f1, opA, opB, cur, wm, wn, 1);
+      mma_step(acc, f0, f1, opA, opB, cur, row0, col0, 1);
       // Stage s + 1 must have landed; loads up to min(s + 3, ksteps - 1) were issued.
       const int last_issued = (s + kStages - 1 < ksteps - 1) ? s + kStages - 1 : ksteps - 1;
-      wait_stage_loads(last_issued - (s + 1));
+      wait_stage_loads<kPer>(last_issued - (s + 1));
       block_sync();
       // On the last stage this reads a stale (in-bounds) buffer; never used.
-      mma_step(acc, f1, f0, opA, opB, smem + ((s + 1) % kStages) * kStageElems, wm, wn, 0);
+      mma_step(acc, f1, f0, opA, opB, smem + ((s + 1) % kStages) * kStageElems, row0, col0, 0);
     }
   }
 
   const int l32 = lane & 31, lhi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + wm * 128 + i * 32 + l32;
+    const int64_t m = m0 + row0 + i * 32 + l32;
     if (m >= d.M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kFJ; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * 128 + j * 32 + q * 8 + lhi * 4;
+        const int64_t n = n0 + col0 + j * 32 + q * 8 + lhi * 4;
         if (n >= d.N) continue;
         float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
                       acc[i][j][q * 4 + 3]};
@@ -619,7 +646,7 @@ static hipError_t launch_mfma_v1(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool kAK, bool kBKm, int kEpi>
+template <bool kAK, bool kBKm, int kEpi, int kWN>
 static hipError_t launch_mfma_v2(const GemmDesc& d, hipStream_t s) {
   using namespace mfma2;
   const int64_t tiles_m = (d.M + kBM - 1) / kBM, tiles_n = (d.N + kBM - 1) / kBM;
@@ -628,7 +655,7 @@ static hipError_t launch_mfma_v2(const GemmDesc& d, hipStream_t s) {
   k_per = (k_per + kBK - 1) / kBK * kBK;
   const int64_t blocks = tiles_m * tiles_n * splits;
   const size_t lds = static_cast<size_t>(kStages) * kStageElems * sizeof(uint16_t);  // 128 KiB
-  auto kern = k_gemm2<kAK, kBKm, kEpi>;
+  auto kern = k_gemm2<kAK, kBKm, kEpi, kWN>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -639,8 +666,8 @@ static hipError_t launch_mfma_v2(const GemmDesc& d, hipStream_t s) {
   }
   GemmDesc dd = d;
   dd.k_splits = splits;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), lds, s, dd, tiles_m,
-                     tiles_n, k_per);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * kWM * kWN), lds, s, dd,
+                     tiles_m, tiles_n, k_per);
   return hipGetLastError();
 }
 
@@ -648,9 +675,11 @@ template <bool kAK, bool kBKm, int kEpi>
 static hipError_t launch_mfma(const GemmDesc& d, hipStream_t s) {
   static const int variant = [] {
     const char* e = getenv("LCE03_GEMM_VARIANT");
-    return e ? atoi(e) : 2;
+    return e ? atoi(e) : 3;
   }();
-  return variant == 1 ? launch_mfma_v1<kAK, kBKm, kEpi>(d, s) : launch_mfma_v2<kAK, kBKm, kEpi>(d, s);
+  if (variant == 1) return launch_mfma_v1<kAK, kBKm, kEpi>(d, s);
+  if (variant == 2) return launch_mfma_v2<kAK, kBKm, kEpi, 2>(d, s);
+  return launch_mfma_v2<kAK, kBKm, kEpi, 4>(d, s);
 }
 
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
