@@ -19,6 +19,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -36,6 +38,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-ce", action="store_true", help="skip the standalone CE measurement")
+    ap.add_argument("--profile-step", action="store_true",
+                    help="for rocprofv3 counter runs: a 1 GiB device copy (counter calibration), "
+                         "then one warmup and one timed FLCE step; prints nothing else")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of --profile-step (FETCH_SIZE, "
+                         "WRITE_SIZE) into profiles/traffic_<workload>.json and exit")
     return ap.parse_args()
 
 
@@ -59,7 +68,6 @@ def gpu_inputs(torch, inp):
 
 def cpu_baseline(inp, cfg, target_s):
     """Time the FP64 oracle on the first R rows of the same inputs (full W)."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import flce_oracle as O
@@ -96,13 +104,143 @@ def cpu_baseline(inp, cfg, target_s):
     }
 
 
+KERNEL_KINDS = {  # kernel-name fragment -> kind reported by the timing hooks
+    "k_gemm2<true, true, 0": "logits_gemm",
+    "k_gemm2<true, false, 1": "grad_x_gemm",
+    "k_gemm2<false, false, 1": "grad_w_gemm",
+    "k_gemm2<false, false, 2": "grad_w_gemm",
+    "k_row_ce": "row_ce",
+}
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources; traffic figures are valid only for this hash."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_cross_entropy_03_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def summarise_traffic(workload, fetch_dir, write_dir):
+    """Per-launch HBM bytes per kernel class from FETCH_SIZE / WRITE_SIZE runs
+    (KiB per dispatch), each scaled by the same counter's reading for the
+    1 GiB device copy that --profile-step runs first."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {"workload": workload, "source_hash": kernel_source_hash(), "copy_bytes": 1 << 30,
+           "kernels": {}}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = per_kernel(d, counter)
+        copy = [v for k, v in vals.items() if "copyBuffer" in k or "copy_kernel" in k]
+        if not copy:
+            raise SystemExit(f"no copy kernel found in {d}")
+        copy_kib = float(np.median(copy[0]))
+        factor = (1 << 30) / (copy_kib * 1024.0)
+        out[f"{counter}_copy_kib"] = copy_kib
+        out[f"{counter}_factor"] = factor
+        for name, v in vals.items():
+            kind = next((k2 for frag, k2 in KERNEL_KINDS.items() if frag in name), None)
+            if kind is None:
+                continue
+            e = out["kernels"].setdefault(kind, {})
+            # second step's dispatches (the first step is warmup)
+            e[counter.lower() + "_bytes"] = float(np.mean(v[len(v) // 2:])) * 1024.0 * factor
+    for e in out["kernels"].values():
+        e["traffic_bytes"] = e.get("fetch_size_bytes", 0.0) + e.get("write_size_bytes", 0.0)
+    with open(traffic_path(workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def load_traffic(workload):
+    try:
+        with open(traffic_path(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t if t.get("source_hash") == kernel_source_hash() else None
+
+
+def bench_ce(torch, B, reps=40):
+    """Standalone CE over bf16 logits [1024, 32768] (one vocabulary shard,
+    std 2, 5% ignored), gradient to a separate buffer, mean reduction. Eight
+    buffer sets (1 GiB) are rotated so the 256 MB Infinity Cache cannot hold
+    the working set. Algorithmic bytes per call: read logits + write grad
+    (2 x N x V x 2) + targets 4N + per-row losses 4N."""
+    from linear_cross_entropy_03_amd import synth
+    N, V = 1024, 32768
+    inp = synth.make_ce_inputs(N, V, "bf16", std=2.0, ignore_frac=0.05)
+    base = torch.from_numpy(inp["logits"].view(np.int16)).view(torch.bfloat16).cuda()
+    y = torch.from_numpy(inp["targets"]).cuda()
+    sets = [(base.clone(), torch.empty_like(base)) for _ in range(8)]
+    loss = torch.empty(1, device="cuda")
+    ws = torch.empty(B.ce_workspace_bytes(N, V), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(8):
+        B.ce_forward_backward(sets[i][0], y, grad_logits=sets[i][1], loss=loss, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    B.flce_timing_reset()
+    B.flce_timing_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for r in range(reps):
+        lg, g = sets[r % 8]
+        B.ce_forward_backward(lg, y, grad_logits=g, loss=loss, workspace=ws, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    B.flce_timing_enable(False)
+    call_us = a.elapsed_time(b) / reps * 1e3
+    k_ms, k_n = B.flce_timing_read("row_ce")
+    B.flce_timing_reset()
+    algo = 2.0 * N * V * 2 + 8.0 * N
+    kern_us = k_ms / k_n * 1e3
+    # shard statistics over the same shard (read-only pass)
+    m = torch.empty(N, device="cuda"); s_ = torch.empty(N, device="cuda"); t = torch.empty(N, device="cuda")
+    a.record(stream)
+    for r in range(reps):
+        B.ce_shard_stats(sets[r % 8][0], y, 0, 2 * V, out=(m, s_, t), workspace=ws, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    st_us = a.elapsed_time(b) / reps * 1e3
+    st_algo = 1.0 * N * V * 2 + 16.0 * N
+    return {
+        "workload": "ce_shard_bf16 (logits [1024, 32768] bf16, mean, grad out of place)",
+        "us_per_call": call_us, "row_ce_kernel_us": kern_us,
+        "algorithmic_bytes": algo,
+        "achieved_GBps_call": algo / (call_us * 1e-6) / 1e9,
+        "achieved_GBps_kernel": algo / (kern_us * 1e-6) / 1e9,
+        "frac_hbm_kernel": algo / (kern_us * 1e-6) / PEAK_HBM_BYTES,
+        "shard_stats_us_per_call": st_us,
+        "shard_stats_GBps": st_algo / (st_us * 1e-6) / 1e9,
+    }
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        summarise_traffic(args.workload, *args.traffic_from)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from linear_cross_entropy_03_amd import binding as B
@@ -114,6 +252,11 @@ def main():
     N, H, V = cfg["N"], cfg["H"], cfg["V"]
     dt = B.BF16 if cfg["dtype"] == "bf16" else B.F32
     torch.cuda.set_device(0)
+    if args.profile_step:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        torch.empty_like(a).copy_(a)  # 1 GiB read + 1 GiB write: counter calibration
+        torch.cuda.synchronize()
+        del a
     log(f"generating {args.workload}: N={N} H={H} V={V} {cfg['dtype']}")
     t0 = time.time()
     inp = synth.make_workload(args.workload)
@@ -138,6 +281,12 @@ def main():
                                 chunk_rows=args.chunk_rows, stream=stream)
 
     log(f"plan: chunk_rows={chunk} dx_splits={splits} workspace={ws_bytes / 2**30:.2f} GiB; warmup")
+    if args.profile_step:
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        log("profile step done")
+        return
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -186,8 +335,15 @@ def main():
     dom_kind = max((k for k in kernels if "achieved" in kernels[k]),
                    key=lambda k: kernels[k]["ms_per_launch"] * kernels[k]["launches"])
     dom = kernels[dom_kind]
+    traffic = load_traffic(args.workload)
+    t_dom = None
+    if traffic is not None:
+        for kind, entry in kernels.items():
+            if kind in traffic["kernels"]:
+                entry["traffic_bytes_per_launch"] = traffic["kernels"][kind]["traffic_bytes"]
+        t_dom = traffic["kernels"].get(dom_kind, {}).get("traffic_bytes")
     roofline = {"kernel": dom_kind, "bound": dom["bound"], "achieved": dom["achieved"],
-                "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"], "traffic": None,
+                "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"], "traffic": t_dom,
                 "algorithmic_per_launch": dom["algorithmic_per_launch"]}
 
     tokens_per_s = N / (ms * 1e-3)
@@ -220,9 +376,15 @@ def main():
         "kernels": kernels,
         "loss": float(loss.item()),
     }
+    if not args.no_ce:
+        log("standalone CE")
+        del ws
+        result["ce"] = bench_ce(torch, B)
+    else:
+        del ws
     if not args.no_cpu_baseline:
         log("timing the FP64 oracle on a CPU sample")
-        del ws, gX, gW
+        del gX, gW
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None

@@ -33,14 +33,18 @@ def to_dev(arr, dtype):
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
-def to_host(t):
+def to_host(t, f64=True):
+    """Host copy of a device tensor (bf16 -> exact float values); float64
+    unless f64 is False (then float32, for very large gradients)."""
     import torch
     if t is None:
         return None
     if t.dtype == torch.bfloat16:
         bits = t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
-        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    return t.detach().cpu().numpy().astype(np.float64)
+        a = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    else:
+        a = t.detach().cpu().numpy()
+    return a.astype(np.float64) if f64 else a
 
 
 def check_scalar(gpu, ref, rtol, what="loss"):

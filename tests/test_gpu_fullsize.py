@@ -1,0 +1,136 @@
+"""GPU parity at the full benchmark shapes, in the launch configuration the
+benchmark times (planner-chosen chunking), on outputs the FP64 oracle can
+compute one by one, plus properties that hold at any size.
+
+Shapes: Llama-3.2-1B head (N 8192, H 2048, V 128256, mean), Llama-3-8B head
+(N 32768, H 4096, V 128256, Zipf targets, mean), 256k vocabulary with bias
+(N 32768, H 4096, V 256000, sum).
+
+Per workload:
+  * sampled token rows: per-row loss and grad_X rows against the oracle
+    (bf16 bar: 2e-3 of the largest sampled loss, 1e-2 of the largest sampled
+    |grad_X|), ignored rows exactly zero;
+  * the reduced loss equals the float64 reduction of the per-row losses of a
+    reduction="none" call on the same inputs;
+  * sum over v of grad_W[v, :] and of grad_bias vanish up to bf16 dlogits
+    rounding (at most 2**-8 per valid row);
+  * sampled vocabulary rows of grad_W (and grad_bias): the most frequent
+    target, a target-free row and random rows, against the oracle (this needs
+    the oracle's float64 logsumexp of every token row).
+"""
+
+import numpy as np
+import pytest
+
+from gpu_util import TOL, check_max_rel, check_scalar, say, to_dev, to_host, torch_or_skip
+from linear_cross_entropy_03_amd import synth
+from oracle import flce_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+WORKLOADS = ["llama1b_head_bf16", "llama8b_head_bf16", "vocab256k_bias_bf16"]
+_CACHE = {}
+
+
+@pytest.fixture(scope="module")
+def B():
+    torch_or_skip()
+    from linear_cross_entropy_03_amd import binding
+    binding.lib()
+    yield binding
+    _CACHE.clear()
+
+
+@pytest.fixture(scope="module", params=WORKLOADS)
+def workload(request, B):
+    """Module-scoped so pytest runs every check of one shape back to back."""
+    return _results(B, request.param)
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def _results(B, name):
+    """Inputs and GPU outputs of one workload (computed once per module)."""
+    if _CACHE.get("name") == name:
+        return _CACHE
+    import torch
+    _CACHE.clear()
+    cfg = synth.WORKLOADS[name]
+    say(name, "generating inputs")
+    inp = synth.make_workload(name)
+    X, W, b = (to_dev(inp[k], "bf16") for k in ("X", "W", "bias"))
+    y = to_dev(inp["targets"], "i32")
+    say(name, "flce", cfg["reduction"], "launch configuration", B.flce_plan(cfg["N"], cfg["H"], cfg["V"], B.BF16))
+    loss, gX, gW, gb = B.flce_forward_backward(X, W, y, bias=b, reduction=cfg["reduction"])
+    torch.cuda.synchronize()
+    out = {"loss": to_host(loss), "gX": to_host(gX, f64=False), "gW": to_host(gW, f64=False),
+           "gb": to_host(gb)}
+    del gX, gW, gb
+    say(name, "flce none (loss only)")
+    rows, _, _, _ = B.flce_forward_backward(X, W, y, bias=b, reduction="none", grad_X=False,
+                                            grad_W=False, grad_bias=False)
+    torch.cuda.synchronize()
+    out["rows"] = to_host(rows)
+    del X, W, b, y
+    torch.cuda.empty_cache()
+    _CACHE.update(name=name, cfg=cfg, inp=inp, **out)
+    return _CACHE
+
+
+@pytest.mark.timeout(300)
+def test_fullsize_rows_and_properties(workload):
+    r = workload
+    cfg, inp, name = r["cfg"], r["inp"], r["name"]
+    y = inp["targets"]
+    valid = y != -100
+    n_valid = int(valid.sum())
+    red = cfg["reduction"]
+
+    # Reduced loss == float64 reduction of the per-row losses.
+    total = float(np.sum(r["rows"]))
+    expect = total / n_valid if red == "mean" else total
+    check_scalar(r["loss"], expect, 1e-6, "loss vs its rows")
+    assert np.all(r["rows"][~valid] == 0.0)
+    assert np.all(r["gX"][~valid] == 0.0)
+
+    # Sampled token rows against the oracle.
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([
+        rng.choice(cfg["N"], 24, replace=False),
+        np.flatnonzero(~valid)[:2],
+        np.flatnonzero(y == np.bincount(y[valid]).argmax())[:2],
+        [0, cfg["N"] - 1]]))
+    say(name, "oracle rows", len(rows))
+    lr, gx = O.flce_rows(_f64(inp["X_f32"]), _f64(inp["W_f32"]), y, rows, bias=_f64(inp["bias_f32"]),
+                         reduction=red)
+    t = TOL["bf16"]
+    check_max_rel(r["rows"][rows], lr, t["loss"], "sampled loss rows")
+    check_max_rel(r["gX"][rows].astype(np.float64), gx, t["grad"], "sampled grad_X rows")
+
+    # Row sums of dlogits vanish: sum_v grad_W[v, :] ~ 0, sum grad_bias ~ 0.
+    s = 1.0 / n_valid if red == "mean" else 1.0
+    xmax = float(np.abs(inp["X_f32"]).max())
+    assert np.abs(r["gW"].sum(axis=0, dtype=np.float64)).max() <= n_valid * 2.0 ** -8 * s * xmax
+    if r["gb"] is not None:
+        assert abs(float(r["gb"].sum())) <= n_valid * 2.0 ** -8 * s
+
+
+@pytest.mark.timeout(300)
+def test_fullsize_grad_w_rows(workload):
+    r = workload
+    cfg, inp, name = r["cfg"], r["inp"], r["name"]
+    y = inp["targets"]
+    valid = y != -100
+    counts = np.bincount(y[valid], minlength=cfg["V"])
+    rng = np.random.default_rng(7)
+    vrows = np.unique(np.concatenate([[int(counts.argmax())], [int(np.flatnonzero(counts == 0)[0])],
+                                      rng.choice(cfg["V"], 6, replace=False)]))
+    say(name, "oracle grad_W rows (float64 logsumexp over every token row)")
+    gw, gb = O.flce_grad_w_rows(_f64(inp["X_f32"]), _f64(inp["W_f32"]), y, vrows,
+                                bias=_f64(inp["bias_f32"]), reduction=cfg["reduction"])
+    t = TOL["bf16"]
+    check_max_rel(r["gW"][vrows].astype(np.float64), gw, t["grad"], "sampled grad_W rows")
+    if r["gb"] is not None:
+        check_max_rel(r["gb"][vrows], gb, t["grad"], "sampled grad_bias entries")
