@@ -51,18 +51,19 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
 // 16 KiB). Each stage is filled by buffer_load_dwordx4 ... lds: the data never
 // passes through registers, and rows past the operand's end and K-tails read
 // as zero through the buffer descriptor's range check instead of branches.
-// Loads run three stages ahead of the MFMAs. The LDS-DMA loads are issued
-// from inline assembly and their completion is tracked here with explicit
-// vmcnt waits (the compiler would otherwise wait for every load in flight
-// before each LDS read). One barrier per stage sits between the stage's two
-// 16-wide k steps, so the next stage's first fragments are read from LDS while
-// the current stage's second k step is on the MFMA pipe.
+// Loads run three stages ahead of the MFMAs. The four stage buffers are four
+// LDS objects and the main loop is unrolled by four, so the compiler sees
+// which buffer each direct load writes and each LDS read reads: it then waits
+// only for the loads a read depends on, and the loads can be scheduled
+// between the MFMAs like any other instruction (one direct load per four
+// MFMAs; the texture unit takes about 16 clocks per 1 KiB instruction, so a
+// burst of them would hold the issuing wave). One barrier per stage sits
+// between the stage's two 16-wide k steps, so the next stage's first
+// fragments are read from LDS while the current stage's second k step is on
+// the MFMA pipe.
 //
-// The 256x256 tile is split over kWM x kWN waves. With 2 x 4 waves (two per
-// SIMD, 128x64 each) one wave keeps the MFMA pipe busy while the other is
-// held at a DMA issue (the texture unit accepts about 64 bytes per clock, so
-// a stage's 32 KiB of DMA keeps it busy for ~512 cycles); with 2 x 2 waves
-// (128x128 each) there is no such cover.
+// The 256x256 tile is split over kWM x kWN waves: 2 x 4 waves, two per SIMD,
+// 128x64 each, so one wave's MFMAs cover the other's waits.
 //
 // Operands that are k-contiguous in HBM are stored [row][k] and read with
 // ds_read_b128; m/n-contiguous operands are stored [k][mn] as loaded and read
@@ -71,14 +72,13 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
 // reads are bank-conflict free.
 namespace mfma2 {
 
-constexpr int kBM = 256, kBK = 32, kStages = 4;
+constexpr int kBM = 256, kBK = 32;
 constexpr int kWM = 2;                        // waves along M (each 128 rows)
 constexpr int kOpElems = kBM * kBK;           // one operand, one stage: 8192 bf16
 constexpr int kStageElems = 2 * kOpElems;     // A then B
 constexpr int kOOB = 0x7FFFFFF0;              // buffer offset that reads as zero
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4_t lds_v4;
 
@@ -100,29 +100,23 @@ __device__ __forceinline__ int moff(int k, int mn) {
   return k * kBM + (((mn >> 3) ^ mswz(k)) << 3) + (mn & 7);
 }
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
 // Raw buffer descriptor over [base, base + bytes) in scalar registers; reads
 // past the end return zero.
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int64_t bytes) {
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : static_cast<int>(bytes));
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a));
-  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)) & 0xFFFF;  // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane(n);
-  r[3] = 0x00020000;
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(p)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
 // 16 bytes per lane from buffer offset voff to LDS dst + 16 * lane.
-__device__ __forceinline__ void dma16(const i32x4_t& r, uint32_t dst, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(dst), "v"(voff), "s"(r)
-               : "memory");
+__device__ __forceinline__ void dma16(rsrc_t r, uint16_t* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
 }
 
 template <int kN>
@@ -133,19 +127,27 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
-// Wait until at most `ahead` stages of loads (kPer instructions each) are in flight.
-template <int kPer>
-__device__ __forceinline__ void wait_stage_loads(int ahead) {
-  if (ahead >= 3) wait_vmcnt<3 * kPer>();
-  else if (ahead == 2) wait_vmcnt<2 * kPer>();
-  else if (ahead == 1) wait_vmcnt<kPer>();
-  else wait_vmcnt<0>();
-}
 __device__ __forceinline__ void block_sync() {
   __builtin_amdgcn_sched_barrier(0);
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// The four stage buffers are separate LDS objects: the compiler can then tell
+// the direct loads into one buffer from LDS reads of another, and waits only
+// for the loads that a read depends on.
+__shared__ __align__(16) uint16_t g_stage0[kStageElems];
+__shared__ __align__(16) uint16_t g_stage1[kStageElems];
+__shared__ __align__(16) uint16_t g_stage2[kStageElems];
+__shared__ __align__(16) uint16_t g_stage3[kStageElems];
+
+template <int kB>
+__device__ __forceinline__ uint16_t* stage_buf() {
+  if constexpr (kB == 0) return g_stage0;
+  else if constexpr (kB == 1) return g_stage1;
+  else if constexpr (kB == 2) return g_stage2;
+  else return g_stage3;
 }
 
 // One operand of the GEMM: issues this wave's share of a stage's direct loads
@@ -157,7 +159,7 @@ struct Operand {
   static constexpr int kInstr = kKMajor ? kBM / 16 / kWaves : kBK / 2 / kWaves;
   const uint16_t* P;
   int64_t ld, rows, r0;     // r0: first m/n row of this tile
-  i32x4_t tile_rsrc;        // k-major: the tile's rows
+  rsrc_t tile_rsrc;         // k-major: the tile's rows
   int voff0[kInstr];        // k-major: per-lane byte offset of (row, chunk) at k = 0
   int kc8[kInstr];          // k-major: per-lane chunk start (elements)
   int moff0[kInstr];        // mn-major: per-lane byte offset inside a stage
@@ -202,15 +204,15 @@ struct Operand {
 #pragma unroll
       for (int t = 0; t < kInstr; ++t) {
         const int voff = kc8[t] < klim ? voff0[t] + static_cast<int>(k0 * 2) : kOOB;
-        dma16(tile_rsrc, lds_addr(dst + first_row(w, t) * kBK), voff);
+        dma16(tile_rsrc, dst + first_row(w, t) * kBK, voff);
       }
     } else {
       int64_t nk = kend - k0;
       if (nk > kBK) nk = kBK;
       // From (k0, r0) to the end of row k0 + nk - 1.
-      const i32x4_t r = make_rsrc(P + k0 * ld + r0, (nk * ld - r0) * 2);
+      const rsrc_t r = make_rsrc(P + k0 * ld + r0, (nk * ld - r0) * 2);
 #pragma unroll
-      for (int t = 0; t < kInstr; ++t) dma16(r, lds_addr(dst + first_k(w, t) * kBM), moff0[t]);
+      for (int t = 0; t < kInstr; ++t) dma16(r, dst + first_k(w, t) * kBM, moff0[t]);
     }
   }
 
@@ -219,8 +221,9 @@ struct Operand {
   __device__ __forceinline__ bf16x8_t frag(const uint16_t* src, int base, int kk) const {
     const int lane = threadIdx.x & 63;
     if constexpr (kKMajor) {
-      const int row = base + (lane & 31);
-      return *reinterpret_cast<const bf16x8_t*>(src + koff(row, kk * 2 + (lane >> 5)));
+      // base is a multiple of 32 and the swizzle depends on row bits 1..3
+      // only, so base contributes a constant (immediate) offset.
+      return *reinterpret_cast<const bf16x8_t*>(src + base * kBK + koff(lane & 31, kk * 2 + (lane >> 5)));
     } else {
       const int i = (lane & 15) >> 2, q = lane & 3;
       const int k = kk * 16 + (lane >> 5) * 8 + i;
@@ -255,11 +258,15 @@ __device__ __forceinline__ void load_frags(Frags<kFJ>& f, const Operand<kAK, kW>
 // One 16-wide k step: read the next fragments `nf` from LDS and run the
 // 4 x kFJ MFMAs on `f`; the scheduler is told to interleave the LDS reads one
 // per MFMA so neither pipe waits on a burst of the other.
-template <int kFJ, bool kAK, bool kBKm, int kW>
+template <int kHalf, int kFJ, bool kAK, bool kBKm, int kW>
 __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][kFJ], const Frags<kFJ>& f,
                                          Frags<kFJ>& nf, const Operand<kAK, kW>& A,
                                          const Operand<kBKm, kW>& B, const uint16_t* src,
-                                         int row0, int col0, int kk) {
+                                         int row0, int col0, int kk, uint16_t* dst, int64_t k0,
+                                         int64_t kend) {
+  constexpr int kDma = kHalf == 0 ? Operand<kAK, kW>::kInstr : Operand<kBKm, kW>::kInstr;
+  if constexpr (kHalf == 0) A.issue(dst, k0, kend);
+  else B.issue(dst + kOpElems, k0, kend);
   load_frags(nf, A, B, src, row0, col0, kk);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -272,8 +279,31 @@ __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][kFJ], const Frags<kF
   for (int t = 0; t < 4 * kFJ; ++t) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     if (t < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    if (t % (4 * kFJ / kDma) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
   }
   if constexpr (kReads > 4 * kFJ) __builtin_amdgcn_sched_group_barrier(0x100, kReads - 4 * kFJ, 0);
+}
+
+// Stage s (buffer kB = s % 4): its second k step on the MFMA pipe while the
+// first fragments of stage s + 1 are read, with the loads of stage s + 3 into
+// buffer (s + 3) % 4 spread over both steps (A in the first, B in the
+// second). Buffer (s + 3) % 4 last held stage s - 1, whose reads all finished
+// before the previous barrier. Loads past the end of K read zeros, so every
+// stage issues the same number of loads.
+template <int kB, int kFJ, bool kAK, bool kBKm, int kW>
+__device__ __forceinline__ void stage_iter(f32x16_t (&acc)[4][kFJ], Frags<kFJ>& f0, Frags<kFJ>& f1,
+                                           const Operand<kAK, kW>& A, const Operand<kBKm, kW>& B,
+                                           int row0, int col0, int64_t k0, int64_t kend) {
+  constexpr int kPerA = Operand<kAK, kW>::kInstr, kPer = kPerA + Operand<kBKm, kW>::kInstr;
+  uint16_t* dst = stage_buf<(kB + 3) & 3>();
+  mma_step<0>(acc, f0, f1, A, B, stage_buf<kB>(), row0, col0, 1, dst, k0, kend);
+  // Stage s + 1 has landed once only the loads issued after it (stage s + 2
+  // and the A half of stage s + 3) are in flight. The count holds because the
+  // loop issues no other vector memory instruction: no register spills, which
+  // the launcher checks.
+  wait_vmcnt<kPer + kPerA>();
+  block_sync();
+  mma_step<1>(acc, f1, f0, A, B, stage_buf<(kB + 1) & 3>(), row0, col0, 0, dst, k0, kend);
 }
 
 template <bool kAK, bool kBKm, int kEpi, int kWN>
@@ -282,7 +312,6 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
   constexpr int kWaves = kWM * kWN;
   constexpr int kFJ = kBM / kWN / 32;  // 32-column MFMA blocks per wave
   constexpr int kPer = Operand<kAK, kWaves>::kInstr + Operand<kBKm, kWaves>::kInstr;
-  extern __shared__ __align__(16) uint16_t smem[];
 
   int64_t tm, tn;
   int sp;
@@ -316,32 +345,33 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
   // last reader (stage s - 1) finished before the previous barrier. The
   // barrier of stage s (between its two k steps) waits for stage s + 1.
   if (ksteps > 0) {
-    const int pre = ksteps < kStages - 1 ? ksteps : kStages - 1;
-    for (int s = 0; s < pre; ++s) {
-      uint16_t* st = smem + s * kStageElems;
-      opA.issue(st, kbeg + static_cast<int64_t>(s) * kBK, kend);
-      opB.issue(st + kOpElems, kbeg + static_cast<int64_t>(s) * kBK, kend);
-    }
-    wait_stage_loads<kPer>(pre - 1);
+    opA.issue(stage_buf<0>(), kbeg, kend);
+    opB.issue(stage_buf<0>() + kOpElems, kbeg, kend);
+    opA.issue(stage_buf<1>(), kbeg + kBK, kend);
+    opB.issue(stage_buf<1>() + kOpElems, kbeg + kBK, kend);
+    opA.issue(stage_buf<2>(), kbeg + 2 * kBK, kend);
+    opB.issue(stage_buf<2>() + kOpElems, kbeg + 2 * kBK, kend);
+    wait_vmcnt<2 * kPer>();
     block_sync();
     Frags<kFJ> f0, f1;
-    load_frags(f0, opA, opB, smem, row0, col0, 0);
-    for (int s = 0; s < ksteps; ++s) {
-      const uint16_t* cur = smem + (s % kStages) * kStageElems;
-      if (s + kStages - 1 < ksteps) {
-        uint16_t* st = smem + ((s + kStages - 1) % kStages) * kStageElems;
-        const int64_t k0 = kbeg + static_cast<int64_t>(s + kStages - 1) * kBK;
-        opA.issue(st, k0, kend);
-        opB.issue(st + kOpElems, k0, kend);
-      }
-      mma_step(acc, f0, f1, opA, opB, cur, row0, col0, 1);
-      // Stage s + 1 must have landed; loads up to min(s + 3, ksteps - 1) were issued.
-      const int last_issued = (s + kStages - 1 < ksteps - 1) ? s + kStages - 1 : ksteps - 1;
-      wait_stage_loads<kPer>(last_issued - (s + 1));
-      block_sync();
-      // On the last stage this reads a stale (in-bounds) buffer; never used.
-      mma_step(acc, f1, f0, opA, opB, smem + ((s + 1) % kStages) * kStageElems, row0, col0, 0);
+    load_frags(f0, opA, opB, stage_buf<0>(), row0, col0, 0);
+    // The buffer of stage s must be known at compile time, hence four stages
+    // per trip. The last stage's second step reads fragments of a stage past
+    // the end (zeros or stale, in bounds); they are never used.
+    int s = 0;
+    for (; s + 4 <= ksteps; s += 4) {
+      const int64_t k3 = kbeg + static_cast<int64_t>(s + 3) * kBK;
+      stage_iter<0>(acc, f0, f1, opA, opB, row0, col0, k3, kend);
+      stage_iter<1>(acc, f0, f1, opA, opB, row0, col0, k3 + kBK, kend);
+      stage_iter<2>(acc, f0, f1, opA, opB, row0, col0, k3 + 2 * kBK, kend);
+      stage_iter<3>(acc, f0, f1, opA, opB, row0, col0, k3 + 3 * kBK, kend);
     }
+    const int64_t k3 = kbeg + static_cast<int64_t>(s + 3) * kBK;
+    if (s < ksteps) stage_iter<0>(acc, f0, f1, opA, opB, row0, col0, k3, kend);
+    if (s + 1 < ksteps) stage_iter<1>(acc, f0, f1, opA, opB, row0, col0, k3 + kBK, kend);
+    if (s + 2 < ksteps) stage_iter<2>(acc, f0, f1, opA, opB, row0, col0, k3 + 2 * kBK, kend);
+    // Loads past the end are still in flight; they write this workgroup's LDS.
+    wait_vmcnt<0>();
   }
 
   const int l32 = lane & 31, lhi = lane >> 5;
@@ -404,19 +434,19 @@ static hipError_t launch_mfma_v2(const GemmDesc& d, hipStream_t s) {
   int64_t k_per = (d.K + splits - 1) / splits;
   k_per = (k_per + kBK - 1) / kBK * kBK;
   const int64_t blocks = tiles_m * tiles_n * splits;
-  const size_t lds = static_cast<size_t>(kStages) * kStageElems * sizeof(uint16_t);  // 128 KiB
   auto kern = k_gemm2<kAK, kBKm, kEpi, kWN>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
+  // Spill stores would be counted by the loop's explicit vmcnt waits.
+  static int spills = -1;
+  if (spills < 0) {
+    hipFuncAttributes fa;
+    const hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    spills = fa.localSizeBytes != 0;
   }
+  if (spills) return hipErrorInvalidDeviceFunction;
   GemmDesc dd = d;
   dd.k_splits = splits;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * kWM * kWN), lds, s, dd,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * kWM * kWN), 0, s, dd,
                      tiles_m, tiles_n, k_per);
   return hipGetLastError();
 }
