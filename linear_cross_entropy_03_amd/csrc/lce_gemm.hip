@@ -306,6 +306,141 @@ __device__ __forceinline__ void stage_iter(f32x16_t (&acc)[4][kFJ], Frags<kFJ>& 
   mma_step<1>(acc, f1, f0, A, B, stage_buf<(kB + 1) & 3>(), row0, col0, 0, dst, k0, kend);
 }
 
+// Output through LDS. The MFMA result layout gives each lane 4 consecutive
+// columns of one row, so direct stores touch 32 rows per instruction with 8
+// or 16 bytes each. Each wave instead writes half of its 128 x 64 result
+// (64 rows) into its own LDS region and reads it back as whole row segments:
+// 8 lanes per 128-byte row (bf16) or 16 lanes per 256-byte row (fp32), so
+// every store instruction covers full cache lines. Slots are XOR-swizzled by
+// row to spread the column-wise writes over the banks.
+
+// This wave's region: kBytes each, packed into the 32 KiB stage buffers.
+template <int kBytes>
+__device__ __forceinline__ char* epi_region(int w) {
+  constexpr int kPerBuf = 2 * kOpElems * 2 / kBytes;  // waves per stage buffer
+  const int b = w / kPerBuf, o = (w % kPerBuf) * kBytes;
+  char* base = b == 0 ? reinterpret_cast<char*>(g_stage0)
+             : b == 1 ? reinterpret_cast<char*>(g_stage1)
+             : b == 2 ? reinterpret_cast<char*>(g_stage2)
+                      : reinterpret_cast<char*>(g_stage3);
+  return base + o;
+}
+
+// Lanes of one wave exchange data through LDS: LDS executes a wave's
+// instructions in order, so only the compiler must not reorder.
+__device__ __forceinline__ void wave_lds_fence() {
+  wait_lgkm0();
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int kFJ>
+__device__ __forceinline__ void epilogue_bf16(const f32x16_t (&acc)[4][kFJ], const GemmDesc& d,
+                                              int64_t m0, int64_t n0, int row0, int col0, int wave) {
+  static_assert(kFJ == 2, "64 output columns per wave");
+  const int lane = threadIdx.x & 63, l32 = lane & 31, lhi = lane >> 5;
+  char* reg = epi_region<8192>(wave);
+  const uint16_t* bias = static_cast<const uint16_t*>(d.bias);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int r = ii * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < kFJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16_t& a = acc[2 * h + ii][j];
+          float v[4] = {a[q * 4 + 0], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]};
+          if (bias != nullptr) {
+            const int64_t n = n0 + col0 + j * 32 + q * 8 + lhi * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < d.N) v[e] += bf16_to_f32(bias[n + e]);
+          }
+          const int slot = j * 4 + q;
+          *reinterpret_cast<uint2*>(reg + r * 128 + ((slot ^ ((r >> 1) & 7)) << 4) + lhi * 8) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = u * 8 + (lane >> 3), sl = lane & 7;
+      const uint4 val = *reinterpret_cast<const uint4*>(reg + r * 128 + ((sl ^ ((r >> 1) & 7)) << 4));
+      const int64_t m = m0 + row0 + h * 64 + r;
+      const int64_t n = n0 + col0 + sl * 8;
+      if (m >= d.M || n >= d.N) continue;
+      uint16_t* c = static_cast<uint16_t*>(d.C) + m * d.ldc + n;
+      if (n + 7 < d.N) {
+        *reinterpret_cast<uint4*>(c) = val;
+      } else {
+        const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+        for (int e = 0; e < 8 && n + e < d.N; ++e)
+          c[e] = static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16));
+      }
+    }
+    wave_lds_fence();
+  }
+}
+
+template <int kEpi, int kFJ>
+__device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], const GemmDesc& d,
+                                             int64_t m0, int64_t n0, int sp, int row0, int col0,
+                                             int wave) {
+  static_assert(kFJ == 2, "64 output columns per wave");
+  const int lane = threadIdx.x & 63, l32 = lane & 31, lhi = lane >> 5;
+  char* reg = epi_region<8192>(wave);
+  float* C = static_cast<float*>(d.C) + static_cast<int64_t>(sp) * d.split_stride;
+  // A quarter (32 rows) of the wave's result at a time.
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int64_t mh = m0 + row0 + h * 32;
+    // Accumulating: fetch the quarter's old row segments first, in one batch
+    // (range-checked buffer loads read zeros outside the matrix), so their
+    // latency overlaps the staging through LDS.
+    float4 old[8];
+    if constexpr (kEpi == kEpiAccumF32) {
+      const rsrc_t rc = make_rsrc(C + mh * d.ldc + n0 + col0, 32 * d.ldc * 4);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = u * 4 + (lane >> 4), sl = lane & 15;
+        const bool ok = mh + r < d.M && n0 + col0 + sl * 4 + 3 < d.N;
+        const int voff = ok ? static_cast<int>(r * d.ldc * 4) + sl * 16 : kOOB;
+        old[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kFJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16_t& a = acc[h][j];
+        const int slot = j * 8 + q * 2 + lhi;
+        *reinterpret_cast<float4*>(reg + l32 * 256 + ((slot ^ (l32 & 15)) << 4)) =
+            make_float4(a[q * 4 + 0], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]);
+      }
+    wave_lds_fence();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = u * 4 + (lane >> 4), sl = lane & 15;
+      float4 o = *reinterpret_cast<const float4*>(reg + r * 256 + ((sl ^ (r & 15)) << 4));
+      const int64_t m = mh + r;
+      const int64_t n = n0 + col0 + sl * 4;
+      if (m >= d.M || n >= d.N) continue;
+      float* c = C + m * d.ldc + n;
+      if (n + 3 < d.N) {
+        if constexpr (kEpi == kEpiAccumF32) {
+          o.x += old[u].x; o.y += old[u].y; o.z += old[u].z; o.w += old[u].w;
+        }
+        *reinterpret_cast<float4*>(c) = o;
+      } else {
+        const float w[4] = {o.x, o.y, o.z, o.w};
+        for (int e = 0; e < 4 && n + e < d.N; ++e) c[e] = (kEpi == kEpiAccumF32) ? c[e] + w[e] : w[e];
+      }
+    }
+    wave_lds_fence();
+  }
+}
+
 template <bool kAK, bool kBKm, int kEpi, int kWN>
 __global__ __launch_bounds__(64 * kWM * kWN) __attribute__((amdgpu_waves_per_eu(kWN / 2, kWN / 2)))
 void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
@@ -327,7 +462,6 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
   opA.init(static_cast<const uint16_t*>(d.A), d.lda, d.M, m0);
   opB.init(static_cast<const uint16_t*>(d.B), d.ldb, d.N, n0);
 
-  const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave / kWN, wn = wave % kWN;
   const int row0 = wm * (kBM / kWM), col0 = wn * (kBM / kWN);
@@ -374,54 +508,10 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
     wait_vmcnt<0>();
   }
 
-  const int l32 = lane & 31, lhi = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + row0 + i * 32 + l32;
-    if (m >= d.M) continue;
-#pragma unroll
-    for (int j = 0; j < kFJ; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + col0 + j * 32 + q * 8 + lhi * 4;
-        if (n >= d.N) continue;
-        float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
-                      acc[i][j][q * 4 + 3]};
-        const bool full = n + 3 < d.N;
-        if constexpr (kEpi == kEpiLogits) {
-          if (d.bias != nullptr) {
-            const uint16_t* b = static_cast<const uint16_t*>(d.bias);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < d.N) v[e] += bf16_to_f32(b[n + e]);
-          }
-          uint16_t* c = static_cast<uint16_t*>(d.C) + m * d.ldc + n;
-          if (full) {
-            *reinterpret_cast<uint2*>(c) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < d.N) c[e] = f32_to_bf16(v[e]);
-          }
-        } else {
-          float* c = static_cast<float*>(d.C) + static_cast<int64_t>(sp) * d.split_stride +
-                     m * d.ldc + n;
-          if (full) {
-            float4 o = make_float4(v[0], v[1], v[2], v[3]);
-            if constexpr (kEpi == kEpiAccumF32) {
-              const float4 old = *reinterpret_cast<const float4*>(c);
-              o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
-            }
-            *reinterpret_cast<float4*>(c) = o;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < d.N) c[e] = (kEpi == kEpiAccumF32) ? c[e] + v[e] : v[e];
-          }
-        }
-      }
-    }
-  }
+  // Every wave is done with the stage buffers; they now stage the output.
+  block_sync();
+  if constexpr (kEpi == kEpiLogits) epilogue_bf16<kFJ>(acc, d, m0, n0, row0, col0, wave);
+  else epilogue_f32<kEpi, kFJ>(acc, d, m0, n0, sp, row0, col0, wave);
 }
 
 }  // namespace mfma2
