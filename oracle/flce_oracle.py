@@ -32,6 +32,9 @@ Readings where the pages say nothing (each is also listed in the design notes):
     column sum of dZ.
   * shard statistics are taken relative to the shard's own maximum; the target
     logit is 0 when the target is outside the shard or the row is ignored.
+  * a shard's backward takes the global per-row lse as input (the pages
+    exchange the statistics, not the gradient); validity and the mean's
+    N_valid are judged against the whole vocabulary.
 
 Every function here evaluates the plain definition. The only partition is the
 row blocking of `flce`, which the FLCE description itself prescribes (rows are
@@ -259,6 +262,60 @@ def flce_shard_stats(X, W_shard, targets, vocab_start, V_global, bias_shard=None
         m, s, t = shard_stats(Z, y[r0:r1], vocab_start, V_global, ignore_index)
         out[0][r0:r1], out[1][r0:r1], out[2][r0:r1] = m, s, t
     return tuple(out)
+
+
+def shard_loss(lse, z_target, targets, V_global, ignore_index=-100, reduction="mean"):
+    """The global loss from combined shard statistics: loss_n = lse_n - z_y for
+    rows valid w.r.t. the whole vocabulary, 0 otherwise, then reduced.
+    Returns (loss, loss_rows, n_valid)."""
+    y = np.asarray(targets).astype(np.int64)
+    valid, _ = target_masks(y, V_global, ignore_index)
+    n_valid = int(valid.sum())
+    rows = np.where(valid, _f64(lse) - _f64(z_target), 0.0)
+    return _reduce(rows, n_valid, reduction), rows, n_valid
+
+
+def flce_shard_backward(X, W_shard, targets, vocab_start, V_global, lse, bias_shard=None,
+                        ignore_index=-100, reduction="mean", row_block=1024):
+    """The part of the global FLCE gradients that one vocabulary shard owns
+    (DeepSpeed vocab-parallel CE page: each rank holds the head rows of its
+    vocabulary range; the per-row normaliser is global).
+
+    With z = X W_shard^T (+ b_shard) over global ids [vocab_start,
+    vocab_start + V_local) and the global lse_n of every row:
+      dZ[n, j] = scale * (exp(z[n, j] - lse_n) - [vocab_start + j == y_n])
+    for rows valid w.r.t. V_global (0 for the others), scale = 1/N_valid
+    (mean) or 1; then
+      grad_X partial = dZ W_shard   (the shards' partials sum to grad_X),
+      grad_W_shard   = dZ^T X       (rows [vocab_start, ...) of grad_W),
+      grad_b_shard   = column sums of dZ.
+    Returns (grad_X_partial, grad_W_shard, grad_b_shard or None).
+    """
+    X = _f64(X)
+    Ws = _f64(W_shard)
+    lse = _f64(lse)
+    y = np.asarray(targets).astype(np.int64)
+    N = X.shape[0]
+    Vl = Ws.shape[0]
+    valid, _ = target_masks(y, V_global, ignore_index)
+    scale = reduction_scale(int(valid.sum()), reduction)
+    gX = np.zeros_like(X)
+    gW = np.zeros_like(Ws)
+    gb = np.zeros(Vl) if bias_shard is not None else None
+    cols = int(vocab_start) + np.arange(Vl)
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        Z = X[r0:r1] @ Ws.T
+        if bias_shard is not None:
+            Z = Z + _f64(bias_shard)[None, :]
+        onehot = (cols[None, :] == y[r0:r1, None]).astype(np.float64)
+        dZ = scale * (np.exp(Z - lse[r0:r1, None]) - onehot)
+        dZ[~valid[r0:r1]] = 0.0
+        gX[r0:r1] = dZ @ Ws
+        gW += dZ.T @ X[r0:r1]
+        if gb is not None:
+            gb += dZ.sum(axis=0)
+    return gX, gW, gb
 
 
 def materialised_logits_bytes(n_tokens, vocab, elem_bytes):

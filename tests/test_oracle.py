@@ -354,3 +354,78 @@ def test_sampled_helpers_agree_with_full():
     gw, gb = O.flce_grad_w_rows(X, W, y, vr, bias=b, reduction="mean", row_block=5)
     np.testing.assert_allclose(gw, g["W"][vr], atol=1e-14)
     np.testing.assert_allclose(gb, g["bias"][vr], atol=1e-14)
+
+
+# ------------------------------------------------- vocabulary-shard backward
+
+def _lse_by_loops(Z):
+    return np.array([math.log(sum(math.exp(v) for v in row)) for row in Z])
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_shard_backward_with_one_shard_is_flce(reduction):
+    rng = np.random.default_rng(18)
+    X, W, b, y = _rand_problem(rng, N=23, H=6, V=17, n_ignored=4)
+    y[3] = 17  # bad target: treated as ignored on both sides
+    _, g, _ = O.flce(X, W, y, bias=b, reduction=reduction)
+    lse = _lse_by_loops(X @ W.T + b)
+    gx, gw, gb = O.flce_shard_backward(X, W, y, 0, 17, lse, bias_shard=b, reduction=reduction,
+                                       row_block=5)
+    np.testing.assert_allclose(gx, g["X"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gw, g["W"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gb, g["bias"], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_vocab_parallel_pipeline_is_flce(reduction):
+    """Shard stats -> combine -> loss, then each shard's backward: the loss,
+    the sum of the grad_X partials and the concatenated grad_W / grad_bias
+    shards equal the unsharded FLCE."""
+    rng = np.random.default_rng(19)
+    V = 29
+    X, W, b, y = _rand_problem(rng, N=31, H=7, V=V, n_ignored=5)
+    y[0] = -3   # bad target
+    loss, g, info = O.flce(X, W, y, bias=b, reduction=reduction)
+    bounds = [0, 5, 18, V]   # uneven shards
+    stats = [O.flce_shard_stats(X, W[a:c], y, a, V, bias_shard=b[a:c], row_block=8)
+             for a, c in zip(bounds[:-1], bounds[1:])]
+    lse, zt = O.combine_shard_stats(stats)
+    sl, rows, n_valid = O.shard_loss(lse, zt, y, V, reduction=reduction)
+    assert n_valid == info["n_valid"]
+    np.testing.assert_allclose(rows, info["loss_rows"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sl, loss, rtol=1e-12, atol=1e-14)
+    parts = [O.flce_shard_backward(X, W[a:c], y, a, V, lse, bias_shard=b[a:c], reduction=reduction)
+             for a, c in zip(bounds[:-1], bounds[1:])]
+    np.testing.assert_allclose(sum(p[0] for p in parts), g["X"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(np.concatenate([p[1] for p in parts]), g["W"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(np.concatenate([p[2] for p in parts]), g["bias"], rtol=1e-12, atol=1e-14)
+
+
+def test_shard_backward_finite_differences():
+    """grad_W_shard is the derivative of the global mean loss w.r.t. the
+    shard's head rows (central differences through the unsharded loss)."""
+    rng = np.random.default_rng(20)
+    V = 11
+    X, W, b, y = _rand_problem(rng, N=9, H=4, V=V, n_ignored=2)
+    a, c = 4, 9
+    lse = _lse_by_loops(X @ W.T + b)
+    gx, gw, gb = O.flce_shard_backward(X, W[a:c], y, a, V, lse, bias_shard=b[a:c])
+    h = 1e-6
+    for (i, j) in [(0, 0), (2, 3), (4, 1)]:
+        Wp, Wm = W.copy(), W.copy()
+        Wp[a + i, j] += h
+        Wm[a + i, j] -= h
+        lp, _, _ = O.flce(X, Wp, y, bias=b, want_grads=False)
+        lm, _, _ = O.flce(X, Wm, y, bias=b, want_grads=False)
+        assert abs((lp - lm) / (2 * h) - gw[i, j]) < 1e-8
+    # grad_X partials: the other shards' columns are missing, so compare the
+    # sum over a full partition instead.
+    rest = [O.flce_shard_backward(X, W[p:q], y, p, V, lse, bias_shard=b[p:q])[0]
+            for p, q in ((0, a), (c, V))]
+    Xp = X.copy()
+    Xp[1, 2] += h
+    Xm = X.copy()
+    Xm[1, 2] -= h
+    lp, _, _ = O.flce(Xp, W, y, bias=b, want_grads=False)
+    lm, _, _ = O.flce(Xm, W, y, bias=b, want_grads=False)
+    assert abs((lp - lm) / (2 * h) - (gx + rest[0] + rest[1])[1, 2]) < 1e-8
