@@ -72,7 +72,8 @@ typedef enum {
 const char* flce_status_string(int status);
 
 /*
- * Bytes of workspace flce_forward_backward / flce_shard_stats need for this
+ * Bytes of workspace flce_forward_backward / flce_shard_stats /
+ * flce_shard_backward (with V = V_local for the shard calls) need for this
  * problem and chunk size (chunk_rows 0 = the planner's choice). Pure host
  * computation; returns 0 for invalid sizes.
  */
@@ -111,7 +112,8 @@ int flce_forward_backward(const void* X, const void* W, const void* bias,
                           void* workspace, size_t workspace_bytes, int64_t chunk_rows,
                           void* stream);
 
-/* Bytes of workspace ce_forward_backward / ce_shard_stats need. */
+/* Bytes of workspace ce_forward_backward / ce_shard_stats /
+ * ce_combine_shard_stats (V = V_global) need. */
 size_t ce_workspace_bytes(int64_t N, int64_t V);
 
 /*
@@ -157,6 +159,51 @@ int flce_shard_stats(const void* X, const void* W_shard, const void* bias_shard,
                      int32_t ignore_index, float* row_max, float* row_sumexp,
                      float* row_target_logit, void* workspace, size_t workspace_bytes,
                      int64_t chunk_rows, void* stream);
+
+/*
+ * Combine the statistics of P vocabulary shards into the global per-row
+ * log-sum-exp and the loss (the exchange step of vocab-parallel CE on the
+ * DeepSpeed page, done on one device; the collective that gathers the shards'
+ * statistics is the caller's). Shards are combined in index order, in float64:
+ * M = max_k m_k, lse = M + ln sum_k s_k exp(m_k - M), z_y = sum_k t_k, so the
+ * result does not depend on how the statistics were produced.
+ *
+ *   shard_max, shard_sumexp, shard_target_logit  [P, N] float32, shard-major
+ *     (row k holds shard k's ce_shard_stats / flce_shard_stats outputs)
+ *   targets   [N] int32 global ids, validity judged against [0, V_global)
+ *   row_lse   [N] float32 global lse per row, or NULL
+ *   loss      [1] float32 (SUM / MEAN) or [N] (NONE): loss_n = lse_n - z_y
+ *             for valid rows, 0 for ignored or bad ones
+ *   workspace of at least ce_workspace_bytes(N, V_global)
+ * Bad targets are reported by flce_check_device_error on this workspace.
+ */
+int ce_combine_shard_stats(const float* shard_max, const float* shard_sumexp,
+                           const float* shard_target_logit, int64_t P, int64_t N,
+                           const int32_t* targets, int64_t V_global, int32_t ignore_index,
+                           int reduction, float* row_lse, float* loss, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * The backward of FLCE for one vocabulary shard (the per-rank gradient step of
+ * vocab-parallel CE on the DeepSpeed page): with the global row_lse from
+ * ce_combine_shard_stats, for each chunk of rows
+ *   dZ = c * (exp(X W_shard^T (+ bias_shard) - lse) - onehot)   (shard columns,
+ *        one-hot only where the global target falls in the shard; c = 1/N_valid
+ *        for MEAN, 1 otherwise; 0 for ignored or bad rows)
+ *   grad_X         [N, H] float32 or NULL: this shard's partial dZ W_shard,
+ *                  overwritten; the shards' partials sum to grad_X (the
+ *                  caller's all-reduce)
+ *   grad_W_shard   [V_local, H] float32 or NULL: dZ^T X, overwritten
+ *   grad_bias_shard[V_local] float32 or NULL (NULL when bias_shard is NULL)
+ * Workspace: flce_workspace_bytes(N, H, V_local, dtype, chunk_rows). Same
+ * layout, alignment and error rules as flce_forward_backward.
+ */
+int flce_shard_backward(const void* X, const void* W_shard, const void* bias_shard,
+                        const int32_t* targets, int64_t N, int64_t H, int64_t V_local,
+                        int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
+                        int reduction, const float* row_lse, float* grad_X, float* grad_W_shard,
+                        float* grad_bias_shard, void* workspace, size_t workspace_bytes,
+                        int64_t chunk_rows, void* stream);
 
 /*
  * Waits for `stream`, then reports whether the last call that used this

@@ -39,6 +39,10 @@ _SIGNATURES = {
                               _sz, _vp]),
     "flce_shard_stats": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i32,
                                 _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
+    "ce_combine_shard_stats": (_int, [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32, _int, _vp, _vp,
+                                      _vp, _sz, _vp]),
+    "flce_shard_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i32,
+                                   _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
     "flce_check_device_error": (_int, [_vp, _vp]),
     "flce_timing_enable": (_int, [_int]),
     "flce_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
@@ -143,6 +147,13 @@ def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
 
 
+def _grad_arg(want, shape, device):
+    """A gradient output: the given tensor, a new float32 one (True), or None."""
+    if isinstance(want, torch.Tensor):
+        return want
+    return _empty(shape, torch.float32, device) if want else None
+
+
 def flce_forward_backward(X, W, targets, bias=None, ignore_index=-100, reduction="mean",
                           grad_X=True, grad_W=True, grad_bias=None, loss=None, workspace=None,
                           chunk_rows=0, stream=None):
@@ -159,15 +170,9 @@ def flce_forward_backward(X, W, targets, bias=None, ignore_index=-100, reduction
     dt = _dtype_code(X)
     if grad_bias is None:
         grad_bias = bias is not None
-    outs = []
-    for want, shape in ((grad_X, (N, H)), (grad_W, (V, H)), (grad_bias, (V,))):
-        if isinstance(want, torch.Tensor):
-            outs.append(want)
-        elif want:
-            outs.append(_empty(shape, torch.float32, dev))
-        else:
-            outs.append(None)
-    gX, gW, gb = outs
+    gX = _grad_arg(grad_X, (N, H), dev)
+    gW = _grad_arg(grad_W, (V, H), dev)
+    gb = _grad_arg(grad_bias, (V,), dev)
     if loss is None:
         loss = _empty((N,) if reduction == "none" else (1,), torch.float32, dev)
     if workspace is None:
@@ -248,6 +253,59 @@ def flce_shard_stats(X, W_shard, targets, vocab_start, V_global, bias_shard=None
         workspace.numel() * workspace.element_size(), chunk_rows, _stream(stream))
     _check(st, "flce_shard_stats")
     return m, s, t
+
+
+def ce_combine_shard_stats(shard_max, shard_sumexp, shard_target_logit, targets, V_global,
+                           ignore_index=-100, reduction="mean", row_lse=None, loss=None,
+                           workspace=None, stream=None):
+    """Global per-row lse and the loss from P shards' statistics ([P, N] each).
+    Returns (loss, row_lse)."""
+    P, N = shard_max.shape
+    dev = shard_max.device
+    red = _red(reduction)
+    if row_lse is None:
+        row_lse = _empty((N,), torch.float32, dev)
+    if loss is None:
+        loss = _empty((N,) if reduction == "none" else (1,), torch.float32, dev)
+    if workspace is None:
+        workspace = _empty((max(1, ce_workspace_bytes(N, V_global)),), torch.uint8, dev)
+    st = lib().ce_combine_shard_stats(
+        _ptr(shard_max, "shard_max", torch.float32), _ptr(shard_sumexp, "shard_sumexp", torch.float32),
+        _ptr(shard_target_logit, "shard_target_logit", torch.float32), P, N,
+        _ptr(targets, "targets", torch.int32), V_global, ignore_index, red,
+        _ptr(row_lse, "row_lse", torch.float32), _ptr(loss, "loss", torch.float32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "ce_combine_shard_stats")
+    return loss, row_lse
+
+
+def flce_shard_backward(X, W_shard, targets, row_lse, vocab_start, V_global, bias_shard=None,
+                        ignore_index=-100, reduction="mean", grad_X=True, grad_W=True,
+                        grad_bias=None, workspace=None, chunk_rows=0, stream=None):
+    """One vocabulary shard's part of the FLCE gradients, given the global
+    row lse. Gradient arguments: True = allocate, False/None = skip, or a
+    tensor to write into. Returns (grad_X partial, grad_W_shard, grad_bias_shard)."""
+    N, H = X.shape
+    Vl = W_shard.shape[0]
+    dev = X.device
+    dt = _dtype_code(X)
+    red = _red(reduction)
+    if grad_bias is None:
+        grad_bias = bias_shard is not None
+    gX = _grad_arg(grad_X, (N, H), dev)
+    gW = _grad_arg(grad_W, (Vl, H), dev)
+    gb = _grad_arg(grad_bias, (Vl,), dev)
+    if workspace is None:
+        workspace = _empty((max(1, flce_workspace_bytes(N, H, Vl, dt, chunk_rows)),), torch.uint8, dev)
+    st = lib().flce_shard_backward(
+        _ptr(X, "X"), _ptr(W_shard, "W_shard", X.dtype), _ptr(bias_shard, "bias_shard", X.dtype),
+        _ptr(targets, "targets", torch.int32), N, H, Vl, vocab_start, V_global, dt, ignore_index,
+        red, _ptr(row_lse, "row_lse", torch.float32), _ptr(gX, "grad_X", torch.float32),
+        _ptr(gW, "grad_W_shard", torch.float32), _ptr(gb, "grad_bias_shard", torch.float32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
+        _stream(stream))
+    _check(st, "flce_shard_backward")
+    return gX, gW, gb
 
 
 def flce_check_device_error(workspace, stream=None):

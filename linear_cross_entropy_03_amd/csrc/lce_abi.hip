@@ -404,6 +404,134 @@ int flce_shard_stats(const void* X, const void* W_shard, const void* bias_shard,
   return FLCE_OK;
 }
 
+int ce_combine_shard_stats(const float* shard_max, const float* shard_sumexp,
+                           const float* shard_target_logit, int64_t P, int64_t N,
+                           const int32_t* targets, int64_t V_global, int32_t ignore_index,
+                           int reduction, float* row_lse, float* loss, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (reduction < FLCE_REDUCTION_NONE || reduction > FLCE_REDUCTION_MEAN) return FLCE_E_INVALID_ARG;
+  if (P <= 0 || N < 0 || V_global <= 0 || loss == nullptr) return FLCE_E_INVALID_ARG;
+  if (N > 0 && (shard_max == nullptr || shard_sumexp == nullptr || shard_target_logit == nullptr ||
+                targets == nullptr))
+    return FLCE_E_INVALID_ARG;
+  if (N >= kMaxRows || V_global >= kMaxDim || P >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  const void* ptrs[] = {shard_max, shard_sumexp, shard_target_logit, targets, row_lse, loss, workspace};
+  for (const void* q : ptrs)
+    if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < ce_ws_bytes(N)) return FLCE_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  float* loss_rows = reduction == FLCE_REDUCTION_NONE ? loss : reinterpret_cast<float*>(ws + align_up(sizeof(WsHeader)));
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, N, V_global, ignore_index, reduction, hdr, s);
+  }));
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_combine_stats(shard_max, shard_sumexp, shard_target_logit, P, N, targets,
+                                ignore_index, V_global, row_lse, loss_rows, s);
+  }));
+  if (reduction != FLCE_REDUCTION_NONE)
+    LCE_TRY(timed(kKindOther, s, [&] {
+      return launch_reduce_loss(loss_rows, N, hdr, reduction, loss, s);
+    }));
+  return FLCE_OK;
+}
+
+int flce_shard_backward(const void* X, const void* W_shard, const void* bias_shard,
+                        const int32_t* targets, int64_t N, int64_t H, int64_t V_local,
+                        int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
+                        int reduction, const float* row_lse, float* grad_X, float* grad_W_shard,
+                        float* grad_bias_shard, void* workspace, size_t workspace_bytes,
+                        int64_t chunk_rows, void* stream) {
+  int st = validate_common(dtype, reduction);
+  if (st != FLCE_OK) return st;
+  if (N < 0 || H <= 0 || V_local <= 0 || vocab_start < 0 || V_global < vocab_start + V_local ||
+      chunk_rows < 0)
+    return FLCE_E_INVALID_ARG;
+  if (W_shard == nullptr) return FLCE_E_INVALID_ARG;
+  if (N > 0 && (X == nullptr || targets == nullptr || row_lse == nullptr)) return FLCE_E_INVALID_ARG;
+  if (grad_bias_shard != nullptr && bias_shard == nullptr) return FLCE_E_INVALID_ARG;
+  if (N >= kMaxRows || H >= kMaxDim || V_global >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  const void* ptrs[] = {X, W_shard, bias_shard, targets, row_lse, grad_X, grad_W_shard,
+                        grad_bias_shard, workspace};
+  for (const void* q : ptrs)
+    if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
+  if (dtype == FLCE_BF16 && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  Plan p;
+  if (!make_plan(N, H, V_local, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  void* zbuf = ws + p.off_chunk;
+  float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
+  const size_t e = elem_bytes(dtype);
+  auto gemm = dtype == FLCE_BF16 ? launch_gemm_bf16 : launch_gemm_f32;
+
+  // Validity and the mean's N_valid are judged against the whole vocabulary.
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, N, V_global, ignore_index, reduction, hdr, s);
+  }));
+  if (N == 0) {
+    if (grad_W_shard)
+      LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W_shard, V_local * H, 0.0f, s); }));
+    if (grad_bias_shard)
+      LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_bias_shard, V_local, 0.0f, s); }));
+  }
+  for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
+    const int64_t rows = std::min(p.chunk, N - r0);
+    const bool first = r0 == 0;
+    const char* Xc = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+
+    GemmDesc g1{};
+    g1.A = Xc; g1.lda = H; g1.a_kmajor = true;
+    g1.B = W_shard; g1.ldb = H; g1.b_kmajor = true;
+    g1.C = zbuf; g1.ldc = p.ldz; g1.bias = bias_shard;
+    g1.M = rows; g1.N = V_local; g1.K = H;
+    g1.epilogue = kEpiLogits; g1.k_splits = 1;
+    LCE_TRY(timed(kKindLogits, s, [&] { return gemm(g1, s); }));
+    LCE_TRY(timed(kKindRowCE, s, [&] {
+      return launch_shard_grad(dtype, zbuf, p.ldz, rows, V_local, p.ldz - V_local, vocab_start,
+                               V_global, targets + r0, ignore_index, row_lse + r0, hdr, s);
+    }));
+    if (grad_bias_shard)
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, !first, s);
+      }));
+    if (grad_X) {
+      GemmDesc g2{};
+      g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
+      g2.B = W_shard; g2.ldb = H; g2.b_kmajor = false;
+      g2.M = rows; g2.N = H; g2.K = V_local;
+      g2.epilogue = kEpiStoreF32;
+      float* out = grad_X + static_cast<size_t>(r0) * H;
+      if (p.dx_splits > 1) {
+        g2.C = split_buf; g2.ldc = H;
+        g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
+        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+        LCE_TRY(timed(kKindOther, s, [&] {
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, s);
+        }));
+      } else {
+        g2.C = out; g2.ldc = H; g2.k_splits = 1;
+        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+      }
+    }
+    if (grad_W_shard) {
+      GemmDesc g3{};
+      g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
+      g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
+      g3.C = grad_W_shard; g3.ldc = H;
+      g3.M = V_local; g3.N = H; g3.K = rows;
+      g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32;
+      g3.k_splits = 1;
+      LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
+    }
+  }
+  return FLCE_OK;
+}
+
 int flce_check_device_error(const void* workspace, void* stream) {
   if (workspace == nullptr) return FLCE_E_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);

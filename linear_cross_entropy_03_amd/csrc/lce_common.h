@@ -176,6 +176,13 @@ hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t row
                               const int32_t* targets, int32_t ignore_index, float* row_max,
                               float* row_sumexp, float* row_target, hipStream_t s);
 
+hipError_t launch_shard_grad(int dtype, void* Z, int64_t ldz, int64_t rows, int64_t V_local,
+                             int64_t pad_cols, int64_t vocab_start, int64_t V_global,
+                             const int32_t* targets, int32_t ign, const float* lse,
+                             const WsHeader* hdr, hipStream_t s);
+hipError_t launch_combine_stats(const float* ms, const float* ss, const float* ts, int64_t P,
+                                int64_t N, const int32_t* targets, int32_t ign, int64_t V_global,
+                                float* lse, float* loss_rows, hipStream_t s);
 hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader* hdr,
                               int reduction, float* loss, hipStream_t s);
 

@@ -305,6 +305,102 @@ hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t row
   return hipGetLastError();
 }
 
+// ------------------------------------------------- vocabulary-shard backward
+
+// In place over one shard's logits [rows, V_local] (global ids v0 + j), given
+// the global lse of each row: dZ = c * (exp(z - lse) - [v0 + j == y]) with
+// c = the reduction scale for rows valid w.r.t. V_global, 0 otherwise. One
+// read and one write per element; pad columns [V_local, V_local + pad) are
+// zeroed for the GEMMs that read the chunk.
+template <typename T, int kThreads>
+__global__ __launch_bounds__(kThreads) void k_shard_grad(T* Z, int64_t ldz, int64_t Vl,
+                                                         int64_t pad_cols, int64_t v0, int64_t Vg,
+                                                         const int32_t* __restrict__ targets,
+                                                         int32_t ign, const float* __restrict__ lse,
+                                                         const WsHeader* __restrict__ hdr) {
+  using E = Elem<T>;
+  constexpr int kVec = E::kVec;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  T* z = Z + row * ldz;
+  const int32_t y = targets[row];
+  const bool valid = (y != ign) && y >= 0 && static_cast<int64_t>(y) < Vg;
+  const float c = valid ? hdr->scale : 0.0f;
+  const float L = lse[row];
+  const int64_t jt = valid ? static_cast<int64_t>(y) - v0 : -1;  // may fall outside the shard
+  auto grad_of = [&](float x, int64_t j) -> float {
+    if (!valid) return 0.0f;
+    const float p = __builtin_amdgcn_exp2f((x - L) * kLog2e);
+    return c * (j == jt ? p - 1.0f : p);
+  };
+  const RowSplit rs = split_row(z, Vl);
+  uint4* zv = reinterpret_cast<uint4*>(z + rs.head);
+  for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+    float f[kVec];
+    E::unpack(zv[vi], f);
+    const int64_t j0 = rs.head + vi * kVec;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], j0 + i);
+    zv[vi] = E::pack(f);
+  }
+  if (tid < rs.head) E::store(z + tid, grad_of(E::load(z + tid), tid));
+  if (tid < Vl - rs.tail0) {
+    const int64_t j = rs.tail0 + tid;
+    E::store(z + j, grad_of(E::load(z + j), j));
+  }
+  if (tid < pad_cols) E::store(z + Vl + tid, 0.0f);
+}
+
+hipError_t launch_shard_grad(int dtype, void* Z, int64_t ldz, int64_t rows, int64_t V_local,
+                             int64_t pad_cols, int64_t vocab_start, int64_t V_global,
+                             const int32_t* targets, int32_t ign, const float* lse,
+                             const WsHeader* hdr, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(rows));
+  if (dtype == 1)
+    hipLaunchKernelGGL((k_shard_grad<uint16_t, 256>), grid, dim3(256), 0, s, static_cast<uint16_t*>(Z),
+                       ldz, V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr);
+  else
+    hipLaunchKernelGGL((k_shard_grad<float, 256>), grid, dim3(256), 0, s, static_cast<float*>(Z), ldz,
+                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr);
+  return hipGetLastError();
+}
+
+// Combine P shards' (max, sumexp, target logit) per row, shards in index
+// order, in float64: M = max m_k, lse = M + ln sum_k s_k exp(m_k - M),
+// z_y = sum_k t_k; loss row = lse - z_y for valid rows, 0 otherwise.
+__global__ __launch_bounds__(256) void k_combine_stats(const float* __restrict__ ms,
+                                                       const float* __restrict__ ss,
+                                                       const float* __restrict__ ts, int64_t P,
+                                                       int64_t N, const int32_t* __restrict__ targets,
+                                                       int32_t ign, int64_t Vg,
+                                                       float* __restrict__ lse_out,
+                                                       float* __restrict__ loss_rows) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (n >= N) return;
+  double M = -INFINITY;
+  for (int64_t k = 0; k < P; ++k) M = fmax(M, static_cast<double>(ms[k * N + n]));
+  double S = 0.0, t = 0.0;
+  for (int64_t k = 0; k < P; ++k) {
+    S += static_cast<double>(ss[k * N + n]) * exp(static_cast<double>(ms[k * N + n]) - M);
+    t += static_cast<double>(ts[k * N + n]);
+  }
+  const double lse = M + log(S);
+  const int32_t y = targets[n];
+  const bool valid = (y != ign) && y >= 0 && static_cast<int64_t>(y) < Vg;
+  if (lse_out != nullptr) lse_out[n] = static_cast<float>(lse);
+  loss_rows[n] = valid ? static_cast<float>(lse - t) : 0.0f;
+}
+
+hipError_t launch_combine_stats(const float* ms, const float* ss, const float* ts, int64_t P,
+                                int64_t N, const int32_t* targets, int32_t ign, int64_t V_global,
+                                float* lse, float* loss_rows, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine_stats, dim3(static_cast<unsigned>((N + 255) / 256)), dim3(256), 0, s,
+                     ms, ss, ts, P, N, targets, ign, V_global, lse, loss_rows);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ loss reduce
 
 // Sum of per-row losses in float64, in a fixed order independent of how the

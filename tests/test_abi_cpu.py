@@ -95,3 +95,36 @@ def test_ce_and_shard_argument_errors(B):
     assert L.flce_shard_stats(16, 16, None, 16, 4, 8, 10, 0, 10, B.BF16, -100, 16, 16, 16, 16, 8, 0,
                               None) == B.E_WORKSPACE
     assert L.flce_check_device_error(None, None) == B.E_INVALID_ARG
+
+
+def test_vocab_parallel_argument_errors(B):
+    L = B.lib()
+    # ce_combine_shard_stats(max, sumexp, target, P, N, targets, V_global, ign, red, lse, loss, ws, wsb, stream)
+    ok = dict(m=16, s=16, t=16, P=2, N=4, y=16, Vg=10, ign=-100, red=2, lse=16, loss=16, ws=16, wsb=1 << 20)
+
+    def comb(**kw):
+        a = dict(ok, **kw)
+        return L.ce_combine_shard_stats(a["m"], a["s"], a["t"], a["P"], a["N"], a["y"], a["Vg"], a["ign"],
+                                        a["red"], a["lse"], a["loss"], a["ws"], a["wsb"], None)
+    assert comb(P=0) == B.E_INVALID_ARG
+    assert comb(red=7) == B.E_INVALID_ARG
+    assert comb(loss=None) == B.E_INVALID_ARG
+    assert comb(m=None) == B.E_INVALID_ARG
+    assert comb(lse=40) == B.E_UNSUPPORTED           # misaligned
+    assert comb(wsb=8) == B.E_WORKSPACE
+
+    # flce_shard_backward(X, Ws, bs, y, N, H, Vl, v0, Vg, dtype, ign, red, lse, gX, gW, gb, ws, wsb, chunk, stream)
+    okb = dict(X=16, Ws=16, bs=None, y=16, N=4, H=8, Vl=10, v0=0, Vg=10, dt=B.BF16, ign=-100, red=2,
+               lse=16, gX=16, gW=16, gb=None, ws=16, wsb=1 << 30, chunk=0)
+
+    def bwd(**kw):
+        a = dict(okb, **kw)
+        return L.flce_shard_backward(a["X"], a["Ws"], a["bs"], a["y"], a["N"], a["H"], a["Vl"], a["v0"],
+                                     a["Vg"], a["dt"], a["ign"], a["red"], a["lse"], a["gX"], a["gW"],
+                                     a["gb"], a["ws"], a["wsb"], a["chunk"], None)
+    assert bwd(v0=5) == B.E_INVALID_ARG              # shard past the global vocabulary
+    assert bwd(lse=None) == B.E_INVALID_ARG
+    assert bwd(gb=16) == B.E_INVALID_ARG             # grad_bias without bias
+    assert bwd(Ws=None) == B.E_INVALID_ARG
+    assert bwd(H=12) == B.E_UNSUPPORTED
+    assert bwd(ws=None) == B.E_WORKSPACE

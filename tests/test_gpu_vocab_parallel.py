@@ -1,0 +1,225 @@
+"""GPU parity of the vocabulary-parallel path on one device: per-shard
+statistics -> combine -> per-shard backward, against the FP64 oracle's
+unsharded FLCE (the pages' claim: sharding the vocabulary changes nothing but
+the order of sums), plus each step against its own oracle function, edge
+cases, and the real shard shape of the 8B head split 8 ways."""
+
+import math
+
+import numpy as np
+import pytest
+
+from gpu_util import (TOL, check_max_rel, check_scalar, oracle_inputs, say, to_dev, to_host,
+                      torch_or_skip)
+from linear_cross_entropy_03_amd import synth
+from oracle import flce_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    torch_or_skip()
+    from linear_cross_entropy_03_amd import binding
+    binding.lib()
+    return binding
+
+
+def run_vp(B, inp, bounds, reduction, chunk_rows=0):
+    """The whole vocab-parallel pipeline on the GPU; returns host arrays
+    (loss, lse, grad_X = sum of partials, grad_W and grad_bias concatenated)."""
+    import torch
+    dt = inp["dtype"]
+    V = inp["V"]
+    X = to_dev(inp["X"], dt)
+    y = to_dev(inp["targets"], "i32")
+    shards = list(zip(bounds[:-1], bounds[1:]))
+    Ws = [to_dev(np.ascontiguousarray(inp["W"][a:c]), dt) for a, c in shards]
+    bs = [None if inp["bias"] is None else to_dev(np.ascontiguousarray(inp["bias"][a:c]), dt)
+          for a, c in shards]
+    stats = [B.flce_shard_stats(X, W, y, a, V, bias_shard=b, chunk_rows=chunk_rows)
+             for (a, _), W, b in zip(shards, Ws, bs)]
+    ms, ss, ts = (torch.stack([st[i] for st in stats]).contiguous() for i in range(3))
+    loss, lse = B.ce_combine_shard_stats(ms, ss, ts, y, V, reduction=reduction)
+    gX = None
+    gW, gb = [], []
+    for (a, _), W, b in zip(shards, Ws, bs):
+        px, pw, pb = B.flce_shard_backward(X, W, y, lse, a, V, bias_shard=b, reduction=reduction,
+                                           chunk_rows=chunk_rows)
+        gX = px if gX is None else gX + px
+        gW.append(pw)
+        if pb is not None:
+            gb.append(pb)
+    torch.cuda.synchronize()
+    return (to_host(loss), to_host(lse), to_host(gX), to_host(torch.cat(gW)),
+            to_host(torch.cat(gb)) if gb else None)
+
+
+@pytest.mark.parametrize("dtype,reduction,bias,chunk", [
+    ("bf16", "mean", False, 0), ("bf16", "sum", True, 256), ("f32", "none", True, 0),
+    ("f32", "mean", False, 128)])
+def test_vocab_parallel_matches_flce(B, dtype, reduction, bias, chunk):
+    """Three uneven shards of a ragged vocabulary (V 3001) reproduce the
+    unsharded FLCE loss and gradients."""
+    N, H, V = (700, 128, 3001) if dtype == "bf16" else (300, 64, 1001)
+    inp = synth.make_flce_inputs(N, H, V, dtype, bias_std=0.05 if bias else None,
+                                 ignore_frac=0.1, seed=31)
+    inp["targets"][5] = V + 3   # a bad target: ignored, reported
+    bounds = [0, V // 3 + 7, 2 * V // 3 - 5, V]
+    say("vocab-parallel", dtype, reduction, "bias" if bias else "", "chunk", chunk, bounds)
+    loss, lse, gX, gW, gb = run_vp(B, inp, bounds, reduction, chunk)
+    X, W, b, y = oracle_inputs(inp)
+    ref_loss, ref_g, info = O.flce(X, W, y, bias=b, reduction=reduction)
+    t = TOL[dtype]
+    Z = X @ W.T + (0 if b is None else b)
+    check_max_rel(lse, O.logsumexp_rows(Z), t["loss"], "row lse")
+    if reduction == "none":
+        check_max_rel(loss, ref_loss, t["loss"], "loss rows")
+    else:
+        check_scalar(loss, ref_loss, t["loss"])
+    check_max_rel(gX, ref_g["X"], t["grad"], "grad_X (sum of shard partials)")
+    check_max_rel(gW, ref_g["W"], t["grad"], "grad_W (concatenated shards)")
+    if bias:
+        check_max_rel(gb, ref_g["bias"], t["grad"], "grad_bias (concatenated shards)")
+    ignored = (y == -100) | (y >= V)
+    assert np.all(gX[ignored] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_shard_backward_given_lse(B, dtype):
+    """One shard's backward against the oracle's, with the oracle's global lse
+    (rounded to float32, as the GPU receives it) as the input."""
+    import torch
+    N, H, V = (517, 96, 2500) if dtype == "bf16" else (257, 32, 900)
+    inp = synth.make_flce_inputs(N, H, V, dtype, bias_std=0.1, ignore_frac=0.1, seed=32)
+    X, W, b, y = oracle_inputs(inp)
+    lse32 = O.logsumexp_rows(X @ W.T + b).astype(np.float32)
+    a, c = V // 4, V // 4 + V // 3
+    ref = O.flce_shard_backward(X, W[a:c], y, a, V, lse32.astype(np.float64), bias_shard=b[a:c],
+                                reduction="mean")
+    say("shard backward given lse", dtype, N, H, V, a, c)
+    dt = inp["dtype"]
+    gx, gw, gb = B.flce_shard_backward(
+        to_dev(inp["X"], dt), to_dev(np.ascontiguousarray(inp["W"][a:c]), dt), to_dev(y.astype(np.int32), "i32"),
+        torch.from_numpy(lse32).cuda(), a, V, bias_shard=to_dev(np.ascontiguousarray(inp["bias"][a:c]), dt),
+        reduction="mean")
+    torch.cuda.synchronize()
+    t = TOL[dtype]
+    check_max_rel(to_host(gx), ref[0], t["grad"], "grad_X partial")
+    check_max_rel(to_host(gw), ref[1], t["grad"], "grad_W shard")
+    check_max_rel(to_host(gb), ref[2], t["grad"], "grad_bias shard")
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_combine_against_oracle(B, reduction):
+    import torch
+    rng = np.random.default_rng(33)
+    P, N, V = 5, 3000, 50000
+    m = (rng.standard_normal((P, N)) * 3).astype(np.float32)
+    s = rng.uniform(1.0, 500.0, (P, N)).astype(np.float32)
+    t = np.zeros((P, N), np.float32)
+    y = rng.integers(0, V, N).astype(np.int32)
+    y[rng.choice(N, 300, replace=False)] = -100
+    y[7] = V   # bad
+    owner = rng.integers(0, P, N)
+    t[owner, np.arange(N)] = rng.standard_normal(N).astype(np.float32)
+    t[:, y == -100] = 0.0
+    t[:, 7] = 0.0
+    lse_ref, zt_ref = O.combine_shard_stats([(m[k], s[k], t[k]) for k in range(P)])
+    loss_ref, rows_ref, _ = O.shard_loss(lse_ref, zt_ref, y, V, reduction=reduction)
+    ws = torch.empty(B.ce_workspace_bytes(N, V), dtype=torch.uint8, device="cuda")
+    say("combine", reduction, P, N)
+    loss, lse = B.ce_combine_shard_stats(torch.from_numpy(m).cuda(), torch.from_numpy(s).cuda(),
+                                         torch.from_numpy(t).cuda(), torch.from_numpy(y).cuda(), V,
+                                         reduction=reduction, workspace=ws)
+    torch.cuda.synchronize()
+    check_max_rel(to_host(lse), lse_ref, 1e-6, "lse")
+    if reduction == "none":
+        check_max_rel(to_host(loss), rows_ref, 1e-6, "loss rows")
+    else:
+        check_scalar(to_host(loss), loss_ref, 1e-6)
+    assert B.flce_check_device_error(ws) == B.E_TARGET
+
+
+def test_vocab_parallel_edge_cases(B):
+    import torch
+    H, V = 64, 1000
+    W = torch.randn(V // 2, H, device="cuda").to(torch.bfloat16)
+    # No rows: the shard's head gradient is zero, the loss is 0.
+    X0 = torch.empty(0, H, device="cuda", dtype=torch.bfloat16)
+    y0 = torch.empty(0, device="cuda", dtype=torch.int32)
+    lse0 = torch.empty(0, device="cuda")
+    say("vocab-parallel N=0")
+    gx, gw, _ = B.flce_shard_backward(X0, W, y0, lse0, 0, V)
+    torch.cuda.synchronize()
+    assert gx.shape == (0, H) and float(gw.abs().max()) == 0.0
+    e = torch.empty(1, 0, device="cuda")
+    loss, _ = B.ce_combine_shard_stats(e, e, e, y0, V, reduction="mean")
+    torch.cuda.synchronize()
+    assert float(loss[0]) == 0.0
+    # Every row ignored: zero gradients, zero loss.
+    N = 300
+    X = torch.randn(N, H, device="cuda").to(torch.bfloat16)
+    y = torch.full((N,), -100, device="cuda", dtype=torch.int32)
+    m, s, t = B.flce_shard_stats(X, W, y, V // 2, V)
+    loss, lse = B.ce_combine_shard_stats(m[None].contiguous(), s[None].contiguous(),
+                                         t[None].contiguous(), y, V, reduction="mean")
+    gx, gw, _ = B.flce_shard_backward(X, W, y, lse, V // 2, V)
+    torch.cuda.synchronize()
+    assert float(loss[0]) == 0.0
+    assert float(gx.abs().max()) == 0.0 and float(gw.abs().max()) == 0.0
+
+
+@pytest.mark.timeout(300)
+def test_shard_of_8b_head_full_size(B):
+    """The real shard shape: Llama-3-8B head (N 32768, H 4096, V 128256)
+    split 8 ways, shard 3 (V_local 16032), Zipf targets, sum reduction. The
+    global lse is an input of the shard backward; here it is the oracle's
+    float64 lse over this shard plus ln 8 (as if the 8 shards carried equal
+    mass), rounded to float32 for both sides. Checked on sampled token rows
+    (shard statistics, grad_X partial) and sampled vocabulary rows (grad_W)."""
+    import torch
+    cfg = synth.WORKLOADS["llama8b_head_bf16"]
+    say("shard full size: generating inputs")
+    inp = synth.make_workload("llama8b_head_bf16")
+    N, H, V = cfg["N"], cfg["H"], cfg["V"]
+    Vl = V // 8
+    a = 3 * Vl
+    X = np.asarray(inp["X_f32"], np.float64)
+    Ws = np.asarray(inp["W_f32"][a:a + Vl], np.float64)
+    y = inp["targets"]
+    say("shard full size: oracle shard statistics over every row")
+    m, s, t = O.flce_shard_stats(X, Ws, y, a, V)
+    lse32 = (m + np.log(s) + math.log(8.0)).astype(np.float32)
+    Xd = to_dev(inp["X"], "bf16")
+    Wd = to_dev(np.ascontiguousarray(inp["W"][a:a + Vl]), "bf16")
+    yd = to_dev(y, "i32")
+    say("shard full size: GPU shard stats and backward", B.flce_plan(N, H, Vl, B.BF16))
+    gm, gs, gt = B.flce_shard_stats(Xd, Wd, yd, a, V)
+    gx, gw, _ = B.flce_shard_backward(Xd, Wd, yd, torch.from_numpy(lse32).cuda(), a, V,
+                                      reduction="sum", grad_bias=False)
+    torch.cuda.synchronize()
+    tol = TOL["bf16"]
+    rng = np.random.default_rng(34)
+    rows = np.unique(np.concatenate([rng.choice(N, 24, replace=False), [0, N - 1],
+                                     np.flatnonzero((y >= a) & (y < a + Vl))[:3],
+                                     np.flatnonzero(y == -100)[:2]]))
+    # The statistics come from bf16-rounded logits: the shard lse (m + ln s)
+    # is held to the loss bar, the raw target logit to bf16's half ulp.
+    glse = to_host(gm)[rows] + np.log(to_host(gs)[rows])
+    check_max_rel(glse, m[rows] + np.log(s[rows]), tol["loss"], "sampled shard lse")
+    check_max_rel(to_host(gt)[rows], t[rows], 2.0 ** -8, "sampled target logits")
+    lse = lse32.astype(np.float64)
+    gx_ref, _, _ = O.flce_shard_backward(X[rows], Ws, y[rows], a, V, lse[rows], reduction="sum")
+    check_max_rel(to_host(gx, f64=False)[rows].astype(np.float64), gx_ref, tol["grad"],
+                  "sampled grad_X partial rows")
+    # grad_W_shard[j] = sum_n dZ[n, j] x_n over every row (sum reduction).
+    counts = np.bincount(y[(y >= a) & (y < a + Vl)] - a, minlength=Vl)
+    cols = np.unique(np.concatenate([[int(counts.argmax())], rng.choice(Vl, 5, replace=False)]))
+    valid = (y != -100) & (y >= 0) & (y < V)
+    Zc = X @ Ws[cols].T                                 # [N, len(cols)]
+    dZ = np.exp(Zc - lse[:, None]) - ((a + cols)[None, :] == y[:, None])
+    dZ[~valid] = 0.0
+    gw_ref = dZ.T @ X
+    check_max_rel(to_host(gw, f64=False)[cols].astype(np.float64), gw_ref, tol["grad"],
+                  "sampled grad_W shard rows")
