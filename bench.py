@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-ce", action="store_true", help="skip the standalone CE measurement")
+    ap.add_argument("--no-vp", action="store_true",
+                    help="skip the vocabulary-parallel shard measurement")
     ap.add_argument("--profile-step", action="store_true",
                     help="for rocprofv3 counter runs: a 1 GiB device copy (counter calibration), "
                          "then one warmup and one timed FLCE step; prints nothing else")
@@ -232,6 +234,76 @@ def bench_ce(torch, B, reps=40):
     }
 
 
+def bench_vocab_parallel(torch, B, X, W, y, cfg, reps=5):
+    """The vocabulary-parallel path at a real shard shape: the 8B head split 8
+    ways, shard 3 (V_local 16032). One rank's work per step: shard statistics
+    (logits GEMM + statistics), the combine of 8 shards' statistics (the same
+    statistics replicated, so only the arithmetic is real), then the shard's
+    backward (logits GEMM again, dZ from the global lse, grad_X partial and
+    grad_W shard). GEMM work per step: 4 x 2 x N x H x V_local flop."""
+    N, H, V = cfg["N"], cfg["H"], cfg["V"]
+    P = 8
+    Vl = V // P
+    a = 3 * Vl
+    Ws = W[a:a + Vl]
+    stream = torch.cuda.current_stream()
+    m, s_, t = (torch.empty(N, device="cuda") for _ in range(3))
+    ms, ss, ts = (torch.empty(P, N, device="cuda") for _ in range(3))
+    lse = torch.empty(N, device="cuda")
+    loss = torch.empty(1, device="cuda")
+    gX = torch.empty(N, H, device="cuda")
+    gW = torch.empty(Vl, H, device="cuda")
+    ws = torch.empty(B.flce_workspace_bytes(N, H, Vl, B.BF16), dtype=torch.uint8, device="cuda")
+    cws = torch.empty(B.ce_workspace_bytes(N, V), dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def once(record):
+        if record:
+            ev[0].record(stream)
+        B.flce_shard_stats(X, Ws, y, a, V, out=(m, s_, t), workspace=ws, stream=stream)
+        for k in range(P):
+            ms[k].copy_(m); ss[k].copy_(s_); ts[k].copy_(t)
+        if record:
+            ev[1].record(stream)
+        B.ce_combine_shard_stats(ms, ss, ts, y, V, reduction=cfg["reduction"], row_lse=lse, loss=loss,
+                                 workspace=cws, stream=stream)
+        if record:
+            ev[2].record(stream)
+        B.flce_shard_backward(X, Ws, y, lse, a, V, reduction=cfg["reduction"], grad_X=gX, grad_W=gW,
+                              grad_bias=False, workspace=ws, stream=stream)
+        if record:
+            ev[3].record(stream)
+
+    once(False)
+    torch.cuda.synchronize()
+    tot = [0.0, 0.0, 0.0]
+    B.flce_timing_reset()
+    B.flce_timing_enable(True)
+    for _ in range(reps):
+        once(True)
+        torch.cuda.synchronize()
+        for i in range(3):
+            tot[i] += ev[i].elapsed_time(ev[i + 1])
+    B.flce_timing_enable(False)
+    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm"))
+    row_ms, row_n = B.flce_timing_read("row_ce")
+    B.flce_timing_reset()
+    stats_ms, comb_ms, bwd_ms = (x / reps for x in tot)
+    step_ms = stats_ms + comb_ms + bwd_ms
+    gemm_flops = 4 * 2.0 * N * H * Vl
+    return {
+        "workload": f"llama8b_head_bf16 vocabulary shard 3 of {P} (N {N}, H {H}, V_local {Vl}, "
+                    f"V {V}, {cfg['reduction']})",
+        "ms_shard_stats": stats_ms, "ms_combine": comb_ms, "ms_shard_backward": bwd_ms,
+        "ms_per_step": step_ms, "tokens_per_s": N / (step_ms * 1e-3),
+        "gemm_tflops": gemm_flops / (gemm_ms / reps * 1e-3) / 1e12,
+        "gemm_frac": gemm_flops / (gemm_ms / reps * 1e-3) / PEAK_BF16_FLOPS,
+        "row_kernels_ms_per_step": row_ms / reps, "row_kernel_launches_per_step": row_n / reps,
+        "note": "the shard-stats step's 8 statistics copies are replicated on the device; "
+                "no collective runs (one GPU)",
+    }
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -376,6 +448,11 @@ def main():
         "kernels": kernels,
         "loss": float(loss.item()),
     }
+    if not args.no_vp:
+        log("vocabulary-parallel shard")
+        del ws
+        result["vocab_parallel"] = bench_vocab_parallel(torch, B, X, W, y, cfg)
+        ws = None
     if not args.no_ce:
         log("standalone CE")
         del ws
