@@ -24,9 +24,12 @@
  *     and row-major (the last index is contiguous). Base pointers must be
  *     16-byte aligned. The library never allocates or frees device memory:
  *     scratch space is the caller's `workspace`.
- *   - Element type of X, W, bias and logits: FLCE_F32 (float) or FLCE_BF16
- *     (bfloat16 bit patterns, uint16). All of a call's floating inputs share
- *     one type. Losses, statistics and FLCE gradients are float32.
+ *   - Element type of X, W, bias and logits: FLCE_F32 (float), FLCE_BF16
+ *     (bfloat16 bit patterns, uint16) or FLCE_F16 (IEEE half; the DeepSpeed
+ *     vocab-parallel CE page tests FP32/FP16/BF16 logits). All of a call's
+ *     floating inputs share one type; 16-bit types need H % 8 == 0. Chunk
+ *     logits and dlogits are stored in that type; losses, statistics and
+ *     FLCE gradients are float32.
  *   - Targets are int32 class ids. A row is ignored iff its target equals
  *     ignore_index. A target that is not ignore_index and lies outside
  *     [0, V) is a device-detected error: the row is treated as ignored (zero
@@ -60,7 +63,7 @@ typedef enum {
   FLCE_E_HIP = 5          /* a HIP runtime call or kernel launch failed */
 } flce_status;
 
-typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1 } flce_dtype;
+typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1, FLCE_F16 = 2 } flce_dtype;
 
 typedef enum {
   FLCE_REDUCTION_NONE = 0,

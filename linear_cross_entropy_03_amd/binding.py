@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblce03.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "flce.h")
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 OK, E_INVALID_ARG, E_WORKSPACE, E_UNSUPPORTED, E_TARGET, E_HIP = range(6)
 TIMING_KINDS = {"logits_gemm": 0, "row_ce": 1, "grad_x_gemm": 2, "grad_w_gemm": 3, "other": 4}
@@ -98,7 +98,9 @@ def _dtype_code(t):
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return F16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or float16")
 
 
 def _ptr(t, name, dtype=None):

@@ -26,7 +26,14 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-inline size_t elem_bytes(int dtype) { return dtype == FLCE_BF16 ? 2 : 4; }
+inline size_t elem_bytes(int dtype) { return dtype == FLCE_F32 ? 4 : 2; }
+inline bool is16(int dtype) { return dtype == FLCE_BF16 || dtype == FLCE_F16; }
+inline bool valid_dtype(int dtype) { return dtype == FLCE_F32 || is16(dtype); }
+
+// The GEMM for the call's element type.
+inline hipError_t gemm_for(int dtype, const GemmDesc& d, hipStream_t s) {
+  return is16(dtype) ? launch_gemm_16(d, dtype == FLCE_F16, s) : launch_gemm_f32(d, s);
+}
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxRows = int64_t(1) << 31;     // grid.x of the row kernels
@@ -67,7 +74,7 @@ int choose_dx_splits(int64_t chunk, int64_t H, int64_t V) {
 
 bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, Plan* p) {
   if (N < 0 || H <= 0 || V <= 0 || N >= kMaxRows || H >= kMaxDim || V >= kMaxDim) return false;
-  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return false;
+  if (!valid_dtype(dtype)) return false;
   if (chunk_rows < 0) return false;
   const size_t e = elem_bytes(dtype);
   const int64_t ldz = round_up(V, 8);
@@ -91,7 +98,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
   }
   p->chunk = chunk;
   p->ldz = ldz;
-  p->dx_splits = dtype == FLCE_BF16 ? choose_dx_splits(chunk, H, V) : 1;
+  p->dx_splits = is16(dtype) ? choose_dx_splits(chunk, H, V) : 1;
   size_t off = align_up(sizeof(WsHeader));
   p->off_rows = off;
   off += align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float));
@@ -190,7 +197,7 @@ size_t ce_workspace_bytes(int64_t N, int64_t V) {
 }
 
 static int validate_common(int dtype, int reduction) {
-  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_E_INVALID_ARG;
+  if (!valid_dtype(dtype)) return FLCE_E_INVALID_ARG;
   if (reduction < FLCE_REDUCTION_NONE || reduction > FLCE_REDUCTION_MEAN) return FLCE_E_INVALID_ARG;
   return FLCE_OK;
 }
@@ -210,7 +217,7 @@ int flce_forward_backward(const void* X, const void* W, const void* bias, const 
   const void* ptrs[] = {X, W, bias, targets, loss, grad_X, grad_W, grad_bias, workspace};
   for (const void* q : ptrs)
     if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
-  if (dtype == FLCE_BF16 && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  if (is16(dtype) && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
   Plan p;
   if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
@@ -223,7 +230,7 @@ int flce_forward_backward(const void* X, const void* W, const void* bias, const 
   float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   const size_t e = elem_bytes(dtype);
   const bool need_grad = grad_X != nullptr || grad_W != nullptr || grad_bias != nullptr;
-  auto gemm = dtype == FLCE_BF16 ? launch_gemm_bf16 : launch_gemm_f32;
+  auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
 
   LCE_TRY(timed(kKindOther, s, [&] {
     return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
@@ -331,7 +338,7 @@ int ce_shard_stats(const void* logits_shard, const int32_t* targets, int64_t N, 
                    int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
                    float* row_max, float* row_sumexp, float* row_target_logit, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_E_INVALID_ARG;
+  if (!valid_dtype(dtype)) return FLCE_E_INVALID_ARG;
   if (N < 0 || V_local <= 0 || vocab_start < 0 || V_global < vocab_start + V_local)
     return FLCE_E_INVALID_ARG;
   if (N > 0 && (logits_shard == nullptr || targets == nullptr || row_max == nullptr ||
@@ -359,7 +366,7 @@ int flce_shard_stats(const void* X, const void* W_shard, const void* bias_shard,
                      int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
                      float* row_max, float* row_sumexp, float* row_target_logit, void* workspace,
                      size_t workspace_bytes, int64_t chunk_rows, void* stream) {
-  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_E_INVALID_ARG;
+  if (!valid_dtype(dtype)) return FLCE_E_INVALID_ARG;
   if (N < 0 || H <= 0 || V_local <= 0 || vocab_start < 0 || V_global < vocab_start + V_local ||
       chunk_rows < 0)
     return FLCE_E_INVALID_ARG;
@@ -371,7 +378,7 @@ int flce_shard_stats(const void* X, const void* W_shard, const void* bias_shard,
   const void* ptrs[] = {X, W_shard, bias_shard, targets, row_max, row_sumexp, row_target_logit, workspace};
   for (const void* q : ptrs)
     if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
-  if (dtype == FLCE_BF16 && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  if (is16(dtype) && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
   Plan p;
   if (!make_plan(N, H, V_local, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
@@ -381,7 +388,7 @@ int flce_shard_stats(const void* X, const void* W_shard, const void* bias_shard,
   WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
   void* zbuf = ws + p.off_chunk;
   const size_t e = elem_bytes(dtype);
-  auto gemm = dtype == FLCE_BF16 ? launch_gemm_bf16 : launch_gemm_f32;
+  auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
   LCE_TRY(timed(kKindOther, s, [&] {
     return launch_count_targets(targets, N, V_global, ignore_index, FLCE_REDUCTION_SUM, hdr, s);
   }));
@@ -456,7 +463,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
                         grad_bias_shard, workspace};
   for (const void* q : ptrs)
     if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
-  if (dtype == FLCE_BF16 && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  if (is16(dtype) && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
   Plan p;
   if (!make_plan(N, H, V_local, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
@@ -467,7 +474,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
   void* zbuf = ws + p.off_chunk;
   float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   const size_t e = elem_bytes(dtype);
-  auto gemm = dtype == FLCE_BF16 ? launch_gemm_bf16 : launch_gemm_f32;
+  auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
 
   // Validity and the mean's N_valid are judged against the whole vocabulary.
   LCE_TRY(timed(kKindOther, s, [&] {

@@ -42,7 +42,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xFFFFu);
 }
 
-// Element access for the two storage types.
+// ---------------------------------------------------------------- fp16 bits
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Storage tag of an IEEE half element (2 bytes, like the bf16 uint16_t).
+struct Half {
+  uint16_t bits;
+};
+static_assert(sizeof(Half) == 2, "half storage is 2 bytes");
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+// Two floats -> packed half pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// Element access for the storage types: float, bf16 (uint16_t bits) and
+// fp16 (Half).
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int kVec = 4;  // elements per 16-byte vector
@@ -68,6 +88,26 @@ template <> struct Elem<uint16_t> {
   __device__ static uint4 pack(const float* f) {
     return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+  }
+};
+
+template <> struct Elem<Half> {
+  static constexpr int kVec = 8;
+  __device__ static float load(const Half* p) { return f16_to_f32(p->bits); }
+  __device__ static void store(Half* p, float v) {
+    p->bits = static_cast<uint16_t>(pack_f16x2(v, 0.0f) & 0xFFFFu);
+  }
+  __device__ static void unpack(const uint4& u, float* f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = f16_to_f32(static_cast<uint16_t>(w[i] & 0xFFFFu));
+      f[2 * i + 1] = f16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+    }
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]),
+                      pack_f16x2(f[4], f[5]), pack_f16x2(f[6], f[7]));
   }
 };
 
@@ -155,7 +195,8 @@ struct GemmDesc {
   int64_t split_stride;
 };
 
-hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s);
+// 16-bit inputs (bf16, or fp16 when f16 is set), fp32 accumulation.
+hipError_t launch_gemm_16(const GemmDesc& d, bool f16, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s);
 
 hipError_t launch_count_targets(const int32_t* targets, int64_t n, int64_t V,

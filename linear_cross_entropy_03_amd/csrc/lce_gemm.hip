@@ -5,14 +5,17 @@
 //   grad_X   dX_c = dZ_c W          A = dZ_c (k-major)  B = W  (n-major)
 //   grad_W   dW  += dZ_c^T X_c      A = dZ_c (m-major)  B = X_c (n-major)
 //
-// bf16 path: one MFMA kernel template (namespace mfma2) for all three,
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; see the comment there.
+// 16-bit path: one MFMA kernel template (namespace mfma2) for all three,
+// v_mfma_f32_32x32x16_bf16 (or _f16 for IEEE half inputs, the DeepSpeed
+// vocab-parallel CE page's FP16 case) with fp32 accumulation; see the comment
+// there.
 // fp32 path: a plain LDS-tiled VALU kernel (namespace valu).
 #include "lce_common.h"
 
 namespace lce {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 namespace tiles {
@@ -258,7 +261,7 @@ __device__ __forceinline__ void load_frags(Frags<kFJ>& f, const Operand<kAK, kW>
 // One 16-wide k step: read the next fragments `nf` from LDS and run the
 // 4 x kFJ MFMAs on `f`; the scheduler is told to interleave the LDS reads one
 // per MFMA so neither pipe waits on a burst of the other.
-template <int kHalf, int kFJ, bool kAK, bool kBKm, int kW>
+template <int kTy, int kHalf, int kFJ, bool kAK, bool kBKm, int kW>
 __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][kFJ], const Frags<kFJ>& f,
                                          Frags<kFJ>& nf, const Operand<kAK, kW>& A,
                                          const Operand<kBKm, kW>& B, const uint16_t* src,
@@ -273,7 +276,12 @@ __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][kFJ], const Frags<kF
 #pragma unroll
     for (int j = 0; j < kFJ; ++j)
       // B first: each 32x32 result block is C^T, so a lane holds 4 consecutive n.
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+      if constexpr (kTy == 1)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, f.b[j]),
+                                                           __builtin_bit_cast(f16x8_t, f.a[i]),
+                                                           acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   constexpr int kReads = (kAK ? 4 : 8) + (kBKm ? kFJ : 2 * kFJ);  // LDS reads per step
 #pragma unroll
   for (int t = 0; t < 4 * kFJ; ++t) {
@@ -290,20 +298,20 @@ __device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][kFJ], const Frags<kF
 // second). Buffer (s + 3) % 4 last held stage s - 1, whose reads all finished
 // before the previous barrier. Loads past the end of K read zeros, so every
 // stage issues the same number of loads.
-template <int kB, int kFJ, bool kAK, bool kBKm, int kW>
+template <int kTy, int kB, int kFJ, bool kAK, bool kBKm, int kW>
 __device__ __forceinline__ void stage_iter(f32x16_t (&acc)[4][kFJ], Frags<kFJ>& f0, Frags<kFJ>& f1,
                                            const Operand<kAK, kW>& A, const Operand<kBKm, kW>& B,
                                            int row0, int col0, int64_t k0, int64_t kend) {
   constexpr int kPerA = Operand<kAK, kW>::kInstr, kPer = kPerA + Operand<kBKm, kW>::kInstr;
   uint16_t* dst = stage_buf<(kB + 3) & 3>();
-  mma_step<0>(acc, f0, f1, A, B, stage_buf<kB>(), row0, col0, 1, dst, k0, kend);
+  mma_step<kTy, 0>(acc, f0, f1, A, B, stage_buf<kB>(), row0, col0, 1, dst, k0, kend);
   // Stage s + 1 has landed once only the loads issued after it (stage s + 2
   // and the A half of stage s + 3) are in flight. The count holds because the
   // loop issues no other vector memory instruction: no register spills, which
   // the launcher checks.
   wait_vmcnt<kPer + kPerA>();
   block_sync();
-  mma_step<1>(acc, f1, f0, A, B, stage_buf<(kB + 1) & 3>(), row0, col0, 0, dst, k0, kend);
+  mma_step<kTy, 1>(acc, f1, f0, A, B, stage_buf<(kB + 1) & 3>(), row0, col0, 0, dst, k0, kend);
 }
 
 // Output through LDS. The MFMA result layout gives each lane 4 consecutive
@@ -333,8 +341,9 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int kFJ>
-__device__ __forceinline__ void epilogue_bf16(const f32x16_t (&acc)[4][kFJ], const GemmDesc& d,
+// 16-bit logits (+ bias): kTy 0 bf16, 1 fp16.
+template <int kTy, int kFJ>
+__device__ __forceinline__ void epilogue_16(const f32x16_t (&acc)[4][kFJ], const GemmDesc& d,
                                               int64_t m0, int64_t n0, int row0, int col0, int wave) {
   static_assert(kFJ == 2, "64 output columns per wave");
   const int lane = threadIdx.x & 63, l32 = lane & 31, lhi = lane >> 5;
@@ -355,11 +364,12 @@ __device__ __forceinline__ void epilogue_bf16(const f32x16_t (&acc)[4][kFJ], con
             const int64_t n = n0 + col0 + j * 32 + q * 8 + lhi * 4;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (n + e < d.N) v[e] += bf16_to_f32(bias[n + e]);
+              if (n + e < d.N) v[e] += kTy == 1 ? f16_to_f32(bias[n + e]) : bf16_to_f32(bias[n + e]);
           }
           const int slot = j * 4 + q;
           *reinterpret_cast<uint2*>(reg + r * 128 + ((slot ^ ((r >> 1) & 7)) << 4) + lhi * 8) =
-              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+              kTy == 1 ? make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]))
+                       : make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
     }
     wave_lds_fence();
@@ -441,7 +451,7 @@ __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], cons
   }
 }
 
-template <bool kAK, bool kBKm, int kEpi, int kWN>
+template <bool kAK, bool kBKm, int kEpi, int kWN, int kTy>
 __global__ __launch_bounds__(64 * kWM * kWN) __attribute__((amdgpu_waves_per_eu(kWN / 2, kWN / 2)))
 void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
   constexpr int kWaves = kWM * kWN;
@@ -495,28 +505,28 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
     int s = 0;
     for (; s + 4 <= ksteps; s += 4) {
       const int64_t k3 = kbeg + static_cast<int64_t>(s + 3) * kBK;
-      stage_iter<0>(acc, f0, f1, opA, opB, row0, col0, k3, kend);
-      stage_iter<1>(acc, f0, f1, opA, opB, row0, col0, k3 + kBK, kend);
-      stage_iter<2>(acc, f0, f1, opA, opB, row0, col0, k3 + 2 * kBK, kend);
-      stage_iter<3>(acc, f0, f1, opA, opB, row0, col0, k3 + 3 * kBK, kend);
+      stage_iter<kTy, 0>(acc, f0, f1, opA, opB, row0, col0, k3, kend);
+      stage_iter<kTy, 1>(acc, f0, f1, opA, opB, row0, col0, k3 + kBK, kend);
+      stage_iter<kTy, 2>(acc, f0, f1, opA, opB, row0, col0, k3 + 2 * kBK, kend);
+      stage_iter<kTy, 3>(acc, f0, f1, opA, opB, row0, col0, k3 + 3 * kBK, kend);
     }
     const int64_t k3 = kbeg + static_cast<int64_t>(s + 3) * kBK;
-    if (s < ksteps) stage_iter<0>(acc, f0, f1, opA, opB, row0, col0, k3, kend);
-    if (s + 1 < ksteps) stage_iter<1>(acc, f0, f1, opA, opB, row0, col0, k3 + kBK, kend);
-    if (s + 2 < ksteps) stage_iter<2>(acc, f0, f1, opA, opB, row0, col0, k3 + 2 * kBK, kend);
+    if (s < ksteps) stage_iter<kTy, 0>(acc, f0, f1, opA, opB, row0, col0, k3, kend);
+    if (s + 1 < ksteps) stage_iter<kTy, 1>(acc, f0, f1, opA, opB, row0, col0, k3 + kBK, kend);
+    if (s + 2 < ksteps) stage_iter<kTy, 2>(acc, f0, f1, opA, opB, row0, col0, k3 + 2 * kBK, kend);
     // Loads past the end are still in flight; they write this workgroup's LDS.
     wait_vmcnt<0>();
   }
 
   // Every wave is done with the stage buffers; they now stage the output.
   block_sync();
-  if constexpr (kEpi == kEpiLogits) epilogue_bf16<kFJ>(acc, d, m0, n0, row0, col0, wave);
+  if constexpr (kEpi == kEpiLogits) epilogue_16<kTy, kFJ>(acc, d, m0, n0, row0, col0, wave);
   else epilogue_f32<kEpi, kFJ>(acc, d, m0, n0, sp, row0, col0, wave);
 }
 
 }  // namespace mfma2
 
-template <bool kAK, bool kBKm, int kEpi, int kWN>
+template <bool kAK, bool kBKm, int kEpi, int kWN, int kTy>
 static hipError_t launch_mfma_v2(const GemmDesc& d, hipStream_t s) {
   using namespace mfma2;
   const int64_t tiles_m = (d.M + kBM - 1) / kBM, tiles_n = (d.N + kBM - 1) / kBM;
@@ -524,7 +534,7 @@ static hipError_t launch_mfma_v2(const GemmDesc& d, hipStream_t s) {
   int64_t k_per = (d.K + splits - 1) / splits;
   k_per = (k_per + kBK - 1) / kBK * kBK;
   const int64_t blocks = tiles_m * tiles_n * splits;
-  auto kern = k_gemm2<kAK, kBKm, kEpi, kWN>;
+  auto kern = k_gemm2<kAK, kBKm, kEpi, kWN, kTy>;
   // Spill stores would be counted by the loop's explicit vmcnt waits.
   static int spills = -1;
   if (spills < 0) {
@@ -541,18 +551,23 @@ static hipError_t launch_mfma_v2(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool kAK, bool kBKm, int kEpi>
-static hipError_t launch_mfma(const GemmDesc& d, hipStream_t s) {
-  return launch_mfma_v2<kAK, kBKm, kEpi, 4>(d, s);  // 2 x 4 waves
+template <int kTy>
+static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
+  // 2 x 4 waves
+  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits)
+    return launch_mfma_v2<true, true, kEpiLogits, 4, kTy>(d, s);
+  if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
+    return launch_mfma_v2<true, false, kEpiStoreF32, 4, kTy>(d, s);
+  if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
+    return launch_mfma_v2<false, false, kEpiStoreF32, 4, kTy>(d, s);
+  if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
+    return launch_mfma_v2<false, false, kEpiAccumF32, 4, kTy>(d, s);
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
+hipError_t launch_gemm_16(const GemmDesc& d, bool f16, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
-  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits) return launch_mfma<true, true, kEpiLogits>(d, s);
-  if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32) return launch_mfma<true, false, kEpiStoreF32>(d, s);
-  if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32) return launch_mfma<false, false, kEpiStoreF32>(d, s);
-  if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32) return launch_mfma<false, false, kEpiAccumF32>(d, s);
-  return hipErrorInvalidValue;
+  return f16 ? launch_mfma_ty<1>(d, s) : launch_mfma_ty<0>(d, s);
 }
 
 // ------------------------------------------------------------- fp32 VALU

@@ -245,6 +245,12 @@ hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* G, int64_t
                : row_ce_dispatch<uint16_t, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign,
                                                 hdr, loss_rows, s);
   }
+  if (dtype == 2) {
+    return big ? row_ce_dispatch<Half, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
+                                             loss_rows, s)
+               : row_ce_dispatch<Half, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
+                                            loss_rows, s);
+  }
   return big ? row_ce_dispatch<float, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
                                             loss_rows, s)
              : row_ce_dispatch<float, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
@@ -297,6 +303,10 @@ hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t row
   if (dtype == 1)
     hipLaunchKernelGGL((k_shard_stats<uint16_t, 1024>), grid, dim3(1024), 0, s,
                        static_cast<const uint16_t*>(Z), ldz, V_local, vocab_start, V_global, targets,
+                       ign, row_max, row_sumexp, row_target);
+  else if (dtype == 2)
+    hipLaunchKernelGGL((k_shard_stats<Half, 1024>), grid, dim3(1024), 0, s,
+                       static_cast<const Half*>(Z), ldz, V_local, vocab_start, V_global, targets,
                        ign, row_max, row_sumexp, row_target);
   else
     hipLaunchKernelGGL((k_shard_stats<float, 1024>), grid, dim3(1024), 0, s,
@@ -360,6 +370,9 @@ hipError_t launch_shard_grad(int dtype, void* Z, int64_t ldz, int64_t rows, int6
   if (dtype == 1)
     hipLaunchKernelGGL((k_shard_grad<uint16_t, 256>), grid, dim3(256), 0, s, static_cast<uint16_t*>(Z),
                        ldz, V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr);
+  else if (dtype == 2)
+    hipLaunchKernelGGL((k_shard_grad<Half, 256>), grid, dim3(256), 0, s, static_cast<Half*>(Z), ldz,
+                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr);
   else
     hipLaunchKernelGGL((k_shard_grad<float, 256>), grid, dim3(256), 0, s, static_cast<float*>(Z), ldz,
                        V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr);
@@ -468,6 +481,9 @@ hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, in
   if (dtype == 1)
     hipLaunchKernelGGL(k_colsum<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(Z),
                        ldz, rows, V, out, accumulate ? 1 : 0);
+  else if (dtype == 2)
+    hipLaunchKernelGGL(k_colsum<Half>, grid, dim3(256), 0, s, static_cast<const Half*>(Z), ldz, rows,
+                       V, out, accumulate ? 1 : 0);
   else
     hipLaunchKernelGGL(k_colsum<float>, grid, dim3(256), 0, s, static_cast<const float*>(Z), ldz,
                        rows, V, out, accumulate ? 1 : 0);

@@ -3,10 +3,11 @@ and the benchmark.
 
 This module only draws data: it holds none of the loss arithmetic. Values are
 drawn in float32 with numpy.random.default_rng(seed) in a fixed order (X, W,
-bias, targets, ignored positions) and, for bf16, rounded to the nearest bf16
-(ties to even). Each array is returned twice: as the storage the GPU receives
-(uint16 bit patterns for bf16, float32 for fp32) and as the exact float32 value
-of that storage, which the oracle upcasts to float64.
+bias, targets, ignored positions) and, for bf16 or fp16, rounded to the nearest
+representable value (ties to even). Each array is returned twice: as the
+storage the GPU receives (uint16 bit patterns for bf16 and fp16, float32 for
+fp32) and as the exact float32 value of that storage, which the oracle upcasts
+to float64.
 
 Workload shapes follow the pages' workloads: a Llama-3.2-1B head (H 2048,
 V 128256), a Llama-3-8B head at batch 8 x seq 4096 (H 4096, V 128256), a 256k
@@ -17,7 +18,7 @@ blog, Figure 1), and a CE-only vocabulary shard of 32768 of 65536 at 1024 tokens
 
 import numpy as np
 
-DTYPES = ("f32", "bf16")
+DTYPES = ("f32", "bf16", "f16")
 
 
 def f32_to_bf16_bits(a):
@@ -36,6 +37,9 @@ def _store(values_f32, dtype):
     if dtype == "bf16":
         bits = f32_to_bf16_bits(values_f32)
         return bits, bf16_bits_to_f32(bits)
+    if dtype == "f16":
+        h = np.ascontiguousarray(values_f32, dtype=np.float32).astype(np.float16)  # nearest-even
+        return h.view(np.uint16), h.astype(np.float32)
     if dtype == "f32":
         v = np.ascontiguousarray(values_f32, dtype=np.float32)
         return v, v

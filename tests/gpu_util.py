@@ -8,7 +8,9 @@ import sys
 import numpy as np
 import pytest
 
-TOL = {"f32": {"loss": 1e-5, "grad": 1e-5}, "bf16": {"loss": 2e-3, "grad": 1e-2}}
+# fp16 (10 stored mantissa bits against bf16's 7) is held to the bf16 bar.
+TOL = {"f32": {"loss": 1e-5, "grad": 1e-5}, "bf16": {"loss": 2e-3, "grad": 1e-2},
+       "f16": {"loss": 2e-3, "grad": 1e-2}}
 
 
 def torch_or_skip():
@@ -30,6 +32,8 @@ def to_dev(arr, dtype):
         return None
     if dtype == "bf16" and arr.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    if dtype == "f16" and arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.float16)).cuda()
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
@@ -42,6 +46,8 @@ def to_host(t, f64=True):
     if t.dtype == torch.bfloat16:
         bits = t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
         a = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    elif t.dtype == torch.float16:
+        a = t.detach().cpu().numpy().astype(np.float32)
     else:
         a = t.detach().cpu().numpy()
     return a.astype(np.float64) if f64 else a

@@ -97,6 +97,18 @@ def test_ce_bf16_ragged_and_streaming(B, V):
     check_max_rel(g, ref_g, TOL["bf16"]["grad"], "grad_logits")
 
 
+@pytest.mark.parametrize("V", [1003, 300001])
+def test_ce_f16(B, V):
+    """Half-precision logits: register-resident and streaming rows."""
+    N = 24 if V > 100000 else 129
+    inp = synth.make_ce_inputs(N, V, "f16", std=2.0, ignore_frac=0.1, seed=V + 1)
+    say("ce f16", N, V)
+    loss, g, _, _ = _run_ce(B, inp, "mean")
+    ref_loss, ref_g, _ = O.cross_entropy(inp["logits_f32"], inp["targets"], reduction="mean")
+    check_scalar(loss, ref_loss, TOL["f16"]["loss"])
+    check_max_rel(g, ref_g, TOL["f16"]["grad"], "grad_logits")
+
+
 def test_ce_all_ignored_and_empty(B):
     import torch
     inp = synth.make_ce_inputs(16, 100, "f32", ignore_frac=1.0)

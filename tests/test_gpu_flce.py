@@ -84,6 +84,15 @@ def test_bf16_ragged_tiles(B, reduction, chunk):
     check_against_oracle(inp, reduction, run_flce(B, inp, reduction, chunk_rows=chunk))
 
 
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_f16_ragged_tiles_and_chunks(B, reduction):
+    """IEEE half inputs (the fp16 MFMA path): N 600, H 136, V 1000, bias, 3
+    chunks of 256/256/88 rows."""
+    inp = synth.make_flce_inputs(600, 136, 1000, "f16", bias_std=0.1, ignore_frac=0.1, seed=14)
+    say("flce f16 ragged", reduction)
+    check_against_oracle(inp, reduction, run_flce(B, inp, reduction, chunk_rows=256))
+
+
 def test_bf16_multi_chunk_mid(B):
     """N 1024 in 4 chunks, H 512, V 4099: the grad_W read-modify-write path."""
     inp = synth.make_flce_inputs(1024, 512, 4099, "bf16", ignore_frac=0.1, seed=12)

@@ -19,6 +19,21 @@ def test_bf16_rounding_matches_torch_nearest_even():
     np.testing.assert_array_equal(back, torch.from_numpy(a).to(torch.bfloat16).float().numpy())
 
 
+def test_f16_storage_matches_torch_nearest_even():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    a = np.concatenate([rng.standard_normal(4096).astype(np.float32) * 3,
+                        np.array([1.00048828125, 1.00146484375, 65504.0, 70000.0, 6e-8, -0.0],
+                                 dtype=np.float32)])
+    inp = synth.make_ce_inputs(4, 8, "f16")  # exercises the f16 branch end to end
+    assert inp["logits"].dtype == np.uint16
+    with np.errstate(over="ignore"):   # 70000 rounds to inf, as in torch
+        bits, exact = synth._store(a, "f16")
+    ref = torch.from_numpy(a).to(torch.float16)
+    np.testing.assert_array_equal(bits, ref.view(torch.int16).numpy().view(np.uint16))
+    np.testing.assert_array_equal(exact, ref.float().numpy())
+
+
 def test_ignore_counts_and_ranges():
     inp = synth.make_flce_inputs(256, 64, 1024, "f32", ignore_frac=0.1)
     y = inp["targets"]
