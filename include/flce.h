@@ -209,6 +209,18 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
                         int64_t chunk_rows, void* stream);
 
 /*
+ * Causal-LM targets from token labels (the DeepSpeed vocab-parallel CE page
+ * keeps the label shift of causal language modelling as part of the loss
+ * contract, "Changes"): labels [B, S] int32 row-major,
+ * targets [B * S] int32 with targets[b*S + s] = labels[b*S + s + 1] for
+ * s < S - 1 and ignore_index at each sequence's last position. The result is
+ * the `targets` argument of the other calls for X = hidden states [B*S, H].
+ * targets must not alias labels. Asynchronous on `stream`.
+ */
+int flce_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ignore_index,
+                      int32_t* targets, void* stream);
+
+/*
  * Waits for `stream`, then reports whether the last call that used this
  * workspace met an out-of-range target: FLCE_OK, FLCE_E_TARGET or FLCE_E_HIP.
  */

@@ -43,6 +43,7 @@ _SIGNATURES = {
                                       _vp, _sz, _vp]),
     "flce_shard_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i32,
                                    _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
+    "flce_shift_labels": (_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "flce_check_device_error": (_int, [_vp, _vp]),
     "flce_timing_enable": (_int, [_int]),
     "flce_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
@@ -308,6 +309,17 @@ def flce_shard_backward(X, W_shard, targets, row_lse, vocab_start, V_global, bia
         _stream(stream))
     _check(st, "flce_shard_backward")
     return gX, gW, gb
+
+
+def flce_shift_labels(labels, ignore_index=-100, out=None, stream=None):
+    """Causal-LM targets [B*S] from labels [B, S] (int32)."""
+    Bn, S = labels.shape
+    if out is None:
+        out = _empty((Bn * S,), torch.int32, labels.device)
+    _check(lib().flce_shift_labels(_ptr(labels, "labels", torch.int32), Bn, S, ignore_index,
+                                   _ptr(out, "targets", torch.int32), _stream(stream)),
+           "flce_shift_labels")
+    return out
 
 
 def flce_check_device_error(workspace, stream=None):

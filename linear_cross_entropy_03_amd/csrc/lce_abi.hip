@@ -539,6 +539,17 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
   return FLCE_OK;
 }
 
+int flce_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ignore_index,
+                      int32_t* targets, void* stream) {
+  if (B < 0 || S <= 0) return FLCE_E_INVALID_ARG;
+  if (B > 0 && (labels == nullptr || targets == nullptr)) return FLCE_E_INVALID_ARG;
+  if (B * S >= kMaxRows || B >= kMaxRows) return FLCE_E_UNSUPPORTED;
+  if (B > 0 && labels == targets) return FLCE_E_INVALID_ARG;  // not in place
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LCE_TRY(timed(kKindOther, s, [&] { return launch_shift_labels(labels, B, S, ignore_index, targets, s); }));
+  return FLCE_OK;
+}
+
 int flce_check_device_error(const void* workspace, void* stream) {
   if (workspace == nullptr) return FLCE_E_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);

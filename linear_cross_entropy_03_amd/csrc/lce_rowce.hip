@@ -414,6 +414,27 @@ hipError_t launch_combine_stats(const float* ms, const float* ss, const float* t
   return hipGetLastError();
 }
 
+// ------------------------------------------------------ causal label shift
+
+// targets[b * S + s] = labels[b * S + s + 1] for s < S - 1, ignore_index at
+// the last position of each sequence.
+__global__ __launch_bounds__(256) void k_shift_labels(const int32_t* __restrict__ labels, int64_t n,
+                                                      int64_t S, int32_t ign,
+                                                      int32_t* __restrict__ targets) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  targets[i] = (i % S == S - 1) ? ign : labels[i + 1];
+}
+
+hipError_t launch_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ign,
+                               int32_t* targets, hipStream_t s) {
+  const int64_t n = B * S;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_shift_labels, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                     labels, n, S, ign, targets);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ loss reduce
 
 // Sum of per-row losses in float64, in a fixed order independent of how the

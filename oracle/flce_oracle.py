@@ -318,6 +318,19 @@ def flce_shard_backward(X, W_shard, targets, vocab_start, V_global, lse, bias_sh
     return gX, gW, gb
 
 
+def shift_labels(labels, ignore_index=-100):
+    """Causal-LM targets from labels [B, S]: position s of sequence b predicts
+    token s + 1, so targets[b, s] = labels[b, s + 1] and the last position of
+    each sequence has no target (ignore_index). Returns int32 [B * S]
+    (DeepSpeed vocab-parallel CE page, "Changes": the loss keeps the label
+    shift of causal language modelling)."""
+    lab = np.asarray(labels)
+    B, S = lab.shape
+    out = np.full((B, S), ignore_index, dtype=np.int64)
+    out[:, :-1] = lab[:, 1:]
+    return out.reshape(B * S).astype(np.int32)
+
+
 def materialised_logits_bytes(n_tokens, vocab, elem_bytes):
     """Bytes of a full [tokens, vocab] logits tensor: what FLCE avoids holding."""
     return int(n_tokens) * int(vocab) * int(elem_bytes)

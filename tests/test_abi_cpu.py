@@ -128,3 +128,11 @@ def test_vocab_parallel_argument_errors(B):
     assert bwd(Ws=None) == B.E_INVALID_ARG
     assert bwd(H=12) == B.E_UNSUPPORTED
     assert bwd(ws=None) == B.E_WORKSPACE
+
+
+def test_shift_labels_argument_errors(B):
+    L = B.lib()
+    assert L.flce_shift_labels(None, 2, 3, -100, 16, None) == B.E_INVALID_ARG
+    assert L.flce_shift_labels(16, 2, 0, -100, 32, None) == B.E_INVALID_ARG
+    assert L.flce_shift_labels(16, 2, 3, -100, 16, None) == B.E_INVALID_ARG   # in place
+    assert L.flce_shift_labels(None, 0, 3, -100, None, None) == B.OK          # nothing to do

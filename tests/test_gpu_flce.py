@@ -221,3 +221,15 @@ def test_shard_stats_of_projection(B):
     check_max_rel(to_host(s), rs, 2e-2, "row sumexp")
     check_max_rel(to_host(t), rt, 1e-2, "target logit")
     assert np.all(to_host(t)[(inp["targets"] < v0) | (inp["targets"] >= v0 + Vl)] == 0.0)
+
+
+def test_shift_labels_bit_exact(B):
+    """Integer work: bit-exact against the oracle, including S = 1."""
+    import torch
+    rng = np.random.default_rng(41)
+    for Bn, S in ((7, 513), (3, 1), (1, 4096)):
+        lab = rng.integers(0, 128256, (Bn, S)).astype(np.int32)
+        say("shift labels", Bn, S)
+        got = B.flce_shift_labels(torch.from_numpy(lab).cuda())
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy(), O.shift_labels(lab))

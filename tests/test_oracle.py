@@ -429,3 +429,10 @@ def test_shard_backward_finite_differences():
     lp, _, _ = O.flce(Xp, W, y, bias=b, want_grads=False)
     lm, _, _ = O.flce(Xm, W, y, bias=b, want_grads=False)
     assert abs((lp - lm) / (2 * h) - (gx + rest[0] + rest[1])[1, 2]) < 1e-8
+
+
+def test_shift_labels_hand_example():
+    """Position s predicts token s + 1; each sequence's last position has no target."""
+    lab = np.array([[5, 6, 7], [1, 2, 3]])
+    np.testing.assert_array_equal(O.shift_labels(lab), [6, 7, -100, 2, 3, -100])
+    np.testing.assert_array_equal(O.shift_labels(np.array([[9], [4]]), ignore_index=-1), [-1, -1])
