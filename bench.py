@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-ce", action="store_true", help="skip the standalone CE measurement")
     ap.add_argument("--no-vp", action="store_true",
                     help="skip the vocabulary-parallel shard measurement")
+    ap.add_argument("--no-mh", action="store_true", help="skip the multi-head measurement")
     ap.add_argument("--profile-step", action="store_true",
                     help="for rocprofv3 counter runs: a 1 GiB device copy (counter calibration), "
                          "then one warmup and one timed FLCE step; prints nothing else")
@@ -304,6 +305,48 @@ def bench_vocab_parallel(torch, B, X, W, y, cfg, reps=5):
     }
 
 
+def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
+    """K LM heads over shared hidden states (the liger README's Medusa example:
+    5 heads) at the 8B head's shape on the first n_rows token rows. Head k's
+    weight is the workload's W rolled by 7k rows and its targets are the
+    targets shifted by k positions (a head predicting further ahead); all on
+    the device, no new host draws. GEMM work per call: K x 6 x n x H x V flop."""
+    N, H, V = n_rows, cfg["H"], cfg["V"]
+    Xm = X[:N]
+    Wk = torch.stack([torch.roll(W, shifts=7 * k, dims=0) for k in range(K)]).contiguous()
+    yk = torch.stack([torch.roll(y[:N], shifts=-k) for k in range(K)]).contiguous()
+    loss = torch.empty(K, device="cuda")
+    gX = torch.empty(N, H, device="cuda")
+    gW = torch.empty(K, V, H, device="cuda")
+    ws = torch.empty(B.flce_multihead_workspace_bytes(N, H, V, K, B.BF16), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        B.flce_multihead_forward_backward(Xm, Wk, yk, reduction=cfg["reduction"], grad_X=gX,
+                                          grad_W=gW, grad_bias=False, loss=loss, workspace=ws,
+                                          stream=stream)
+    call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = K * 6.0 * N * H * V
+    out = {
+        "workload": f"{K} heads over llama8b_head_bf16 hidden states (N {N}, H {H}, V {V}, "
+                    f"{cfg['reduction']})",
+        "ms_per_call": ms, "tokens_per_s": N / (ms * 1e-3),
+        "tflops": flops / (ms * 1e-3) / 1e12, "frac_bf16_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        "head_losses": [float(v) for v in loss.cpu()],
+    }
+    del Wk, gW, ws
+    return out
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -448,17 +491,17 @@ def main():
         "kernels": kernels,
         "loss": float(loss.item()),
     }
+    del ws
+    torch.cuda.empty_cache()
     if not args.no_vp:
         log("vocabulary-parallel shard")
-        del ws
         result["vocab_parallel"] = bench_vocab_parallel(torch, B, X, W, y, cfg)
-        ws = None
+    if not args.no_mh:
+        log("multi-head")
+        result["multihead"] = bench_multihead(torch, B, X, W, y, cfg)
     if not args.no_ce:
         log("standalone CE")
-        del ws
         result["ce"] = bench_ce(torch, B)
-    else:
-        del ws
     if not args.no_cpu_baseline:
         log("timing the FP64 oracle on a CPU sample")
         del gX, gW

@@ -115,6 +115,33 @@ int flce_forward_backward(const void* X, const void* W, const void* bias,
                           void* workspace, size_t workspace_bytes, int64_t chunk_rows,
                           void* stream);
 
+/*
+ * Several LM heads over the same hidden states in one call (the Medusa
+ * example the liger README points FusedLinearCrossEntropy users to: extra
+ * heads predicting tokens further ahead). Head k has its own weight, bias,
+ * targets and loss; the hidden-state gradient is the sum over heads:
+ *
+ *   W        [K, V, H]  the heads' weights, head-major
+ *   bias     [K, V] or NULL
+ *   targets  [K, N] int32 (head k's targets, e.g. labels shifted by k + 1)
+ *   loss     [K] float32 (head k's loss with its own N_valid for MEAN), or
+ *            [K, N] for FLCE_REDUCTION_NONE
+ *   grad_X   [N, H] float32 or NULL: sum over heads of dZ_k W_k
+ *   grad_W   [K, V, H] float32 or NULL;  grad_bias [K, V] float32 or NULL
+ *   workspace of at least flce_multihead_workspace_bytes(N, H, V, K, ...)
+ * The gradients are those of the sum of the K heads' losses. Heads run one
+ * after another through the same chunk buffer, so peak scratch is that of one
+ * head.
+ */
+size_t flce_multihead_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t K, int dtype,
+                                      int64_t chunk_rows);
+int flce_multihead_forward_backward(const void* X, const void* W, const void* bias,
+                                    const int32_t* targets, int64_t N, int64_t H, int64_t V,
+                                    int64_t K, int dtype, int32_t ignore_index, int reduction,
+                                    float* loss, float* grad_X, float* grad_W, float* grad_bias,
+                                    void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                                    void* stream);
+
 /* Bytes of workspace ce_forward_backward / ce_shard_stats /
  * ce_combine_shard_stats (V = V_global) need. */
 size_t ce_workspace_bytes(int64_t N, int64_t V);

@@ -44,6 +44,10 @@ _SIGNATURES = {
     "flce_shard_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i32,
                                    _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
     "flce_shift_labels": (_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "flce_multihead_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int, _i64]),
+    "flce_multihead_forward_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
+                                               _i32, _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64,
+                                               _vp]),
     "flce_check_device_error": (_int, [_vp, _vp]),
     "flce_timing_enable": (_int, [_int]),
     "flce_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
@@ -188,6 +192,41 @@ def flce_forward_backward(X, W, targets, bias=None, ignore_index=-100, reduction
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
         _stream(stream))
     _check(st, "flce_forward_backward")
+    return loss, gX, gW, gb
+
+
+def flce_multihead_workspace_bytes(N, H, V, K, dtype=BF16, chunk_rows=0):
+    return int(lib().flce_multihead_workspace_bytes(N, H, V, K, dtype, chunk_rows))
+
+
+def flce_multihead_forward_backward(X, W, targets, bias=None, ignore_index=-100, reduction="mean",
+                                    grad_X=True, grad_W=True, grad_bias=None, loss=None,
+                                    workspace=None, chunk_rows=0, stream=None):
+    """K heads over shared X [N, H]: W [K, V, H], targets [K, N] (int32),
+    bias [K, V] or None. Returns (loss [K] or [K, N], grad_X (sum over heads),
+    grad_W [K, V, H], grad_bias [K, V])."""
+    N, H = X.shape
+    K, V, _ = W.shape
+    dev = X.device
+    dt = _dtype_code(X)
+    if grad_bias is None:
+        grad_bias = bias is not None
+    gX = _grad_arg(grad_X, (N, H), dev)
+    gW = _grad_arg(grad_W, (K, V, H), dev)
+    gb = _grad_arg(grad_bias, (K, V), dev)
+    if loss is None:
+        loss = _empty((K, N) if reduction == "none" else (K,), torch.float32, dev)
+    if workspace is None:
+        workspace = _empty((max(1, flce_multihead_workspace_bytes(N, H, V, K, dt, chunk_rows)),),
+                           torch.uint8, dev)
+    st = lib().flce_multihead_forward_backward(
+        _ptr(X, "X"), _ptr(W, "W", X.dtype), _ptr(bias, "bias", X.dtype),
+        _ptr(targets, "targets", torch.int32), N, H, V, K, dt, ignore_index, _red(reduction),
+        _ptr(loss, "loss", torch.float32), _ptr(gX, "grad_X", torch.float32),
+        _ptr(gW, "grad_W", torch.float32), _ptr(gb, "grad_bias", torch.float32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
+        _stream(stream))
+    _check(st, "flce_multihead_forward_backward")
     return loss, gX, gW, gb
 
 

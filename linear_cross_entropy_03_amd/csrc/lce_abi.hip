@@ -202,44 +202,23 @@ static int validate_common(int dtype, int reduction) {
   return FLCE_OK;
 }
 
-int flce_forward_backward(const void* X, const void* W, const void* bias, const int32_t* targets,
-                          int64_t N, int64_t H, int64_t V, int dtype, int32_t ignore_index,
-                          int reduction, float* loss, float* grad_X, float* grad_W,
-                          float* grad_bias, void* workspace, size_t workspace_bytes,
-                          int64_t chunk_rows, void* stream) {
-  int st = validate_common(dtype, reduction);
-  if (st != FLCE_OK) return st;
-  if (N < 0 || H <= 0 || V <= 0 || chunk_rows < 0) return FLCE_E_INVALID_ARG;
-  if (W == nullptr || loss == nullptr) return FLCE_E_INVALID_ARG;
-  if (N > 0 && (X == nullptr || targets == nullptr)) return FLCE_E_INVALID_ARG;
-  if (grad_bias != nullptr && bias == nullptr) return FLCE_E_INVALID_ARG;
-  if (N >= kMaxRows || H >= kMaxDim || V >= kMaxDim) return FLCE_E_UNSUPPORTED;
-  const void* ptrs[] = {X, W, bias, targets, loss, grad_X, grad_W, grad_bias, workspace};
-  for (const void* q : ptrs)
-    if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
-  if (is16(dtype) && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
-  Plan p;
-  if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
-  if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
+}  // extern "C"
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-  float* loss_rows = reduction == FLCE_REDUCTION_NONE ? loss : reinterpret_cast<float*>(ws + p.off_rows);
+namespace {
+
+// The chunk loop of FLCE over all N rows for one head: logits GEMM, row CE
+// (loss rows, dZ in place), bias column sums, grad_X (stored, or added to
+// what is there when accum_gx), grad_W (stored on the first chunk, added
+// after). Targets must have been counted into hdr.
+int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const void* bias,
+                const int32_t* targets, int64_t N, int64_t H, int64_t V, int32_t ignore_index,
+                WsHeader* hdr, float* loss_rows, float* grad_X, bool accum_gx, float* grad_W,
+                float* grad_bias, char* ws, hipStream_t s) {
   void* zbuf = ws + p.off_chunk;
   float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   const size_t e = elem_bytes(dtype);
   const bool need_grad = grad_X != nullptr || grad_W != nullptr || grad_bias != nullptr;
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
-
-  LCE_TRY(timed(kKindOther, s, [&] {
-    return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
-  }));
-  if (N == 0) {
-    if (grad_W) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W, V * H, 0.0f, s); }));
-    if (grad_bias) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_bias, V, 0.0f, s); }));
-  }
-
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
@@ -269,16 +248,17 @@ int flce_forward_backward(const void* X, const void* W, const void* bias, const 
       g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
       g2.B = W; g2.ldb = H; g2.b_kmajor = false;
       g2.M = rows; g2.N = H; g2.K = V;
-      g2.epilogue = kEpiStoreF32;
       float* out = grad_X + static_cast<size_t>(r0) * H;
       if (p.dx_splits > 1) {
+        g2.epilogue = kEpiStoreF32;
         g2.C = split_buf; g2.ldc = H;
         g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, s);
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, accum_gx, s);
         }));
       } else {
+        g2.epilogue = accum_gx ? kEpiAccumF32 : kEpiStoreF32;
         g2.C = out; g2.ldc = H; g2.k_splits = 1;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
       }
@@ -295,11 +275,125 @@ int flce_forward_backward(const void* X, const void* W, const void* bias, const 
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }
+  return FLCE_OK;
+}
 
+// Validation shared by the single- and multi-head calls.
+int validate_flce(const void* X, const void* W, const void* bias, const int32_t* targets,
+                  int64_t N, int64_t H, int64_t V, int dtype, int reduction, const float* loss,
+                  const float* grad_X, const float* grad_W, const float* grad_bias,
+                  int64_t chunk_rows, const void* workspace) {
+  int st = validate_common(dtype, reduction);
+  if (st != FLCE_OK) return st;
+  if (N < 0 || H <= 0 || V <= 0 || chunk_rows < 0) return FLCE_E_INVALID_ARG;
+  if (W == nullptr || loss == nullptr) return FLCE_E_INVALID_ARG;
+  if (N > 0 && (X == nullptr || targets == nullptr)) return FLCE_E_INVALID_ARG;
+  if (grad_bias != nullptr && bias == nullptr) return FLCE_E_INVALID_ARG;
+  if (N >= kMaxRows || H >= kMaxDim || V >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  const void* ptrs[] = {X, W, bias, targets, loss, grad_X, grad_W, grad_bias, workspace};
+  for (const void* q : ptrs)
+    if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
+  if (is16(dtype) && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  return FLCE_OK;
+}
+
+// Per-head counters and loss rows of the multi-head call, after the FLCE plan.
+size_t head_slot_bytes(int64_t N) {
+  return align_up(sizeof(WsHeader)) + align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int flce_forward_backward(const void* X, const void* W, const void* bias, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int dtype, int32_t ignore_index,
+                          int reduction, float* loss, float* grad_X, float* grad_W,
+                          float* grad_bias, void* workspace, size_t workspace_bytes,
+                          int64_t chunk_rows, void* stream) {
+  int st = validate_flce(X, W, bias, targets, N, H, V, dtype, reduction, loss, grad_X, grad_W,
+                         grad_bias, chunk_rows, workspace);
+  if (st != FLCE_OK) return st;
+  Plan p;
+  if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  float* loss_rows = reduction == FLCE_REDUCTION_NONE ? loss : reinterpret_cast<float*>(ws + p.off_rows);
+
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
+  }));
+  if (N == 0) {
+    if (grad_W) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W, V * H, 0.0f, s); }));
+    if (grad_bias) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_bias, V, 0.0f, s); }));
+  }
+  st = flce_chunks(p, dtype, X, W, bias, targets, N, H, V, ignore_index, hdr, loss_rows, grad_X,
+                   false, grad_W, grad_bias, ws, s);
+  if (st != FLCE_OK) return st;
   if (reduction != FLCE_REDUCTION_NONE)
     LCE_TRY(timed(kKindOther, s, [&] {
       return launch_reduce_loss(loss_rows, N, hdr, reduction, loss, s);
     }));
+  return FLCE_OK;
+}
+
+size_t flce_multihead_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t K, int dtype,
+                                      int64_t chunk_rows) {
+  Plan p;
+  if (K <= 0 || K >= kMaxDim || !make_plan(N, H, V, dtype, chunk_rows, &p)) return 0;
+  return p.total + static_cast<size_t>(K) * head_slot_bytes(N);
+}
+
+int flce_multihead_forward_backward(const void* X, const void* W, const void* bias,
+                                    const int32_t* targets, int64_t N, int64_t H, int64_t V,
+                                    int64_t K, int dtype, int32_t ignore_index, int reduction,
+                                    float* loss, float* grad_X, float* grad_W, float* grad_bias,
+                                    void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                                    void* stream) {
+  if (K <= 0 || K >= kMaxDim) return FLCE_E_INVALID_ARG;
+  int st = validate_flce(X, W, bias, targets, N, H, V, dtype, reduction, loss, grad_X, grad_W,
+                         grad_bias, chunk_rows, workspace);
+  if (st != FLCE_OK) return st;
+  Plan p;
+  if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
+  const size_t slot = head_slot_bytes(N);
+  if (workspace == nullptr || workspace_bytes < p.total + static_cast<size_t>(K) * slot)
+    return FLCE_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const size_t e = elem_bytes(dtype);
+  // The call's own header (first slot of the plan) collects nothing; each
+  // head counts its targets into its own slot so N_valid is per head.
+  for (int64_t k = 0; k < K; ++k) {
+    char* hs = ws + p.total + static_cast<size_t>(k) * slot;
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(hs);
+    float* loss_rows = reduction == FLCE_REDUCTION_NONE
+                           ? loss + static_cast<size_t>(k) * N
+                           : reinterpret_cast<float*>(hs + align_up(sizeof(WsHeader)));
+    const int32_t* tk = targets + static_cast<size_t>(k) * N;
+    const char* Wk = static_cast<const char*>(W) + static_cast<size_t>(k) * V * H * e;
+    const char* bk = bias ? static_cast<const char*>(bias) + static_cast<size_t>(k) * V * e : nullptr;
+    float* gWk = grad_W ? grad_W + static_cast<size_t>(k) * V * H : nullptr;
+    float* gbk = grad_bias ? grad_bias + static_cast<size_t>(k) * V : nullptr;
+    LCE_TRY(timed(kKindOther, s, [&] {
+      return launch_count_targets(tk, N, V, ignore_index, reduction, hdr, s);
+    }));
+    if (N == 0) {
+      if (gWk) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(gWk, V * H, 0.0f, s); }));
+      if (gbk) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(gbk, V, 0.0f, s); }));
+    }
+    st = flce_chunks(p, dtype, X, Wk, bk, tk, N, H, V, ignore_index, hdr, loss_rows, grad_X, k > 0,
+                     gWk, gbk, ws, s);
+    if (st != FLCE_OK) return st;
+    if (reduction != FLCE_REDUCTION_NONE)
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_reduce_loss(loss_rows, N, hdr, reduction, loss + k, s);
+      }));
+  }
   return FLCE_OK;
 }
 
@@ -518,7 +612,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
         g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, s);
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, false, s);
         }));
       } else {
         g2.C = out; g2.ldc = H; g2.k_splits = 1;

@@ -234,7 +234,7 @@ hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, in
 
 hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride,
                                 int64_t rows, int64_t cols, int64_t ld_out, float* out,
-                                hipStream_t s);
+                                bool accumulate, hipStream_t s);
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 

@@ -558,6 +558,8 @@ static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
     return launch_mfma_v2<true, true, kEpiLogits, 4, kTy>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
     return launch_mfma_v2<true, false, kEpiStoreF32, 4, kTy>(d, s);
+  if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
+    return launch_mfma_v2<true, false, kEpiAccumF32, 4, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
     return launch_mfma_v2<false, false, kEpiStoreF32, 4, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
@@ -655,6 +657,7 @@ hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
   if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits) return launch_valu<true, true, kEpiLogits>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32) return launch_valu<true, false, kEpiStoreF32>(d, s);
+  if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32) return launch_valu<true, false, kEpiAccumF32>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32) return launch_valu<false, false, kEpiStoreF32>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32) return launch_valu<false, false, kEpiAccumF32>(d, s);
   return hipErrorInvalidValue;

@@ -513,22 +513,26 @@ hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, in
 
 // -------------------------------------------------------- split-K reduce
 
+// out (+)= sum of the K-split partials, splits in index order.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ parts, int splits,
                                                        int64_t stride, int64_t rows, int64_t cols,
-                                                       int64_t ld_out, float* __restrict__ out) {
+                                                       int64_t ld_out, float* __restrict__ out,
+                                                       int accumulate) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= rows * cols) return;
   const int64_t r = i / cols, c = i - r * cols;
   float acc = parts[r * cols + c];
   for (int sp = 1; sp < splits; ++sp) acc += parts[sp * stride + r * cols + c];
+  if (accumulate) acc += out[r * ld_out + c];
   out[r * ld_out + c] = acc;
 }
 
 hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride, int64_t rows,
-                                int64_t cols, int64_t ld_out, float* out, hipStream_t s) {
+                                int64_t cols, int64_t ld_out, float* out, bool accumulate,
+                                hipStream_t s) {
   const int64_t n = rows * cols;
   hipLaunchKernelGGL(k_splitk_reduce, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
-                     parts, splits, split_stride, rows, cols, ld_out, out);
+                     parts, splits, split_stride, rows, cols, ld_out, out, accumulate ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -318,6 +318,27 @@ def flce_shard_backward(X, W_shard, targets, vocab_start, V_global, lse, bias_sh
     return gX, gW, gb
 
 
+def flce_multihead(X, Ws, targets, biases=None, ignore_index=-100, reduction="mean",
+                   row_block=1024):
+    """K LM heads over the same hidden states (the Medusa example of the liger
+    README): head k is an FLCE of X with its own weight Ws[k], bias and
+    targets[k]; the objective is the sum of the K head losses, so grad_X is
+    the sum of the heads' grad_X. Returns (losses [K] or [K, N],
+    {"X", "W" [K, V, H], "bias" [K, V] or None})."""
+    K = len(Ws)
+    losses, gX, gW, gb = [], None, [], []
+    for k in range(K):
+        b = None if biases is None else biases[k]
+        loss, g, _ = flce(X, Ws[k], targets[k], bias=b, ignore_index=ignore_index,
+                          reduction=reduction, row_block=row_block)
+        losses.append(loss)
+        gX = g["X"] if gX is None else gX + g["X"]
+        gW.append(g["W"])
+        gb.append(g["bias"])
+    return np.array(losses), {"X": gX, "W": np.stack(gW),
+                              "bias": None if biases is None else np.stack(gb)}
+
+
 def shift_labels(labels, ignore_index=-100):
     """Causal-LM targets from labels [B, S]: position s of sequence b predicts
     token s + 1, so targets[b, s] = labels[b, s + 1] and the last position of

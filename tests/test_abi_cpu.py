@@ -136,3 +136,23 @@ def test_shift_labels_argument_errors(B):
     assert L.flce_shift_labels(16, 2, 0, -100, 32, None) == B.E_INVALID_ARG
     assert L.flce_shift_labels(16, 2, 3, -100, 16, None) == B.E_INVALID_ARG   # in place
     assert L.flce_shift_labels(None, 0, 3, -100, None, None) == B.OK          # nothing to do
+
+
+def test_multihead_argument_errors(B):
+    L = B.lib()
+    assert B.flce_multihead_workspace_bytes(64, 8, 100, 0) == 0
+    one = B.flce_multihead_workspace_bytes(64, 8, 100, 1)
+    assert B.flce_multihead_workspace_bytes(64, 8, 100, 3) > one > B.flce_workspace_bytes(64, 8, 100)
+
+    def mh(K=2, wsb=1 << 30, **kw):
+        a = dict(X=16, W=16, bias=None, y=16, N=4, H=8, V=10, dt=B.BF16, red=2, loss=16, gX=16,
+                 gW=16, gb=None, ws=16)
+        a.update(kw)
+        return L.flce_multihead_forward_backward(a["X"], a["W"], a["bias"], a["y"], a["N"], a["H"],
+                                                 a["V"], K, a["dt"], -100, a["red"], a["loss"],
+                                                 a["gX"], a["gW"], a["gb"], a["ws"], wsb, 0, None)
+    assert mh(K=0) == B.E_INVALID_ARG
+    assert mh(W=None) == B.E_INVALID_ARG
+    assert mh(gb=16) == B.E_INVALID_ARG
+    assert mh(H=12) == B.E_UNSUPPORTED
+    assert mh(wsb=B.flce_workspace_bytes(4, 8, 10)) == B.E_WORKSPACE

@@ -233,3 +233,48 @@ def test_shift_labels_bit_exact(B):
         got = B.flce_shift_labels(torch.from_numpy(lab).cuda())
         torch.cuda.synchronize()
         np.testing.assert_array_equal(got.cpu().numpy(), O.shift_labels(lab))
+
+
+def _run_multihead(B, inps, reduction, chunk_rows=0):
+    import torch
+    dt = inps[0]["dtype"]
+    X = to_dev(inps[0]["X"], dt)
+    W = torch.stack([to_dev(i["W"], dt) for i in inps]).contiguous()
+    has_b = inps[0]["bias"] is not None
+    b = torch.stack([to_dev(i["bias"], dt) for i in inps]).contiguous() if has_b else None
+    y = torch.stack([to_dev(i["targets"], "i32") for i in inps]).contiguous()
+    loss, gX, gW, gb = B.flce_multihead_forward_backward(X, W, y, bias=b, reduction=reduction,
+                                                         chunk_rows=chunk_rows)
+    torch.cuda.synchronize()
+    return to_host(loss), to_host(gX), to_host(gW), to_host(gb)
+
+
+@pytest.mark.parametrize("dtype,K,reduction,chunk,shape", [
+    ("bf16", 3, "mean", 256, (600, 136, 1000)),
+    ("f32", 2, "none", 0, (300, 64, 900)),
+    ("bf16", 2, "sum", 0, (512, 2048, 16384)),   # grad_X split over K: accumulating reduce
+])
+def test_multihead_against_oracle(B, dtype, K, reduction, chunk, shape):
+    """K heads over shared hidden states: per-head losses, summed grad_X,
+    per-head grad_W / grad_bias."""
+    N, H, V = shape
+    base = synth.make_flce_inputs(N, H, V, dtype, bias_std=0.05 if N < 1000 else None,
+                                  ignore_frac=0.1, seed=50)
+    inps = [base] + [synth.make_flce_inputs(N, H, V, dtype, bias_std=0.05 if N < 1000 else None,
+                                            ignore_frac=0.1, seed=51 + k) for k in range(K - 1)]
+    for i in inps[1:]:                      # the heads share the hidden states
+        i["X"], i["X_f32"] = base["X"], base["X_f32"]
+    say("multihead", dtype, K, reduction, chunk, shape, B.flce_plan(N, H, V, B.BF16))
+    loss, gX, gW, gb = _run_multihead(B, inps, reduction, chunk)
+    X = np.asarray(base["X_f32"], np.float64)
+    Ws = [np.asarray(i["W_f32"], np.float64) for i in inps]
+    bs = None if base["bias"] is None else [np.asarray(i["bias_f32"], np.float64) for i in inps]
+    ys = [i["targets"] for i in inps]
+    ref_loss, ref_g = O.flce_multihead(X, Ws, ys, biases=bs, reduction=reduction)
+    t = TOL[dtype]
+    check_max_rel(loss, ref_loss, t["loss"], "head losses")
+    check_max_rel(gX, ref_g["X"], t["grad"], "grad_X (sum over heads)")
+    for k in range(K):
+        check_max_rel(gW[k], ref_g["W"][k], t["grad"], f"grad_W head {k}")
+        if bs is not None:
+            check_max_rel(gb[k], ref_g["bias"][k], t["grad"], f"grad_bias head {k}")

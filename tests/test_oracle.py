@@ -436,3 +436,36 @@ def test_shift_labels_hand_example():
     lab = np.array([[5, 6, 7], [1, 2, 3]])
     np.testing.assert_array_equal(O.shift_labels(lab), [6, 7, -100, 2, 3, -100])
     np.testing.assert_array_equal(O.shift_labels(np.array([[9], [4]]), ignore_index=-1), [-1, -1])
+
+
+# --------------------------------------------------------------- multi-head
+
+def test_multihead_single_head_is_flce():
+    rng = np.random.default_rng(21)
+    X, W, b, y = _rand_problem(rng, N=13, H=5, V=9)
+    losses, g = O.flce_multihead(X, [W], [y], biases=[b], reduction="sum")
+    loss, g1, _ = O.flce(X, W, y, bias=b, reduction="sum")
+    assert losses.shape == (1,) and losses[0] == loss
+    np.testing.assert_array_equal(g["X"], g1["X"])
+    np.testing.assert_array_equal(g["W"][0], g1["W"])
+
+
+def test_multihead_finite_differences():
+    """grad_X of the multi-head call is the derivative of the summed head
+    losses (each head's mean over its own valid rows)."""
+    rng = np.random.default_rng(22)
+    N, H, V, K = 8, 4, 7, 3
+    X = rng.standard_normal((N, H))
+    Ws = [rng.standard_normal((V, H)) * 0.5 for _ in range(K)]
+    ys = [rng.integers(0, V, N) for _ in range(K)]
+    ys[1][[0, 3]] = -100
+    _, g = O.flce_multihead(X, Ws, ys, reduction="mean")
+
+    def total(Xp):
+        return sum(O.flce(Xp, Ws[k], ys[k], want_grads=False)[0] for k in range(K))
+    h = 1e-6
+    for (i, j) in [(0, 0), (3, 2), (7, 1)]:
+        Xp, Xm = X.copy(), X.copy()
+        Xp[i, j] += h
+        Xm[i, j] -= h
+        assert abs((total(Xp) - total(Xm)) / (2 * h) - g["X"][i, j]) < 1e-8
