@@ -212,6 +212,161 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   if (tid < pad_cols) E::store(g + V + tid, 0.0f);
 }
 
+// Persistent variant for long register-resident rows (1024 lanes, kRes
+// vectors per lane): one workgroup per CU walks rows blockIdx.x, +gridDim.x,
+// ... While a row is reduced and its gradient written, the first kSlices x
+// 16 KiB of the workgroup's next row stream into LDS with direct loads, so
+// HBM stays busy through the row's compute phase. Each lane reads back only
+// the bytes its own direct loads wrote, so the hand-off needs no barrier:
+// the compiler's per-wave wait for those loads is enough.
+namespace pf {
+constexpr int kThreads = 1024;
+constexpr int kMaxSlices = 9;  // 144 KiB of LDS
+__shared__ __align__(16) uint4 g_next[kMaxSlices * kThreads];
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo),
+                                           static_cast<short>(0), n, 0x00020000);
+}
+}  // namespace pf
+
+template <typename T, int kRes>
+__global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t ldz, T* G,
+                                                            int64_t ldg, int64_t rows, int64_t V,
+                                                            int64_t pad_cols,
+                                                            const int32_t* __restrict__ targets,
+                                                            int32_t ign,
+                                                            const WsHeader* __restrict__ hdr,
+                                                            float* __restrict__ loss_rows) {
+  using E = Elem<T>;
+  constexpr int kVec = E::kVec;
+  constexpr int kThreads = pf::kThreads;
+  constexpr int kSlices = kRes < pf::kMaxSlices ? kRes : pf::kMaxSlices;
+  __shared__ float red0[kThreads / 64], red1[kThreads / 64];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // Direct loads of slices 0..kSlices-1 of `row` (vector j*kThreads + tid to
+  // LDS slot j*kThreads + tid); vectors past the row read as zero.
+  auto prefetch = [&](int64_t row) {
+    const T* z = Z + row * ldz;
+    const RowSplit rs = split_row(z, V);
+    const __amdgpu_buffer_rsrc_t r = pf::row_rsrc(z + rs.head, rs.nvec * 16);
+#pragma unroll
+    for (int j = 0; j < kSlices; ++j)  // slice offset in the scalar offset register
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (pf::lds_void*)(&pf::g_next[j * kThreads + wave * 64]), 16, tid * 16,
+          j * kThreads * 16, 0, 0);
+  };
+
+  int64_t row = blockIdx.x;
+  if (row >= rows) return;
+  prefetch(row);
+  for (; row < rows; row += gridDim.x) {
+    const T* z = Z + row * ldz;
+    const int32_t y = targets[row];
+    const bool valid = (y != ign) && y >= 0 && static_cast<int64_t>(y) < V;
+    const RowSplit rs = split_row(z, V);
+    // Here V <= 16 * 1024 vectors: 32-bit element and vector indices.
+    const int nvec = static_cast<int>(rs.nvec), head = static_cast<int>(rs.head);
+    const int tail0 = static_cast<int>(rs.tail0), Vi = static_cast<int>(V);
+    float zt = 0.0f;
+    if (tid == 0 && valid) zt = E::load(z + y);  // before any lane overwrites the row
+
+    uint4 buf[kRes];
+    {
+      const __amdgpu_buffer_rsrc_t r = pf::row_rsrc(z + head, rs.nvec * 16);
+#pragma unroll
+      for (int j = kSlices; j < kRes; ++j)  // range-checked: zeros past the row
+        buf[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               r, tid * 16, j * kThreads * 16, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < kSlices; ++j) buf[j] = pf::g_next[j * kThreads + tid];
+    // The LDS slots are reloaded next: the reads above must have completed.
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    if (row + gridDim.x < rows) prefetch(row + gridDim.x);
+
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRes; ++j) {
+      if (j * kThreads + tid < nvec) {
+        float f[kVec];
+        E::unpack(buf[j], f);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) lm = fmaxf(lm, f[i]);
+      }
+    }
+    if (tid < head) lm = fmaxf(lm, E::load(z + tid));
+    if (tid < Vi - tail0) lm = fmaxf(lm, E::load(z + tail0 + tid));
+    float ls = 0.0f;
+    if (lm != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kRes; ++j) {
+        if (j * kThreads + tid < nvec) {
+          float f[kVec];
+          E::unpack(buf[j], f);
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) ls += __builtin_amdgcn_exp2f((f[i] - lm) * kLog2e);
+        }
+      }
+      if (tid < head) ls += __builtin_amdgcn_exp2f((E::load(z + tid) - lm) * kLog2e);
+      if (tid < Vi - tail0) ls += __builtin_amdgcn_exp2f((E::load(z + tail0 + tid) - lm) * kLog2e);
+    }
+    float M, S;
+    block_lse_parts<kThreads>(lm, ls, red0, red1, M, S);
+    const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
+    if (tid == 0) loss_rows[row] = valid ? (lse - zt) : 0.0f;
+
+    if (G != nullptr) {
+      const float c = valid ? hdr->scale : 0.0f;
+      const int yt = valid ? y : -1;
+      T* g = G + row * ldg;
+      uint4* gv = reinterpret_cast<uint4*>(g + head);
+      auto grad_of = [&](float x, int v) -> float {
+        const float p = __builtin_amdgcn_exp2f((x - lse) * kLog2e);
+        return c * (v == yt ? p - 1.0f : p);
+      };
+#pragma unroll
+      for (int j = 0; j < kRes; ++j) {
+        const int vi = j * kThreads + tid;
+        if (vi < nvec) {
+          float f[kVec];
+          E::unpack(buf[j], f);
+          const int v0 = head + vi * kVec;
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
+          gv[vi] = E::pack(f);
+        }
+      }
+      if (tid < head) E::store(g + tid, grad_of(E::load(z + tid), tid));
+      if (tid < Vi - tail0) E::store(g + tail0 + tid, grad_of(E::load(z + tail0 + tid), tail0 + tid));
+      if (tid < pad_cols) E::store(g + V + tid, 0.0f);
+    }
+    __syncthreads();  // red0 / red1 are rewritten by the next row
+  }
+  // Direct loads past the last row would still be in flight here; none are
+  // issued for rows >= rows.
+}
+
+static int cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      return 256;
+  }
+  return cus;
+}
+
 template <typename T, int kThreads>
 static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                                   int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
@@ -224,6 +379,15 @@ static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t l
 #define LCE_ROW_CE(R)                                                                           \
   hipLaunchKernelGGL((k_row_ce<T, kThreads, R>), grid, block, 0, s, z, ldz, g, ldg, V, pad_cols, \
                      targets, ign, hdr, loss_rows)
+  // Long rows, more rows than CUs: the persistent prefetching variant.
+  if constexpr (kThreads == pf::kThreads) {
+    const int cus = cu_count();
+    if (nvec_max > 8 * kThreads && nvec_max <= 16 * kThreads && rows >= 2 * cus) {
+      hipLaunchKernelGGL((k_row_ce_pf<T, 16>), dim3(static_cast<unsigned>(cus)), block, 0, s, z, ldz,
+                         g, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows);
+      return hipGetLastError();
+    }
+  }
   if (nvec_max <= 1 * kThreads) LCE_ROW_CE(1);
   else if (nvec_max <= 2 * kThreads) LCE_ROW_CE(2);
   else if (nvec_max <= 4 * kThreads) LCE_ROW_CE(4);

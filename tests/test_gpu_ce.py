@@ -170,3 +170,21 @@ def test_shard_stats_two_halves_combine(B):
     check_max_rel(lse, ref_lse, 1e-6, "combined lse")
     valid = inp["targets"] != -100
     assert np.array_equal(zt[valid], inp["logits_f32"][np.arange(1024)[valid], inp["targets"][valid]])
+
+
+@pytest.mark.parametrize("dtype,V,mode", [("bf16", 100003, "out"), ("f16", 100003, "inplace"),
+                                          ("f32", 40001, "out"), ("bf16", 131072, "inplace")])
+def test_ce_long_rows_persistent(B, dtype, V, mode):
+    """Rows of 8193..16384 16-byte vectors with more rows than CUs take the
+    persistent kernel that streams each workgroup's next row into LDS while
+    the current one is reduced; odd V gives misaligned rows (head and tail
+    elements) on every other row."""
+    N = 600
+    inp = synth.make_ce_inputs(N, V, dtype, std=2.0, ignore_frac=0.1, seed=V % 1000)
+    say("ce long rows", dtype, N, V, mode)
+    loss, g, unchanged, _ = _run_ce(B, inp, "mean", mode=mode)
+    ref_loss, ref_g, _ = O.cross_entropy(inp["logits_f32"], inp["targets"], reduction="mean")
+    check_scalar(loss, ref_loss, TOL[dtype]["loss"])
+    check_max_rel(g, ref_g, TOL[dtype]["grad"], "grad_logits")
+    if mode == "out":
+        assert unchanged
