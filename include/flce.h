@@ -27,7 +27,8 @@
  *   - Element type of X, W, bias and logits: FLCE_F32 (float), FLCE_BF16
  *     (bfloat16 bit patterns, uint16) or FLCE_F16 (IEEE half; the DeepSpeed
  *     vocab-parallel CE page tests FP32/FP16/BF16 logits). All of a call's
- *     floating inputs share one type; 16-bit types need H % 8 == 0. Chunk
+ *     floating inputs share one type; 16-bit types need H % 8 == 0 and H,
+ *     V below 2^22 (32-bit offsets inside a GEMM tile). Chunk
  *     logits and dlogits are stored in that type; losses, statistics and
  *     FLCE gradients are float32.
  *   - Targets are int32 class ids. A row is ignored iff its target equals

@@ -30,6 +30,14 @@ inline size_t elem_bytes(int dtype) { return dtype == FLCE_F32 ? 4 : 2; }
 inline bool is16(int dtype) { return dtype == FLCE_BF16 || dtype == FLCE_F16; }
 inline bool valid_dtype(int dtype) { return dtype == FLCE_F32 || is16(dtype); }
 
+// The 16-bit GEMMs address a 256-row tile of an operand or of the chunk
+// buffer with 32-bit byte offsets: row strides (H, and the chunk stride
+// round_up(V, 8)) must stay below 2^22 elements.
+constexpr int64_t kMax16Stride = int64_t(1) << 22;
+inline bool gemm16_fits(int dtype, int64_t H, int64_t V) {
+  return !is16(dtype) || (H < kMax16Stride && round_up(V, 8) < kMax16Stride);
+}
+
 // The GEMM for the call's element type.
 inline hipError_t gemm_for(int dtype, const GemmDesc& d, hipStream_t s) {
   return is16(dtype) ? launch_gemm_16(d, dtype == FLCE_F16, s) : launch_gemm_f32(d, s);
@@ -294,6 +302,7 @@ int validate_flce(const void* X, const void* W, const void* bias, const int32_t*
   for (const void* q : ptrs)
     if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
   if (is16(dtype) && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  if (!gemm16_fits(dtype, H, V)) return FLCE_E_UNSUPPORTED;
   return FLCE_OK;
 }
 
@@ -473,6 +482,7 @@ int flce_shard_stats(const void* X, const void* W_shard, const void* bias_shard,
   for (const void* q : ptrs)
     if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
   if (is16(dtype) && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  if (!gemm16_fits(dtype, H, V_local)) return FLCE_E_UNSUPPORTED;
   Plan p;
   if (!make_plan(N, H, V_local, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
@@ -558,6 +568,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
   for (const void* q : ptrs)
     if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
   if (is16(dtype) && (H % 8) != 0) return FLCE_E_UNSUPPORTED;
+  if (!gemm16_fits(dtype, H, V_local)) return FLCE_E_UNSUPPORTED;
   Plan p;
   if (!make_plan(N, H, V_local, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;

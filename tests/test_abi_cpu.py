@@ -156,3 +156,12 @@ def test_multihead_argument_errors(B):
     assert mh(gb=16) == B.E_INVALID_ARG
     assert mh(H=12) == B.E_UNSUPPORTED
     assert mh(wsb=B.flce_workspace_bytes(4, 8, 10)) == B.E_WORKSPACE
+
+
+def test_16bit_stride_limit(B):
+    """16-bit GEMM tiles use 32-bit byte offsets: H and round_up(V, 8) below 2^22."""
+    big = 1 << 22
+    assert _fb(B, H=big) == B.E_UNSUPPORTED
+    assert _fb(B, V=big - 3) == B.E_UNSUPPORTED          # rounds up to 2^22
+    assert _fb(B, dtype=B.F16, V=big + 8) == B.E_UNSUPPORTED
+    assert _fb(B, dtype=B.F32, H=big, wsb=64) == B.E_WORKSPACE   # fp32 path has no such limit
