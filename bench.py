@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-vp", action="store_true",
                     help="skip the vocabulary-parallel shard measurement")
     ap.add_argument("--no-mh", action="store_true", help="skip the multi-head measurement")
+    ap.add_argument("--no-eager", action="store_true",
+                    help="skip the PyTorch eager context measurement")
     ap.add_argument("--profile-step", action="store_true",
                     help="for rocprofv3 counter runs: a 1 GiB device copy (counter calibration), "
                          "then one warmup and one timed FLCE step; prints nothing else")
@@ -305,6 +307,43 @@ def bench_vocab_parallel(torch, B, X, W, y, cfg, reps=5):
     }
 
 
+def bench_torch_eager(torch, X, W, y, cfg, reps=3):
+    """Context, not a target: the materialised computation in plain PyTorch on
+    the same GPU and inputs: logits = X W^T in bf16 (the vendor GEMM library),
+    upcast to float32, F.cross_entropy (ignore_index, the workload's
+    reduction) and autograd for grad_X and grad_W."""
+    import torch.nn.functional as F
+    Xr = X.detach().clone().requires_grad_(True)
+    Wr = W.detach().clone().requires_grad_(True)
+    yl = y.long()
+
+    def step():
+        Xr.grad = None
+        Wr.grad = None
+        logits = Xr @ Wr.t()
+        loss = F.cross_entropy(logits.float(), yl, ignore_index=-100, reduction=cfg["reduction"])
+        loss.backward()
+        return loss
+
+    step()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        loss = step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    out = {"what": "PyTorch eager, materialised logits (bf16 GEMMs, float32 cross_entropy, autograd)",
+           "ms_per_step": ms, "tokens_per_s": cfg["N"] / (ms * 1e-3),
+           "peak_extra_bytes": torch.cuda.max_memory_allocated() - base, "loss": float(loss.item())}
+    del Xr, Wr
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
     """K LM heads over shared hidden states (the liger README's Medusa example:
     5 heads) at the 8B head's shape on the first n_rows token rows. Head k's
@@ -496,6 +535,9 @@ def main():
     if not args.no_vp:
         log("vocabulary-parallel shard")
         result["vocab_parallel"] = bench_vocab_parallel(torch, B, X, W, y, cfg)
+    if not args.no_eager:
+        log("PyTorch eager context")
+        result["torch_eager_context"] = bench_torch_eager(torch, X, W, y, cfg)
     if not args.no_mh:
         log("multi-head")
         result["multihead"] = bench_multihead(torch, B, X, W, y, cfg)
