@@ -87,21 +87,34 @@ def cpu_baseline(inp, cfg, target_s):
         O.flce(X[:rows], W, y[:rows], bias=b, reduction=cfg["reduction"], row_block=1024)
         return time.perf_counter() - t0
 
-    # Fit t(rows) = fixed + per_row * rows from two probes, then size the
-    # sample to about target_s seconds.
-    t64, t128 = run(64), run(128)
-    per_row = max((t128 - t64) / 64.0, 1e-6)
-    fixed = max(t64 - 64 * per_row, 0.0)
-    rows = int(min(len(y), max(128, (target_s - fixed) / per_row)))
-    rows = max(128, rows // 64 * 64)
+    # Fit t(rows) = fixed + per_row * rows from two probes (each pays the
+    # fixed cost of the [V, H] float64 grad_W), then size the sample to about
+    # target_s seconds; a flat probe pair falls back to the larger probe's
+    # average, and the sample never exceeds a quarter of the rows.
+    t256, t768 = run(256), run(768)
+    per_row = (t768 - t256) / 512.0
+    if per_row <= 0.2 * t768 / 768.0:
+        per_row = t768 / 768.0
+    fixed = max(t768 - 768 * per_row, 0.0)
+    rows = int((target_s - fixed) / per_row)
+    rows = max(256, min(rows, len(y) // 4) // 64 * 64)
     t = run(rows)
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
                   or [1])
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
     return {
         "value": rows / t,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": model,
+        "affinity_cores": len(os.sched_getaffinity(0)),
         "sample": (f"FP64 NumPy oracle (flce: materialised logits per 1024-row block, loss + "
                    f"grad_X + grad_W{' + grad_bias' if b is not None else ''}) on the first "
                    f"{rows} of {len(y)} token rows with the full [{W.shape[0]}, {W.shape[1]}] head; "
@@ -225,6 +238,18 @@ def bench_ce(torch, B, reps=40):
     torch.cuda.synchronize()
     st_us = a.elapsed_time(b) / reps * 1e3
     st_algo = 1.0 * N * V * 2 + 16.0 * N
+    # device-to-device copy of 1 GiB as the practical bandwidth reference
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_GBps = 2.0 * (1 << 30) * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
     return {
         "workload": "ce_shard_bf16 (logits [1024, 32768] bf16, mean, grad out of place)",
         "us_per_call": call_us, "row_ce_kernel_us": kern_us,
@@ -232,6 +257,8 @@ def bench_ce(torch, B, reps=40):
         "achieved_GBps_call": algo / (call_us * 1e-6) / 1e9,
         "achieved_GBps_kernel": algo / (kern_us * 1e-6) / 1e9,
         "frac_hbm_kernel": algo / (kern_us * 1e-6) / PEAK_HBM_BYTES,
+        "copy_GBps": copy_GBps,
+        "frac_of_copy_kernel": algo / (kern_us * 1e-6) / 1e9 / copy_GBps,
         "shard_stats_us_per_call": st_us,
         "shard_stats_GBps": st_algo / (st_us * 1e-6) / 1e9,
     }
@@ -441,9 +468,15 @@ def main():
         torch.cuda.synchronize()
         log("profile step done")
         return
-    for _ in range(args.warmup):
+    first = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for i in range(args.warmup):
+        if i == 0:
+            first[0].record(stream)
         step()
+        if i == 0:
+            first[1].record(stream)
     torch.cuda.synchronize()
+    first_call_ms = first[0].elapsed_time(first[1]) if args.warmup > 0 else None
     if B.flce_check_device_error(ws) != B.OK:
         sys.exit("device reported an out-of-range target")
 
@@ -453,13 +486,17 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     B.flce_timing_enable(False)
     ms = start.elapsed_time(stop) / args.steps
+    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     peak = torch.cuda.max_memory_allocated()
 
     # Per-kernel roofline from the library's HIP events over the timed region.
@@ -501,6 +538,8 @@ def main():
                 "algorithmic_per_launch": dom["algorithmic_per_launch"]}
 
     tokens_per_s = N / (ms * 1e-3)
+    extra_bound = (chunk * ((V + 7) // 8 * 8) * e + (N + V) * 16 + 4096
+                   + (splits * chunk * H * 4 if splits > 1 else 0))
     step_flops = 6.0 * N * H * V
     result = {
         "metric": "FLCE fwd+bwd tokens/s + % bf16 MFMA peak at H4096 V128256; peak HBM bytes",
@@ -520,10 +559,16 @@ def main():
         "config": {"workload": args.workload, "N": N, "H": H, "V": V, "reduction": cfg["reduction"],
                    "bias": bias is not None, "chunk_rows": chunk, "dx_splits": splits,
                    "parallelism": "single GPU"},
+        "step_ms_median": float(np.median(per_step)),
+        "step_ms_min": float(np.min(per_step)),
+        "first_call_ms": first_call_ms,
         "mfma_frac_step": step_flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
         "step_tflops": step_flops / (ms * 1e-3) / 1e12,
         "peak_bytes": peak,
         "extra_bytes": peak - io_bytes,
+        # bound: one chunk of logits + per-row / per-vocab scratch + split-K partials
+        "extra_bound_bytes": extra_bound,
+        "extra_within_bound": peak - io_bytes <= extra_bound,
         "chunk_logits_bytes": chunk * ((V + 7) // 8 * 8) * e,
         "materialised_logits_bytes": N * V * e,
         "roofline": roofline,
