@@ -32,6 +32,9 @@ Readings where the pages say nothing (each is also listed in the design notes):
     column sum of dZ.
   * shard statistics are taken relative to the shard's own maximum; the target
     logit is 0 when the target is outside the shard or the row is ignored.
+  * distillation loss: the standard Jensen-Shannon divergence (equal weights,
+    M = (P + Q) / 2) between softmax(student / T) and softmax(teacher / T), no
+    T^2 factor; the teacher is frozen; target ids only mask rows.
   * a shard's backward takes the global per-row lse as input (the pages
     exchange the statistics, not the gradient); validity and the mean's
     N_valid are judged against the whole vocabulary.
@@ -337,6 +340,60 @@ def flce_multihead(X, Ws, targets, biases=None, ignore_index=-100, reduction="me
         gb.append(g["bias"])
     return np.array(losses), {"X": gX, "W": np.stack(gW),
                               "bias": None if biases is None else np.stack(gb)}
+
+
+def _log_softmax_rows(Z):
+    Z = _f64(Z)
+    return Z - logsumexp_rows(Z)[:, None]
+
+
+def jsd_rows(Zs, Zt, temperature=1.0):
+    """Per-row Jensen-Shannon divergence between the student and teacher
+    distributions P = softmax(Zs / T), Q = softmax(Zt / T):
+    JSD = 1/2 KL(P || M) + 1/2 KL(Q || M) with M = (P + Q) / 2, and its
+    gradient w.r.t. the student logits Zs:
+    dJSD/dZs = (1/T) P * (g - sum_v P g),  g = 1/2 ln(P / M)
+    (d/dP of the divergence is 1/2 ln(P/M); the softmax Jacobian gives the rest).
+    Returns (jsd [n], dZs [n, V])."""
+    T = float(temperature)
+    lp = _log_softmax_rows(_f64(Zs) / T)
+    lq = _log_softmax_rows(_f64(Zt) / T)
+    P, Q = np.exp(lp), np.exp(lq)
+    mx = np.maximum(lp, lq)
+    lm = mx + np.log(0.5 * (np.exp(lp - mx) + np.exp(lq - mx)))   # ln M, without underflow
+    jsd = 0.5 * (P * (lp - lm)).sum(axis=1) + 0.5 * (Q * (lq - lm)).sum(axis=1)
+    g = 0.5 * (lp - lm)
+    dZ = (P * (g - (P * g).sum(axis=1, keepdims=True))) / T
+    return jsd, dZ
+
+
+def flce_jsd(Xs, Ws, Xt, Wt, targets, temperature=1.0, ignore_index=-100, reduction="mean",
+             row_block=1024):
+    """Fused linear Jensen-Shannon distillation loss (the knowledge-distillation
+    member of the chunked-loss family the Megatron integration page lists): the
+    student head Zs = Xs Ws^T and the frozen teacher head Zt = Xt Wt^T over the
+    same vocabulary; loss rows are the JSD of the tempered distributions, rows
+    whose target is ignore_index (or outside [0, V)) are masked out, reduced
+    like CE. Returns (loss, {"X": grad_Xs, "W": grad_Ws}, info)."""
+    Xs, Ws, Xt, Wt = _f64(Xs), _f64(Ws), _f64(Xt), _f64(Wt)
+    y = np.asarray(targets).astype(np.int64)
+    N = Xs.shape[0]
+    V = Ws.shape[0]
+    valid, _ = target_masks(y, V, ignore_index)
+    n_valid = int(valid.sum())
+    scale = reduction_scale(n_valid, reduction)
+    rows = np.zeros(N)
+    gX = np.zeros_like(Xs)
+    gW = np.zeros_like(Ws)
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        jsd, dZ = jsd_rows(Xs[r0:r1] @ Ws.T, Xt[r0:r1] @ Wt.T, temperature)
+        v = valid[r0:r1]
+        rows[r0:r1] = np.where(v, jsd, 0.0)
+        dZ = scale * dZ * v[:, None]
+        gX[r0:r1] = dZ @ Ws
+        gW += dZ.T @ Xs[r0:r1]
+    return _reduce(rows, n_valid, reduction), {"X": gX, "W": gW}, {"n_valid": n_valid, "loss_rows": rows}
 
 
 def shift_labels(labels, ignore_index=-100):

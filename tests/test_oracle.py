@@ -469,3 +469,77 @@ def test_multihead_finite_differences():
         Xp[i, j] += h
         Xm[i, j] -= h
         assert abs((total(Xp) - total(Xm)) / (2 * h) - g["X"][i, j]) < 1e-8
+
+
+# ------------------------------------------------------------ distillation
+
+def _jsd_brute(zs, zt, T):
+    """Pure-Python Jensen-Shannon divergence of one row (no shifts)."""
+    es = [math.exp(v / T) for v in zs]
+    et = [math.exp(v / T) for v in zt]
+    p = [v / sum(es) for v in es]
+    q = [v / sum(et) for v in et]
+    m = [(a + b) / 2 for a, b in zip(p, q)]
+    return 0.5 * sum(a * math.log(a / c) for a, c in zip(p, m)) + \
+        0.5 * sum(b * math.log(b / c) for b, c in zip(q, m))
+
+
+def test_jsd_brute_force_and_bounds():
+    rng = np.random.default_rng(23)
+    Zs, Zt = rng.standard_normal((6, 9)) * 2, rng.standard_normal((6, 9)) * 2
+    for T in (1.0, 2.5):
+        jsd, _ = O.jsd_rows(Zs, Zt, T)
+        ref = [_jsd_brute(Zs[i], Zt[i], T) for i in range(6)]
+        np.testing.assert_allclose(jsd, ref, rtol=1e-12)
+        assert np.all(jsd >= 0) and np.all(jsd <= math.log(2))
+    # identical distributions: zero divergence and zero gradient
+    jsd, dZ = O.jsd_rows(Zs, Zs + 3.0, 1.0)   # a shift leaves softmax unchanged
+    assert np.abs(jsd).max() < 1e-15 and np.abs(dZ).max() < 1e-15
+    # symmetric in its two distributions
+    np.testing.assert_allclose(O.jsd_rows(Zs, Zt)[0], O.jsd_rows(Zt, Zs)[0], rtol=1e-13)
+    # disjoint one-hot limits approach ln 2
+    big = np.full((1, 4), -60.0)
+    a, b = big.copy(), big.copy()
+    a[0, 0] = 60.0
+    b[0, 3] = 60.0
+    assert abs(O.jsd_rows(a, b)[0][0] - math.log(2)) < 1e-12
+
+
+def test_jsd_gradient_finite_differences():
+    rng = np.random.default_rng(24)
+    Zs, Zt = rng.standard_normal((3, 7)), rng.standard_normal((3, 7))
+    for T in (1.0, 1.7):
+        _, dZ = O.jsd_rows(Zs, Zt, T)
+        h = 1e-6
+        for (i, j) in [(0, 0), (1, 4), (2, 6)]:
+            Zp, Zm = Zs.copy(), Zs.copy()
+            Zp[i, j] += h
+            Zm[i, j] -= h
+            fd = (O.jsd_rows(Zp, Zt, T)[0][i] - O.jsd_rows(Zm, Zt, T)[0][i]) / (2 * h)
+            assert abs(fd - dZ[i, j]) < 1e-8
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_flce_jsd_finite_differences_and_masking(reduction):
+    rng = np.random.default_rng(25)
+    N, Hs, Ht, V = 9, 5, 3, 8
+    Xs, Ws = rng.standard_normal((N, Hs)), rng.standard_normal((V, Hs)) * 0.6
+    Xt, Wt = rng.standard_normal((N, Ht)), rng.standard_normal((V, Ht)) * 0.6
+    y = rng.integers(0, V, N)
+    y[[2, 5]] = -100
+    loss, g, info = O.flce_jsd(Xs, Ws, Xt, Wt, y, temperature=1.5, reduction=reduction, row_block=4)
+    assert np.all(info["loss_rows"][[2, 5]] == 0.0) and np.all(g["X"][[2, 5]] == 0.0)
+
+    def total(Xs_, Ws_):
+        return float(np.sum(O.flce_jsd(Xs_, Ws_, Xt, Wt, y, temperature=1.5, reduction=reduction)[0]))
+    h = 1e-6
+    for (i, j) in [(0, 0), (4, 3)]:
+        Xp, Xm = Xs.copy(), Xs.copy()
+        Xp[i, j] += h
+        Xm[i, j] -= h
+        assert abs((total(Xp, Ws) - total(Xm, Ws)) / (2 * h) - g["X"][i, j]) < 1e-7
+    for (i, j) in [(1, 2), (7, 4)]:
+        Wp, Wm = Ws.copy(), Ws.copy()
+        Wp[i, j] += h
+        Wm[i, j] -= h
+        assert abs((total(Xs, Wp) - total(Xs, Wm)) / (2 * h) - g["W"][i, j]) < 1e-7
