@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--no-vp", action="store_true",
                     help="skip the vocabulary-parallel shard measurement")
     ap.add_argument("--no-mh", action="store_true", help="skip the multi-head measurement")
+    ap.add_argument("--no-distill", action="store_true", help="skip the distillation measurement")
     ap.add_argument("--no-eager", action="store_true",
                     help="skip the PyTorch eager context measurement")
     ap.add_argument("--profile-step", action="store_true",
@@ -371,6 +372,57 @@ def bench_torch_eager(torch, X, W, y, cfg, reps=3):
     return out
 
 
+def bench_distill(torch, B, X, W, y, cfg, n_rows=8192, reps=3):
+    """Jensen-Shannon distillation at the 8B head's shape on the first n_rows
+    token rows: the student is the workload's head, the teacher the same head
+    rolled by 11 vocabulary rows over the hidden states rolled by one row (no
+    new host draws), temperature 2. Per call: student and teacher logits,
+    grad_X and grad_W of the student, 8 x n x H x V flop, plus the row kernel's
+    three passes over both chunk logits."""
+    N, H, V = n_rows, cfg["H"], cfg["V"]
+    Xs = X[:N]
+    Xt = torch.roll(X[:N], shifts=1, dims=0).contiguous()
+    Wt = torch.roll(W, shifts=11, dims=0).contiguous()
+    loss = torch.empty(1, device="cuda")
+    gX = torch.empty(N, H, device="cuda")
+    gW = torch.empty(V, H, device="cuda")
+    ws = torch.empty(B.flce_jsd_workspace_bytes(N, H, V, B.BF16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        B.flce_jsd_forward_backward(Xs, W, Xt, Wt, y[:N], temperature=2.0, reduction=cfg["reduction"],
+                                    grad_X=gX, grad_W=gW, loss=loss, workspace=ws, stream=stream)
+    call()
+    torch.cuda.synchronize()
+    B.flce_timing_reset()
+    B.flce_timing_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    B.flce_timing_enable(False)
+    row_ms, row_n = B.flce_timing_read("row_ce")
+    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm"))
+    B.flce_timing_reset()
+    ms = a.elapsed_time(b) / reps
+    flops = 8.0 * N * H * V
+    out = {
+        "workload": f"JSD distillation, llama8b_head_bf16 student and a rolled teacher (N {N}, "
+                    f"H {H}, V {V}, T 2, {cfg['reduction']})",
+        "ms_per_call": ms, "tokens_per_s": N / (ms * 1e-3),
+        "gemm_tflops": flops / (gemm_ms / reps * 1e-3) / 1e12,
+        "jsd_row_kernel_ms_per_call": row_ms / reps,
+        # bytes moved by the row kernel's three passes: 6 row reads + 1 write per element
+        "jsd_row_kernel_GBps": 7.0 * N * ((V + 7) // 8 * 8) * 2 / (row_ms / reps * 1e-3) / 1e9,
+        "loss": float(loss.item()),
+    }
+    del Xt, Wt, gW, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
     """K LM heads over shared hidden states (the liger README's Medusa example:
     5 heads) at the 8B head's shape on the first n_rows token rows. Head k's
@@ -583,6 +635,9 @@ def main():
     if not args.no_eager:
         log("PyTorch eager context")
         result["torch_eager_context"] = bench_torch_eager(torch, X, W, y, cfg)
+    if not args.no_distill:
+        log("distillation")
+        result["distill"] = bench_distill(torch, B, X, W, y, cfg)
     if not args.no_mh:
         log("multi-head")
         result["multihead"] = bench_multihead(torch, B, X, W, y, cfg)

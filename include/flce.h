@@ -237,6 +237,30 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
                         int64_t chunk_rows, void* stream);
 
 /*
+ * Fused linear Jensen-Shannon distillation (the knowledge-distillation loss
+ * the Megatron integration page lists among Liger's chunked losses): per
+ * chunk of rows, student logits X_s W_s^T and frozen-teacher logits
+ * X_t W_t^T over the same vocabulary, then per row
+ *   JSD = 1/2 KL(P || M) + 1/2 KL(Q || M),  P = softmax(student / T),
+ *   Q = softmax(teacher / T),  M = (P + Q) / 2   (no T^2 factor),
+ * reduced over the rows whose target is not ignore_index (targets only mask
+ * rows; out-of-range ones are reported like FLCE's). Gradients are the
+ * student's only.
+ *   X_s [N, H_s], W_s [V, H_s]; X_t [N, H_t], W_t [V, H_t]; one dtype
+ *   loss [1] or [N] (NONE); grad_X_s [N, H_s], grad_W_s [V, H_s] float32 or NULL
+ *   temperature > 0
+ *   workspace of at least flce_jsd_workspace_bytes(N, H_s, V, dtype, chunk_rows)
+ *   (two chunk buffers: student and teacher logits)
+ */
+size_t flce_jsd_workspace_bytes(int64_t N, int64_t H_s, int64_t V, int dtype, int64_t chunk_rows);
+int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t, const void* W_t,
+                              const int32_t* targets, int64_t N, int64_t H_s, int64_t H_t,
+                              int64_t V, int dtype, int32_t ignore_index, int reduction,
+                              float temperature, float* loss, float* grad_X_s, float* grad_W_s,
+                              void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                              void* stream);
+
+/*
  * Causal-LM targets from token labels (the DeepSpeed vocab-parallel CE page
  * keeps the label shift of causal language modelling as part of the loss
  * contract, "Changes"): labels [B, S] int32 row-major,

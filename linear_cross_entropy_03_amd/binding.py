@@ -44,6 +44,10 @@ _SIGNATURES = {
     "flce_shard_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i32,
                                    _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
     "flce_shift_labels": (_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "flce_jsd_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _i64]),
+    "flce_jsd_forward_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
+                                         _i32, _int, ctypes.c_float, _vp, _vp, _vp, _vp, _sz,
+                                         _i64, _vp]),
     "flce_multihead_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int, _i64]),
     "flce_multihead_forward_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
                                                _i32, _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64,
@@ -348,6 +352,38 @@ def flce_shard_backward(X, W_shard, targets, row_lse, vocab_start, V_global, bia
         _stream(stream))
     _check(st, "flce_shard_backward")
     return gX, gW, gb
+
+
+def flce_jsd_workspace_bytes(N, H_s, V, dtype=BF16, chunk_rows=0):
+    return int(lib().flce_jsd_workspace_bytes(N, H_s, V, dtype, chunk_rows))
+
+
+def flce_jsd_forward_backward(X_s, W_s, X_t, W_t, targets, temperature=1.0, ignore_index=-100,
+                              reduction="mean", grad_X=True, grad_W=True, loss=None,
+                              workspace=None, chunk_rows=0, stream=None):
+    """Jensen-Shannon distillation of a student head (X_s, W_s) towards a
+    frozen teacher head (X_t, W_t). Returns (loss, grad_X_s, grad_W_s)."""
+    N, Hs = X_s.shape
+    V = W_s.shape[0]
+    Ht = X_t.shape[1]
+    dev = X_s.device
+    dt = _dtype_code(X_s)
+    gX = _grad_arg(grad_X, (N, Hs), dev)
+    gW = _grad_arg(grad_W, (V, Hs), dev)
+    if loss is None:
+        loss = _empty((N,) if reduction == "none" else (1,), torch.float32, dev)
+    if workspace is None:
+        workspace = _empty((max(1, flce_jsd_workspace_bytes(N, Hs, V, dt, chunk_rows)),),
+                           torch.uint8, dev)
+    st = lib().flce_jsd_forward_backward(
+        _ptr(X_s, "X_s"), _ptr(W_s, "W_s", X_s.dtype), _ptr(X_t, "X_t", X_s.dtype),
+        _ptr(W_t, "W_t", X_s.dtype), _ptr(targets, "targets", torch.int32), N, Hs, Ht, V, dt,
+        ignore_index, _red(reduction), float(temperature), _ptr(loss, "loss", torch.float32),
+        _ptr(gX, "grad_X_s", torch.float32), _ptr(gW, "grad_W_s", torch.float32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
+        _stream(stream))
+    _check(st, "flce_jsd_forward_backward")
+    return loss, gX, gW
 
 
 def flce_shift_labels(labels, ignore_index=-100, out=None, stream=None):

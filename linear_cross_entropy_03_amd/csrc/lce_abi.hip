@@ -644,6 +644,102 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
   return FLCE_OK;
 }
 
+size_t flce_jsd_workspace_bytes(int64_t N, int64_t H_s, int64_t V, int dtype, int64_t chunk_rows) {
+  Plan p;
+  if (!make_plan(N, H_s, V, dtype, chunk_rows, &p)) return 0;
+  return p.total + align_up(static_cast<size_t>(p.chunk) * static_cast<size_t>(p.ldz) * elem_bytes(dtype));
+}
+
+int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t, const void* W_t,
+                              const int32_t* targets, int64_t N, int64_t H_s, int64_t H_t,
+                              int64_t V, int dtype, int32_t ignore_index, int reduction,
+                              float temperature, float* loss, float* grad_X_s, float* grad_W_s,
+                              void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                              void* stream) {
+  int st = validate_flce(X_s, W_s, nullptr, targets, N, H_s, V, dtype, reduction, loss, grad_X_s,
+                         grad_W_s, nullptr, chunk_rows, workspace);
+  if (st != FLCE_OK) return st;
+  if (W_t == nullptr || H_t <= 0 || !(temperature > 0.0f)) return FLCE_E_INVALID_ARG;
+  if (N > 0 && X_t == nullptr) return FLCE_E_INVALID_ARG;
+  if (H_t >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  if ((X_t != nullptr && !aligned16(X_t)) || !aligned16(W_t)) return FLCE_E_UNSUPPORTED;
+  if (is16(dtype) && (H_t % 8) != 0) return FLCE_E_UNSUPPORTED;
+  if (!gemm16_fits(dtype, H_t, V)) return FLCE_E_UNSUPPORTED;
+  Plan p;
+  if (!make_plan(N, H_s, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
+  const size_t e = elem_bytes(dtype);
+  const size_t tbuf = p.total;  // the teacher's chunk logits follow the FLCE layout
+  if (workspace == nullptr ||
+      workspace_bytes < tbuf + align_up(static_cast<size_t>(p.chunk) * static_cast<size_t>(p.ldz) * e))
+    return FLCE_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  float* loss_rows = reduction == FLCE_REDUCTION_NONE ? loss : reinterpret_cast<float*>(ws + p.off_rows);
+  void* zs = ws + p.off_chunk;
+  void* zt = ws + tbuf;
+  float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
+  auto gemm = [dtype](const GemmDesc& d, hipStream_t st2) { return gemm_for(dtype, d, st2); };
+  const float inv_tau = 1.0f / temperature;
+
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
+  }));
+  if (N == 0 && grad_W_s)
+    LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W_s, V * H_s, 0.0f, s); }));
+  for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
+    const int64_t rows = std::min(p.chunk, N - r0);
+    const bool first = r0 == 0;
+    const char* Xs_c = static_cast<const char*>(X_s) + static_cast<size_t>(r0) * H_s * e;
+    const char* Xt_c = static_cast<const char*>(X_t) + static_cast<size_t>(r0) * H_t * e;
+    GemmDesc gs{};
+    gs.A = Xs_c; gs.lda = H_s; gs.a_kmajor = true;
+    gs.B = W_s; gs.ldb = H_s; gs.b_kmajor = true;
+    gs.C = zs; gs.ldc = p.ldz; gs.M = rows; gs.N = V; gs.K = H_s;
+    gs.epilogue = kEpiLogits; gs.k_splits = 1;
+    LCE_TRY(timed(kKindLogits, s, [&] { return gemm(gs, s); }));
+    GemmDesc gt = gs;
+    gt.A = Xt_c; gt.lda = H_t; gt.B = W_t; gt.ldb = H_t; gt.C = zt; gt.K = H_t;
+    LCE_TRY(timed(kKindLogits, s, [&] { return gemm(gt, s); }));
+    LCE_TRY(timed(kKindRowCE, s, [&] {
+      return launch_row_jsd(dtype, zs, zt, p.ldz, rows, V, p.ldz - V, inv_tau, targets + r0,
+                            ignore_index, hdr, loss_rows + r0, s);
+    }));
+    if (grad_X_s) {
+      GemmDesc g2{};
+      g2.A = zs; g2.lda = p.ldz; g2.a_kmajor = true;
+      g2.B = W_s; g2.ldb = H_s; g2.b_kmajor = false;
+      g2.M = rows; g2.N = H_s; g2.K = V;
+      g2.epilogue = kEpiStoreF32;
+      float* out = grad_X_s + static_cast<size_t>(r0) * H_s;
+      if (p.dx_splits > 1) {
+        g2.C = split_buf; g2.ldc = H_s; g2.k_splits = p.dx_splits; g2.split_stride = rows * H_s;
+        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+        LCE_TRY(timed(kKindOther, s, [&] {
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H_s, rows, H_s, H_s, out, false, s);
+        }));
+      } else {
+        g2.C = out; g2.ldc = H_s; g2.k_splits = 1;
+        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+      }
+    }
+    if (grad_W_s) {
+      GemmDesc g3{};
+      g3.A = zs; g3.lda = p.ldz; g3.a_kmajor = false;
+      g3.B = Xs_c; g3.ldb = H_s; g3.b_kmajor = false;
+      g3.C = grad_W_s; g3.ldc = H_s; g3.M = V; g3.N = H_s; g3.K = rows;
+      g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32; g3.k_splits = 1;
+      LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
+    }
+  }
+  if (reduction != FLCE_REDUCTION_NONE)
+    LCE_TRY(timed(kKindOther, s, [&] {
+      return launch_reduce_loss(loss_rows, N, hdr, reduction, loss, s);
+    }));
+  return FLCE_OK;
+}
+
 int flce_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ignore_index,
                       int32_t* targets, void* stream) {
   if (B < 0 || S <= 0) return FLCE_E_INVALID_ARG;

@@ -224,6 +224,9 @@ hipError_t launch_shard_grad(int dtype, void* Z, int64_t ldz, int64_t rows, int6
 hipError_t launch_combine_stats(const float* ms, const float* ss, const float* ts, int64_t P,
                                 int64_t N, const int32_t* targets, int32_t ign, int64_t V_global,
                                 float* lse, float* loss_rows, hipStream_t s);
+hipError_t launch_row_jsd(int dtype, void* S, const void* Tt, int64_t ld, int64_t rows, int64_t V,
+                          int64_t pad_cols, float inv_tau, const int32_t* targets, int32_t ign,
+                          const WsHeader* hdr, float* loss_rows, hipStream_t s);
 hipError_t launch_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ign,
                                int32_t* targets, hipStream_t s);
 hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader* hdr,

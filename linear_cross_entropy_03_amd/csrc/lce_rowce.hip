@@ -578,6 +578,148 @@ hipError_t launch_combine_stats(const float* ms, const float* ss, const float* t
   return hipGetLastError();
 }
 
+// ------------------------------------------------------ JSD distillation
+
+// One row of the Jensen-Shannon distillation loss from the student logits S
+// and the teacher logits T of the same row (both [V], same type), temperature
+// tau: with ls = log softmax(S / tau), lt = log softmax(T / tau) and
+// lm = ln((e^ls + e^lt) / 2), loss = 1/2 sum(e^ls (ls - lm)) + 1/2
+// sum(e^lt (lt - lm)); the student gradient overwrites S:
+// dS = c / tau * e^ls * (g - sum(e^ls g)), g = 1/2 (ls - lm), c the
+// reduction scale (0 for masked rows). Three streaming passes: the two
+// row statistics, the loss and sum(e^ls g), the gradient.
+template <typename T, int kThreads>
+__global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t ld, int64_t V,
+                                                      int64_t pad_cols, float inv_tau,
+                                                      const int32_t* __restrict__ targets,
+                                                      int32_t ign, const WsHeader* __restrict__ hdr,
+                                                      float* __restrict__ loss_rows) {
+  using E = Elem<T>;
+  constexpr int kVec = E::kVec;
+  __shared__ float red0[kThreads / 64], red1[kThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  T* s = S + row * ld;
+  const T* t = Tt + row * ld;
+  const int32_t y = targets[row];
+  const bool valid = (y != ign) && y >= 0 && static_cast<int64_t>(y) < V;
+  // The two buffers share one row stride, so both rows split alike.
+  const RowSplit rs = split_row(static_cast<const T*>(s), V);
+  const uint4* sv = reinterpret_cast<const uint4*>(s + rs.head);
+  const uint4* tv = reinterpret_cast<const uint4*>(t + rs.head);
+
+  // Pass 1: online (max, sum exp) of both tempered rows.
+  float ms = -INFINITY, ss = 0.0f, mt = -INFINITY, st = 0.0f;
+  for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+    float a[kVec], b[kVec];
+    E::unpack(sv[vi], a);
+    E::unpack(tv[vi], b);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) { a[i] *= inv_tau; b[i] *= inv_tau; }
+    online_push_vec<kVec>(ms, ss, a);
+    online_push_vec<kVec>(mt, st, b);
+  }
+  auto scalar_at = [&](int64_t v, float& a, float& b) {
+    a = E::load(s + v) * inv_tau;
+    b = E::load(t + v) * inv_tau;
+  };
+  if (tid < rs.head) { float a, b; scalar_at(tid, a, b); online_push(ms, ss, a); online_push(mt, st, b); }
+  if (tid < V - rs.tail0) {
+    float a, b;
+    scalar_at(rs.tail0 + tid, a, b);
+    online_push(ms, ss, a);
+    online_push(mt, st, b);
+  }
+  float Ms, Ss, Mt, St;
+  block_lse_parts<kThreads>(ms, ss, red0, red1, Ms, Ss);
+  __syncthreads();
+  block_lse_parts<kThreads>(mt, st, red0, red1, Mt, St);
+  const float lse_s = Ms + __builtin_amdgcn_logf(Ss) * kLn2;
+  const float lse_t = Mt + __builtin_amdgcn_logf(St) * kLn2;
+
+  // Per element: the log-probabilities, ln M (log-sum-exp of two, so it
+  // cannot underflow), the loss terms and sum(e^ls g).
+  auto terms = [&](float a, float b, float& lp, float& lm) {
+    lp = a - lse_s;
+    const float lq = b - lse_t;
+    const float mx = fmaxf(lp, lq);
+    lm = mx + __builtin_amdgcn_logf(0.5f * (__builtin_amdgcn_exp2f((lp - mx) * kLog2e) +
+                                            __builtin_amdgcn_exp2f((lq - mx) * kLog2e))) * kLn2;
+    return lq;
+  };
+  float loss = 0.0f, gbar = 0.0f;
+  auto accumulate = [&](float a, float b) {
+    float lp, lm;
+    const float lq = terms(a, b, lp, lm);
+    const float p = __builtin_amdgcn_exp2f(lp * kLog2e), q = __builtin_amdgcn_exp2f(lq * kLog2e);
+    loss += 0.5f * (p * (lp - lm) + q * (lq - lm));
+    gbar += p * 0.5f * (lp - lm);
+  };
+  // Pass 2.
+  for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+    float a[kVec], b[kVec];
+    E::unpack(sv[vi], a);
+    E::unpack(tv[vi], b);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) accumulate(a[i] * inv_tau, b[i] * inv_tau);
+  }
+  if (tid < rs.head) { float a, b; scalar_at(tid, a, b); accumulate(a, b); }
+  if (tid < V - rs.tail0) { float a, b; scalar_at(rs.tail0 + tid, a, b); accumulate(a, b); }
+  __syncthreads();
+  const float L = block_sum<kThreads>(loss, red0);
+  const float Gb = block_sum<kThreads>(gbar, red1);
+  if (tid == 0) loss_rows[row] = valid ? L : 0.0f;
+
+  // Pass 3: the student gradient, in place.
+  const float c = valid ? hdr->scale * inv_tau : 0.0f;
+  auto grad = [&](float a, float b) -> float {
+    float lp, lm;
+    terms(a, b, lp, lm);
+    return c * __builtin_amdgcn_exp2f(lp * kLog2e) * (0.5f * (lp - lm) - Gb);
+  };
+  uint4* svw = reinterpret_cast<uint4*>(s + rs.head);
+  for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+    float a[kVec], b[kVec];
+    E::unpack(sv[vi], a);
+    E::unpack(tv[vi], b);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) a[i] = valid ? grad(a[i] * inv_tau, b[i] * inv_tau) : 0.0f;
+    svw[vi] = E::pack(a);
+  }
+  // Scalar head and tail: each lane owns one element, read before it writes.
+  if (tid < rs.head) {
+    float a, b;
+    scalar_at(tid, a, b);
+    E::store(s + tid, valid ? grad(a, b) : 0.0f);
+  }
+  if (tid < V - rs.tail0) {
+    float a, b;
+    scalar_at(rs.tail0 + tid, a, b);
+    E::store(s + rs.tail0 + tid, valid ? grad(a, b) : 0.0f);
+  }
+  if (tid < pad_cols) E::store(s + V + tid, 0.0f);
+}
+
+hipError_t launch_row_jsd(int dtype, void* S, const void* Tt, int64_t ld, int64_t rows, int64_t V,
+                          int64_t pad_cols, float inv_tau, const int32_t* targets, int32_t ign,
+                          const WsHeader* hdr, float* loss_rows, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(rows));
+  if (dtype == 1)
+    hipLaunchKernelGGL((k_row_jsd<uint16_t, 1024>), grid, dim3(1024), 0, s, static_cast<uint16_t*>(S),
+                       static_cast<const uint16_t*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
+                       loss_rows);
+  else if (dtype == 2)
+    hipLaunchKernelGGL((k_row_jsd<Half, 1024>), grid, dim3(1024), 0, s, static_cast<Half*>(S),
+                       static_cast<const Half*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
+                       loss_rows);
+  else
+    hipLaunchKernelGGL((k_row_jsd<float, 1024>), grid, dim3(1024), 0, s, static_cast<float*>(S),
+                       static_cast<const float*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
+                       loss_rows);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------ causal label shift
 
 // targets[b * S + s] = labels[b * S + s + 1] for s < S - 1, ignore_index at

@@ -165,3 +165,23 @@ def test_16bit_stride_limit(B):
     assert _fb(B, V=big - 3) == B.E_UNSUPPORTED          # rounds up to 2^22
     assert _fb(B, dtype=B.F16, V=big + 8) == B.E_UNSUPPORTED
     assert _fb(B, dtype=B.F32, H=big, wsb=64) == B.E_WORKSPACE   # fp32 path has no such limit
+
+
+def test_jsd_argument_errors(B):
+    L = B.lib()
+
+    def jsd(**kw):
+        a = dict(Xs=16, Ws=16, Xt=16, Wt=16, y=16, N=4, Hs=8, Ht=8, V=10, dt=B.BF16, red=2, T=1.0,
+                 loss=16, gX=16, gW=16, ws=16, wsb=1 << 30)
+        a.update(kw)
+        return L.flce_jsd_forward_backward(a["Xs"], a["Ws"], a["Xt"], a["Wt"], a["y"], a["N"], a["Hs"],
+                                           a["Ht"], a["V"], a["dt"], -100, a["red"], a["T"], a["loss"],
+                                           a["gX"], a["gW"], a["ws"], a["wsb"], 0, None)
+    assert jsd(T=0.0) == B.E_INVALID_ARG
+    assert jsd(T=-1.0) == B.E_INVALID_ARG
+    assert jsd(Wt=None) == B.E_INVALID_ARG
+    assert jsd(Xt=None) == B.E_INVALID_ARG
+    assert jsd(Ht=12) == B.E_UNSUPPORTED
+    assert jsd(Xt=24) == B.E_UNSUPPORTED
+    assert jsd(wsb=B.flce_workspace_bytes(4, 8, 10)) == B.E_WORKSPACE
+    assert B.flce_jsd_workspace_bytes(4, 8, 10) > B.flce_workspace_bytes(4, 8, 10)

@@ -278,3 +278,49 @@ def test_multihead_against_oracle(B, dtype, K, reduction, chunk, shape):
         check_max_rel(gW[k], ref_g["W"][k], t["grad"], f"grad_W head {k}")
         if bs is not None:
             check_max_rel(gb[k], ref_g["bias"][k], t["grad"], f"grad_bias head {k}")
+
+
+def _run_jsd(B, s_inp, t_inp, temperature, reduction, chunk_rows=0):
+    import torch
+    dt = s_inp["dtype"]
+    loss, gX, gW = B.flce_jsd_forward_backward(
+        to_dev(s_inp["X"], dt), to_dev(s_inp["W"], dt), to_dev(t_inp["X"], dt), to_dev(t_inp["W"], dt),
+        to_dev(s_inp["targets"], "i32"), temperature=temperature, reduction=reduction,
+        chunk_rows=chunk_rows)
+    torch.cuda.synchronize()
+    return to_host(loss), to_host(gX), to_host(gW)
+
+
+@pytest.mark.parametrize("dtype,reduction,temperature,chunk", [
+    ("bf16", "mean", 1.0, 256), ("f32", "none", 2.0, 0), ("f16", "sum", 1.5, 0)])
+def test_jsd_distillation_against_oracle(B, dtype, reduction, temperature, chunk):
+    """Student (H 136) distilled towards a teacher with another hidden size
+    (H 72) over a ragged vocabulary (V 1000); 10% of rows masked."""
+    N, Hs, Ht, V = 600, 136, 72, 1000
+    s_inp = synth.make_flce_inputs(N, Hs, V, dtype, w_std=0.08, ignore_frac=0.1, seed=60)
+    t_inp = synth.make_flce_inputs(N, Ht, V, dtype, w_std=0.12, ignore_frac=0.0, seed=61)
+    say("jsd", dtype, reduction, temperature, chunk)
+    loss, gX, gW = _run_jsd(B, s_inp, t_inp, temperature, reduction, chunk)
+    f = lambda a: np.asarray(a, np.float64)
+    ref_loss, ref_g, info = O.flce_jsd(f(s_inp["X_f32"]), f(s_inp["W_f32"]), f(t_inp["X_f32"]),
+                                       f(t_inp["W_f32"]), s_inp["targets"], temperature=temperature,
+                                       reduction=reduction)
+    t = TOL[dtype]
+    if reduction == "none":
+        check_max_rel(loss, ref_loss, t["loss"], "JSD rows")
+    else:
+        check_scalar(loss, ref_loss, t["loss"], "JSD")
+    check_max_rel(gX, ref_g["X"], t["grad"], "grad_X student")
+    check_max_rel(gW, ref_g["W"], t["grad"], "grad_W student")
+    masked = s_inp["targets"] == -100
+    assert np.all(gX[masked] == 0.0)
+
+
+def test_jsd_teacher_equal_to_student_is_exactly_zero(B):
+    """Identical heads give identical logits on both sides: the divergence and
+    every gradient are exactly zero."""
+    inp = synth.make_flce_inputs(512, 64, 3000, "bf16", w_std=0.1, ignore_frac=0.05, seed=62)
+    say("jsd identical heads")
+    loss, gX, gW = _run_jsd(B, inp, inp, 1.0, "sum")
+    assert float(loss[0]) == 0.0
+    assert np.all(gX == 0.0) and np.all(gW == 0.0)
