@@ -324,3 +324,18 @@ def test_jsd_teacher_equal_to_student_is_exactly_zero(B):
     loss, gX, gW = _run_jsd(B, inp, inp, 1.0, "sum")
     assert float(loss[0]) == 0.0
     assert np.all(gX == 0.0) and np.all(gW == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N,H,V", [(1, 8, 1), (2, 8, 3), (257, 8, 9), (3, 16, 70001)])
+def test_degenerate_shapes(B, dtype, N, H, V):
+    """One row, one class (loss and gradients exactly 0), the smallest bf16
+    hidden size, a ragged single row tile, and a long row over very few rows."""
+    inp = synth.make_flce_inputs(N, H, V, dtype, w_std=0.3, ignore_frac=0.0, seed=N + V)
+    say("flce degenerate", dtype, N, H, V)
+    got = run_flce(B, inp, "mean")
+    if V == 1:
+        assert float(got[0][0]) == 0.0
+        assert np.all(got[1] == 0.0) and np.all(got[2] == 0.0)
+    else:
+        check_against_oracle(inp, "mean", got, want=("X", "W"))
