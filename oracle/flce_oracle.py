@@ -35,6 +35,9 @@ Readings where the pages say nothing (each is also listed in the design notes):
   * distillation loss: the standard Jensen-Shannon divergence (equal weights,
     M = (P + Q) / 2) between softmax(student / T) and softmax(teacher / T), no
     T^2 factor; the teacher is frozen; target ids only mask rows.
+  * DPO: the standard sigmoid preference loss on sequence log-probabilities
+    summed over non-ignored target tokens, reference log-probabilities given
+    as inputs, mean over pairs.
   * a shard's backward takes the global per-row lse as input (the pages
     exchange the statistics, not the gradient); validity and the mean's
     N_valid are judged against the whole vocabulary.
@@ -394,6 +397,50 @@ def flce_jsd(Xs, Ws, Xt, Wt, targets, temperature=1.0, ignore_index=-100, reduct
         gX[r0:r1] = dZ @ Ws
         gW += dZ.T @ Xs[r0:r1]
     return _reduce(rows, n_valid, reduction), {"X": gX, "W": gW}, {"n_valid": n_valid, "loss_rows": rows}
+
+
+def flce_dpo(X, W, targets, n_pairs, seq_len, ref_logps, beta=0.1, ignore_index=-100,
+             row_block=1024):
+    """Fused linear DPO loss (the alignment member of the chunked-loss family
+    on the Megatron integration page; the torchtune blog plans its recipe):
+    X holds 2 * n_pairs sequences of seq_len token rows, the n_pairs chosen
+    sequences first, then the rejected ones in the same pair order. A
+    sequence's log-probability is the sum over its non-ignored rows of
+    log softmax(x W^T)[target] = -(CE row loss); with the reference model's
+    sequence log-probabilities ref_logps [2 * n_pairs] (same order),
+      d_b = beta * ((logp_w - ref_w) - (logp_l - ref_l)),
+      loss = mean_b softplus(-d_b)  (= -log sigmoid(d_b)).
+    Gradients: each token row of pair b gets dZ = s (softmax - onehot) with
+    s = +beta sigmoid(-d_b) / n_pairs on chosen rows and the negative on
+    rejected rows. Returns (loss, {"X", "W"}, {"logps", "d", "pair_loss"})."""
+    X, W = _f64(X), _f64(W)
+    y = np.asarray(targets).astype(np.int64)
+    N = X.shape[0]
+    assert N == 2 * n_pairs * seq_len
+    V = W.shape[0]
+    valid, _ = target_masks(y, V, ignore_index)
+    loss_rows = np.zeros(N)
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        lr, _ = _rows_loss_and_dlogits(X[r0:r1] @ W.T, y[r0:r1], valid[r0:r1], 1.0)
+        loss_rows[r0:r1] = lr
+    logps = -loss_rows.reshape(2 * n_pairs, seq_len).sum(axis=1)
+    ref = _f64(ref_logps)
+    d = beta * ((logps[:n_pairs] - ref[:n_pairs]) - (logps[n_pairs:] - ref[n_pairs:]))
+    pair_loss = np.logaddexp(0.0, -d)
+    sig = 1.0 / (1.0 + np.exp(d))                      # sigmoid(-d)
+    coef = np.concatenate([beta * sig, -beta * sig]) / n_pairs
+    row_scale = np.repeat(coef, seq_len)
+    gX = np.zeros_like(X)
+    gW = np.zeros_like(W)
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        _, dZ = _rows_loss_and_dlogits(X[r0:r1] @ W.T, y[r0:r1], valid[r0:r1], 1.0)
+        dZ = dZ * row_scale[r0:r1, None]
+        gX[r0:r1] = dZ @ W
+        gW += dZ.T @ X[r0:r1]
+    return float(pair_loss.mean()), {"X": gX, "W": gW}, {"logps": logps, "d": d,
+                                                         "pair_loss": pair_loss}
 
 
 def shift_labels(labels, ignore_index=-100):

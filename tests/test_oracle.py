@@ -543,3 +543,60 @@ def test_flce_jsd_finite_differences_and_masking(reduction):
         Wp[i, j] += h
         Wm[i, j] -= h
         assert abs((total(Xs, Wp) - total(Xs, Wm)) / (2 * h) - g["W"][i, j]) < 1e-7
+
+
+# -------------------------------------------------------------------- DPO
+
+def _dpo_problem(rng, P=3, S=5, H=4, V=7):
+    X = rng.standard_normal((2 * P * S, H))
+    W = rng.standard_normal((V, H)) * 0.7
+    y = rng.integers(0, V, 2 * P * S)
+    y[[0, 1, P * S, P * S + 1]] = -100       # prompt tokens of two sequences
+    ref = rng.standard_normal(2 * P) - 10.0
+    return X, W, y, ref
+
+
+def test_dpo_logps_and_closed_form():
+    rng = np.random.default_rng(26)
+    P, S = 3, 5
+    X, W, y, ref = _dpo_problem(rng, P, S)
+    loss, g, info = O.flce_dpo(X, W, y, P, S, ref, beta=0.3)
+    # sequence log-probabilities by brute force
+    for k in range(2 * P):
+        lp = 0.0
+        for r in range(k * S, (k + 1) * S):
+            if y[r] == -100:
+                continue
+            z = X[r] @ W.T
+            lp += z[y[r]] - math.log(sum(math.exp(v) for v in z))
+        assert abs(info["logps"][k] - lp) < 1e-12
+    d = 0.3 * ((info["logps"][:P] - ref[:P]) - (info["logps"][P:] - ref[P:]))
+    ref_loss = np.mean([-math.log(1.0 / (1.0 + math.exp(-v))) for v in d])
+    assert abs(loss - ref_loss) < 1e-12
+    # swapping chosen and rejected turns d into -d
+    Xs = np.concatenate([X[P * S:], X[:P * S]])
+    ys = np.concatenate([y[P * S:], y[:P * S]])
+    refs = np.concatenate([ref[P:], ref[:P]])
+    _, _, info2 = O.flce_dpo(Xs, W, ys, P, S, refs, beta=0.3)
+    np.testing.assert_allclose(info2["d"], -info["d"], rtol=1e-12)
+
+
+def test_dpo_finite_differences():
+    rng = np.random.default_rng(27)
+    P, S = 2, 4
+    X, W, y, ref = _dpo_problem(rng, P, S, H=3, V=5)
+    loss, g, _ = O.flce_dpo(X, W, y, P, S, ref, beta=0.5)
+    h = 1e-6
+    for (i, j) in [(2, 0), (9, 2)]:
+        Xp, Xm = X.copy(), X.copy()
+        Xp[i, j] += h
+        Xm[i, j] -= h
+        fd = (O.flce_dpo(Xp, W, y, P, S, ref, beta=0.5)[0] - O.flce_dpo(Xm, W, y, P, S, ref, beta=0.5)[0]) / (2 * h)
+        assert abs(fd - g["X"][i, j]) < 1e-8
+    for (i, j) in [(0, 1), (4, 2)]:
+        Wp, Wm = W.copy(), W.copy()
+        Wp[i, j] += h
+        Wm[i, j] -= h
+        fd = (O.flce_dpo(X, Wp, y, P, S, ref, beta=0.5)[0] - O.flce_dpo(X, Wm, y, P, S, ref, beta=0.5)[0]) / (2 * h)
+        assert abs(fd - g["W"][i, j]) < 1e-8
+    assert np.all(g["X"][[0, 1, P * S, P * S + 1]] == 0.0)   # ignored tokens get no gradient
