@@ -43,6 +43,7 @@ def parse():
                     help="skip the vocabulary-parallel shard measurement")
     ap.add_argument("--no-mh", action="store_true", help="skip the multi-head measurement")
     ap.add_argument("--no-distill", action="store_true", help="skip the distillation measurement")
+    ap.add_argument("--no-dpo", action="store_true", help="skip the DPO measurement")
     ap.add_argument("--no-eager", action="store_true",
                     help="skip the PyTorch eager context measurement")
     ap.add_argument("--profile-step", action="store_true",
@@ -423,6 +424,59 @@ def bench_distill(torch, B, X, W, y, cfg, n_rows=8192, reps=3):
     return out
 
 
+def bench_dpo(torch, B, X, W, y, cfg, n_pairs=4, seq_len=1024, reps=3):
+    """DPO at the 8B head's shape: the first 2 * n_pairs * seq_len token rows
+    as n_pairs chosen and n_pairs rejected sequences, the first quarter of
+    each sequence masked as prompt, synthetic reference log-probabilities
+    (about what a uniform model gives the responses), beta 0.1."""
+    N, H, V = 2 * n_pairs * seq_len, cfg["H"], cfg["V"]
+    Xd = X[:N]
+    yd = y[:N].clone()
+    for k in range(2 * n_pairs):
+        yd[k * seq_len:k * seq_len + seq_len // 4] = -100
+    g = torch.Generator(device="cpu").manual_seed(0)
+    ref = (torch.randn(2 * n_pairs, generator=g) * 3.0 - (3 * seq_len // 4) * float(np.log(V))).cuda()
+    loss = torch.empty(1, device="cuda")
+    gX = torch.empty(N, H, device="cuda")
+    gW = torch.empty(V, H, device="cuda")
+    ws = torch.empty(B.flce_dpo_workspace_bytes(n_pairs, seq_len, H, V, B.BF16), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        B.flce_dpo_forward_backward(Xd, W, yd, n_pairs, seq_len, ref, beta=0.1, grad_X=gX, grad_W=gW,
+                                    pair_loss=False, loss=loss, workspace=ws, stream=stream)
+    call()
+    torch.cuda.synchronize()
+    B.flce_timing_reset()
+    B.flce_timing_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    B.flce_timing_enable(False)
+    logit_ms, logit_n = B.flce_timing_read("logits_gemm")
+    gemm_ms = logit_ms + sum(B.flce_timing_read(k)[0] for k in ("grad_x_gemm", "grad_w_gemm"))
+    B.flce_timing_reset()
+    ms = a.elapsed_time(b) / reps
+    chunk = B.flce_plan(N, H, V, B.BF16)[0]
+    n_logits = logit_n / reps                      # logits GEMMs per call (1 or 2 per chunk)
+    flops = (4.0 + 2.0 * n_logits * chunk / N) * N * H * V
+    out = {
+        "workload": f"DPO, {n_pairs} pairs x 2 x {seq_len} tokens over the llama8b_head_bf16 head "
+                    f"(N {N}, H {H}, V {V}, beta 0.1, prompt quarter masked)",
+        "ms_per_call": ms, "tokens_per_s": N / (ms * 1e-3),
+        "logits_gemms_per_call": n_logits,
+        "gemm_tflops": flops / (gemm_ms / reps * 1e-3) / 1e12,
+        "loss": float(loss.item()),
+    }
+    del gW, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
     """K LM heads over shared hidden states (the liger README's Medusa example:
     5 heads) at the 8B head's shape on the first n_rows token rows. Head k's
@@ -638,6 +692,9 @@ def main():
     if not args.no_distill:
         log("distillation")
         result["distill"] = bench_distill(torch, B, X, W, y, cfg)
+    if not args.no_dpo:
+        log("DPO")
+        result["dpo"] = bench_dpo(torch, B, X, W, y, cfg)
     if not args.no_mh:
         log("multi-head")
         result["multihead"] = bench_multihead(torch, B, X, W, y, cfg)

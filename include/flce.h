@@ -261,6 +261,31 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
                               void* stream);
 
 /*
+ * Fused linear DPO (the alignment loss the Megatron integration page lists
+ * among Liger's chunked losses and the torchtune blog plans a recipe for):
+ * X holds 2 * n_pairs sequences of seq_len token rows, the chosen sequences
+ * first, then the rejected ones in the same pair order; targets [N] mark the
+ * response tokens (ignore_index elsewhere). A sequence's log-probability is
+ * the sum of log softmax(x W^T)[target] over its non-ignored rows; with the
+ * reference log-probabilities ref_logps [2 * n_pairs] (same order),
+ *   d_b = beta ((logp_w - ref_w) - (logp_l - ref_l)),
+ *   loss = mean_b softplus(-d_b) = mean_b -log sigmoid(d_b)
+ * Two passes over the chunks: the token log-probabilities, then the logits
+ * again (skipped when every row fits one chunk) weighted per row by
+ * +-beta sigmoid(-d_b) / n_pairs for the gradient products.
+ *   loss [1]; pair_loss [n_pairs] or NULL; grad_X [N, H], grad_W [V, H] or NULL
+ *   beta > 0; workspace of at least flce_dpo_workspace_bytes(...)
+ */
+size_t flce_dpo_workspace_bytes(int64_t n_pairs, int64_t seq_len, int64_t H, int64_t V, int dtype,
+                                int64_t chunk_rows);
+int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targets, int64_t n_pairs,
+                              int64_t seq_len, int64_t H, int64_t V, int dtype,
+                              int32_t ignore_index, const float* ref_logps, float beta,
+                              float* loss, float* pair_loss, float* grad_X, float* grad_W,
+                              void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                              void* stream);
+
+/*
  * Causal-LM targets from token labels (the DeepSpeed vocab-parallel CE page
  * keeps the label shift of causal language modelling as part of the loss
  * contract, "Changes"): labels [B, S] int32 row-major,

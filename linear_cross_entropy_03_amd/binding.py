@@ -44,6 +44,9 @@ _SIGNATURES = {
     "flce_shard_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i32,
                                    _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
     "flce_shift_labels": (_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "flce_dpo_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int, _i64]),
+    "flce_dpo_forward_backward": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _i32, _vp,
+                                         ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
     "flce_jsd_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _i64]),
     "flce_jsd_forward_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
                                          _i32, _int, ctypes.c_float, _vp, _vp, _vp, _vp, _sz,
@@ -384,6 +387,39 @@ def flce_jsd_forward_backward(X_s, W_s, X_t, W_t, targets, temperature=1.0, igno
         _stream(stream))
     _check(st, "flce_jsd_forward_backward")
     return loss, gX, gW
+
+
+def flce_dpo_workspace_bytes(n_pairs, seq_len, H, V, dtype=BF16, chunk_rows=0):
+    return int(lib().flce_dpo_workspace_bytes(n_pairs, seq_len, H, V, dtype, chunk_rows))
+
+
+def flce_dpo_forward_backward(X, W, targets, n_pairs, seq_len, ref_logps, beta=0.1,
+                              ignore_index=-100, grad_X=True, grad_W=True, pair_loss=True,
+                              loss=None, workspace=None, chunk_rows=0, stream=None):
+    """DPO over 2 * n_pairs sequences of seq_len rows (chosen first).
+    Returns (loss [1], pair_loss [n_pairs] or None, grad_X, grad_W)."""
+    N, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    dt = _dtype_code(X)
+    gX = _grad_arg(grad_X, (N, H), dev)
+    gW = _grad_arg(grad_W, (V, H), dev)
+    pl = pair_loss if isinstance(pair_loss, torch.Tensor) else (
+        _empty((max(1, n_pairs),), torch.float32, dev) if pair_loss else None)
+    if loss is None:
+        loss = _empty((1,), torch.float32, dev)
+    if workspace is None:
+        workspace = _empty((max(1, flce_dpo_workspace_bytes(n_pairs, seq_len, H, V, dt, chunk_rows)),),
+                           torch.uint8, dev)
+    st = lib().flce_dpo_forward_backward(
+        _ptr(X, "X"), _ptr(W, "W", X.dtype), _ptr(targets, "targets", torch.int32), n_pairs, seq_len,
+        H, V, dt, ignore_index, _ptr(ref_logps, "ref_logps", torch.float32), float(beta),
+        _ptr(loss, "loss", torch.float32), _ptr(pl, "pair_loss", torch.float32),
+        _ptr(gX, "grad_X", torch.float32), _ptr(gW, "grad_W", torch.float32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
+        _stream(stream))
+    _check(st, "flce_dpo_forward_backward")
+    return loss, pl, gX, gW
 
 
 def flce_shift_labels(labels, ignore_index=-100, out=None, stream=None):

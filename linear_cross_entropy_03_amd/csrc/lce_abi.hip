@@ -242,7 +242,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
 
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_row_ce(dtype, zbuf, p.ldz, need_grad ? zbuf : nullptr, p.ldz, rows, V,
-                           p.ldz - V, targets + r0, ignore_index, hdr, loss_rows + r0, s);
+                           p.ldz - V, targets + r0, ignore_index, hdr, loss_rows + r0, nullptr, s);
     }));
     if (!need_grad) continue;
 
@@ -428,7 +428,7 @@ int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* ta
   }));
   LCE_TRY(timed(kKindRowCE, s, [&] {
     return launch_row_ce(dtype, logits, V, grad_logits, V, N, V, 0, targets, ignore_index, hdr,
-                         loss_rows, s);
+                         loss_rows, nullptr, s);
   }));
   if (reduction != FLCE_REDUCTION_NONE)
     LCE_TRY(timed(kKindOther, s, [&] {
@@ -737,6 +737,121 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
     LCE_TRY(timed(kKindOther, s, [&] {
       return launch_reduce_loss(loss_rows, N, hdr, reduction, loss, s);
     }));
+  return FLCE_OK;
+}
+
+size_t flce_dpo_workspace_bytes(int64_t n_pairs, int64_t seq_len, int64_t H, int64_t V, int dtype,
+                                int64_t chunk_rows) {
+  if (n_pairs < 0 || seq_len <= 0 || n_pairs * seq_len >= kMaxRows) return 0;
+  const int64_t N = 2 * n_pairs * seq_len;
+  Plan p;
+  if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return 0;
+  return p.total + align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float)) +
+         align_up(static_cast<size_t>(std::max<int64_t>(2 * n_pairs, 1)) * sizeof(double));
+}
+
+int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targets, int64_t n_pairs,
+                              int64_t seq_len, int64_t H, int64_t V, int dtype,
+                              int32_t ignore_index, const float* ref_logps, float beta,
+                              float* loss, float* pair_loss, float* grad_X, float* grad_W,
+                              void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                              void* stream) {
+  if (n_pairs < 0 || seq_len <= 0 || n_pairs * seq_len >= kMaxRows) return FLCE_E_INVALID_ARG;
+  if (!(beta > 0.0f)) return FLCE_E_INVALID_ARG;
+  const int64_t N = 2 * n_pairs * seq_len;
+  int st = validate_flce(X, W, nullptr, targets, N, H, V, dtype, FLCE_REDUCTION_SUM, loss, grad_X,
+                         grad_W, nullptr, chunk_rows, workspace);
+  if (st != FLCE_OK) return st;
+  if (n_pairs > 0 && ref_logps == nullptr) return FLCE_E_INVALID_ARG;
+  if ((ref_logps != nullptr && !aligned16(ref_logps)) || (pair_loss != nullptr && !aligned16(pair_loss)))
+    return FLCE_E_UNSUPPORTED;
+  Plan p;
+  if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
+  const size_t off_scale = p.total;
+  const size_t off_logp = off_scale + align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float));
+  if (workspace == nullptr ||
+      workspace_bytes < off_logp + align_up(static_cast<size_t>(std::max<int64_t>(2 * n_pairs, 1)) * sizeof(double)))
+    return FLCE_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  float* loss_rows = reinterpret_cast<float*>(ws + p.off_rows);
+  float* row_scale = reinterpret_cast<float*>(ws + off_scale);
+  double* logp = reinterpret_cast<double*>(ws + off_logp);
+  void* zbuf = ws + p.off_chunk;
+  float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
+  const size_t e = elem_bytes(dtype);
+  auto gemm = [dtype](const GemmDesc& d, hipStream_t st2) { return gemm_for(dtype, d, st2); };
+  auto logits = [&](int64_t r0, int64_t rows) {
+    GemmDesc g1{};
+    g1.A = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+    g1.lda = H; g1.a_kmajor = true;
+    g1.B = W; g1.ldb = H; g1.b_kmajor = true;
+    g1.C = zbuf; g1.ldc = p.ldz; g1.M = rows; g1.N = V; g1.K = H;
+    g1.epilogue = kEpiLogits; g1.k_splits = 1;
+    return timed(kKindLogits, s, [&] { return gemm(g1, s); });
+  };
+
+  // Validity of every target row (the scale itself is unused: the factors
+  // come per row from the pairs).
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, N, V, ignore_index, FLCE_REDUCTION_SUM, hdr, s);
+  }));
+  if (N == 0 && grad_W)
+    LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W, V * H, 0.0f, s); }));
+  // Pass 1: the CE row losses of every row (= minus the token log-probabilities).
+  for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
+    const int64_t rows = std::min(p.chunk, N - r0);
+    LCE_TRY(logits(r0, rows));
+    LCE_TRY(timed(kKindRowCE, s, [&] {
+      return launch_row_ce(dtype, zbuf, p.ldz, nullptr, p.ldz, rows, V, p.ldz - V, targets + r0,
+                           ignore_index, hdr, loss_rows + r0, nullptr, s);
+    }));
+  }
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_dpo(loss_rows, n_pairs, seq_len, ref_logps, beta, logp, loss, pair_loss,
+                      row_scale, s);
+  }));
+  // Pass 2: per-row weighted dlogits and the two gradient products. With a
+  // single chunk its logits are still in the buffer (pass 1 only read them).
+  const bool one_chunk = N <= p.chunk;
+  for (int64_t r0 = 0; r0 < N && (grad_X || grad_W); r0 += p.chunk) {
+    const int64_t rows = std::min(p.chunk, N - r0);
+    const bool first = r0 == 0;
+    const char* Xc = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+    if (!one_chunk) LCE_TRY(logits(r0, rows));
+    LCE_TRY(timed(kKindRowCE, s, [&] {
+      return launch_row_ce(dtype, zbuf, p.ldz, zbuf, p.ldz, rows, V, p.ldz - V, targets + r0,
+                           ignore_index, hdr, loss_rows + r0, row_scale + r0, s);
+    }));
+    if (grad_X) {
+      GemmDesc g2{};
+      g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
+      g2.B = W; g2.ldb = H; g2.b_kmajor = false;
+      g2.M = rows; g2.N = H; g2.K = V;
+      g2.epilogue = kEpiStoreF32;
+      float* out = grad_X + static_cast<size_t>(r0) * H;
+      if (p.dx_splits > 1) {
+        g2.C = split_buf; g2.ldc = H; g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
+        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+        LCE_TRY(timed(kKindOther, s, [&] {
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, false, s);
+        }));
+      } else {
+        g2.C = out; g2.ldc = H; g2.k_splits = 1;
+        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+      }
+    }
+    if (grad_W) {
+      GemmDesc g3{};
+      g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
+      g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
+      g3.C = grad_W; g3.ldc = H; g3.M = V; g3.N = H; g3.K = rows;
+      g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32; g3.k_splits = 1;
+      LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
+    }
+  }
   return FLCE_OK;
 }
 

@@ -207,10 +207,11 @@ hipError_t launch_count_targets(const int32_t* targets, int64_t n, int64_t V,
 // targets[r]; its loss goes to loss_rows[r]. When grad != null, grad row r
 // (stride ldg; may alias Z) receives scale * (softmax - onehot), and columns
 // [V, V + pad_cols) of it are set to zero.
+// row_scale: per-row gradient factors, or nullptr for the reduction's scale.
 hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* grad, int64_t ldg,
                          int64_t rows, int64_t V, int64_t pad_cols, const int32_t* targets,
-                         int32_t ignore_index, const WsHeader* hdr, float* loss_rows,
-                         hipStream_t s);
+                         int32_t ign, const WsHeader* hdr, float* loss_rows,
+                         const float* row_scale, hipStream_t s);
 
 hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t rows,
                               int64_t V_local, int64_t vocab_start, int64_t V_global,
@@ -227,6 +228,8 @@ hipError_t launch_combine_stats(const float* ms, const float* ss, const float* t
 hipError_t launch_row_jsd(int dtype, void* S, const void* Tt, int64_t ld, int64_t rows, int64_t V,
                           int64_t pad_cols, float inv_tau, const int32_t* targets, int32_t ign,
                           const WsHeader* hdr, float* loss_rows, hipStream_t s);
+hipError_t launch_dpo(const float* loss_rows, int64_t P, int64_t S, const float* ref, float beta,
+                      double* logp, float* loss, float* pair_loss, float* row_scale, hipStream_t s);
 hipError_t launch_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ign,
                                int32_t* targets, hipStream_t s);
 hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader* hdr,

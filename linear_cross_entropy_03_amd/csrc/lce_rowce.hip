@@ -102,7 +102,8 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
                                                      int64_t ldg, int64_t V, int64_t pad_cols,
                                                      const int32_t* __restrict__ targets,
                                                      int32_t ign, const WsHeader* __restrict__ hdr,
-                                                     float* __restrict__ loss_rows) {
+                                                     float* __restrict__ loss_rows,
+                                                     const float* __restrict__ row_scale) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   __shared__ float red0[kThreads / 64], red1[kThreads / 64];
@@ -173,7 +174,9 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   if (tid == 0) loss_rows[row] = valid ? (lse - zt) : 0.0f;
   if (G == nullptr) return;
 
-  const float c = valid ? hdr->scale : 0.0f;
+  // The gradient factor: the reduction's, or a per-row one (sequence-level
+  // losses such as DPO weight each token row separately).
+  const float c = valid ? (row_scale != nullptr ? row_scale[row] : hdr->scale) : 0.0f;
   T* g = G + row * ldg;
   uint4* gv = reinterpret_cast<uint4*>(g + rs.head);
   auto grad_of = [&](float x, int64_t v) -> float {
@@ -242,7 +245,8 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
                                                             const int32_t* __restrict__ targets,
                                                             int32_t ign,
                                                             const WsHeader* __restrict__ hdr,
-                                                            float* __restrict__ loss_rows) {
+                                                            float* __restrict__ loss_rows,
+                                                            const float* __restrict__ row_scale) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   constexpr int kThreads = pf::kThreads;
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
     if (tid == 0) loss_rows[row] = valid ? (lse - zt) : 0.0f;
 
     if (G != nullptr) {
-      const float c = valid ? hdr->scale : 0.0f;
+      const float c = valid ? (row_scale != nullptr ? row_scale[row] : hdr->scale) : 0.0f;
       const int yt = valid ? y : -1;
       T* g = G + row * ldg;
       uint4* gv = reinterpret_cast<uint4*>(g + head);
@@ -370,7 +374,8 @@ static int cu_count() {
 template <typename T, int kThreads>
 static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                                   int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
-                                  const WsHeader* hdr, float* loss_rows, hipStream_t s) {
+                                  const WsHeader* hdr, float* loss_rows, const float* row_scale,
+                                  hipStream_t s) {
   constexpr int kVec = Elem<T>::kVec;
   const int64_t nvec_max = (V + kVec - 1) / kVec;
   const T* z = static_cast<const T*>(Z);
@@ -378,13 +383,13 @@ static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t l
   const dim3 grid(static_cast<unsigned>(rows)), block(kThreads);
 #define LCE_ROW_CE(R)                                                                           \
   hipLaunchKernelGGL((k_row_ce<T, kThreads, R>), grid, block, 0, s, z, ldz, g, ldg, V, pad_cols, \
-                     targets, ign, hdr, loss_rows)
+                     targets, ign, hdr, loss_rows, row_scale)
   // Long rows, more rows than CUs: the persistent prefetching variant.
   if constexpr (kThreads == pf::kThreads) {
     const int cus = cu_count();
     if (nvec_max > 8 * kThreads && nvec_max <= 16 * kThreads && rows >= 2 * cus) {
       hipLaunchKernelGGL((k_row_ce_pf<T, 16>), dim3(static_cast<unsigned>(cus)), block, 0, s, z, ldz,
-                         g, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows);
+                         g, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows, row_scale);
       return hipGetLastError();
     }
   }
@@ -400,25 +405,26 @@ static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t l
 
 hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                          int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
-                         const WsHeader* hdr, float* loss_rows, hipStream_t s) {
+                         const WsHeader* hdr, float* loss_rows, const float* row_scale,
+                         hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const bool big = V >= 16384;
   if (dtype == 1) {
     return big ? row_ce_dispatch<uint16_t, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign,
-                                                 hdr, loss_rows, s)
+                                                 hdr, loss_rows, row_scale, s)
                : row_ce_dispatch<uint16_t, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign,
-                                                hdr, loss_rows, s);
+                                                hdr, loss_rows, row_scale, s);
   }
   if (dtype == 2) {
     return big ? row_ce_dispatch<Half, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                             loss_rows, s)
+                                             loss_rows, row_scale, s)
                : row_ce_dispatch<Half, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                            loss_rows, s);
+                                            loss_rows, row_scale, s);
   }
   return big ? row_ce_dispatch<float, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                            loss_rows, s)
+                                            loss_rows, row_scale, s)
              : row_ce_dispatch<float, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                           loss_rows, s);
+                                           loss_rows, row_scale, s);
 }
 
 // ------------------------------------------------------------ shard stats
@@ -717,6 +723,70 @@ hipError_t launch_row_jsd(int dtype, void* S, const void* Tt, int64_t ld, int64_
     hipLaunchKernelGGL((k_row_jsd<float, 1024>), grid, dim3(1024), 0, s, static_cast<float*>(S),
                        static_cast<const float*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
                        loss_rows);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------- DPO
+
+// Sequence log-probabilities: logp[k] = -sum of the CE row losses of rows
+// [k * S, (k + 1) * S), in a fixed order (strided lane sums, then a tree).
+__global__ __launch_bounds__(256) void k_seq_logp(const float* __restrict__ loss_rows, int64_t S,
+                                                  double* __restrict__ logp) {
+  __shared__ double part[256];
+  const float* r = loss_rows + static_cast<int64_t>(blockIdx.x) * S;
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < S; i += 256) acc += static_cast<double>(r[i]);
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) logp[blockIdx.x] = -part[0];
+}
+
+// Per pair b (chosen sequence b, rejected sequence P + b): the margin
+// d = beta ((logp_w - ref_w) - (logp_l - ref_l)), the pair loss softplus(-d),
+// their mean, and the per-row gradient factors +-beta sigmoid(-d) / P.
+__global__ __launch_bounds__(1024) void k_dpo_pairs(const double* __restrict__ logp,
+                                                    const float* __restrict__ ref, int64_t P,
+                                                    int64_t S, float beta, float* __restrict__ loss,
+                                                    float* __restrict__ pair_loss,
+                                                    float* __restrict__ row_scale) {
+  __shared__ double part[1024];
+  double acc = 0.0;
+  for (int64_t b = threadIdx.x; b < P; b += 1024) {
+    const double d = static_cast<double>(beta) *
+                     ((logp[b] - static_cast<double>(ref[b])) - (logp[P + b] - static_cast<double>(ref[P + b])));
+    const double l = d > 0.0 ? log1p(exp(-d)) : -d + log1p(exp(d));   // softplus(-d)
+    acc += l;
+    if (pair_loss != nullptr) pair_loss[b] = static_cast<float>(l);
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = P > 0 ? static_cast<float>(part[0] / static_cast<double>(P)) : 0.0f;
+  // Row factors, one pair's two sequences per outer step.
+  for (int64_t i = threadIdx.x; i < 2 * P * S; i += 1024) {
+    const int64_t k = i / S, b = k < P ? k : k - P;
+    const double d = static_cast<double>(beta) *
+                     ((logp[b] - static_cast<double>(ref[b])) - (logp[P + b] - static_cast<double>(ref[P + b])));
+    const double c = static_cast<double>(beta) / (1.0 + exp(d)) / static_cast<double>(P);
+    row_scale[i] = static_cast<float>(k < P ? c : -c);
+  }
+}
+
+hipError_t launch_dpo(const float* loss_rows, int64_t P, int64_t S, const float* ref, float beta,
+                      double* logp, float* loss, float* pair_loss, float* row_scale, hipStream_t s) {
+  if (P <= 0) return launch_fill_f32(loss, 1, 0.0f, s);
+  hipLaunchKernelGGL(k_seq_logp, dim3(static_cast<unsigned>(2 * P)), dim3(256), 0, s, loss_rows, S, logp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dpo_pairs, dim3(1), dim3(1024), 0, s, logp, ref, P, S, beta, loss, pair_loss,
+                     row_scale);
   return hipGetLastError();
 }
 

@@ -185,3 +185,20 @@ def test_jsd_argument_errors(B):
     assert jsd(Xt=24) == B.E_UNSUPPORTED
     assert jsd(wsb=B.flce_workspace_bytes(4, 8, 10)) == B.E_WORKSPACE
     assert B.flce_jsd_workspace_bytes(4, 8, 10) > B.flce_workspace_bytes(4, 8, 10)
+
+
+def test_dpo_argument_errors(B):
+    L = B.lib()
+
+    def dpo(**kw):
+        a = dict(X=16, W=16, y=16, P=2, S=3, H=8, V=10, dt=B.BF16, ref=16, beta=0.1, loss=16, pl=None,
+                 gX=16, gW=16, ws=16, wsb=1 << 30)
+        a.update(kw)
+        return L.flce_dpo_forward_backward(a["X"], a["W"], a["y"], a["P"], a["S"], a["H"], a["V"],
+                                           a["dt"], -100, a["ref"], a["beta"], a["loss"], a["pl"],
+                                           a["gX"], a["gW"], a["ws"], a["wsb"], 0, None)
+    assert dpo(beta=0.0) == B.E_INVALID_ARG
+    assert dpo(S=0) == B.E_INVALID_ARG
+    assert dpo(ref=None) == B.E_INVALID_ARG
+    assert dpo(pl=24) == B.E_UNSUPPORTED
+    assert dpo(wsb=B.flce_workspace_bytes(12, 8, 10)) == B.E_WORKSPACE

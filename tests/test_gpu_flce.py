@@ -339,3 +339,35 @@ def test_degenerate_shapes(B, dtype, N, H, V):
         assert np.all(got[1] == 0.0) and np.all(got[2] == 0.0)
     else:
         check_against_oracle(inp, "mean", got, want=("X", "W"))
+
+
+def _dpo_inputs(P, S, H, V, dtype, seed):
+    inp = synth.make_flce_inputs(2 * P * S, H, V, dtype, w_std=0.08, ignore_frac=0.0, seed=seed)
+    y = inp["targets"]
+    for k in range(2 * P):                 # the first S // 4 rows of every sequence are prompt
+        y[k * S:k * S + S // 4] = -100
+    rng = np.random.default_rng(seed + 1)
+    ref = (rng.standard_normal(2 * P) * 3.0 - (3 * S // 4) * np.log(V)).astype(np.float32)
+    return inp, ref
+
+
+@pytest.mark.parametrize("dtype,P,S,H,V,chunk", [
+    ("bf16", 3, 200, 136, 1000, 0),        # one chunk: no recompute
+    ("bf16", 2, 300, 64, 3001, 256),       # four chunks: logits recomputed
+    ("f32", 3, 64, 64, 900, 128)])
+def test_dpo_against_oracle(B, dtype, P, S, H, V, chunk):
+    import torch
+    inp, ref = _dpo_inputs(P, S, H, V, dtype, seed=70 + P)
+    say("dpo", dtype, P, S, H, V, chunk)
+    loss, pl, gX, gW = B.flce_dpo_forward_backward(
+        to_dev(inp["X"], dtype), to_dev(inp["W"], dtype), to_dev(inp["targets"], "i32"), P, S,
+        torch.from_numpy(ref).cuda(), beta=0.2, chunk_rows=chunk)
+    torch.cuda.synchronize()
+    X, W, _, y = oracle_inputs(inp)
+    ref_loss, ref_g, info = O.flce_dpo(X, W, y, P, S, ref.astype(np.float64), beta=0.2)
+    t = TOL[dtype]
+    check_scalar(to_host(loss), ref_loss, t["loss"], "DPO loss")
+    check_max_rel(to_host(pl), info["pair_loss"], t["loss"], "pair losses")
+    check_max_rel(to_host(gX), ref_g["X"], t["grad"], "grad_X")
+    check_max_rel(to_host(gW), ref_g["W"], t["grad"], "grad_W")
+    assert np.all(to_host(gX)[y == -100] == 0.0)
