@@ -48,7 +48,7 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
 }  // namespace tiles
 
 // ---------------------------------------------------------------------------
-// v2: 4-stage pipeline with direct HBM->LDS loads.
+// The pipeline: 4 LDS stages filled by direct HBM->LDS loads.
 //
 // K advances 32 at a time through 4 LDS stages of 32 KiB (A 16 KiB + B
 // 16 KiB). Each stage is filled by buffer_load_dwordx4 ... lds: the data never
@@ -59,8 +59,8 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
 // which buffer each direct load writes and each LDS read reads: it then waits
 // only for the loads a read depends on, and the loads can be scheduled
 // between the MFMAs like any other instruction (one direct load per four
-// MFMAs; the texture unit takes about 16 clocks per 1 KiB instruction, so a
-// burst of them would hold the issuing wave). One barrier per stage sits
+// MFMAs; the texture unit takes roughly 16-20 clocks per 1 KiB instruction, so
+// a burst of them would hold the issuing wave). One barrier per stage sits
 // between the stage's two 16-wide k steps, so the next stage's first
 // fragments are read from LDS while the current stage's second k step is on
 // the MFMA pipe.
@@ -527,7 +527,7 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
 }  // namespace mfma2
 
 template <bool kAK, bool kBKm, int kEpi, int kWN, int kTy>
-static hipError_t launch_mfma_v2(const GemmDesc& d, hipStream_t s) {
+static hipError_t launch_mfma_kernel(const GemmDesc& d, hipStream_t s) {
   using namespace mfma2;
   const int64_t tiles_m = (d.M + kBM - 1) / kBM, tiles_n = (d.N + kBM - 1) / kBM;
   const int splits = d.k_splits > 1 ? d.k_splits : 1;
@@ -555,15 +555,15 @@ template <int kTy>
 static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
   // 2 x 4 waves
   if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits)
-    return launch_mfma_v2<true, true, kEpiLogits, 4, kTy>(d, s);
+    return launch_mfma_kernel<true, true, kEpiLogits, 4, kTy>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
-    return launch_mfma_v2<true, false, kEpiStoreF32, 4, kTy>(d, s);
+    return launch_mfma_kernel<true, false, kEpiStoreF32, 4, kTy>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
-    return launch_mfma_v2<true, false, kEpiAccumF32, 4, kTy>(d, s);
+    return launch_mfma_kernel<true, false, kEpiAccumF32, 4, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
-    return launch_mfma_v2<false, false, kEpiStoreF32, 4, kTy>(d, s);
+    return launch_mfma_kernel<false, false, kEpiStoreF32, 4, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
-    return launch_mfma_v2<false, false, kEpiAccumF32, 4, kTy>(d, s);
+    return launch_mfma_kernel<false, false, kEpiAccumF32, 4, kTy>(d, s);
   return hipErrorInvalidValue;
 }
 
