@@ -5,10 +5,12 @@
 //   grad_X   dX_c = dZ_c W          A = dZ_c (k-major)  B = W  (n-major)
 //   grad_W   dW  += dZ_c^T X_c      A = dZ_c (m-major)  B = X_c (n-major)
 //
-// 16-bit path: one MFMA kernel template (namespace mfma2) for all three,
-// v_mfma_f32_32x32x16_bf16 (or _f16 for IEEE half inputs, the DeepSpeed
-// vocab-parallel CE page's FP16 case) with fp32 accumulation; see the comment
-// there.
+// 16-bit path: v_mfma_f32_32x32x16_bf16 (or _f16 for IEEE half inputs, the
+// DeepSpeed vocab-parallel CE page's FP16 case) with fp32 accumulation, 256x256
+// tiles on 8 waves, operands staged in LDS by direct HBM->LDS loads. Two
+// pipelines (namespace mfma2): 32-wide k stages in four buffers (grad_X), and
+// 64-wide k steps through a ring of five single-operand slots (logits and
+// grad_W); see the comment at each.
 // fp32 path: a plain LDS-tiled VALU kernel (namespace valu).
 #include "lce_common.h"
 
@@ -48,7 +50,8 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
 }  // namespace tiles
 
 // ---------------------------------------------------------------------------
-// The pipeline: 4 LDS stages filled by direct HBM->LDS loads.
+// The four-stage pipeline (grad_X): 32-wide k stages in 4 LDS buffers filled
+// by direct HBM->LDS loads.
 //
 // K advances 32 at a time through 4 LDS stages of 32 KiB (A 16 KiB + B
 // 16 KiB). Each stage is filled by buffer_load_dwordx4 ... lds: the data never
@@ -344,10 +347,9 @@ __device__ __forceinline__ void wave_lds_fence() {
 // 16-bit logits (+ bias): kTy 0 bf16, 1 fp16.
 template <int kTy, int kFJ>
 __device__ __forceinline__ void epilogue_16(const f32x16_t (&acc)[4][kFJ], const GemmDesc& d,
-                                              int64_t m0, int64_t n0, int row0, int col0, int wave) {
+                                              int64_t m0, int64_t n0, int row0, int col0, char* reg) {
   static_assert(kFJ == 2, "64 output columns per wave");
   const int lane = threadIdx.x & 63, l32 = lane & 31, lhi = lane >> 5;
-  char* reg = epi_region<8192>(wave);
   const uint16_t* bias = static_cast<const uint16_t*>(d.bias);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -396,10 +398,9 @@ __device__ __forceinline__ void epilogue_16(const f32x16_t (&acc)[4][kFJ], const
 template <int kEpi, int kFJ>
 __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], const GemmDesc& d,
                                              int64_t m0, int64_t n0, int sp, int row0, int col0,
-                                             int wave) {
+                                             char* reg) {
   static_assert(kFJ == 2, "64 output columns per wave");
   const int lane = threadIdx.x & 63, l32 = lane & 31, lhi = lane >> 5;
-  char* reg = epi_region<8192>(wave);
   float* C = static_cast<float*>(d.C) + static_cast<int64_t>(sp) * d.split_stride;
   // A quarter (32 rows) of the wave's result at a time.
 #pragma unroll
@@ -520,10 +521,265 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
 
   // Every wave is done with the stage buffers; they now stage the output.
   block_sync();
-  if constexpr (kEpi == kEpiLogits) epilogue_16<kTy, kFJ>(acc, d, m0, n0, row0, col0, wave);
-  else epilogue_f32<kEpi, kFJ>(acc, d, m0, n0, sp, row0, col0, wave);
+  if constexpr (kEpi == kEpiLogits) epilogue_16<kTy, kFJ>(acc, d, m0, n0, row0, col0, epi_region<8192>(wave));
+  else epilogue_f32<kEpi, kFJ>(acc, d, m0, n0, sp, row0, col0, epi_region<8192>(wave));
 }
 
+
+// ---------------------------------------------------------------------------
+// The ring pipeline: 64-wide k steps through five LDS slots of 32 KiB.
+//
+// Each slot holds one operand of one k step (256 rows x 64 k). With 64-wide
+// steps a k-major direct load covers 8 rows x 128 bytes, whole cache lines,
+// where a 32-wide stage covers 16 half lines: the texture unit, which limits
+// the k-major loads, handles half as many lines per byte. Two full stages of
+// 64 KiB would leave only one step of loads in flight; five single-operand
+// slots keep three operand loads (96 KiB) in flight while two are read, as
+// much as the four 32-wide stages. Loads go out in the order A_0, B_0, A_1,
+// B_1, ..., load j into slot j % 5, so step s reads A_s from slot 2s % 5 and
+// B_s from slot (2s + 1) % 5; the main loop is unrolled by five steps so that
+// every slot index is a compile-time constant (the same precise-wait argument
+// as for the four stage buffers). Used for logits (both operands k-major) and
+// grad_W (both mn-major); grad_X measured slower on it and keeps the four
+// stages.
+//
+// k-major slots are [row][64] with the 16-byte chunk c of row r at position
+// c ^ rswz(r); mn-major slots are [k][256] with the mn-major swizzle above.
+namespace ring {
+
+constexpr int kRK = 64;
+constexpr int kSlotElems = kBM * kRK;
+
+__shared__ __align__(16) uint16_t g_slot0[kSlotElems];
+__shared__ __align__(16) uint16_t g_slot1[kSlotElems];
+__shared__ __align__(16) uint16_t g_slot2[kSlotElems];
+__shared__ __align__(16) uint16_t g_slot3[kSlotElems];
+__shared__ __align__(16) uint16_t g_slot4[kSlotElems];
+
+template <int kI>
+__device__ __forceinline__ uint16_t* slot_buf() {
+  if constexpr (kI == 0) return g_slot0;
+  else if constexpr (kI == 1) return g_slot1;
+  else if constexpr (kI == 2) return g_slot2;
+  else if constexpr (kI == 3) return g_slot3;
+  else return g_slot4;
+}
+
+// Conflict-free ds_read_b128 of 32 consecutive rows at one chunk, for banks
+// served 8 or 16 lanes at a time: rows 0..7 and each parity class of rows
+// 0..15 map to distinct positions.
+__device__ __forceinline__ int rswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// One operand in the ring: this wave's 4 of the 32 direct loads of a step
+// (issued in parts, kFirst..kFirst+kCount-1) and the MFMA fragment reads.
+template <bool kKMajor>
+struct ROp;
+
+template <>
+struct ROp<true> {
+  static constexpr int kInstr = kBM / 8 / 8;
+  static constexpr int kReads = 1;  // LDS reads per fragment
+  rsrc_t rsrc;
+  int voff0[kInstr], kc8[kInstr];
+
+  __device__ __forceinline__ static int first_row(int w, int t) { return (w * kInstr + t) * 8; }
+
+  __device__ __forceinline__ void init(const uint16_t* P, int64_t ld, int64_t rows, int64_t r0) {
+    const int lane = threadIdx.x & 63, w = wave_id();
+    int64_t nrows = rows - r0;
+    if (nrows > kBM) nrows = kBM;
+    rsrc = make_rsrc(P + r0 * ld, nrows * ld * 2);
+#pragma unroll
+    for (int t = 0; t < kInstr; ++t) {
+      const int row = first_row(w, t) + (lane >> 3);
+      const int kc = (lane & 7) ^ rswz(row);
+      kc8[t] = kc * 8;
+      voff0[t] = static_cast<int>(row * ld * 2) + kc * 16;
+    }
+  }
+  template <int kFirst, int kCount>
+  __device__ __forceinline__ void issue(uint16_t* dst, int64_t k0, int64_t kend) const {
+    const int w = wave_id();
+    const int64_t klim = kend - k0;
+#pragma unroll
+    for (int t = kFirst; t < kFirst + kCount; ++t) {
+      const int voff = kc8[t] < klim ? voff0[t] + static_cast<int>(k0 * 2) : kOOB;
+      dma16(rsrc, dst + first_row(w, t) * kRK, voff);
+    }
+  }
+  __device__ __forceinline__ static bf16x8_t frag(const uint16_t* src, int base, int kk) {
+    const int lane = threadIdx.x & 63, r = lane & 31, c = kk * 2 + (lane >> 5);
+    return *reinterpret_cast<const bf16x8_t*>(src + base * kRK + r * kRK + ((c ^ rswz(r)) << 3));
+  }
+};
+
+template <>
+struct ROp<false> {
+  static constexpr int kInstr = kRK / 2 / 8;
+  static constexpr int kReads = 2;
+  const uint16_t* P;
+  int64_t ld, r0;
+  int moff0[kInstr];
+
+  __device__ __forceinline__ static int first_k(int w, int t) { return (w * kInstr + t) * 2; }
+
+  __device__ __forceinline__ void init(const uint16_t* P_, int64_t ld_, int64_t, int64_t r0_) {
+    P = P_; ld = ld_; r0 = r0_;
+    const int lane = threadIdx.x & 63, w = wave_id();
+#pragma unroll
+    for (int t = 0; t < kInstr; ++t) {
+      const int k = first_k(w, t) + (lane >> 5);
+      const int c = (lane & 31) ^ mswz(k);
+      moff0[t] = static_cast<int>(k * ld * 2) + c * 16;
+    }
+  }
+  template <int kFirst, int kCount>
+  __device__ __forceinline__ void issue(uint16_t* dst, int64_t k0, int64_t kend) const {
+    const int w = wave_id();
+    int64_t nk = kend - k0;
+    if (nk > kRK) nk = kRK;
+    const rsrc_t r = make_rsrc(P + k0 * ld + r0, (nk * ld - r0) * 2);
+#pragma unroll
+    for (int t = kFirst; t < kFirst + kCount; ++t) dma16(r, dst + first_k(w, t) * kBM, moff0[t]);
+  }
+  __device__ __forceinline__ static bf16x8_t frag(const uint16_t* src, int base, int kk) {
+    const int lane = threadIdx.x & 63;
+    const int i = (lane & 15) >> 2, q = lane & 3;
+    const int k = kk * 16 + (lane >> 5) * 8 + i;
+    const int mn = base + ((lane >> 4) & 1) * 16 + q * 4;
+    uint16_t* s = const_cast<uint16_t*>(src);
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s + moff(k, mn)));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s + moff(k + 4, mn)));
+    const short __attribute__((ext_vector_type(8))) v =
+        __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+};
+
+// One 16-wide k sub-step: issue() places kDma direct loads, the next
+// fragments are read, and the 8 MFMAs run on the current ones, interleaved
+// as in mma_step.
+template <int kTy, int kDma, bool kAK, bool kBKm, typename Issue>
+__device__ __forceinline__ void sub(f32x16_t (&acc)[4][2], const Frags<2>& f, Frags<2>& nf,
+                                    const uint16_t* srcA, const uint16_t* srcB, int row0, int col0,
+                                    int kk, Issue&& issue) {
+  issue();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nf.a[i] = ROp<kAK>::frag(srcA, row0 + i * 32, kk);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) nf.b[j] = ROp<kBKm>::frag(srcB, col0 + j * 32, kk);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if constexpr (kTy == 1)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, f.b[j]),
+                                                           __builtin_bit_cast(f16x8_t, f.a[i]),
+                                                           acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  constexpr int kReads = 4 * ROp<kAK>::kReads + 2 * ROp<kBKm>::kReads;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (t < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (kDma > 0)
+      if (t % (8 / kDma) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  if constexpr (kReads > 8) __builtin_amdgcn_sched_group_barrier(0x100, kReads - 8, 0);
+}
+
+// Step s (kS = s % 5) reads A_s from slot 2s % 5 and B_s from (2s + 1) % 5.
+// Its first two k16 sub-steps issue A_{s+2} into the slot B_{s-1} used; the
+// barrier before the last sub-step waits for A_{s+1}, B_{s+1} and frees this
+// step's slots, and the last sub-step issues B_{s+2} into the slot of A_s.
+template <int kTy, int kS, bool kAK, bool kBKm>
+__device__ __forceinline__ void step(f32x16_t (&acc)[4][2], Frags<2>& f0, Frags<2>& f1,
+                                     const ROp<kAK>& A, const ROp<kBKm>& B, int row0, int col0,
+                                     int64_t k2, int64_t kend) {
+  constexpr int sa = (2 * kS) % 5, sb = (2 * kS + 1) % 5, pb = (2 * kS + 4) % 5;
+  constexpr int na = (2 * kS + 2) % 5, nb = (2 * kS + 3) % 5;
+  constexpr int kIA = ROp<kAK>::kInstr, kIB = ROp<kBKm>::kInstr;
+  static_assert(kIA == 4 && kIB == 4, "four loads per operand per wave");
+  const uint16_t* a = slot_buf<sa>();
+  const uint16_t* b = slot_buf<sb>();
+  sub<kTy, 2, kAK, kBKm>(acc, f0, f1, a, b, row0, col0, 1,
+                         [&] { A.template issue<0, 2>(slot_buf<pb>(), k2, kend); });
+  sub<kTy, 2, kAK, kBKm>(acc, f1, f0, a, b, row0, col0, 2,
+                         [&] { A.template issue<2, 2>(slot_buf<pb>(), k2, kend); });
+  sub<kTy, 0, kAK, kBKm>(acc, f0, f1, a, b, row0, col0, 3, [] {});
+  // Only A_{s+2} was issued after B_{s+1}; as in the four-stage loop the
+  // count relies on there being no other vector memory instruction (no
+  // spills, checked by the launcher).
+  wait_vmcnt<kIA>();
+  block_sync();
+  sub<kTy, 4, kAK, kBKm>(acc, f1, f0, slot_buf<na>(), slot_buf<nb>(), row0, col0, 0,
+                         [&] { B.template issue<0, 4>(slot_buf<sa>(), k2, kend); });
+}
+
+template <bool kAK, bool kBKm, int kEpi, int kTy>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
+  int64_t tm, tn;
+  int sp;
+  tiles::tile_of(blockIdx.x, tiles_m, tiles_n, d.k_splits, tm, tn, sp);
+  const int64_t m0 = tm * kBM, n0 = tn * kBM;
+  const int64_t kbeg = static_cast<int64_t>(sp) * k_per_split;
+  int64_t kend = kbeg + k_per_split;
+  if (kend > d.K) kend = d.K;
+  const int ksteps = kend > kbeg ? static_cast<int>((kend - kbeg + kRK - 1) / kRK) : 0;
+  ROp<kAK> A;
+  ROp<kBKm> B;
+  A.init(static_cast<const uint16_t*>(d.A), d.lda, d.M, m0);
+  B.init(static_cast<const uint16_t*>(d.B), d.ldb, d.N, n0);
+  const int wave = wave_id();
+  const int row0 = (wave / 4) * 128, col0 = (wave % 4) * 64;
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  // Prologue: A_0, B_0, A_1, B_1 into slots 0..3; step 0 then issues A_2
+  // into slot 4. Loads past the end of K read zeros, so every step issues
+  // the same loads, and the final steps' look-ahead reads stay in bounds.
+  if (ksteps > 0) {
+    A.template issue<0, 4>(slot_buf<0>(), kbeg, kend);
+    B.template issue<0, 4>(slot_buf<1>(), kbeg, kend);
+    A.template issue<0, 4>(slot_buf<2>(), kbeg + kRK, kend);
+    B.template issue<0, 4>(slot_buf<3>(), kbeg + kRK, kend);
+    wait_vmcnt<2 * 4>();
+    block_sync();
+    Frags<2> f0, f1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f0.a[i] = ROp<kAK>::frag(slot_buf<0>(), row0 + i * 32, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f0.b[j] = ROp<kBKm>::frag(slot_buf<1>(), col0 + j * 32, 0);
+    int s = 0;
+    for (; s + 5 <= ksteps; s += 5) {
+      const int64_t k2 = kbeg + static_cast<int64_t>(s + 2) * kRK;
+      step<kTy, 0>(acc, f0, f1, A, B, row0, col0, k2, kend);
+      step<kTy, 1>(acc, f0, f1, A, B, row0, col0, k2 + kRK, kend);
+      step<kTy, 2>(acc, f0, f1, A, B, row0, col0, k2 + 2 * kRK, kend);
+      step<kTy, 3>(acc, f0, f1, A, B, row0, col0, k2 + 3 * kRK, kend);
+      step<kTy, 4>(acc, f0, f1, A, B, row0, col0, k2 + 4 * kRK, kend);
+    }
+    const int64_t k2 = kbeg + static_cast<int64_t>(s + 2) * kRK;
+    if (s < ksteps) step<kTy, 0>(acc, f0, f1, A, B, row0, col0, k2, kend);
+    if (s + 1 < ksteps) step<kTy, 1>(acc, f0, f1, A, B, row0, col0, k2 + kRK, kend);
+    if (s + 2 < ksteps) step<kTy, 2>(acc, f0, f1, A, B, row0, col0, k2 + 2 * kRK, kend);
+    if (s + 3 < ksteps) step<kTy, 3>(acc, f0, f1, A, B, row0, col0, k2 + 3 * kRK, kend);
+    wait_vmcnt<0>();
+  }
+  // Every wave is done with the slots; slots 0 and 1 stage the output.
+  block_sync();
+  char* reg = reinterpret_cast<char*>(wave < 4 ? g_slot0 : g_slot1) + (wave & 3) * 8192;
+  if constexpr (kEpi == kEpiLogits) epilogue_16<kTy, 2>(acc, d, m0, n0, row0, col0, reg);
+  else epilogue_f32<kEpi, 2>(acc, d, m0, n0, sp, row0, col0, reg);
+}
+
+}  // namespace ring
 }  // namespace mfma2
 
 template <bool kAK, bool kBKm, int kEpi, int kWN, int kTy>
@@ -551,19 +807,43 @@ static hipError_t launch_mfma_kernel(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+template <bool kAK, bool kBKm, int kEpi, int kTy>
+static hipError_t launch_ring(const GemmDesc& d, hipStream_t s) {
+  using namespace mfma2;
+  const int64_t tiles_m = (d.M + kBM - 1) / kBM, tiles_n = (d.N + kBM - 1) / kBM;
+  const int splits = d.k_splits > 1 ? d.k_splits : 1;
+  int64_t k_per = (d.K + splits - 1) / splits;
+  k_per = (k_per + ring::kRK - 1) / ring::kRK * ring::kRK;
+  auto kern = ring::k_ring<kAK, kBKm, kEpi, kTy>;
+  // As for the four-stage kernel: spill stores would break the explicit waits.
+  static int spills = -1;
+  if (spills < 0) {
+    hipFuncAttributes fa;
+    const hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
+    if (e != hipSuccess) return e;
+    spills = fa.localSizeBytes != 0;
+  }
+  if (spills) return hipErrorInvalidDeviceFunction;
+  GemmDesc dd = d;
+  dd.k_splits = splits;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles_m * tiles_n * splits)), dim3(512), 0, s,
+                     dd, tiles_m, tiles_n, k_per);
+  return hipGetLastError();
+}
+
 template <int kTy>
 static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
-  // 2 x 4 waves
   if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits)
-    return launch_mfma_kernel<true, true, kEpiLogits, 4, kTy>(d, s);
+    return launch_ring<true, true, kEpiLogits, kTy>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
     return launch_mfma_kernel<true, false, kEpiStoreF32, 4, kTy>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
     return launch_mfma_kernel<true, false, kEpiAccumF32, 4, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
-    return launch_mfma_kernel<false, false, kEpiStoreF32, 4, kTy>(d, s);
+    return launch_ring<false, false, kEpiStoreF32, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
-    return launch_mfma_kernel<false, false, kEpiAccumF32, 4, kTy>(d, s);
+    return launch_ring<false, false, kEpiAccumF32, kTy>(d, s);
   return hipErrorInvalidValue;
 }
 
