@@ -49,6 +49,9 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;
 // Default byte budget of one chunk's logits (the planner's only memory knob).
 constexpr double kChunkBudget = 2.4e9;
 constexpr int64_t kRowQuantum = 256;  // GEMM tile rows
+// Standalone CE calls up to this many rows count their targets inside the row
+// kernel (each workgroup reads all of them: at most 8 KiB).
+constexpr int64_t kSelfCountRows = 2048;
 
 struct Plan {
   int64_t chunk;    // rows per chunk
@@ -423,13 +426,21 @@ int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* ta
   char* ws = static_cast<char*>(workspace);
   WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
   float* loss_rows = reduction == FLCE_REDUCTION_NONE ? loss : reinterpret_cast<float*>(ws + align_up(sizeof(WsHeader)));
-  LCE_TRY(timed(kKindOther, s, [&] {
-    return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
-  }));
-  LCE_TRY(timed(kKindRowCE, s, [&] {
-    return launch_row_ce(dtype, logits, V, grad_logits, V, N, V, 0, targets, ignore_index, hdr,
-                         loss_rows, nullptr, s);
-  }));
+  if (N > 0 && N <= kSelfCountRows) {
+    // One launch: the row kernel counts the targets itself.
+    LCE_TRY(timed(kKindRowCE, s, [&] {
+      return launch_row_ce_counted(dtype, logits, grad_logits, N, V, targets, ignore_index,
+                                   reduction, hdr, loss_rows, s);
+    }));
+  } else {
+    LCE_TRY(timed(kKindOther, s, [&] {
+      return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
+    }));
+    LCE_TRY(timed(kKindRowCE, s, [&] {
+      return launch_row_ce(dtype, logits, V, grad_logits, V, N, V, 0, targets, ignore_index, hdr,
+                           loss_rows, nullptr, s);
+    }));
+  }
   if (reduction != FLCE_REDUCTION_NONE)
     LCE_TRY(timed(kKindOther, s, [&] {
       return launch_reduce_loss(loss_rows, N, hdr, reduction, loss, s);

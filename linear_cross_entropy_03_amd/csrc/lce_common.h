@@ -213,6 +213,14 @@ hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* grad, int6
                          int32_t ign, const WsHeader* hdr, float* loss_rows,
                          const float* row_scale, hipStream_t s);
 
+// Row CE over a whole call of `rows` rows (contiguous, stride V) that also
+// counts the targets: fills hdr (n_bad, n_valid, scale) as launch_count_targets
+// would, in the same launch (two launches where the persistent row kernel
+// applies). For calls with few rows (every workgroup reads all targets).
+hipError_t launch_row_ce_counted(int dtype, const void* Z, void* grad, int64_t rows, int64_t V,
+                                 const int32_t* targets, int32_t ign, int reduction, WsHeader* hdr,
+                                 float* loss_rows, hipStream_t s);
+
 hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t rows,
                               int64_t V_local, int64_t vocab_start, int64_t V_global,
                               const int32_t* targets, int32_t ignore_index, float* row_max,

@@ -94,6 +94,80 @@ __device__ __forceinline__ void block_lse_parts(float m, float s, float* red0, f
   S = block_sum<kThreads>(mine, red1);
 }
 
+// Target count inside the row kernel, for calls of one launch over few rows:
+// every workgroup counts all n targets itself (n * 4 bytes from L2) and
+// workgroup 0 writes the header, which saves the separate count launch.
+struct SelfCount {
+  int64_t n;        // rows of the call; 0: read the scale from the header
+  int reduction;    // 0 none, 1 sum, 2 mean
+  WsHeader* out;    // header written by workgroup 0
+};
+
+// The reduction's gradient factor from all targets of the call (same rules
+// as k_count_targets).
+// Raw buffer descriptor over [base, base + bytes) (bytes < 2^31) in scalar
+// registers: loads outside the range return zero, so loads need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo),
+                                           static_cast<short>(0), n, 0x00020000);
+}
+
+// One element's bits through a buffer descriptor (zero out of range).
+template <typename T>
+__device__ __forceinline__ T load_elem_bits(__amdgpu_buffer_rsrc_t r, int voff) {
+  if constexpr (sizeof(T) == 2)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0));
+  else
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
+// Per-wave target counts into cnt[0][wave] (valid) and cnt[1][wave] (bad);
+// read with count_finish after the next barrier. `first` is t[threadIdx.x]
+// (ign past the end), loaded by the caller before the row: loads complete in
+// order, so a target load issued after the row's would wait for the whole row.
+template <int kThreads>
+__device__ __forceinline__ void count_partial(const SelfCount& sc, const int32_t* __restrict__ t,
+                                              int64_t V, int32_t ign, int32_t first,
+                                              float (*cnt)[kThreads / 64]) {
+  int valid = 0, bad = 0;
+  auto tally = [&](int32_t y) {
+    if (y == ign) return;
+    if (y >= 0 && static_cast<int64_t>(y) < V) ++valid; else ++bad;
+  };
+  tally(first);
+  for (int64_t i = threadIdx.x + kThreads; i < sc.n; i += kThreads) tally(t[i]);
+  // Counts stay below 2^24, so float sums are exact.
+  const float v = wave_sum(static_cast<float>(valid)), b = wave_sum(static_cast<float>(bad));
+  if ((threadIdx.x & 63) == 0) {
+    cnt[0][threadIdx.x >> 6] = v;
+    cnt[1][threadIdx.x >> 6] = b;
+  }
+}
+
+// The reduction's gradient factor from the per-wave counts (same rules as
+// k_count_targets); workgroup 0 writes the header.
+template <int kThreads>
+__device__ __forceinline__ float count_finish(const SelfCount& sc, const float (*cnt)[kThreads / 64]) {
+  float v = 0.0f, b = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    v += cnt[0][w];
+    b += cnt[1][w];
+  }
+  const int nv = static_cast<int>(v);
+  const float scale = sc.reduction == 2 ? (nv > 0 ? 1.0f / static_cast<float>(nv) : 0.0f) : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    sc.out->n_bad = static_cast<int>(b);
+    sc.out->n_valid = nv;
+    sc.out->scale = scale;
+  }
+  return scale;
+}
+
 // kRes > 0: the row's vectors stay in registers (kRes per lane); kRes == 0:
 // two streaming passes over the row. Z and G may be the same rows (in-place),
 // so neither is declared __restrict__.
@@ -103,10 +177,12 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
                                                      const int32_t* __restrict__ targets,
                                                      int32_t ign, const WsHeader* __restrict__ hdr,
                                                      float* __restrict__ loss_rows,
-                                                     const float* __restrict__ row_scale) {
+                                                     const float* __restrict__ row_scale,
+                                                     SelfCount sc) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   __shared__ float red0[kThreads / 64], red1[kThreads / 64];
+  __shared__ float cnt[2][kThreads / 64];  // self-count: per-wave target counts
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const T* z = Z + row * ldz;
@@ -115,18 +191,31 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   const RowSplit rs = split_row(z, V);
   const uint4* zv = reinterpret_cast<const uint4*>(z + rs.head);
 
-  // The target logit is read before any lane can overwrite the row.
+  // The target logit is read before any lane can overwrite the row: the
+  // block reductions below end in __syncthreads, which waits for every load
+  // of the wave, and all writes come after them. In the register-resident
+  // path it is loaded after the row so the row's loads go out first.
   float zt = 0.0f;
-  if (tid == 0 && valid) zt = E::load(z + y);
+  T zt_bits{};
+  if (kRes == 0 && tid == 0 && valid) zt = E::load(z + y);
 
-  float m = -INFINITY, s = 0.0f;
+  float m = -INFINITY, s = 0.0f, self_scale = 0.0f;
+  const int32_t t_first = (sc.n > 0 && tid < sc.n) ? targets[tid] : ign;
   uint4 buf[kRes > 0 ? kRes : 1];
   if constexpr (kRes > 0) {
+    // Branch-free loads (zeros past the row's vectors), then the target
+    // element (every lane reads the same one; zero when the row is ignored),
+    // so the waits below can count loads exactly. Rows here hold at most
+    // 16 x kThreads vectors, so byte offsets fit in 32 bits.
+    const __amdgpu_buffer_rsrc_t rv = row_rsrc(zv, rs.nvec * 16);
 #pragma unroll
-    for (int j = 0; j < kRes; ++j) {
-      const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
-      buf[j] = vi < rs.nvec ? zv[vi] : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int j = 0; j < kRes; ++j)
+      buf[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rv, (j * kThreads + tid) * 16, 0, 0));
+    zt_bits = load_elem_bits<T>(row_rsrc(z, V * static_cast<int64_t>(sizeof(T))),
+                                valid ? static_cast<int>(y * sizeof(T)) : 0x7FFFFFF0);
+    // The count overlaps the row's loads in flight.
+    if (sc.n > 0) count_partial<kThreads>(sc, targets, V, ign, t_first, cnt);
     // max first, then one exp per element against the lane maximum.
     float lm = -INFINITY;
 #pragma unroll
@@ -159,6 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
     m = lm;
     s = ls;
   } else {
+    if (sc.n > 0) count_partial<kThreads>(sc, targets, V, ign, t_first, cnt);
     for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
       float f[kVec];
       E::unpack(zv[vi], f);
@@ -168,15 +258,20 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
     if (tid < V - rs.tail0) online_push(m, s, E::load(z + rs.tail0 + tid));
   }
 
+  // The reduction's barriers also publish the per-wave counts.
   float M, S;
   block_lse_parts<kThreads>(m, s, red0, red1, M, S);
   const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
+  if (sc.n > 0) self_scale = count_finish<kThreads>(sc, cnt);
+  if constexpr (kRes > 0) zt = E::load(&zt_bits);
   if (tid == 0) loss_rows[row] = valid ? (lse - zt) : 0.0f;
   if (G == nullptr) return;
 
   // The gradient factor: the reduction's, or a per-row one (sequence-level
   // losses such as DPO weight each token row separately).
-  const float c = valid ? (row_scale != nullptr ? row_scale[row] : hdr->scale) : 0.0f;
+  const float c = valid ? (row_scale != nullptr ? row_scale[row]
+                                                : (sc.n > 0 ? self_scale : hdr->scale))
+                        : 0.0f;
   T* g = G + row * ldg;
   uint4* gv = reinterpret_cast<uint4*>(g + rs.head);
   auto grad_of = [&](float x, int64_t v) -> float {
@@ -228,14 +323,6 @@ constexpr int kMaxSlices = 9;  // 144 KiB of LDS
 __shared__ __align__(16) uint4 g_next[kMaxSlices * kThreads];
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
-  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo),
-                                           static_cast<short>(0), n, 0x00020000);
-}
 }  // namespace pf
 
 template <typename T, int kRes>
@@ -260,7 +347,7 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
   auto prefetch = [&](int64_t row) {
     const T* z = Z + row * ldz;
     const RowSplit rs = split_row(z, V);
-    const __amdgpu_buffer_rsrc_t r = pf::row_rsrc(z + rs.head, rs.nvec * 16);
+    const __amdgpu_buffer_rsrc_t r = row_rsrc(z + rs.head, rs.nvec * 16);
 #pragma unroll
     for (int j = 0; j < kSlices; ++j)  // slice offset in the scalar offset register
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -284,7 +371,7 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
 
     uint4 buf[kRes];
     {
-      const __amdgpu_buffer_rsrc_t r = pf::row_rsrc(z + head, rs.nvec * 16);
+      const __amdgpu_buffer_rsrc_t r = row_rsrc(z + head, rs.nvec * 16);
 #pragma unroll
       for (int j = kSlices; j < kRes; ++j)  // range-checked: zeros past the row
         buf[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -371,11 +458,17 @@ static int cu_count() {
   return cus;
 }
 
+// Rows of 8193..16384 16-byte vectors (1024-lane workgroups), at least two
+// per CU: the persistent prefetching kernel.
+static bool takes_persistent(int64_t nvec, int64_t rows) {
+  return nvec > 8 * pf::kThreads && nvec <= 16 * pf::kThreads && rows >= 2 * cu_count();
+}
+
 template <typename T, int kThreads>
 static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                                   int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
                                   const WsHeader* hdr, float* loss_rows, const float* row_scale,
-                                  hipStream_t s) {
+                                  SelfCount sc, hipStream_t s) {
   constexpr int kVec = Elem<T>::kVec;
   const int64_t nvec_max = (V + kVec - 1) / kVec;
   const T* z = static_cast<const T*>(Z);
@@ -383,13 +476,12 @@ static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t l
   const dim3 grid(static_cast<unsigned>(rows)), block(kThreads);
 #define LCE_ROW_CE(R)                                                                           \
   hipLaunchKernelGGL((k_row_ce<T, kThreads, R>), grid, block, 0, s, z, ldz, g, ldg, V, pad_cols, \
-                     targets, ign, hdr, loss_rows, row_scale)
+                     targets, ign, hdr, loss_rows, row_scale, sc)
   // Long rows, more rows than CUs: the persistent prefetching variant.
   if constexpr (kThreads == pf::kThreads) {
-    const int cus = cu_count();
-    if (nvec_max > 8 * kThreads && nvec_max <= 16 * kThreads && rows >= 2 * cus) {
-      hipLaunchKernelGGL((k_row_ce_pf<T, 16>), dim3(static_cast<unsigned>(cus)), block, 0, s, z, ldz,
-                         g, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows, row_scale);
+    if (sc.n == 0 && takes_persistent(nvec_max, rows)) {
+      hipLaunchKernelGGL((k_row_ce_pf<T, 16>), dim3(static_cast<unsigned>(cu_count())), block, 0, s,
+                         z, ldz, g, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows, row_scale);
       return hipGetLastError();
     }
   }
@@ -403,28 +495,54 @@ static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t l
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t row_ce_by_width(const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
+                                  int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
+                                  const WsHeader* hdr, float* loss_rows, const float* row_scale,
+                                  SelfCount sc, hipStream_t s) {
+  if (V >= 16384)
+    return row_ce_dispatch<T, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
+                                    row_scale, sc, s);
+  return row_ce_dispatch<T, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
+                                 row_scale, sc, s);
+}
+
+static hipError_t row_ce_typed(int dtype, const void* Z, int64_t ldz, void* G, int64_t ldg,
+                               int64_t rows, int64_t V, int64_t pad_cols, const int32_t* targets,
+                               int32_t ign, const WsHeader* hdr, float* loss_rows,
+                               const float* row_scale, SelfCount sc, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == 1)
+    return row_ce_by_width<uint16_t>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
+                                     loss_rows, row_scale, sc, s);
+  if (dtype == 2)
+    return row_ce_by_width<Half>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
+                                 row_scale, sc, s);
+  return row_ce_by_width<float>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
+                                row_scale, sc, s);
+}
+
 hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                          int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
                          const WsHeader* hdr, float* loss_rows, const float* row_scale,
                          hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const bool big = V >= 16384;
-  if (dtype == 1) {
-    return big ? row_ce_dispatch<uint16_t, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign,
-                                                 hdr, loss_rows, row_scale, s)
-               : row_ce_dispatch<uint16_t, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign,
-                                                hdr, loss_rows, row_scale, s);
+  return row_ce_typed(dtype, Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
+                      row_scale, SelfCount{0, 0, nullptr}, s);
+}
+
+hipError_t launch_row_ce_counted(int dtype, const void* Z, void* G, int64_t rows, int64_t V,
+                                 const int32_t* targets, int32_t ign, int reduction, WsHeader* hdr,
+                                 float* loss_rows, hipStream_t s) {
+  // Rows that the persistent prefetching kernel takes (it does not count)
+  // keep the separate count launch.
+  const int vec = dtype == 0 ? 4 : 8;  // elements per 16-byte vector
+  if (V >= 16384 && takes_persistent((V + vec - 1) / vec, rows)) {
+    const hipError_t e = launch_count_targets(targets, rows, V, ign, reduction, hdr, s);
+    if (e != hipSuccess) return e;
+    return launch_row_ce(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr, s);
   }
-  if (dtype == 2) {
-    return big ? row_ce_dispatch<Half, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                             loss_rows, row_scale, s)
-               : row_ce_dispatch<Half, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                            loss_rows, row_scale, s);
-  }
-  return big ? row_ce_dispatch<float, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                            loss_rows, row_scale, s)
-             : row_ce_dispatch<float, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                           loss_rows, row_scale, s);
+  return row_ce_typed(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr,
+                      SelfCount{rows, reduction, hdr}, s);
 }
 
 // ------------------------------------------------------------ shard stats

@@ -145,6 +145,26 @@ def test_ce_bad_target_is_reported_and_ignored(B):
     assert B.flce_check_device_error(ws) == B.OK
 
 
+@pytest.mark.parametrize("N", [2048, 2049])
+def test_ce_target_count_paths(B, N):
+    """Calls of up to 2048 rows count their targets inside the row kernel,
+    larger ones in a separate launch: both give the mean over valid rows and
+    report a bad target."""
+    import torch
+    inp = synth.make_ce_inputs(N, 777, "bf16", std=2.0, ignore_frac=0.3, seed=N)
+    y = inp["targets"].copy()
+    y[N - 1] = 777
+    ws = torch.zeros(B.ce_workspace_bytes(N, 777), dtype=torch.uint8, device="cuda")
+    say("ce count paths", N)
+    loss, g = B.ce_forward_backward(to_dev(inp["logits"], "bf16"), to_dev(y, "i32"),
+                                    reduction="mean", workspace=ws)
+    assert B.flce_check_device_error(ws) == B.E_TARGET
+    ref_loss, ref_g, info = O.cross_entropy(inp["logits_f32"], y, reduction="mean")
+    assert info["n_bad"] == 1
+    check_scalar(to_host(loss), ref_loss, TOL["bf16"]["loss"])
+    check_max_rel(to_host(g), ref_g, TOL["bf16"]["grad"], "grad")
+
+
 def test_shard_stats_two_halves_combine(B):
     """[1024, 65536] bf16 logits split into vocabulary shards [0, 32768) and
     [32768, 65536); the host combination of the two shards' statistics equals
