@@ -49,8 +49,8 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;
 // Default byte budget of one chunk's logits (the planner's only memory knob).
 constexpr double kChunkBudget = 2.4e9;
 constexpr int64_t kRowQuantum = 256;  // GEMM tile rows
-// Standalone CE calls up to this many rows count their targets inside the row
-// kernel (each workgroup reads all of them: at most 8 KiB).
+// Standalone CE and shard-statistics calls up to this many rows count their
+// targets inside the row kernel (each workgroup reads all of them: 8 KiB).
 constexpr int64_t kSelfCountRows = 2048;
 
 struct Plan {
@@ -465,6 +465,15 @@ int ce_shard_stats(const void* logits_shard, const int32_t* targets, int64_t N, 
   if (workspace == nullptr || workspace_bytes < ce_ws_bytes(N)) return FLCE_E_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   WsHeader* hdr = static_cast<WsHeader*>(workspace);
+  if (N > 0 && N <= kSelfCountRows) {
+    // One launch: the statistics kernel counts the targets itself.
+    LCE_TRY(timed(kKindRowCE, s, [&] {
+      return launch_shard_stats_counted(dtype, logits_shard, N, V_local, vocab_start, V_global,
+                                        targets, ignore_index, row_max, row_sumexp,
+                                        row_target_logit, hdr, s);
+    }));
+    return FLCE_OK;
+  }
   LCE_TRY(timed(kKindOther, s, [&] {
     return launch_count_targets(targets, N, V_global, ignore_index, FLCE_REDUCTION_SUM, hdr, s);
   }));

@@ -225,6 +225,14 @@ hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t row
                               int64_t V_local, int64_t vocab_start, int64_t V_global,
                               const int32_t* targets, int32_t ignore_index, float* row_max,
                               float* row_sumexp, float* row_target, hipStream_t s);
+// Shard statistics over a whole call of `rows` rows (stride V_local) that also
+// counts the targets against V_global into hdr (sum reduction), in the same
+// launch. For calls with few rows.
+hipError_t launch_shard_stats_counted(int dtype, const void* Z, int64_t rows, int64_t V_local,
+                                      int64_t vocab_start, int64_t V_global,
+                                      const int32_t* targets, int32_t ign, float* row_max,
+                                      float* row_sumexp, float* row_target, WsHeader* hdr,
+                                      hipStream_t s);
 
 hipError_t launch_shard_grad(int dtype, void* Z, int64_t ldz, int64_t rows, int64_t V_local,
                              int64_t pad_cols, int64_t vocab_start, int64_t V_global,

@@ -547,60 +547,145 @@ hipError_t launch_row_ce_counted(int dtype, const void* Z, void* G, int64_t rows
 
 // ------------------------------------------------------------ shard stats
 
-template <typename T, int kThreads>
+// kRes > 0: the row's vectors are loaded at once into registers (kRes per
+// lane), as in k_row_ce; kRes == 0: one streaming online pass.
+template <typename T, int kThreads, int kRes>
 __global__ __launch_bounds__(kThreads) void k_shard_stats(const T* __restrict__ Z, int64_t ldz,
                                                           int64_t Vl, int64_t v0, int64_t Vg,
                                                           const int32_t* __restrict__ targets,
                                                           int32_t ign, float* __restrict__ rmax,
                                                           float* __restrict__ rsum,
-                                                          float* __restrict__ rtgt) {
+                                                          float* __restrict__ rtgt, SelfCount sc) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   __shared__ float red0[kThreads / 64], red1[kThreads / 64];
+  __shared__ float cnt[2][kThreads / 64];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const T* z = Z + row * ldz;
+  const int32_t y = targets[row];
+  const int64_t local = static_cast<int64_t>(y) - v0;
+  const bool here = (y != ign) && y >= 0 && static_cast<int64_t>(y) < Vg && local >= 0 && local < Vl;
   const RowSplit rs = split_row(z, Vl);
   const uint4* zv = reinterpret_cast<const uint4*>(z + rs.head);
-  float m = -INFINITY, s = 0.0f;
-  for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
-    float f[kVec];
-    E::unpack(zv[vi], f);
-    online_push_vec<kVec>(m, s, f);
+  const int32_t t_first = (sc.n > 0 && tid < sc.n) ? targets[tid] : ign;
+  float m = -INFINITY, s = 0.0f, zt = 0.0f;
+  if constexpr (kRes > 0) {
+    // As in k_row_ce: branch-free loads, then the target element; rows here
+    // hold at most 16 x kThreads vectors, so byte offsets fit in 32 bits.
+    const __amdgpu_buffer_rsrc_t rv = row_rsrc(zv, rs.nvec * 16);
+    uint4 buf[kRes];
+#pragma unroll
+    for (int j = 0; j < kRes; ++j)
+      buf[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rv, (j * kThreads + tid) * 16, 0, 0));
+    const T zt_bits = load_elem_bits<T>(row_rsrc(z, Vl * static_cast<int64_t>(sizeof(T))),
+                                        here ? static_cast<int>(local * sizeof(T)) : 0x7FFFFFF0);
+    if (sc.n > 0) count_partial<kThreads>(sc, targets, Vg, ign, t_first, cnt);
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRes; ++j) {
+      if (j * kThreads + tid < rs.nvec) {
+        float f[kVec];
+        E::unpack(buf[j], f);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) lm = fmaxf(lm, f[i]);
+      }
+    }
+    if (tid < rs.head) lm = fmaxf(lm, E::load(z + tid));
+    if (tid < Vl - rs.tail0) lm = fmaxf(lm, E::load(z + rs.tail0 + tid));
+    float ls = 0.0f;
+    if (lm != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kRes; ++j) {
+        if (j * kThreads + tid < rs.nvec) {
+          float f[kVec];
+          E::unpack(buf[j], f);
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) ls += __builtin_amdgcn_exp2f((f[i] - lm) * kLog2e);
+        }
+      }
+      if (tid < rs.head) ls += __builtin_amdgcn_exp2f((E::load(z + tid) - lm) * kLog2e);
+      if (tid < Vl - rs.tail0) ls += __builtin_amdgcn_exp2f((E::load(z + rs.tail0 + tid) - lm) * kLog2e);
+    }
+    m = lm;
+    s = ls;
+    zt = E::load(&zt_bits);
+  } else {
+    if (sc.n > 0) count_partial<kThreads>(sc, targets, Vg, ign, t_first, cnt);
+    for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+      float f[kVec];
+      E::unpack(zv[vi], f);
+      online_push_vec<kVec>(m, s, f);
+    }
+    if (tid < rs.head) online_push(m, s, E::load(z + tid));
+    if (tid < Vl - rs.tail0) online_push(m, s, E::load(z + rs.tail0 + tid));
+    if (tid == 0 && here) zt = E::load(z + local);
   }
-  if (tid < rs.head) online_push(m, s, E::load(z + tid));
-  if (tid < Vl - rs.tail0) online_push(m, s, E::load(z + rs.tail0 + tid));
+  // The reduction's barriers also publish the per-wave counts.
   float M, S;
   block_lse_parts<kThreads>(m, s, red0, red1, M, S);
+  if (sc.n > 0) count_finish<kThreads>(sc, cnt);
   if (tid == 0) {
-    const int32_t y = targets[row];
-    const int64_t local = static_cast<int64_t>(y) - v0;
-    const bool here = (y != ign) && y >= 0 && static_cast<int64_t>(y) < Vg && local >= 0 && local < Vl;
     rmax[row] = M;
     rsum[row] = S;
-    rtgt[row] = here ? E::load(z + local) : 0.0f;
+    rtgt[row] = here ? zt : 0.0f;
   }
+}
+
+template <typename T>
+static hipError_t shard_stats_typed(const void* Z, int64_t ldz, int64_t rows, int64_t Vl,
+                                    int64_t v0, int64_t Vg, const int32_t* targets, int32_t ign,
+                                    float* rmax, float* rsum, float* rtgt, SelfCount sc,
+                                    hipStream_t s) {
+  constexpr int kThreads = 1024;
+  const int64_t nvec_max = (Vl + Elem<T>::kVec - 1) / Elem<T>::kVec;
+  const T* z = static_cast<const T*>(Z);
+  const dim3 grid(static_cast<unsigned>(rows)), block(kThreads);
+#define LCE_SHARD(R)                                                                            \
+  hipLaunchKernelGGL((k_shard_stats<T, kThreads, R>), grid, block, 0, s, z, ldz, Vl, v0, Vg,     \
+                     targets, ign, rmax, rsum, rtgt, sc)
+  if (nvec_max <= 1 * kThreads) LCE_SHARD(1);
+  else if (nvec_max <= 2 * kThreads) LCE_SHARD(2);
+  else if (nvec_max <= 4 * kThreads) LCE_SHARD(4);
+  else if (nvec_max <= 8 * kThreads) LCE_SHARD(8);
+  else if (nvec_max <= 16 * kThreads) LCE_SHARD(16);
+  else LCE_SHARD(0);
+#undef LCE_SHARD
+  return hipGetLastError();
+}
+
+static hipError_t shard_stats_any(int dtype, const void* Z, int64_t ldz, int64_t rows,
+                                  int64_t V_local, int64_t vocab_start, int64_t V_global,
+                                  const int32_t* targets, int32_t ign, float* row_max,
+                                  float* row_sumexp, float* row_target, SelfCount sc,
+                                  hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == 1)
+    return shard_stats_typed<uint16_t>(Z, ldz, rows, V_local, vocab_start, V_global, targets, ign,
+                                       row_max, row_sumexp, row_target, sc, s);
+  if (dtype == 2)
+    return shard_stats_typed<Half>(Z, ldz, rows, V_local, vocab_start, V_global, targets, ign,
+                                   row_max, row_sumexp, row_target, sc, s);
+  return shard_stats_typed<float>(Z, ldz, rows, V_local, vocab_start, V_global, targets, ign,
+                                  row_max, row_sumexp, row_target, sc, s);
 }
 
 hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V_local,
                               int64_t vocab_start, int64_t V_global, const int32_t* targets,
                               int32_t ign, float* row_max, float* row_sumexp, float* row_target,
                               hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(rows));
-  if (dtype == 1)
-    hipLaunchKernelGGL((k_shard_stats<uint16_t, 1024>), grid, dim3(1024), 0, s,
-                       static_cast<const uint16_t*>(Z), ldz, V_local, vocab_start, V_global, targets,
-                       ign, row_max, row_sumexp, row_target);
-  else if (dtype == 2)
-    hipLaunchKernelGGL((k_shard_stats<Half, 1024>), grid, dim3(1024), 0, s,
-                       static_cast<const Half*>(Z), ldz, V_local, vocab_start, V_global, targets,
-                       ign, row_max, row_sumexp, row_target);
-  else
-    hipLaunchKernelGGL((k_shard_stats<float, 1024>), grid, dim3(1024), 0, s,
-                       static_cast<const float*>(Z), ldz, V_local, vocab_start, V_global, targets,
-                       ign, row_max, row_sumexp, row_target);
-  return hipGetLastError();
+  return shard_stats_any(dtype, Z, ldz, rows, V_local, vocab_start, V_global, targets, ign,
+                         row_max, row_sumexp, row_target, SelfCount{0, 0, nullptr}, s);
+}
+
+hipError_t launch_shard_stats_counted(int dtype, const void* Z, int64_t rows, int64_t V_local,
+                                      int64_t vocab_start, int64_t V_global,
+                                      const int32_t* targets, int32_t ign, float* row_max,
+                                      float* row_sumexp, float* row_target, WsHeader* hdr,
+                                      hipStream_t s) {
+  return shard_stats_any(dtype, Z, V_local, rows, V_local, vocab_start, V_global, targets, ign,
+                         row_max, row_sumexp, row_target, SelfCount{rows, 1, hdr}, s);
 }
 
 // ------------------------------------------------- vocabulary-shard backward

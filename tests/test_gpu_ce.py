@@ -165,6 +165,34 @@ def test_ce_target_count_paths(B, N):
     check_max_rel(to_host(g), ref_g, TOL["bf16"]["grad"], "grad")
 
 
+@pytest.mark.parametrize("N,Vl,dtype", [(64, 1000, "bf16"), (2049, 1000, "f32"), (8, 70001, "f16"),
+                                        (8, 140001, "bf16")])
+def test_shard_stats_bad_target_and_paths(B, N, Vl, dtype):
+    """Shard statistics of shard [1000, 1000 + Vl) of a 3 * Vl vocabulary:
+    register-resident (with the target count in the same launch up to 2048
+    rows, a separate count above) and streaming rows; a target outside the
+    global vocabulary is reported and a clean call clears the report."""
+    import torch
+    V = 3 * Vl
+    inp = synth.make_ce_inputs(N, Vl, dtype, std=2.0, ignore_frac=0.2, seed=Vl + N)
+    rng = np.random.default_rng(N)
+    y = rng.integers(0, V, size=N).astype(np.int32)
+    y[inp["targets"] == -100] = -100
+    y[0] = V
+    y[1] = 1000 + Vl // 2
+    ws = torch.zeros(B.ce_workspace_bytes(N, V), dtype=torch.uint8, device="cuda")
+    say("shard stats paths", N, Vl, dtype)
+    m, s, t = B.ce_shard_stats(to_dev(inp["logits"], dtype), to_dev(y, "i32"), 1000, V, workspace=ws)
+    assert B.flce_check_device_error(ws) == B.E_TARGET
+    rm, rs, rt = O.shard_stats(inp["logits_f32"], y, 1000, V)
+    assert np.array_equal(to_host(m), rm), "row max must be exact"
+    check_max_rel(to_host(s), rs, 1e-5, "sumexp")
+    assert np.array_equal(to_host(t), rt), "target logit must be exact"
+    y[0] = -100
+    B.ce_shard_stats(to_dev(inp["logits"], dtype), to_dev(y, "i32"), 1000, V, workspace=ws)
+    assert B.flce_check_device_error(ws) == B.OK
+
+
 def test_shard_stats_two_halves_combine(B):
     """[1024, 65536] bf16 logits split into vocabulary shards [0, 32768) and
     [32768, 65536); the host combination of the two shards' statistics equals
