@@ -30,7 +30,11 @@
  *     floating inputs share one type; 16-bit types need H % 8 == 0 and H,
  *     V below 2^22 (32-bit offsets inside a GEMM tile). Chunk
  *     logits and dlogits are stored in that type; losses, statistics and
- *     FLCE gradients are float32.
+ *     FLCE gradients are float32. With FLCE_F16 the dlogits inside the FLCE
+ *     calls are stored times a power of two and without the reduction's
+ *     scale, which the float32 gradient products apply (so a large
+ *     vocabulary's probabilities stay in fp16's normal range); the standalone
+ *     CE writes its fp16 gradient with the scale applied, as PyTorch does.
  *   - Targets are int32 class ids. A row is ignored iff its target equals
  *     ignore_index. A target that is not ignore_index and lies outside
  *     [0, V) is a device-detected error: the row is treated as ignored (zero

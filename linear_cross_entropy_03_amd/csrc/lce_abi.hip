@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <vector>
 
@@ -43,6 +44,31 @@ inline hipError_t gemm_for(int dtype, const GemmDesc& d, hipStream_t s) {
   return is16(dtype) ? launch_gemm_16(d, dtype == FLCE_F16, s) : launch_gemm_f32(d, s);
 }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Scaling of the gradients in the chunk buffer: fp16 dlogits are stored times
+// 2^kF16GradShift and without the reduction's scale (hdr->scale, or nothing
+// when the rows carry their own factors: hdr == null), which the gradient
+// GEMMs and column sums apply in fp32; other types store the scaled gradient.
+struct GradScaling {
+  int row_shift;           // grad_shift of the row kernel
+  const float* out_scale;  // consumers' device factor (null: 1)
+  int out_shift;           // consumers' power-of-two factor 2^-out_shift
+};
+// `bound` bounds the row kernel's factor before the shift (1 for the CE
+// rows, beta / P for DPO's per-row factors, 1 / T for distillation); the
+// shift is the largest that keeps bound * 2^shift within 2^kF16GradShift, so
+// the stored values stay finite in fp16 (at least 1).
+inline GradScaling grad_scaling(int dtype, const WsHeader* hdr, double bound = 1.0) {
+  if (dtype != FLCE_F16) return {0, nullptr, 0};
+  const double cap = std::ldexp(1.0, kF16GradShift);
+  int shift = 1;
+  while (shift < 30 && std::ldexp(bound, shift + 1) <= cap) ++shift;
+  return {shift, hdr != nullptr ? &hdr->scale : nullptr, shift};
+}
+inline void scale_output(GemmDesc& d, const GradScaling& g) {
+  d.out_scale = g.out_scale;
+  d.out_shift = g.out_shift;
+}
 
 constexpr int64_t kMaxRows = int64_t(1) << 31;     // grid.x of the row kernels
 constexpr int64_t kMaxDim = int64_t(1) << 30;
@@ -230,6 +256,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
   const size_t e = elem_bytes(dtype);
   const bool need_grad = grad_X != nullptr || grad_W != nullptr || grad_bias != nullptr;
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
+  const GradScaling gsc = grad_scaling(dtype, hdr);
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
@@ -245,13 +272,15 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
 
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_row_ce(dtype, zbuf, p.ldz, need_grad ? zbuf : nullptr, p.ldz, rows, V,
-                           p.ldz - V, targets + r0, ignore_index, hdr, loss_rows + r0, nullptr, s);
+                           p.ldz - V, targets + r0, ignore_index, hdr, loss_rows + r0, nullptr,
+                           gsc.row_shift, s);
     }));
     if (!need_grad) continue;
 
     if (grad_bias)
       LCE_TRY(timed(kKindOther, s, [&] {
-        return launch_colsum(dtype, zbuf, p.ldz, rows, V, grad_bias, !first, s);
+        return launch_colsum(dtype, zbuf, p.ldz, rows, V, grad_bias, !first, gsc.out_scale,
+                             gsc.out_shift, s);
       }));
 
     if (grad_X) {
@@ -259,6 +288,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
       g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
       g2.B = W; g2.ldb = H; g2.b_kmajor = false;
       g2.M = rows; g2.N = H; g2.K = V;
+      scale_output(g2, gsc);
       float* out = grad_X + static_cast<size_t>(r0) * H;
       if (p.dx_splits > 1) {
         g2.epilogue = kEpiStoreF32;
@@ -283,6 +313,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
       g3.M = V; g3.N = H; g3.K = rows;
       g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32;
       g3.k_splits = 1;
+      scale_output(g3, gsc);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }
@@ -438,7 +469,7 @@ int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* ta
     }));
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_row_ce(dtype, logits, V, grad_logits, V, N, V, 0, targets, ignore_index, hdr,
-                           loss_rows, nullptr, s);
+                           loss_rows, nullptr, 0, s);
     }));
   }
   if (reduction != FLCE_REDUCTION_NONE)
@@ -600,6 +631,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
   float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   const size_t e = elem_bytes(dtype);
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
+  const GradScaling gsc = grad_scaling(dtype, hdr);
 
   // Validity and the mean's N_valid are judged against the whole vocabulary.
   LCE_TRY(timed(kKindOther, s, [&] {
@@ -625,11 +657,13 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
     LCE_TRY(timed(kKindLogits, s, [&] { return gemm(g1, s); }));
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_shard_grad(dtype, zbuf, p.ldz, rows, V_local, p.ldz - V_local, vocab_start,
-                               V_global, targets + r0, ignore_index, row_lse + r0, hdr, s);
+                               V_global, targets + r0, ignore_index, row_lse + r0, hdr,
+                               gsc.row_shift, s);
     }));
     if (grad_bias_shard)
       LCE_TRY(timed(kKindOther, s, [&] {
-        return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, !first, s);
+        return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, !first,
+                             gsc.out_scale, gsc.out_shift, s);
       }));
     if (grad_X) {
       GemmDesc g2{};
@@ -637,6 +671,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
       g2.B = W_shard; g2.ldb = H; g2.b_kmajor = false;
       g2.M = rows; g2.N = H; g2.K = V_local;
       g2.epilogue = kEpiStoreF32;
+      scale_output(g2, gsc);
       float* out = grad_X + static_cast<size_t>(r0) * H;
       if (p.dx_splits > 1) {
         g2.C = split_buf; g2.ldc = H;
@@ -658,6 +693,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
       g3.M = V_local; g3.N = H; g3.K = rows;
       g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32;
       g3.k_splits = 1;
+      scale_output(g3, gsc);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }
@@ -702,6 +738,7 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
   float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st2) { return gemm_for(dtype, d, st2); };
   const float inv_tau = 1.0f / temperature;
+  const GradScaling gsc = grad_scaling(dtype, hdr, inv_tau);
 
   LCE_TRY(timed(kKindOther, s, [&] {
     return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
@@ -724,7 +761,7 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
     LCE_TRY(timed(kKindLogits, s, [&] { return gemm(gt, s); }));
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_row_jsd(dtype, zs, zt, p.ldz, rows, V, p.ldz - V, inv_tau, targets + r0,
-                            ignore_index, hdr, loss_rows + r0, s);
+                            ignore_index, hdr, loss_rows + r0, gsc.row_shift, s);
     }));
     if (grad_X_s) {
       GemmDesc g2{};
@@ -732,6 +769,7 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
       g2.B = W_s; g2.ldb = H_s; g2.b_kmajor = false;
       g2.M = rows; g2.N = H_s; g2.K = V;
       g2.epilogue = kEpiStoreF32;
+      scale_output(g2, gsc);
       float* out = grad_X_s + static_cast<size_t>(r0) * H_s;
       if (p.dx_splits > 1) {
         g2.C = split_buf; g2.ldc = H_s; g2.k_splits = p.dx_splits; g2.split_stride = rows * H_s;
@@ -750,6 +788,7 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
       g3.B = Xs_c; g3.ldb = H_s; g3.b_kmajor = false;
       g3.C = grad_W_s; g3.ldc = H_s; g3.M = V; g3.N = H_s; g3.K = rows;
       g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32; g3.k_splits = 1;
+      scale_output(g3, gsc);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }
@@ -826,7 +865,7 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
     LCE_TRY(logits(r0, rows));
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_row_ce(dtype, zbuf, p.ldz, nullptr, p.ldz, rows, V, p.ldz - V, targets + r0,
-                           ignore_index, hdr, loss_rows + r0, nullptr, s);
+                           ignore_index, hdr, loss_rows + r0, nullptr, 0, s);
     }));
   }
   LCE_TRY(timed(kKindOther, s, [&] {
@@ -836,6 +875,9 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
   // Pass 2: per-row weighted dlogits and the two gradient products. With a
   // single chunk its logits are still in the buffer (pass 1 only read them).
   const bool one_chunk = N <= p.chunk;
+  // The rows carry their own factors, |±beta sigma(-d) / P| <= beta / P.
+  const GradScaling gsc =
+      grad_scaling(dtype, nullptr, static_cast<double>(beta) / static_cast<double>(std::max<int64_t>(n_pairs, 1)));
   for (int64_t r0 = 0; r0 < N && (grad_X || grad_W); r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
@@ -843,7 +885,7 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
     if (!one_chunk) LCE_TRY(logits(r0, rows));
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_row_ce(dtype, zbuf, p.ldz, zbuf, p.ldz, rows, V, p.ldz - V, targets + r0,
-                           ignore_index, hdr, loss_rows + r0, row_scale + r0, s);
+                           ignore_index, hdr, loss_rows + r0, row_scale + r0, gsc.row_shift, s);
     }));
     if (grad_X) {
       GemmDesc g2{};
@@ -851,6 +893,7 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
       g2.B = W; g2.ldb = H; g2.b_kmajor = false;
       g2.M = rows; g2.N = H; g2.K = V;
       g2.epilogue = kEpiStoreF32;
+      scale_output(g2, gsc);
       float* out = grad_X + static_cast<size_t>(r0) * H;
       if (p.dx_splits > 1) {
         g2.C = split_buf; g2.ldc = H; g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
@@ -869,6 +912,7 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
       g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
       g3.C = grad_W; g3.ldc = H; g3.M = V; g3.N = H; g3.K = rows;
       g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32; g3.k_splits = 1;
+      scale_output(g3, gsc);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }

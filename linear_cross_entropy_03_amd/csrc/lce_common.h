@@ -193,7 +193,20 @@ struct GemmDesc {
   int epilogue;
   int k_splits;        // >1: split K; split s writes C + s*split_stride (kEpiStoreF32 only)
   int64_t split_stride;
+  // fp32 epilogues: the product is multiplied by 2^-out_shift and by *out_scale
+  // (when not null) before it is stored or added (deferred gradient scaling).
+  const float* out_scale;
+  int out_shift;
 };
+
+// fp16 dlogits in the chunk buffer: the row kernels store them times a power
+// of two (2^15 for the CE rows, whose factor before the shift is at most 1 in
+// magnitude) and without the reduction's scale, and the gradient GEMMs and
+// column sums apply scale * 2^-shift in fp32. Stored with the mean's
+// 1/N_valid, most probabilities of a 128k vocabulary (~1e-5 before scaling)
+// would fall below fp16's normal range (6.1e-5); the one-hot term times 2^15
+// stays below fp16's largest finite value.
+constexpr int kF16GradShift = 15;
 
 // 16-bit inputs (bf16, or fp16 when f16 is set), fp32 accumulation.
 hipError_t launch_gemm_16(const GemmDesc& d, bool f16, hipStream_t s);
@@ -208,10 +221,12 @@ hipError_t launch_count_targets(const int32_t* targets, int64_t n, int64_t V,
 // (stride ldg; may alias Z) receives scale * (softmax - onehot), and columns
 // [V, V + pad_cols) of it are set to zero.
 // row_scale: per-row gradient factors, or nullptr for the reduction's scale.
+// grad_shift > 0: the gradient is stored times 2^grad_shift (times row_scale
+// when given) and without the reduction's scale, which the consumer applies.
 hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* grad, int64_t ldg,
                          int64_t rows, int64_t V, int64_t pad_cols, const int32_t* targets,
                          int32_t ign, const WsHeader* hdr, float* loss_rows,
-                         const float* row_scale, hipStream_t s);
+                         const float* row_scale, int grad_shift, hipStream_t s);
 
 // Row CE over a whole call of `rows` rows (contiguous, stride V) that also
 // counts the targets: fills hdr (n_bad, n_valid, scale) as launch_count_targets
@@ -237,13 +252,13 @@ hipError_t launch_shard_stats_counted(int dtype, const void* Z, int64_t rows, in
 hipError_t launch_shard_grad(int dtype, void* Z, int64_t ldz, int64_t rows, int64_t V_local,
                              int64_t pad_cols, int64_t vocab_start, int64_t V_global,
                              const int32_t* targets, int32_t ign, const float* lse,
-                             const WsHeader* hdr, hipStream_t s);
+                             const WsHeader* hdr, int grad_shift, hipStream_t s);
 hipError_t launch_combine_stats(const float* ms, const float* ss, const float* ts, int64_t P,
                                 int64_t N, const int32_t* targets, int32_t ign, int64_t V_global,
                                 float* lse, float* loss_rows, hipStream_t s);
 hipError_t launch_row_jsd(int dtype, void* S, const void* Tt, int64_t ld, int64_t rows, int64_t V,
                           int64_t pad_cols, float inv_tau, const int32_t* targets, int32_t ign,
-                          const WsHeader* hdr, float* loss_rows, hipStream_t s);
+                          const WsHeader* hdr, float* loss_rows, int grad_shift, hipStream_t s);
 hipError_t launch_dpo(const float* loss_rows, int64_t P, int64_t S, const float* ref, float beta,
                       double* logp, float* loss, float* pair_loss, float* row_scale, hipStream_t s);
 hipError_t launch_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ign,
@@ -251,8 +266,10 @@ hipError_t launch_shift_labels(const int32_t* labels, int64_t B, int64_t S, int3
 hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader* hdr,
                               int reduction, float* loss, hipStream_t s);
 
+// Column sums of Z times 2^-out_shift (and *out_scale when not null).
 hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V,
-                         float* out, bool accumulate, hipStream_t s);
+                         float* out, bool accumulate, const float* out_scale, int out_shift,
+                         hipStream_t s);
 
 hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride,
                                 int64_t rows, int64_t cols, int64_t ld_out, float* out,

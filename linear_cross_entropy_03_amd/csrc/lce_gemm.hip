@@ -402,6 +402,8 @@ __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], cons
   static_assert(kFJ == 2, "64 output columns per wave");
   const int lane = threadIdx.x & 63, l32 = lane & 31, lhi = lane >> 5;
   float* C = static_cast<float*>(d.C) + static_cast<int64_t>(sp) * d.split_stride;
+  // Deferred gradient scaling (exact power of two, then the device scale).
+  const float f = __builtin_ldexpf(d.out_scale != nullptr ? *d.out_scale : 1.0f, -d.out_shift);
   // A quarter (32 rows) of the wave's result at a time.
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
@@ -434,6 +436,7 @@ __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], cons
     for (int u = 0; u < 8; ++u) {
       const int r = u * 4 + (lane >> 4), sl = lane & 15;
       float4 o = *reinterpret_cast<const float4*>(reg + r * 256 + ((sl ^ (r & 15)) << 4));
+      o.x *= f; o.y *= f; o.z *= f; o.w *= f;
       const int64_t m = mh + r;
       const int64_t n = n0 + col0 + sl * 4;
       if (m >= d.M || n >= d.N) continue;
@@ -913,6 +916,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmDesc d, int64_t tiles_n, i
         if (d.bias != nullptr) v += static_cast<const float*>(d.bias)[n];
         static_cast<float*>(d.C)[m * d.ldc + n] = v;
       } else {
+        v = __builtin_ldexpf(v * (d.out_scale != nullptr ? *d.out_scale : 1.0f), -d.out_shift);
         float* c = static_cast<float*>(d.C) + static_cast<int64_t>(sp) * d.split_stride + m * d.ldc + n;
         *c = (kEpi == kEpiAccumF32) ? *c + v : v;
       }

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
                                                      int32_t ign, const WsHeader* __restrict__ hdr,
                                                      float* __restrict__ loss_rows,
                                                      const float* __restrict__ row_scale,
-                                                     SelfCount sc) {
+                                                     int grad_shift, SelfCount sc) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   __shared__ float red0[kThreads / 64], red1[kThreads / 64];
@@ -268,10 +268,11 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   if (G == nullptr) return;
 
   // The gradient factor: the reduction's, or a per-row one (sequence-level
-  // losses such as DPO weight each token row separately).
-  const float c = valid ? (row_scale != nullptr ? row_scale[row]
-                                                : (sc.n > 0 ? self_scale : hdr->scale))
-                        : 0.0f;
+  // losses such as DPO weight each token row separately); with grad_shift
+  // the reduction's scale is left to the consumer.
+  const float c = !valid ? 0.0f
+                  : grad_shift > 0 ? __builtin_ldexpf(row_scale != nullptr ? row_scale[row] : 1.0f, grad_shift)
+                  : (row_scale != nullptr ? row_scale[row] : (sc.n > 0 ? self_scale : hdr->scale));
   T* g = G + row * ldg;
   uint4* gv = reinterpret_cast<uint4*>(g + rs.head);
   auto grad_of = [&](float x, int64_t v) -> float {
@@ -333,7 +334,8 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
                                                             int32_t ign,
                                                             const WsHeader* __restrict__ hdr,
                                                             float* __restrict__ loss_rows,
-                                                            const float* __restrict__ row_scale) {
+                                                            const float* __restrict__ row_scale,
+                                                            int grad_shift) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   constexpr int kThreads = pf::kThreads;
@@ -415,7 +417,9 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
     if (tid == 0) loss_rows[row] = valid ? (lse - zt) : 0.0f;
 
     if (G != nullptr) {
-      const float c = valid ? (row_scale != nullptr ? row_scale[row] : hdr->scale) : 0.0f;
+      const float c = !valid ? 0.0f
+                      : grad_shift > 0 ? __builtin_ldexpf(row_scale != nullptr ? row_scale[row] : 1.0f, grad_shift)
+                      : (row_scale != nullptr ? row_scale[row] : hdr->scale);
       const int yt = valid ? y : -1;
       T* g = G + row * ldg;
       uint4* gv = reinterpret_cast<uint4*>(g + head);
@@ -468,7 +472,7 @@ template <typename T, int kThreads>
 static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                                   int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
                                   const WsHeader* hdr, float* loss_rows, const float* row_scale,
-                                  SelfCount sc, hipStream_t s) {
+                                  int grad_shift, SelfCount sc, hipStream_t s) {
   constexpr int kVec = Elem<T>::kVec;
   const int64_t nvec_max = (V + kVec - 1) / kVec;
   const T* z = static_cast<const T*>(Z);
@@ -476,12 +480,13 @@ static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t l
   const dim3 grid(static_cast<unsigned>(rows)), block(kThreads);
 #define LCE_ROW_CE(R)                                                                           \
   hipLaunchKernelGGL((k_row_ce<T, kThreads, R>), grid, block, 0, s, z, ldz, g, ldg, V, pad_cols, \
-                     targets, ign, hdr, loss_rows, row_scale, sc)
+                     targets, ign, hdr, loss_rows, row_scale, grad_shift, sc)
   // Long rows, more rows than CUs: the persistent prefetching variant.
   if constexpr (kThreads == pf::kThreads) {
     if (sc.n == 0 && takes_persistent(nvec_max, rows)) {
       hipLaunchKernelGGL((k_row_ce_pf<T, 16>), dim3(static_cast<unsigned>(cu_count())), block, 0, s,
-                         z, ldz, g, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows, row_scale);
+                         z, ldz, g, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows, row_scale,
+                         grad_shift);
       return hipGetLastError();
     }
   }
@@ -499,35 +504,36 @@ template <typename T>
 static hipError_t row_ce_by_width(const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                                   int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
                                   const WsHeader* hdr, float* loss_rows, const float* row_scale,
-                                  SelfCount sc, hipStream_t s) {
+                                  int grad_shift, SelfCount sc, hipStream_t s) {
   if (V >= 16384)
     return row_ce_dispatch<T, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                                    row_scale, sc, s);
+                                    row_scale, grad_shift, sc, s);
   return row_ce_dispatch<T, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                                 row_scale, sc, s);
+                                 row_scale, grad_shift, sc, s);
 }
 
 static hipError_t row_ce_typed(int dtype, const void* Z, int64_t ldz, void* G, int64_t ldg,
                                int64_t rows, int64_t V, int64_t pad_cols, const int32_t* targets,
                                int32_t ign, const WsHeader* hdr, float* loss_rows,
-                               const float* row_scale, SelfCount sc, hipStream_t s) {
+                               const float* row_scale, int grad_shift, SelfCount sc,
+                               hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (dtype == 1)
     return row_ce_by_width<uint16_t>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                     loss_rows, row_scale, sc, s);
+                                     loss_rows, row_scale, grad_shift, sc, s);
   if (dtype == 2)
     return row_ce_by_width<Half>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                                 row_scale, sc, s);
+                                 row_scale, grad_shift, sc, s);
   return row_ce_by_width<float>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                                row_scale, sc, s);
+                                row_scale, grad_shift, sc, s);
 }
 
 hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                          int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
                          const WsHeader* hdr, float* loss_rows, const float* row_scale,
-                         hipStream_t s) {
+                         int grad_shift, hipStream_t s) {
   return row_ce_typed(dtype, Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                      row_scale, SelfCount{0, 0, nullptr}, s);
+                      row_scale, grad_shift, SelfCount{0, 0, nullptr}, s);
 }
 
 hipError_t launch_row_ce_counted(int dtype, const void* Z, void* G, int64_t rows, int64_t V,
@@ -539,9 +545,9 @@ hipError_t launch_row_ce_counted(int dtype, const void* Z, void* G, int64_t rows
   if (V >= 16384 && takes_persistent((V + vec - 1) / vec, rows)) {
     const hipError_t e = launch_count_targets(targets, rows, V, ign, reduction, hdr, s);
     if (e != hipSuccess) return e;
-    return launch_row_ce(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr, s);
+    return launch_row_ce(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr, 0, s);
   }
-  return row_ce_typed(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr,
+  return row_ce_typed(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr, 0,
                       SelfCount{rows, reduction, hdr}, s);
 }
 
@@ -692,7 +698,8 @@ hipError_t launch_shard_stats_counted(int dtype, const void* Z, int64_t rows, in
 
 // In place over one shard's logits [rows, V_local] (global ids v0 + j), given
 // the global lse of each row: dZ = c * (exp(z - lse) - [v0 + j == y]) with
-// c = the reduction scale for rows valid w.r.t. V_global, 0 otherwise. One
+// c = the reduction scale (2^grad_shift instead when grad_shift > 0) for rows
+// valid w.r.t. V_global, 0 otherwise. One
 // read and one write per element; pad columns [V_local, V_local + pad) are
 // zeroed for the GEMMs that read the chunk.
 template <typename T, int kThreads>
@@ -700,7 +707,8 @@ __global__ __launch_bounds__(kThreads) void k_shard_grad(T* Z, int64_t ldz, int6
                                                          int64_t pad_cols, int64_t v0, int64_t Vg,
                                                          const int32_t* __restrict__ targets,
                                                          int32_t ign, const float* __restrict__ lse,
-                                                         const WsHeader* __restrict__ hdr) {
+                                                         const WsHeader* __restrict__ hdr,
+                                                         int grad_shift) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   const int64_t row = blockIdx.x;
@@ -708,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void k_shard_grad(T* Z, int64_t ldz, int6
   T* z = Z + row * ldz;
   const int32_t y = targets[row];
   const bool valid = (y != ign) && y >= 0 && static_cast<int64_t>(y) < Vg;
-  const float c = valid ? hdr->scale : 0.0f;
+  const float c = !valid ? 0.0f : grad_shift > 0 ? __builtin_ldexpf(1.0f, grad_shift) : hdr->scale;
   const float L = lse[row];
   const int64_t jt = valid ? static_cast<int64_t>(y) - v0 : -1;  // may fall outside the shard
   auto grad_of = [&](float x, int64_t j) -> float {
@@ -737,18 +745,19 @@ __global__ __launch_bounds__(kThreads) void k_shard_grad(T* Z, int64_t ldz, int6
 hipError_t launch_shard_grad(int dtype, void* Z, int64_t ldz, int64_t rows, int64_t V_local,
                              int64_t pad_cols, int64_t vocab_start, int64_t V_global,
                              const int32_t* targets, int32_t ign, const float* lse,
-                             const WsHeader* hdr, hipStream_t s) {
+                             const WsHeader* hdr, int grad_shift, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(rows));
   if (dtype == 1)
     hipLaunchKernelGGL((k_shard_grad<uint16_t, 256>), grid, dim3(256), 0, s, static_cast<uint16_t*>(Z),
-                       ldz, V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr);
+                       ldz, V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr,
+                       grad_shift);
   else if (dtype == 2)
     hipLaunchKernelGGL((k_shard_grad<Half, 256>), grid, dim3(256), 0, s, static_cast<Half*>(Z), ldz,
-                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr);
+                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr, grad_shift);
   else
     hipLaunchKernelGGL((k_shard_grad<float, 256>), grid, dim3(256), 0, s, static_cast<float*>(Z), ldz,
-                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr);
+                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr, grad_shift);
   return hipGetLastError();
 }
 
@@ -802,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t
                                                       int64_t pad_cols, float inv_tau,
                                                       const int32_t* __restrict__ targets,
                                                       int32_t ign, const WsHeader* __restrict__ hdr,
-                                                      float* __restrict__ loss_rows) {
+                                                      float* __restrict__ loss_rows, int grad_shift) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   __shared__ float red0[kThreads / 64], red1[kThreads / 64];
@@ -880,7 +889,8 @@ __global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t
   if (tid == 0) loss_rows[row] = valid ? L : 0.0f;
 
   // Pass 3: the student gradient, in place.
-  const float c = valid ? hdr->scale * inv_tau : 0.0f;
+  const float c = !valid ? 0.0f
+                  : (grad_shift > 0 ? __builtin_ldexpf(1.0f, grad_shift) : hdr->scale) * inv_tau;
   auto grad = [&](float a, float b) -> float {
     float lp, lm;
     terms(a, b, lp, lm);
@@ -911,21 +921,21 @@ __global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t
 
 hipError_t launch_row_jsd(int dtype, void* S, const void* Tt, int64_t ld, int64_t rows, int64_t V,
                           int64_t pad_cols, float inv_tau, const int32_t* targets, int32_t ign,
-                          const WsHeader* hdr, float* loss_rows, hipStream_t s) {
+                          const WsHeader* hdr, float* loss_rows, int grad_shift, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(rows));
   if (dtype == 1)
     hipLaunchKernelGGL((k_row_jsd<uint16_t, 1024>), grid, dim3(1024), 0, s, static_cast<uint16_t*>(S),
                        static_cast<const uint16_t*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
-                       loss_rows);
+                       loss_rows, grad_shift);
   else if (dtype == 2)
     hipLaunchKernelGGL((k_row_jsd<Half, 1024>), grid, dim3(1024), 0, s, static_cast<Half*>(S),
                        static_cast<const Half*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
-                       loss_rows);
+                       loss_rows, grad_shift);
   else
     hipLaunchKernelGGL((k_row_jsd<float, 1024>), grid, dim3(1024), 0, s, static_cast<float*>(S),
                        static_cast<const float*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
-                       loss_rows);
+                       loss_rows, grad_shift);
   return hipGetLastError();
 }
 
@@ -1045,11 +1055,13 @@ hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader*
 
 // ---------------------------------------------------- bias-gradient colsum
 
-// out[v] (+)= sum over rows of Z[r, v]; each lane owns two adjacent columns
-// and walks the rows in order (deterministic).
+// out[v] (+)= f * sum over rows of Z[r, v], f = 2^-out_shift (* *out_scale);
+// each lane owns two adjacent columns and walks the rows in order
+// (deterministic).
 template <typename T>
 __global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ Z, int64_t ldz, int64_t rows,
-                                                int64_t V, float* __restrict__ out, int accumulate) {
+                                                int64_t V, float* __restrict__ out, int accumulate,
+                                                const float* __restrict__ out_scale, int out_shift) {
   const int64_t v = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 2;
   if (v >= V) return;
   const bool two = v + 1 < V;
@@ -1070,23 +1082,26 @@ __global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ Z, int64_t
     a0 += Elem<T>::load(p + r * ldz);
     if (two) a1 += Elem<T>::load(p + r * ldz + 1);
   }
+  const float f = __builtin_ldexpf(out_scale != nullptr ? *out_scale : 1.0f, -out_shift);
+  a0 *= f;
+  a1 *= f;
   if (accumulate) { a0 += out[v]; if (two) a1 += out[v + 1]; }
   out[v] = a0;
   if (two) out[v + 1] = a1;
 }
 
 hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V, float* out,
-                         bool accumulate, hipStream_t s) {
+                         bool accumulate, const float* out_scale, int out_shift, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((V + 511) / 512));
   if (dtype == 1)
     hipLaunchKernelGGL(k_colsum<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(Z),
-                       ldz, rows, V, out, accumulate ? 1 : 0);
+                       ldz, rows, V, out, accumulate ? 1 : 0, out_scale, out_shift);
   else if (dtype == 2)
     hipLaunchKernelGGL(k_colsum<Half>, grid, dim3(256), 0, s, static_cast<const Half*>(Z), ldz, rows,
-                       V, out, accumulate ? 1 : 0);
+                       V, out, accumulate ? 1 : 0, out_scale, out_shift);
   else
     hipLaunchKernelGGL(k_colsum<float>, grid, dim3(256), 0, s, static_cast<const float*>(Z), ldz,
-                       rows, V, out, accumulate ? 1 : 0);
+                       rows, V, out, accumulate ? 1 : 0, out_scale, out_shift);
   return hipGetLastError();
 }
 

@@ -106,6 +106,8 @@ WORKLOADS = {
                           reduction="mean", std=2.0, ignore_frac=0.05),
     "llama1b_head_bf16": dict(kind="flce", N=8192, H=2048, V=128256, dtype="bf16",
                               reduction="mean", ignore_frac=0.1),
+    "llama1b_head_f16": dict(kind="flce", N=8192, H=2048, V=128256, dtype="f16",
+                             reduction="mean", ignore_frac=0.1),
     "llama8b_head_bf16": dict(kind="flce", N=32768, H=4096, V=128256, dtype="bf16",
                               reduction="mean", ignore_frac=0.1, target_dist="zipf"),
     "vocab256k_bias_bf16": dict(kind="flce", N=32768, H=4096, V=256000, dtype="bf16",

@@ -292,7 +292,8 @@ def _run_jsd(B, s_inp, t_inp, temperature, reduction, chunk_rows=0):
 
 
 @pytest.mark.parametrize("dtype,reduction,temperature,chunk", [
-    ("bf16", "mean", 1.0, 256), ("f32", "none", 2.0, 0), ("f16", "sum", 1.5, 0)])
+    ("bf16", "mean", 1.0, 256), ("f32", "none", 2.0, 0), ("f16", "sum", 1.5, 0),
+    ("f16", "mean", 0.5, 256)])
 def test_jsd_distillation_against_oracle(B, dtype, reduction, temperature, chunk):
     """Student (H 136) distilled towards a teacher with another hidden size
     (H 72) over a ragged vocabulary (V 1000); 10% of rows masked."""
@@ -354,7 +355,8 @@ def _dpo_inputs(P, S, H, V, dtype, seed):
 @pytest.mark.parametrize("dtype,P,S,H,V,chunk", [
     ("bf16", 3, 200, 136, 1000, 0),        # one chunk: no recompute
     ("bf16", 2, 300, 64, 3001, 256),       # four chunks: logits recomputed
-    ("f32", 3, 64, 64, 900, 128)])
+    ("f32", 3, 64, 64, 900, 128),
+    ("f16", 2, 300, 64, 3001, 256)])       # fp16: per-row factors with a power-of-two shift
 def test_dpo_against_oracle(B, dtype, P, S, H, V, chunk):
     import torch
     inp, ref = _dpo_inputs(P, S, H, V, dtype, seed=70 + P)

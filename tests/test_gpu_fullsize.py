@@ -2,17 +2,17 @@
 benchmark times (planner-chosen chunking), on outputs the FP64 oracle can
 compute one by one, plus properties that hold at any size.
 
-Shapes: Llama-3.2-1B head (N 8192, H 2048, V 128256, mean), Llama-3-8B head
-(N 32768, H 4096, V 128256, Zipf targets, mean), 256k vocabulary with bias
-(N 32768, H 4096, V 256000, sum).
+Shapes: Llama-3.2-1B head (N 8192, H 2048, V 128256, mean; bf16 and IEEE half),
+Llama-3-8B head (N 32768, H 4096, V 128256, Zipf targets, mean), 256k vocabulary with
+bias (N 32768, H 4096, V 256000, sum).
 
 Per workload:
   * sampled token rows: per-row loss and grad_X rows against the oracle
-    (bf16 bar: 2e-3 of the largest sampled loss, 1e-2 of the largest sampled
-    |grad_X|), ignored rows exactly zero;
+    (the 16-bit bar: 2e-3 of the largest sampled loss, 1e-2 of the largest
+    sampled |grad_X|), ignored rows exactly zero;
   * the reduced loss equals the float64 reduction of the per-row losses of a
     reduction="none" call on the same inputs;
-  * sum over v of grad_W[v, :] and of grad_bias vanish up to bf16 dlogits
+  * sum over v of grad_W[v, :] and of grad_bias vanish up to 16-bit dlogits
     rounding (at most 2**-8 per valid row);
   * sampled vocabulary rows of grad_W (and grad_bias): the most frequent
     target, a target-free row and random rows, against the oracle (this needs
@@ -28,7 +28,7 @@ from oracle import flce_oracle as O
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = ["llama1b_head_bf16", "llama8b_head_bf16", "vocab256k_bias_bf16"]
+WORKLOADS = ["llama1b_head_bf16", "llama1b_head_f16", "llama8b_head_bf16", "vocab256k_bias_bf16"]
 _CACHE = {}
 
 
@@ -60,9 +60,11 @@ def _results(B, name):
     cfg = synth.WORKLOADS[name]
     say(name, "generating inputs")
     inp = synth.make_workload(name)
-    X, W, b = (to_dev(inp[k], "bf16") for k in ("X", "W", "bias"))
+    dt = cfg["dtype"]
+    X, W, b = (to_dev(inp[k], dt) for k in ("X", "W", "bias"))
     y = to_dev(inp["targets"], "i32")
-    say(name, "flce", cfg["reduction"], "launch configuration", B.flce_plan(cfg["N"], cfg["H"], cfg["V"], B.BF16))
+    code = B.F16 if dt == "f16" else B.BF16
+    say(name, "flce", cfg["reduction"], "launch configuration", B.flce_plan(cfg["N"], cfg["H"], cfg["V"], code))
     loss, gX, gW, gb = B.flce_forward_backward(X, W, y, bias=b, reduction=cfg["reduction"])
     torch.cuda.synchronize()
     out = {"loss": to_host(loss), "gX": to_host(gX, f64=False), "gW": to_host(gW, f64=False),
@@ -105,7 +107,7 @@ def test_fullsize_rows_and_properties(workload):
     say(name, "oracle rows", len(rows))
     lr, gx = O.flce_rows(_f64(inp["X_f32"]), _f64(inp["W_f32"]), y, rows, bias=_f64(inp["bias_f32"]),
                          reduction=red)
-    t = TOL["bf16"]
+    t = TOL[cfg["dtype"]]
     check_max_rel(r["rows"][rows], lr, t["loss"], "sampled loss rows")
     check_max_rel(r["gX"][rows].astype(np.float64), gx, t["grad"], "sampled grad_X rows")
 
@@ -130,7 +132,7 @@ def test_fullsize_grad_w_rows(workload):
     say(name, "oracle grad_W rows (float64 logsumexp over every token row)")
     gw, gb = O.flce_grad_w_rows(_f64(inp["X_f32"]), _f64(inp["W_f32"]), y, vrows,
                                 bias=_f64(inp["bias_f32"]), reduction=cfg["reduction"])
-    t = TOL["bf16"]
+    t = TOL[cfg["dtype"]]
     check_max_rel(r["gW"][vrows].astype(np.float64), gw, t["grad"], "sampled grad_W rows")
     if r["gb"] is not None:
         check_max_rel(r["gb"][vrows], gb, t["grad"], "sampled grad_bias entries")
