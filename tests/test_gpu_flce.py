@@ -342,6 +342,17 @@ def test_degenerate_shapes(B, dtype, N, H, V):
         check_against_oracle(inp, "mean", got, want=("X", "W"))
 
 
+@pytest.mark.parametrize("N,H,V", [(32, 8, (1 << 22) - 8), (8, (1 << 22) - 8, 8)])
+def test_maximum_strides_bf16(B, N, H, V):
+    """The largest row strides the 16-bit path accepts (H and the chunk buffer's
+    row stride below 2^22 elements): a GEMM tile's byte offsets reach
+    255 * 2 * (2^22 - 8), just inside 32 bits; the long rows also take the
+    streaming row kernel and split-K for grad_X."""
+    inp = synth.make_flce_inputs(N, H, V, "bf16", w_std=0.05, ignore_frac=0.1, seed=5)
+    say("flce maximum strides", N, H, V, B.flce_plan(N, H, V, B.BF16))
+    check_against_oracle(inp, "mean", run_flce(B, inp, "mean"), want=("X", "W"))
+
+
 def _dpo_inputs(P, S, H, V, dtype, seed):
     inp = synth.make_flce_inputs(2 * P * S, H, V, dtype, w_std=0.08, ignore_frac=0.0, seed=seed)
     y = inp["targets"]
