@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-vp", action="store_true",
                     help="skip the vocabulary-parallel shard measurement")
     ap.add_argument("--no-mh", action="store_true", help="skip the multi-head measurement")
+    ap.add_argument("--no-g16", action="store_true",
+                    help="skip the 16-bit-gradient measurement")
     ap.add_argument("--no-distill", action="store_true", help="skip the distillation measurement")
     ap.add_argument("--no-dpo", action="store_true", help="skip the DPO measurement")
     ap.add_argument("--no-eager", action="store_true",
@@ -477,6 +479,40 @@ def bench_dpo(torch, B, X, W, y, cfg, n_pairs=4, seq_len=1024, reps=3):
     return out
 
 
+def bench_grad16(torch, B, X, W, y, cfg, reps=5):
+    """The same FLCE step with the gradients written in the input's 16-bit type
+    (flce_forward_backward_ex): grad_W accumulated chunk by chunk in bf16."""
+    N, H, V = cfg["N"], cfg["H"], cfg["V"]
+    gX = torch.empty(N, H, dtype=X.dtype, device="cuda")
+    gW = torch.empty(V, H, dtype=X.dtype, device="cuda")
+    loss = torch.empty(1, device="cuda")
+    ws = torch.empty(B.flce_workspace_bytes(N, H, V, B.BF16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        B.flce_forward_backward(X, W, y, reduction=cfg["reduction"], grad_X=gX, grad_W=gW,
+                                grad_bias=False, loss=loss, workspace=ws, stream=stream,
+                                grad_dtype="input")
+    call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    out = {
+        "workload": "llama8b_head_bf16 with bf16 grad_X and grad_W",
+        "ms_per_step": ms, "tokens_per_s": N / (ms * 1e-3),
+        "frac_bf16_peak": 6.0 * N * H * V / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        "gradient_output_bytes": (N * H + V * H) * 2, "float32_gradient_output_bytes": (N * H + V * H) * 4,
+        "loss": float(loss.item()),
+    }
+    del gX, gW, ws
+    return out
+
+
 def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
     """K LM heads over shared hidden states (the liger README's Medusa example:
     5 heads) at the 8B head's shape on the first n_rows token rows. Head k's
@@ -695,6 +731,9 @@ def main():
     if not args.no_dpo:
         log("DPO")
         result["dpo"] = bench_dpo(torch, B, X, W, y, cfg)
+    if not args.no_g16:
+        log("16-bit gradients")
+        result["grad16"] = bench_grad16(torch, B, X, W, y, cfg)
     if not args.no_mh:
         log("multi-head")
         result["multihead"] = bench_multihead(torch, B, X, W, y, cfg)

@@ -121,6 +121,26 @@ int flce_forward_backward(const void* X, const void* W, const void* bias,
                           void* stream);
 
 /*
+ * As flce_forward_backward, with the gradients in the input's 16-bit type
+ * when grad_dtype equals dtype (FLCE_BF16 or FLCE_F16): grad_X, grad_W and
+ * grad_bias then point to arrays of that type. grad_dtype FLCE_F32 gives
+ * float32 gradients (flce_forward_backward). The pages test FP16/BF16 logits
+ * and gradients (DeepSpeed vocab-parallel CE page, Real-device validation) but
+ * fix no accumulation rule; here products are accumulated in float32 within a
+ * chunk and rounded to the output type once per chunk: grad_X rows once,
+ * grad_W and grad_bias once per chunk they are added to (read, add in float32,
+ * round), so their rounding depends on chunk_rows. It halves the gradient
+ * outputs' memory (grad_W of a 128k x 4096 head: 1.05 GB instead of 2.1 GB).
+ * FLCE_E_INVALID_ARG for any other grad_dtype (float32 inputs take
+ * FLCE_F32 only).
+ */
+int flce_forward_backward_ex(const void* X, const void* W, const void* bias,
+                             const int32_t* targets, int64_t N, int64_t H, int64_t V, int dtype,
+                             int32_t ignore_index, int reduction, int grad_dtype, float* loss,
+                             void* grad_X, void* grad_W, void* grad_bias, void* workspace,
+                             size_t workspace_bytes, int64_t chunk_rows, void* stream);
+
+/*
  * Several LM heads over the same hidden states in one call (the Medusa
  * example the liger README points FusedLinearCrossEntropy users to: extra
  * heads predicting tokens further ahead). Head k has its own weight, bias,

@@ -33,6 +33,8 @@ _SIGNATURES = {
     "flce_plan": (_int, [_i64, _i64, _i64, _int, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
     "flce_forward_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _i32, _int,
                                      _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
+    "flce_forward_backward_ex": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _i32, _int,
+                                        _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
     "ce_workspace_bytes": (_sz, [_i64, _i64]),
     "ce_forward_backward": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _i32, _int, _vp, _vp, _sz, _vp]),
     "ce_shard_stats": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _int, _i32, _vp, _vp, _vp, _vp,
@@ -161,44 +163,55 @@ def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
 
 
-def _grad_arg(want, shape, device):
-    """A gradient output: the given tensor, a new float32 one (True), or None."""
+def _grad_arg(want, shape, device, dtype=None):
+    """A gradient output: the given tensor, a new one (True; float32 unless
+    dtype is given), or None."""
     if isinstance(want, torch.Tensor):
         return want
-    return _empty(shape, torch.float32, device) if want else None
+    return _empty(shape, dtype or torch.float32, device) if want else None
 
 
 def flce_forward_backward(X, W, targets, bias=None, ignore_index=-100, reduction="mean",
                           grad_X=True, grad_W=True, grad_bias=None, loss=None, workspace=None,
-                          chunk_rows=0, stream=None):
+                          chunk_rows=0, stream=None, grad_dtype="f32"):
     """Fused linear cross-entropy forward + backward.
 
-    X [N, H] and W [V, H] (and bias [V]) share one dtype (float32 or bfloat16);
-    targets is int32 [N]. grad_X / grad_W / grad_bias: a preallocated float32
-    tensor, True (allocate), or False/None (skip; grad_bias defaults to
-    bias is not None). Returns (loss, grad_X, grad_W, grad_bias).
+    X [N, H] and W [V, H] (and bias [V]) share one dtype (float32, bfloat16 or
+    float16); targets is int32 [N]. grad_X / grad_W / grad_bias: a
+    preallocated tensor, True (allocate), or False/None (skip; grad_bias
+    defaults to bias is not None). grad_dtype "f32" gives float32 gradients;
+    "input" gives them in X's 16-bit dtype (flce_forward_backward_ex).
+    Returns (loss, grad_X, grad_W, grad_bias).
     """
     N, H = X.shape
     V = W.shape[0]
     dev = X.device
     dt = _dtype_code(X)
+    if grad_dtype not in ("f32", "input"):
+        raise ValueError("grad_dtype must be 'f32' or 'input'")
+    g16 = grad_dtype == "input"
+    gtorch = X.dtype if g16 else torch.float32
     if grad_bias is None:
         grad_bias = bias is not None
-    gX = _grad_arg(grad_X, (N, H), dev)
-    gW = _grad_arg(grad_W, (V, H), dev)
-    gb = _grad_arg(grad_bias, (V,), dev)
+    gX = _grad_arg(grad_X, (N, H), dev, gtorch)
+    gW = _grad_arg(grad_W, (V, H), dev, gtorch)
+    gb = _grad_arg(grad_bias, (V,), dev, gtorch)
     if loss is None:
         loss = _empty((N,) if reduction == "none" else (1,), torch.float32, dev)
     if workspace is None:
         workspace = _empty((max(1, flce_workspace_bytes(N, H, V, dt, chunk_rows)),), torch.uint8, dev)
-    st = lib().flce_forward_backward(
-        _ptr(X, "X"), _ptr(W, "W", X.dtype), _ptr(bias, "bias", X.dtype),
-        _ptr(targets, "targets", torch.int32), N, H, V, dt, ignore_index, _red(reduction),
-        _ptr(loss, "loss", torch.float32), _ptr(gX, "grad_X", torch.float32),
-        _ptr(gW, "grad_W", torch.float32), _ptr(gb, "grad_bias", torch.float32),
-        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
-        _stream(stream))
-    _check(st, "flce_forward_backward")
+    args = [_ptr(X, "X"), _ptr(W, "W", X.dtype), _ptr(bias, "bias", X.dtype),
+            _ptr(targets, "targets", torch.int32), N, H, V, dt, ignore_index, _red(reduction)]
+    rest = [_ptr(loss, "loss", torch.float32), _ptr(gX, "grad_X", gtorch),
+            _ptr(gW, "grad_W", gtorch), _ptr(gb, "grad_bias", gtorch),
+            _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
+            _stream(stream)]
+    if g16:
+        st = lib().flce_forward_backward_ex(*args, dt, *rest)
+        _check(st, "flce_forward_backward_ex")
+    else:
+        st = lib().flce_forward_backward(*args, *rest)
+        _check(st, "flce_forward_backward")
     return loss, gX, gW, gb
 
 

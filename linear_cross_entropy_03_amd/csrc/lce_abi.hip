@@ -249,8 +249,12 @@ namespace {
 // after). Targets must have been counted into hdr.
 int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const void* bias,
                 const int32_t* targets, int64_t N, int64_t H, int64_t V, int32_t ignore_index,
-                WsHeader* hdr, float* loss_rows, float* grad_X, bool accum_gx, float* grad_W,
-                float* grad_bias, char* ws, hipStream_t s) {
+                WsHeader* hdr, float* loss_rows, void* grad_X, bool accum_gx, void* grad_W,
+                void* grad_bias, int grad_dtype, char* ws, hipStream_t s) {
+  // grad_dtype: FLCE_F32, or the 16-bit input type (gradients rounded to it;
+  // grad_W and grad_bias are accumulated across chunks in that type).
+  const bool g16 = grad_dtype != FLCE_F32;
+  const size_t ge = g16 ? 2 : 4;
   void* zbuf = ws + p.off_chunk;
   float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   const size_t e = elem_bytes(dtype);
@@ -279,8 +283,8 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
 
     if (grad_bias)
       LCE_TRY(timed(kKindOther, s, [&] {
-        return launch_colsum(dtype, zbuf, p.ldz, rows, V, grad_bias, !first, gsc.out_scale,
-                             gsc.out_shift, s);
+        return launch_colsum(dtype, zbuf, p.ldz, rows, V, grad_bias, grad_dtype, !first,
+                             gsc.out_scale, gsc.out_shift, s);
       }));
 
     if (grad_X) {
@@ -289,17 +293,18 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
       g2.B = W; g2.ldb = H; g2.b_kmajor = false;
       g2.M = rows; g2.N = H; g2.K = V;
       scale_output(g2, gsc);
-      float* out = grad_X + static_cast<size_t>(r0) * H;
+      void* out = static_cast<char*>(grad_X) + static_cast<size_t>(r0) * H * ge;
       if (p.dx_splits > 1) {
         g2.epilogue = kEpiStoreF32;
         g2.C = split_buf; g2.ldc = H;
         g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, accum_gx, s);
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, grad_dtype,
+                                      accum_gx, s);
         }));
       } else {
-        g2.epilogue = accum_gx ? kEpiAccumF32 : kEpiStoreF32;
+        g2.epilogue = accum_gx ? (g16 ? kEpiAccum16 : kEpiAccumF32) : (g16 ? kEpiStore16 : kEpiStoreF32);
         g2.C = out; g2.ldc = H; g2.k_splits = 1;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
       }
@@ -311,7 +316,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
       g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
       g3.C = grad_W; g3.ldc = H;
       g3.M = V; g3.N = H; g3.K = rows;
-      g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32;
+      g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
       g3.k_splits = 1;
       scale_output(g3, gsc);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
@@ -323,7 +328,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
 // Validation shared by the single- and multi-head calls.
 int validate_flce(const void* X, const void* W, const void* bias, const int32_t* targets,
                   int64_t N, int64_t H, int64_t V, int dtype, int reduction, const float* loss,
-                  const float* grad_X, const float* grad_W, const float* grad_bias,
+                  const void* grad_X, const void* grad_W, const void* grad_bias,
                   int64_t chunk_rows, const void* workspace) {
   int st = validate_common(dtype, reduction);
   if (st != FLCE_OK) return st;
@@ -345,18 +350,15 @@ size_t head_slot_bytes(int64_t N) {
   return align_up(sizeof(WsHeader)) + align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float));
 }
 
-}  // namespace
-
-extern "C" {
-
-int flce_forward_backward(const void* X, const void* W, const void* bias, const int32_t* targets,
-                          int64_t N, int64_t H, int64_t V, int dtype, int32_t ignore_index,
-                          int reduction, float* loss, float* grad_X, float* grad_W,
-                          float* grad_bias, void* workspace, size_t workspace_bytes,
-                          int64_t chunk_rows, void* stream) {
+int flce_forward_backward_impl(const void* X, const void* W, const void* bias,
+                               const int32_t* targets, int64_t N, int64_t H, int64_t V, int dtype,
+                               int32_t ignore_index, int reduction, int grad_dtype, float* loss,
+                               void* grad_X, void* grad_W, void* grad_bias, void* workspace,
+                               size_t workspace_bytes, int64_t chunk_rows, void* stream) {
   int st = validate_flce(X, W, bias, targets, N, H, V, dtype, reduction, loss, grad_X, grad_W,
                          grad_bias, chunk_rows, workspace);
   if (st != FLCE_OK) return st;
+  if (grad_dtype != FLCE_F32 && grad_dtype != dtype) return FLCE_E_INVALID_ARG;
   Plan p;
   if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < p.total) return FLCE_E_WORKSPACE;
@@ -370,17 +372,41 @@ int flce_forward_backward(const void* X, const void* W, const void* bias, const 
     return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
   }));
   if (N == 0) {
-    if (grad_W) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W, V * H, 0.0f, s); }));
-    if (grad_bias) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_bias, V, 0.0f, s); }));
+    if (grad_W) LCE_TRY(timed(kKindOther, s, [&] { return launch_zero(grad_W, V * H, grad_dtype, s); }));
+    if (grad_bias) LCE_TRY(timed(kKindOther, s, [&] { return launch_zero(grad_bias, V, grad_dtype, s); }));
   }
   st = flce_chunks(p, dtype, X, W, bias, targets, N, H, V, ignore_index, hdr, loss_rows, grad_X,
-                   false, grad_W, grad_bias, ws, s);
+                   false, grad_W, grad_bias, grad_dtype, ws, s);
   if (st != FLCE_OK) return st;
   if (reduction != FLCE_REDUCTION_NONE)
     LCE_TRY(timed(kKindOther, s, [&] {
       return launch_reduce_loss(loss_rows, N, hdr, reduction, loss, s);
     }));
   return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flce_forward_backward(const void* X, const void* W, const void* bias, const int32_t* targets,
+                          int64_t N, int64_t H, int64_t V, int dtype, int32_t ignore_index,
+                          int reduction, float* loss, float* grad_X, float* grad_W,
+                          float* grad_bias, void* workspace, size_t workspace_bytes,
+                          int64_t chunk_rows, void* stream) {
+  return flce_forward_backward_impl(X, W, bias, targets, N, H, V, dtype, ignore_index, reduction,
+                                    FLCE_F32, loss, grad_X, grad_W, grad_bias, workspace,
+                                    workspace_bytes, chunk_rows, stream);
+}
+
+int flce_forward_backward_ex(const void* X, const void* W, const void* bias,
+                             const int32_t* targets, int64_t N, int64_t H, int64_t V, int dtype,
+                             int32_t ignore_index, int reduction, int grad_dtype, float* loss,
+                             void* grad_X, void* grad_W, void* grad_bias, void* workspace,
+                             size_t workspace_bytes, int64_t chunk_rows, void* stream) {
+  return flce_forward_backward_impl(X, W, bias, targets, N, H, V, dtype, ignore_index, reduction,
+                                    grad_dtype, loss, grad_X, grad_W, grad_bias, workspace,
+                                    workspace_bytes, chunk_rows, stream);
 }
 
 size_t flce_multihead_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t K, int dtype,
@@ -430,7 +456,7 @@ int flce_multihead_forward_backward(const void* X, const void* W, const void* bi
       if (gbk) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(gbk, V, 0.0f, s); }));
     }
     st = flce_chunks(p, dtype, X, Wk, bk, tk, N, H, V, ignore_index, hdr, loss_rows, grad_X, k > 0,
-                     gWk, gbk, ws, s);
+                     gWk, gbk, FLCE_F32, ws, s);
     if (st != FLCE_OK) return st;
     if (reduction != FLCE_REDUCTION_NONE)
       LCE_TRY(timed(kKindOther, s, [&] {
@@ -662,7 +688,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
     }));
     if (grad_bias_shard)
       LCE_TRY(timed(kKindOther, s, [&] {
-        return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, !first,
+        return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, FLCE_F32, !first,
                              gsc.out_scale, gsc.out_shift, s);
       }));
     if (grad_X) {
@@ -678,7 +704,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
         g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, false, s);
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, FLCE_F32, false, s);
         }));
       } else {
         g2.C = out; g2.ldc = H; g2.k_splits = 1;
@@ -775,7 +801,7 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
         g2.C = split_buf; g2.ldc = H_s; g2.k_splits = p.dx_splits; g2.split_stride = rows * H_s;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H_s, rows, H_s, H_s, out, false, s);
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H_s, rows, H_s, H_s, out, FLCE_F32, false, s);
         }));
       } else {
         g2.C = out; g2.ldc = H_s; g2.k_splits = 1;
@@ -899,7 +925,7 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
         g2.C = split_buf; g2.ldc = H; g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, false, s);
+          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, FLCE_F32, false, s);
         }));
       } else {
         g2.C = out; g2.ldc = H; g2.k_splits = 1;

@@ -179,7 +179,9 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 enum Epilogue : int {
   kEpiLogits = 0,   // C (input dtype) = acc (+ bias[n]); C is [M, ldc]
   kEpiStoreF32 = 1, // C (float) = acc
-  kEpiAccumF32 = 2  // C (float) += acc
+  kEpiAccumF32 = 2, // C (float) += acc
+  kEpiStore16 = 3,  // C (input dtype) = round(acc)
+  kEpiAccum16 = 4   // C (input dtype) = round(C + acc)
 };
 
 struct GemmDesc {
@@ -266,15 +268,20 @@ hipError_t launch_shift_labels(const int32_t* labels, int64_t B, int64_t S, int3
 hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader* hdr,
                               int reduction, float* loss, hipStream_t s);
 
-// Column sums of Z times 2^-out_shift (and *out_scale when not null).
+// Column sums of Z times 2^-out_shift (and *out_scale when not null) into out
+// of out_dtype (0 float, 1 bf16, 2 fp16; accumulation rounds once per call).
 hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V,
-                         float* out, bool accumulate, const float* out_scale, int out_shift,
-                         hipStream_t s);
+                         void* out, int out_dtype, bool accumulate, const float* out_scale,
+                         int out_shift, hipStream_t s);
 
+// out (+)= the sum of the K-split partials; out_dtype 0 float, 1 bf16, 2 fp16
+// (16-bit outputs are rounded once, after the fp32 sum).
 hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride,
-                                int64_t rows, int64_t cols, int64_t ld_out, float* out,
-                                bool accumulate, hipStream_t s);
+                                int64_t rows, int64_t cols, int64_t ld_out, void* out,
+                                int out_dtype, bool accumulate, hipStream_t s);
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// Zeros n elements of out_dtype (0 float, 1 bf16, 2 fp16).
+hipError_t launch_zero(void* p, int64_t n, int out_dtype, hipStream_t s);
 
 }  // namespace lce

@@ -395,15 +395,22 @@ __device__ __forceinline__ void epilogue_16(const f32x16_t (&acc)[4][kFJ], const
   }
 }
 
-template <int kEpi, int kFJ>
+template <int kEpi, int kTy, int kFJ>
 __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], const GemmDesc& d,
                                              int64_t m0, int64_t n0, int sp, int row0, int col0,
                                              char* reg) {
   static_assert(kFJ == 2, "64 output columns per wave");
+  // fp32 accumulators out as float, or rounded to the 16-bit input type
+  // (kTy 0 bf16, 1 fp16); accumulating variants add the old value first.
+  constexpr bool k16 = kEpi == kEpiStore16 || kEpi == kEpiAccum16;
+  constexpr bool kAcc = kEpi == kEpiAccumF32 || kEpi == kEpiAccum16;
+  constexpr int kEb = k16 ? 2 : 4;  // output element bytes
   const int lane = threadIdx.x & 63, l32 = lane & 31, lhi = lane >> 5;
-  float* C = static_cast<float*>(d.C) + static_cast<int64_t>(sp) * d.split_stride;
+  char* C = static_cast<char*>(d.C) + (static_cast<int64_t>(sp) * d.split_stride) * kEb;
   // Deferred gradient scaling (exact power of two, then the device scale).
   const float f = __builtin_ldexpf(d.out_scale != nullptr ? *d.out_scale : 1.0f, -d.out_shift);
+  auto to_f32 = [](uint16_t h) { return kTy == 1 ? f16_to_f32(h) : bf16_to_f32(h); };
+  auto pack2 = [](float x, float y) { return kTy == 1 ? pack_f16x2(x, y) : pack_bf16x2(x, y); };
   // A quarter (32 rows) of the wave's result at a time.
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
@@ -412,14 +419,20 @@ __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], cons
     // (range-checked buffer loads read zeros outside the matrix), so their
     // latency overlaps the staging through LDS.
     float4 old[8];
-    if constexpr (kEpi == kEpiAccumF32) {
-      const rsrc_t rc = make_rsrc(C + mh * d.ldc + n0 + col0, 32 * d.ldc * 4);
+    if constexpr (kAcc) {
+      const rsrc_t rc = make_rsrc(C + (mh * d.ldc + n0 + col0) * kEb, 32 * d.ldc * kEb);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int r = u * 4 + (lane >> 4), sl = lane & 15;
         const bool ok = mh + r < d.M && n0 + col0 + sl * 4 + 3 < d.N;
-        const int voff = ok ? static_cast<int>(r * d.ldc * 4) + sl * 16 : kOOB;
-        old[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff, 0, 0));
+        const int voff = ok ? static_cast<int>(r * d.ldc * kEb) + sl * 4 * kEb : kOOB;
+        if constexpr (k16) {
+          const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, voff, 0, 0));
+          old[u] = make_float4(to_f32(static_cast<uint16_t>(w.x)), to_f32(static_cast<uint16_t>(w.x >> 16)),
+                               to_f32(static_cast<uint16_t>(w.y)), to_f32(static_cast<uint16_t>(w.y >> 16)));
+        } else {
+          old[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff, 0, 0));
+        }
       }
     }
 #pragma unroll
@@ -440,15 +453,27 @@ __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], cons
       const int64_t m = mh + r;
       const int64_t n = n0 + col0 + sl * 4;
       if (m >= d.M || n >= d.N) continue;
-      float* c = C + m * d.ldc + n;
+      char* c = C + (m * d.ldc + n) * kEb;
       if (n + 3 < d.N) {
-        if constexpr (kEpi == kEpiAccumF32) {
+        if constexpr (kAcc) {
           o.x += old[u].x; o.y += old[u].y; o.z += old[u].z; o.w += old[u].w;
         }
-        *reinterpret_cast<float4*>(c) = o;
+        if constexpr (k16)
+          *reinterpret_cast<uint2*>(c) = make_uint2(pack2(o.x, o.y), pack2(o.z, o.w));
+        else
+          *reinterpret_cast<float4*>(c) = o;
       } else {
         const float w[4] = {o.x, o.y, o.z, o.w};
-        for (int e = 0; e < 4 && n + e < d.N; ++e) c[e] = (kEpi == kEpiAccumF32) ? c[e] + w[e] : w[e];
+        for (int e = 0; e < 4 && n + e < d.N; ++e) {
+          if constexpr (k16) {
+            uint16_t* c16 = reinterpret_cast<uint16_t*>(c) + e;
+            const float v = kAcc ? to_f32(*c16) + w[e] : w[e];
+            *c16 = static_cast<uint16_t>(pack2(v, 0.0f) & 0xFFFFu);
+          } else {
+            float* c32 = reinterpret_cast<float*>(c) + e;
+            *c32 = kAcc ? *c32 + w[e] : w[e];
+          }
+        }
       }
     }
     wave_lds_fence();
@@ -525,7 +550,7 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
   // Every wave is done with the stage buffers; they now stage the output.
   block_sync();
   if constexpr (kEpi == kEpiLogits) epilogue_16<kTy, kFJ>(acc, d, m0, n0, row0, col0, epi_region<8192>(wave));
-  else epilogue_f32<kEpi, kFJ>(acc, d, m0, n0, sp, row0, col0, epi_region<8192>(wave));
+  else epilogue_f32<kEpi, kTy, kFJ>(acc, d, m0, n0, sp, row0, col0, epi_region<8192>(wave));
 }
 
 
@@ -779,7 +804,7 @@ void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
   block_sync();
   char* reg = reinterpret_cast<char*>(wave < 4 ? g_slot0 : g_slot1) + (wave & 3) * 8192;
   if constexpr (kEpi == kEpiLogits) epilogue_16<kTy, 2>(acc, d, m0, n0, row0, col0, reg);
-  else epilogue_f32<kEpi, 2>(acc, d, m0, n0, sp, row0, col0, reg);
+  else epilogue_f32<kEpi, kTy, 2>(acc, d, m0, n0, sp, row0, col0, reg);
 }
 
 }  // namespace ring
@@ -843,6 +868,12 @@ static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
     return launch_mfma_kernel<true, false, kEpiStoreF32, 4, kTy>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
     return launch_mfma_kernel<true, false, kEpiAccumF32, 4, kTy>(d, s);
+  if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStore16)
+    return launch_mfma_kernel<true, false, kEpiStore16, 4, kTy>(d, s);
+  if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStore16)
+    return launch_ring<false, false, kEpiStore16, kTy>(d, s);
+  if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)
+    return launch_ring<false, false, kEpiAccum16, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
     return launch_ring<false, false, kEpiStoreF32, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)

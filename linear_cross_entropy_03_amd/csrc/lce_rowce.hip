@@ -1058,9 +1058,9 @@ hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader*
 // out[v] (+)= f * sum over rows of Z[r, v], f = 2^-out_shift (* *out_scale);
 // each lane owns two adjacent columns and walks the rows in order
 // (deterministic).
-template <typename T>
+template <typename T, typename TO>
 __global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ Z, int64_t ldz, int64_t rows,
-                                                int64_t V, float* __restrict__ out, int accumulate,
+                                                int64_t V, TO* __restrict__ out, int accumulate,
                                                 const float* __restrict__ out_scale, int out_shift) {
   const int64_t v = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 2;
   if (v >= V) return;
@@ -1085,48 +1085,75 @@ __global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ Z, int64_t
   const float f = __builtin_ldexpf(out_scale != nullptr ? *out_scale : 1.0f, -out_shift);
   a0 *= f;
   a1 *= f;
-  if (accumulate) { a0 += out[v]; if (two) a1 += out[v + 1]; }
-  out[v] = a0;
-  if (two) out[v + 1] = a1;
+  if (accumulate) {
+    a0 += Elem<TO>::load(out + v);
+    if (two) a1 += Elem<TO>::load(out + v + 1);
+  }
+  Elem<TO>::store(out + v, a0);
+  if (two) Elem<TO>::store(out + v + 1, a1);
 }
 
-hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V, float* out,
-                         bool accumulate, const float* out_scale, int out_shift, hipStream_t s) {
+template <typename T>
+static hipError_t colsum_to(const void* Z, int64_t ldz, int64_t rows, int64_t V, void* out,
+                            int out_dtype, bool accumulate, const float* out_scale, int out_shift,
+                            hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((V + 511) / 512));
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_colsum<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(Z),
-                       ldz, rows, V, out, accumulate ? 1 : 0, out_scale, out_shift);
-  else if (dtype == 2)
-    hipLaunchKernelGGL(k_colsum<Half>, grid, dim3(256), 0, s, static_cast<const Half*>(Z), ldz, rows,
-                       V, out, accumulate ? 1 : 0, out_scale, out_shift);
+  const T* z = static_cast<const T*>(Z);
+  const int acc = accumulate ? 1 : 0;
+  if (out_dtype == 1)
+    hipLaunchKernelGGL((k_colsum<T, uint16_t>), grid, dim3(256), 0, s, z, ldz, rows, V,
+                       static_cast<uint16_t*>(out), acc, out_scale, out_shift);
+  else if (out_dtype == 2)
+    hipLaunchKernelGGL((k_colsum<T, Half>), grid, dim3(256), 0, s, z, ldz, rows, V,
+                       static_cast<Half*>(out), acc, out_scale, out_shift);
   else
-    hipLaunchKernelGGL(k_colsum<float>, grid, dim3(256), 0, s, static_cast<const float*>(Z), ldz,
-                       rows, V, out, accumulate ? 1 : 0, out_scale, out_shift);
+    hipLaunchKernelGGL((k_colsum<T, float>), grid, dim3(256), 0, s, z, ldz, rows, V,
+                       static_cast<float*>(out), acc, out_scale, out_shift);
   return hipGetLastError();
+}
+
+hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V, void* out,
+                         int out_dtype, bool accumulate, const float* out_scale, int out_shift,
+                         hipStream_t s) {
+  if (dtype == 1)
+    return colsum_to<uint16_t>(Z, ldz, rows, V, out, out_dtype, accumulate, out_scale, out_shift, s);
+  if (dtype == 2)
+    return colsum_to<Half>(Z, ldz, rows, V, out, out_dtype, accumulate, out_scale, out_shift, s);
+  return colsum_to<float>(Z, ldz, rows, V, out, out_dtype, accumulate, out_scale, out_shift, s);
 }
 
 // -------------------------------------------------------- split-K reduce
 
 // out (+)= sum of the K-split partials, splits in index order.
+template <typename TO>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ parts, int splits,
                                                        int64_t stride, int64_t rows, int64_t cols,
-                                                       int64_t ld_out, float* __restrict__ out,
+                                                       int64_t ld_out, TO* __restrict__ out,
                                                        int accumulate) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= rows * cols) return;
   const int64_t r = i / cols, c = i - r * cols;
   float acc = parts[r * cols + c];
   for (int sp = 1; sp < splits; ++sp) acc += parts[sp * stride + r * cols + c];
-  if (accumulate) acc += out[r * ld_out + c];
-  out[r * ld_out + c] = acc;
+  if (accumulate) acc += Elem<TO>::load(out + r * ld_out + c);
+  Elem<TO>::store(out + r * ld_out + c, acc);
 }
 
 hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride, int64_t rows,
-                                int64_t cols, int64_t ld_out, float* out, bool accumulate,
-                                hipStream_t s) {
+                                int64_t cols, int64_t ld_out, void* out, int out_dtype,
+                                bool accumulate, hipStream_t s) {
   const int64_t n = rows * cols;
-  hipLaunchKernelGGL(k_splitk_reduce, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
-                     parts, splits, split_stride, rows, cols, ld_out, out, accumulate ? 1 : 0);
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  const int acc = accumulate ? 1 : 0;
+  if (out_dtype == 1)
+    hipLaunchKernelGGL(k_splitk_reduce<uint16_t>, grid, dim3(256), 0, s, parts, splits, split_stride,
+                       rows, cols, ld_out, static_cast<uint16_t*>(out), acc);
+  else if (out_dtype == 2)
+    hipLaunchKernelGGL(k_splitk_reduce<Half>, grid, dim3(256), 0, s, parts, splits, split_stride,
+                       rows, cols, ld_out, static_cast<Half*>(out), acc);
+  else
+    hipLaunchKernelGGL(k_splitk_reduce<float>, grid, dim3(256), 0, s, parts, splits, split_stride,
+                       rows, cols, ld_out, static_cast<float*>(out), acc);
   return hipGetLastError();
 }
 
@@ -1136,6 +1163,22 @@ __global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ p, int64_t
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * 256)
     p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_zero16(uint16_t* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0;
+}
+
+hipError_t launch_zero(void* p, int64_t n, int out_dtype, hipStream_t s) {
+  if (out_dtype == 0) return launch_fill_f32(static_cast<float*>(p), n, 0.0f, s);
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_zero16, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<uint16_t*>(p), n);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {

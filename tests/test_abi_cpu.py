@@ -84,6 +84,22 @@ def test_flce_argument_errors(B):
     assert _fb(B, wsb=64) == B.E_WORKSPACE
 
 
+def test_flce_ex_gradient_type_errors(B):
+    """The 16-bit-gradient entry point accepts FLCE_F32 or the input's own
+    16-bit type only; everything here fails before any launch."""
+    L = B.lib()
+
+    def ex(dtype, gdt, wsb=1 << 30):
+        return L.flce_forward_backward_ex(16, 16, None, 16, 4, 8, 10, dtype, -100, 2, gdt, 16, 16, 16,
+                                          None, 16, wsb, 0, None)
+    assert ex(B.BF16, 7) == B.E_INVALID_ARG
+    assert ex(B.BF16, B.F16) == B.E_INVALID_ARG
+    assert ex(B.F16, B.BF16) == B.E_INVALID_ARG
+    assert ex(B.F32, B.BF16) == B.E_INVALID_ARG
+    assert ex(B.BF16, B.BF16, wsb=64) == B.E_WORKSPACE
+    assert ex(B.F16, B.F32, wsb=64) == B.E_WORKSPACE
+
+
 def test_ce_and_shard_argument_errors(B):
     L = B.lib()
     assert L.ce_forward_backward(16, 16, 16, 4, 10, B.BF16, -100, 9, 16, 16, 1 << 20, None) == B.E_INVALID_ARG

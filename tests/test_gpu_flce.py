@@ -93,6 +93,36 @@ def test_f16_ragged_tiles_and_chunks(B, reduction):
     check_against_oracle(inp, reduction, run_flce(B, inp, reduction, chunk_rows=256))
 
 
+@pytest.mark.parametrize("dtype,N,H,V,chunk", [
+    ("bf16", 1000, 136, 4099, 256),      # 4 chunks: grad_W / grad_bias rounded at each add
+    ("f16", 600, 136, 1000, 0),
+    ("bf16", 512, 2048, 16384, 0)])      # split-K grad_X reduced in fp32, rounded once
+def test_gradients_in_the_input_type(B, dtype, N, H, V, chunk):
+    """flce_forward_backward_ex with 16-bit gradient outputs, against the
+    oracle at the 16-bit bar, and against the float32-gradient call: each
+    16-bit gradient is within a few roundings of the float32 one."""
+    import torch
+    inp = synth.make_flce_inputs(N, H, V, dtype, bias_std=0.1, ignore_frac=0.1, seed=N + V)
+    X, W = to_dev(inp["X"], dtype), to_dev(inp["W"], dtype)
+    b, y = to_dev(inp["bias"], dtype), to_dev(inp["targets"], "i32")
+    say("flce 16-bit gradients", dtype, N, H, V, chunk)
+    l16, gX16, gW16, gb16 = B.flce_forward_backward(X, W, y, bias=b, chunk_rows=chunk, grad_dtype="input")
+    l32, gX32, gW32, gb32 = B.flce_forward_backward(X, W, y, bias=b, chunk_rows=chunk)
+    torch.cuda.synchronize()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    assert gX16.dtype == tdt and gW16.dtype == tdt and gb16.dtype == tdt
+    assert float(l16[0]) == float(l32[0])
+    got = (to_host(l16), gX16.float().cpu().numpy(), gW16.float().cpu().numpy(),
+           gb16.float().cpu().numpy())
+    check_against_oracle(inp, "mean", got)
+    chunks = -(-N // (chunk or B.flce_plan(N, H, V, B.BF16 if dtype == "bf16" else B.F16)[0]))
+    ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    for g16, g32, name in ((gX16, gX32, "grad_X"), (gW16, gW32, "grad_W"), (gb16, gb32, "grad_bias")):
+        a, r = g16.double().cpu().numpy(), g32.double().cpu().numpy()
+        rounds = 1 if name == "grad_X" else chunks
+        assert np.abs(a - r).max() <= rounds * ulp * np.abs(r).max() + 1e-30, name
+
+
 def test_bf16_multi_chunk_mid(B):
     """N 1024 in 4 chunks, H 512, V 4099: the grad_W read-modify-write path."""
     inp = synth.make_flce_inputs(1024, 512, 4099, "bf16", ignore_frac=0.1, seed=12)
