@@ -29,6 +29,22 @@ def test_exports_every_declared_function(B):
         assert n in B._SIGNATURES, f"binding lacks {n}"
 
 
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++17")])
+def test_header_compiles_standalone(tmp_path, lang, std):
+    """include/flce.h needs nothing but the standard headers it includes."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / ("use.c" if lang == "c" else "use.cpp")
+    src.write_text('#include "flce.h"\nint use(void) { return FLCE_OK; }\n')
+    r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+
+
 def test_status_strings(B):
     for code in range(6):
         assert B.status_text(code)
