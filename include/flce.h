@@ -167,6 +167,20 @@ int flce_multihead_forward_backward(const void* X, const void* W, const void* bi
                                     void* workspace, size_t workspace_bytes, int64_t chunk_rows,
                                     void* stream);
 
+/*
+ * As flce_multihead_forward_backward, with the gradients in the input's
+ * 16-bit type when grad_dtype equals dtype (rounding as in
+ * flce_forward_backward_ex; grad_X is summed over the heads in that type,
+ * rounded once per head). FLCE_E_INVALID_ARG for any other grad_dtype than
+ * FLCE_F32 or dtype.
+ */
+int flce_multihead_forward_backward_ex(const void* X, const void* W, const void* bias,
+                                       const int32_t* targets, int64_t N, int64_t H, int64_t V,
+                                       int64_t K, int dtype, int32_t ignore_index, int reduction,
+                                       int grad_dtype, float* loss, void* grad_X, void* grad_W,
+                                       void* grad_bias, void* workspace, size_t workspace_bytes,
+                                       int64_t chunk_rows, void* stream);
+
 /* Bytes of workspace ce_forward_backward / ce_shard_stats /
  * ce_combine_shard_stats (V = V_global) need. */
 size_t ce_workspace_bytes(int64_t N, int64_t V);

@@ -57,6 +57,9 @@ _SIGNATURES = {
     "flce_multihead_forward_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
                                                _i32, _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64,
                                                _vp]),
+    "flce_multihead_forward_backward_ex": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                  _int, _i32, _int, _int, _vp, _vp, _vp, _vp, _vp,
+                                                  _sz, _i64, _vp]),
     "flce_check_device_error": (_int, [_vp, _vp]),
     "flce_timing_enable": (_int, [_int]),
     "flce_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
@@ -221,32 +224,40 @@ def flce_multihead_workspace_bytes(N, H, V, K, dtype=BF16, chunk_rows=0):
 
 def flce_multihead_forward_backward(X, W, targets, bias=None, ignore_index=-100, reduction="mean",
                                     grad_X=True, grad_W=True, grad_bias=None, loss=None,
-                                    workspace=None, chunk_rows=0, stream=None):
+                                    workspace=None, chunk_rows=0, stream=None, grad_dtype="f32"):
     """K heads over shared X [N, H]: W [K, V, H], targets [K, N] (int32),
     bias [K, V] or None. Returns (loss [K] or [K, N], grad_X (sum over heads),
-    grad_W [K, V, H], grad_bias [K, V])."""
+    grad_W [K, V, H], grad_bias [K, V]); grad_dtype as in flce_forward_backward."""
     N, H = X.shape
     K, V, _ = W.shape
     dev = X.device
     dt = _dtype_code(X)
+    if grad_dtype not in ("f32", "input"):
+        raise ValueError("grad_dtype must be 'f32' or 'input'")
+    g16 = grad_dtype == "input"
+    gtorch = X.dtype if g16 else torch.float32
     if grad_bias is None:
         grad_bias = bias is not None
-    gX = _grad_arg(grad_X, (N, H), dev)
-    gW = _grad_arg(grad_W, (K, V, H), dev)
-    gb = _grad_arg(grad_bias, (K, V), dev)
+    gX = _grad_arg(grad_X, (N, H), dev, gtorch)
+    gW = _grad_arg(grad_W, (K, V, H), dev, gtorch)
+    gb = _grad_arg(grad_bias, (K, V), dev, gtorch)
     if loss is None:
         loss = _empty((K, N) if reduction == "none" else (K,), torch.float32, dev)
     if workspace is None:
         workspace = _empty((max(1, flce_multihead_workspace_bytes(N, H, V, K, dt, chunk_rows)),),
                            torch.uint8, dev)
-    st = lib().flce_multihead_forward_backward(
-        _ptr(X, "X"), _ptr(W, "W", X.dtype), _ptr(bias, "bias", X.dtype),
-        _ptr(targets, "targets", torch.int32), N, H, V, K, dt, ignore_index, _red(reduction),
-        _ptr(loss, "loss", torch.float32), _ptr(gX, "grad_X", torch.float32),
-        _ptr(gW, "grad_W", torch.float32), _ptr(gb, "grad_bias", torch.float32),
-        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
-        _stream(stream))
-    _check(st, "flce_multihead_forward_backward")
+    args = [_ptr(X, "X"), _ptr(W, "W", X.dtype), _ptr(bias, "bias", X.dtype),
+            _ptr(targets, "targets", torch.int32), N, H, V, K, dt, ignore_index, _red(reduction)]
+    rest = [_ptr(loss, "loss", torch.float32), _ptr(gX, "grad_X", gtorch),
+            _ptr(gW, "grad_W", gtorch), _ptr(gb, "grad_bias", gtorch),
+            _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
+            _stream(stream)]
+    if g16:
+        st = lib().flce_multihead_forward_backward_ex(*args, dt, *rest)
+        _check(st, "flce_multihead_forward_backward_ex")
+    else:
+        st = lib().flce_multihead_forward_backward(*args, *rest)
+        _check(st, "flce_multihead_forward_backward")
     return loss, gX, gW, gb
 
 

@@ -416,16 +416,20 @@ size_t flce_multihead_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t K
   return p.total + static_cast<size_t>(K) * head_slot_bytes(N);
 }
 
-int flce_multihead_forward_backward(const void* X, const void* W, const void* bias,
-                                    const int32_t* targets, int64_t N, int64_t H, int64_t V,
-                                    int64_t K, int dtype, int32_t ignore_index, int reduction,
-                                    float* loss, float* grad_X, float* grad_W, float* grad_bias,
-                                    void* workspace, size_t workspace_bytes, int64_t chunk_rows,
-                                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+int flce_multihead_impl(const void* X, const void* W, const void* bias, const int32_t* targets,
+                        int64_t N, int64_t H, int64_t V, int64_t K, int dtype, int32_t ignore_index,
+                        int reduction, int grad_dtype, float* loss, void* grad_X, void* grad_W,
+                        void* grad_bias, void* workspace, size_t workspace_bytes,
+                        int64_t chunk_rows, void* stream) {
   if (K <= 0 || K >= kMaxDim) return FLCE_E_INVALID_ARG;
   int st = validate_flce(X, W, bias, targets, N, H, V, dtype, reduction, loss, grad_X, grad_W,
                          grad_bias, chunk_rows, workspace);
   if (st != FLCE_OK) return st;
+  if (grad_dtype != FLCE_F32 && grad_dtype != dtype) return FLCE_E_INVALID_ARG;
   Plan p;
   if (!make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
   const size_t slot = head_slot_bytes(N);
@@ -435,6 +439,7 @@ int flce_multihead_forward_backward(const void* X, const void* W, const void* bi
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const size_t e = elem_bytes(dtype);
+  const size_t ge = grad_dtype == FLCE_F32 ? 4 : 2;
   // The call's own header (first slot of the plan) collects nothing; each
   // head counts its targets into its own slot so N_valid is per head.
   for (int64_t k = 0; k < K; ++k) {
@@ -446,17 +451,17 @@ int flce_multihead_forward_backward(const void* X, const void* W, const void* bi
     const int32_t* tk = targets + static_cast<size_t>(k) * N;
     const char* Wk = static_cast<const char*>(W) + static_cast<size_t>(k) * V * H * e;
     const char* bk = bias ? static_cast<const char*>(bias) + static_cast<size_t>(k) * V * e : nullptr;
-    float* gWk = grad_W ? grad_W + static_cast<size_t>(k) * V * H : nullptr;
-    float* gbk = grad_bias ? grad_bias + static_cast<size_t>(k) * V : nullptr;
+    void* gWk = grad_W ? static_cast<char*>(grad_W) + static_cast<size_t>(k) * V * H * ge : nullptr;
+    void* gbk = grad_bias ? static_cast<char*>(grad_bias) + static_cast<size_t>(k) * V * ge : nullptr;
     LCE_TRY(timed(kKindOther, s, [&] {
       return launch_count_targets(tk, N, V, ignore_index, reduction, hdr, s);
     }));
     if (N == 0) {
-      if (gWk) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(gWk, V * H, 0.0f, s); }));
-      if (gbk) LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(gbk, V, 0.0f, s); }));
+      if (gWk) LCE_TRY(timed(kKindOther, s, [&] { return launch_zero(gWk, V * H, grad_dtype, s); }));
+      if (gbk) LCE_TRY(timed(kKindOther, s, [&] { return launch_zero(gbk, V, grad_dtype, s); }));
     }
     st = flce_chunks(p, dtype, X, Wk, bk, tk, N, H, V, ignore_index, hdr, loss_rows, grad_X, k > 0,
-                     gWk, gbk, FLCE_F32, ws, s);
+                     gWk, gbk, grad_dtype, ws, s);
     if (st != FLCE_OK) return st;
     if (reduction != FLCE_REDUCTION_NONE)
       LCE_TRY(timed(kKindOther, s, [&] {
@@ -464,6 +469,32 @@ int flce_multihead_forward_backward(const void* X, const void* W, const void* bi
       }));
   }
   return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flce_multihead_forward_backward(const void* X, const void* W, const void* bias,
+                                    const int32_t* targets, int64_t N, int64_t H, int64_t V,
+                                    int64_t K, int dtype, int32_t ignore_index, int reduction,
+                                    float* loss, float* grad_X, float* grad_W, float* grad_bias,
+                                    void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                                    void* stream) {
+  return flce_multihead_impl(X, W, bias, targets, N, H, V, K, dtype, ignore_index, reduction,
+                             FLCE_F32, loss, grad_X, grad_W, grad_bias, workspace, workspace_bytes,
+                             chunk_rows, stream);
+}
+
+int flce_multihead_forward_backward_ex(const void* X, const void* W, const void* bias,
+                                       const int32_t* targets, int64_t N, int64_t H, int64_t V,
+                                       int64_t K, int dtype, int32_t ignore_index, int reduction,
+                                       int grad_dtype, float* loss, void* grad_X, void* grad_W,
+                                       void* grad_bias, void* workspace, size_t workspace_bytes,
+                                       int64_t chunk_rows, void* stream) {
+  return flce_multihead_impl(X, W, bias, targets, N, H, V, K, dtype, ignore_index, reduction,
+                             grad_dtype, loss, grad_X, grad_W, grad_bias, workspace,
+                             workspace_bytes, chunk_rows, stream);
 }
 
 int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* targets, int64_t N,

@@ -870,6 +870,8 @@ static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
     return launch_mfma_kernel<true, false, kEpiAccumF32, 4, kTy>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStore16)
     return launch_mfma_kernel<true, false, kEpiStore16, 4, kTy>(d, s);
+  if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)
+    return launch_mfma_kernel<true, false, kEpiAccum16, 4, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStore16)
     return launch_ring<false, false, kEpiStore16, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)

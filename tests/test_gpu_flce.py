@@ -123,6 +123,31 @@ def test_gradients_in_the_input_type(B, dtype, N, H, V, chunk):
         assert np.abs(a - r).max() <= rounds * ulp * np.abs(r).max() + 1e-30, name
 
 
+def test_multihead_gradients_in_the_input_type(B):
+    """Three bf16 heads with 16-bit gradients against the float32-gradient
+    call: grad_X is summed over the heads in bf16 (one rounding per head),
+    grad_W per head rounded once per chunk."""
+    import torch
+    K, N, H, V = 3, 700, 136, 1500
+    inp = synth.make_flce_inputs(N, H, K * V, "bf16", ignore_frac=0.1, seed=33)
+    X = to_dev(inp["X"], "bf16")
+    W = to_dev(inp["W"], "bf16").reshape(K, V, H).contiguous()
+    rng = np.random.default_rng(34)
+    yk = rng.integers(0, V, size=(K, N)).astype(np.int32)
+    yk[:, ::7] = -100
+    y = to_dev(yk, "i32")
+    say("multihead 16-bit gradients", K, N, H, V)
+    l16, gX16, gW16, _ = B.flce_multihead_forward_backward(X, W, y, chunk_rows=256, grad_dtype="input")
+    l32, gX32, gW32, _ = B.flce_multihead_forward_backward(X, W, y, chunk_rows=256)
+    torch.cuda.synchronize()
+    assert gX16.dtype == torch.bfloat16 and gW16.dtype == torch.bfloat16
+    assert torch.equal(l16, l32)
+    ulp = 2.0 ** -8
+    for g16, g32, rounds in ((gX16, gX32, K), (gW16, gW32, 3)):
+        a, r = g16.double().cpu().numpy(), g32.double().cpu().numpy()
+        assert np.abs(a - r).max() <= rounds * ulp * np.abs(r).max()
+
+
 def test_bf16_multi_chunk_mid(B):
     """N 1024 in 4 chunks, H 512, V 4099: the grad_W read-modify-write path."""
     inp = synth.make_flce_inputs(1024, 512, 4099, "bf16", ignore_frac=0.1, seed=12)
