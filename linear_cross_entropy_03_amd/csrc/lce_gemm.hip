@@ -598,14 +598,15 @@ __device__ __forceinline__ uint16_t* slot_buf() {
 // 0..15 map to distinct positions.
 __device__ __forceinline__ int rswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// One operand in the ring: this wave's 4 of the 32 direct loads of a step
-// (issued in parts, kFirst..kFirst+kCount-1) and the MFMA fragment reads.
-template <bool kKMajor>
+// One operand in the ring: this wave's kInstr of the 32 direct loads of a
+// step (kW waves share them; issued in parts, kFirst..kFirst+kCount-1) and
+// the MFMA fragment reads.
+template <bool kKMajor, int kW>
 struct ROp;
 
-template <>
-struct ROp<true> {
-  static constexpr int kInstr = kBM / 8 / 8;
+template <int kW>
+struct ROp<true, kW> {
+  static constexpr int kInstr = kBM / 8 / kW;
   static constexpr int kReads = 1;  // LDS reads per fragment
   rsrc_t rsrc;
   int voff0[kInstr], kc8[kInstr];
@@ -641,9 +642,9 @@ struct ROp<true> {
   }
 };
 
-template <>
-struct ROp<false> {
-  static constexpr int kInstr = kRK / 2 / 8;
+template <int kW>
+struct ROp<false, kW> {
+  static constexpr int kInstr = kRK / 2 / kW;
   static constexpr int kReads = 2;
   const uint16_t* P;
   int64_t ld, r0;
@@ -685,69 +686,75 @@ struct ROp<false> {
 };
 
 // One 16-wide k sub-step: issue() places kDma direct loads, the next
-// fragments are read, and the 8 MFMAs run on the current ones, interleaved
-// as in mma_step.
-template <int kTy, int kDma, bool kAK, bool kBKm, typename Issue>
-__device__ __forceinline__ void sub(f32x16_t (&acc)[4][2], const Frags<2>& f, Frags<2>& nf,
+// fragments are read, and the 4 x kFJ MFMAs run on the current ones,
+// interleaved as in mma_step.
+template <int kTy, int kDma, bool kAK, bool kBKm, int kW, int kFJ, typename Issue>
+__device__ __forceinline__ void sub(f32x16_t (&acc)[4][kFJ], const Frags<kFJ>& f, Frags<kFJ>& nf,
                                     const uint16_t* srcA, const uint16_t* srcB, int row0, int col0,
                                     int kk, Issue&& issue) {
   issue();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) nf.a[i] = ROp<kAK>::frag(srcA, row0 + i * 32, kk);
+  for (int i = 0; i < 4; ++i) nf.a[i] = ROp<kAK, kW>::frag(srcA, row0 + i * 32, kk);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) nf.b[j] = ROp<kBKm>::frag(srcB, col0 + j * 32, kk);
+  for (int j = 0; j < kFJ; ++j) nf.b[j] = ROp<kBKm, kW>::frag(srcB, col0 + j * 32, kk);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kFJ; ++j)
       if constexpr (kTy == 1)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, f.b[j]),
                                                            __builtin_bit_cast(f16x8_t, f.a[i]),
                                                            acc[i][j], 0, 0, 0);
       else
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-  constexpr int kReads = 4 * ROp<kAK>::kReads + 2 * ROp<kBKm>::kReads;
+  constexpr int kMfma = 4 * kFJ;
+  constexpr int kReads = 4 * ROp<kAK, kW>::kReads + kFJ * ROp<kBKm, kW>::kReads;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < kMfma; ++t) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (t < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     if constexpr (kDma > 0)
-      if (t % (8 / kDma) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (t % (kMfma / kDma) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
-  if constexpr (kReads > 8) __builtin_amdgcn_sched_group_barrier(0x100, kReads - 8, 0);
+  if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
 }
 
 // Step s (kS = s % 5) reads A_s from slot 2s % 5 and B_s from (2s + 1) % 5.
 // Its first two k16 sub-steps issue A_{s+2} into the slot B_{s-1} used; the
 // barrier before the last sub-step waits for A_{s+1}, B_{s+1} and frees this
 // step's slots, and the last sub-step issues B_{s+2} into the slot of A_s.
-template <int kTy, int kS, bool kAK, bool kBKm>
-__device__ __forceinline__ void step(f32x16_t (&acc)[4][2], Frags<2>& f0, Frags<2>& f1,
-                                     const ROp<kAK>& A, const ROp<kBKm>& B, int row0, int col0,
-                                     int64_t k2, int64_t kend) {
+template <int kTy, int kS, bool kAK, bool kBKm, int kW, int kFJ>
+__device__ __forceinline__ void step(f32x16_t (&acc)[4][kFJ], Frags<kFJ>& f0, Frags<kFJ>& f1,
+                                     const ROp<kAK, kW>& A, const ROp<kBKm, kW>& B, int row0,
+                                     int col0, int64_t k2, int64_t kend) {
   constexpr int sa = (2 * kS) % 5, sb = (2 * kS + 1) % 5, pb = (2 * kS + 4) % 5;
   constexpr int na = (2 * kS + 2) % 5, nb = (2 * kS + 3) % 5;
-  constexpr int kIA = ROp<kAK>::kInstr, kIB = ROp<kBKm>::kInstr;
-  static_assert(kIA == 4 && kIB == 4, "four loads per operand per wave");
+  constexpr int kI = ROp<kAK, kW>::kInstr, kH = kI / 2;
+  static_assert(kI == ROp<kBKm, kW>::kInstr, "equal load counts per operand");
   const uint16_t* a = slot_buf<sa>();
   const uint16_t* b = slot_buf<sb>();
-  sub<kTy, 2, kAK, kBKm>(acc, f0, f1, a, b, row0, col0, 1,
-                         [&] { A.template issue<0, 2>(slot_buf<pb>(), k2, kend); });
-  sub<kTy, 2, kAK, kBKm>(acc, f1, f0, a, b, row0, col0, 2,
-                         [&] { A.template issue<2, 2>(slot_buf<pb>(), k2, kend); });
-  sub<kTy, 0, kAK, kBKm>(acc, f0, f1, a, b, row0, col0, 3, [] {});
+  sub<kTy, kH, kAK, kBKm, kW>(acc, f0, f1, a, b, row0, col0, 1,
+                              [&] { A.template issue<0, kH>(slot_buf<pb>(), k2, kend); });
+  sub<kTy, kH, kAK, kBKm, kW>(acc, f1, f0, a, b, row0, col0, 2,
+                              [&] { A.template issue<kH, kH>(slot_buf<pb>(), k2, kend); });
+  sub<kTy, 0, kAK, kBKm, kW>(acc, f0, f1, a, b, row0, col0, 3, [] {});
   // Only A_{s+2} was issued after B_{s+1}; as in the four-stage loop the
   // count relies on there being no other vector memory instruction (no
   // spills, checked by the launcher).
-  wait_vmcnt<kIA>();
+  wait_vmcnt<kI>();
   block_sync();
-  sub<kTy, 4, kAK, kBKm>(acc, f1, f0, slot_buf<na>(), slot_buf<nb>(), row0, col0, 0,
-                         [&] { B.template issue<0, 4>(slot_buf<sa>(), k2, kend); });
+  sub<kTy, kI, kAK, kBKm, kW>(acc, f1, f0, slot_buf<na>(), slot_buf<nb>(), row0, col0, 0,
+                              [&] { B.template issue<0, kI>(slot_buf<sa>(), k2, kend); });
 }
 
-template <bool kAK, bool kBKm, int kEpi, int kTy>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// kW = 8: 2 x 4 waves of 128 x 64, two per SIMD (grad_W). kW = 4: 2 x 2 waves
+// of 128 x 128, one per SIMD with the 256 accumulators in AGPRs, a third
+// fewer LDS reads per MFMA (logits: +1.4 to +2.3% over 8 waves; grad_W: no
+// change).
+template <bool kAK, bool kBKm, int kEpi, int kTy, int kW>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4, kW / 4)))
 void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
+  constexpr int kFJ = 8 / (kW / 2);  // 32-column MFMA blocks per wave
   int64_t tm, tn;
   int sp;
   tiles::tile_of(blockIdx.x, tiles_m, tiles_n, d.k_splits, tm, tn, sp);
@@ -756,34 +763,35 @@ void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
   int64_t kend = kbeg + k_per_split;
   if (kend > d.K) kend = d.K;
   const int ksteps = kend > kbeg ? static_cast<int>((kend - kbeg + kRK - 1) / kRK) : 0;
-  ROp<kAK> A;
-  ROp<kBKm> B;
+  constexpr int kI = ROp<kAK, kW>::kInstr;
+  ROp<kAK, kW> A;
+  ROp<kBKm, kW> B;
   A.init(static_cast<const uint16_t*>(d.A), d.lda, d.M, m0);
   B.init(static_cast<const uint16_t*>(d.B), d.ldb, d.N, n0);
   const int wave = wave_id();
-  const int row0 = (wave / 4) * 128, col0 = (wave % 4) * 64;
-  f32x16_t acc[4][2];
+  const int row0 = (wave / (kW / 2)) * 128, col0 = (wave % (kW / 2)) * (kFJ * 32);
+  f32x16_t acc[4][kFJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kFJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   // Prologue: A_0, B_0, A_1, B_1 into slots 0..3; step 0 then issues A_2
   // into slot 4. Loads past the end of K read zeros, so every step issues
   // the same loads, and the final steps' look-ahead reads stay in bounds.
   if (ksteps > 0) {
-    A.template issue<0, 4>(slot_buf<0>(), kbeg, kend);
-    B.template issue<0, 4>(slot_buf<1>(), kbeg, kend);
-    A.template issue<0, 4>(slot_buf<2>(), kbeg + kRK, kend);
-    B.template issue<0, 4>(slot_buf<3>(), kbeg + kRK, kend);
-    wait_vmcnt<2 * 4>();
+    A.template issue<0, kI>(slot_buf<0>(), kbeg, kend);
+    B.template issue<0, kI>(slot_buf<1>(), kbeg, kend);
+    A.template issue<0, kI>(slot_buf<2>(), kbeg + kRK, kend);
+    B.template issue<0, kI>(slot_buf<3>(), kbeg + kRK, kend);
+    wait_vmcnt<2 * kI>();
     block_sync();
-    Frags<2> f0, f1;
+    Frags<kFJ> f0, f1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f0.a[i] = ROp<kAK>::frag(slot_buf<0>(), row0 + i * 32, 0);
+    for (int i = 0; i < 4; ++i) f0.a[i] = ROp<kAK, kW>::frag(slot_buf<0>(), row0 + i * 32, 0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) f0.b[j] = ROp<kBKm>::frag(slot_buf<1>(), col0 + j * 32, 0);
+    for (int j = 0; j < kFJ; ++j) f0.b[j] = ROp<kBKm, kW>::frag(slot_buf<1>(), col0 + j * 32, 0);
     int s = 0;
     for (; s + 5 <= ksteps; s += 5) {
       const int64_t k2 = kbeg + static_cast<int64_t>(s + 2) * kRK;
@@ -800,11 +808,18 @@ void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
     if (s + 3 < ksteps) step<kTy, 3>(acc, f0, f1, A, B, row0, col0, k2 + 3 * kRK, kend);
     wait_vmcnt<0>();
   }
-  // Every wave is done with the slots; slots 0 and 1 stage the output.
+  // Every wave is done with the slots; each wave stages its output through
+  // 8 KiB of slots 0 and 1, 64 columns at a time.
   block_sync();
   char* reg = reinterpret_cast<char*>(wave < 4 ? g_slot0 : g_slot1) + (wave & 3) * 8192;
-  if constexpr (kEpi == kEpiLogits) epilogue_16<kTy, 2>(acc, d, m0, n0, row0, col0, reg);
-  else epilogue_f32<kEpi, kTy, 2>(acc, d, m0, n0, sp, row0, col0, reg);
+#pragma unroll
+  for (int hj = 0; hj < kFJ / 2; ++hj) {
+    f32x16_t part[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { part[i][0] = acc[i][2 * hj]; part[i][1] = acc[i][2 * hj + 1]; }
+    if constexpr (kEpi == kEpiLogits) epilogue_16<kTy, 2>(part, d, m0, n0, row0, col0 + hj * 64, reg);
+    else epilogue_f32<kEpi, kTy, 2>(part, d, m0, n0, sp, row0, col0 + hj * 64, reg);
+  }
 }
 
 }  // namespace ring
@@ -836,14 +851,14 @@ static hipError_t launch_mfma_kernel(const GemmDesc& d, hipStream_t s) {
 }
 
 
-template <bool kAK, bool kBKm, int kEpi, int kTy>
+template <bool kAK, bool kBKm, int kEpi, int kTy, int kW>
 static hipError_t launch_ring(const GemmDesc& d, hipStream_t s) {
   using namespace mfma2;
   const int64_t tiles_m = (d.M + kBM - 1) / kBM, tiles_n = (d.N + kBM - 1) / kBM;
   const int splits = d.k_splits > 1 ? d.k_splits : 1;
   int64_t k_per = (d.K + splits - 1) / splits;
   k_per = (k_per + ring::kRK - 1) / ring::kRK * ring::kRK;
-  auto kern = ring::k_ring<kAK, kBKm, kEpi, kTy>;
+  auto kern = ring::k_ring<kAK, kBKm, kEpi, kTy, kW>;
   // As for the four-stage kernel: spill stores would break the explicit waits.
   static int spills = -1;
   if (spills < 0) {
@@ -855,15 +870,15 @@ static hipError_t launch_ring(const GemmDesc& d, hipStream_t s) {
   if (spills) return hipErrorInvalidDeviceFunction;
   GemmDesc dd = d;
   dd.k_splits = splits;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles_m * tiles_n * splits)), dim3(512), 0, s,
-                     dd, tiles_m, tiles_n, k_per);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles_m * tiles_n * splits)), dim3(64 * kW), 0,
+                     s, dd, tiles_m, tiles_n, k_per);
   return hipGetLastError();
 }
 
 template <int kTy>
 static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
   if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits)
-    return launch_ring<true, true, kEpiLogits, kTy>(d, s);
+    return launch_ring<true, true, kEpiLogits, kTy, 4>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
     return launch_mfma_kernel<true, false, kEpiStoreF32, 4, kTy>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
@@ -873,13 +888,13 @@ static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)
     return launch_mfma_kernel<true, false, kEpiAccum16, 4, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStore16)
-    return launch_ring<false, false, kEpiStore16, kTy>(d, s);
+    return launch_ring<false, false, kEpiStore16, kTy, 8>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)
-    return launch_ring<false, false, kEpiAccum16, kTy>(d, s);
+    return launch_ring<false, false, kEpiAccum16, kTy, 8>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
-    return launch_ring<false, false, kEpiStoreF32, kTy>(d, s);
+    return launch_ring<false, false, kEpiStoreF32, kTy, 8>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
-    return launch_ring<false, false, kEpiAccumF32, kTy>(d, s);
+    return launch_ring<false, false, kEpiAccumF32, kTy, 8>(d, s);
   return hipErrorInvalidValue;
 }
 
