@@ -46,6 +46,11 @@ def parse():
                     help="skip the 16-bit-gradient measurement")
     ap.add_argument("--no-distill", action="store_true", help="skip the distillation measurement")
     ap.add_argument("--no-dpo", action="store_true", help="skip the DPO measurement")
+    ap.add_argument("--no-packing", action="store_true",
+                    help="run the FLCE step with row packing off (every row through the "
+                         "products, ignored ones included)")
+    ap.add_argument("--no-unpacked", action="store_true",
+                    help="skip the comparison steps with row packing off")
     ap.add_argument("--no-eager", action="store_true",
                     help="skip the PyTorch eager context measurement")
     ap.add_argument("--profile-step", action="store_true",
@@ -479,6 +484,14 @@ def bench_dpo(torch, B, X, W, y, cfg, n_pairs=4, seq_len=1024, reps=3):
     return out
 
 
+def rows_through_products(B, y):
+    """Rows an FLCE call over targets y runs through its products: the
+    non-ignored ones when row packing is on, else all."""
+    packing = B.flce_set_row_packing(True)
+    B.flce_set_row_packing(packing)
+    return int((y != -100).sum().item()) if packing else int(y.numel())
+
+
 def bench_grad16(torch, B, X, W, y, cfg, reps=5):
     """The same FLCE step with the gradients written in the input's 16-bit type
     (flce_forward_backward_ex): grad_W accumulated chunk by chunk in bf16."""
@@ -502,10 +515,12 @@ def bench_grad16(torch, B, X, W, y, cfg, reps=5):
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
+    live = rows_through_products(B, y)
     out = {
         "workload": "llama8b_head_bf16 with bf16 grad_X and grad_W",
         "ms_per_step": ms, "tokens_per_s": N / (ms * 1e-3),
-        "frac_bf16_peak": 6.0 * N * H * V / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        "rows_through_products": live,
+        "frac_bf16_peak": 6.0 * live * H * V / (ms * 1e-3) / PEAK_BF16_FLOPS,
         "gradient_output_bytes": (N * H + V * H) * 2, "float32_gradient_output_bytes": (N * H + V * H) * 4,
         "loss": float(loss.item()),
     }
@@ -543,7 +558,8 @@ def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
-    flops = K * 6.0 * N * H * V
+    # Head 0 runs packed (when packing is on); the others take every row.
+    flops = (rows_through_products(B, yk[0]) + (K - 1) * N) * 6.0 * H * V
     out = {
         "workload": f"{K} heads over llama8b_head_bf16 hidden states (N {N}, H {H}, V {V}, "
                     f"{cfg['reduction']})",
@@ -587,6 +603,11 @@ def main():
     X, W, bias, y = gpu_inputs(torch, inp)
 
     chunk, splits = B.flce_plan(N, H, V, dt, args.chunk_rows)
+    packing = dt != B.F32 and not args.no_packing
+    B.flce_set_row_packing(packing)
+    # Rows that go through the products: with packing, those whose target is
+    # not ignored (the ignored ones add nothing to the loss or any gradient).
+    n_live = int(np.count_nonzero(inp["targets"] != -100)) if packing else N
     ws_bytes = B.flce_workspace_bytes(N, H, V, dt, args.chunk_rows)
     loss = torch.empty((1,), dtype=torch.float32, device="cuda")
     gX = torch.empty((N, H), dtype=torch.float32, device="cuda")
@@ -641,9 +662,10 @@ def main():
     per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     peak = torch.cuda.max_memory_allocated()
 
-    # Per-kernel roofline from the library's HIP events over the timed region.
+    # Per-kernel roofline from the library's HIP events over the timed region;
+    # the work is that of the rows the kernels process (n_live).
     e = 2 if cfg["dtype"] == "bf16" else 4
-    gemm_flops_per_step = 2.0 * N * H * V
+    gemm_flops_per_step = 2.0 * n_live * H * V
     kernels = {}
     for kind in ("logits_gemm", "grad_x_gemm", "grad_w_gemm", "row_ce", "other"):
         tot_ms, launches = B.flce_timing_read(kind)
@@ -656,7 +678,7 @@ def main():
                          achieved=per_launch / (tot_ms / launches * 1e-3) / 1e12,
                          peak=PEAK_BF16_FLOPS / 1e12)
         elif kind == "row_ce":
-            per_launch = 2.0 * N * V * e * args.steps / launches
+            per_launch = 2.0 * n_live * V * e * args.steps / launches
             entry.update(bound="hbm", unit="GB/s", algorithmic_per_launch=per_launch,
                          achieved=per_launch / (tot_ms / launches * 1e-3) / 1e9,
                          peak=PEAK_HBM_BYTES / 1e9)
@@ -680,9 +702,32 @@ def main():
                 "algorithmic_per_launch": dom["algorithmic_per_launch"]}
 
     tokens_per_s = N / (ms * 1e-3)
+    unpacked = None
+    if packing and not args.no_unpacked:
+        # The same step with every row through the products, for comparison.
+        B.flce_set_row_packing(False)
+        step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = 5
+        ev[0].record(stream)
+        for _ in range(reps):
+            step()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        B.flce_set_row_packing(True)
+        ums = ev[0].elapsed_time(ev[1]) / reps
+        unpacked = {"ms_per_step": ums, "tokens_per_s": N / (ums * 1e-3),
+                    "mfma_frac_step": 6.0 * N * H * V / (ums * 1e-3) / PEAK_BF16_FLOPS,
+                    "steps": reps}
+    # One chunk of logits, per-row / per-vocabulary scratch, the grad_X K-split
+    # partials (the last packed chunk splits in two) and, for 16-bit inputs,
+    # the packed-row lists and the chunk's gathered hidden states.
+    max_splits = max(splits, 2 if (e == 2 and splits == 1 and V // 2 >= 2048) else splits)
     extra_bound = (chunk * ((V + 7) // 8 * 8) * e + (N + V) * 16 + 4096
-                   + (splits * chunk * H * 4 if splits > 1 else 0))
-    step_flops = 6.0 * N * H * V
+                   + (max_splits * chunk * H * 4 if max_splits > 1 else 0)
+                   + ((chunk * H * e + 8 * N + 4096) if e == 2 else 0))
+    step_flops = 6.0 * n_live * H * V
     result = {
         "metric": "FLCE fwd+bwd tokens/s + % bf16 MFMA peak at H4096 V128256; peak HBM bytes",
         "value": tokens_per_s,
@@ -700,12 +745,18 @@ def main():
                 + ", 10% ignore_index)",
         "config": {"workload": args.workload, "N": N, "H": H, "V": V, "reduction": cfg["reduction"],
                    "bias": bias is not None, "chunk_rows": chunk, "dx_splits": splits,
-                   "parallelism": "single GPU"},
+                   "row_packing": packing, "parallelism": "single GPU"},
+        "rows_through_products": n_live,
         "step_ms_median": float(np.median(per_step)),
         "step_ms_min": float(np.min(per_step)),
         "first_call_ms": first_call_ms,
+        # Executed work: 6 * rows_through_products * H * V flops per step.
         "mfma_frac_step": step_flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
         "step_tflops": step_flops / (ms * 1e-3) / 1e12,
+        # 6 * N * H * V over the step time: counts the ignored rows' products,
+        # which packing does not run, so it is not a measure of MFMA use.
+        "nominal_6NHV_frac_step": 6.0 * N * H * V / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        "unpacked": unpacked,
         "peak_bytes": peak,
         "extra_bytes": peak - io_bytes,
         # bound: one chunk of logits + per-row / per-vocab scratch + split-K partials

@@ -44,7 +44,8 @@
  *   - Gradient outputs are overwritten, never accumulated into.
  *   - Every call is asynchronous: work is enqueued on `stream` (a hipStream_t;
  *     NULL = the default stream) and the call returns without waiting. The
- *     library keeps no state between calls, so concurrent calls on different
+ *     library keeps no data between calls (only the row-packing and timing
+ *     switches below), so concurrent calls on different
  *     streams are safe as long as their workspaces and outputs do not overlap.
  *   - Errors are returned as flce_status; host-detectable errors are returned
  *     before anything is enqueued. No exception crosses the ABI.
@@ -340,6 +341,26 @@ int flce_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ignor
  * workspace met an out-of-range target: FLCE_OK, FLCE_E_TARGET or FLCE_E_HIP.
  */
 int flce_check_device_error(const void* workspace, void* stream);
+
+/*
+ * Row packing in the FLCE calls with 16-bit inputs (flce_forward_backward,
+ * its _ex variant, and the first head of the multi-head calls). A row whose
+ * target is ignore_index has zero loss and a zero dlogits row (the definition
+ * at the top of this header), so it adds nothing to grad_W or grad_bias and
+ * its grad_X row is zero. The chunk loop therefore lists the other rows on
+ * the device and runs the logits, grad_X and grad_W products and the
+ * row kernel over those only; the results land in the original rows, and
+ * grad_X rows of ignored rows are zero. The host never reads the count back:
+ * every chunk is launched for the largest possible size and its kernels stop
+ * at the count, so the calls stay asynchronous. The last chunk, usually
+ * part-full, splits the K of its grad_X product in two. The loss is bitwise
+ * the same either way, and so are the grad_X rows outside the last chunk;
+ * the rest differ only in rounding order (the last chunk's split, and where
+ * the chunk boundaries fall in the grad_W and grad_bias sums). On by default; `enable` 0 turns it
+ * off (for comparisons). Returns the previous setting. Process-wide, not
+ * thread-safe; the workspace size does not depend on it.
+ */
+int flce_set_row_packing(int enable);
 
 /*
  * Kernel timing for measurement. While enabled, the library brackets each

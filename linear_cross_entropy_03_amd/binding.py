@@ -61,6 +61,7 @@ _SIGNATURES = {
                                                   _int, _i32, _int, _int, _vp, _vp, _vp, _vp, _vp,
                                                   _sz, _i64, _vp]),
     "flce_check_device_error": (_int, [_vp, _vp]),
+    "flce_set_row_packing": (_int, [_int]),
     "flce_timing_enable": (_int, [_int]),
     "flce_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "flce_timing_reset": (_int, []),
@@ -460,6 +461,11 @@ def flce_shift_labels(labels, ignore_index=-100, out=None, stream=None):
 def flce_check_device_error(workspace, stream=None):
     """Status of the last call that used `workspace` (waits for the stream)."""
     return int(lib().flce_check_device_error(_ptr(workspace, "workspace"), _stream(stream)))
+
+
+def flce_set_row_packing(enable=True):
+    """Turn row packing of ignored rows on or off; returns the previous setting."""
+    return bool(lib().flce_set_row_packing(1 if enable else 0))
 
 
 def flce_timing_enable(enable=True):

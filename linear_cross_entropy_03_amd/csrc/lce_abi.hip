@@ -83,9 +83,15 @@ struct Plan {
   int64_t chunk;    // rows per chunk
   int64_t ldz;      // row stride of the chunk buffer (elements)
   int dx_splits;    // K-splits of the grad_X GEMM
+  int last_splits;  // K-splits of the last chunk's grad_X GEMM when packed
   size_t off_rows;  // per-row losses [N] float
   size_t off_chunk; // chunk buffer [chunk, ldz]
   size_t off_split; // split-K partials [dx_splits, chunk, H] float (dx_splits > 1)
+  // Row packing (16-bit inputs): packed-row map [N], packed targets [N], the
+  // pack kernels' block counts, and the chunk's gathered hidden states
+  // [chunk, H]. pack_ok is false for float32 inputs (no buffers).
+  bool pack_ok;
+  size_t off_map, off_ptgt, off_bcnt, off_xs;
   size_t total;
 };
 
@@ -136,15 +142,33 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
   p->chunk = chunk;
   p->ldz = ldz;
   p->dx_splits = is16(dtype) ? choose_dx_splits(chunk, H, V) : 1;
+  // Packed, the last chunk usually holds fewer live rows than the others;
+  // its grad_X tiles (256 rows x 256 columns) then fill the CUs unevenly, and
+  // splitting K in two halves the granularity.
+  p->last_splits = (is16(dtype) && p->dx_splits == 1 && V / 2 >= 2048) ? 2 : p->dx_splits;
+  const int max_splits = std::max(p->dx_splits, p->last_splits);
   size_t off = align_up(sizeof(WsHeader));
   p->off_rows = off;
   off += align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float));
   p->off_chunk = off;
   off += align_up(static_cast<size_t>(chunk) * static_cast<size_t>(ldz) * e);
   p->off_split = off;
-  if (p->dx_splits > 1)
-    off += align_up(static_cast<size_t>(p->dx_splits) * static_cast<size_t>(chunk) *
+  if (max_splits > 1)
+    off += align_up(static_cast<size_t>(max_splits) * static_cast<size_t>(chunk) *
                     static_cast<size_t>(H) * sizeof(float));
+  p->pack_ok = is16(dtype);
+  p->off_map = p->off_ptgt = p->off_bcnt = p->off_xs = off;
+  if (p->pack_ok) {
+    const size_t n1 = static_cast<size_t>(std::max<int64_t>(N, 1));
+    p->off_map = off;
+    off += align_up(n1 * sizeof(int32_t));
+    p->off_ptgt = off;
+    off += align_up(n1 * sizeof(int32_t));
+    p->off_bcnt = off;
+    off += align_up(static_cast<size_t>(std::max<int64_t>(pack_block_count(N), 1)) * sizeof(int32_t));
+    p->off_xs = off;
+    off += align_up(static_cast<size_t>(chunk) * static_cast<size_t>(H) * e);
+  }
   p->total = off;
   return true;
 }
@@ -192,6 +216,9 @@ hipError_t timed(int kind, hipStream_t s, F&& launch) {
 
 enum Kind { kKindLogits = 0, kKindRowCE = 1, kKindGradX = 2, kKindGradW = 3, kKindOther = 4 };
 
+// Row packing switch (flce_set_row_packing); on by default.
+bool g_row_packing = true;
+
 #define LCE_TRY(expr)                          \
   do {                                         \
     if ((expr) != hipSuccess) return FLCE_E_HIP; \
@@ -228,6 +255,12 @@ int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, in
   return FLCE_OK;
 }
 
+int flce_set_row_packing(int enable) {
+  const int was = g_row_packing ? 1 : 0;
+  g_row_packing = enable != 0;
+  return was;
+}
+
 size_t ce_workspace_bytes(int64_t N, int64_t V) {
   if (N < 0 || V <= 0 || N >= kMaxRows || V >= kMaxDim) return 0;
   return ce_ws_bytes(N);
@@ -247,6 +280,16 @@ namespace {
 // (loss rows, dZ in place), bias column sums, grad_X (stored, or added to
 // what is there when accum_gx), grad_W (stored on the first chunk, added
 // after). Targets must have been counted into hdr.
+//
+// Row packing (16-bit inputs, grad_X stored): rows with an ignored or
+// invalid target contribute nothing, so they are listed out first and every
+// chunk covers the next `chunk` of the remaining rows. The host does not know
+// how many remain (the count lives on the device and is never read back), so
+// it launches every chunk for `chunk` rows and the kernels stop at the live
+// count: GEMM tiles past it exit, the grad_W product shortens its K loop. The
+// chunk's hidden states are gathered into the workspace for the logits and
+// grad_W products; loss and grad_X rows are written back to their original
+// rows, and grad_X rows of the dropped rows are zeroed.
 int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const void* bias,
                 const int32_t* targets, int64_t N, int64_t H, int64_t V, int32_t ignore_index,
                 WsHeader* hdr, float* loss_rows, void* grad_X, bool accum_gx, void* grad_W,
@@ -261,10 +304,39 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
   const bool need_grad = grad_X != nullptr || grad_W != nullptr || grad_bias != nullptr;
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
   const GradScaling gsc = grad_scaling(dtype, hdr);
+
+  const bool pack = g_row_packing && p.pack_ok && !accum_gx && N > 0;
+  int32_t* map = reinterpret_cast<int32_t*>(ws + p.off_map);
+  const int32_t* ptgt = reinterpret_cast<const int32_t*>(ws + p.off_ptgt);
+  char* xs = ws + p.off_xs;
+  if (pack) {
+    LCE_TRY(timed(kKindOther, s, [&] {
+      return launch_pack_rows(targets, N, V, ignore_index, map, const_cast<int32_t*>(ptgt),
+                              reinterpret_cast<int32_t*>(ws + p.off_bcnt), hdr, loss_rows, s);
+    }));
+    if (grad_X)
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_zero_dead_rows(targets, N, V, ignore_index, grad_X,
+                                     H * static_cast<int64_t>(ge), s);
+      }));
+  }
+
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
+    // Packed: chunk rows are packed rows r0.. (live up to hdr->n_packed).
+    const RowPack pk = pack ? RowPack{map + r0, &hdr->n_packed, r0} : RowPack{nullptr, nullptr, 0};
     const char* Xc = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+    if (pack) {
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_gather_rows(X, H * static_cast<int64_t>(e), rows, pk, xs, s);
+      }));
+      Xc = xs;
+    }
+    auto live = [&](GemmDesc& d, int dim) {
+      if (!pack) return;
+      d.live = pk.live; d.live_base = pk.base; d.live_dim = dim;
+    };
 
     GemmDesc g1{};
     g1.A = Xc; g1.lda = H; g1.a_kmajor = true;
@@ -272,19 +344,20 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
     g1.C = zbuf; g1.ldc = p.ldz; g1.bias = bias;
     g1.M = rows; g1.N = V; g1.K = H;
     g1.epilogue = kEpiLogits; g1.k_splits = 1;
+    live(g1, 0);
     LCE_TRY(timed(kKindLogits, s, [&] { return gemm(g1, s); }));
 
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_row_ce(dtype, zbuf, p.ldz, need_grad ? zbuf : nullptr, p.ldz, rows, V,
-                           p.ldz - V, targets + r0, ignore_index, hdr, loss_rows + r0, nullptr,
-                           gsc.row_shift, s);
+                           p.ldz - V, (pack ? ptgt : targets) + r0, ignore_index, hdr,
+                           pack ? loss_rows : loss_rows + r0, nullptr, gsc.row_shift, s, pk);
     }));
     if (!need_grad) continue;
 
     if (grad_bias)
       LCE_TRY(timed(kKindOther, s, [&] {
         return launch_colsum(dtype, zbuf, p.ldz, rows, V, grad_bias, grad_dtype, !first,
-                             gsc.out_scale, gsc.out_shift, s);
+                             gsc.out_scale, gsc.out_shift, s, pk);
       }));
 
     if (grad_X) {
@@ -293,19 +366,22 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
       g2.B = W; g2.ldb = H; g2.b_kmajor = false;
       g2.M = rows; g2.N = H; g2.K = V;
       scale_output(g2, gsc);
-      void* out = static_cast<char*>(grad_X) + static_cast<size_t>(r0) * H * ge;
-      if (p.dx_splits > 1) {
+      live(g2, 0);
+      void* out = static_cast<char*>(grad_X) + (pack ? 0 : static_cast<size_t>(r0) * H * ge);
+      const int splits = (pack && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
+      if (splits > 1) {
         g2.epilogue = kEpiStoreF32;
         g2.C = split_buf; g2.ldc = H;
-        g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
+        g2.k_splits = splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, grad_dtype,
-                                      accum_gx, s);
+          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype,
+                                      accum_gx, s, pk);
         }));
       } else {
         g2.epilogue = accum_gx ? (g16 ? kEpiAccum16 : kEpiAccumF32) : (g16 ? kEpiStore16 : kEpiStoreF32);
         g2.C = out; g2.ldc = H; g2.k_splits = 1;
+        if (pack) g2.row_map = pk.map;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
       }
     }
@@ -319,6 +395,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
       g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
       g3.k_splits = 1;
       scale_output(g3, gsc);
+      live(g3, 1);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }

@@ -22,7 +22,8 @@ struct WsHeader {
   int32_t n_bad;    // targets neither ignore_index nor inside [0, V)
   int32_t n_valid;  // rows that contribute to the loss
   float scale;      // gradient factor: 1/n_valid (mean, 0 if none), else 1
-  int32_t pad[61];
+  int32_t n_packed; // rows listed by the row-packing kernels (== n_valid)
+  int32_t pad[60];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte slot");
 
@@ -199,6 +200,24 @@ struct GemmDesc {
   // (when not null) before it is stored or added (deferred gradient scaling).
   const float* out_scale;
   int out_shift;
+  // Row packing: when `live` is not null the extent of M (live_dim 0) or of K
+  // (live_dim 1) is read on the device as clamp(*live - live_base, 0, M or K);
+  // tiles past it exit at once. When `row_map` is not null, output row m of a
+  // storing fp32/16-bit epilogue goes to row row_map[m] of C.
+  const int32_t* live;
+  int64_t live_base;
+  int live_dim;
+  const int32_t* row_map;
+};
+
+// The live rows of a chunk of packed rows: row r of the chunk exists when
+// r < *live - base, and its results belong to original row map[r] (map is
+// already offset to the chunk). A null `live` means every row exists and a
+// null `map` that row r is row r.
+struct RowPack {
+  const int32_t* map;
+  const int32_t* live;
+  int64_t base;
 };
 
 // fp16 dlogits in the chunk buffer: the row kernels store them times a power
@@ -225,10 +244,13 @@ hipError_t launch_count_targets(const int32_t* targets, int64_t n, int64_t V,
 // row_scale: per-row gradient factors, or nullptr for the reduction's scale.
 // grad_shift > 0: the gradient is stored times 2^grad_shift (times row_scale
 // when given) and without the reduction's scale, which the consumer applies.
+// pk: rows past pk.live are skipped and row r's loss goes to
+// loss_rows[pk.map[r]] (row packing).
 hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* grad, int64_t ldg,
                          int64_t rows, int64_t V, int64_t pad_cols, const int32_t* targets,
                          int32_t ign, const WsHeader* hdr, float* loss_rows,
-                         const float* row_scale, int grad_shift, hipStream_t s);
+                         const float* row_scale, int grad_shift, hipStream_t s,
+                         RowPack pk = RowPack{nullptr, nullptr, 0});
 
 // Row CE over a whole call of `rows` rows (contiguous, stride V) that also
 // counts the targets: fills hdr (n_bad, n_valid, scale) as launch_count_targets
@@ -270,15 +292,36 @@ hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader*
 
 // Column sums of Z times 2^-out_shift (and *out_scale when not null) into out
 // of out_dtype (0 float, 1 bf16, 2 fp16; accumulation rounds once per call).
+// pk.live limits the rows summed (row packing).
 hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V,
                          void* out, int out_dtype, bool accumulate, const float* out_scale,
-                         int out_shift, hipStream_t s);
+                         int out_shift, hipStream_t s, RowPack pk = RowPack{nullptr, nullptr, 0});
 
 // out (+)= the sum of the K-split partials; out_dtype 0 float, 1 bf16, 2 fp16
 // (16-bit outputs are rounded once, after the fp32 sum).
+// pk: only live rows are reduced, row r into out row pk.map[r].
 hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride,
                                 int64_t rows, int64_t cols, int64_t ld_out, void* out,
-                                int out_dtype, bool accumulate, hipStream_t s);
+                                int out_dtype, bool accumulate, hipStream_t s,
+                                RowPack pk = RowPack{nullptr, nullptr, 0});
+
+// Row packing. Rows whose target is ignore_index (or outside [0, V)) add
+// nothing to the loss or to any gradient, so the chunk loop can run over the
+// other rows only. launch_pack_rows lists them in ascending order: map[j] =
+// original row of packed row j, packed_targets[j] its target, hdr->n_packed
+// their count; loss_rows[r] = 0 for every other row r (when loss_rows is not
+// null). block_counts needs pack_block_count(n) ints.
+int64_t pack_block_count(int64_t n);
+hipError_t launch_pack_rows(const int32_t* targets, int64_t n, int64_t V, int32_t ign,
+                            int32_t* map, int32_t* packed_targets, int32_t* block_counts,
+                            WsHeader* hdr, float* loss_rows, hipStream_t s);
+// out[r, :] = src[pk.map[r], :] for the live rows r < rows of a chunk; rows
+// of row_bytes bytes (a multiple of 16, 16-byte aligned).
+hipError_t launch_gather_rows(const void* src, int64_t row_bytes, int64_t rows, RowPack pk,
+                              void* out, hipStream_t s);
+// Zeros the rows r of G ([n, row_bytes]) whose target is not packed.
+hipError_t launch_zero_dead_rows(const int32_t* targets, int64_t n, int64_t V, int32_t ign,
+                                 void* G, int64_t row_bytes, hipStream_t s);
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 // Zeros n elements of out_dtype (0 float, 1 bf16, 2 fp16).

@@ -49,6 +49,24 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
 
 }  // namespace tiles
 
+// Row packing: the extent of M or K that exists for this call, read on the
+// device (the host launches the grid for the largest possible chunk). A
+// shorter M also shortens the tile list: the live tiles are renumbered from
+// workgroup 0, so they are dealt over all eight XCDs as a full grid's are,
+// and the workgroups past them exit. Returns false for those.
+__device__ __forceinline__ bool apply_live(GemmDesc& d, int64_t& tiles_m, int64_t tiles_n, int bm) {
+  if (d.live == nullptr) return true;
+  int64_t n = static_cast<int64_t>(*d.live) - d.live_base;
+  if (n < 0) n = 0;
+  if (d.live_dim == 0) {
+    if (n < d.M) d.M = n;
+    tiles_m = (d.M + bm - 1) / bm;
+    return static_cast<int64_t>(blockIdx.x) < tiles_m * tiles_n * d.k_splits;
+  }
+  if (n < d.K) d.K = n;
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // The four-stage pipeline (grad_X): 32-wide k stages in 4 LDS buffers filled
 // by direct HBM->LDS loads.
@@ -453,7 +471,9 @@ __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], cons
       const int64_t m = mh + r;
       const int64_t n = n0 + col0 + sl * 4;
       if (m >= d.M || n >= d.N) continue;
-      char* c = C + (m * d.ldc + n) * kEb;
+      // Packed rows go back to their original row (storing epilogues only).
+      const int64_t mo = (!kAcc && d.row_map != nullptr) ? static_cast<int64_t>(d.row_map[m]) : m;
+      char* c = C + (mo * d.ldc + n) * kEb;
       if (n + 3 < d.N) {
         if constexpr (kAcc) {
           o.x += old[u].x; o.y += old[u].y; o.z += old[u].z; o.w += old[u].w;
@@ -486,7 +506,10 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
   constexpr int kWaves = kWM * kWN;
   constexpr int kFJ = kBM / kWN / 32;  // 32-column MFMA blocks per wave
   constexpr int kPer = Operand<kAK, kWaves>::kInstr + Operand<kBKm, kWaves>::kInstr;
+  constexpr bool kAcc = kEpi == kEpiAccumF32 || kEpi == kEpiAccum16;
 
+  // Whole workgroups leave here, before any barrier.
+  if (!apply_live(d, tiles_m, tiles_n, kBM)) return;
   int64_t tm, tn;
   int sp;
   tiles::tile_of(blockIdx.x, tiles_m, tiles_n, d.k_splits, tm, tn, sp);
@@ -495,6 +518,7 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
   int64_t kend = kbeg + k_per_split;
   if (kend > d.K) kend = d.K;
   const int ksteps = kend > kbeg ? static_cast<int>((kend - kbeg + kBK - 1) / kBK) : 0;
+  if (kAcc && ksteps == 0) return;  // adds nothing
 
   Operand<kAK, kWaves> opA;
   Operand<kBKm, kWaves> opB;
@@ -755,6 +779,9 @@ template <bool kAK, bool kBKm, int kEpi, int kTy, int kW>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4, kW / 4)))
 void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
   constexpr int kFJ = 8 / (kW / 2);  // 32-column MFMA blocks per wave
+  constexpr bool kAcc = kEpi == kEpiAccumF32 || kEpi == kEpiAccum16;
+  // Whole workgroups leave here, before any barrier.
+  if (!apply_live(d, tiles_m, tiles_n, kBM)) return;
   int64_t tm, tn;
   int sp;
   tiles::tile_of(blockIdx.x, tiles_m, tiles_n, d.k_splits, tm, tn, sp);
@@ -763,6 +790,7 @@ void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
   int64_t kend = kbeg + k_per_split;
   if (kend > d.K) kend = d.K;
   const int ksteps = kend > kbeg ? static_cast<int>((kend - kbeg + kRK - 1) / kRK) : 0;
+  if (kAcc && ksteps == 0) return;  // adds nothing
   constexpr int kI = ROp<kAK, kW>::kInstr;
   ROp<kAK, kW> A;
   ROp<kBKm, kW> B;
@@ -900,6 +928,11 @@ static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
 
 hipError_t launch_gemm_16(const GemmDesc& d, bool f16, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
+  // A row map redirects stored rows; an accumulating epilogue reads its old
+  // values as contiguous rows and takes none.
+  if (d.row_map != nullptr &&
+      (d.epilogue == kEpiLogits || d.epilogue == kEpiAccumF32 || d.epilogue == kEpiAccum16))
+    return hipErrorInvalidValue;
   return f16 ? launch_mfma_ty<1>(d, s) : launch_mfma_ty<0>(d, s);
 }
 
@@ -987,6 +1020,7 @@ static hipError_t launch_valu(const GemmDesc& d, hipStream_t s) {
 
 hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
+  if (d.live != nullptr || d.row_map != nullptr) return hipErrorInvalidValue;  // 16-bit path only
   if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits) return launch_valu<true, true, kEpiLogits>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32) return launch_valu<true, false, kEpiStoreF32>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32) return launch_valu<true, false, kEpiAccumF32>(d, s);

@@ -178,13 +178,15 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
                                                      int32_t ign, const WsHeader* __restrict__ hdr,
                                                      float* __restrict__ loss_rows,
                                                      const float* __restrict__ row_scale,
-                                                     int grad_shift, SelfCount sc) {
+                                                     int grad_shift, SelfCount sc, RowPack pk) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   __shared__ float red0[kThreads / 64], red1[kThreads / 64];
   __shared__ float cnt[2][kThreads / 64];  // self-count: per-wave target counts
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
+  // Packed chunks: rows past the live count do not exist (whole workgroup).
+  if (pk.live != nullptr && row >= static_cast<int64_t>(*pk.live) - pk.base) return;
   const T* z = Z + row * ldz;
   const int32_t y = targets[row];
   const bool valid = (y != ign) && y >= 0 && static_cast<int64_t>(y) < V;
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
   if (sc.n > 0) self_scale = count_finish<kThreads>(sc, cnt);
   if constexpr (kRes > 0) zt = E::load(&zt_bits);
-  if (tid == 0) loss_rows[row] = valid ? (lse - zt) : 0.0f;
+  if (tid == 0) loss_rows[pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row] = valid ? (lse - zt) : 0.0f;
   if (G == nullptr) return;
 
   // The gradient factor: the reduction's, or a per-row one (sequence-level
@@ -335,10 +337,15 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
                                                             const WsHeader* __restrict__ hdr,
                                                             float* __restrict__ loss_rows,
                                                             const float* __restrict__ row_scale,
-                                                            int grad_shift) {
+                                                            int grad_shift, RowPack pk) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   constexpr int kThreads = pf::kThreads;
+  // Packed chunks: only the live rows exist.
+  if (pk.live != nullptr) {
+    const int64_t live = static_cast<int64_t>(*pk.live) - pk.base;
+    if (live < rows) rows = live;
+  }
   constexpr int kSlices = kRes < pf::kMaxSlices ? kRes : pf::kMaxSlices;
   __shared__ float red0[kThreads / 64], red1[kThreads / 64];
   const int tid = threadIdx.x;
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
     float M, S;
     block_lse_parts<kThreads>(lm, ls, red0, red1, M, S);
     const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
-    if (tid == 0) loss_rows[row] = valid ? (lse - zt) : 0.0f;
+    if (tid == 0) loss_rows[pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row] = valid ? (lse - zt) : 0.0f;
 
     if (G != nullptr) {
       const float c = !valid ? 0.0f
@@ -472,7 +479,7 @@ template <typename T, int kThreads>
 static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                                   int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
                                   const WsHeader* hdr, float* loss_rows, const float* row_scale,
-                                  int grad_shift, SelfCount sc, hipStream_t s) {
+                                  int grad_shift, SelfCount sc, RowPack pk, hipStream_t s) {
   constexpr int kVec = Elem<T>::kVec;
   const int64_t nvec_max = (V + kVec - 1) / kVec;
   const T* z = static_cast<const T*>(Z);
@@ -480,13 +487,13 @@ static hipError_t row_ce_dispatch(const void* Z, int64_t ldz, void* G, int64_t l
   const dim3 grid(static_cast<unsigned>(rows)), block(kThreads);
 #define LCE_ROW_CE(R)                                                                           \
   hipLaunchKernelGGL((k_row_ce<T, kThreads, R>), grid, block, 0, s, z, ldz, g, ldg, V, pad_cols, \
-                     targets, ign, hdr, loss_rows, row_scale, grad_shift, sc)
+                     targets, ign, hdr, loss_rows, row_scale, grad_shift, sc, pk)
   // Long rows, more rows than CUs: the persistent prefetching variant.
   if constexpr (kThreads == pf::kThreads) {
     if (sc.n == 0 && takes_persistent(nvec_max, rows)) {
       hipLaunchKernelGGL((k_row_ce_pf<T, 16>), dim3(static_cast<unsigned>(cu_count())), block, 0, s,
                          z, ldz, g, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows, row_scale,
-                         grad_shift);
+                         grad_shift, pk);
       return hipGetLastError();
     }
   }
@@ -504,36 +511,36 @@ template <typename T>
 static hipError_t row_ce_by_width(const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                                   int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
                                   const WsHeader* hdr, float* loss_rows, const float* row_scale,
-                                  int grad_shift, SelfCount sc, hipStream_t s) {
+                                  int grad_shift, SelfCount sc, RowPack pk, hipStream_t s) {
   if (V >= 16384)
     return row_ce_dispatch<T, 1024>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                                    row_scale, grad_shift, sc, s);
+                                    row_scale, grad_shift, sc, pk, s);
   return row_ce_dispatch<T, 256>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                                 row_scale, grad_shift, sc, s);
+                                 row_scale, grad_shift, sc, pk, s);
 }
 
 static hipError_t row_ce_typed(int dtype, const void* Z, int64_t ldz, void* G, int64_t ldg,
                                int64_t rows, int64_t V, int64_t pad_cols, const int32_t* targets,
                                int32_t ign, const WsHeader* hdr, float* loss_rows,
                                const float* row_scale, int grad_shift, SelfCount sc,
-                               hipStream_t s) {
+                               RowPack pk, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (dtype == 1)
     return row_ce_by_width<uint16_t>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr,
-                                     loss_rows, row_scale, grad_shift, sc, s);
+                                     loss_rows, row_scale, grad_shift, sc, pk, s);
   if (dtype == 2)
     return row_ce_by_width<Half>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                                 row_scale, grad_shift, sc, s);
+                                 row_scale, grad_shift, sc, pk, s);
   return row_ce_by_width<float>(Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                                row_scale, grad_shift, sc, s);
+                                row_scale, grad_shift, sc, pk, s);
 }
 
 hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* G, int64_t ldg, int64_t rows,
                          int64_t V, int64_t pad_cols, const int32_t* targets, int32_t ign,
                          const WsHeader* hdr, float* loss_rows, const float* row_scale,
-                         int grad_shift, hipStream_t s) {
+                         int grad_shift, hipStream_t s, RowPack pk) {
   return row_ce_typed(dtype, Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                      row_scale, grad_shift, SelfCount{0, 0, nullptr}, s);
+                      row_scale, grad_shift, SelfCount{0, 0, nullptr}, pk, s);
 }
 
 hipError_t launch_row_ce_counted(int dtype, const void* Z, void* G, int64_t rows, int64_t V,
@@ -548,7 +555,7 @@ hipError_t launch_row_ce_counted(int dtype, const void* Z, void* G, int64_t rows
     return launch_row_ce(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr, 0, s);
   }
   return row_ce_typed(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr, 0,
-                      SelfCount{rows, reduction, hdr}, s);
+                      SelfCount{rows, reduction, hdr}, RowPack{nullptr, nullptr, 0}, s);
 }
 
 // ------------------------------------------------------------ shard stats
@@ -1061,9 +1068,15 @@ hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader*
 template <typename T, typename TO>
 __global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ Z, int64_t ldz, int64_t rows,
                                                 int64_t V, TO* __restrict__ out, int accumulate,
-                                                const float* __restrict__ out_scale, int out_shift) {
+                                                const float* __restrict__ out_scale, int out_shift,
+                                                const int32_t* __restrict__ live, int64_t live_base) {
   const int64_t v = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 2;
   if (v >= V) return;
+  if (live != nullptr) {  // packed chunk: only the live rows
+    int64_t n = static_cast<int64_t>(*live) - live_base;
+    if (n < 0) n = 0;
+    if (n < rows) rows = n;
+  }
   const bool two = v + 1 < V;
   float a0 = 0.0f, a1 = 0.0f;
   const T* p = Z + v;
@@ -1096,30 +1109,30 @@ __global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ Z, int64_t
 template <typename T>
 static hipError_t colsum_to(const void* Z, int64_t ldz, int64_t rows, int64_t V, void* out,
                             int out_dtype, bool accumulate, const float* out_scale, int out_shift,
-                            hipStream_t s) {
+                            RowPack pk, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((V + 511) / 512));
   const T* z = static_cast<const T*>(Z);
   const int acc = accumulate ? 1 : 0;
   if (out_dtype == 1)
     hipLaunchKernelGGL((k_colsum<T, uint16_t>), grid, dim3(256), 0, s, z, ldz, rows, V,
-                       static_cast<uint16_t*>(out), acc, out_scale, out_shift);
+                       static_cast<uint16_t*>(out), acc, out_scale, out_shift, pk.live, pk.base);
   else if (out_dtype == 2)
     hipLaunchKernelGGL((k_colsum<T, Half>), grid, dim3(256), 0, s, z, ldz, rows, V,
-                       static_cast<Half*>(out), acc, out_scale, out_shift);
+                       static_cast<Half*>(out), acc, out_scale, out_shift, pk.live, pk.base);
   else
     hipLaunchKernelGGL((k_colsum<T, float>), grid, dim3(256), 0, s, z, ldz, rows, V,
-                       static_cast<float*>(out), acc, out_scale, out_shift);
+                       static_cast<float*>(out), acc, out_scale, out_shift, pk.live, pk.base);
   return hipGetLastError();
 }
 
 hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V, void* out,
                          int out_dtype, bool accumulate, const float* out_scale, int out_shift,
-                         hipStream_t s) {
+                         hipStream_t s, RowPack pk) {
   if (dtype == 1)
-    return colsum_to<uint16_t>(Z, ldz, rows, V, out, out_dtype, accumulate, out_scale, out_shift, s);
+    return colsum_to<uint16_t>(Z, ldz, rows, V, out, out_dtype, accumulate, out_scale, out_shift, pk, s);
   if (dtype == 2)
-    return colsum_to<Half>(Z, ldz, rows, V, out, out_dtype, accumulate, out_scale, out_shift, s);
-  return colsum_to<float>(Z, ldz, rows, V, out, out_dtype, accumulate, out_scale, out_shift, s);
+    return colsum_to<Half>(Z, ldz, rows, V, out, out_dtype, accumulate, out_scale, out_shift, pk, s);
+  return colsum_to<float>(Z, ldz, rows, V, out, out_dtype, accumulate, out_scale, out_shift, pk, s);
 }
 
 // -------------------------------------------------------- split-K reduce
@@ -1129,31 +1142,36 @@ template <typename TO>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ parts, int splits,
                                                        int64_t stride, int64_t rows, int64_t cols,
                                                        int64_t ld_out, TO* __restrict__ out,
-                                                       int accumulate) {
+                                                       int accumulate, RowPack pk) {
+  if (pk.live != nullptr) {  // packed chunk: only the live rows
+    const int64_t n = static_cast<int64_t>(*pk.live) - pk.base;
+    if (n < rows) rows = n;
+  }
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= rows * cols) return;
   const int64_t r = i / cols, c = i - r * cols;
   float acc = parts[r * cols + c];
   for (int sp = 1; sp < splits; ++sp) acc += parts[sp * stride + r * cols + c];
-  if (accumulate) acc += Elem<TO>::load(out + r * ld_out + c);
-  Elem<TO>::store(out + r * ld_out + c, acc);
+  const int64_t ro = pk.map != nullptr ? static_cast<int64_t>(pk.map[r]) : r;
+  if (accumulate) acc += Elem<TO>::load(out + ro * ld_out + c);
+  Elem<TO>::store(out + ro * ld_out + c, acc);
 }
 
 hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride, int64_t rows,
                                 int64_t cols, int64_t ld_out, void* out, int out_dtype,
-                                bool accumulate, hipStream_t s) {
+                                bool accumulate, hipStream_t s, RowPack pk) {
   const int64_t n = rows * cols;
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
   const int acc = accumulate ? 1 : 0;
   if (out_dtype == 1)
     hipLaunchKernelGGL(k_splitk_reduce<uint16_t>, grid, dim3(256), 0, s, parts, splits, split_stride,
-                       rows, cols, ld_out, static_cast<uint16_t*>(out), acc);
+                       rows, cols, ld_out, static_cast<uint16_t*>(out), acc, pk);
   else if (out_dtype == 2)
     hipLaunchKernelGGL(k_splitk_reduce<Half>, grid, dim3(256), 0, s, parts, splits, split_stride,
-                       rows, cols, ld_out, static_cast<Half*>(out), acc);
+                       rows, cols, ld_out, static_cast<Half*>(out), acc, pk);
   else
     hipLaunchKernelGGL(k_splitk_reduce<float>, grid, dim3(256), 0, s, parts, splits, split_stride,
-                       rows, cols, ld_out, static_cast<float*>(out), acc);
+                       rows, cols, ld_out, static_cast<float*>(out), acc, pk);
   return hipGetLastError();
 }
 
@@ -1186,6 +1204,166 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(k_fill_f32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ row packing
+//
+// A row whose target is ignore_index (or outside [0, V), flagged as an
+// error and treated as ignored) has zero loss and a zero dlogits row, so it
+// adds nothing to grad_W or grad_bias and its grad_X row is zero. The chunk
+// loop can therefore run the three products and the row kernel over the other
+// rows only. The list is built in three launches (block counts, their
+// exclusive scan, the writes) and keeps the rows in ascending order, so every
+// result is deterministic.
+
+constexpr int kPackThreads = 1024, kPackPer = 4;
+constexpr int64_t kPackRows = kPackThreads * kPackPer;
+
+int64_t pack_block_count(int64_t n) { return (n + kPackRows - 1) / kPackRows; }
+
+__device__ __forceinline__ bool packed_target(int32_t y, int32_t ign, int64_t V) {
+  return y != ign && y >= 0 && static_cast<int64_t>(y) < V;
+}
+
+// Exclusive prefix of v over the 1024 lanes of the block (lane order) and the
+// block total. wsum holds 16 ints; the caller syncs before reusing it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kPackThreads / 64; ++i) {
+    const int t = wsum[i];
+    base += i < w ? t : 0;
+    tot += t;
+  }
+  total = tot;
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kPackThreads) void k_pack_count(const int32_t* __restrict__ t,
+                                                             int64_t n, int64_t V, int32_t ign,
+                                                             int32_t* __restrict__ counts) {
+  __shared__ int wsum[kPackThreads / 64];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kPackRows + threadIdx.x * kPackPer;
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < kPackPer; ++i)
+    if (r0 + i < n && packed_target(t[r0 + i], ign, V)) ++c;
+  int total;
+  block_exclusive_scan(c, wsum, total);
+  if (threadIdx.x == 0) counts[blockIdx.x] = total;
+}
+
+// counts[b] := rows packed by blocks before b; hdr->n_packed := all of them.
+__global__ __launch_bounds__(kPackThreads) void k_pack_scan(int32_t* __restrict__ counts,
+                                                            int64_t nb, WsHeader* __restrict__ hdr) {
+  __shared__ int wsum[kPackThreads / 64];
+  int carry = 0;
+  for (int64_t b0 = 0; b0 < nb; b0 += kPackThreads) {
+    const int64_t b = b0 + threadIdx.x;
+    const int v = b < nb ? counts[b] : 0;
+    int total;
+    const int ex = block_exclusive_scan(v, wsum, total);
+    if (b < nb) counts[b] = carry + ex;
+    carry += total;
+    __syncthreads();  // wsum is rewritten by the next round
+  }
+  if (threadIdx.x == 0) hdr->n_packed = carry;
+}
+
+__global__ __launch_bounds__(kPackThreads) void k_pack_write(const int32_t* __restrict__ t,
+                                                             int64_t n, int64_t V, int32_t ign,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ map,
+                                                             int32_t* __restrict__ packed,
+                                                             float* __restrict__ loss_rows) {
+  __shared__ int wsum[kPackThreads / 64];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kPackRows + threadIdx.x * kPackPer;
+  int32_t y[kPackPer];
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < kPackPer; ++i) {
+    y[i] = r0 + i < n ? t[r0 + i] : ign;
+    c += packed_target(y[i], ign, V) ? 1 : 0;
+  }
+  int total;
+  int64_t pos = static_cast<int64_t>(offsets[blockIdx.x]) + block_exclusive_scan(c, wsum, total);
+#pragma unroll
+  for (int i = 0; i < kPackPer; ++i) {
+    const int64_t r = r0 + i;
+    if (r >= n) break;
+    if (packed_target(y[i], ign, V)) {
+      map[pos] = static_cast<int32_t>(r);
+      packed[pos] = y[i];
+      ++pos;
+    } else if (loss_rows != nullptr) {
+      loss_rows[r] = 0.0f;
+    }
+  }
+}
+
+hipError_t launch_pack_rows(const int32_t* targets, int64_t n, int64_t V, int32_t ign,
+                            int32_t* map, int32_t* packed_targets, int32_t* block_counts,
+                            WsHeader* hdr, float* loss_rows, hipStream_t s) {
+  const int64_t nb = pack_block_count(n);
+  if (nb > 0) {
+    hipLaunchKernelGGL(k_pack_count, dim3(static_cast<unsigned>(nb)), dim3(kPackThreads), 0, s,
+                       targets, n, V, ign, block_counts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_pack_scan, dim3(1), dim3(kPackThreads), 0, s, block_counts, nb, hdr);
+  if (nb == 0) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_pack_write, dim3(static_cast<unsigned>(nb)), dim3(kPackThreads), 0, s,
+                     targets, n, V, ign, block_counts, map, packed_targets, loss_rows);
+  return hipGetLastError();
+}
+
+// One workgroup per chunk row; 16-byte copies.
+__global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ src, int64_t vecs,
+                                                     RowPack pk, uint4* __restrict__ out) {
+  const int64_t r = blockIdx.x;
+  if (r >= static_cast<int64_t>(*pk.live) - pk.base) return;
+  const uint4* a = src + static_cast<int64_t>(pk.map[r]) * vecs;
+  uint4* b = out + r * vecs;
+  for (int64_t v = threadIdx.x; v < vecs; v += 256) b[v] = a[v];
+}
+
+hipError_t launch_gather_rows(const void* src, int64_t row_bytes, int64_t rows, RowPack pk,
+                              void* out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (row_bytes % 16 != 0 || pk.live == nullptr || pk.map == nullptr) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gather_rows, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s,
+                     static_cast<const uint4*>(src), row_bytes / 16, pk, static_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_zero_dead_rows(const int32_t* __restrict__ t, int64_t V,
+                                                        int32_t ign, uint4* __restrict__ G,
+                                                        int64_t vecs) {
+  const int64_t r = blockIdx.x;
+  if (packed_target(t[r], ign, V)) return;
+  uint4* g = G + r * vecs;
+  for (int64_t v = threadIdx.x; v < vecs; v += 256) g[v] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero_dead_rows(const int32_t* targets, int64_t n, int64_t V, int32_t ign,
+                                 void* G, int64_t row_bytes, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (row_bytes % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_zero_dead_rows, dim3(static_cast<unsigned>(n)), dim3(256), 0, s, targets, V,
+                     ign, static_cast<uint4*>(G), row_bytes / 16);
   return hipGetLastError();
 }
 

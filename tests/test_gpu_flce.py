@@ -178,20 +178,24 @@ def test_bf16_zipf_targets_with_skipped_grads(B):
     check_against_oracle(inp, "mean", got, want=())
 
 
-def test_loss_bitwise_independent_of_chunking_and_deterministic(B):
+@pytest.mark.parametrize("pack", [True, False])
+def test_loss_bitwise_independent_of_chunking_and_deterministic(packing, pack):
     """Per-row losses (hence the loss) are bitwise independent of the chunk
-    size; grad_X is bitwise equal whenever the grad_X K-split is the same (a
-    different split only changes its rounding order); repeated calls are
-    bitwise identical."""
+    size, with row packing on or off; unpacked, grad_X is bitwise equal
+    whenever the grad_X K-split is the same (a different split only changes
+    its rounding order; packed, the last chunk may split its K in two);
+    repeated calls are bitwise identical."""
+    B = packing
+    B.flce_set_row_packing(pack)
     inp = synth.make_flce_inputs(1000, 256, 5000, "bf16", bias_std=0.02, seed=15)
-    say("flce chunk independence")
+    say("flce chunk independence, packing", pack)
     chunks = (0, 256, 512, 1000)
     runs = {c: run_flce(B, inp, "none", chunk_rows=c) for c in chunks}
     splits = {c: B.flce_plan(1000, 256, 5000, B.BF16, c)[1] for c in chunks}
     base = runs[1000]
     for c, r in runs.items():
         assert np.array_equal(r[0], base[0]), f"loss rows differ at chunk {c}"
-        if splits[c] == splits[1000]:
+        if splits[c] == splits[1000] and not pack:
             assert np.array_equal(r[1], base[1]), f"grad_X differs at chunk {c}"
         else:
             check_max_rel(r[1], base[1], 1e-5, f"grad_X chunk {c} vs 1000")
@@ -254,6 +258,107 @@ def test_bad_target_reported(B):
         workspace=ws)
     assert B.flce_check_device_error(ws) == B.E_TARGET
     check_against_oracle(inp2, "none", (to_host(loss), to_host(gX), to_host(gW), None))
+
+
+@pytest.fixture
+def packing(B):
+    """Restores the row-packing switch after a test that flips it."""
+    was = B.flce_set_row_packing(True)
+    yield B
+    B.flce_set_row_packing(was)
+
+
+def _flce_dev(B, inp, reduction, chunk, grad_dtype=None):
+    import torch
+    dt = inp["dtype"]
+    X, W = to_dev(inp["X"], dt), to_dev(inp["W"], dt)
+    b, y = to_dev(inp["bias"], dt), to_dev(inp["targets"], "i32")
+    kw = {} if grad_dtype is None else {"grad_dtype": grad_dtype}
+    out = B.flce_forward_backward(X, W, y, bias=b, reduction=reduction, chunk_rows=chunk, **kw)
+    torch.cuda.synchronize()
+    return tuple(None if t is None else t.double().cpu().numpy() for t in out)
+
+
+@pytest.mark.parametrize("dtype,N,H,V,chunk,ignore,reduction,bias", [
+    ("bf16", 1024, 136, 1000, 256, 0.6, "mean", True),   # packed rows fill 2 of 4 chunks
+    ("bf16", 600, 136, 1000, 0, 0.1, "none", True),      # one chunk, ragged tiles
+    ("bf16", 1000, 264, 4099, 128, 0.35, "sum", False),  # 8 chunks, a partial live tile
+    ("f16", 700, 136, 1500, 256, 0.5, "mean", True),
+    ("bf16", 512, 2048, 16384, 0, 0.3, "mean", False),   # split-K grad_X reduced through the map
+])
+def test_row_packing_against_oracle_and_unpacked(packing, dtype, N, H, V, chunk, ignore, reduction,
+                                                 bias):
+    """Packed chunk loop (ignored rows listed out on the device) against the
+    FP64 oracle, and against the same call with packing off: the loss (every
+    row for none) is bitwise equal, and so is grad_X outside the last chunk;
+    the rest differ only in float32 summation order (the last chunk's K
+    split, where chunk boundaries fall in the grad_W and grad_bias sums)."""
+    B = packing
+    inp = synth.make_flce_inputs(N, H, V, dtype, bias_std=0.1 if bias else 0.0,
+                                 ignore_frac=ignore, seed=N + H)
+    say("flce row packing", dtype, N, H, V, chunk, ignore, reduction)
+    packed = _flce_dev(B, inp, reduction, chunk)
+    check_against_oracle(inp, reduction, packed)
+    B.flce_set_row_packing(False)
+    say("flce row packing off", dtype, N, H, V, chunk, ignore, reduction)
+    plain = _flce_dev(B, inp, reduction, chunk)
+    B.flce_set_row_packing(True)
+    assert np.array_equal(packed[0], plain[0]), "loss differs with packing"
+    # grad_X rows are bitwise equal, except those packed into the last chunk,
+    # whose K may be split in two (only the summation order differs).
+    c = chunk or B.flce_plan(N, H, V, B.BF16 if dtype == "bf16" else B.F16)[0]
+    last0 = (-(-N // c) - 1) * c
+    live_rows = np.flatnonzero(inp["targets"] != -100)
+    tail = live_rows[last0:]
+    same = np.ones(N, dtype=bool)
+    same[tail] = False
+    assert np.array_equal(packed[1][same], plain[1][same]), "grad_X differs with packing"
+    check_max_rel(packed[1], plain[1], 1e-6, "grad_X packed vs plain")
+    check_max_rel(packed[2], plain[2], 1e-5, "grad_W packed vs plain")
+    if bias:
+        check_max_rel(packed[3], plain[3], 1e-5, "grad_bias packed vs plain")
+
+
+def test_row_packing_16bit_gradients(packing):
+    """flce_forward_backward_ex (bf16 gradient outputs) through the packed
+    loop: grad_X rows rounded once, so bitwise equal to the unpacked call;
+    zero rows for the ignored targets."""
+    B = packing
+    inp = synth.make_flce_inputs(900, 136, 2000, "bf16", bias_std=0.1, ignore_frac=0.4, seed=41)
+    say("flce row packing, bf16 gradients")
+    packed = _flce_dev(B, inp, "mean", 256, grad_dtype="input")
+    B.flce_set_row_packing(False)
+    plain = _flce_dev(B, inp, "mean", 256, grad_dtype="input")
+    B.flce_set_row_packing(True)
+    assert np.array_equal(packed[0], plain[0]) and np.array_equal(packed[1], plain[1])
+    assert np.all(packed[1][inp["targets"] == -100] == 0.0)
+    check_against_oracle(inp, "mean", packed)
+
+
+def test_row_packing_all_ignored_and_bad_targets_bf16(B):
+    """16-bit inputs take the packed loop: with every row ignored no row is
+    live (loss 0, all gradients 0, including grad_W's first-chunk store);
+    an out-of-range target is reported and its row is left out like an
+    ignored one."""
+    import torch
+    inp = synth.make_flce_inputs(300, 64, 500, "bf16", bias_std=0.1, ignore_frac=1.0, seed=42)
+    say("flce bf16 all ignored (packed)")
+    for red in ("mean", "sum", "none"):
+        loss, gX, gW, gb = run_flce(B, inp, red, chunk_rows=128)
+        assert np.all(loss == 0.0) and np.all(gX == 0) and np.all(gW == 0) and np.all(gb == 0)
+    inp = synth.make_flce_inputs(300, 64, 500, "bf16", ignore_frac=0.2, seed=43)
+    y = inp["targets"].copy()
+    y[7], y[200] = 500, -5
+    ws = torch.zeros(B.flce_workspace_bytes(300, 64, 500, B.BF16, 128), dtype=torch.uint8, device="cuda")
+    say("flce bf16 bad targets (packed)")
+    loss, gX, gW, _ = B.flce_forward_backward(
+        to_dev(inp["X"], "bf16"), to_dev(inp["W"], "bf16"), to_dev(y, "i32"), reduction="none",
+        chunk_rows=128, workspace=ws)
+    assert B.flce_check_device_error(ws) == B.E_TARGET
+    got = (to_host(loss), to_host(gX), to_host(gW), None)
+    assert got[0][7] == 0.0 and got[0][200] == 0.0
+    assert np.all(got[1][[7, 200]] == 0.0)
+    check_against_oracle(dict(inp, targets=y), "none", got)
 
 
 def test_shard_stats_of_projection(B):
