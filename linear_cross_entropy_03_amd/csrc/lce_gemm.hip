@@ -94,6 +94,12 @@ __device__ __forceinline__ bool apply_live(GemmDesc& d, int64_t& tiles_m, int64_
 // with ds_read_b64_tr_b16, which hands each lane four consecutive k of one
 // column. Both layouts XOR-swizzle their 16-byte slots so the MFMA operand
 // reads are bank-conflict free.
+// Non-temporal output stores (out_store): 0.2-0.3% per FLCE step in
+// alternating same-box runs; 0 gives plain stores.
+#ifndef LCE_NT_STORES
+#define LCE_NT_STORES 1
+#endif
+
 namespace mfma2 {
 
 constexpr int kBM = 256, kBK = 32;
@@ -355,6 +361,24 @@ __device__ __forceinline__ char* epi_region(int w) {
   return base + o;
 }
 
+// Output stores. With LCE_NT_STORES they are non-temporal: the outputs
+// (chunk logits, gradients) are not read again by this kernel, so they are
+// kept from displacing the operand panels that other tiles still read.
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+template <typename V>
+__device__ __forceinline__ void out_store(V* p, const V& v) {
+#if LCE_NT_STORES
+  static_assert(sizeof(V) == 8 || sizeof(V) == 16, "8- or 16-byte stores");
+  if constexpr (sizeof(V) == 16)
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(p));
+  else
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x2_t, v), reinterpret_cast<u32x2_t*>(p));
+#else
+  *p = v;
+#endif
+}
+
 // Lanes of one wave exchange data through LDS: LDS executes a wave's
 // instructions in order, so only the compiler must not reorder.
 __device__ __forceinline__ void wave_lds_fence() {
@@ -402,7 +426,7 @@ __device__ __forceinline__ void epilogue_16(const f32x16_t (&acc)[4][kFJ], const
       if (m >= d.M || n >= d.N) continue;
       uint16_t* c = static_cast<uint16_t*>(d.C) + m * d.ldc + n;
       if (n + 7 < d.N) {
-        *reinterpret_cast<uint4*>(c) = val;
+        out_store(reinterpret_cast<uint4*>(c), val);
       } else {
         const uint32_t w[4] = {val.x, val.y, val.z, val.w};
         for (int e = 0; e < 8 && n + e < d.N; ++e)
@@ -479,9 +503,9 @@ __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], cons
           o.x += old[u].x; o.y += old[u].y; o.z += old[u].z; o.w += old[u].w;
         }
         if constexpr (k16)
-          *reinterpret_cast<uint2*>(c) = make_uint2(pack2(o.x, o.y), pack2(o.z, o.w));
+          out_store(reinterpret_cast<uint2*>(c), make_uint2(pack2(o.x, o.y), pack2(o.z, o.w)));
         else
-          *reinterpret_cast<float4*>(c) = o;
+          out_store(reinterpret_cast<float4*>(c), o);
       } else {
         const float w[4] = {o.x, o.y, o.z, o.w};
         for (int e = 0; e < 4 && n + e < d.N; ++e) {
