@@ -558,8 +558,8 @@ def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
-    # Head 0 runs packed (when packing is on); the others take every row.
-    flops = (rows_through_products(B, yk[0]) + (K - 1) * N) * 6.0 * H * V
+    # Each head runs over its own non-ignored rows (when packing is on).
+    flops = sum(rows_through_products(B, yk[k]) for k in range(K)) * 6.0 * H * V
     out = {
         "workload": f"{K} heads over llama8b_head_bf16 hidden states (N {N}, H {H}, V {V}, "
                     f"{cfg['reduction']})",
@@ -725,7 +725,7 @@ def main():
     # the packed-row lists and the chunk's gathered hidden states.
     max_splits = max(splits, 2 if (e == 2 and splits == 1 and V // 2 >= 2048) else splits)
     extra_bound = (chunk * ((V + 7) // 8 * 8) * e + (N + V) * 16 + 4096
-                   + (max_splits * chunk * H * 4 if max_splits > 1 else 0)
+                   + (max_splits * chunk * H * 4 if (max_splits > 1 or e == 2) else 0)
                    + ((chunk * H * e + 8 * N + 4096) if e == 2 else 0))
     step_flops = 6.0 * n_live * H * V
     result = {

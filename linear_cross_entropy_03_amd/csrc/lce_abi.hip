@@ -146,14 +146,16 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
   // its grad_X tiles (256 rows x 256 columns) then fill the CUs unevenly, and
   // splitting K in two halves the granularity.
   p->last_splits = (is16(dtype) && p->dx_splits == 1 && V / 2 >= 2048) ? 2 : p->dx_splits;
-  const int max_splits = std::max(p->dx_splits, p->last_splits);
+  // Packed heads that add to grad_X reduce it through the partial buffer
+  // (one split), so 16-bit plans always hold at least one.
+  const int max_splits = std::max(std::max(p->dx_splits, p->last_splits), is16(dtype) ? 1 : 0);
   size_t off = align_up(sizeof(WsHeader));
   p->off_rows = off;
   off += align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float));
   p->off_chunk = off;
   off += align_up(static_cast<size_t>(chunk) * static_cast<size_t>(ldz) * e);
   p->off_split = off;
-  if (max_splits > 1)
+  if (max_splits > 1 || is16(dtype))
     off += align_up(static_cast<size_t>(max_splits) * static_cast<size_t>(chunk) *
                     static_cast<size_t>(H) * sizeof(float));
   p->pack_ok = is16(dtype);
@@ -281,7 +283,7 @@ namespace {
 // what is there when accum_gx), grad_W (stored on the first chunk, added
 // after). Targets must have been counted into hdr.
 //
-// Row packing (16-bit inputs, grad_X stored): rows with an ignored or
+// Row packing (16-bit inputs): rows with an ignored or
 // invalid target contribute nothing, so they are listed out first and every
 // chunk covers the next `chunk` of the remaining rows. The host does not know
 // how many remain (the count lives on the device and is never read back), so
@@ -289,7 +291,9 @@ namespace {
 // count: GEMM tiles past it exit, the grad_W product shortens its K loop. The
 // chunk's hidden states are gathered into the workspace for the logits and
 // grad_W products; loss and grad_X rows are written back to their original
-// rows, and grad_X rows of the dropped rows are zeroed.
+// rows, and grad_X rows of the dropped rows are zeroed (or, when adding to
+// grad_X, left as they are: the chunk's partial products then go through the
+// split-K buffer and its reduction adds them to the original rows).
 int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const void* bias,
                 const int32_t* targets, int64_t N, int64_t H, int64_t V, int32_t ignore_index,
                 WsHeader* hdr, float* loss_rows, void* grad_X, bool accum_gx, void* grad_W,
@@ -305,7 +309,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
   const GradScaling gsc = grad_scaling(dtype, hdr);
 
-  const bool pack = g_row_packing && p.pack_ok && !accum_gx && N > 0;
+  const bool pack = g_row_packing && p.pack_ok && N > 0;
   int32_t* map = reinterpret_cast<int32_t*>(ws + p.off_map);
   const int32_t* ptgt = reinterpret_cast<const int32_t*>(ws + p.off_ptgt);
   char* xs = ws + p.off_xs;
@@ -314,7 +318,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
       return launch_pack_rows(targets, N, V, ignore_index, map, const_cast<int32_t*>(ptgt),
                               reinterpret_cast<int32_t*>(ws + p.off_bcnt), hdr, loss_rows, s);
     }));
-    if (grad_X)
+    if (grad_X && !accum_gx)
       LCE_TRY(timed(kKindOther, s, [&] {
         return launch_zero_dead_rows(targets, N, V, ignore_index, grad_X,
                                      H * static_cast<int64_t>(ge), s);
@@ -369,7 +373,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
       live(g2, 0);
       void* out = static_cast<char*>(grad_X) + (pack ? 0 : static_cast<size_t>(r0) * H * ge);
       const int splits = (pack && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
-      if (splits > 1) {
+      if (splits > 1 || (pack && accum_gx)) {
         g2.epilogue = kEpiStoreF32;
         g2.C = split_buf; g2.ldc = H;
         g2.k_splits = splits; g2.split_stride = rows * H;

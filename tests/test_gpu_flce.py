@@ -335,6 +335,36 @@ def test_row_packing_16bit_gradients(packing):
     check_against_oracle(inp, "mean", packed)
 
 
+def test_row_packing_multihead(packing):
+    """Multi-head call with every head packed over its own targets (heads
+    after the first add their grad_X rows through the partial buffer): the
+    head losses are bitwise those of the unpacked call, the gradients equal
+    up to float32 summation order."""
+    import torch
+    B = packing
+    K, N, H, V = 3, 900, 136, 2100
+    inp = synth.make_flce_inputs(N, H, K * V, "bf16", ignore_frac=0.0, seed=44)
+    X = to_dev(inp["X"], "bf16")
+    W = to_dev(inp["W"], "bf16").reshape(K, V, H).contiguous()
+    rng = np.random.default_rng(45)
+    yk = rng.integers(0, V, size=(K, N)).astype(np.int32)
+    for k in range(K):  # different ignored rows per head, 10% to 50%
+        yk[k, rng.choice(N, int(N * (0.1 + 0.2 * k)), replace=False)] = -100
+    y = to_dev(yk, "i32")
+    out = {}
+    for pack in (True, False):
+        B.flce_set_row_packing(pack)
+        say("multihead packing", pack, K, N, H, V)
+        res = B.flce_multihead_forward_backward(X, W, y, reduction="none", chunk_rows=256)
+        torch.cuda.synchronize()
+        out[pack] = [None if t is None else t.double().cpu().numpy() for t in res]
+    B.flce_set_row_packing(True)
+    assert np.array_equal(out[True][0], out[False][0]), "head losses differ with packing"
+    check_max_rel(out[True][1], out[False][1], 1e-6, "grad_X packed vs plain")
+    check_max_rel(out[True][2], out[False][2], 1e-5, "grad_W packed vs plain")
+    assert np.all(out[True][1][(yk == -100).all(axis=0)] == 0.0)
+
+
 def test_row_packing_all_ignored_and_bad_targets_bf16(B):
     """16-bit inputs take the packed loop: with every row ignored no row is
     live (loss 0, all gradients 0, including grad_W's first-chunk store);
