@@ -70,6 +70,10 @@ inline void scale_output(GemmDesc& d, const GradScaling& g) {
   d.out_shift = g.out_shift;
 }
 
+#ifndef LCE_LAST_SPLITS
+#define LCE_LAST_SPLITS 2
+#endif
+
 constexpr int64_t kMaxRows = int64_t(1) << 31;     // grid.x of the row kernels
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 // Default byte budget of one chunk's logits (the planner's only memory knob).
@@ -145,7 +149,9 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
   // Packed, the last chunk usually holds fewer live rows than the others;
   // its grad_X tiles (256 rows x 256 columns) then fill the CUs unevenly, and
   // splitting K in two halves the granularity.
-  p->last_splits = (is16(dtype) && p->dx_splits == 1 && V / 2 >= 2048) ? 2 : p->dx_splits;
+  p->last_splits = p->dx_splits;
+  if (is16(dtype))
+    while (p->last_splits < LCE_LAST_SPLITS && V / (2 * p->last_splits) >= 2048) p->last_splits *= 2;
   // Packed heads that add to grad_X reduce it through the partial buffer
   // (one split), so 16-bit plans always hold at least one.
   const int max_splits = std::max(std::max(p->dx_splits, p->last_splits), is16(dtype) ? 1 : 0);

@@ -70,6 +70,30 @@ def test_workspace_queries_and_plan(B):
     assert B.ce_workspace_bytes(-1, 5) == 0
 
 
+def test_row_packing_switch_and_workspace(B):
+    """The packing switch returns the previous setting and does not change the
+    workspace size; 16-bit plans hold the packing buffers (row map and packed
+    targets, 4 bytes per row each, the chunk's gathered rows, one split-K
+    partial at least), float32 plans none of them."""
+    was = B.flce_set_row_packing(False)
+    try:
+        assert B.flce_set_row_packing(True) is False
+        assert B.flce_set_row_packing(True) is True
+        N, H, V, C = 4096, 512, 3000, 1024
+        on = B.flce_workspace_bytes(N, H, V, B.BF16, C)
+        B.flce_set_row_packing(False)
+        assert B.flce_workspace_bytes(N, H, V, B.BF16, C) == on
+        f32 = B.flce_workspace_bytes(N, H, V, B.F32, C)
+        ldz = (V + 7) // 8 * 8
+        assert f32 >= 256 + N * 4 + C * ldz * 4
+        assert f32 < 256 + N * 4 + C * ldz * 4 + 4 * 256
+        base16 = 256 + N * 4 + C * ldz * 2
+        assert on >= base16 + C * H * 4 + 2 * N * 4 + C * H * 2
+        assert on < base16 + C * H * 4 + 2 * N * 4 + C * H * 2 + 16 * 256
+    finally:
+        B.flce_set_row_packing(was)
+
+
 def _fb(B, **kw):
     args = dict(X=16, W=16, bias=None, targets=16, N=4, H=8, V=10, dtype=B.BF16, ign=-100, red=2,
                 loss=16, gX=16, gW=16, gb=None, ws=16, wsb=1 << 30, chunk=0, stream=None)
