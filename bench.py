@@ -279,7 +279,9 @@ def bench_vocab_parallel(torch, B, X, W, y, cfg, reps=5):
     (logits GEMM + statistics), the combine of 8 shards' statistics (the same
     statistics replicated, so only the arithmetic is real), then the shard's
     backward (logits GEMM again, dZ from the global lse, grad_X partial and
-    grad_W shard). GEMM work per step: 4 x 2 x N x H x V_local flop."""
+    grad_W shard). GEMM work per step: 2 x N x H x V_local flop for the
+    statistics (every row) and 3 x 2 x L x H x V_local for the backward, L the
+    rows it runs over (the non-ignored ones when row packing is on)."""
     N, H, V = cfg["N"], cfg["H"], cfg["V"]
     P = 8
     Vl = V // P
@@ -329,7 +331,7 @@ def bench_vocab_parallel(torch, B, X, W, y, cfg, reps=5):
     B.flce_timing_reset()
     stats_ms, comb_ms, bwd_ms = (x / reps for x in tot)
     step_ms = stats_ms + comb_ms + bwd_ms
-    gemm_flops = 4 * 2.0 * N * H * Vl
+    gemm_flops = 2.0 * (N + 3 * rows_through_products(B, y)) * H * Vl
     return {
         "workload": f"llama8b_head_bf16 vocabulary shard 3 of {P} (N {N}, H {H}, V_local {Vl}, "
                     f"V {V}, {cfg['reduction']})",
@@ -470,7 +472,9 @@ def bench_dpo(torch, B, X, W, y, cfg, n_pairs=4, seq_len=1024, reps=3):
     ms = a.elapsed_time(b) / reps
     chunk = B.flce_plan(N, H, V, B.BF16)[0]
     n_logits = logit_n / reps                      # logits GEMMs per call (1 or 2 per chunk)
-    flops = (4.0 + 2.0 * n_logits * chunk / N) * N * H * V
+    # Passes over the logits (1 with one chunk, else 2), each over the rows
+    # that go through the products.
+    flops = (4.0 + 2.0 * n_logits * chunk / N) * rows_through_products(B, yd) * H * V
     out = {
         "workload": f"DPO, {n_pairs} pairs x 2 x {seq_len} tokens over the llama8b_head_bf16 head "
                     f"(N {N}, H {H}, V {V}, beta 0.1, prompt quarter masked)",

@@ -284,6 +284,57 @@ static int validate_common(int dtype, int reduction) {
 
 namespace {
 
+// Row packing state of one call's chunk loop (see flce_chunks).
+struct Packer {
+  bool on = false;
+  int32_t* map = nullptr;          // packed row -> original row [N]
+  const int32_t* ptgt = nullptr;   // packed targets [N]
+  char* xs = nullptr;              // the chunk's gathered hidden states [chunk, H]
+  const int32_t* live = nullptr;   // &hdr->n_packed
+
+  // Lists the rows whose target is valid against V_valid, zeroes the other
+  // rows' loss entries (loss_rows may be null) and, when grad_X is given,
+  // their grad_X rows of gx_row_bytes bytes.
+  int setup(const Plan& p, char* ws, WsHeader* hdr, const int32_t* targets, int64_t N,
+            int64_t V_valid, int32_t ign, float* loss_rows, void* grad_X, int64_t gx_row_bytes,
+            hipStream_t s) {
+    on = g_row_packing && p.pack_ok && N > 0;
+    if (!on) return FLCE_OK;
+    map = reinterpret_cast<int32_t*>(ws + p.off_map);
+    ptgt = reinterpret_cast<const int32_t*>(ws + p.off_ptgt);
+    xs = ws + p.off_xs;
+    live = &hdr->n_packed;
+    LCE_TRY(timed(kKindOther, s, [&] {
+      return launch_pack_rows(targets, N, V_valid, ign, map, const_cast<int32_t*>(ptgt),
+                              reinterpret_cast<int32_t*>(ws + p.off_bcnt), hdr, loss_rows, s);
+    }));
+    if (grad_X)
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_zero_dead_rows(targets, N, V_valid, ign, grad_X, gx_row_bytes, s);
+      }));
+    return FLCE_OK;
+  }
+  RowPack chunk(int64_t r0) const {
+    return on ? RowPack{map + r0, live, r0} : RowPack{nullptr, nullptr, 0};
+  }
+  // The chunk's rows of X: gathered when packed, else rows r0.. of X.
+  int rows_of(const void* X, int64_t r0, int64_t rows, int64_t H, size_t e, hipStream_t s,
+              const char** Xc) const {
+    *Xc = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+    if (!on) return FLCE_OK;
+    LCE_TRY(timed(kKindOther, s, [&] {
+      return launch_gather_rows(X, H * static_cast<int64_t>(e), rows, chunk(r0), xs, s);
+    }));
+    *Xc = xs;
+    return FLCE_OK;
+  }
+  // A GEMM whose M (dim 0) or K (dim 1) runs over the chunk's rows.
+  void limit(GemmDesc& d, int dim, int64_t r0) const {
+    if (!on) return;
+    d.live = live; d.live_base = r0; d.live_dim = dim;
+  }
+};
+
 // The chunk loop of FLCE over all N rows for one head: logits GEMM, row CE
 // (loss rows, dZ in place), bias column sums, grad_X (stored, or added to
 // what is there when accum_gx), grad_W (stored on the first chunk, added
@@ -315,38 +366,22 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
   const GradScaling gsc = grad_scaling(dtype, hdr);
 
-  const bool pack = g_row_packing && p.pack_ok && N > 0;
-  int32_t* map = reinterpret_cast<int32_t*>(ws + p.off_map);
-  const int32_t* ptgt = reinterpret_cast<const int32_t*>(ws + p.off_ptgt);
-  char* xs = ws + p.off_xs;
-  if (pack) {
-    LCE_TRY(timed(kKindOther, s, [&] {
-      return launch_pack_rows(targets, N, V, ignore_index, map, const_cast<int32_t*>(ptgt),
-                              reinterpret_cast<int32_t*>(ws + p.off_bcnt), hdr, loss_rows, s);
-    }));
-    if (grad_X && !accum_gx)
-      LCE_TRY(timed(kKindOther, s, [&] {
-        return launch_zero_dead_rows(targets, N, V, ignore_index, grad_X,
-                                     H * static_cast<int64_t>(ge), s);
-      }));
-  }
+  Packer pkr;
+  int st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows,
+                     accum_gx ? nullptr : grad_X, H * static_cast<int64_t>(ge), s);
+  if (st != FLCE_OK) return st;
+  const bool pack = pkr.on;
+  const int32_t* ptgt = pkr.ptgt;
 
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
     // Packed: chunk rows are packed rows r0.. (live up to hdr->n_packed).
-    const RowPack pk = pack ? RowPack{map + r0, &hdr->n_packed, r0} : RowPack{nullptr, nullptr, 0};
-    const char* Xc = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
-    if (pack) {
-      LCE_TRY(timed(kKindOther, s, [&] {
-        return launch_gather_rows(X, H * static_cast<int64_t>(e), rows, pk, xs, s);
-      }));
-      Xc = xs;
-    }
-    auto live = [&](GemmDesc& d, int dim) {
-      if (!pack) return;
-      d.live = pk.live; d.live_base = pk.base; d.live_dim = dim;
-    };
+    const RowPack pk = pkr.chunk(r0);
+    const char* Xc;
+    st = pkr.rows_of(X, r0, rows, H, e, s, &Xc);
+    if (st != FLCE_OK) return st;
+    auto live = [&](GemmDesc& d, int dim) { pkr.limit(d, dim, r0); };
 
     GemmDesc g1{};
     g1.A = Xc; g1.lda = H; g1.a_kmajor = true;
@@ -787,10 +822,19 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
     if (grad_bias_shard)
       LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_bias_shard, V_local, 0.0f, s); }));
   }
+  // Rows with an ignored or invalid target have zero dlogits over every
+  // shard: packed as in flce_chunks (validity against V_global).
+  Packer pkr;
+  st = pkr.setup(p, ws, hdr, targets, N, V_global, ignore_index, nullptr, grad_X,
+                 H * static_cast<int64_t>(sizeof(float)), s);
+  if (st != FLCE_OK) return st;
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
-    const char* Xc = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+    const RowPack pk = pkr.chunk(r0);
+    const char* Xc;
+    st = pkr.rows_of(X, r0, rows, H, e, s, &Xc);
+    if (st != FLCE_OK) return st;
 
     GemmDesc g1{};
     g1.A = Xc; g1.lda = H; g1.a_kmajor = true;
@@ -798,16 +842,17 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
     g1.C = zbuf; g1.ldc = p.ldz; g1.bias = bias_shard;
     g1.M = rows; g1.N = V_local; g1.K = H;
     g1.epilogue = kEpiLogits; g1.k_splits = 1;
+    pkr.limit(g1, 0, r0);
     LCE_TRY(timed(kKindLogits, s, [&] { return gemm(g1, s); }));
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_shard_grad(dtype, zbuf, p.ldz, rows, V_local, p.ldz - V_local, vocab_start,
-                               V_global, targets + r0, ignore_index, row_lse + r0, hdr,
-                               gsc.row_shift, s);
+                               V_global, (pkr.on ? pkr.ptgt : targets) + r0, ignore_index,
+                               pkr.on ? row_lse : row_lse + r0, hdr, gsc.row_shift, s, pk);
     }));
     if (grad_bias_shard)
       LCE_TRY(timed(kKindOther, s, [&] {
         return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, FLCE_F32, !first,
-                             gsc.out_scale, gsc.out_shift, s);
+                             gsc.out_scale, gsc.out_shift, s, pk);
       }));
     if (grad_X) {
       GemmDesc g2{};
@@ -816,16 +861,20 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
       g2.M = rows; g2.N = H; g2.K = V_local;
       g2.epilogue = kEpiStoreF32;
       scale_output(g2, gsc);
-      float* out = grad_X + static_cast<size_t>(r0) * H;
-      if (p.dx_splits > 1) {
+      pkr.limit(g2, 0, r0);
+      float* out = grad_X + (pkr.on ? 0 : static_cast<size_t>(r0) * H);
+      const int splits = (pkr.on && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
+      if (splits > 1) {
         g2.C = split_buf; g2.ldc = H;
-        g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
+        g2.k_splits = splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, FLCE_F32, false, s);
+          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, FLCE_F32, false,
+                                      s, pk);
         }));
       } else {
         g2.C = out; g2.ldc = H; g2.k_splits = 1;
+        if (pkr.on) g2.row_map = pk.map;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
       }
     }
@@ -838,6 +887,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
       g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32;
       g3.k_splits = 1;
       scale_output(g3, gsc);
+      pkr.limit(g3, 1, r0);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }
@@ -986,13 +1036,21 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
   float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   const size_t e = elem_bytes(dtype);
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st2) { return gemm_for(dtype, d, st2); };
-  auto logits = [&](int64_t r0, int64_t rows) {
+  // Rows with an ignored or invalid target (the masked prompt tokens) add
+  // nothing to the log-probabilities or the gradients: both passes run over
+  // the packed rows (as in flce_chunks).
+  Packer pkr;
+  // Chunk rows (gathered when packed) and their logits.
+  auto logits = [&](int64_t r0, int64_t rows, const char** Xc) {
+    int r = pkr.rows_of(X, r0, rows, H, e, s, Xc);
+    if (r != FLCE_OK) return hipErrorUnknown;
     GemmDesc g1{};
-    g1.A = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+    g1.A = *Xc;
     g1.lda = H; g1.a_kmajor = true;
     g1.B = W; g1.ldb = H; g1.b_kmajor = true;
     g1.C = zbuf; g1.ldc = p.ldz; g1.M = rows; g1.N = V; g1.K = H;
     g1.epilogue = kEpiLogits; g1.k_splits = 1;
+    pkr.limit(g1, 0, r0);
     return timed(kKindLogits, s, [&] { return gemm(g1, s); });
   };
 
@@ -1003,13 +1061,19 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
   }));
   if (N == 0 && grad_W)
     LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W, V * H, 0.0f, s); }));
+  st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows, grad_X,
+                 H * static_cast<int64_t>(sizeof(float)), s);
+  if (st != FLCE_OK) return st;
+  const int32_t* tg = pkr.on ? pkr.ptgt : targets;
   // Pass 1: the CE row losses of every row (= minus the token log-probabilities).
+  const char* Xc = nullptr;
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
-    LCE_TRY(logits(r0, rows));
+    LCE_TRY(logits(r0, rows, &Xc));
     LCE_TRY(timed(kKindRowCE, s, [&] {
-      return launch_row_ce(dtype, zbuf, p.ldz, nullptr, p.ldz, rows, V, p.ldz - V, targets + r0,
-                           ignore_index, hdr, loss_rows + r0, nullptr, 0, s);
+      return launch_row_ce(dtype, zbuf, p.ldz, nullptr, p.ldz, rows, V, p.ldz - V, tg + r0,
+                           ignore_index, hdr, pkr.on ? loss_rows : loss_rows + r0, nullptr, 0, s,
+                           pkr.chunk(r0));
     }));
   }
   LCE_TRY(timed(kKindOther, s, [&] {
@@ -1017,7 +1081,8 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
                       row_scale, s);
   }));
   // Pass 2: per-row weighted dlogits and the two gradient products. With a
-  // single chunk its logits are still in the buffer (pass 1 only read them).
+  // single chunk its logits (and gathered rows) are still in the buffers
+  // (pass 1 only read them).
   const bool one_chunk = N <= p.chunk;
   // The rows carry their own factors, |±beta sigma(-d) / P| <= beta / P.
   const GradScaling gsc =
@@ -1025,11 +1090,12 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
   for (int64_t r0 = 0; r0 < N && (grad_X || grad_W); r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
-    const char* Xc = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
-    if (!one_chunk) LCE_TRY(logits(r0, rows));
+    const RowPack pk = pkr.chunk(r0);
+    if (!one_chunk) LCE_TRY(logits(r0, rows, &Xc));
     LCE_TRY(timed(kKindRowCE, s, [&] {
-      return launch_row_ce(dtype, zbuf, p.ldz, zbuf, p.ldz, rows, V, p.ldz - V, targets + r0,
-                           ignore_index, hdr, loss_rows + r0, row_scale + r0, gsc.row_shift, s);
+      return launch_row_ce(dtype, zbuf, p.ldz, zbuf, p.ldz, rows, V, p.ldz - V, tg + r0,
+                           ignore_index, hdr, pkr.on ? loss_rows : loss_rows + r0,
+                           pkr.on ? row_scale : row_scale + r0, gsc.row_shift, s, pk);
     }));
     if (grad_X) {
       GemmDesc g2{};
@@ -1038,15 +1104,19 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
       g2.M = rows; g2.N = H; g2.K = V;
       g2.epilogue = kEpiStoreF32;
       scale_output(g2, gsc);
-      float* out = grad_X + static_cast<size_t>(r0) * H;
-      if (p.dx_splits > 1) {
-        g2.C = split_buf; g2.ldc = H; g2.k_splits = p.dx_splits; g2.split_stride = rows * H;
+      pkr.limit(g2, 0, r0);
+      float* out = grad_X + (pkr.on ? 0 : static_cast<size_t>(r0) * H);
+      const int splits = (pkr.on && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
+      if (splits > 1) {
+        g2.C = split_buf; g2.ldc = H; g2.k_splits = splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H, rows, H, H, out, FLCE_F32, false, s);
+          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, FLCE_F32, false,
+                                      s, pk);
         }));
       } else {
         g2.C = out; g2.ldc = H; g2.k_splits = 1;
+        if (pkr.on) g2.row_map = pk.map;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
       }
     }
@@ -1057,6 +1127,7 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
       g3.C = grad_W; g3.ldc = H; g3.M = V; g3.N = H; g3.K = rows;
       g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32; g3.k_splits = 1;
       scale_output(g3, gsc);
+      pkr.limit(g3, 1, r0);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }

@@ -244,8 +244,8 @@ hipError_t launch_count_targets(const int32_t* targets, int64_t n, int64_t V,
 // row_scale: per-row gradient factors, or nullptr for the reduction's scale.
 // grad_shift > 0: the gradient is stored times 2^grad_shift (times row_scale
 // when given) and without the reduction's scale, which the consumer applies.
-// pk: rows past pk.live are skipped and row r's loss goes to
-// loss_rows[pk.map[r]] (row packing).
+// pk: rows past pk.live are skipped, and row r's loss goes to
+// loss_rows[pk.map[r]] and its factor is row_scale[pk.map[r]] (row packing).
 hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* grad, int64_t ldg,
                          int64_t rows, int64_t V, int64_t pad_cols, const int32_t* targets,
                          int32_t ign, const WsHeader* hdr, float* loss_rows,
@@ -276,7 +276,8 @@ hipError_t launch_shard_stats_counted(int dtype, const void* Z, int64_t rows, in
 hipError_t launch_shard_grad(int dtype, void* Z, int64_t ldz, int64_t rows, int64_t V_local,
                              int64_t pad_cols, int64_t vocab_start, int64_t V_global,
                              const int32_t* targets, int32_t ign, const float* lse,
-                             const WsHeader* hdr, int grad_shift, hipStream_t s);
+                             const WsHeader* hdr, int grad_shift, hipStream_t s,
+                             RowPack pk = RowPack{nullptr, nullptr, 0});
 hipError_t launch_combine_stats(const float* ms, const float* ss, const float* ts, int64_t P,
                                 int64_t N, const int32_t* targets, int32_t ign, int64_t V_global,
                                 float* lse, float* loss_rows, hipStream_t s);

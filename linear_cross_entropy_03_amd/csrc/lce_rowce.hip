@@ -266,15 +266,17 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
   if (sc.n > 0) self_scale = count_finish<kThreads>(sc, cnt);
   if constexpr (kRes > 0) zt = E::load(&zt_bits);
-  if (tid == 0) loss_rows[pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row] = valid ? (lse - zt) : 0.0f;
+  // Loss and per-row factor belong to the original row (packed chunks).
+  const int64_t orow = pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row;
+  if (tid == 0) loss_rows[orow] = valid ? (lse - zt) : 0.0f;
   if (G == nullptr) return;
 
   // The gradient factor: the reduction's, or a per-row one (sequence-level
   // losses such as DPO weight each token row separately); with grad_shift
   // the reduction's scale is left to the consumer.
   const float c = !valid ? 0.0f
-                  : grad_shift > 0 ? __builtin_ldexpf(row_scale != nullptr ? row_scale[row] : 1.0f, grad_shift)
-                  : (row_scale != nullptr ? row_scale[row] : (sc.n > 0 ? self_scale : hdr->scale));
+                  : grad_shift > 0 ? __builtin_ldexpf(row_scale != nullptr ? row_scale[orow] : 1.0f, grad_shift)
+                  : (row_scale != nullptr ? row_scale[orow] : (sc.n > 0 ? self_scale : hdr->scale));
   T* g = G + row * ldg;
   uint4* gv = reinterpret_cast<uint4*>(g + rs.head);
   auto grad_of = [&](float x, int64_t v) -> float {
@@ -421,12 +423,13 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
     float M, S;
     block_lse_parts<kThreads>(lm, ls, red0, red1, M, S);
     const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
-    if (tid == 0) loss_rows[pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row] = valid ? (lse - zt) : 0.0f;
+    const int64_t orow = pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row;
+    if (tid == 0) loss_rows[orow] = valid ? (lse - zt) : 0.0f;
 
     if (G != nullptr) {
       const float c = !valid ? 0.0f
-                      : grad_shift > 0 ? __builtin_ldexpf(row_scale != nullptr ? row_scale[row] : 1.0f, grad_shift)
-                      : (row_scale != nullptr ? row_scale[row] : hdr->scale);
+                      : grad_shift > 0 ? __builtin_ldexpf(row_scale != nullptr ? row_scale[orow] : 1.0f, grad_shift)
+                      : (row_scale != nullptr ? row_scale[orow] : hdr->scale);
       const int yt = valid ? y : -1;
       T* g = G + row * ldg;
       uint4* gv = reinterpret_cast<uint4*>(g + head);
@@ -715,16 +718,18 @@ __global__ __launch_bounds__(kThreads) void k_shard_grad(T* Z, int64_t ldz, int6
                                                          const int32_t* __restrict__ targets,
                                                          int32_t ign, const float* __restrict__ lse,
                                                          const WsHeader* __restrict__ hdr,
-                                                         int grad_shift) {
+                                                         int grad_shift, RowPack pk) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
+  // Packed chunks: rows past the live count do not exist (whole workgroup).
+  if (pk.live != nullptr && row >= static_cast<int64_t>(*pk.live) - pk.base) return;
   T* z = Z + row * ldz;
   const int32_t y = targets[row];
   const bool valid = (y != ign) && y >= 0 && static_cast<int64_t>(y) < Vg;
   const float c = !valid ? 0.0f : grad_shift > 0 ? __builtin_ldexpf(1.0f, grad_shift) : hdr->scale;
-  const float L = lse[row];
+  const float L = lse[pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row];
   const int64_t jt = valid ? static_cast<int64_t>(y) - v0 : -1;  // may fall outside the shard
   auto grad_of = [&](float x, int64_t j) -> float {
     if (!valid) return 0.0f;
@@ -752,19 +757,19 @@ __global__ __launch_bounds__(kThreads) void k_shard_grad(T* Z, int64_t ldz, int6
 hipError_t launch_shard_grad(int dtype, void* Z, int64_t ldz, int64_t rows, int64_t V_local,
                              int64_t pad_cols, int64_t vocab_start, int64_t V_global,
                              const int32_t* targets, int32_t ign, const float* lse,
-                             const WsHeader* hdr, int grad_shift, hipStream_t s) {
+                             const WsHeader* hdr, int grad_shift, hipStream_t s, RowPack pk) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(rows));
   if (dtype == 1)
     hipLaunchKernelGGL((k_shard_grad<uint16_t, 256>), grid, dim3(256), 0, s, static_cast<uint16_t*>(Z),
                        ldz, V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr,
-                       grad_shift);
+                       grad_shift, pk);
   else if (dtype == 2)
     hipLaunchKernelGGL((k_shard_grad<Half, 256>), grid, dim3(256), 0, s, static_cast<Half*>(Z), ldz,
-                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr, grad_shift);
+                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr, grad_shift, pk);
   else
     hipLaunchKernelGGL((k_shard_grad<float, 256>), grid, dim3(256), 0, s, static_cast<float*>(Z), ldz,
-                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr, grad_shift);
+                       V_local, pad_cols, vocab_start, V_global, targets, ign, lse, hdr, grad_shift, pk);
   return hipGetLastError();
 }
 

@@ -110,6 +110,49 @@ def test_shard_backward_given_lse(B, dtype):
     check_max_rel(to_host(gb), ref[2], t["grad"], "grad_bias shard")
 
 
+@pytest.mark.parametrize("chunk", [128, 0])
+def test_shard_backward_row_packing(B, chunk):
+    """The shard backward over packed rows (40% ignored, several chunks of
+    which the last ones are empty) against the oracle's shard backward and
+    against the same call with packing off (grad_X rows bitwise equal outside
+    the last chunk, the shard's grad_W and grad_bias up to float32 summation
+    order)."""
+    import torch
+    N, H, V = 900, 64, 6000
+    inp = synth.make_flce_inputs(N, H, V, "bf16", bias_std=0.1, ignore_frac=0.4, seed=35)
+    X, W, b, y = oracle_inputs(inp)
+    lse32 = O.logsumexp_rows(X @ W.T + b).astype(np.float32)
+    a, c = 1500, 5000
+    ref = O.flce_shard_backward(X, W[a:c], y, a, V, lse32.astype(np.float64), bias_shard=b[a:c],
+                                reduction="sum")
+    args = (to_dev(inp["X"], "bf16"), to_dev(np.ascontiguousarray(inp["W"][a:c]), "bf16"),
+            to_dev(y.astype(np.int32), "i32"), torch.from_numpy(lse32).cuda(), a, V)
+    kw = dict(bias_shard=to_dev(np.ascontiguousarray(inp["bias"][a:c]), "bf16"), reduction="sum",
+              chunk_rows=chunk)
+    out = {}
+    was = B.flce_set_row_packing(True)
+    try:
+        for pack in (True, False):
+            B.flce_set_row_packing(pack)
+            say("shard backward packing", pack, "chunk", chunk)
+            res = B.flce_shard_backward(*args, **kw)
+            torch.cuda.synchronize()
+            out[pack] = [to_host(t) for t in res]
+    finally:
+        B.flce_set_row_packing(was)
+    t = TOL["bf16"]
+    for name, g, r in zip(("grad_X partial", "grad_W shard", "grad_bias shard"), out[True], ref):
+        check_max_rel(g, r, t["grad"], name)
+    assert np.all(out[True][0][y == -100] == 0.0)
+    cc = chunk or B.flce_plan(N, H, c - a, B.BF16)[0]
+    live_rows = np.flatnonzero(y != -100)
+    same = np.ones(N, dtype=bool)
+    same[live_rows[(-(-N // cc) - 1) * cc:]] = False
+    assert np.array_equal(out[True][0][same], out[False][0][same])
+    for g, r, name in zip(out[True], out[False], ("grad_X", "grad_W", "grad_bias")):
+        check_max_rel(g, r, 1e-5, name + " packed vs plain")
+
+
 @pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
 def test_combine_against_oracle(B, reduction):
     import torch
