@@ -417,7 +417,10 @@ def bench_distill(torch, B, X, W, y, cfg, n_rows=8192, reps=3):
     gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm"))
     B.flce_timing_reset()
     ms = a.elapsed_time(b) / reps
-    flops = 8.0 * N * H * V
+    # Two logits GEMMs and the two gradient products over the rows they run on
+    # (the non-ignored ones when packed: the teacher here is as wide as the student).
+    live = rows_through_products(B, y[:N])
+    flops = 8.0 * live * H * V
     out = {
         "workload": f"JSD distillation, llama8b_head_bf16 student and a rolled teacher (N {N}, "
                     f"H {H}, V {V}, T 2, {cfg['reduction']})",
@@ -425,7 +428,7 @@ def bench_distill(torch, B, X, W, y, cfg, n_rows=8192, reps=3):
         "gemm_tflops": flops / (gemm_ms / reps * 1e-3) / 1e12,
         "jsd_row_kernel_ms_per_call": row_ms / reps,
         # bytes moved by the row kernel's three passes: 6 row reads + 1 write per element
-        "jsd_row_kernel_GBps": 7.0 * N * ((V + 7) // 8 * 8) * 2 / (row_ms / reps * 1e-3) / 1e9,
+        "jsd_row_kernel_GBps": 7.0 * live * ((V + 7) // 8 * 8) * 2 / (row_ms / reps * 1e-3) / 1e9,
         "loss": float(loss.item()),
     }
     del Xt, Wt, gW, ws

@@ -345,8 +345,9 @@ int flce_check_device_error(const void* workspace, void* stream);
 /*
  * Row packing in the FLCE calls with 16-bit inputs (flce_forward_backward,
  * its _ex variant, each head of the multi-head calls, flce_shard_backward and
- * both passes of flce_dpo_forward_backward; not flce_shard_stats, whose
- * statistics cover every row, nor the distillation call). A row whose
+ * both passes of flce_dpo_forward_backward, and flce_jsd_forward_backward
+ * when chunk_rows x H_t teacher elements fit the student's split-K buffer;
+ * not flce_shard_stats, whose statistics cover every row). A row whose
  * target is ignore_index has zero loss and a zero dlogits row (the definition
  * at the top of this header), so it adds nothing to grad_W or grad_bias and
  * its grad_X row is zero. The chunk loop therefore lists the other rows on

@@ -297,8 +297,8 @@ struct Packer {
   // their grad_X rows of gx_row_bytes bytes.
   int setup(const Plan& p, char* ws, WsHeader* hdr, const int32_t* targets, int64_t N,
             int64_t V_valid, int32_t ign, float* loss_rows, void* grad_X, int64_t gx_row_bytes,
-            hipStream_t s) {
-    on = g_row_packing && p.pack_ok && N > 0;
+            hipStream_t s, bool allow = true) {
+    on = allow && g_row_packing && p.pack_ok && N > 0;
     if (!on) return FLCE_OK;
     map = reinterpret_cast<int32_t*>(ws + p.off_map);
     ptgt = reinterpret_cast<const int32_t*>(ws + p.off_ptgt);
@@ -939,23 +939,42 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
   }));
   if (N == 0 && grad_W_s)
     LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W_s, V * H_s, 0.0f, s); }));
+  // Packed rows (as in flce_chunks) when the teacher's gathered hidden states
+  // fit the split-K partial buffer, which is free until the grad_X product.
+  const size_t split_bytes = p.off_map - p.off_split;
+  const bool teacher_fits = static_cast<size_t>(p.chunk) * static_cast<size_t>(H_t) * e <= split_bytes;
+  Packer pkr;
+  st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows, grad_X_s,
+                 H_s * static_cast<int64_t>(sizeof(float)), s, teacher_fits);
+  if (st != FLCE_OK) return st;
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
-    const char* Xs_c = static_cast<const char*>(X_s) + static_cast<size_t>(r0) * H_s * e;
+    const RowPack pk = pkr.chunk(r0);
+    const char* Xs_c;
+    st = pkr.rows_of(X_s, r0, rows, H_s, e, s, &Xs_c);
+    if (st != FLCE_OK) return st;
     const char* Xt_c = static_cast<const char*>(X_t) + static_cast<size_t>(r0) * H_t * e;
+    if (pkr.on) {
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_gather_rows(X_t, H_t * static_cast<int64_t>(e), rows, pk, split_buf, s);
+      }));
+      Xt_c = reinterpret_cast<const char*>(split_buf);
+    }
     GemmDesc gs{};
     gs.A = Xs_c; gs.lda = H_s; gs.a_kmajor = true;
     gs.B = W_s; gs.ldb = H_s; gs.b_kmajor = true;
     gs.C = zs; gs.ldc = p.ldz; gs.M = rows; gs.N = V; gs.K = H_s;
     gs.epilogue = kEpiLogits; gs.k_splits = 1;
+    pkr.limit(gs, 0, r0);
     LCE_TRY(timed(kKindLogits, s, [&] { return gemm(gs, s); }));
     GemmDesc gt = gs;
     gt.A = Xt_c; gt.lda = H_t; gt.B = W_t; gt.ldb = H_t; gt.C = zt; gt.K = H_t;
     LCE_TRY(timed(kKindLogits, s, [&] { return gemm(gt, s); }));
     LCE_TRY(timed(kKindRowCE, s, [&] {
-      return launch_row_jsd(dtype, zs, zt, p.ldz, rows, V, p.ldz - V, inv_tau, targets + r0,
-                            ignore_index, hdr, loss_rows + r0, gsc.row_shift, s);
+      return launch_row_jsd(dtype, zs, zt, p.ldz, rows, V, p.ldz - V, inv_tau,
+                            (pkr.on ? pkr.ptgt : targets) + r0, ignore_index, hdr,
+                            pkr.on ? loss_rows : loss_rows + r0, gsc.row_shift, s, pk);
     }));
     if (grad_X_s) {
       GemmDesc g2{};
@@ -964,15 +983,19 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
       g2.M = rows; g2.N = H_s; g2.K = V;
       g2.epilogue = kEpiStoreF32;
       scale_output(g2, gsc);
-      float* out = grad_X_s + static_cast<size_t>(r0) * H_s;
-      if (p.dx_splits > 1) {
-        g2.C = split_buf; g2.ldc = H_s; g2.k_splits = p.dx_splits; g2.split_stride = rows * H_s;
+      pkr.limit(g2, 0, r0);
+      float* out = grad_X_s + (pkr.on ? 0 : static_cast<size_t>(r0) * H_s);
+      const int splits = (pkr.on && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
+      if (splits > 1) {
+        g2.C = split_buf; g2.ldc = H_s; g2.k_splits = splits; g2.split_stride = rows * H_s;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, p.dx_splits, rows * H_s, rows, H_s, H_s, out, FLCE_F32, false, s);
+          return launch_splitk_reduce(split_buf, splits, rows * H_s, rows, H_s, H_s, out, FLCE_F32,
+                                      false, s, pk);
         }));
       } else {
         g2.C = out; g2.ldc = H_s; g2.k_splits = 1;
+        if (pkr.on) g2.row_map = pk.map;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
       }
     }
@@ -983,6 +1006,7 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
       g3.C = grad_W_s; g3.ldc = H_s; g3.M = V; g3.N = H_s; g3.K = rows;
       g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32; g3.k_splits = 1;
       scale_output(g3, gsc);
+      pkr.limit(g3, 1, r0);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }

@@ -283,7 +283,8 @@ hipError_t launch_combine_stats(const float* ms, const float* ss, const float* t
                                 float* lse, float* loss_rows, hipStream_t s);
 hipError_t launch_row_jsd(int dtype, void* S, const void* Tt, int64_t ld, int64_t rows, int64_t V,
                           int64_t pad_cols, float inv_tau, const int32_t* targets, int32_t ign,
-                          const WsHeader* hdr, float* loss_rows, int grad_shift, hipStream_t s);
+                          const WsHeader* hdr, float* loss_rows, int grad_shift, hipStream_t s,
+                          RowPack pk = RowPack{nullptr, nullptr, 0});
 hipError_t launch_dpo(const float* loss_rows, int64_t P, int64_t S, const float* ref, float beta,
                       double* logp, float* loss, float* pair_loss, float* row_scale, hipStream_t s);
 hipError_t launch_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ign,

@@ -823,11 +823,14 @@ __global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t
                                                       int64_t pad_cols, float inv_tau,
                                                       const int32_t* __restrict__ targets,
                                                       int32_t ign, const WsHeader* __restrict__ hdr,
-                                                      float* __restrict__ loss_rows, int grad_shift) {
+                                                      float* __restrict__ loss_rows, int grad_shift,
+                                                      RowPack pk) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
   __shared__ float red0[kThreads / 64], red1[kThreads / 64];
   const int64_t row = blockIdx.x;
+  // Packed chunks: rows past the live count do not exist (whole workgroup).
+  if (pk.live != nullptr && row >= static_cast<int64_t>(*pk.live) - pk.base) return;
   const int tid = threadIdx.x;
   T* s = S + row * ld;
   const T* t = Tt + row * ld;
@@ -898,7 +901,7 @@ __global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t
   __syncthreads();
   const float L = block_sum<kThreads>(loss, red0);
   const float Gb = block_sum<kThreads>(gbar, red1);
-  if (tid == 0) loss_rows[row] = valid ? L : 0.0f;
+  if (tid == 0) loss_rows[pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row] = valid ? L : 0.0f;
 
   // Pass 3: the student gradient, in place.
   const float c = !valid ? 0.0f
@@ -933,21 +936,22 @@ __global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t
 
 hipError_t launch_row_jsd(int dtype, void* S, const void* Tt, int64_t ld, int64_t rows, int64_t V,
                           int64_t pad_cols, float inv_tau, const int32_t* targets, int32_t ign,
-                          const WsHeader* hdr, float* loss_rows, int grad_shift, hipStream_t s) {
+                          const WsHeader* hdr, float* loss_rows, int grad_shift, hipStream_t s,
+                          RowPack pk) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(rows));
   if (dtype == 1)
     hipLaunchKernelGGL((k_row_jsd<uint16_t, 1024>), grid, dim3(1024), 0, s, static_cast<uint16_t*>(S),
                        static_cast<const uint16_t*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
-                       loss_rows, grad_shift);
+                       loss_rows, grad_shift, pk);
   else if (dtype == 2)
     hipLaunchKernelGGL((k_row_jsd<Half, 1024>), grid, dim3(1024), 0, s, static_cast<Half*>(S),
                        static_cast<const Half*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
-                       loss_rows, grad_shift);
+                       loss_rows, grad_shift, pk);
   else
     hipLaunchKernelGGL((k_row_jsd<float, 1024>), grid, dim3(1024), 0, s, static_cast<float*>(S),
                        static_cast<const float*>(Tt), ld, V, pad_cols, inv_tau, targets, ign, hdr,
-                       loss_rows, grad_shift);
+                       loss_rows, grad_shift, pk);
   return hipGetLastError();
 }
 

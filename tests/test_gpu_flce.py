@@ -365,6 +365,35 @@ def test_row_packing_multihead(packing):
     assert np.all(out[True][1][(yk == -100).all(axis=0)] == 0.0)
 
 
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_ignore_index_inside_vocabulary_bf16(B, reduction):
+    """ignore_index 7, a legal class id: rows with target 7 are ignored (and
+    packed out), the other rows keep their targets; against the oracle with
+    the same ignore_index."""
+    import torch
+    N, H, V = 700, 136, 1500
+    inp = synth.make_flce_inputs(N, H, V, "bf16", bias_std=0.1, ignore_frac=0.0, seed=46)
+    y = inp["targets"].copy()
+    y[np.random.default_rng(47).choice(N, 120, replace=False)] = 7
+    X, W, b, _ = oracle_inputs(inp)
+    ref_loss, ref_g, _ = O.flce(X, W, y, bias=b, ignore_index=7, reduction=reduction)
+    say("flce bf16 ignore_index 7", reduction)
+    loss, gX, gW, gb = B.flce_forward_backward(
+        to_dev(inp["X"], "bf16"), to_dev(inp["W"], "bf16"), to_dev(y, "i32"),
+        bias=to_dev(inp["bias"], "bf16"), ignore_index=7, reduction=reduction, chunk_rows=256)
+    torch.cuda.synchronize()
+    t = TOL["bf16"]
+    if reduction == "none":
+        check_max_rel(to_host(loss), ref_loss, t["loss"], "loss rows")
+        assert np.all(to_host(loss)[y == 7] == 0.0)
+    else:
+        check_scalar(to_host(loss), ref_loss, t["loss"])
+    check_max_rel(to_host(gX), ref_g["X"], t["grad"], "grad_X")
+    assert np.all(to_host(gX)[y == 7] == 0.0)
+    check_max_rel(to_host(gW), ref_g["W"], t["grad"], "grad_W")
+    check_max_rel(to_host(gb), ref_g["bias"], t["grad"], "grad_bias")
+
+
 def test_row_packing_all_ignored_and_bad_targets_bf16(B):
     """16-bit inputs take the packed loop: with every row ignored no row is
     live (loss 0, all gradients 0, including grad_W's first-chunk store);
@@ -505,6 +534,26 @@ def test_jsd_distillation_against_oracle(B, dtype, reduction, temperature, chunk
     check_max_rel(gW, ref_g["W"], t["grad"], "grad_W student")
     masked = s_inp["targets"] == -100
     assert np.all(gX[masked] == 0.0)
+
+
+def test_jsd_wide_teacher_bf16(B):
+    """A teacher much wider than the student (H 520 against 64): its gathered
+    rows do not fit the student's split-K buffer, so the call runs unpacked;
+    against the oracle."""
+    N, Hs, Ht, V = 300, 64, 520, 900
+    s_inp = synth.make_flce_inputs(N, Hs, V, "bf16", w_std=0.08, ignore_frac=0.2, seed=62)
+    t_inp = synth.make_flce_inputs(N, Ht, V, "bf16", w_std=0.05, ignore_frac=0.0, seed=63)
+    say("jsd wide teacher")
+    loss, gX, gW = _run_jsd(B, s_inp, t_inp, 1.0, "mean", 128)
+    f = lambda a: np.asarray(a, np.float64)
+    ref_loss, ref_g, _ = O.flce_jsd(f(s_inp["X_f32"]), f(s_inp["W_f32"]), f(t_inp["X_f32"]),
+                                    f(t_inp["W_f32"]), s_inp["targets"], temperature=1.0,
+                                    reduction="mean")
+    t = TOL["bf16"]
+    check_scalar(loss, ref_loss, t["loss"], "JSD")
+    check_max_rel(gX, ref_g["X"], t["grad"], "grad_X student")
+    check_max_rel(gW, ref_g["W"], t["grad"], "grad_W student")
+    assert np.all(gX[s_inp["targets"] == -100] == 0.0)
 
 
 def test_jsd_teacher_equal_to_student_is_exactly_zero(B):
