@@ -1043,21 +1043,24 @@ hipError_t launch_shift_labels(const int32_t* labels, int64_t B, int64_t S, int3
 // ------------------------------------------------------------ loss reduce
 
 // Sum of per-row losses in float64, in a fixed order independent of how the
-// rows were chunked; mean divides by the valid-row count.
+// rows were chunked (lane-strided partial sums, a butterfly within each wave,
+// the 16 wave sums in wave order); mean divides by the valid-row count. One
+// barrier: the launch is latency-bound, so the tree through LDS is kept short.
 __global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ rows, int64_t n,
                                                       const WsHeader* __restrict__ hdr,
                                                       int reduction, float* __restrict__ out) {
-  __shared__ double part[1024];
+  __shared__ double wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += 1024) acc += static_cast<double>(rows[i]);
-  part[threadIdx.x] = acc;
+  for (int64_t i = tid; i < n; i += 1024) acc += static_cast<double>(rows[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) wsum[w] = acc;
   __syncthreads();
-  for (int w = 512; w > 0; w >>= 1) {
-    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    double total = part[0];
+  if (tid == 0) {
+    double total = 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) total += wsum[k];
     if (reduction == 2) total = hdr->n_valid > 0 ? total / static_cast<double>(hdr->n_valid) : 0.0;
     out[0] = static_cast<float>(total);
   }
