@@ -729,11 +729,13 @@ def main():
                     "steps": reps}
     # One chunk of logits, per-row / per-vocabulary scratch, the grad_X K-split
     # partials (the last packed chunk splits in two) and, for 16-bit inputs,
-    # the packed-row lists and the chunk's gathered hidden states.
+    # the packed-row lists, the chunk's gathered hidden states and W^T.
     max_splits = max(splits, 2 if (e == 2 and splits == 1 and V // 2 >= 2048) else splits)
     extra_bound = (chunk * ((V + 7) // 8 * 8) * e + (N + V) * 16 + 4096
                    + (max_splits * chunk * H * 4 if (max_splits > 1 or e == 2) else 0)
-                   + ((chunk * H * e + 8 * N + 4096) if e == 2 else 0))
+                   + ((chunk * H * e + 8 * N + 4096) if e == 2 else 0)
+                   # the transposed head for grad_X (16-bit, H <= chunk)
+                   + ((V + 63) // 64 * 64 * H * e if (e == 2 and H <= chunk) else 0))
     step_flops = 6.0 * n_live * H * V
     result = {
         "metric": "FLCE fwd+bwd tokens/s + % bf16 MFMA peak at H4096 V128256; peak HBM bytes",

@@ -96,6 +96,11 @@ struct Plan {
   // [chunk, H]. pack_ok is false for float32 inputs (no buffers).
   bool pack_ok;
   size_t off_map, off_ptgt, off_bcnt, off_xs;
+  // Transposed head (16-bit, H <= chunk): W^T [H, ldw], ldw = round_up(V, 64),
+  // the k-major B operand of the grad_X product.
+  bool wt;
+  int64_t ldw;
+  size_t off_wt;
   size_t total;
 };
 
@@ -177,6 +182,14 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
     p->off_xs = off;
     off += align_up(static_cast<size_t>(chunk) * static_cast<size_t>(H) * e);
   }
+  // With W transposed, grad_X = dZ W has both operands k-major and runs on
+  // the logits' pipeline (11% faster than reading W n-major); it costs one
+  // copy of W per call and W's size in workspace, taken only when that is at
+  // most one chunk of logits (H <= chunk).
+  p->wt = is16(dtype) && H <= chunk;
+  p->ldw = round_up(V, 64);
+  p->off_wt = off;
+  if (p->wt) off += align_up(static_cast<size_t>(H) * static_cast<size_t>(p->ldw) * e);
   p->total = off;
   return true;
 }
@@ -335,6 +348,22 @@ struct Packer {
   }
 };
 
+// The B operand of the grad_X product dZ_c W: the transposed head W^T
+// (k-major, written into the workspace once per call) when the plan holds
+// it, else W itself (n-major).
+void grad_x_head(const Plan& p, const void* W, int64_t H, char* ws, GemmDesc& g2) {
+  if (p.wt) {
+    g2.B = ws + p.off_wt; g2.ldb = p.ldw; g2.b_kmajor = true;
+  } else {
+    g2.B = W; g2.ldb = H; g2.b_kmajor = false;
+  }
+}
+int transpose_head(const Plan& p, const void* W, int64_t V, int64_t H, char* ws, hipStream_t s) {
+  if (!p.wt) return FLCE_OK;
+  LCE_TRY(timed(kKindOther, s, [&] { return launch_transpose16(W, V, H, ws + p.off_wt, p.ldw, s); }));
+  return FLCE_OK;
+}
+
 // The chunk loop of FLCE over all N rows for one head: logits GEMM, row CE
 // (loss rows, dZ in place), bias column sums, grad_X (stored, or added to
 // what is there when accum_gx), grad_W (stored on the first chunk, added
@@ -373,6 +402,10 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
   const bool pack = pkr.on;
   const int32_t* ptgt = pkr.ptgt;
 
+  if (grad_X != nullptr && N > 0) {
+    st = transpose_head(p, W, V, H, ws, s);
+    if (st != FLCE_OK) return st;
+  }
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
@@ -408,7 +441,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
     if (grad_X) {
       GemmDesc g2{};
       g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
-      g2.B = W; g2.ldb = H; g2.b_kmajor = false;
+      grad_x_head(p, W, H, ws, g2);
       g2.M = rows; g2.N = H; g2.K = V;
       scale_output(g2, gsc);
       live(g2, 0);
@@ -828,6 +861,10 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
   st = pkr.setup(p, ws, hdr, targets, N, V_global, ignore_index, nullptr, grad_X,
                  H * static_cast<int64_t>(sizeof(float)), s);
   if (st != FLCE_OK) return st;
+  if (grad_X != nullptr && N > 0) {
+    st = transpose_head(p, W_shard, V_local, H, ws, s);
+    if (st != FLCE_OK) return st;
+  }
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
@@ -857,7 +894,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
     if (grad_X) {
       GemmDesc g2{};
       g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
-      g2.B = W_shard; g2.ldb = H; g2.b_kmajor = false;
+      grad_x_head(p, W_shard, H, ws, g2);
       g2.M = rows; g2.N = H; g2.K = V_local;
       g2.epilogue = kEpiStoreF32;
       scale_output(g2, gsc);
@@ -947,6 +984,10 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
   st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows, grad_X_s,
                  H_s * static_cast<int64_t>(sizeof(float)), s, teacher_fits);
   if (st != FLCE_OK) return st;
+  if (grad_X_s != nullptr && N > 0) {
+    st = transpose_head(p, W_s, V, H_s, ws, s);
+    if (st != FLCE_OK) return st;
+  }
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
@@ -979,7 +1020,7 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
     if (grad_X_s) {
       GemmDesc g2{};
       g2.A = zs; g2.lda = p.ldz; g2.a_kmajor = true;
-      g2.B = W_s; g2.ldb = H_s; g2.b_kmajor = false;
+      grad_x_head(p, W_s, H_s, ws, g2);
       g2.M = rows; g2.N = H_s; g2.K = V;
       g2.epilogue = kEpiStoreF32;
       scale_output(g2, gsc);
@@ -1088,6 +1129,10 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
   st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows, grad_X,
                  H * static_cast<int64_t>(sizeof(float)), s);
   if (st != FLCE_OK) return st;
+  if (grad_X != nullptr && N > 0) {
+    st = transpose_head(p, W, V, H, ws, s);
+    if (st != FLCE_OK) return st;
+  }
   const int32_t* tg = pkr.on ? pkr.ptgt : targets;
   // Pass 1: the CE row losses of every row (= minus the token log-probabilities).
   const char* Xc = nullptr;
@@ -1124,7 +1169,7 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
     if (grad_X) {
       GemmDesc g2{};
       g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
-      g2.B = W; g2.ldb = H; g2.b_kmajor = false;
+      grad_x_head(p, W, H, ws, g2);
       g2.M = rows; g2.N = H; g2.K = V;
       g2.epilogue = kEpiStoreF32;
       scale_output(g2, gsc);

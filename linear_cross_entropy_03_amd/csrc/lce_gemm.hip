@@ -931,6 +931,16 @@ template <int kTy>
 static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
   if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits)
     return launch_ring<true, true, kEpiLogits, kTy, 4>(d, s);
+  // grad_X against the transposed head (both operands k-major): the ring on
+  // 4 waves of 128 x 128, like the logits.
+  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiStoreF32)
+    return launch_ring<true, true, kEpiStoreF32, kTy, 4>(d, s);
+  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiAccumF32)
+    return launch_ring<true, true, kEpiAccumF32, kTy, 4>(d, s);
+  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiStore16)
+    return launch_ring<true, true, kEpiStore16, kTy, 4>(d, s);
+  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiAccum16)
+    return launch_ring<true, true, kEpiAccum16, kTy, 4>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
     return launch_mfma_kernel<true, false, kEpiStoreF32, 4, kTy>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)

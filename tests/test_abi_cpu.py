@@ -74,7 +74,8 @@ def test_row_packing_switch_and_workspace(B):
     """The packing switch returns the previous setting and does not change the
     workspace size; 16-bit plans hold the packing buffers (row map and packed
     targets, 4 bytes per row each, the chunk's gathered rows, one split-K
-    partial at least), float32 plans none of them."""
+    partial at least, and the transposed head when H <= chunk), float32 plans
+    none of them."""
     was = B.flce_set_row_packing(False)
     try:
         assert B.flce_set_row_packing(True) is False
@@ -88,8 +89,14 @@ def test_row_packing_switch_and_workspace(B):
         assert f32 >= 256 + N * 4 + C * ldz * 4
         assert f32 < 256 + N * 4 + C * ldz * 4 + 4 * 256
         base16 = 256 + N * 4 + C * ldz * 2
-        assert on >= base16 + C * H * 4 + 2 * N * 4 + C * H * 2
-        assert on < base16 + C * H * 4 + 2 * N * 4 + C * H * 2 + 16 * 256
+        # ... and, as H <= chunk, the transposed head W^T [H, round_up(V, 64)].
+        wt = H * ((V + 63) // 64 * 64) * 2
+        assert on >= base16 + C * H * 4 + 2 * N * 4 + C * H * 2 + wt
+        assert on < base16 + C * H * 4 + 2 * N * 4 + C * H * 2 + wt + 16 * 256
+        # A chunk shorter than H leaves the head untransposed.
+        short = B.flce_workspace_bytes(N, H, V, B.BF16, 256)
+        base = 256 + N * 4 + 256 * ldz * 2 + 256 * H * 4 + 2 * N * 4 + 256 * H * 2
+        assert base <= short < base + 16 * 256
     finally:
         B.flce_set_row_packing(was)
 
