@@ -133,7 +133,8 @@ def cpu_baseline(inp, cfg, target_s):
 
 KERNEL_KINDS = {  # kernel-name fragment -> kind reported by the timing hooks
     "k_ring<true, true, 0": "logits_gemm",
-    "k_gemm2<true, false, 1": "grad_x_gemm",
+    "k_gemm2<true, false, 1": "grad_x_gemm",     # W read n-major (chunk shorter than H)
+    "k_ring<true, true, 1": "grad_x_gemm",       # against the transposed head
     "k_ring<false, false, 1": "grad_w_gemm",
     "k_ring<false, false, 2": "grad_w_gemm",
     "k_row_ce": "row_ce",
