@@ -110,7 +110,9 @@ int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
  *   grad_bias[V] float32 or NULL (must be NULL when bias is NULL)
  *   workspace of at least flce_workspace_bytes(N, H, V, dtype, chunk_rows)
  *   chunk_rows: rows per chunk, 0 = planner's choice; peak scratch is about
- *   chunk_rows * V elements of the input type.
+ *   chunk_rows * V elements of the input type, plus, for 16-bit inputs with
+ *   H <= chunk_rows, a transposed copy of W (V * H elements) that the grad_X
+ *   product reads k-major; a chunk shorter than H leaves W untransposed.
  * Results do not depend on chunk_rows except for the rounding order of grad_W
  * and grad_bias; the loss is bitwise independent of it.
  */
