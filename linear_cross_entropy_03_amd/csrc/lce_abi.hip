@@ -90,7 +90,8 @@ struct Plan {
   int last_splits;  // K-splits of the last chunk's grad_X GEMM when packed
   size_t off_rows;  // per-row losses [N] float
   size_t off_chunk; // chunk buffer [chunk, ldz]
-  size_t off_split; // split-K partials [dx_splits, chunk, H] float (dx_splits > 1)
+  size_t off_split; // split-K partials [S, chunk, H] float, S = the largest split used
+                    // (present when S > 1, and always for 16-bit inputs)
   // Row packing (16-bit inputs): packed-row map [N], packed targets [N], the
   // pack kernels' block counts, and the chunk's gathered hidden states
   // [chunk, H]. pack_ok is false for float32 inputs (no buffers).
