@@ -276,6 +276,19 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
                         int reduction, const float* row_lse, float* grad_X, float* grad_W_shard,
                         float* grad_bias_shard, void* workspace, size_t workspace_bytes,
                         int64_t chunk_rows, void* stream);
+/*
+ * As flce_shard_backward, with the gradients in the 16-bit input type when
+ * grad_dtype equals dtype (the rounding rules of flce_forward_backward_ex:
+ * float32 products rounded once per chunk, grad_W_shard and grad_bias_shard
+ * read, added in float32 and rounded at every chunk after the first);
+ * FLCE_F32 is flce_shard_backward. FLCE_E_INVALID_ARG for another grad_dtype.
+ */
+int flce_shard_backward_ex(const void* X, const void* W_shard, const void* bias_shard,
+                           const int32_t* targets, int64_t N, int64_t H, int64_t V_local,
+                           int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
+                           int reduction, const float* row_lse, int grad_dtype, void* grad_X,
+                           void* grad_W_shard, void* grad_bias_shard, void* workspace,
+                           size_t workspace_bytes, int64_t chunk_rows, void* stream);
 
 /*
  * Fused linear Jensen-Shannon distillation (the knowledge-distillation loss
@@ -300,6 +313,14 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
                               float temperature, float* loss, float* grad_X_s, float* grad_W_s,
                               void* workspace, size_t workspace_bytes, int64_t chunk_rows,
                               void* stream);
+/* As flce_jsd_forward_backward, with the student's gradients in the 16-bit
+ * input type when grad_dtype equals dtype (rounding as flce_forward_backward_ex). */
+int flce_jsd_forward_backward_ex(const void* X_s, const void* W_s, const void* X_t, const void* W_t,
+                                 const int32_t* targets, int64_t N, int64_t H_s, int64_t H_t,
+                                 int64_t V, int dtype, int32_t ignore_index, int reduction,
+                                 float temperature, int grad_dtype, float* loss, void* grad_X_s,
+                                 void* grad_W_s, void* workspace, size_t workspace_bytes,
+                                 int64_t chunk_rows, void* stream);
 
 /*
  * Fused linear DPO (the alignment loss the Megatron integration page lists
@@ -325,6 +346,14 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
                               float* loss, float* pair_loss, float* grad_X, float* grad_W,
                               void* workspace, size_t workspace_bytes, int64_t chunk_rows,
                               void* stream);
+/* As flce_dpo_forward_backward, with grad_X and grad_W in the 16-bit input
+ * type when grad_dtype equals dtype (rounding as flce_forward_backward_ex). */
+int flce_dpo_forward_backward_ex(const void* X, const void* W, const int32_t* targets,
+                                 int64_t n_pairs, int64_t seq_len, int64_t H, int64_t V, int dtype,
+                                 int32_t ignore_index, const float* ref_logps, float beta,
+                                 int grad_dtype, float* loss, float* pair_loss, void* grad_X,
+                                 void* grad_W, void* workspace, size_t workspace_bytes,
+                                 int64_t chunk_rows, void* stream);
 
 /*
  * Causal-LM targets from token labels (the DeepSpeed vocab-parallel CE page

@@ -45,11 +45,19 @@ _SIGNATURES = {
                                       _vp, _sz, _vp]),
     "flce_shard_backward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i32,
                                    _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
+    "flce_shard_backward_ex": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int,
+                                      _i32, _int, _vp, _int, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
     "flce_shift_labels": (_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "flce_dpo_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int, _i64]),
     "flce_dpo_forward_backward": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _i32, _vp,
                                          ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
+    "flce_dpo_forward_backward_ex": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _i32,
+                                            _vp, ctypes.c_float, _int, _vp, _vp, _vp, _vp, _vp,
+                                            _sz, _i64, _vp]),
     "flce_jsd_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _i64]),
+    "flce_jsd_forward_backward_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                            _int, _i32, _int, ctypes.c_float, _int, _vp, _vp,
+                                            _vp, _vp, _sz, _i64, _vp]),
     "flce_jsd_forward_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
                                          _i32, _int, ctypes.c_float, _vp, _vp, _vp, _vp, _sz,
                                          _i64, _vp]),
@@ -353,32 +361,45 @@ def ce_combine_shard_stats(shard_max, shard_sumexp, shard_target_logit, targets,
     return loss, row_lse
 
 
+def _grad_type(X, grad_dtype):
+    """(16-bit?, torch dtype) of the gradient outputs for grad_dtype "f32" or "input"."""
+    if grad_dtype not in ("f32", "input"):
+        raise ValueError("grad_dtype must be 'f32' or 'input'")
+    g16 = grad_dtype == "input"
+    return g16, (X.dtype if g16 else torch.float32)
+
+
 def flce_shard_backward(X, W_shard, targets, row_lse, vocab_start, V_global, bias_shard=None,
                         ignore_index=-100, reduction="mean", grad_X=True, grad_W=True,
-                        grad_bias=None, workspace=None, chunk_rows=0, stream=None):
+                        grad_bias=None, workspace=None, chunk_rows=0, stream=None,
+                        grad_dtype="f32"):
     """One vocabulary shard's part of the FLCE gradients, given the global
     row lse. Gradient arguments: True = allocate, False/None = skip, or a
-    tensor to write into. Returns (grad_X partial, grad_W_shard, grad_bias_shard)."""
+    tensor to write into; grad_dtype "input" writes them in X's 16-bit dtype
+    (flce_shard_backward_ex). Returns (grad_X partial, grad_W_shard, grad_bias_shard)."""
     N, H = X.shape
     Vl = W_shard.shape[0]
     dev = X.device
     dt = _dtype_code(X)
     red = _red(reduction)
+    g16, gtorch = _grad_type(X, grad_dtype)
     if grad_bias is None:
         grad_bias = bias_shard is not None
-    gX = _grad_arg(grad_X, (N, H), dev)
-    gW = _grad_arg(grad_W, (Vl, H), dev)
-    gb = _grad_arg(grad_bias, (Vl,), dev)
+    gX = _grad_arg(grad_X, (N, H), dev, gtorch)
+    gW = _grad_arg(grad_W, (Vl, H), dev, gtorch)
+    gb = _grad_arg(grad_bias, (Vl,), dev, gtorch)
     if workspace is None:
         workspace = _empty((max(1, flce_workspace_bytes(N, H, Vl, dt, chunk_rows)),), torch.uint8, dev)
-    st = lib().flce_shard_backward(
-        _ptr(X, "X"), _ptr(W_shard, "W_shard", X.dtype), _ptr(bias_shard, "bias_shard", X.dtype),
-        _ptr(targets, "targets", torch.int32), N, H, Vl, vocab_start, V_global, dt, ignore_index,
-        red, _ptr(row_lse, "row_lse", torch.float32), _ptr(gX, "grad_X", torch.float32),
-        _ptr(gW, "grad_W_shard", torch.float32), _ptr(gb, "grad_bias_shard", torch.float32),
-        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
-        _stream(stream))
-    _check(st, "flce_shard_backward")
+    head = [_ptr(X, "X"), _ptr(W_shard, "W_shard", X.dtype), _ptr(bias_shard, "bias_shard", X.dtype),
+            _ptr(targets, "targets", torch.int32), N, H, Vl, vocab_start, V_global, dt, ignore_index,
+            red, _ptr(row_lse, "row_lse", torch.float32)]
+    tail = [_ptr(gX, "grad_X", gtorch), _ptr(gW, "grad_W_shard", gtorch),
+            _ptr(gb, "grad_bias_shard", gtorch), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), chunk_rows, _stream(stream)]
+    if g16:
+        _check(lib().flce_shard_backward_ex(*head, dt, *tail), "flce_shard_backward_ex")
+    else:
+        _check(lib().flce_shard_backward(*head, *tail), "flce_shard_backward")
     return gX, gW, gb
 
 
@@ -388,29 +409,33 @@ def flce_jsd_workspace_bytes(N, H_s, V, dtype=BF16, chunk_rows=0):
 
 def flce_jsd_forward_backward(X_s, W_s, X_t, W_t, targets, temperature=1.0, ignore_index=-100,
                               reduction="mean", grad_X=True, grad_W=True, loss=None,
-                              workspace=None, chunk_rows=0, stream=None):
+                              workspace=None, chunk_rows=0, stream=None, grad_dtype="f32"):
     """Jensen-Shannon distillation of a student head (X_s, W_s) towards a
-    frozen teacher head (X_t, W_t). Returns (loss, grad_X_s, grad_W_s)."""
+    frozen teacher head (X_t, W_t); grad_dtype "input" writes the gradients in
+    X_s's 16-bit dtype (flce_jsd_forward_backward_ex). Returns (loss, grad_X_s, grad_W_s)."""
     N, Hs = X_s.shape
     V = W_s.shape[0]
     Ht = X_t.shape[1]
     dev = X_s.device
     dt = _dtype_code(X_s)
-    gX = _grad_arg(grad_X, (N, Hs), dev)
-    gW = _grad_arg(grad_W, (V, Hs), dev)
+    g16, gtorch = _grad_type(X_s, grad_dtype)
+    gX = _grad_arg(grad_X, (N, Hs), dev, gtorch)
+    gW = _grad_arg(grad_W, (V, Hs), dev, gtorch)
     if loss is None:
         loss = _empty((N,) if reduction == "none" else (1,), torch.float32, dev)
     if workspace is None:
         workspace = _empty((max(1, flce_jsd_workspace_bytes(N, Hs, V, dt, chunk_rows)),),
                            torch.uint8, dev)
-    st = lib().flce_jsd_forward_backward(
-        _ptr(X_s, "X_s"), _ptr(W_s, "W_s", X_s.dtype), _ptr(X_t, "X_t", X_s.dtype),
-        _ptr(W_t, "W_t", X_s.dtype), _ptr(targets, "targets", torch.int32), N, Hs, Ht, V, dt,
-        ignore_index, _red(reduction), float(temperature), _ptr(loss, "loss", torch.float32),
-        _ptr(gX, "grad_X_s", torch.float32), _ptr(gW, "grad_W_s", torch.float32),
-        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
-        _stream(stream))
-    _check(st, "flce_jsd_forward_backward")
+    head = [_ptr(X_s, "X_s"), _ptr(W_s, "W_s", X_s.dtype), _ptr(X_t, "X_t", X_s.dtype),
+            _ptr(W_t, "W_t", X_s.dtype), _ptr(targets, "targets", torch.int32), N, Hs, Ht, V, dt,
+            ignore_index, _red(reduction), float(temperature)]
+    tail = [_ptr(loss, "loss", torch.float32), _ptr(gX, "grad_X_s", gtorch),
+            _ptr(gW, "grad_W_s", gtorch), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), chunk_rows, _stream(stream)]
+    if g16:
+        _check(lib().flce_jsd_forward_backward_ex(*head, dt, *tail), "flce_jsd_forward_backward_ex")
+    else:
+        _check(lib().flce_jsd_forward_backward(*head, *tail), "flce_jsd_forward_backward")
     return loss, gX, gW
 
 
@@ -420,15 +445,19 @@ def flce_dpo_workspace_bytes(n_pairs, seq_len, H, V, dtype=BF16, chunk_rows=0):
 
 def flce_dpo_forward_backward(X, W, targets, n_pairs, seq_len, ref_logps, beta=0.1,
                               ignore_index=-100, grad_X=True, grad_W=True, pair_loss=True,
-                              loss=None, workspace=None, chunk_rows=0, stream=None):
-    """DPO over 2 * n_pairs sequences of seq_len rows (chosen first).
-    Returns (loss [1], pair_loss [n_pairs] or None, grad_X, grad_W)."""
+                              loss=None, workspace=None, chunk_rows=0, stream=None,
+                              grad_dtype="f32"):
+    """DPO over 2 * n_pairs sequences of seq_len rows (chosen first);
+    grad_dtype "input" writes the gradients in X's 16-bit dtype
+    (flce_dpo_forward_backward_ex). Returns (loss [1], pair_loss [n_pairs] or
+    None, grad_X, grad_W)."""
     N, H = X.shape
     V = W.shape[0]
     dev = X.device
     dt = _dtype_code(X)
-    gX = _grad_arg(grad_X, (N, H), dev)
-    gW = _grad_arg(grad_W, (V, H), dev)
+    g16, gtorch = _grad_type(X, grad_dtype)
+    gX = _grad_arg(grad_X, (N, H), dev, gtorch)
+    gW = _grad_arg(grad_W, (V, H), dev, gtorch)
     pl = pair_loss if isinstance(pair_loss, torch.Tensor) else (
         _empty((max(1, n_pairs),), torch.float32, dev) if pair_loss else None)
     if loss is None:
@@ -436,14 +465,15 @@ def flce_dpo_forward_backward(X, W, targets, n_pairs, seq_len, ref_logps, beta=0
     if workspace is None:
         workspace = _empty((max(1, flce_dpo_workspace_bytes(n_pairs, seq_len, H, V, dt, chunk_rows)),),
                            torch.uint8, dev)
-    st = lib().flce_dpo_forward_backward(
-        _ptr(X, "X"), _ptr(W, "W", X.dtype), _ptr(targets, "targets", torch.int32), n_pairs, seq_len,
-        H, V, dt, ignore_index, _ptr(ref_logps, "ref_logps", torch.float32), float(beta),
-        _ptr(loss, "loss", torch.float32), _ptr(pl, "pair_loss", torch.float32),
-        _ptr(gX, "grad_X", torch.float32), _ptr(gW, "grad_W", torch.float32),
-        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), chunk_rows,
-        _stream(stream))
-    _check(st, "flce_dpo_forward_backward")
+    head = [_ptr(X, "X"), _ptr(W, "W", X.dtype), _ptr(targets, "targets", torch.int32), n_pairs,
+            seq_len, H, V, dt, ignore_index, _ptr(ref_logps, "ref_logps", torch.float32), float(beta)]
+    tail = [_ptr(loss, "loss", torch.float32), _ptr(pl, "pair_loss", torch.float32),
+            _ptr(gX, "grad_X", gtorch), _ptr(gW, "grad_W", gtorch), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), chunk_rows, _stream(stream)]
+    if g16:
+        _check(lib().flce_dpo_forward_backward_ex(*head, dt, *tail), "flce_dpo_forward_backward_ex")
+    else:
+        _check(lib().flce_dpo_forward_backward(*head, *tail), "flce_dpo_forward_backward")
     return loss, pl, gX, gW
 
 

@@ -812,14 +812,18 @@ int ce_combine_shard_stats(const float* shard_max, const float* shard_sumexp,
   return FLCE_OK;
 }
 
-int flce_shard_backward(const void* X, const void* W_shard, const void* bias_shard,
-                        const int32_t* targets, int64_t N, int64_t H, int64_t V_local,
-                        int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
-                        int reduction, const float* row_lse, float* grad_X, float* grad_W_shard,
-                        float* grad_bias_shard, void* workspace, size_t workspace_bytes,
-                        int64_t chunk_rows, void* stream) {
+static int shard_backward_impl(const void* X, const void* W_shard, const void* bias_shard,
+                               const int32_t* targets, int64_t N, int64_t H, int64_t V_local,
+                               int64_t vocab_start, int64_t V_global, int dtype,
+                               int32_t ignore_index, int reduction, const float* row_lse,
+                               int grad_dtype, void* grad_X, void* grad_W_shard,
+                               void* grad_bias_shard, void* workspace, size_t workspace_bytes,
+                               int64_t chunk_rows, void* stream) {
   int st = validate_common(dtype, reduction);
   if (st != FLCE_OK) return st;
+  if (grad_dtype != FLCE_F32 && grad_dtype != dtype) return FLCE_E_INVALID_ARG;
+  const bool g16 = grad_dtype != FLCE_F32;
+  const size_t ge = g16 ? 2 : 4;
   if (N < 0 || H <= 0 || V_local <= 0 || vocab_start < 0 || V_global < vocab_start + V_local ||
       chunk_rows < 0)
     return FLCE_E_INVALID_ARG;
@@ -852,15 +856,15 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
   }));
   if (N == 0) {
     if (grad_W_shard)
-      LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W_shard, V_local * H, 0.0f, s); }));
+      LCE_TRY(timed(kKindOther, s, [&] { return launch_zero(grad_W_shard, V_local * H, grad_dtype, s); }));
     if (grad_bias_shard)
-      LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_bias_shard, V_local, 0.0f, s); }));
+      LCE_TRY(timed(kKindOther, s, [&] { return launch_zero(grad_bias_shard, V_local, grad_dtype, s); }));
   }
   // Rows with an ignored or invalid target have zero dlogits over every
   // shard: packed as in flce_chunks (validity against V_global).
   Packer pkr;
   st = pkr.setup(p, ws, hdr, targets, N, V_global, ignore_index, nullptr, grad_X,
-                 H * static_cast<int64_t>(sizeof(float)), s);
+                 H * static_cast<int64_t>(ge), s);
   if (st != FLCE_OK) return st;
   if (grad_X != nullptr && N > 0) {
     st = transpose_head(p, W_shard, V_local, H, ws, s);
@@ -889,7 +893,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
     }));
     if (grad_bias_shard)
       LCE_TRY(timed(kKindOther, s, [&] {
-        return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, FLCE_F32, !first,
+        return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, grad_dtype, !first,
                              gsc.out_scale, gsc.out_shift, s, pk);
       }));
     if (grad_X) {
@@ -900,18 +904,19 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
       g2.epilogue = kEpiStoreF32;
       scale_output(g2, gsc);
       pkr.limit(g2, 0, r0);
-      float* out = grad_X + (pkr.on ? 0 : static_cast<size_t>(r0) * H);
+      void* out = static_cast<char*>(grad_X) + (pkr.on ? 0 : static_cast<size_t>(r0) * H * ge);
       const int splits = (pkr.on && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
       if (splits > 1) {
         g2.C = split_buf; g2.ldc = H;
         g2.k_splits = splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, FLCE_F32, false,
+          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype, false,
                                       s, pk);
         }));
       } else {
         g2.C = out; g2.ldc = H; g2.k_splits = 1;
+        g2.epilogue = g16 ? kEpiStore16 : kEpiStoreF32;
         if (pkr.on) g2.row_map = pk.map;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
       }
@@ -922,7 +927,7 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
       g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
       g3.C = grad_W_shard; g3.ldc = H;
       g3.M = V_local; g3.N = H; g3.K = rows;
-      g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32;
+      g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
       g3.k_splits = 1;
       scale_output(g3, gsc);
       pkr.limit(g3, 1, r0);
@@ -932,21 +937,47 @@ int flce_shard_backward(const void* X, const void* W_shard, const void* bias_sha
   return FLCE_OK;
 }
 
+int flce_shard_backward(const void* X, const void* W_shard, const void* bias_shard,
+                        const int32_t* targets, int64_t N, int64_t H, int64_t V_local,
+                        int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
+                        int reduction, const float* row_lse, float* grad_X, float* grad_W_shard,
+                        float* grad_bias_shard, void* workspace, size_t workspace_bytes,
+                        int64_t chunk_rows, void* stream) {
+  return shard_backward_impl(X, W_shard, bias_shard, targets, N, H, V_local, vocab_start, V_global,
+                             dtype, ignore_index, reduction, row_lse, FLCE_F32, grad_X,
+                             grad_W_shard, grad_bias_shard, workspace, workspace_bytes, chunk_rows,
+                             stream);
+}
+
+int flce_shard_backward_ex(const void* X, const void* W_shard, const void* bias_shard,
+                           const int32_t* targets, int64_t N, int64_t H, int64_t V_local,
+                           int64_t vocab_start, int64_t V_global, int dtype, int32_t ignore_index,
+                           int reduction, const float* row_lse, int grad_dtype, void* grad_X,
+                           void* grad_W_shard, void* grad_bias_shard, void* workspace,
+                           size_t workspace_bytes, int64_t chunk_rows, void* stream) {
+  return shard_backward_impl(X, W_shard, bias_shard, targets, N, H, V_local, vocab_start, V_global,
+                             dtype, ignore_index, reduction, row_lse, grad_dtype, grad_X,
+                             grad_W_shard, grad_bias_shard, workspace, workspace_bytes, chunk_rows,
+                             stream);
+}
+
 size_t flce_jsd_workspace_bytes(int64_t N, int64_t H_s, int64_t V, int dtype, int64_t chunk_rows) {
   Plan p;
   if (!make_plan(N, H_s, V, dtype, chunk_rows, &p)) return 0;
   return p.total + align_up(static_cast<size_t>(p.chunk) * static_cast<size_t>(p.ldz) * elem_bytes(dtype));
 }
 
-int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t, const void* W_t,
-                              const int32_t* targets, int64_t N, int64_t H_s, int64_t H_t,
-                              int64_t V, int dtype, int32_t ignore_index, int reduction,
-                              float temperature, float* loss, float* grad_X_s, float* grad_W_s,
-                              void* workspace, size_t workspace_bytes, int64_t chunk_rows,
-                              void* stream) {
+static int jsd_impl(const void* X_s, const void* W_s, const void* X_t, const void* W_t,
+                    const int32_t* targets, int64_t N, int64_t H_s, int64_t H_t, int64_t V,
+                    int dtype, int32_t ignore_index, int reduction, float temperature,
+                    int grad_dtype, float* loss, void* grad_X_s, void* grad_W_s, void* workspace,
+                    size_t workspace_bytes, int64_t chunk_rows, void* stream) {
   int st = validate_flce(X_s, W_s, nullptr, targets, N, H_s, V, dtype, reduction, loss, grad_X_s,
                          grad_W_s, nullptr, chunk_rows, workspace);
   if (st != FLCE_OK) return st;
+  if (grad_dtype != FLCE_F32 && grad_dtype != dtype) return FLCE_E_INVALID_ARG;
+  const bool g16 = grad_dtype != FLCE_F32;
+  const size_t ge = g16 ? 2 : 4;
   if (W_t == nullptr || H_t <= 0 || !(temperature > 0.0f)) return FLCE_E_INVALID_ARG;
   if (N > 0 && X_t == nullptr) return FLCE_E_INVALID_ARG;
   if (H_t >= kMaxDim) return FLCE_E_UNSUPPORTED;
@@ -976,14 +1007,14 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
     return launch_count_targets(targets, N, V, ignore_index, reduction, hdr, s);
   }));
   if (N == 0 && grad_W_s)
-    LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W_s, V * H_s, 0.0f, s); }));
+    LCE_TRY(timed(kKindOther, s, [&] { return launch_zero(grad_W_s, V * H_s, grad_dtype, s); }));
   // Packed rows (as in flce_chunks) when the teacher's gathered hidden states
   // fit the split-K partial buffer, which is free until the grad_X product.
   const size_t split_bytes = p.off_map - p.off_split;
   const bool teacher_fits = static_cast<size_t>(p.chunk) * static_cast<size_t>(H_t) * e <= split_bytes;
   Packer pkr;
   st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows, grad_X_s,
-                 H_s * static_cast<int64_t>(sizeof(float)), s, teacher_fits);
+                 H_s * static_cast<int64_t>(ge), s, teacher_fits);
   if (st != FLCE_OK) return st;
   if (grad_X_s != nullptr && N > 0) {
     st = transpose_head(p, W_s, V, H_s, ws, s);
@@ -1026,17 +1057,18 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
       g2.epilogue = kEpiStoreF32;
       scale_output(g2, gsc);
       pkr.limit(g2, 0, r0);
-      float* out = grad_X_s + (pkr.on ? 0 : static_cast<size_t>(r0) * H_s);
+      void* out = static_cast<char*>(grad_X_s) + (pkr.on ? 0 : static_cast<size_t>(r0) * H_s * ge);
       const int splits = (pkr.on && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
       if (splits > 1) {
         g2.C = split_buf; g2.ldc = H_s; g2.k_splits = splits; g2.split_stride = rows * H_s;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, splits, rows * H_s, rows, H_s, H_s, out, FLCE_F32,
+          return launch_splitk_reduce(split_buf, splits, rows * H_s, rows, H_s, H_s, out, grad_dtype,
                                       false, s, pk);
         }));
       } else {
         g2.C = out; g2.ldc = H_s; g2.k_splits = 1;
+        g2.epilogue = g16 ? kEpiStore16 : kEpiStoreF32;
         if (pkr.on) g2.row_map = pk.map;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
       }
@@ -1046,7 +1078,8 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
       g3.A = zs; g3.lda = p.ldz; g3.a_kmajor = false;
       g3.B = Xs_c; g3.ldb = H_s; g3.b_kmajor = false;
       g3.C = grad_W_s; g3.ldc = H_s; g3.M = V; g3.N = H_s; g3.K = rows;
-      g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32; g3.k_splits = 1;
+      g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
+      g3.k_splits = 1;
       scale_output(g3, gsc);
       pkr.limit(g3, 1, r0);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
@@ -1059,6 +1092,28 @@ int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
   return FLCE_OK;
 }
 
+int flce_jsd_forward_backward(const void* X_s, const void* W_s, const void* X_t, const void* W_t,
+                              const int32_t* targets, int64_t N, int64_t H_s, int64_t H_t,
+                              int64_t V, int dtype, int32_t ignore_index, int reduction,
+                              float temperature, float* loss, float* grad_X_s, float* grad_W_s,
+                              void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                              void* stream) {
+  return jsd_impl(X_s, W_s, X_t, W_t, targets, N, H_s, H_t, V, dtype, ignore_index, reduction,
+                  temperature, FLCE_F32, loss, grad_X_s, grad_W_s, workspace, workspace_bytes,
+                  chunk_rows, stream);
+}
+
+int flce_jsd_forward_backward_ex(const void* X_s, const void* W_s, const void* X_t, const void* W_t,
+                                 const int32_t* targets, int64_t N, int64_t H_s, int64_t H_t,
+                                 int64_t V, int dtype, int32_t ignore_index, int reduction,
+                                 float temperature, int grad_dtype, float* loss, void* grad_X_s,
+                                 void* grad_W_s, void* workspace, size_t workspace_bytes,
+                                 int64_t chunk_rows, void* stream) {
+  return jsd_impl(X_s, W_s, X_t, W_t, targets, N, H_s, H_t, V, dtype, ignore_index, reduction,
+                  temperature, grad_dtype, loss, grad_X_s, grad_W_s, workspace, workspace_bytes,
+                  chunk_rows, stream);
+}
+
 size_t flce_dpo_workspace_bytes(int64_t n_pairs, int64_t seq_len, int64_t H, int64_t V, int dtype,
                                 int64_t chunk_rows) {
   if (n_pairs < 0 || seq_len <= 0 || n_pairs * seq_len >= kMaxRows) return 0;
@@ -1069,13 +1124,15 @@ size_t flce_dpo_workspace_bytes(int64_t n_pairs, int64_t seq_len, int64_t H, int
          align_up(static_cast<size_t>(std::max<int64_t>(2 * n_pairs, 1)) * sizeof(double));
 }
 
-int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targets, int64_t n_pairs,
-                              int64_t seq_len, int64_t H, int64_t V, int dtype,
-                              int32_t ignore_index, const float* ref_logps, float beta,
-                              float* loss, float* pair_loss, float* grad_X, float* grad_W,
-                              void* workspace, size_t workspace_bytes, int64_t chunk_rows,
-                              void* stream) {
+static int dpo_impl(const void* X, const void* W, const int32_t* targets, int64_t n_pairs,
+                    int64_t seq_len, int64_t H, int64_t V, int dtype, int32_t ignore_index,
+                    const float* ref_logps, float beta, int grad_dtype, float* loss,
+                    float* pair_loss, void* grad_X, void* grad_W, void* workspace,
+                    size_t workspace_bytes, int64_t chunk_rows, void* stream) {
   if (n_pairs < 0 || seq_len <= 0 || n_pairs * seq_len >= kMaxRows) return FLCE_E_INVALID_ARG;
+  if (grad_dtype != FLCE_F32 && grad_dtype != dtype) return FLCE_E_INVALID_ARG;
+  const bool g16 = grad_dtype != FLCE_F32;
+  const size_t ge = g16 ? 2 : 4;
   if (!(beta > 0.0f)) return FLCE_E_INVALID_ARG;
   const int64_t N = 2 * n_pairs * seq_len;
   int st = validate_flce(X, W, nullptr, targets, N, H, V, dtype, FLCE_REDUCTION_SUM, loss, grad_X,
@@ -1126,9 +1183,9 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
     return launch_count_targets(targets, N, V, ignore_index, FLCE_REDUCTION_SUM, hdr, s);
   }));
   if (N == 0 && grad_W)
-    LCE_TRY(timed(kKindOther, s, [&] { return launch_fill_f32(grad_W, V * H, 0.0f, s); }));
+    LCE_TRY(timed(kKindOther, s, [&] { return launch_zero(grad_W, V * H, grad_dtype, s); }));
   st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows, grad_X,
-                 H * static_cast<int64_t>(sizeof(float)), s);
+                 H * static_cast<int64_t>(ge), s);
   if (st != FLCE_OK) return st;
   if (grad_X != nullptr && N > 0) {
     st = transpose_head(p, W, V, H, ws, s);
@@ -1175,17 +1232,18 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
       g2.epilogue = kEpiStoreF32;
       scale_output(g2, gsc);
       pkr.limit(g2, 0, r0);
-      float* out = grad_X + (pkr.on ? 0 : static_cast<size_t>(r0) * H);
+      void* out = static_cast<char*>(grad_X) + (pkr.on ? 0 : static_cast<size_t>(r0) * H * ge);
       const int splits = (pkr.on && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
       if (splits > 1) {
         g2.C = split_buf; g2.ldc = H; g2.k_splits = splits; g2.split_stride = rows * H;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
         LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, FLCE_F32, false,
+          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype, false,
                                       s, pk);
         }));
       } else {
         g2.C = out; g2.ldc = H; g2.k_splits = 1;
+        g2.epilogue = g16 ? kEpiStore16 : kEpiStoreF32;
         if (pkr.on) g2.row_map = pk.map;
         LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
       }
@@ -1195,13 +1253,36 @@ int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targe
       g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
       g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
       g3.C = grad_W; g3.ldc = H; g3.M = V; g3.N = H; g3.K = rows;
-      g3.epilogue = first ? kEpiStoreF32 : kEpiAccumF32; g3.k_splits = 1;
+      g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
+      g3.k_splits = 1;
       scale_output(g3, gsc);
       pkr.limit(g3, 1, r0);
       LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
   }
   return FLCE_OK;
+}
+
+int flce_dpo_forward_backward(const void* X, const void* W, const int32_t* targets, int64_t n_pairs,
+                              int64_t seq_len, int64_t H, int64_t V, int dtype,
+                              int32_t ignore_index, const float* ref_logps, float beta,
+                              float* loss, float* pair_loss, float* grad_X, float* grad_W,
+                              void* workspace, size_t workspace_bytes, int64_t chunk_rows,
+                              void* stream) {
+  return dpo_impl(X, W, targets, n_pairs, seq_len, H, V, dtype, ignore_index, ref_logps, beta,
+                  FLCE_F32, loss, pair_loss, grad_X, grad_W, workspace, workspace_bytes,
+                  chunk_rows, stream);
+}
+
+int flce_dpo_forward_backward_ex(const void* X, const void* W, const int32_t* targets,
+                                 int64_t n_pairs, int64_t seq_len, int64_t H, int64_t V, int dtype,
+                                 int32_t ignore_index, const float* ref_logps, float beta,
+                                 int grad_dtype, float* loss, float* pair_loss, void* grad_X,
+                                 void* grad_W, void* workspace, size_t workspace_bytes,
+                                 int64_t chunk_rows, void* stream) {
+  return dpo_impl(X, W, targets, n_pairs, seq_len, H, V, dtype, ignore_index, ref_logps, beta,
+                  grad_dtype, loss, pair_loss, grad_X, grad_W, workspace, workspace_bytes,
+                  chunk_rows, stream);
 }
 
 int flce_shift_labels(const int32_t* labels, int64_t B, int64_t S, int32_t ignore_index,

@@ -623,3 +623,53 @@ def test_dpo_against_oracle(B, dtype, P, S, H, V, chunk):
     check_max_rel(to_host(gX), ref_g["X"], t["grad"], "grad_X")
     check_max_rel(to_host(gW), ref_g["W"], t["grad"], "grad_W")
     assert np.all(to_host(gX)[y == -100] == 0.0)
+
+
+def _rounds_ok(g16, g32, rounds, ulp, name):
+    a, r = g16.double().cpu().numpy(), g32.double().cpu().numpy()
+    err = np.abs(a - r).max()
+    assert err <= rounds * ulp * np.abs(r).max() + 1e-30, f"{name}: {err} > {rounds} ulp"
+
+
+def test_jsd_and_dpo_gradients_in_the_input_type(B):
+    """flce_jsd_forward_backward_ex and flce_dpo_forward_backward_ex with bf16
+    gradient outputs: the same loss as the float32-gradient calls, grad_X within
+    one bf16 rounding of theirs, grad_W within one rounding per chunk, and the
+    oracle's bar."""
+    import torch
+    ulp = 2.0 ** -8
+    N, Hs, Ht, V, chunk = 600, 136, 72, 1000, 256
+    s_inp = synth.make_flce_inputs(N, Hs, V, "bf16", w_std=0.08, ignore_frac=0.1, seed=80)
+    t_inp = synth.make_flce_inputs(N, Ht, V, "bf16", w_std=0.12, ignore_frac=0.0, seed=81)
+    args = (to_dev(s_inp["X"], "bf16"), to_dev(s_inp["W"], "bf16"), to_dev(t_inp["X"], "bf16"),
+            to_dev(t_inp["W"], "bf16"), to_dev(s_inp["targets"], "i32"))
+    say("jsd 16-bit gradients")
+    l16, gX16, gW16 = B.flce_jsd_forward_backward(*args, temperature=1.5, chunk_rows=chunk,
+                                                  grad_dtype="input")
+    l32, gX32, gW32 = B.flce_jsd_forward_backward(*args, temperature=1.5, chunk_rows=chunk)
+    torch.cuda.synchronize()
+    assert gX16.dtype == torch.bfloat16 and gW16.dtype == torch.bfloat16
+    assert torch.equal(l16, l32)
+    _rounds_ok(gX16, gX32, 1, ulp, "JSD grad_X")
+    _rounds_ok(gW16, gW32, -(-N // chunk), ulp, "JSD grad_W")
+    f = lambda a: np.asarray(a, np.float64)
+    _, ref_g, _ = O.flce_jsd(f(s_inp["X_f32"]), f(s_inp["W_f32"]), f(t_inp["X_f32"]),
+                             f(t_inp["W_f32"]), s_inp["targets"], temperature=1.5)
+    check_max_rel(gX16.float().cpu().numpy(), ref_g["X"], TOL["bf16"]["grad"], "JSD grad_X bf16")
+    check_max_rel(gW16.float().cpu().numpy(), ref_g["W"], TOL["bf16"]["grad"], "JSD grad_W bf16")
+
+    P, S, H, V = 2, 300, 64, 3001
+    inp, ref = _dpo_inputs(P, S, H, V, "bf16", seed=82)
+    args = (to_dev(inp["X"], "bf16"), to_dev(inp["W"], "bf16"), to_dev(inp["targets"], "i32"), P, S,
+            torch.from_numpy(ref).cuda())
+    say("dpo 16-bit gradients")
+    l16, _, gX16, gW16 = B.flce_dpo_forward_backward(*args, beta=0.2, chunk_rows=256, grad_dtype="input")
+    l32, _, gX32, gW32 = B.flce_dpo_forward_backward(*args, beta=0.2, chunk_rows=256)
+    torch.cuda.synchronize()
+    assert gX16.dtype == torch.bfloat16 and torch.equal(l16, l32)
+    _rounds_ok(gX16, gX32, 1, ulp, "DPO grad_X")
+    _rounds_ok(gW16, gW32, -(-(2 * P * S) // 256), ulp, "DPO grad_W")
+    X, W, _, y = oracle_inputs(inp)
+    _, ref_g, _ = O.flce_dpo(X, W, y, P, S, ref.astype(np.float64), beta=0.2)
+    check_max_rel(gX16.float().cpu().numpy(), ref_g["X"], TOL["bf16"]["grad"], "DPO grad_X bf16")
+    check_max_rel(gW16.float().cpu().numpy(), ref_g["W"], TOL["bf16"]["grad"], "DPO grad_W bf16")

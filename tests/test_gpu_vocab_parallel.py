@@ -266,3 +266,33 @@ def test_shard_of_8b_head_full_size(B):
     gw_ref = dZ.T @ X
     check_max_rel(to_host(gw, f64=False)[cols].astype(np.float64), gw_ref, tol["grad"],
                   "sampled grad_W shard rows")
+
+
+def test_shard_backward_gradients_in_the_input_type(B):
+    """flce_shard_backward_ex with bf16 gradient outputs against the float32
+    call: grad_X within one bf16 rounding, the shard's grad_W and grad_bias
+    within one rounding per chunk, and the oracle's bar."""
+    import torch
+    N, H, V, chunk = 700, 136, 3001, 256
+    inp = synth.make_flce_inputs(N, H, V, "bf16", bias_std=0.1, ignore_frac=0.2, seed=36)
+    X, W, b, y = oracle_inputs(inp)
+    lse32 = O.logsumexp_rows(X @ W.T + b).astype(np.float32)
+    a, c = 1000, 2500
+    args = (to_dev(inp["X"], "bf16"), to_dev(np.ascontiguousarray(inp["W"][a:c]), "bf16"),
+            to_dev(y.astype(np.int32), "i32"), torch.from_numpy(lse32).cuda(), a, V)
+    kw = dict(bias_shard=to_dev(np.ascontiguousarray(inp["bias"][a:c]), "bf16"), reduction="mean",
+              chunk_rows=chunk)
+    say("shard backward 16-bit gradients")
+    g16 = B.flce_shard_backward(*args, grad_dtype="input", **kw)
+    g32 = B.flce_shard_backward(*args, **kw)
+    torch.cuda.synchronize()
+    assert all(t.dtype == torch.bfloat16 for t in g16)
+    ulp = 2.0 ** -8
+    chunks = -(-N // chunk)
+    for t16, t32, rounds, name in zip(g16, g32, (1, chunks, chunks), ("grad_X", "grad_W", "grad_bias")):
+        a16, r = t16.double().cpu().numpy(), t32.double().cpu().numpy()
+        assert np.abs(a16 - r).max() <= rounds * ulp * np.abs(r).max() + 1e-30, name
+    ref = O.flce_shard_backward(X, W[a:c], y, a, V, lse32.astype(np.float64), bias_shard=b[a:c],
+                                reduction="mean")
+    for t16, rg, name in zip(g16, ref, ("grad_X", "grad_W", "grad_bias")):
+        check_max_rel(t16.float().cpu().numpy(), rg, TOL["bf16"]["grad"], name + " bf16")
