@@ -795,10 +795,10 @@ __device__ __forceinline__ void step(f32x16_t (&acc)[4][kFJ], Frags<kFJ>& f0, Fr
                               [&] { B.template issue<0, kI>(slot_buf<sa>(), k2, kend); });
 }
 
-// kW = 8: 2 x 4 waves of 128 x 64, two per SIMD (grad_W). kW = 4: 2 x 2 waves
-// of 128 x 128, one per SIMD with the 256 accumulators in AGPRs, a third
-// fewer LDS reads per MFMA (logits: +1.4 to +2.3% over 8 waves; grad_W: no
-// change).
+// kW = 8: 2 x 4 waves of 128 x 64, two per SIMD. kW = 4: 2 x 2 waves of
+// 128 x 128, one per SIMD with the 256 accumulators in AGPRs, a third fewer
+// LDS reads per MFMA (logits +1.4 to +2.3% over 8 waves; grad_W 0.7% in
+// alternating same-box runs). All three products run on 4 waves.
 template <bool kAK, bool kBKm, int kEpi, int kTy, int kW>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4, kW / 4)))
 void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
@@ -950,13 +950,13 @@ static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)
     return launch_mfma_kernel<true, false, kEpiAccum16, 4, kTy>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStore16)
-    return launch_ring<false, false, kEpiStore16, kTy, 8>(d, s);
+    return launch_ring<false, false, kEpiStore16, kTy, 4>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)
-    return launch_ring<false, false, kEpiAccum16, kTy, 8>(d, s);
+    return launch_ring<false, false, kEpiAccum16, kTy, 4>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
-    return launch_ring<false, false, kEpiStoreF32, kTy, 8>(d, s);
+    return launch_ring<false, false, kEpiStoreF32, kTy, 4>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
-    return launch_ring<false, false, kEpiAccumF32, kTy, 8>(d, s);
+    return launch_ring<false, false, kEpiAccumF32, kTy, 4>(d, s);
   return hipErrorInvalidValue;
 }
 
