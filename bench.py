@@ -492,6 +492,18 @@ def bench_dpo(torch, B, X, W, y, cfg, n_pairs=4, seq_len=1024, reps=3):
     return out
 
 
+def extra_bound_bytes(N, H, V, chunk, splits, e):
+    """The memory model of one FLCE call's scratch: one chunk of logits,
+    per-row / per-vocabulary scratch, the grad_X K-split partials (the last
+    packed chunk splits in two) and, for 16-bit inputs, the packed-row lists,
+    the chunk's gathered hidden states and the transposed head W^T (H <= chunk)."""
+    max_splits = max(splits, 2 if (e == 2 and splits == 1 and V // 2 >= 2048) else splits)
+    return (chunk * ((V + 7) // 8 * 8) * e + (N + V) * 16 + 4096
+            + (max_splits * chunk * H * 4 if (max_splits > 1 or e == 2) else 0)
+            + ((chunk * H * e + 8 * N + 4096) if e == 2 else 0)
+            + ((V + 63) // 64 * 64 * H * e if (e == 2 and H <= chunk) else 0))
+
+
 def rows_through_products(B, y):
     """Rows an FLCE call over targets y runs through its products: the
     non-ignored ones when row packing is on, else all."""
@@ -728,15 +740,7 @@ def main():
         unpacked = {"ms_per_step": ums, "tokens_per_s": N / (ums * 1e-3),
                     "mfma_frac_step": 6.0 * N * H * V / (ums * 1e-3) / PEAK_BF16_FLOPS,
                     "steps": reps}
-    # One chunk of logits, per-row / per-vocabulary scratch, the grad_X K-split
-    # partials (the last packed chunk splits in two) and, for 16-bit inputs,
-    # the packed-row lists, the chunk's gathered hidden states and W^T.
-    max_splits = max(splits, 2 if (e == 2 and splits == 1 and V // 2 >= 2048) else splits)
-    extra_bound = (chunk * ((V + 7) // 8 * 8) * e + (N + V) * 16 + 4096
-                   + (max_splits * chunk * H * 4 if (max_splits > 1 or e == 2) else 0)
-                   + ((chunk * H * e + 8 * N + 4096) if e == 2 else 0)
-                   # the transposed head for grad_X (16-bit, H <= chunk)
-                   + ((V + 63) // 64 * 64 * H * e if (e == 2 and H <= chunk) else 0))
+    extra_bound = extra_bound_bytes(N, H, V, chunk, splits, e)
     step_flops = 6.0 * n_live * H * V
     result = {
         "metric": "FLCE fwd+bwd tokens/s + % bf16 MFMA peak at H4096 V128256; peak HBM bytes",

@@ -91,3 +91,20 @@ def test_kernel_classes_cover_the_launched_gemms():
     for name, kind in names.items():
         got = [k for frag, k in bench.KERNEL_KINDS.items() if frag in name]
         assert got == [kind], name
+
+
+@pytest.mark.parametrize("N,H,V,dtype,chunk", [
+    (32768, 4096, 128256, "bf16", 0), (8192, 2048, 128256, "bf16", 0),
+    (32768, 4096, 256000, "bf16", 0), (32768, 4096, 128256, "bf16", 2048),
+    (256, 64, 1024, "f32", 0), (1000, 136, 4099, "bf16", 256)])
+def test_memory_bound_covers_the_workspace(N, H, V, dtype, chunk):
+    """The bench's memory model (extra_bound_bytes) holds the library's own
+    workspace query for the planned chunk, with under 1% to spare beyond the
+    256-byte alignment of its regions: peak extra memory is the workspace."""
+    from linear_cross_entropy_03_amd import binding as B
+    dt = B.BF16 if dtype == "bf16" else B.F32
+    c, s = B.flce_plan(N, H, V, dt, chunk)
+    ws = B.flce_workspace_bytes(N, H, V, dt, chunk)
+    bound = bench.extra_bound_bytes(N, H, V, c, s, 2 if dtype == "bf16" else 4)
+    assert ws <= bound
+    assert bound - ws <= 0.01 * ws + 16 * 256 + (N + V) * 16
