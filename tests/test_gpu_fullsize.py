@@ -136,3 +136,36 @@ def test_fullsize_grad_w_rows(workload):
     check_max_rel(r["gW"][vrows].astype(np.float64), gw, t["grad"], "sampled grad_W rows")
     if r["gb"] is not None:
         check_max_rel(r["gb"][vrows], gb, t["grad"], "sampled grad_bias entries")
+
+
+@pytest.mark.timeout(300)
+def test_fullsize_packing_matches_unpacked(B):
+    """The Llama-3-8B head with row packing (the benchmarked configuration)
+    against the same call with packing off, compared on the device: the loss
+    is bitwise equal, grad_X differs only in the last chunk's rows (whose K
+    is split in two) and by float32 summation order, grad_W by where the
+    chunk boundaries fall, and ignored rows of grad_X are exactly zero."""
+    import torch
+    name = "llama8b_head_bf16"
+    cfg = synth.WORKLOADS[name]
+    say(name, "packed against unpacked: generating inputs")
+    inp = synth.make_workload(name)
+    X, W = to_dev(inp["X"], "bf16"), to_dev(inp["W"], "bf16")
+    y = to_dev(inp["targets"], "i32")
+    out = {}
+    was = B.flce_set_row_packing(True)
+    try:
+        for pack in (True, False):
+            B.flce_set_row_packing(pack)
+            say(name, "packing", pack)
+            out[pack] = B.flce_forward_backward(X, W, y, reduction=cfg["reduction"])
+            torch.cuda.synchronize()
+    finally:
+        B.flce_set_row_packing(was)
+    (l1, gx1, gw1, _), (l0, gx0, gw0, _) = out[True], out[False]
+    assert float(l1[0]) == float(l0[0])
+    for a, r, name_ in ((gx1, gx0, "grad_X"), (gw1, gw0, "grad_W")):
+        err = float((a - r).abs().max())
+        assert err <= 1e-5 * float(r.abs().max()), f"{name_}: {err}"
+    ignored = y == -100
+    assert float(gx1[ignored].abs().max()) == 0.0
