@@ -673,3 +673,39 @@ def test_jsd_and_dpo_gradients_in_the_input_type(B):
     _, ref_g, _ = O.flce_dpo(X, W, y, P, S, ref.astype(np.float64), beta=0.2)
     check_max_rel(gX16.float().cpu().numpy(), ref_g["X"], TOL["bf16"]["grad"], "DPO grad_X bf16")
     check_max_rel(gW16.float().cpu().numpy(), ref_g["W"], TOL["bf16"]["grad"], "DPO grad_W bf16")
+
+
+@pytest.mark.timeout(300)
+def test_row_packing_over_a_thousand_pack_blocks(packing):
+    """4.2 million rows (H 8, V 64, 30% ignored): the packing kernels' block
+    prefix runs over more than 1024 blocks of 4096 rows (several rounds of its
+    single-workgroup scan). Against the unpacked call: per-row losses bitwise,
+    grad_X and grad_W to float32 summation order; sampled rows' losses against
+    the oracle."""
+    import torch
+    B = packing
+    N, H, V = 1024 * 4096 + 3001, 8, 64
+    inp = synth.make_flce_inputs(N, H, V, "bf16", ignore_frac=0.3, seed=90)
+    X, W, y = to_dev(inp["X"], "bf16"), to_dev(inp["W"], "bf16"), to_dev(inp["targets"], "i32")
+    out = {}
+    for pack in (True, False):
+        B.flce_set_row_packing(pack)
+        say("flce 4.2M rows, packing", pack)
+        out[pack] = B.flce_forward_backward(X, W, y, reduction="none")
+        torch.cuda.synchronize()
+    B.flce_set_row_packing(True)
+    (l1, gx1, gw1, _), (l0, gx0, gw0, _) = out[True], out[False]
+    assert torch.equal(l1, l0), "per-row losses differ with packing"
+    # grad_X rows sum 64 products: float32 order only. grad_W entries are
+    # float32 sums over ~2.9 million rows, split into chunks at different rows
+    # by the two paths; each sum carries a rounding error of order
+    # sqrt(n) * 2^-24 of its magnitude (~1e-4 here), so the two may differ by
+    # about twice that.
+    for a, r, name, tol in ((gx1, gx0, "grad_X", 1e-5), (gw1, gw0, "grad_W", 2e-4)):
+        err = float((a - r).abs().max())
+        assert err <= tol * float(r.abs().max()), f"{name}: {err}"
+    assert float(gx1[y == -100].abs().max()) == 0.0
+    rows = np.random.default_rng(91).choice(N, 64, replace=False)
+    Xs, Ws, _, ys = oracle_inputs(inp)
+    ref_rows, _, _ = O.flce(Xs[rows], Ws, ys[rows], reduction="none", want_grads=False)
+    check_max_rel(l1.cpu().numpy()[rows], ref_rows, TOL["bf16"]["loss"], "sampled row losses")
