@@ -51,6 +51,10 @@ def parse():
                          "products, ignored ones included)")
     ap.add_argument("--no-unpacked", action="store_true",
                     help="skip the comparison steps with row packing off")
+    ap.add_argument("--no-strict", action="store_true",
+                    help="skip the comparison step with the transposed head off")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other full-size workloads (Llama-3.2-1B head, 256k vocabulary)")
     ap.add_argument("--no-eager", action="store_true",
                     help="skip the PyTorch eager context measurement")
     ap.add_argument("--profile-step", action="store_true",
@@ -133,6 +137,7 @@ def cpu_baseline(inp, cfg, target_s):
 
 KERNEL_KINDS = {  # kernel-name fragment -> kind reported by the timing hooks
     "k_ring<true, true, 0": "logits_gemm",
+    "k_ring_xw<": "grad_xw_gemm",                # grad_X and grad_W of a chunk in one launch
     "k_gemm2<true, false, 1": "grad_x_gemm",     # W read n-major (chunk shorter than H)
     "k_ring<true, true, 1": "grad_x_gemm",       # against the transposed head
     "k_ring<false, false, 1": "grad_w_gemm",
@@ -206,6 +211,29 @@ def load_traffic(workload):
     return t if t.get("source_hash") == kernel_source_hash() else None
 
 
+def time_calls(torch, stream, call, reps):
+    """Milliseconds per call over `reps` back-to-back calls on `stream`
+    (timing hooks off)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def hooked_pass(torch, B, call, reps):
+    """`reps` more calls with the library's per-kernel timing hooks on; the
+    tallies are left for flce_timing_read."""
+    B.flce_timing_reset()
+    B.flce_timing_enable(True)
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    B.flce_timing_enable(False)
+
+
 def bench_ce(torch, B, reps=40):
     """Standalone CE over bf16 logits [1024, 32768] (one vocabulary shard,
     std 2, 5% ignored), gradient to a separate buffer, mean reduction. Eight
@@ -224,18 +252,25 @@ def bench_ce(torch, B, reps=40):
     for i in range(8):
         B.ce_forward_backward(sets[i][0], y, grad_logits=sets[i][1], loss=loss, workspace=ws, stream=stream)
     torch.cuda.synchronize()
-    B.flce_timing_reset()
-    B.flce_timing_enable(True)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The call, hooks off.
     a.record(stream)
     for r in range(reps):
         lg, g = sets[r % 8]
         B.ce_forward_backward(lg, y, grad_logits=g, loss=loss, workspace=ws, stream=stream)
     b.record(stream)
     torch.cuda.synchronize()
-    B.flce_timing_enable(False)
     call_us = a.elapsed_time(b) / reps * 1e3
+    # Its kernels, hooks on (a separate pass).
+    B.flce_timing_reset()
+    B.flce_timing_enable(True)
+    for r in range(reps):
+        lg, g = sets[r % 8]
+        B.ce_forward_backward(lg, y, grad_logits=g, loss=loss, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    B.flce_timing_enable(False)
     k_ms, k_n = B.flce_timing_read("row_ce")
+    o_ms, o_n = B.flce_timing_read("other")
     B.flce_timing_reset()
     algo = 2.0 * N * V * 2 + 8.0 * N
     kern_us = k_ms / k_n * 1e3
@@ -263,6 +298,9 @@ def bench_ce(torch, B, reps=40):
     return {
         "workload": "ce_shard_bf16 (logits [1024, 32768] bf16, mean, grad out of place)",
         "us_per_call": call_us, "row_ce_kernel_us": kern_us,
+        "launches_per_call": (k_n + o_n) / reps,
+        "other_kernels_us_per_call": o_ms / reps * 1e3,
+        "frac_hbm_call": algo / (call_us * 1e-6) / PEAK_HBM_BYTES,
         "algorithmic_bytes": algo,
         "achieved_GBps_call": algo / (call_us * 1e-6) / 1e9,
         "achieved_GBps_kernel": algo / (kern_us * 1e-6) / 1e9,
@@ -319,15 +357,19 @@ def bench_vocab_parallel(torch, B, X, W, y, cfg, reps=5):
     once(False)
     torch.cuda.synchronize()
     tot = [0.0, 0.0, 0.0]
-    B.flce_timing_reset()
-    B.flce_timing_enable(True)
     for _ in range(reps):
         once(True)
         torch.cuda.synchronize()
         for i in range(3):
             tot[i] += ev[i].elapsed_time(ev[i + 1])
+    # Kernel times in a separate pass with the hooks on.
+    B.flce_timing_reset()
+    B.flce_timing_enable(True)
+    for _ in range(reps):
+        once(False)
+    torch.cuda.synchronize()
     B.flce_timing_enable(False)
-    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm"))
+    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm", "grad_xw_gemm"))
     row_ms, row_n = B.flce_timing_read("row_ce")
     B.flce_timing_reset()
     stats_ms, comb_ms, bwd_ms = (x / reps for x in tot)
@@ -405,19 +447,11 @@ def bench_distill(torch, B, X, W, y, cfg, n_rows=8192, reps=3):
                                     grad_X=gX, grad_W=gW, loss=loss, workspace=ws, stream=stream)
     call()
     torch.cuda.synchronize()
-    B.flce_timing_reset()
-    B.flce_timing_enable(True)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        call()
-    b.record(stream)
-    torch.cuda.synchronize()
-    B.flce_timing_enable(False)
+    ms = time_calls(torch, stream, call, reps)
+    hooked_pass(torch, B, call, reps)
     row_ms, row_n = B.flce_timing_read("row_ce")
-    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm"))
+    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm", "grad_xw_gemm"))
     B.flce_timing_reset()
-    ms = a.elapsed_time(b) / reps
     # Two logits GEMMs and the two gradient products over the rows they run on
     # (the non-ignored ones when packed: the teacher here is as wide as the student).
     live = rows_through_products(B, y[:N])
@@ -461,19 +495,11 @@ def bench_dpo(torch, B, X, W, y, cfg, n_pairs=4, seq_len=1024, reps=3):
                                     pair_loss=False, loss=loss, workspace=ws, stream=stream)
     call()
     torch.cuda.synchronize()
-    B.flce_timing_reset()
-    B.flce_timing_enable(True)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        call()
-    b.record(stream)
-    torch.cuda.synchronize()
-    B.flce_timing_enable(False)
+    ms = time_calls(torch, stream, call, reps)
+    hooked_pass(torch, B, call, reps)
     logit_ms, logit_n = B.flce_timing_read("logits_gemm")
-    gemm_ms = logit_ms + sum(B.flce_timing_read(k)[0] for k in ("grad_x_gemm", "grad_w_gemm"))
+    gemm_ms = logit_ms + sum(B.flce_timing_read(k)[0] for k in ("grad_x_gemm", "grad_w_gemm", "grad_xw_gemm"))
     B.flce_timing_reset()
-    ms = a.elapsed_time(b) / reps
     chunk = B.flce_plan(N, H, V, B.BF16)[0]
     n_logits = logit_n / reps                      # logits GEMMs per call (1 or 2 per chunk)
     # Passes over the logits (1 with one chunk, else 2), each over the rows
@@ -492,16 +518,21 @@ def bench_dpo(torch, B, X, W, y, cfg, n_pairs=4, seq_len=1024, reps=3):
     return out
 
 
-def extra_bound_bytes(N, H, V, chunk, splits, e):
-    """The memory model of one FLCE call's scratch: one chunk of logits,
-    per-row / per-vocabulary scratch, the grad_X K-split partials (the last
-    packed chunk splits in two) and, for 16-bit inputs, the packed-row lists,
-    the chunk's gathered hidden states and the transposed head W^T (H <= chunk)."""
-    max_splits = max(splits, 2 if (e == 2 and splits == 1 and V // 2 >= 2048) else splits)
-    return (chunk * ((V + 7) // 8 * 8) * e + (N + V) * 16 + 4096
-            + (max_splits * chunk * H * 4 if (max_splits > 1 or e == 2) else 0)
-            + ((chunk * H * e + 8 * N + 4096) if e == 2 else 0)
-            + ((V + 63) // 64 * 64 * H * e if (e == 2 and H <= chunk) else 0))
+def scratch_parts(B, N, H, V, dt, chunk_rows=0):
+    """Bytes of each region of one FLCE call's workspace, from the library's
+    own query: chunk logits / dlogits, grad_X K-split partials, the transposed
+    head W^T, the chunk's gathered hidden states, and the O(N) rest (header,
+    per-row losses, packed-row lists)."""
+    parts = B.flce_workspace_parts(N, H, V, dt, chunk_rows)
+    parts["workspace"] = sum(parts.values())
+    return parts
+
+
+def survey_bound_bytes(parts, N, V):
+    """Peak extra memory allowed for one call: one chunk of logits, O((N + V)
+    x 16) bytes of per-row and per-vocabulary scratch, and the split-K partials
+    of the grad_X product."""
+    return parts["chunk_logits"] + (N + V) * 16 + parts["split_partials"]
 
 
 def rows_through_products(B, y):
@@ -591,6 +622,150 @@ def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
     return out
 
 
+def kernel_table(B, n_live, H, V, e, steps, step_ms):
+    """Per-class kernel times from the library's HIP-event hooks (read after
+    `steps` hooked steps): ms per launch, and for the GEMMs and the row CE the
+    algorithmic work per launch (2 x rows x H x V flop; 2 x rows x V x e bytes)
+    over that time against the MI355X peak."""
+    gemm_flops_per_step = 2.0 * n_live * H * V
+    kernels = {}
+    for kind in ("logits_gemm", "grad_xw_gemm", "grad_x_gemm", "grad_w_gemm", "row_ce", "other"):
+        tot_ms, launches = B.flce_timing_read(kind)
+        if launches == 0:
+            continue
+        entry = {"ms_per_launch": tot_ms / launches, "launches": launches}
+        if kind.endswith("gemm"):
+            # the paired launch runs two products
+            per_launch = (2 if kind == "grad_xw_gemm" else 1) * gemm_flops_per_step * steps / launches
+            entry.update(bound="mfma", unit="TFLOP/s", algorithmic_per_launch=per_launch,
+                         achieved=per_launch / (tot_ms / launches * 1e-3) / 1e12,
+                         peak=PEAK_BF16_FLOPS / 1e12)
+        elif kind == "row_ce":
+            per_launch = 2.0 * n_live * V * e * steps / launches
+            entry.update(bound="hbm", unit="GB/s", algorithmic_per_launch=per_launch,
+                         achieved=per_launch / (tot_ms / launches * 1e-3) / 1e9,
+                         peak=PEAK_HBM_BYTES / 1e9)
+        if "achieved" in entry:
+            entry["frac"] = entry["achieved"] / entry["peak"]
+        entry["share_of_step"] = tot_ms / steps / step_ms
+        kernels[kind] = entry
+    B.flce_timing_reset()
+    return kernels
+
+
+def measure_flce(torch, B, cfg, inp, dev, steps, warmup, chunk_rows=0, packing=True,
+                 hook_steps=None):
+    """Times `steps` FLCE steps of one workload (inputs resident on the GPU,
+    hooks off), then `hook_steps` more with the per-kernel HIP-event hooks on
+    (a separate pass, so the hooks' event records stay out of the headline).
+    Returns step times, executed-flop fractions, the kernel table, the peak
+    extra device memory against the one-chunk bound, and the loss."""
+    X, W, bias, y = dev
+    N, H, V = cfg["N"], cfg["H"], cfg["V"]
+    dt = B.BF16 if cfg["dtype"] == "bf16" else (B.F16 if cfg["dtype"] == "f16" else B.F32)
+    e = 4 if dt == B.F32 else 2
+    packing = packing and dt != B.F32
+    B.flce_set_row_packing(packing)
+    chunk, splits = B.flce_plan(N, H, V, dt, chunk_rows)
+    n_live = int(np.count_nonzero(inp["targets"] != -100)) if packing else N
+    parts = scratch_parts(B, N, H, V, dt, chunk_rows)
+    loss = torch.empty((1,), dtype=torch.float32, device="cuda")
+    gX = torch.empty((N, H), dtype=torch.float32, device="cuda")
+    gW = torch.empty((V, H), dtype=torch.float32, device="cuda")
+    gb = torch.empty((V,), dtype=torch.float32, device="cuda") if bias is not None else None
+    torch.cuda.synchronize()
+    io_bytes = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    ws = torch.empty((parts["workspace"],), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.flce_forward_backward(X, W, y, bias=bias, reduction=cfg["reduction"], grad_X=gX,
+                                grad_W=gW, grad_bias=gb, loss=loss, workspace=ws,
+                                chunk_rows=chunk_rows, stream=stream)
+
+    first = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for i in range(warmup):
+        if i == 0:
+            first[0].record(stream)
+        step()
+        if i == 0:
+            first[1].record(stream)
+    torch.cuda.synchronize()
+    first_call_ms = first[0].elapsed_time(first[1]) if warmup > 0 else None
+    if B.flce_check_device_error(ws) != B.OK:
+        sys.exit("device reported an out-of-range target")
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record(stream)
+    for i in range(steps):
+        step()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = marks[0].elapsed_time(marks[steps]) / steps
+    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
+    peak = torch.cuda.max_memory_allocated()
+    hook_steps = steps if hook_steps is None else hook_steps
+    B.flce_timing_reset()
+    B.flce_timing_enable(True)
+    hm = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    hm[0].record(stream)
+    for _ in range(hook_steps):
+        step()
+    hm[1].record(stream)
+    torch.cuda.synchronize()
+    B.flce_timing_enable(False)
+    hooked_ms = hm[0].elapsed_time(hm[1]) / hook_steps
+    kernels = kernel_table(B, n_live, H, V, e, hook_steps, hooked_ms)
+    step_flops = 6.0 * n_live * H * V
+    extra = peak - io_bytes
+    bound = survey_bound_bytes(parts, N, V)
+    out = {
+        "N": N, "H": H, "V": V, "reduction": cfg["reduction"], "bias": bias is not None,
+        "chunk_rows": chunk, "dx_splits": splits, "row_packing": packing,
+        "rows_through_products": n_live,
+        "ms_per_step": ms, "tokens_per_s": N / (ms * 1e-3),
+        "step_ms_median": float(np.median(per_step)), "step_ms_min": float(np.min(per_step)),
+        "first_call_ms": first_call_ms,
+        # Executed work: 6 x rows_through_products x H x V flops per step.
+        "mfma_frac_step": step_flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        "step_tflops": step_flops / (ms * 1e-3) / 1e12,
+        # 6 N H V over the step time: counts the ignored rows' products, which
+        # packing does not run, so it is not a measure of MFMA use.
+        "nominal_6NHV_frac_step": 6.0 * N * H * V / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        "peak_bytes": peak, "extra_bytes": extra,
+        "workspace_parts": parts,
+        "chunk_logits_bytes": parts["chunk_logits"],
+        "extra_over_chunk_logits": extra / parts["chunk_logits"],
+        # one chunk of logits + (N + V) x 16 bytes + the split-K partials
+        "extra_bound_bytes": bound,
+        "extra_within_bound": extra <= bound,
+        "materialised_logits_bytes": N * V * e,
+        "hooked_ms_per_step": hooked_ms, "hooked_steps": hook_steps,
+        "kernels": kernels,
+        "loss": float(loss.item()),
+    }
+    del ws, gX, gW, gb
+    torch.cuda.empty_cache()
+    return out
+
+
+def other_config(torch, B, name, steps=5, warmup=2):
+    """One of the other full-size FLCE workloads (its own inputs), timed like
+    the headline with fewer steps."""
+    from linear_cross_entropy_03_amd import synth
+    cfg = dict(synth.WORKLOADS[name])
+    t0 = time.time()
+    inp = synth.make_workload(name)
+    log(f"{name}: inputs ready in {time.time() - t0:.1f}s")
+    dev = gpu_inputs(torch, inp)
+    out = measure_flce(torch, B, cfg, inp, dev, steps, warmup, hook_steps=3)
+    out["workload"] = name
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -621,92 +796,29 @@ def main():
     inp = synth.make_workload(args.workload)
     log(f"inputs ready in {time.time() - t0:.1f}s; uploading")
     X, W, bias, y = gpu_inputs(torch, inp)
-
-    chunk, splits = B.flce_plan(N, H, V, dt, args.chunk_rows)
     packing = dt != B.F32 and not args.no_packing
-    B.flce_set_row_packing(packing)
-    # Rows that go through the products: with packing, those whose target is
-    # not ignored (the ignored ones add nothing to the loss or any gradient).
-    n_live = int(np.count_nonzero(inp["targets"] != -100)) if packing else N
-    ws_bytes = B.flce_workspace_bytes(N, H, V, dt, args.chunk_rows)
-    loss = torch.empty((1,), dtype=torch.float32, device="cuda")
-    gX = torch.empty((N, H), dtype=torch.float32, device="cuda")
-    gW = torch.empty((V, H), dtype=torch.float32, device="cuda")
-    gb = torch.empty((V,), dtype=torch.float32, device="cuda") if bias is not None else None
-    torch.cuda.synchronize()
-    io_bytes = torch.cuda.memory_allocated()
-    torch.cuda.reset_peak_memory_stats()
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
 
-    def step():
-        B.flce_forward_backward(X, W, y, bias=bias, reduction=cfg["reduction"], grad_X=gX,
-                                grad_W=gW, grad_bias=gb, loss=loss, workspace=ws,
-                                chunk_rows=args.chunk_rows, stream=stream)
-
-    log(f"plan: chunk_rows={chunk} dx_splits={splits} workspace={ws_bytes / 2**30:.2f} GiB; warmup")
     if args.profile_step:
+        B.flce_set_row_packing(packing)
+        ws = torch.empty((B.flce_workspace_bytes(N, H, V, dt, args.chunk_rows),), dtype=torch.uint8,
+                         device="cuda")
+        gX = torch.empty((N, H), device="cuda")
+        gW = torch.empty((V, H), device="cuda")
+        gb = torch.empty((V,), device="cuda") if bias is not None else None
         for _ in range(2):
-            step()
+            B.flce_forward_backward(X, W, y, bias=bias, reduction=cfg["reduction"], grad_X=gX,
+                                    grad_W=gW, grad_bias=gb, workspace=ws,
+                                    chunk_rows=args.chunk_rows)
         torch.cuda.synchronize()
         log("profile step done")
         return
-    first = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for i in range(args.warmup):
-        if i == 0:
-            first[0].record(stream)
-        step()
-        if i == 0:
-            first[1].record(stream)
-    torch.cuda.synchronize()
-    first_call_ms = first[0].elapsed_time(first[1]) if args.warmup > 0 else None
-    if B.flce_check_device_error(ws) != B.OK:
-        sys.exit("device reported an out-of-range target")
 
-    log(f"timing {args.steps} steps")
-    B.flce_timing_reset()
-    B.flce_timing_enable(True)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    start.record(stream)
-    marks[0].record(stream)
-    for i in range(args.steps):
-        step()
-        marks[i + 1].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    B.flce_timing_enable(False)
-    ms = start.elapsed_time(stop) / args.steps
-    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
-    peak = torch.cuda.max_memory_allocated()
-
-    # Per-kernel roofline from the library's HIP events over the timed region;
-    # the work is that of the rows the kernels process (n_live).
-    e = 2 if cfg["dtype"] == "bf16" else 4
-    gemm_flops_per_step = 2.0 * n_live * H * V
-    kernels = {}
-    for kind in ("logits_gemm", "grad_x_gemm", "grad_w_gemm", "row_ce", "other"):
-        tot_ms, launches = B.flce_timing_read(kind)
-        if launches == 0:
-            continue
-        entry = {"ms_per_launch": tot_ms / launches, "launches": launches}
-        if kind.endswith("gemm"):
-            per_launch = gemm_flops_per_step * args.steps / launches
-            entry.update(bound="mfma", unit="TFLOP/s", algorithmic_per_launch=per_launch,
-                         achieved=per_launch / (tot_ms / launches * 1e-3) / 1e12,
-                         peak=PEAK_BF16_FLOPS / 1e12)
-        elif kind == "row_ce":
-            per_launch = 2.0 * n_live * V * e * args.steps / launches
-            entry.update(bound="hbm", unit="GB/s", algorithmic_per_launch=per_launch,
-                         achieved=per_launch / (tot_ms / launches * 1e-3) / 1e9,
-                         peak=PEAK_HBM_BYTES / 1e9)
-        if "achieved" in entry:
-            entry["frac"] = entry["achieved"] / entry["peak"]
-        entry["share_of_step"] = tot_ms / args.steps / ms
-        kernels[kind] = entry
-    B.flce_timing_reset()
+    chunk, splits = B.flce_plan(N, H, V, dt, args.chunk_rows)
+    log(f"plan: chunk_rows={chunk} dx_splits={splits}; {args.warmup} warmup, {args.steps} timed steps")
+    head = measure_flce(torch, B, cfg, inp, (X, W, bias, y), args.steps, args.warmup,
+                        chunk_rows=args.chunk_rows, packing=packing)
+    ms = head["ms_per_step"]
+    kernels = head["kernels"]
     dom_kind = max((k for k in kernels if "achieved" in kernels[k]),
                    key=lambda k: kernels[k]["ms_per_launch"] * kernels[k]["launches"])
     dom = kernels[dom_kind]
@@ -719,32 +831,30 @@ def main():
         t_dom = traffic["kernels"].get(dom_kind, {}).get("traffic_bytes")
     roofline = {"kernel": dom_kind, "bound": dom["bound"], "achieved": dom["achieved"],
                 "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"], "traffic": t_dom,
-                "algorithmic_per_launch": dom["algorithmic_per_launch"]}
+                "algorithmic_per_launch": dom["algorithmic_per_launch"],
+                "timing": "HIP events around each launch on the library's stream, "
+                          f"over {head['hooked_steps']} steps timed after the headline's"}
 
-    tokens_per_s = N / (ms * 1e-3)
     unpacked = None
     if packing and not args.no_unpacked:
-        # The same step with every row through the products, for comparison.
-        B.flce_set_row_packing(False)
-        step()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        reps = 5
-        ev[0].record(stream)
-        for _ in range(reps):
-            step()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        B.flce_set_row_packing(True)
-        ums = ev[0].elapsed_time(ev[1]) / reps
-        unpacked = {"ms_per_step": ums, "tokens_per_s": N / (ums * 1e-3),
-                    "mfma_frac_step": 6.0 * N * H * V / (ums * 1e-3) / PEAK_BF16_FLOPS,
-                    "steps": reps}
-    extra_bound = extra_bound_bytes(N, H, V, chunk, splits, e)
-    step_flops = 6.0 * n_live * H * V
+        log("comparison: row packing off")
+        u = measure_flce(torch, B, cfg, inp, (X, W, bias, y), 5, 1, chunk_rows=args.chunk_rows,
+                         packing=False, hook_steps=1)
+        B.flce_set_row_packing(packing)
+        unpacked = {k: u[k] for k in ("ms_per_step", "tokens_per_s", "mfma_frac_step")}
+    strict = None
+    if dt != B.F32 and not args.no_strict:
+        log("comparison: transposed head off (scratch bounded by one chunk of logits)")
+        was = B.flce_set_transposed_head(False)
+        u = measure_flce(torch, B, cfg, inp, (X, W, bias, y), 5, 1, chunk_rows=args.chunk_rows,
+                         packing=packing, hook_steps=1)
+        B.flce_set_transposed_head(was)
+        strict = {k: u[k] for k in ("ms_per_step", "tokens_per_s", "mfma_frac_step", "extra_bytes",
+                                    "extra_bound_bytes", "extra_within_bound",
+                                    "extra_over_chunk_logits", "workspace_parts")}
     result = {
         "metric": "FLCE fwd+bwd tokens/s + % bf16 MFMA peak at H4096 V128256; peak HBM bytes",
-        "value": tokens_per_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -759,31 +869,18 @@ def main():
                 + ", 10% ignore_index)",
         "config": {"workload": args.workload, "N": N, "H": H, "V": V, "reduction": cfg["reduction"],
                    "bias": bias is not None, "chunk_rows": chunk, "dx_splits": splits,
-                   "row_packing": packing, "parallelism": "single GPU"},
-        "rows_through_products": n_live,
-        "step_ms_median": float(np.median(per_step)),
-        "step_ms_min": float(np.min(per_step)),
-        "first_call_ms": first_call_ms,
-        # Executed work: 6 * rows_through_products * H * V flops per step.
-        "mfma_frac_step": step_flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
-        "step_tflops": step_flops / (ms * 1e-3) / 1e12,
-        # 6 * N * H * V over the step time: counts the ignored rows' products,
-        # which packing does not run, so it is not a measure of MFMA use.
-        "nominal_6NHV_frac_step": 6.0 * N * H * V / (ms * 1e-3) / PEAK_BF16_FLOPS,
-        "unpacked": unpacked,
-        "peak_bytes": peak,
-        "extra_bytes": peak - io_bytes,
-        # bound: one chunk of logits + per-row / per-vocab scratch + split-K partials
-        "extra_bound_bytes": extra_bound,
-        "extra_within_bound": peak - io_bytes <= extra_bound,
-        "chunk_logits_bytes": chunk * ((V + 7) // 8 * 8) * e,
-        "materialised_logits_bytes": N * V * e,
+                   "row_packing": packing, "transposed_head": head["workspace_parts"]["transposed_head"] > 0,
+                   "parallelism": "single GPU"},
         "roofline": roofline,
-        "kernels": kernels,
-        "loss": float(loss.item()),
     }
-    del ws
-    torch.cuda.empty_cache()
+    for k in ("rows_through_products", "step_ms_median", "step_ms_min", "first_call_ms",
+              "mfma_frac_step", "step_tflops", "nominal_6NHV_frac_step", "peak_bytes", "extra_bytes",
+              "extra_bound_bytes", "extra_within_bound", "extra_over_chunk_logits",
+              "chunk_logits_bytes", "workspace_parts", "materialised_logits_bytes",
+              "hooked_ms_per_step", "kernels", "loss"):
+        result[k] = head[k]
+    result["unpacked"] = unpacked
+    result["transposed_head_off"] = strict
     if not args.no_vp:
         log("vocabulary-parallel shard")
         result["vocab_parallel"] = bench_vocab_parallel(torch, B, X, W, y, cfg)
@@ -805,9 +902,14 @@ def main():
     if not args.no_ce:
         log("standalone CE")
         result["ce"] = bench_ce(torch, B)
+    del X, W, bias, y
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        for key, name in (("c3", "llama1b_head_bf16"), ("c5", "vocab256k_bias_bf16")):
+            log(f"full-size workload {name}")
+            result[key] = other_config(torch, B, name)
     if not args.no_cpu_baseline:
         log("timing the FP64 oracle on a CPU sample")
-        del gX, gW
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None

@@ -97,6 +97,19 @@ int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
               int64_t* chunk_rows_out, int32_t* dx_splits_out);
 
 /*
+ * The workspace of flce_forward_backward split into its regions (pure host
+ * computation), in bytes, each rounded up to 256: parts[0] the header and the
+ * per-row losses, [1] one chunk of logits / dlogits (chunk x round_up(V, 8)
+ * elements), [2] the grad_X K-split partials (float32), [3] the packed-row
+ * lists, [4] the chunk's gathered hidden states (chunk x H elements), [5] the
+ * transposed head (H x round_up(V, 64) elements, 0 when the plan has none).
+ * The parts sum to flce_workspace_bytes. parts must hold 6 entries. Returns
+ * FLCE_OK or FLCE_E_INVALID_ARG.
+ */
+int flce_workspace_parts(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
+                         size_t* parts);
+
+/*
  * Fused linear cross-entropy, forward and backward in one call (the liger
  * README's FusedLinearCrossEntropy; the steps of the torchtune blog, Figure 1).
  *
@@ -397,10 +410,24 @@ int flce_check_device_error(const void* workspace, void* stream);
 int flce_set_row_packing(int enable);
 
 /*
+ * Transposed head for the grad_X product, on by default. With 16-bit inputs
+ * and H <= chunk rows the planner then reserves H x round_up(V, 64) elements
+ * of workspace for W^T, written once per call, so that grad_X = dZ W reads
+ * both operands k-major (a faster product); off, grad_X reads W as it is and
+ * the workspace holds no copy of W (peak scratch: one chunk of logits plus
+ * O(chunk x H) bytes). Plans, workspace sizes and calls made after the switch
+ * follow it; a workspace sized under the other setting may be too small
+ * (FLCE_E_WORKSPACE). Returns the previous setting. Process-wide, not
+ * thread-safe.
+ */
+int flce_set_transposed_head(int enable);
+
+/*
  * Kernel timing for measurement. While enabled, the library brackets each
  * kernel it launches with HIP events on that kernel's stream. flce_timing_read
  * waits for the recorded events, returns for kernel class `kind` (0 logits
- * GEMM, 1 row CE, 2 grad_X GEMM, 3 grad_W GEMM, 4 other) the summed duration
+ * GEMM, 1 row CE, 2 grad_X GEMM, 3 grad_W GEMM, 4 other, 5 grad_X and grad_W
+ * GEMMs of one chunk in a single launch) the summed duration
  * in milliseconds and the number of launches since the last reset, and
  * flce_timing_reset clears the tallies. Not thread-safe; off by default.
  */

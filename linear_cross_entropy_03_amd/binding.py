@@ -22,7 +22,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "flce.h")
 F32, BF16, F16 = 0, 1, 2
 REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 OK, E_INVALID_ARG, E_WORKSPACE, E_UNSUPPORTED, E_TARGET, E_HIP = range(6)
-TIMING_KINDS = {"logits_gemm": 0, "row_ce": 1, "grad_x_gemm": 2, "grad_w_gemm": 3, "other": 4}
+TIMING_KINDS = {"logits_gemm": 0, "row_ce": 1, "grad_x_gemm": 2, "grad_w_gemm": 3, "other": 4,
+                "grad_xw_gemm": 5}
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _int = ctypes.c_int
@@ -70,6 +71,8 @@ _SIGNATURES = {
                                                   _sz, _i64, _vp]),
     "flce_check_device_error": (_int, [_vp, _vp]),
     "flce_set_row_packing": (_int, [_int]),
+    "flce_set_transposed_head": (_int, [_int]),
+    "flce_workspace_parts": (_int, [_i64, _i64, _i64, _int, _i64, ctypes.POINTER(_sz)]),
     "flce_timing_enable": (_int, [_int]),
     "flce_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "flce_timing_reset": (_int, []),
@@ -169,6 +172,18 @@ def flce_plan(N, H, V, dtype=BF16, chunk_rows=0):
     s = _i32()
     _check(lib().flce_plan(N, H, V, dtype, chunk_rows, ctypes.byref(c), ctypes.byref(s)), "flce_plan")
     return int(c.value), int(s.value)
+
+
+WORKSPACE_PARTS = ("rows", "chunk_logits", "split_partials", "pack_lists", "gathered_rows",
+                   "transposed_head")
+
+
+def flce_workspace_parts(N, H, V, dtype=BF16, chunk_rows=0):
+    """The planner's workspace regions in bytes, by name (they sum to
+    flce_workspace_bytes)."""
+    arr = (_sz * 6)()
+    _check(lib().flce_workspace_parts(N, H, V, dtype, chunk_rows, arr), "flce_workspace_parts")
+    return dict(zip(WORKSPACE_PARTS, (int(v) for v in arr)))
 
 
 def _empty(shape, dtype, device):
@@ -496,6 +511,12 @@ def flce_check_device_error(workspace, stream=None):
 def flce_set_row_packing(enable=True):
     """Turn row packing of ignored rows on or off; returns the previous setting."""
     return bool(lib().flce_set_row_packing(1 if enable else 0))
+
+
+def flce_set_transposed_head(enable=True):
+    """Turns the grad_X product's transposed head on or off; returns the
+    previous setting (workspace sizes follow it)."""
+    return bool(lib().flce_set_transposed_head(1 if enable else 0))
 
 
 def flce_timing_enable(enable=True):

@@ -125,6 +125,9 @@ int choose_dx_splits(int64_t chunk, int64_t H, int64_t V) {
   return best;
 }
 
+// Transposed-head switch (flce_set_transposed_head); on by default.
+bool g_transposed_head = true;
+
 bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, Plan* p) {
   if (N < 0 || H <= 0 || V <= 0 || N >= kMaxRows || H >= kMaxDim || V >= kMaxDim) return false;
   if (!valid_dtype(dtype)) return false;
@@ -187,7 +190,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
   // the logits' pipeline (11% faster than reading W n-major); it costs one
   // copy of W per call and W's size in workspace, taken only when that is at
   // most one chunk of logits (H <= chunk).
-  p->wt = is16(dtype) && H <= chunk;
+  p->wt = g_transposed_head && is16(dtype) && H <= chunk;
   p->ldw = round_up(V, 64);
   p->off_wt = off;
   if (p->wt) off += align_up(static_cast<size_t>(H) * static_cast<size_t>(p->ldw) * e);
@@ -236,7 +239,16 @@ hipError_t timed(int kind, hipStream_t s, F&& launch) {
   return hipSuccess;
 }
 
-enum Kind { kKindLogits = 0, kKindRowCE = 1, kKindGradX = 2, kKindGradW = 3, kKindOther = 4 };
+enum Kind {
+  kKindLogits = 0, kKindRowCE = 1, kKindGradX = 2, kKindGradW = 3, kKindOther = 4,
+  kKindGradXW = 5  // grad_X and grad_W of a chunk in one launch
+};
+
+// Paired gradient products (one launch per chunk); 0 launches them one by one.
+#ifndef LCE_PAIR_PRODUCTS
+#define LCE_PAIR_PRODUCTS 1
+#endif
+constexpr bool g_pair_products = LCE_PAIR_PRODUCTS != 0;
 
 // Row packing switch (flce_set_row_packing); on by default.
 bool g_row_packing = true;
@@ -275,6 +287,25 @@ int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, in
   if (chunk_rows_out) *chunk_rows_out = p.chunk;
   if (dx_splits_out) *dx_splits_out = p.dx_splits;
   return FLCE_OK;
+}
+
+int flce_workspace_parts(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
+                         size_t* parts) {
+  Plan p;
+  if (parts == nullptr || !make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
+  parts[0] = p.off_chunk;                                  // header + per-row losses
+  parts[1] = p.off_split - p.off_chunk;                    // chunk logits / dlogits
+  parts[2] = (p.pack_ok ? p.off_map : p.off_wt) - p.off_split;  // grad_X K-split partials
+  parts[3] = p.pack_ok ? p.off_xs - p.off_map : 0;         // packed-row lists
+  parts[4] = p.pack_ok ? p.off_wt - p.off_xs : 0;          // gathered hidden states
+  parts[5] = p.total - p.off_wt;                           // transposed head
+  return FLCE_OK;
+}
+
+int flce_set_transposed_head(int enable) {
+  const int was = g_transposed_head ? 1 : 0;
+  g_transposed_head = enable != 0;
+  return was;
 }
 
 int flce_set_row_packing(int enable) {
@@ -439,34 +470,8 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
                              gsc.out_scale, gsc.out_shift, s, pk);
       }));
 
-    if (grad_X) {
-      GemmDesc g2{};
-      g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
-      grad_x_head(p, W, H, ws, g2);
-      g2.M = rows; g2.N = H; g2.K = V;
-      scale_output(g2, gsc);
-      live(g2, 0);
-      void* out = static_cast<char*>(grad_X) + (pack ? 0 : static_cast<size_t>(r0) * H * ge);
-      const int splits = (pack && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
-      if (splits > 1 || (pack && accum_gx)) {
-        g2.epilogue = kEpiStoreF32;
-        g2.C = split_buf; g2.ldc = H;
-        g2.k_splits = splits; g2.split_stride = rows * H;
-        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
-        LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype,
-                                      accum_gx, s, pk);
-        }));
-      } else {
-        g2.epilogue = accum_gx ? (g16 ? kEpiAccum16 : kEpiAccumF32) : (g16 ? kEpiStore16 : kEpiStoreF32);
-        g2.C = out; g2.ldc = H; g2.k_splits = 1;
-        if (pack) g2.row_map = pk.map;
-        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
-      }
-    }
-
+    GemmDesc g3{};
     if (grad_W) {
-      GemmDesc g3{};
       g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
       g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
       g3.C = grad_W; g3.ldc = H;
@@ -475,8 +480,47 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
       g3.k_splits = 1;
       scale_output(g3, gsc);
       live(g3, 1);
-      LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
     }
+    // With the transposed head, grad_X and grad_W run as one launch (the
+    // grad_W tiles fill the CUs grad_X's last round of tiles leaves idle),
+    // so the last packed chunk needs no extra K split for its tail.
+    const bool pair_ok = grad_X != nullptr && grad_W != nullptr && p.wt && g_pair_products;
+    if (grad_X) {
+      GemmDesc g2{};
+      g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
+      grad_x_head(p, W, H, ws, g2);
+      g2.M = rows; g2.N = H; g2.K = V;
+      scale_output(g2, gsc);
+      live(g2, 0);
+      void* out = static_cast<char*>(grad_X) + (pack ? 0 : static_cast<size_t>(r0) * H * ge);
+      const int splits = (pack && r0 + p.chunk >= N && !pair_ok) ? p.last_splits : p.dx_splits;
+      const bool via_split = splits > 1 || (pack && accum_gx);
+      if (via_split) {
+        g2.epilogue = kEpiStoreF32;
+        g2.C = split_buf; g2.ldc = H;
+        g2.k_splits = splits; g2.split_stride = rows * H;
+      } else {
+        g2.epilogue = accum_gx ? (g16 ? kEpiAccum16 : kEpiAccumF32) : (g16 ? kEpiStore16 : kEpiStoreF32);
+        g2.C = out; g2.ldc = H; g2.k_splits = 1;
+        if (pack) g2.row_map = pk.map;
+      }
+      if (pair_ok && gemm16_pair_supported(g2, g3)) {
+        LCE_TRY(timed(kKindGradXW, s, [&] { return launch_gemm16_pair(g2, g3, dtype == FLCE_F16, s); }));
+        if (via_split)
+          LCE_TRY(timed(kKindOther, s, [&] {
+            return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype,
+                                        accum_gx, s, pk);
+          }));
+        continue;  // grad_W of this chunk is done too
+      }
+      LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+      if (via_split)
+        LCE_TRY(timed(kKindOther, s, [&] {
+          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype,
+                                      accum_gx, s, pk);
+        }));
+    }
+    if (grad_W) LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
   }
   return FLCE_OK;
 }
@@ -596,8 +640,13 @@ int flce_multihead_impl(const void* X, const void* W, const void* bias, const in
   char* ws = static_cast<char*>(workspace);
   const size_t e = elem_bytes(dtype);
   const size_t ge = grad_dtype == FLCE_F32 ? 4 : 2;
-  // The call's own header (first slot of the plan) collects nothing; each
-  // head counts its targets into its own slot so N_valid is per head.
+  // Each head counts its targets into its own slot so N_valid is per head;
+  // the call's own header (the first slot of the plan) counts all K x N
+  // targets, so that flce_check_device_error sees a bad target in any head.
+  LCE_TRY(timed(kKindOther, s, [&] {
+    return launch_count_targets(targets, K * N, V, ignore_index, reduction,
+                                reinterpret_cast<WsHeader*>(ws), s);
+  }));
   for (int64_t k = 0; k < K; ++k) {
     char* hs = ws + p.total + static_cast<size_t>(k) * slot;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(hs);

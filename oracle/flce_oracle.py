@@ -193,6 +193,49 @@ def flce_rows(X, W, targets, rows, bias=None, ignore_index=-100, reduction="mean
     return lr, dZ @ W
 
 
+def flce_sampled(X, W, targets, token_rows, vocab_rows, bias=None, ignore_index=-100,
+                 reduction="mean", row_block=1024):
+    """`flce` for shapes whose full gradients are too large to keep: the loss
+    of every row and the reduced loss, with grad_X only for the listed token
+    rows and grad_W / grad_bias only for the listed vocabulary rows. The same
+    definition and row blocking as `flce`, in one pass over the row blocks:
+    each block's logits are materialised, its loss rows and dlogits taken,
+    and only the requested gradient rows kept.
+
+    Returns (loss, loss_rows [N], grad_X_rows [R, H], grad_W_rows [Q, H],
+    grad_bias_rows [Q] or None, n_valid)."""
+    X = _f64(X)
+    W = _f64(W)
+    N, H = X.shape
+    V = W.shape[0]
+    b = None if bias is None else _f64(bias)
+    y = np.asarray(targets).astype(np.int64)
+    valid, _ = target_masks(y, V, ignore_index)
+    n_valid = int(valid.sum())
+    scale = reduction_scale(n_valid, reduction)
+    tr = np.asarray(token_rows, dtype=np.int64)
+    vr = np.asarray(vocab_rows, dtype=np.int64)
+    loss_rows = np.zeros(N)
+    gX = np.zeros((len(tr), H))
+    gW = np.zeros((len(vr), H))
+    gb = np.zeros(len(vr)) if b is not None else None
+    for r0 in range(0, N, max(1, int(row_block))):
+        r1 = min(N, r0 + int(row_block))
+        Xb = X[r0:r1]
+        Z = Xb @ W.T
+        if b is not None:
+            Z = Z + b[None, :]
+        lr, dZ = _rows_loss_and_dlogits(Z, y[r0:r1], valid[r0:r1], scale)
+        loss_rows[r0:r1] = lr
+        here = np.flatnonzero((tr >= r0) & (tr < r1))
+        if len(here):
+            gX[here] = dZ[tr[here] - r0] @ W
+        gW += dZ[:, vr].T @ Xb
+        if gb is not None:
+            gb += dZ[:, vr].sum(axis=0)
+    return _reduce(loss_rows, n_valid, reduction), loss_rows, gX, gW, gb, n_valid
+
+
 def flce_grad_w_rows(X, W, targets, vocab_rows, bias=None, ignore_index=-100,
                      reduction="mean", row_block=1024):
     """grad_W[v, :] and grad_bias[v] for selected vocabulary rows v, summed over

@@ -97,14 +97,29 @@ def test_kernel_classes_cover_the_launched_gemms():
     (32768, 4096, 128256, "bf16", 0), (8192, 2048, 128256, "bf16", 0),
     (32768, 4096, 256000, "bf16", 0), (32768, 4096, 128256, "bf16", 2048),
     (256, 64, 1024, "f32", 0), (1000, 136, 4099, "bf16", 256)])
-def test_memory_bound_covers_the_workspace(N, H, V, dtype, chunk):
-    """The bench's memory model (extra_bound_bytes) holds the library's own
-    workspace query for the planned chunk, with under 1% to spare beyond the
-    256-byte alignment of its regions: peak extra memory is the workspace."""
+def test_workspace_parts_and_the_one_chunk_bound(N, H, V, dtype, chunk):
+    """The library's workspace regions sum to its workspace query and have the
+    documented sizes; the bench's bound (one chunk of logits + (N + V) x 16 +
+    split-K partials) then holds the workspace except for the transposed head
+    and the chunk's gathered hidden states, which the bench reports apart."""
     from linear_cross_entropy_03_amd import binding as B
     dt = B.BF16 if dtype == "bf16" else B.F32
-    c, s = B.flce_plan(N, H, V, dt, chunk)
-    ws = B.flce_workspace_bytes(N, H, V, dt, chunk)
-    bound = bench.extra_bound_bytes(N, H, V, c, s, 2 if dtype == "bf16" else 4)
-    assert ws <= bound
-    assert bound - ws <= 0.01 * ws + 16 * 256 + (N + V) * 16
+    e = 2 if dtype == "bf16" else 4
+    up = lambda x: (x + 255) // 256 * 256
+    for wt_on in (True, False):
+        was = B.flce_set_transposed_head(wt_on)
+        try:
+            c, s = B.flce_plan(N, H, V, dt, chunk)
+            ws = B.flce_workspace_bytes(N, H, V, dt, chunk)
+            parts = bench.scratch_parts(B, N, H, V, dt, chunk)
+        finally:
+            B.flce_set_transposed_head(was)
+        assert parts["workspace"] == ws
+        assert parts["chunk_logits"] == up(c * ((V + 7) // 8 * 8) * e)
+        has_wt = wt_on and e == 2 and H <= c
+        assert parts["transposed_head"] == (up(H * ((V + 63) // 64 * 64) * e) if has_wt else 0)
+        assert parts["gathered_rows"] == (up(c * H * e) if e == 2 else 0)
+        assert parts["rows"] <= 256 + up(4 * N) and parts["pack_lists"] <= 3 * up(4 * N) + 4096
+        bound = bench.survey_bound_bytes(parts, N, V)
+        rest = ws - parts["transposed_head"] - parts["gathered_rows"]
+        assert rest <= bound

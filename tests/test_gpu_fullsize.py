@@ -1,35 +1,50 @@
 """GPU parity at the full benchmark shapes, in the launch configuration the
-benchmark times (planner-chosen chunking), on outputs the FP64 oracle can
-compute one by one, plus properties that hold at any size.
+benchmark times (planner-chosen chunking), against the FP64 oracle's values
+stored under tests/golden/fullsize_<workload>.npz (written by
+tests/golden/make_fullsize_golden.py, which calls only the oracle).
 
 Shapes: Llama-3.2-1B head (N 8192, H 2048, V 128256, mean; bf16 and IEEE half),
 Llama-3-8B head (N 32768, H 4096, V 128256, Zipf targets, mean), 256k vocabulary with
 bias (N 32768, H 4096, V 256000, sum).
 
-Per workload:
-  * sampled token rows: per-row loss and grad_X rows against the oracle
-    (the 16-bit bar: 2e-3 of the largest sampled loss, 1e-2 of the largest
-    sampled |grad_X|), ignored rows exactly zero;
-  * the reduced loss equals the float64 reduction of the per-row losses of a
-    reduction="none" call on the same inputs;
+Per workload, at the 16-bit bar (loss relative error 2e-3, gradients 1e-2 of
+the oracle's largest |g| over the stored rows):
+  * the reduced loss against the oracle's;
+  * every row's loss (a reduction="none" call) against the oracle's, with
+    ignored rows exactly zero;
+  * grad_X on 256 stored token rows (first, last, ignored rows, rows of the
+    most frequent target, random rows), ignored rows exactly zero;
+  * grad_W and grad_bias on 64 stored vocabulary rows (the most frequent
+    target, a target-free id, the first and last ids, random ids);
   * sum over v of grad_W[v, :] and of grad_bias vanish up to 16-bit dlogits
-    rounding (at most 2**-8 per valid row);
-  * sampled vocabulary rows of grad_W (and grad_bias): the most frequent
-    target, a target-free row and random rows, against the oracle (this needs
-    the oracle's float64 logsumexp of every token row).
+    rounding (at most 2**-8 per valid row).
+The inputs are regenerated from their seed; a SHA-256 of each input array
+stored with the expected values guards against a changed generator.
 """
+
+import hashlib
+import os
 
 import numpy as np
 import pytest
 
-from gpu_util import TOL, check_max_rel, check_scalar, say, to_dev, to_host, torch_or_skip
+from gpu_util import ROOT, TOL, check_max_rel, check_scalar, say, to_dev, to_host, torch_or_skip
 from linear_cross_entropy_03_amd import synth
-from oracle import flce_oracle as O
 
 pytestmark = pytest.mark.gpu
 
 WORKLOADS = ["llama1b_head_bf16", "llama1b_head_f16", "llama8b_head_bf16", "vocab256k_bias_bf16"]
 _CACHE = {}
+
+
+def golden(name):
+    path = os.path.join(ROOT, "tests", "golden", f"fullsize_{name}.npz")
+    with np.load(path, allow_pickle=False) as z:
+        return {k: z[k] for k in z.files}
+
+
+def _digest(arr):
+    return "" if arr is None else hashlib.sha256(np.ascontiguousarray(arr).tobytes()).hexdigest()
 
 
 @pytest.fixture(scope="module")
@@ -47,19 +62,19 @@ def workload(request, B):
     return _results(B, request.param)
 
 
-def _f64(a):
-    return None if a is None else np.asarray(a, dtype=np.float64)
-
-
 def _results(B, name):
-    """Inputs and GPU outputs of one workload (computed once per module)."""
+    """Inputs, expected values and GPU outputs of one workload (computed once
+    per module; the gradients are kept only at the stored rows)."""
     if _CACHE.get("name") == name:
         return _CACHE
     import torch
     _CACHE.clear()
     cfg = synth.WORKLOADS[name]
+    g = golden(name)
     say(name, "generating inputs")
     inp = synth.make_workload(name)
+    for k in ("X", "W", "bias", "targets"):
+        assert _digest(inp[k]) == str(g["sha_" + k]), f"{name}: regenerated {k} differs from the stored inputs"
     dt = cfg["dtype"]
     X, W, b = (to_dev(inp[k], dt) for k in ("X", "W", "bias"))
     y = to_dev(inp["targets"], "i32")
@@ -67,8 +82,14 @@ def _results(B, name):
     say(name, "flce", cfg["reduction"], "launch configuration", B.flce_plan(cfg["N"], cfg["H"], cfg["V"], code))
     loss, gX, gW, gb = B.flce_forward_backward(X, W, y, bias=b, reduction=cfg["reduction"])
     torch.cuda.synchronize()
-    out = {"loss": to_host(loss), "gX": to_host(gX, f64=False), "gW": to_host(gW, f64=False),
-           "gb": to_host(gb)}
+    tr = torch.from_numpy(g["token_rows"]).cuda()
+    vr = torch.from_numpy(g["vocab_rows"]).cuda()
+    valid = y != -100
+    out = {"loss": to_host(loss), "gX_rows": to_host(gX[tr]), "gW_rows": to_host(gW[vr]),
+           "gb_rows": None if gb is None else to_host(gb[vr]),
+           "gX_ignored_absmax": float(gX[~valid].abs().max()),
+           "gW_colsum": to_host(gW.sum(dim=0, dtype=torch.float64)),
+           "gb_sum": None if gb is None else float(gb.sum(dtype=torch.float64))}
     del gX, gW, gb
     say(name, "flce none (loss only)")
     rows, _, _, _ = B.flce_forward_backward(X, W, y, bias=b, reduction="none", grad_X=False,
@@ -77,95 +98,89 @@ def _results(B, name):
     out["rows"] = to_host(rows)
     del X, W, b, y
     torch.cuda.empty_cache()
-    _CACHE.update(name=name, cfg=cfg, inp=inp, **out)
+    _CACHE.update(name=name, cfg=cfg, inp=inp, golden=g, **out)
     return _CACHE
 
 
 @pytest.mark.timeout(300)
-def test_fullsize_rows_and_properties(workload):
+def test_fullsize_loss_and_every_row(workload):
     r = workload
-    cfg, inp, name = r["cfg"], r["inp"], r["name"]
-    y = inp["targets"]
-    valid = y != -100
-    n_valid = int(valid.sum())
-    red = cfg["reduction"]
-
-    # Reduced loss == float64 reduction of the per-row losses.
-    total = float(np.sum(r["rows"]))
-    expect = total / n_valid if red == "mean" else total
-    check_scalar(r["loss"], expect, 1e-6, "loss vs its rows")
-    assert np.all(r["rows"][~valid] == 0.0)
-    assert np.all(r["gX"][~valid] == 0.0)
-
-    # Sampled token rows against the oracle.
-    rng = np.random.default_rng(123)
-    rows = np.unique(np.concatenate([
-        rng.choice(cfg["N"], 24, replace=False),
-        np.flatnonzero(~valid)[:2],
-        np.flatnonzero(y == np.bincount(y[valid]).argmax())[:2],
-        [0, cfg["N"] - 1]]))
-    say(name, "oracle rows", len(rows))
-    lr, gx = O.flce_rows(_f64(inp["X_f32"]), _f64(inp["W_f32"]), y, rows, bias=_f64(inp["bias_f32"]),
-                         reduction=red)
+    cfg, inp, g = r["cfg"], r["inp"], r["golden"]
     t = TOL[cfg["dtype"]]
-    check_max_rel(r["rows"][rows], lr, t["loss"], "sampled loss rows")
-    check_max_rel(r["gX"][rows].astype(np.float64), gx, t["grad"], "sampled grad_X rows")
+    valid = inp["targets"] != -100
+    assert int(g["n_valid"]) == int(valid.sum())
+    check_scalar(r["loss"], float(g["loss"]), t["loss"], "reduced loss")
+    check_max_rel(r["rows"], g["loss_rows"], t["loss"], "every row's loss")
+    assert np.all(r["rows"][~valid] == 0.0), "ignored rows must have exact zero loss"
 
-    # Row sums of dlogits vanish: sum_v grad_W[v, :] ~ 0, sum grad_bias ~ 0.
-    s = 1.0 / n_valid if red == "mean" else 1.0
+
+@pytest.mark.timeout(300)
+def test_fullsize_gradient_rows(workload):
+    r = workload
+    cfg, g = r["cfg"], r["golden"]
+    t = TOL[cfg["dtype"]]
+    check_max_rel(r["gX_rows"], g["grad_X_rows"].astype(np.float64), t["grad"], "grad_X rows")
+    assert r["gX_ignored_absmax"] == 0.0, "ignored rows must have exact zero grad_X"
+    check_max_rel(r["gW_rows"], g["grad_W_rows"].astype(np.float64), t["grad"], "grad_W rows")
+    if r["gb_rows"] is not None:
+        check_max_rel(r["gb_rows"], g["grad_bias_rows"], t["grad"], "grad_bias rows")
+
+
+@pytest.mark.timeout(300)
+def test_fullsize_dlogits_rows_sum_to_zero(workload):
+    """Each dlogits row sums to zero, so sum_v grad_W[v, :] and sum grad_bias
+    vanish up to the 16-bit rounding of the stored dlogits."""
+    r = workload
+    cfg, inp = r["cfg"], r["inp"]
+    n_valid = int((inp["targets"] != -100).sum())
+    s = 1.0 / n_valid if cfg["reduction"] == "mean" else 1.0
     xmax = float(np.abs(inp["X_f32"]).max())
-    assert np.abs(r["gW"].sum(axis=0, dtype=np.float64)).max() <= n_valid * 2.0 ** -8 * s * xmax
-    if r["gb"] is not None:
-        assert abs(float(r["gb"].sum())) <= n_valid * 2.0 ** -8 * s
+    assert np.abs(r["gW_colsum"]).max() <= n_valid * 2.0 ** -8 * s * xmax
+    if r["gb_sum"] is not None:
+        assert abs(r["gb_sum"]) <= n_valid * 2.0 ** -8 * s
 
 
 @pytest.mark.timeout(300)
-def test_fullsize_grad_w_rows(workload):
-    r = workload
-    cfg, inp, name = r["cfg"], r["inp"], r["name"]
-    y = inp["targets"]
-    valid = y != -100
-    counts = np.bincount(y[valid], minlength=cfg["V"])
-    rng = np.random.default_rng(7)
-    vrows = np.unique(np.concatenate([[int(counts.argmax())], [int(np.flatnonzero(counts == 0)[0])],
-                                      rng.choice(cfg["V"], 6, replace=False)]))
-    say(name, "oracle grad_W rows (float64 logsumexp over every token row)")
-    gw, gb = O.flce_grad_w_rows(_f64(inp["X_f32"]), _f64(inp["W_f32"]), y, vrows,
-                                bias=_f64(inp["bias_f32"]), reduction=cfg["reduction"])
-    t = TOL[cfg["dtype"]]
-    check_max_rel(r["gW"][vrows].astype(np.float64), gw, t["grad"], "sampled grad_W rows")
-    if r["gb"] is not None:
-        check_max_rel(r["gb"][vrows], gb, t["grad"], "sampled grad_bias entries")
-
-
-@pytest.mark.timeout(300)
-def test_fullsize_packing_matches_unpacked(B):
-    """The Llama-3-8B head with row packing (the benchmarked configuration)
-    against the same call with packing off, compared on the device: the loss
-    is bitwise equal, grad_X differs only in the last chunk's rows (whose K
-    is split in two) and by float32 summation order, grad_W by where the
-    chunk boundaries fall, and ignored rows of grad_X are exactly zero."""
+def test_fullsize_packing_and_transposed_head_switches(B):
+    """The Llama-3-8B head in its benchmarked configuration (row packing and
+    the transposed head on) against the same call with packing off and with
+    the transposed head off, compared on the device: the loss is bitwise
+    equal, grad_X and grad_W differ by float32 summation order only (the last
+    chunk's K split, chunk boundaries, a different grad_X kernel), ignored
+    rows of grad_X are exactly zero; each variant's stored rows also meet the
+    oracle's bar."""
     import torch
     name = "llama8b_head_bf16"
     cfg = synth.WORKLOADS[name]
-    say(name, "packed against unpacked: generating inputs")
+    g = golden(name)
+    say(name, "switches: generating inputs")
     inp = synth.make_workload(name)
     X, W = to_dev(inp["X"], "bf16"), to_dev(inp["W"], "bf16")
     y = to_dev(inp["targets"], "i32")
+    tr = torch.from_numpy(g["token_rows"]).cuda()
+    vr = torch.from_numpy(g["vocab_rows"]).cuda()
     out = {}
-    was = B.flce_set_row_packing(True)
+    was_p, was_t = B.flce_set_row_packing(True), B.flce_set_transposed_head(True)
     try:
-        for pack in (True, False):
+        for key, pack, wt in (("ref", True, True), ("unpacked", False, True), ("no_wt", True, False)):
             B.flce_set_row_packing(pack)
-            say(name, "packing", pack)
-            out[pack] = B.flce_forward_backward(X, W, y, reduction=cfg["reduction"])
+            B.flce_set_transposed_head(wt)
+            say(name, key, "packing", pack, "transposed head", wt)
+            out[key] = B.flce_forward_backward(X, W, y, reduction=cfg["reduction"])
             torch.cuda.synchronize()
     finally:
-        B.flce_set_row_packing(was)
-    (l1, gx1, gw1, _), (l0, gx0, gw0, _) = out[True], out[False]
-    assert float(l1[0]) == float(l0[0])
-    for a, r, name_ in ((gx1, gx0, "grad_X"), (gw1, gw0, "grad_W")):
-        err = float((a - r).abs().max())
-        assert err <= 1e-5 * float(r.abs().max()), f"{name_}: {err}"
+        B.flce_set_row_packing(was_p)
+        B.flce_set_transposed_head(was_t)
+    l1, gx1, gw1, _ = out["ref"]
     ignored = y == -100
-    assert float(gx1[ignored].abs().max()) == 0.0
+    for key in ("unpacked", "no_wt"):
+        l0, gx0, gw0, _ = out[key]
+        assert float(l1[0]) == float(l0[0]), key
+        for a, r_, what in ((gx1, gx0, "grad_X"), (gw1, gw0, "grad_W")):
+            err = float((a - r_).abs().max())
+            assert err <= 1e-5 * float(r_.abs().max()), f"{key} {what}: {err}"
+        assert float(gx0[ignored].abs().max()) == 0.0, key
+        check_max_rel(to_host(gx0[tr]), g["grad_X_rows"].astype(np.float64), TOL["bf16"]["grad"],
+                      f"{key} grad_X rows")
+        check_max_rel(to_host(gw0[vr]), g["grad_W_rows"].astype(np.float64), TOL["bf16"]["grad"],
+                      f"{key} grad_W rows")

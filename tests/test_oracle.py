@@ -356,6 +356,29 @@ def test_sampled_helpers_agree_with_full():
     np.testing.assert_allclose(gb, g["bias"][vr], atol=1e-14)
 
 
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_one_pass_sampled_flce_agrees_with_full(reduction):
+    """flce_sampled (the full-size golden values) keeps exactly the rows the
+    full oracle computes: every loss row, the reduction, and the selected
+    grad_X / grad_W / grad_bias rows, across several row blocks."""
+    rng = np.random.default_rng(18)
+    X, W, b, y = _rand_problem(rng, N=37, H=6, V=15, n_ignored=5)
+    y[3] = 40  # out of range: treated as ignored
+    loss, g, info = O.flce(X, W, y, bias=b, reduction=reduction, row_block=8)
+    tr, vr = np.array([0, 7, 8, 36, 3]), np.array([14, 0, 6])
+    l2, rows, gx, gw, gb, nv = O.flce_sampled(X, W, y, tr, vr, bias=b, reduction=reduction,
+                                              row_block=8)
+    np.testing.assert_allclose(np.asarray(l2), np.asarray(loss), rtol=1e-15, atol=0)
+    np.testing.assert_array_equal(rows, info["loss_rows"])
+    assert nv == info["n_valid"]
+    np.testing.assert_allclose(gx, g["X"][tr], atol=1e-15)
+    np.testing.assert_allclose(gw, g["W"][vr], atol=1e-14)
+    np.testing.assert_allclose(gb, g["bias"][vr], atol=1e-14)
+    assert np.all(gx[4] == 0.0)
+    _, _, _, _, gb0, _ = O.flce_sampled(X, W, y, tr, vr, reduction=reduction)
+    assert gb0 is None
+
+
 # ------------------------------------------------- vocabulary-shard backward
 
 def _lse_by_loops(Z):
