@@ -216,6 +216,24 @@ int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* ta
                         size_t workspace_bytes, void* stream);
 
 /*
+ * ce_forward_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The call's scratch (the 256-byte header
+ * and one float per row) lives in a static device array of 16 MiB + 256 bytes
+ * that the library holds on each device it runs on until the process ends;
+ * the call itself allocates nothing. N is limited to 4194304 rows
+ * (FLCE_E_UNSUPPORTED beyond, before anything is launched). All calls on one
+ * device share that array: calls that overlap on one device (different
+ * streams, or threads) race and must be serialised by the caller. Other
+ * arguments, outputs and errors as ce_forward_backward; an out-of-range
+ * target is treated as ignored, and is not reported (there is no workspace to
+ * pass to flce_check_device_error).
+ */
+int ce_forward_backward_noalloc(const void* logits, void* grad_logits, const int32_t* targets,
+                                int64_t N, int64_t V, int dtype, int32_t ignore_index,
+                                int reduction, float* loss, void* stream);
+
+/*
  * Statistics of one vocabulary shard (the per-rank part of vocab-parallel CE in
  * the DeepSpeed and Megatron pages), for logits columns covering global ids
  * [vocab_start, vocab_start + V_local) of V_global. For each row n:

@@ -38,6 +38,7 @@ _SIGNATURES = {
                                         _int, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _vp]),
     "ce_workspace_bytes": (_sz, [_i64, _i64]),
     "ce_forward_backward": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _i32, _int, _vp, _vp, _sz, _vp]),
+    "ce_forward_backward_noalloc": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _i32, _int, _vp, _vp]),
     "ce_shard_stats": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _int, _i32, _vp, _vp, _vp, _vp,
                               _sz, _vp]),
     "flce_shard_stats": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _i32,
@@ -311,6 +312,29 @@ def ce_forward_backward(logits, targets, ignore_index=-100, reduction="mean", gr
         _ptr(loss, "loss", torch.float32), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "ce_forward_backward")
+    return loss, g
+
+
+def ce_forward_backward_noalloc(logits, targets, ignore_index=-100, reduction="mean",
+                                grad_logits=True, loss=None, stream=None):
+    """ce_forward_backward through the entry point that takes no workspace
+    (its scratch is the library's per-device static array; N <= 4194304).
+    Outputs are the caller's (allocated here with torch when not given)."""
+    N, V = logits.shape
+    dt = _dtype_code(logits)
+    if isinstance(grad_logits, torch.Tensor):
+        g = grad_logits
+    elif grad_logits:
+        g = torch.empty_like(logits)
+    else:
+        g = None
+    if loss is None:
+        loss = _empty((N,) if reduction == "none" else (1,), torch.float32, logits.device)
+    st = lib().ce_forward_backward_noalloc(
+        _ptr(logits, "logits"), _ptr(g, "grad_logits", logits.dtype),
+        _ptr(targets, "targets", torch.int32), N, V, dt, ignore_index, _red(reduction),
+        _ptr(loss, "loss", torch.float32), _stream(stream))
+    _check(st, "ce_forward_backward_noalloc")
     return loss, g
 
 

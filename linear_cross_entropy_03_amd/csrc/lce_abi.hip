@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "../../include/flce.h"
@@ -739,6 +740,68 @@ int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* ta
       return launch_reduce_loss(loss_rows, N, hdr, reduction, loss, s);
     }));
   return FLCE_OK;
+}
+
+}  // extern "C"
+
+// Scratch of ce_forward_backward_noalloc: the workspace of a standalone CE
+// call of up to kNoAllocMaxRows rows (the 256-byte header and one float per
+// row), 16 MiB + 256 bytes per device, held until the process ends. Host code
+// never passes `scratch` itself to a kernel (on the host the name is only a
+// stand-in); it uses the device address that hipGetSymbolAddress returns for
+// each device.
+namespace {
+constexpr int64_t kNoAllocMaxRows = int64_t(1) << 22;
+constexpr size_t kNoAllocBytes = 256 + (size_t(1) << 22) * sizeof(float);
+constexpr int kMaxDevices = 64;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device of `stream` (looked up once
+// per device, with that device current); null on a HIP error.
+void* scratch_on(hipStream_t stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (e != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int ce_forward_backward_noalloc(const void* logits, void* grad_logits, const int32_t* targets,
+                                int64_t N, int64_t V, int dtype, int32_t ignore_index,
+                                int reduction, float* loss, void* stream) {
+  if (N > kNoAllocMaxRows) return FLCE_E_UNSUPPORTED;
+  int st = validate_common(dtype, reduction);
+  if (st != FLCE_OK) return st;
+  if (N < 0 || V <= 0 || loss == nullptr) return FLCE_E_INVALID_ARG;
+  if (N > 0 && (logits == nullptr || targets == nullptr)) return FLCE_E_INVALID_ARG;
+  void* ws = scratch_on(static_cast<hipStream_t>(stream));
+  if (ws == nullptr) return FLCE_E_HIP;
+  // Same kernels as the workspace call; every header field and loss row they
+  // read is written earlier in the same call, so nothing needs clearing.
+  return ce_forward_backward(logits, grad_logits, targets, N, V, dtype, ignore_index, reduction,
+                             loss, ws, kNoAllocBytes, stream);
 }
 
 int ce_shard_stats(const void* logits_shard, const int32_t* targets, int64_t N, int64_t V_local,

@@ -160,6 +160,18 @@ def test_ce_and_shard_argument_errors(B):
     assert L.flce_check_device_error(None, None) == B.E_INVALID_ARG
 
 
+def test_noalloc_ce_argument_errors(B):
+    """The entry point without a workspace rejects sizes beyond its static
+    scratch (and other bad arguments) before touching the device."""
+    L = B.lib()
+    assert L.ce_forward_backward_noalloc(16, 16, 16, (1 << 22) + 1, 10, B.BF16, -100, 2, 16,
+                                         None) == B.E_UNSUPPORTED
+    assert L.ce_forward_backward_noalloc(16, 16, 16, 4, 10, B.BF16, -100, 9, 16, None) == B.E_INVALID_ARG
+    assert L.ce_forward_backward_noalloc(16, 16, 16, 4, 0, B.BF16, -100, 2, 16, None) == B.E_INVALID_ARG
+    assert L.ce_forward_backward_noalloc(16, 16, 16, 4, 10, B.BF16, -100, 2, None, None) == B.E_INVALID_ARG
+    assert L.ce_forward_backward_noalloc(None, 16, 16, 4, 10, B.BF16, -100, 2, 16, None) == B.E_INVALID_ARG
+
+
 def test_vocab_parallel_argument_errors(B):
     L = B.lib()
     # ce_combine_shard_stats(max, sumexp, target, P, N, targets, V_global, ign, red, lse, loss, ws, wsb, stream)

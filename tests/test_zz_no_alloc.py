@@ -1,0 +1,63 @@
+"""The entry point that allocates nothing (ce_forward_backward_noalloc),
+through the C ABI, against ce_forward_backward with a workspace: the same
+kernels, so the loss and the gradient are bitwise equal, on two calls in a
+row (the second with fewer rows, so the per-device scratch still holds the
+first call's contents) and across the two launch paths (rows counted inside
+the row kernel for N <= 2048, by a separate launch above)."""
+
+import numpy as np
+import pytest
+
+from gpu_util import say, to_dev, torch_or_skip
+from linear_cross_entropy_03_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    torch_or_skip()
+    from linear_cross_entropy_03_amd import binding
+    binding.lib()
+    return binding
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_noalloc_matches_workspace_call(B, reduction):
+    import torch
+    outs = []
+    for N, V, seed in ((3000, 4099, 71), (700, 4099, 72)):
+        inp = synth.make_ce_inputs(N, V, "bf16", std=2.0, ignore_frac=0.05, seed=seed)
+        Z, y = to_dev(inp["logits"], "bf16"), to_dev(inp["targets"], "i32")
+        say("noalloc CE", reduction, N, V)
+        l0, g0 = B.ce_forward_backward_noalloc(Z, y, reduction=reduction)
+        l1, g1 = B.ce_forward_backward(Z, y, reduction=reduction)
+        torch.cuda.synchronize()
+        assert torch.equal(l0, l1), (N, reduction)
+        assert torch.equal(g0.view(torch.int16), g1.view(torch.int16)), (N, reduction)
+        outs.append(float(l0.double().sum()))
+    assert np.isfinite(outs).all()
+
+
+def test_noalloc_in_place_fp32(B):
+    import torch
+    inp = synth.make_ce_inputs(2048, 1000, "f32", std=2.0, ignore_frac=0.1, seed=73)
+    Z = to_dev(inp["logits"], "f32")
+    y = to_dev(inp["targets"], "i32")
+    ref_l, ref_g = B.ce_forward_backward(Z.clone(), y, reduction="mean")
+    say("noalloc CE in place fp32")
+    l0, g0 = B.ce_forward_backward_noalloc(Z, y, reduction="mean", grad_logits=Z)
+    torch.cuda.synchronize()
+    assert g0.data_ptr() == Z.data_ptr()
+    assert torch.equal(l0, ref_l) and torch.equal(g0, ref_g)
+
+
+def test_noalloc_size_limit(B):
+    import torch
+    Z = torch.zeros(16, 8, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(16, dtype=torch.int32, device="cuda")
+    loss = torch.zeros(1, device="cuda")
+    st = B.lib().ce_forward_backward_noalloc(Z.data_ptr(), Z.data_ptr(), y.data_ptr(),
+                                             (1 << 22) + 1, 8, B.BF16, -100, 2, loss.data_ptr(),
+                                             torch.cuda.current_stream().cuda_stream)
+    assert st == B.E_UNSUPPORTED
