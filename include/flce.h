@@ -209,6 +209,8 @@ size_t ce_workspace_bytes(int64_t N, int64_t V);
  *   grad_logits [N, V] (same dtype), or == logits (in place), or NULL (loss only)
  *   targets     [N] int32;  loss [1] or [N] (NONE) float32
  * When grad_logits is neither NULL nor logits, logits is not modified.
+ * N is limited to 4194303 rows (one launch covers all rows with one
+ * workgroup of up to 1024 lanes each): FLCE_E_UNSUPPORTED beyond.
  */
 int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* targets,
                         int64_t N, int64_t V, int dtype, int32_t ignore_index,
@@ -221,8 +223,9 @@ int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* ta
  * harnesses that forbid hipMalloc). The call's scratch (the 256-byte header
  * and one float per row) lives in a static device array of 16 MiB + 256 bytes
  * that the library holds on each device it runs on until the process ends;
- * the call itself allocates nothing. N is limited to 4194304 rows
- * (FLCE_E_UNSUPPORTED beyond, before anything is launched). All calls on one
+ * the call itself allocates nothing. N is limited to 4194303 rows, as for
+ * ce_forward_backward (FLCE_E_UNSUPPORTED beyond, before anything is
+ * launched). All calls on one
  * device share that array: calls that overlap on one device (different
  * streams, or threads) race and must be serialised by the caller. Other
  * arguments, outputs and errors as ce_forward_backward; an out-of-range
@@ -243,7 +246,7 @@ int ce_forward_backward_noalloc(const void* logits, void* grad_logits, const int
  *                         target inside the shard, else 0
  * Combining shards k: M = max m_k, lse = M + ln sum_k s_k exp(m_k - M),
  * z_y = sum_k t_k. No collective is performed. Targets are global ids checked
- * against [0, V_global).
+ * against [0, V_global). N is limited to 4194303 rows (FLCE_E_UNSUPPORTED).
  */
 int ce_shard_stats(const void* logits_shard, const int32_t* targets, int64_t N,
                    int64_t V_local, int64_t vocab_start, int64_t V_global, int dtype,

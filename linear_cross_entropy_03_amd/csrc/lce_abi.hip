@@ -26,7 +26,7 @@ using namespace lce;
 namespace {
 
 constexpr size_t kAlign = 256;
-inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+constexpr size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline size_t elem_bytes(int dtype) { return dtype == FLCE_F32 ? 4 : 2; }
 inline bool is16(int dtype) { return dtype == FLCE_BF16 || dtype == FLCE_F16; }
@@ -75,11 +75,16 @@ inline void scale_output(GemmDesc& d, const GradScaling& g) {
 #define LCE_LAST_SPLITS 2
 #endif
 
-constexpr int64_t kMaxRows = int64_t(1) << 31;     // grid.x of the row kernels
+constexpr int64_t kMaxRows = int64_t(1) << 31;     // int32 row indices
+// Rows of one launch of a one-workgroup-per-row kernel: 1024-lane workgroups
+// keep a launch within 2^32 - 1 work-items. Standalone calls (a launch over
+// all N rows) are limited to this; FLCE chunks are clamped to it.
+constexpr int64_t kMaxLaunchRows = (int64_t(1) << 22) - 1;
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 // Default byte budget of one chunk's logits (the planner's only memory knob).
 constexpr double kChunkBudget = 2.4e9;
 constexpr int64_t kRowQuantum = 256;  // GEMM tile rows
+constexpr int64_t kMinChunkRows = 8192;
 // Standalone CE and shard-statistics calls up to this many rows count their
 // targets inside the row kernel (each workgroup reads all of them: 8 KiB).
 constexpr int64_t kSelfCountRows = 2048;
@@ -137,12 +142,18 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
   const int64_t ldz = round_up(V, 8);
   int64_t chunk;
   if (chunk_rows > 0) {
-    chunk = std::min(chunk_rows, std::max<int64_t>(N, 1));
+    chunk = std::min(std::min(chunk_rows, std::max<int64_t>(N, 1)), kMaxLaunchRows);
   } else {
     // Largest multiple of 256 rows under the budget, then evened out over
     // the chunks; never one chunk holding every row of a multi-tile batch,
     // so the [N, V] logits are never materialised.
     int64_t cmax = static_cast<int64_t>(kChunkBudget / (static_cast<double>(ldz) * e));
+    // The grad_W product reads and rewrites the float32 [V, H] gradient once
+    // per chunk, so its K (the chunk's rows) should not be short: up to twice
+    // the budget is spent to reach kMinChunkRows.
+    if (cmax < kMinChunkRows)
+      cmax = std::min<int64_t>(kMinChunkRows,
+                               static_cast<int64_t>(2.0 * kChunkBudget / (static_cast<double>(ldz) * e)));
     cmax = std::max<int64_t>(kRowQuantum, cmax / kRowQuantum * kRowQuantum);
     if (N > 2 * kRowQuantum) cmax = std::min(cmax, round_up((N + 1) / 2, kRowQuantum));
     const int64_t n1 = std::max<int64_t>(N, 1);
@@ -199,7 +210,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
   return true;
 }
 
-size_t ce_ws_bytes(int64_t N) {
+constexpr size_t ce_ws_bytes(int64_t N) {
   return align_up(sizeof(WsHeader)) + align_up(static_cast<size_t>(std::max<int64_t>(N, 1)) * sizeof(float));
 }
 
@@ -710,7 +721,7 @@ int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* ta
   if (st != FLCE_OK) return st;
   if (N < 0 || V <= 0 || loss == nullptr) return FLCE_E_INVALID_ARG;
   if (N > 0 && (logits == nullptr || targets == nullptr)) return FLCE_E_INVALID_ARG;
-  if (N >= kMaxRows || V >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  if (N > kMaxLaunchRows || V >= kMaxDim) return FLCE_E_UNSUPPORTED;
   const void* ptrs[] = {logits, grad_logits, targets, loss, workspace};
   for (const void* q : ptrs)
     if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;
@@ -751,8 +762,8 @@ int ce_forward_backward(const void* logits, void* grad_logits, const int32_t* ta
 // stand-in); it uses the device address that hipGetSymbolAddress returns for
 // each device.
 namespace {
-constexpr int64_t kNoAllocMaxRows = int64_t(1) << 22;
-constexpr size_t kNoAllocBytes = 256 + (size_t(1) << 22) * sizeof(float);
+constexpr int64_t kNoAllocMaxRows = kMaxLaunchRows;
+constexpr size_t kNoAllocBytes = ce_ws_bytes(kNoAllocMaxRows);
 constexpr int kMaxDevices = 64;
 }  // namespace
 static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
@@ -814,7 +825,7 @@ int ce_shard_stats(const void* logits_shard, const int32_t* targets, int64_t N, 
   if (N > 0 && (logits_shard == nullptr || targets == nullptr || row_max == nullptr ||
                 row_sumexp == nullptr || row_target_logit == nullptr))
     return FLCE_E_INVALID_ARG;
-  if (N >= kMaxRows || V_global >= kMaxDim) return FLCE_E_UNSUPPORTED;
+  if (N > kMaxLaunchRows || V_global >= kMaxDim) return FLCE_E_UNSUPPORTED;
   const void* ptrs[] = {logits_shard, targets, row_max, row_sumexp, row_target_logit, workspace};
   for (const void* q : ptrs)
     if (q != nullptr && !aligned16(q)) return FLCE_E_UNSUPPORTED;

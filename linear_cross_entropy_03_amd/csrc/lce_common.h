@@ -262,6 +262,7 @@ hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* grad, int6
 // counts the targets: fills hdr (n_bad, n_valid, scale) as launch_count_targets
 // would, in the same launch (two launches where the persistent row kernel
 // applies). For calls with few rows (every workgroup reads all targets).
+// Gradient stores are non-temporal (the caller's gradient is not reread).
 hipError_t launch_row_ce_counted(int dtype, const void* Z, void* grad, int64_t rows, int64_t V,
                                  const int32_t* targets, int32_t ign, int reduction, WsHeader* hdr,
                                  float* loss_rows, hipStream_t s);
@@ -300,7 +301,8 @@ hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader*
 
 // Column sums of Z times 2^-out_shift (and *out_scale when not null) into out
 // of out_dtype (0 float, 1 bf16, 2 fp16; accumulation rounds once per call).
-// pk.live limits the rows summed (row packing).
+// pk.live limits the rows summed (row packing). Z 16-byte aligned, ldz a
+// multiple of 8 elements.
 hipError_t launch_colsum(int dtype, const void* Z, int64_t ldz, int64_t rows, int64_t V,
                          void* out, int out_dtype, bool accumulate, const float* out_scale,
                          int out_shift, hipStream_t s, RowPack pk = RowPack{nullptr, nullptr, 0});

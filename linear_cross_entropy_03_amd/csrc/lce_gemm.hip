@@ -394,6 +394,37 @@ __device__ __forceinline__ void epilogue_16(const f32x16_t (&acc)[4][kFJ], const
   static_assert(kFJ == 2, "64 output columns per wave");
   const int lane = threadIdx.x & 63, l32 = lane & 31, lhi = lane >> 5;
   const uint16_t* bias = static_cast<const uint16_t*>(d.bias);
+  // The lane's bias values: 4 consecutive columns for each (j, q), the same
+  // for every row, loaded once: as 8-byte vectors when the bias is 8-byte
+  // aligned (n is a multiple of 4), else, and at the end of the row,
+  // element by element.
+  float bv[kFJ][4][4];
+#pragma unroll
+  for (int j = 0; j < kFJ; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[j][q][e] = 0.0f;
+  if (bias != nullptr) {
+    auto to_f32 = [](uint16_t h) { return kTy == 1 ? f16_to_f32(h) : bf16_to_f32(h); };
+#pragma unroll
+    for (int j = 0; j < kFJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + col0 + j * 32 + q * 8 + lhi * 4;
+        if (n + 3 < d.N && (reinterpret_cast<uintptr_t>(bias) & 7u) == 0) {
+          const uint2 w = *reinterpret_cast<const uint2*>(bias + n);
+          bv[j][q][0] = to_f32(static_cast<uint16_t>(w.x));
+          bv[j][q][1] = to_f32(static_cast<uint16_t>(w.x >> 16));
+          bv[j][q][2] = to_f32(static_cast<uint16_t>(w.y));
+          bv[j][q][3] = to_f32(static_cast<uint16_t>(w.y >> 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < d.N) bv[j][q][e] = to_f32(bias[n + e]);
+        }
+      }
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -404,13 +435,8 @@ __device__ __forceinline__ void epilogue_16(const f32x16_t (&acc)[4][kFJ], const
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x16_t& a = acc[2 * h + ii][j];
-          float v[4] = {a[q * 4 + 0], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]};
-          if (bias != nullptr) {
-            const int64_t n = n0 + col0 + j * 32 + q * 8 + lhi * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < d.N) v[e] += kTy == 1 ? f16_to_f32(bias[n + e]) : bf16_to_f32(bias[n + e]);
-          }
+          float v[4] = {a[q * 4 + 0] + bv[j][q][0], a[q * 4 + 1] + bv[j][q][1],
+                        a[q * 4 + 2] + bv[j][q][2], a[q * 4 + 3] + bv[j][q][3]};
           const int slot = j * 4 + q;
           *reinterpret_cast<uint2*>(reg + r * 128 + ((slot ^ ((r >> 1) & 7)) << 4) + lhi * 8) =
               kTy == 1 ? make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]))

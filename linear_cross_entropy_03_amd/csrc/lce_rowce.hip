@@ -101,6 +101,7 @@ struct SelfCount {
   int64_t n;        // rows of the call; 0: read the scale from the header
   int reduction;    // 0 none, 1 sum, 2 mean
   WsHeader* out;    // header written by workgroup 0
+  int nt_grad;      // gradient stores non-temporal (the caller's gradient is not reread here)
 };
 
 // The reduction's gradient factor from all targets of the call (same rules
@@ -167,6 +168,22 @@ __device__ __forceinline__ float count_finish(const SelfCount& sc, const float (
   }
   return scale;
 }
+
+// A 16-byte gradient vector: non-temporal when the caller does not reread it
+// here (standalone CE), else a plain store (the FLCE products read the
+// chunk's dlogits next).
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_grad_vec(uint4* p, const uint4& v, int nt) {
+  if (nt) __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, v), reinterpret_cast<u32x4_nt*>(p));
+  else *p = v;
+}
+
+template <typename T, int kThreads, int kRes>
+__device__ __forceinline__ void row_ce_grad(const T* Z, int64_t ldz, T* G, int64_t ldg, int64_t V,
+                                            int64_t pad_cols, int64_t row, int32_t y, bool valid,
+                                            float lse, const RowSplit& rs, const uint4* buf,
+                                            const float* __restrict__ row_scale, int64_t orow,
+                                            int grad_shift, float red_scale, int nt);
 
 // kRes > 0: the row's vectors stay in registers (kRes per lane); kRes == 0:
 // two streaming passes over the row. Z and G may be the same rows (in-place),
@@ -269,14 +286,31 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   // Loss and per-row factor belong to the original row (packed chunks).
   const int64_t orow = pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row;
   if (tid == 0) loss_rows[orow] = valid ? (lse - zt) : 0.0f;
-  if (G == nullptr) return;
+  if (G != nullptr) row_ce_grad<T, kThreads, kRes>(Z, ldz, G, ldg, V, pad_cols, row, y, valid,
+                                                  lse, rs, buf, row_scale, orow, grad_shift,
+                                                  sc.n > 0 ? self_scale : hdr->scale, sc.nt_grad);
+}
+
+// The gradient part of k_row_ce: grad row = c (softmax - onehot), from the
+// registers (kRes > 0) or a second streaming pass; pad columns set to zero.
+template <typename T, int kThreads, int kRes>
+__device__ __forceinline__ void row_ce_grad(const T* Z, int64_t ldz, T* G, int64_t ldg, int64_t V,
+                                            int64_t pad_cols, int64_t row, int32_t y, bool valid,
+                                            float lse, const RowSplit& rs, const uint4* buf,
+                                            const float* __restrict__ row_scale, int64_t orow,
+                                            int grad_shift, float red_scale, int nt) {
+  using E = Elem<T>;
+  constexpr int kVec = E::kVec;
+  const int tid = threadIdx.x;
+  const T* z = Z + row * ldz;
+  const uint4* zv = reinterpret_cast<const uint4*>(z + rs.head);
 
   // The gradient factor: the reduction's, or a per-row one (sequence-level
   // losses such as DPO weight each token row separately); with grad_shift
   // the reduction's scale is left to the consumer.
   const float c = !valid ? 0.0f
                   : grad_shift > 0 ? __builtin_ldexpf(row_scale != nullptr ? row_scale[orow] : 1.0f, grad_shift)
-                  : (row_scale != nullptr ? row_scale[orow] : (sc.n > 0 ? self_scale : hdr->scale));
+                  : (row_scale != nullptr ? row_scale[orow] : red_scale);
   T* g = G + row * ldg;
   uint4* gv = reinterpret_cast<uint4*>(g + rs.head);
   auto grad_of = [&](float x, int64_t v) -> float {
@@ -294,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
         const int64_t v0 = rs.head + vi * kVec;
 #pragma unroll
         for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
-        gv[vi] = E::pack(f);
+        store_grad_vec(gv + vi, E::pack(f), nt);
       }
     }
   } else {
@@ -304,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
       const int64_t v0 = rs.head + vi * kVec;
 #pragma unroll
       for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
-      gv[vi] = E::pack(f);
+      store_grad_vec(gv + vi, E::pack(f), nt);
     }
   }
   if (tid < rs.head) E::store(g + tid, grad_of(E::load(z + tid), tid));
@@ -543,7 +577,31 @@ hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* G, int64_t
                          const WsHeader* hdr, float* loss_rows, const float* row_scale,
                          int grad_shift, hipStream_t s, RowPack pk) {
   return row_ce_typed(dtype, Z, ldz, G, ldg, rows, V, pad_cols, targets, ign, hdr, loss_rows,
-                      row_scale, grad_shift, SelfCount{0, 0, nullptr}, pk, s);
+                      row_scale, grad_shift, SelfCount{0, 0, nullptr, 0}, pk, s);
+}
+
+// Standalone calls of up to 4096 16-byte vectors per lane group of 512:
+// 512-lane workgroups (kRes = vectors per lane), four of them per CU, so
+// 1024 rows are all resident at once.
+template <typename T>
+static bool row_ce_512(const void* Z, void* G, int64_t rows, int64_t V, const int32_t* targets,
+                       int32_t ign, const WsHeader* hdr, float* loss_rows, SelfCount sc,
+                       hipStream_t s) {
+  constexpr int kVec = Elem<T>::kVec;
+  const int64_t nvec = (V + kVec - 1) / kVec;
+  const T* z = static_cast<const T*>(Z);
+  T* g = static_cast<T*>(G);
+  const dim3 grid(static_cast<unsigned>(rows)), block(512);
+  const RowPack pk{nullptr, nullptr, 0};
+#define LCE_ROW_CE512(R)                                                                        \
+  hipLaunchKernelGGL((k_row_ce<T, 512, R>), grid, block, 0, s, z, V, g, V, V, int64_t(0), targets, \
+                     ign, hdr, loss_rows, static_cast<const float*>(nullptr), 0, sc, pk)
+  if (nvec <= 4 * 512) LCE_ROW_CE512(4);
+  else if (nvec <= 8 * 512) LCE_ROW_CE512(8);
+  else if (nvec <= 16 * 512) LCE_ROW_CE512(16);
+  else return false;
+#undef LCE_ROW_CE512
+  return true;
 }
 
 hipError_t launch_row_ce_counted(int dtype, const void* Z, void* G, int64_t rows, int64_t V,
@@ -557,8 +615,19 @@ hipError_t launch_row_ce_counted(int dtype, const void* Z, void* G, int64_t rows
     if (e != hipSuccess) return e;
     return launch_row_ce(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr, 0, s);
   }
-  return row_ce_typed(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr, 0,
-                      SelfCount{rows, reduction, hdr}, RowPack{nullptr, nullptr, 0}, s);
+  const SelfCount sc{rows, reduction, hdr, 1};
+  hipError_t e = hipSuccess;
+  bool done = false;
+  if (V >= 16384) {
+    if (dtype == 1) done = row_ce_512<uint16_t>(Z, G, rows, V, targets, ign, hdr, loss_rows, sc, s);
+    else if (dtype == 2) done = row_ce_512<Half>(Z, G, rows, V, targets, ign, hdr, loss_rows, sc, s);
+    else done = row_ce_512<float>(Z, G, rows, V, targets, ign, hdr, loss_rows, sc, s);
+    if (done) e = hipGetLastError();
+  }
+  if (!done)
+    e = row_ce_typed(dtype, Z, V, G, V, rows, V, 0, targets, ign, hdr, loss_rows, nullptr, 0, sc,
+                     RowPack{nullptr, nullptr, 0}, s);
+  return e;
 }
 
 // ------------------------------------------------------------ shard stats
@@ -692,7 +761,7 @@ hipError_t launch_shard_stats(int dtype, const void* Z, int64_t ldz, int64_t row
                               int32_t ign, float* row_max, float* row_sumexp, float* row_target,
                               hipStream_t s) {
   return shard_stats_any(dtype, Z, ldz, rows, V_local, vocab_start, V_global, targets, ign,
-                         row_max, row_sumexp, row_target, SelfCount{0, 0, nullptr}, s);
+                         row_max, row_sumexp, row_target, SelfCount{0, 0, nullptr, 0}, s);
 }
 
 hipError_t launch_shard_stats_counted(int dtype, const void* Z, int64_t rows, int64_t V_local,
@@ -701,7 +770,7 @@ hipError_t launch_shard_stats_counted(int dtype, const void* Z, int64_t rows, in
                                       float* row_sumexp, float* row_target, WsHeader* hdr,
                                       hipStream_t s) {
   return shard_stats_any(dtype, Z, V_local, rows, V_local, vocab_start, V_global, targets, ign,
-                         row_max, row_sumexp, row_target, SelfCount{rows, 1, hdr}, s);
+                         row_max, row_sumexp, row_target, SelfCount{rows, 1, hdr, 0}, s);
 }
 
 // ------------------------------------------------- vocabulary-shard backward
@@ -1074,55 +1143,79 @@ hipError_t launch_reduce_loss(const float* loss_rows, int64_t n, const WsHeader*
 
 // ---------------------------------------------------- bias-gradient colsum
 
-// out[v] (+)= f * sum over rows of Z[r, v], f = 2^-out_shift (* *out_scale);
-// each lane owns two adjacent columns and walks the rows in order
-// (deterministic).
+// out[v] (+)= f * sum over rows of Z[r, v], f = 2^-out_shift (* *out_scale).
+// A workgroup of 4 waves owns a slab of 64 x kVec columns: lane l of every
+// wave holds columns [slab + l kVec, + kVec) as one 16-byte vector per row,
+// wave w sums rows w, w + 4, w + 8, ... in that order (8 rows' loads in
+// flight per lane), and the four waves' sums are added in wave order through
+// LDS. The order is fixed, so the sums are deterministic. Z must be 16-byte
+// aligned with ldz a multiple of 8 elements (the chunk buffer's layout).
 template <typename T, typename TO>
 __global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ Z, int64_t ldz, int64_t rows,
                                                 int64_t V, TO* __restrict__ out, int accumulate,
                                                 const float* __restrict__ out_scale, int out_shift,
                                                 const int32_t* __restrict__ live, int64_t live_base) {
-  const int64_t v = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 2;
-  if (v >= V) return;
+  using E = Elem<T>;
+  constexpr int kVec = E::kVec;
+  __shared__ float part[3][64 * kVec];
   if (live != nullptr) {  // packed chunk: only the live rows
     int64_t n = static_cast<int64_t>(*live) - live_base;
     if (n < 0) n = 0;
     if (n < rows) rows = n;
   }
-  const bool two = v + 1 < V;
-  float a0 = 0.0f, a1 = 0.0f;
-  const T* p = Z + v;
-  int64_t r = 0;
-  for (; r + 4 <= rows; r += 4) {
-    float x[4], w[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t v = (static_cast<int64_t>(blockIdx.x) * 64 + lane) * kVec;
+  const bool on = v < V;  // then v + kVec <= ldz: the vector stays inside the row
+  float acc[kVec];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      x[u] = Elem<T>::load(p + (r + u) * ldz);
-      w[u] = two ? Elem<T>::load(p + (r + u) * ldz + 1) : 0.0f;
+  for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
+  if (on) {
+    const T* p = Z + v;
+    int64_t r = w;
+    for (; r + 28 < rows; r += 32) {
+      uint4 u[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const uint4*>(p + (r + 4 * i) * ldz);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float f[kVec];
+        E::unpack(u[i], f);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc[e] += f[e];
+      }
     }
+    for (; r < rows; r += 4) {
+      float f[kVec];
+      E::unpack(*reinterpret_cast<const uint4*>(p + r * ldz), f);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) { a0 += x[u]; a1 += w[u]; }
+      for (int e = 0; e < kVec; ++e) acc[e] += f[e];
+    }
   }
-  for (; r < rows; ++r) {
-    a0 += Elem<T>::load(p + r * ldz);
-    if (two) a1 += Elem<T>::load(p + r * ldz + 1);
+  if (w > 0) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) part[w - 1][lane * kVec + e] = acc[e];
   }
+  __syncthreads();
+  if (w != 0 || !on) return;
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) acc[e] += part[k][lane * kVec + e];
   const float f = __builtin_ldexpf(out_scale != nullptr ? *out_scale : 1.0f, -out_shift);
-  a0 *= f;
-  a1 *= f;
-  if (accumulate) {
-    a0 += Elem<TO>::load(out + v);
-    if (two) a1 += Elem<TO>::load(out + v + 1);
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) {
+    if (v + e >= V) break;
+    float val = acc[e] * f;
+    if (accumulate) val += Elem<TO>::load(out + v + e);
+    Elem<TO>::store(out + v + e, val);
   }
-  Elem<TO>::store(out + v, a0);
-  if (two) Elem<TO>::store(out + v + 1, a1);
 }
 
 template <typename T>
 static hipError_t colsum_to(const void* Z, int64_t ldz, int64_t rows, int64_t V, void* out,
                             int out_dtype, bool accumulate, const float* out_scale, int out_shift,
                             RowPack pk, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((V + 511) / 512));
+  const dim3 grid(static_cast<unsigned>((V + 64 * Elem<T>::kVec - 1) / (64 * Elem<T>::kVec)));
   const T* z = static_cast<const T*>(Z);
   const int acc = accumulate ? 1 : 0;
   if (out_dtype == 1)
@@ -1400,21 +1493,24 @@ hipError_t launch_transpose16(const void* W, int64_t V, int64_t H, void* out, in
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void k_zero_dead_rows(const int32_t* __restrict__ t, int64_t V,
-                                                        int32_t ign, uint4* __restrict__ G,
-                                                        int64_t vecs) {
-  const int64_t r = blockIdx.x;
-  if (packed_target(t[r], ign, V)) return;
-  uint4* g = G + r * vecs;
-  for (int64_t v = threadIdx.x; v < vecs; v += 256) g[v] = make_uint4(0u, 0u, 0u, 0u);
+// Workgroups stride over the rows (the grid is capped, so any n launches).
+__global__ __launch_bounds__(256) void k_zero_dead_rows(const int32_t* __restrict__ t, int64_t n,
+                                                        int64_t V, int32_t ign,
+                                                        uint4* __restrict__ G, int64_t vecs) {
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    if (packed_target(t[r], ign, V)) continue;
+    uint4* g = G + r * vecs;
+    for (int64_t v = threadIdx.x; v < vecs; v += 256) g[v] = make_uint4(0u, 0u, 0u, 0u);
+  }
 }
 
 hipError_t launch_zero_dead_rows(const int32_t* targets, int64_t n, int64_t V, int32_t ign,
                                  void* G, int64_t row_bytes, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (row_bytes % 16 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_zero_dead_rows, dim3(static_cast<unsigned>(n)), dim3(256), 0, s, targets, V,
-                     ign, static_cast<uint4*>(G), row_bytes / 16);
+  const int64_t blocks = n < 65536 ? n : 65536;
+  hipLaunchKernelGGL(k_zero_dead_rows, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     targets, n, V, ign, static_cast<uint4*>(G), row_bytes / 16);
   return hipGetLastError();
 }
 

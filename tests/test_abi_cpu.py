@@ -62,7 +62,9 @@ def test_workspace_queries_and_plan(B):
     for N, H, V in ((8192, 2048, 128256), (32768, 4096, 128256), (32768, 4096, 256000)):
         c, s = B.flce_plan(N, H, V, B.BF16)
         assert c % 256 == 0 and c < N
-        assert c * ((V + 7) // 8 * 8) * 2 <= 2.5e9
+        # one chunk of logits stays within the 2.4 GB budget, or within twice
+        # it when that reaches 8192 rows (the grad_W product's K)
+        assert c * ((V + 7) // 8 * 8) * 2 <= (2.5e9 if c < 8192 else 4.8e9)
         assert s in (1, 2, 4, 8)
     assert B.flce_plan(256, 64, 1024, B.F32) == (256, 1)
     assert B.flce_plan(300, 64, 1000, B.F32, 64)[0] == 64
@@ -160,11 +162,27 @@ def test_ce_and_shard_argument_errors(B):
     assert L.flce_check_device_error(None, None) == B.E_INVALID_ARG
 
 
+def test_row_launch_limit(B):
+    """Standalone CE and shard statistics cover all N rows in one launch of
+    one workgroup (up to 1024 lanes) per row, so N is limited to 2^22 - 1
+    rows: one more is refused before anything runs (no device needed)."""
+    L = B.lib()
+    big = 1 << 22
+    assert L.ce_forward_backward(16, 16, 16, big, 32768, B.BF16, -100, 2, 16, 16, 1 << 40,
+                                 None) == B.E_UNSUPPORTED
+    assert L.ce_shard_stats(16, 16, big, 16, 0, 32, B.BF16, -100, 16, 16, 16, 16, 1 << 40,
+                            None) == B.E_UNSUPPORTED
+    assert L.ce_forward_backward_noalloc(16, 16, 16, big, 32768, B.BF16, -100, 2, 16,
+                                         None) == B.E_UNSUPPORTED
+    # FLCE chunks are clamped to the same count
+    assert B.flce_plan(1 << 23, 64, 1000, B.BF16, 1 << 23)[0] == big - 1
+
+
 def test_noalloc_ce_argument_errors(B):
     """The entry point without a workspace rejects sizes beyond its static
     scratch (and other bad arguments) before touching the device."""
     L = B.lib()
-    assert L.ce_forward_backward_noalloc(16, 16, 16, (1 << 22) + 1, 10, B.BF16, -100, 2, 16,
+    assert L.ce_forward_backward_noalloc(16, 16, 16, 1 << 22, 10, B.BF16, -100, 2, 16,
                                          None) == B.E_UNSUPPORTED
     assert L.ce_forward_backward_noalloc(16, 16, 16, 4, 10, B.BF16, -100, 9, 16, None) == B.E_INVALID_ARG
     assert L.ce_forward_backward_noalloc(16, 16, 16, 4, 0, B.BF16, -100, 2, 16, None) == B.E_INVALID_ARG

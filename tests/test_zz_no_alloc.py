@@ -58,6 +58,6 @@ def test_noalloc_size_limit(B):
     y = torch.zeros(16, dtype=torch.int32, device="cuda")
     loss = torch.zeros(1, device="cuda")
     st = B.lib().ce_forward_backward_noalloc(Z.data_ptr(), Z.data_ptr(), y.data_ptr(),
-                                             (1 << 22) + 1, 8, B.BF16, -100, 2, loss.data_ptr(),
+                                             1 << 22, 8, B.BF16, -100, 2, loss.data_ptr(),
                                              torch.cuda.current_stream().cuda_stream)
     assert st == B.E_UNSUPPORTED
