@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--profile-step", action="store_true",
                     help="for rocprofv3 counter runs: a 1 GiB device copy (counter calibration), "
                          "then one warmup and one timed FLCE step; prints nothing else")
+    ap.add_argument("--counters-from", nargs="+", metavar="PMC_DIR",
+                    help="summarise rocprofv3 --pmc runs of --profile-step per kernel class into "
+                         "profiles/counters_<workload>.json and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of --profile-step (FETCH_SIZE, "
                          "WRITE_SIZE) into profiles/traffic_<workload>.json and exit")
@@ -200,6 +203,34 @@ def summarise_traffic(workload, fetch_dir, write_dir):
     with open(traffic_path(workload), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def summarise_counters(workload, dirs):
+    """Per kernel class, the mean per dispatch over the timed step (the second
+    half of the dispatches) of every counter in one or more rocprofv3 --pmc
+    runs of --profile-step; writes profiles/counters_<workload>.json and
+    prints a markdown table."""
+    import csv
+    import glob
+    per = {}
+    for d in dirs:
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            kind = next((k2 for frag, k2 in KERNEL_KINDS.items() if frag in r["Kernel_Name"]), None)
+            if kind is None:
+                continue
+            vals.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        for (kind, name), v in vals.items():
+            per.setdefault(kind, {})[name] = float(np.mean(v[len(v) // 2:]))
+    out = {"workload": workload, "source_hash": kernel_source_hash(), "kernels": per}
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    names = sorted({n for k in per.values() for n in k})
+    print("| kernel | " + " | ".join(names) + " |")
+    print("|---" * (len(names) + 1) + "|")
+    for kind, k in per.items():
+        print(f"| {kind} | " + " | ".join(f"{k.get(n, float('nan')):.4g}" for n in names) + " |")
 
 
 def load_traffic(workload):
@@ -611,14 +642,30 @@ def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
     ms = a.elapsed_time(b) / reps
     # Each head runs over its own non-ignored rows (when packing is on).
     flops = sum(rows_through_products(B, yk[k]) for k in range(K)) * 6.0 * H * V
+    # The same rows through one head alone (head 0 in a single-head call), for
+    # the per-head comparison at this N.
+    del ws
+    gW1 = gW[0]
+    ws1 = torch.empty(B.flce_workspace_bytes(N, H, V, B.BF16), dtype=torch.uint8, device="cuda")
+    l1 = torch.empty(1, device="cuda")
+
+    def one():
+        B.flce_forward_backward(Xm, Wk[0], yk[0], reduction=cfg["reduction"], grad_X=gX, grad_W=gW1,
+                                grad_bias=False, loss=l1, workspace=ws1, stream=stream)
+    one()
+    torch.cuda.synchronize()
+    ms1 = time_calls(torch, stream, one, reps)
+    f1 = rows_through_products(B, yk[0]) * 6.0 * H * V
     out = {
         "workload": f"{K} heads over llama8b_head_bf16 hidden states (N {N}, H {H}, V {V}, "
                     f"{cfg['reduction']})",
         "ms_per_call": ms, "tokens_per_s": N / (ms * 1e-3),
         "tflops": flops / (ms * 1e-3) / 1e12, "frac_bf16_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        "single_head_same_rows": {"ms_per_call": ms1,
+                                  "frac_bf16_peak": f1 / (ms1 * 1e-3) / PEAK_BF16_FLOPS},
         "head_losses": [float(v) for v in loss.cpu()],
     }
-    del Wk, gW, ws
+    del Wk, gW, ws1
     return out
 
 
@@ -770,6 +817,9 @@ def main():
     args = parse()
     if args.traffic_from:
         summarise_traffic(args.workload, *args.traffic_from)
+        return
+    if args.counters_from:
+        summarise_counters(args.workload, args.counters_from)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))

@@ -408,6 +408,74 @@ int transpose_head(const Plan& p, const void* W, int64_t V, int64_t H, char* ws,
   return FLCE_OK;
 }
 
+// The two gradient products of one chunk whose dlogits are in zbuf:
+//   grad_X rows = dZ_c W (stored, or added when accum_gx), against the
+//   plan's transposed head when it holds one, else W itself;
+//   grad_W = dZ_c^T X_c (stored on the first chunk, added after).
+// With the transposed head they run as one paired launch (the grad_W tiles
+// fill the CUs that grad_X's last round of tiles leaves idle, so the last
+// packed chunk needs no extra K split); otherwise one after the other, the
+// last packed chunk's grad_X split along K. grad_X goes through the split-K
+// partial buffer when it is split, or when a packed chunk adds to grad_X
+// (the reduction then adds each row to its original row). Either gradient
+// may be null.
+int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_t V, void* zbuf,
+                      const char* Xc, int64_t rows, int64_t r0, int64_t N, bool first,
+                      const Packer& pkr, const RowPack& pk, void* grad_X, bool accum_gx,
+                      void* grad_W, int grad_dtype, const GradScaling& gsc, char* ws,
+                      hipStream_t s) {
+  const bool g16 = grad_dtype != FLCE_F32;
+  const size_t ge = g16 ? 2 : 4;
+  const bool pack = pkr.on;
+  float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
+  auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
+  GemmDesc g3{};
+  if (grad_W) {
+    g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
+    g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
+    g3.C = grad_W; g3.ldc = H;
+    g3.M = V; g3.N = H; g3.K = rows;
+    g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
+    g3.k_splits = 1;
+    scale_output(g3, gsc);
+    pkr.limit(g3, 1, r0);
+  }
+  const bool pair_ok = grad_X != nullptr && grad_W != nullptr && p.wt && g_pair_products;
+  if (grad_X) {
+    GemmDesc g2{};
+    g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
+    grad_x_head(p, W, H, ws, g2);
+    g2.M = rows; g2.N = H; g2.K = V;
+    scale_output(g2, gsc);
+    pkr.limit(g2, 0, r0);
+    void* out = static_cast<char*>(grad_X) + (pack ? 0 : static_cast<size_t>(r0) * H * ge);
+    const int splits = (pack && r0 + p.chunk >= N && !pair_ok) ? p.last_splits : p.dx_splits;
+    const bool via_split = splits > 1 || (pack && accum_gx);
+    if (via_split) {
+      g2.epilogue = kEpiStoreF32;
+      g2.C = split_buf; g2.ldc = H;
+      g2.k_splits = splits; g2.split_stride = rows * H;
+    } else {
+      g2.epilogue = accum_gx ? (g16 ? kEpiAccum16 : kEpiAccumF32) : (g16 ? kEpiStore16 : kEpiStoreF32);
+      g2.C = out; g2.ldc = H; g2.k_splits = 1;
+      if (pack) g2.row_map = pk.map;
+    }
+    const bool paired = pair_ok && gemm16_pair_supported(g2, g3);
+    if (paired)
+      LCE_TRY(timed(kKindGradXW, s, [&] { return launch_gemm16_pair(g2, g3, dtype == FLCE_F16, s); }));
+    else
+      LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+    if (via_split)
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype,
+                                    accum_gx, s, pk);
+      }));
+    if (paired) return FLCE_OK;  // grad_W of this chunk is done too
+  }
+  if (grad_W) LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
+  return FLCE_OK;
+}
+
 // The chunk loop of FLCE over all N rows for one head: logits GEMM, row CE
 // (loss rows, dZ in place), bias column sums, grad_X (stored, or added to
 // what is there when accum_gx), grad_W (stored on the first chunk, added
@@ -433,7 +501,6 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
   const bool g16 = grad_dtype != FLCE_F32;
   const size_t ge = g16 ? 2 : 4;
   void* zbuf = ws + p.off_chunk;
-  float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   const size_t e = elem_bytes(dtype);
   const bool need_grad = grad_X != nullptr || grad_W != nullptr || grad_bias != nullptr;
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
@@ -482,57 +549,9 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
                              gsc.out_scale, gsc.out_shift, s, pk);
       }));
 
-    GemmDesc g3{};
-    if (grad_W) {
-      g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
-      g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
-      g3.C = grad_W; g3.ldc = H;
-      g3.M = V; g3.N = H; g3.K = rows;
-      g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
-      g3.k_splits = 1;
-      scale_output(g3, gsc);
-      live(g3, 1);
-    }
-    // With the transposed head, grad_X and grad_W run as one launch (the
-    // grad_W tiles fill the CUs grad_X's last round of tiles leaves idle),
-    // so the last packed chunk needs no extra K split for its tail.
-    const bool pair_ok = grad_X != nullptr && grad_W != nullptr && p.wt && g_pair_products;
-    if (grad_X) {
-      GemmDesc g2{};
-      g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
-      grad_x_head(p, W, H, ws, g2);
-      g2.M = rows; g2.N = H; g2.K = V;
-      scale_output(g2, gsc);
-      live(g2, 0);
-      void* out = static_cast<char*>(grad_X) + (pack ? 0 : static_cast<size_t>(r0) * H * ge);
-      const int splits = (pack && r0 + p.chunk >= N && !pair_ok) ? p.last_splits : p.dx_splits;
-      const bool via_split = splits > 1 || (pack && accum_gx);
-      if (via_split) {
-        g2.epilogue = kEpiStoreF32;
-        g2.C = split_buf; g2.ldc = H;
-        g2.k_splits = splits; g2.split_stride = rows * H;
-      } else {
-        g2.epilogue = accum_gx ? (g16 ? kEpiAccum16 : kEpiAccumF32) : (g16 ? kEpiStore16 : kEpiStoreF32);
-        g2.C = out; g2.ldc = H; g2.k_splits = 1;
-        if (pack) g2.row_map = pk.map;
-      }
-      if (pair_ok && gemm16_pair_supported(g2, g3)) {
-        LCE_TRY(timed(kKindGradXW, s, [&] { return launch_gemm16_pair(g2, g3, dtype == FLCE_F16, s); }));
-        if (via_split)
-          LCE_TRY(timed(kKindOther, s, [&] {
-            return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype,
-                                        accum_gx, s, pk);
-          }));
-        continue;  // grad_W of this chunk is done too
-      }
-      LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
-      if (via_split)
-        LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype,
-                                      accum_gx, s, pk);
-        }));
-    }
-    if (grad_W) LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
+    st = gradient_products(p, dtype, W, H, V, zbuf, Xc, rows, r0, N, first, pkr, pk, grad_X,
+                           accum_gx, grad_W, grad_dtype, gsc, ws, s);
+    if (st != FLCE_OK) return st;
   }
   return FLCE_OK;
 }
@@ -968,7 +987,6 @@ static int shard_backward_impl(const void* X, const void* W_shard, const void* b
   char* ws = static_cast<char*>(workspace);
   WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
   void* zbuf = ws + p.off_chunk;
-  float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   const size_t e = elem_bytes(dtype);
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
   const GradScaling gsc = grad_scaling(dtype, hdr);
@@ -1019,43 +1037,9 @@ static int shard_backward_impl(const void* X, const void* W_shard, const void* b
         return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, grad_dtype, !first,
                              gsc.out_scale, gsc.out_shift, s, pk);
       }));
-    if (grad_X) {
-      GemmDesc g2{};
-      g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
-      grad_x_head(p, W_shard, H, ws, g2);
-      g2.M = rows; g2.N = H; g2.K = V_local;
-      g2.epilogue = kEpiStoreF32;
-      scale_output(g2, gsc);
-      pkr.limit(g2, 0, r0);
-      void* out = static_cast<char*>(grad_X) + (pkr.on ? 0 : static_cast<size_t>(r0) * H * ge);
-      const int splits = (pkr.on && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
-      if (splits > 1) {
-        g2.C = split_buf; g2.ldc = H;
-        g2.k_splits = splits; g2.split_stride = rows * H;
-        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
-        LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype, false,
-                                      s, pk);
-        }));
-      } else {
-        g2.C = out; g2.ldc = H; g2.k_splits = 1;
-        g2.epilogue = g16 ? kEpiStore16 : kEpiStoreF32;
-        if (pkr.on) g2.row_map = pk.map;
-        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
-      }
-    }
-    if (grad_W_shard) {
-      GemmDesc g3{};
-      g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
-      g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
-      g3.C = grad_W_shard; g3.ldc = H;
-      g3.M = V_local; g3.N = H; g3.K = rows;
-      g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
-      g3.k_splits = 1;
-      scale_output(g3, gsc);
-      pkr.limit(g3, 1, r0);
-      LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
-    }
+    st = gradient_products(p, dtype, W_shard, H, V_local, zbuf, Xc, rows, r0, N, first, pkr, pk,
+                           grad_X, false, grad_W_shard, grad_dtype, gsc, ws, s);
+    if (st != FLCE_OK) return st;
   }
   return FLCE_OK;
 }
@@ -1172,41 +1156,9 @@ static int jsd_impl(const void* X_s, const void* W_s, const void* X_t, const voi
                             (pkr.on ? pkr.ptgt : targets) + r0, ignore_index, hdr,
                             pkr.on ? loss_rows : loss_rows + r0, gsc.row_shift, s, pk);
     }));
-    if (grad_X_s) {
-      GemmDesc g2{};
-      g2.A = zs; g2.lda = p.ldz; g2.a_kmajor = true;
-      grad_x_head(p, W_s, H_s, ws, g2);
-      g2.M = rows; g2.N = H_s; g2.K = V;
-      g2.epilogue = kEpiStoreF32;
-      scale_output(g2, gsc);
-      pkr.limit(g2, 0, r0);
-      void* out = static_cast<char*>(grad_X_s) + (pkr.on ? 0 : static_cast<size_t>(r0) * H_s * ge);
-      const int splits = (pkr.on && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
-      if (splits > 1) {
-        g2.C = split_buf; g2.ldc = H_s; g2.k_splits = splits; g2.split_stride = rows * H_s;
-        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
-        LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, splits, rows * H_s, rows, H_s, H_s, out, grad_dtype,
-                                      false, s, pk);
-        }));
-      } else {
-        g2.C = out; g2.ldc = H_s; g2.k_splits = 1;
-        g2.epilogue = g16 ? kEpiStore16 : kEpiStoreF32;
-        if (pkr.on) g2.row_map = pk.map;
-        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
-      }
-    }
-    if (grad_W_s) {
-      GemmDesc g3{};
-      g3.A = zs; g3.lda = p.ldz; g3.a_kmajor = false;
-      g3.B = Xs_c; g3.ldb = H_s; g3.b_kmajor = false;
-      g3.C = grad_W_s; g3.ldc = H_s; g3.M = V; g3.N = H_s; g3.K = rows;
-      g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
-      g3.k_splits = 1;
-      scale_output(g3, gsc);
-      pkr.limit(g3, 1, r0);
-      LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
-    }
+    st = gradient_products(p, dtype, W_s, H_s, V, zs, Xs_c, rows, r0, N, first, pkr, pk, grad_X_s,
+                           false, grad_W_s, grad_dtype, gsc, ws, s);
+    if (st != FLCE_OK) return st;
   }
   if (reduction != FLCE_REDUCTION_NONE)
     LCE_TRY(timed(kKindOther, s, [&] {
@@ -1279,7 +1231,6 @@ static int dpo_impl(const void* X, const void* W, const int32_t* targets, int64_
   float* row_scale = reinterpret_cast<float*>(ws + off_scale);
   double* logp = reinterpret_cast<double*>(ws + off_logp);
   void* zbuf = ws + p.off_chunk;
-  float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   const size_t e = elem_bytes(dtype);
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st2) { return gemm_for(dtype, d, st2); };
   // Rows with an ignored or invalid target (the masked prompt tokens) add
@@ -1347,41 +1298,9 @@ static int dpo_impl(const void* X, const void* W, const int32_t* targets, int64_
                            ignore_index, hdr, pkr.on ? loss_rows : loss_rows + r0,
                            pkr.on ? row_scale : row_scale + r0, gsc.row_shift, s, pk);
     }));
-    if (grad_X) {
-      GemmDesc g2{};
-      g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
-      grad_x_head(p, W, H, ws, g2);
-      g2.M = rows; g2.N = H; g2.K = V;
-      g2.epilogue = kEpiStoreF32;
-      scale_output(g2, gsc);
-      pkr.limit(g2, 0, r0);
-      void* out = static_cast<char*>(grad_X) + (pkr.on ? 0 : static_cast<size_t>(r0) * H * ge);
-      const int splits = (pkr.on && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
-      if (splits > 1) {
-        g2.C = split_buf; g2.ldc = H; g2.k_splits = splits; g2.split_stride = rows * H;
-        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
-        LCE_TRY(timed(kKindOther, s, [&] {
-          return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype, false,
-                                      s, pk);
-        }));
-      } else {
-        g2.C = out; g2.ldc = H; g2.k_splits = 1;
-        g2.epilogue = g16 ? kEpiStore16 : kEpiStoreF32;
-        if (pkr.on) g2.row_map = pk.map;
-        LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
-      }
-    }
-    if (grad_W) {
-      GemmDesc g3{};
-      g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
-      g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
-      g3.C = grad_W; g3.ldc = H; g3.M = V; g3.N = H; g3.K = rows;
-      g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
-      g3.k_splits = 1;
-      scale_output(g3, gsc);
-      pkr.limit(g3, 1, r0);
-      LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
-    }
+    st = gradient_products(p, dtype, W, H, V, zbuf, Xc, rows, r0, N, first, pkr, pk, grad_X, false,
+                           grad_W, grad_dtype, gsc, ws, s);
+    if (st != FLCE_OK) return st;
   }
   return FLCE_OK;
 }

@@ -22,7 +22,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 namespace tiles {
 
-constexpr int kGroupM = 4;  // m-tiles per group in the tile order
+#ifndef LCE_GROUP_M
+#define LCE_GROUP_M 4
+#endif
+constexpr int kGroupM = LCE_GROUP_M;  // m-tiles per group in the tile order
 
 // Linear workgroup id -> (split, m-tile, n-tile). Workgroups are dealt to
 // the 8 XCDs round-robin, so ids are first regrouped so that each XCD gets a
