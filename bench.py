@@ -140,7 +140,6 @@ def cpu_baseline(inp, cfg, target_s):
 
 KERNEL_KINDS = {  # kernel-name fragment -> kind reported by the timing hooks
     "k_ring<true, true, 0": "logits_gemm",
-    "k_ring_xw<": "grad_xw_gemm",                # grad_X and grad_W of a chunk in one launch
     "k_gemm2<true, false, 1": "grad_x_gemm",     # W read n-major (chunk shorter than H)
     "k_ring<true, true, 1": "grad_x_gemm",       # against the transposed head
     "k_ring<false, false, 1": "grad_w_gemm",
@@ -400,7 +399,7 @@ def bench_vocab_parallel(torch, B, X, W, y, cfg, reps=5):
         once(False)
     torch.cuda.synchronize()
     B.flce_timing_enable(False)
-    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm", "grad_xw_gemm"))
+    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm"))
     row_ms, row_n = B.flce_timing_read("row_ce")
     B.flce_timing_reset()
     stats_ms, comb_ms, bwd_ms = (x / reps for x in tot)
@@ -481,7 +480,7 @@ def bench_distill(torch, B, X, W, y, cfg, n_rows=8192, reps=3):
     ms = time_calls(torch, stream, call, reps)
     hooked_pass(torch, B, call, reps)
     row_ms, row_n = B.flce_timing_read("row_ce")
-    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm", "grad_xw_gemm"))
+    gemm_ms = sum(B.flce_timing_read(k)[0] for k in ("logits_gemm", "grad_x_gemm", "grad_w_gemm"))
     B.flce_timing_reset()
     # Two logits GEMMs and the two gradient products over the rows they run on
     # (the non-ignored ones when packed: the teacher here is as wide as the student).
@@ -529,7 +528,7 @@ def bench_dpo(torch, B, X, W, y, cfg, n_pairs=4, seq_len=1024, reps=3):
     ms = time_calls(torch, stream, call, reps)
     hooked_pass(torch, B, call, reps)
     logit_ms, logit_n = B.flce_timing_read("logits_gemm")
-    gemm_ms = logit_ms + sum(B.flce_timing_read(k)[0] for k in ("grad_x_gemm", "grad_w_gemm", "grad_xw_gemm"))
+    gemm_ms = logit_ms + sum(B.flce_timing_read(k)[0] for k in ("grad_x_gemm", "grad_w_gemm"))
     B.flce_timing_reset()
     chunk = B.flce_plan(N, H, V, B.BF16)[0]
     n_logits = logit_n / reps                      # logits GEMMs per call (1 or 2 per chunk)
@@ -676,14 +675,13 @@ def kernel_table(B, n_live, H, V, e, steps, step_ms):
     over that time against the MI355X peak."""
     gemm_flops_per_step = 2.0 * n_live * H * V
     kernels = {}
-    for kind in ("logits_gemm", "grad_xw_gemm", "grad_x_gemm", "grad_w_gemm", "row_ce", "other"):
+    for kind in ("logits_gemm", "grad_x_gemm", "grad_w_gemm", "row_ce", "other"):
         tot_ms, launches = B.flce_timing_read(kind)
         if launches == 0:
             continue
         entry = {"ms_per_launch": tot_ms / launches, "launches": launches}
         if kind.endswith("gemm"):
-            # the paired launch runs two products
-            per_launch = (2 if kind == "grad_xw_gemm" else 1) * gemm_flops_per_step * steps / launches
+            per_launch = gemm_flops_per_step * steps / launches
             entry.update(bound="mfma", unit="TFLOP/s", algorithmic_per_launch=per_launch,
                          achieved=per_launch / (tot_ms / launches * 1e-3) / 1e12,
                          peak=PEAK_BF16_FLOPS / 1e12)

@@ -447,8 +447,7 @@ int flce_set_transposed_head(int enable);
  * Kernel timing for measurement. While enabled, the library brackets each
  * kernel it launches with HIP events on that kernel's stream. flce_timing_read
  * waits for the recorded events, returns for kernel class `kind` (0 logits
- * GEMM, 1 row CE, 2 grad_X GEMM, 3 grad_W GEMM, 4 other, 5 grad_X and grad_W
- * GEMMs of one chunk in a single launch) the summed duration
+ * GEMM, 1 row CE, 2 grad_X GEMM, 3 grad_W GEMM, 4 other) the summed duration
  * in milliseconds and the number of launches since the last reset, and
  * flce_timing_reset clears the tallies. Not thread-safe; off by default.
  */

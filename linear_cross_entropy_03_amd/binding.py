@@ -22,8 +22,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "flce.h")
 F32, BF16, F16 = 0, 1, 2
 REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 OK, E_INVALID_ARG, E_WORKSPACE, E_UNSUPPORTED, E_TARGET, E_HIP = range(6)
-TIMING_KINDS = {"logits_gemm": 0, "row_ce": 1, "grad_x_gemm": 2, "grad_w_gemm": 3, "other": 4,
-                "grad_xw_gemm": 5}
+TIMING_KINDS = {"logits_gemm": 0, "row_ce": 1, "grad_x_gemm": 2, "grad_w_gemm": 3, "other": 4}
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _int = ctypes.c_int

@@ -251,16 +251,7 @@ hipError_t timed(int kind, hipStream_t s, F&& launch) {
   return hipSuccess;
 }
 
-enum Kind {
-  kKindLogits = 0, kKindRowCE = 1, kKindGradX = 2, kKindGradW = 3, kKindOther = 4,
-  kKindGradXW = 5  // grad_X and grad_W of a chunk in one launch
-};
-
-// Paired gradient products (one launch per chunk); 0 launches them one by one.
-#ifndef LCE_PAIR_PRODUCTS
-#define LCE_PAIR_PRODUCTS 1
-#endif
-constexpr bool g_pair_products = LCE_PAIR_PRODUCTS != 0;
+enum Kind { kKindLogits = 0, kKindRowCE = 1, kKindGradX = 2, kKindGradW = 3, kKindOther = 4 };
 
 // Row packing switch (flce_set_row_packing); on by default.
 bool g_row_packing = true;
@@ -412,13 +403,10 @@ int transpose_head(const Plan& p, const void* W, int64_t V, int64_t H, char* ws,
 //   grad_X rows = dZ_c W (stored, or added when accum_gx), against the
 //   plan's transposed head when it holds one, else W itself;
 //   grad_W = dZ_c^T X_c (stored on the first chunk, added after).
-// With the transposed head they run as one paired launch (the grad_W tiles
-// fill the CUs that grad_X's last round of tiles leaves idle, so the last
-// packed chunk needs no extra K split); otherwise one after the other, the
-// last packed chunk's grad_X split along K. grad_X goes through the split-K
-// partial buffer when it is split, or when a packed chunk adds to grad_X
-// (the reduction then adds each row to its original row). Either gradient
-// may be null.
+// The last packed chunk's grad_X is split along K (its part-full tile rounds
+// are then half as long). grad_X goes through the split-K partial buffer
+// when it is split, or when a packed chunk adds to grad_X (the reduction then
+// adds each row to its original row). Either gradient may be null.
 int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_t V, void* zbuf,
                       const char* Xc, int64_t rows, int64_t r0, int64_t N, bool first,
                       const Packer& pkr, const RowPack& pk, void* grad_X, bool accum_gx,
@@ -440,7 +428,6 @@ int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_
     scale_output(g3, gsc);
     pkr.limit(g3, 1, r0);
   }
-  const bool pair_ok = grad_X != nullptr && grad_W != nullptr && p.wt && g_pair_products;
   if (grad_X) {
     GemmDesc g2{};
     g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
@@ -449,7 +436,7 @@ int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_
     scale_output(g2, gsc);
     pkr.limit(g2, 0, r0);
     void* out = static_cast<char*>(grad_X) + (pack ? 0 : static_cast<size_t>(r0) * H * ge);
-    const int splits = (pack && r0 + p.chunk >= N && !pair_ok) ? p.last_splits : p.dx_splits;
+    const int splits = (pack && r0 + p.chunk >= N) ? p.last_splits : p.dx_splits;
     const bool via_split = splits > 1 || (pack && accum_gx);
     if (via_split) {
       g2.epilogue = kEpiStoreF32;
@@ -460,17 +447,12 @@ int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_
       g2.C = out; g2.ldc = H; g2.k_splits = 1;
       if (pack) g2.row_map = pk.map;
     }
-    const bool paired = pair_ok && gemm16_pair_supported(g2, g3);
-    if (paired)
-      LCE_TRY(timed(kKindGradXW, s, [&] { return launch_gemm16_pair(g2, g3, dtype == FLCE_F16, s); }));
-    else
-      LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
+    LCE_TRY(timed(kKindGradX, s, [&] { return gemm(g2, s); }));
     if (via_split)
       LCE_TRY(timed(kKindOther, s, [&] {
         return launch_splitk_reduce(split_buf, splits, rows * H, rows, H, H, out, grad_dtype,
                                     accum_gx, s, pk);
       }));
-    if (paired) return FLCE_OK;  // grad_W of this chunk is done too
   }
   if (grad_W) LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
   return FLCE_OK;

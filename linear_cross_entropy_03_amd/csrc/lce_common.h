@@ -232,12 +232,7 @@ constexpr int kF16GradShift = 15;
 // 16-bit inputs (bf16, or fp16 when f16 is set), fp32 accumulation.
 hipError_t launch_gemm_16(const GemmDesc& d, bool f16, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s);
-// The grad_X product dx (both operands k-major, storing epilogue) and the
-// grad_W product dw (both operands mn-major, storing or accumulating, no row
-// map) of one chunk in a single 16-bit launch; gemm16_pair_supported tells
-// whether a pair qualifies (else the products are launched one by one).
-bool gemm16_pair_supported(const GemmDesc& dx, const GemmDesc& dw);
-hipError_t launch_gemm16_pair(const GemmDesc& dx, const GemmDesc& dw, bool f16, hipStream_t s);
+
 
 hipError_t launch_count_targets(const int32_t* targets, int64_t n, int64_t V,
                                 int32_t ignore_index, int reduction, WsHeader* hdr,

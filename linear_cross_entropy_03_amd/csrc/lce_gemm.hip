@@ -912,26 +912,6 @@ void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
   ring_tile<kAK, kBKm, kEpi, kTy, kW>(d, blockIdx.x, tiles_m, tiles_n, k_per_split);
 }
 
-// Both gradient products of a chunk in one launch: workgroups below
-// first_w take the tiles of grad_X = dZ_c W (both operands k-major, against
-// the transposed head), the others those of grad_W (+)= dZ_c^T X_c (both
-// mn-major). grad_X has few tiles with a long K (V) and grad_W many with a
-// short K (the chunk's rows); launched together, the grad_W tiles fill the
-// CUs that grad_X's last, partly filled round of tiles leaves idle, and
-// workgroups are dispatched in id order, so the long tiles start first.
-// first_w is a multiple of 8, so both products keep their XCD-aware tile
-// order.
-template <int kEpiX, int kEpiW, int kTy>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_ring_xw(GemmDesc dx, int64_t tiles_mx, int64_t tiles_nx, int64_t k_per_x, GemmDesc dw,
-               int64_t tiles_mw, int64_t tiles_nw, int64_t k_per_w, int64_t first_w) {
-  const int64_t bid = blockIdx.x;
-  if (bid < first_w)
-    ring_tile<true, true, kEpiX, kTy, 4>(dx, bid, tiles_mx, tiles_nx, k_per_x);
-  else
-    ring_tile<false, false, kEpiW, kTy, 4>(dw, bid - first_w, tiles_mw, tiles_nw, k_per_w);
-}
-
 }  // namespace ring
 }  // namespace mfma2
 
@@ -983,61 +963,6 @@ static hipError_t launch_ring(const GemmDesc& d, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles_m * tiles_n * splits)), dim3(64 * kW), 0,
                      s, dd, tiles_m, tiles_n, k_per);
   return hipGetLastError();
-}
-
-template <int kEpiX, int kEpiW, int kTy>
-static hipError_t launch_ring_xw(const GemmDesc& dx, const GemmDesc& dw, hipStream_t s) {
-  using namespace mfma2;
-  auto kern = ring::k_ring_xw<kEpiX, kEpiW, kTy>;
-  static int spills = -1;  // spill stores would break the explicit waits
-  if (spills < 0) {
-    hipFuncAttributes fa;
-    const hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
-    if (e != hipSuccess) return e;
-    spills = fa.localSizeBytes != 0;
-  }
-  if (spills) return hipErrorInvalidDeviceFunction;
-  GemmDesc x = dx, w = dw;
-  x.k_splits = dx.k_splits > 1 ? dx.k_splits : 1;
-  w.k_splits = dw.k_splits > 1 ? dw.k_splits : 1;
-  const int64_t tmx = (x.M + kBM - 1) / kBM, tnx = (x.N + kBM - 1) / kBM;
-  const int64_t tmw = (w.M + kBM - 1) / kBM, tnw = (w.N + kBM - 1) / kBM;
-  auto kper = [](const GemmDesc& d) {
-    const int64_t k = (d.K + d.k_splits - 1) / d.k_splits;
-    return (k + ring::kRK - 1) / ring::kRK * ring::kRK;
-  };
-  const int64_t first_w = (tmx * tnx * x.k_splits + 7) / 8 * 8;
-  const int64_t blocks = first_w + tmw * tnw * w.k_splits;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, x, tmx, tnx, kper(x),
-                     w, tmw, tnw, kper(w), first_w);
-  return hipGetLastError();
-}
-
-template <int kTy>
-static hipError_t launch_xw_ty(const GemmDesc& dx, const GemmDesc& dw, hipStream_t s) {
-  if (dx.epilogue == kEpiStoreF32 && dw.epilogue == kEpiStoreF32)
-    return launch_ring_xw<kEpiStoreF32, kEpiStoreF32, kTy>(dx, dw, s);
-  if (dx.epilogue == kEpiStoreF32 && dw.epilogue == kEpiAccumF32)
-    return launch_ring_xw<kEpiStoreF32, kEpiAccumF32, kTy>(dx, dw, s);
-  if (dx.epilogue == kEpiStore16 && dw.epilogue == kEpiStore16)
-    return launch_ring_xw<kEpiStore16, kEpiStore16, kTy>(dx, dw, s);
-  if (dx.epilogue == kEpiStore16 && dw.epilogue == kEpiAccum16)
-    return launch_ring_xw<kEpiStore16, kEpiAccum16, kTy>(dx, dw, s);
-  return hipErrorInvalidValue;
-}
-
-bool gemm16_pair_supported(const GemmDesc& dx, const GemmDesc& dw) {
-  const bool x_ok = dx.a_kmajor && dx.b_kmajor &&
-                    (dx.epilogue == kEpiStoreF32 || dx.epilogue == kEpiStore16);
-  const bool w_ok = !dw.a_kmajor && !dw.b_kmajor && dw.row_map == nullptr &&
-                    (dw.epilogue == (dx.epilogue == kEpiStoreF32 ? kEpiStoreF32 : kEpiStore16) ||
-                     dw.epilogue == (dx.epilogue == kEpiStoreF32 ? kEpiAccumF32 : kEpiAccum16));
-  return x_ok && w_ok && dx.M > 0 && dx.N > 0 && dw.M > 0 && dw.N > 0;
-}
-
-hipError_t launch_gemm16_pair(const GemmDesc& dx, const GemmDesc& dw, bool f16, hipStream_t s) {
-  if (!gemm16_pair_supported(dx, dw)) return hipErrorInvalidValue;
-  return f16 ? launch_xw_ty<1>(dx, dw, s) : launch_xw_ty<0>(dx, dw, s);
 }
 
 template <int kTy>
