@@ -51,8 +51,6 @@ def parse():
                          "products, ignored ones included)")
     ap.add_argument("--no-unpacked", action="store_true",
                     help="skip the comparison steps with row packing off")
-    ap.add_argument("--no-strict", action="store_true",
-                    help="skip the comparison step with the transposed head off")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other full-size workloads (Llama-3.2-1B head, 256k vocabulary)")
     ap.add_argument("--no-eager", action="store_true",
@@ -139,11 +137,9 @@ def cpu_baseline(inp, cfg, target_s):
 
 
 KERNEL_KINDS = {  # kernel-name fragment -> kind reported by the timing hooks
-    "k_ring<true, true, 0": "logits_gemm",
-    "k_gemm2<true, false, 1": "grad_x_gemm",     # W read n-major (chunk shorter than H)
-    "k_ring<true, true, 1": "grad_x_gemm",       # against the transposed head
-    "k_ring<false, false, 1": "grad_w_gemm",
-    "k_ring<false, false, 2": "grad_w_gemm",
+    "k_ring<true, true, 0": "logits_gemm",     # X W^T (both operands k-contiguous)
+    "k_ring<true, false": "grad_x_gemm",       # dZ W
+    "k_ring<false, false": "grad_w_gemm",      # dZ^T X
     "k_row_ce": "row_ce",
 }
 
@@ -550,9 +546,9 @@ def bench_dpo(torch, B, X, W, y, cfg, n_pairs=4, seq_len=1024, reps=3):
 
 def scratch_parts(B, N, H, V, dt, chunk_rows=0):
     """Bytes of each region of one FLCE call's workspace, from the library's
-    own query: chunk logits / dlogits, grad_X K-split partials, the transposed
-    head W^T, the chunk's gathered hidden states, and the O(N) rest (header,
-    per-row losses, packed-row lists)."""
+    own query: chunk logits / dlogits, grad_X K-split partials (which also
+    hold the chunk's gathered hidden states when rows are packed), and the
+    O(N) rest (header, per-row losses, packed-row lists)."""
     parts = B.flce_workspace_parts(N, H, V, dt, chunk_rows)
     parts["workspace"] = sum(parts.values())
     return parts
@@ -890,16 +886,6 @@ def main():
                          packing=False, hook_steps=1)
         B.flce_set_row_packing(packing)
         unpacked = {k: u[k] for k in ("ms_per_step", "tokens_per_s", "mfma_frac_step")}
-    strict = None
-    if dt != B.F32 and not args.no_strict:
-        log("comparison: transposed head off (scratch bounded by one chunk of logits)")
-        was = B.flce_set_transposed_head(False)
-        u = measure_flce(torch, B, cfg, inp, (X, W, bias, y), 5, 1, chunk_rows=args.chunk_rows,
-                         packing=packing, hook_steps=1)
-        B.flce_set_transposed_head(was)
-        strict = {k: u[k] for k in ("ms_per_step", "tokens_per_s", "mfma_frac_step", "extra_bytes",
-                                    "extra_bound_bytes", "extra_within_bound",
-                                    "extra_over_chunk_logits", "workspace_parts")}
     result = {
         "metric": "FLCE fwd+bwd tokens/s + % bf16 MFMA peak at H4096 V128256; peak HBM bytes",
         "value": head["tokens_per_s"],
@@ -917,7 +903,7 @@ def main():
                 + ", 10% ignore_index)",
         "config": {"workload": args.workload, "N": N, "H": H, "V": V, "reduction": cfg["reduction"],
                    "bias": bias is not None, "chunk_rows": chunk, "dx_splits": splits,
-                   "row_packing": packing, "transposed_head": head["workspace_parts"]["transposed_head"] > 0,
+                   "row_packing": packing,
                    "parallelism": "single GPU"},
         "roofline": roofline,
     }
@@ -928,7 +914,6 @@ def main():
               "hooked_ms_per_step", "kernels", "loss"):
         result[k] = head[k]
     result["unpacked"] = unpacked
-    result["transposed_head_off"] = strict
     if not args.no_vp:
         log("vocabulary-parallel shard")
         result["vocab_parallel"] = bench_vocab_parallel(torch, B, X, W, y, cfg)

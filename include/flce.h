@@ -100,11 +100,12 @@ int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
  * The workspace of flce_forward_backward split into its regions (pure host
  * computation), in bytes, each rounded up to 256: parts[0] the header and the
  * per-row losses, [1] one chunk of logits / dlogits (chunk x round_up(V, 8)
- * elements), [2] the grad_X K-split partials (float32), [3] the packed-row
- * lists, [4] the chunk's gathered hidden states (chunk x H elements), [5] the
- * transposed head (H x round_up(V, 64) elements, 0 when the plan has none).
- * The parts sum to flce_workspace_bytes. parts must hold 6 entries. Returns
- * FLCE_OK or FLCE_E_INVALID_ARG.
+ * elements), [2] the grad_X K-split partials (float32, S x chunk x H for the
+ * largest split S used, at least one for 16-bit inputs; with row packing a
+ * chunk's gathered hidden states, chunk x H 16-bit elements, share its first
+ * half), [3] the packed-row lists (3 x N int32 and the pack kernels' block
+ * counts; 0 for float32 inputs). The parts sum to flce_workspace_bytes.
+ * parts must hold 4 entries. Returns FLCE_OK or FLCE_E_INVALID_ARG.
  */
 int flce_workspace_parts(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
                          size_t* parts);
@@ -122,10 +123,10 @@ int flce_workspace_parts(int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
  *   grad_W   [V, H] float32 or NULL (NULL skips the grad_W product)
  *   grad_bias[V] float32 or NULL (must be NULL when bias is NULL)
  *   workspace of at least flce_workspace_bytes(N, H, V, dtype, chunk_rows)
- *   chunk_rows: rows per chunk, 0 = planner's choice; peak scratch is about
- *   chunk_rows * V elements of the input type, plus, for 16-bit inputs with
- *   H <= chunk_rows, a transposed copy of W (V * H elements) that the grad_X
- *   product reads k-major; a chunk shorter than H leaves W untransposed.
+ *   chunk_rows: rows per chunk, 0 = planner's choice; the workspace is one
+ *   chunk of logits (chunk_rows x round_up(V, 8) elements of the input
+ *   type), the grad_X K-split partials (float32, a multiple of
+ *   chunk_rows x H) and O(N) bytes of per-row data (flce_workspace_parts).
  * Results do not depend on chunk_rows except for the rounding order of grad_W
  * and grad_bias; the loss is bitwise independent of it.
  */
@@ -429,19 +430,6 @@ int flce_check_device_error(const void* workspace, void* stream);
  * thread-safe; the workspace size does not depend on it.
  */
 int flce_set_row_packing(int enable);
-
-/*
- * Transposed head for the grad_X product, on by default. With 16-bit inputs
- * and H <= chunk rows the planner then reserves H x round_up(V, 64) elements
- * of workspace for W^T, written once per call, so that grad_X = dZ W reads
- * both operands k-major (a faster product); off, grad_X reads W as it is and
- * the workspace holds no copy of W (peak scratch: one chunk of logits plus
- * O(chunk x H) bytes). Plans, workspace sizes and calls made after the switch
- * follow it; a workspace sized under the other setting may be too small
- * (FLCE_E_WORKSPACE). Returns the previous setting. Process-wide, not
- * thread-safe.
- */
-int flce_set_transposed_head(int enable);
 
 /*
  * Kernel timing for measurement. While enabled, the library brackets each

@@ -71,7 +71,6 @@ _SIGNATURES = {
                                                   _sz, _i64, _vp]),
     "flce_check_device_error": (_int, [_vp, _vp]),
     "flce_set_row_packing": (_int, [_int]),
-    "flce_set_transposed_head": (_int, [_int]),
     "flce_workspace_parts": (_int, [_i64, _i64, _i64, _int, _i64, ctypes.POINTER(_sz)]),
     "flce_timing_enable": (_int, [_int]),
     "flce_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
@@ -174,14 +173,13 @@ def flce_plan(N, H, V, dtype=BF16, chunk_rows=0):
     return int(c.value), int(s.value)
 
 
-WORKSPACE_PARTS = ("rows", "chunk_logits", "split_partials", "pack_lists", "gathered_rows",
-                   "transposed_head")
+WORKSPACE_PARTS = ("rows", "chunk_logits", "split_partials", "pack_lists")
 
 
 def flce_workspace_parts(N, H, V, dtype=BF16, chunk_rows=0):
     """The planner's workspace regions in bytes, by name (they sum to
     flce_workspace_bytes)."""
-    arr = (_sz * 6)()
+    arr = (_sz * len(WORKSPACE_PARTS))()
     _check(lib().flce_workspace_parts(N, H, V, dtype, chunk_rows, arr), "flce_workspace_parts")
     return dict(zip(WORKSPACE_PARTS, (int(v) for v in arr)))
 
@@ -534,12 +532,6 @@ def flce_check_device_error(workspace, stream=None):
 def flce_set_row_packing(enable=True):
     """Turn row packing of ignored rows on or off; returns the previous setting."""
     return bool(lib().flce_set_row_packing(1 if enable else 0))
-
-
-def flce_set_transposed_head(enable=True):
-    """Turns the grad_X product's transposed head on or off; returns the
-    previous setting (workspace sizes follow it)."""
-    return bool(lib().flce_set_transposed_head(1 if enable else 0))
 
 
 def flce_timing_enable(enable=True):

@@ -98,16 +98,13 @@ struct Plan {
   size_t off_chunk; // chunk buffer [chunk, ldz]
   size_t off_split; // split-K partials [S, chunk, H] float, S = the largest split used
                     // (present when S > 1, and always for 16-bit inputs)
-  // Row packing (16-bit inputs): packed-row map [N], packed targets [N], the
-  // pack kernels' block counts, and the chunk's gathered hidden states
-  // [chunk, H]. pack_ok is false for float32 inputs (no buffers).
+  // Row packing (16-bit inputs): packed-row map [N], packed targets [N] and
+  // the pack kernels' block counts. The chunk's gathered hidden states
+  // [chunk, H] (16-bit, half a split's bytes) sit at the start of the split-K
+  // partials: each chunk's grad_W product, their last reader, runs before its
+  // grad_X product writes partials. pack_ok is false for float32 inputs.
   bool pack_ok;
   size_t off_map, off_ptgt, off_bcnt, off_xs;
-  // Transposed head (16-bit, H <= chunk): W^T [H, ldw], ldw = round_up(V, 64),
-  // the k-major B operand of the grad_X product.
-  bool wt;
-  int64_t ldw;
-  size_t off_wt;
   size_t total;
 };
 
@@ -130,9 +127,6 @@ int choose_dx_splits(int64_t chunk, int64_t H, int64_t V) {
   }
   return best;
 }
-
-// Transposed-head switch (flce_set_transposed_head); on by default.
-bool g_transposed_head = true;
 
 bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, Plan* p) {
   if (N < 0 || H <= 0 || V <= 0 || N >= kMaxRows || H >= kMaxDim || V >= kMaxDim) return false;
@@ -186,7 +180,8 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
     off += align_up(static_cast<size_t>(max_splits) * static_cast<size_t>(chunk) *
                     static_cast<size_t>(H) * sizeof(float));
   p->pack_ok = is16(dtype);
-  p->off_map = p->off_ptgt = p->off_bcnt = p->off_xs = off;
+  p->off_xs = p->off_split;
+  p->off_map = p->off_ptgt = p->off_bcnt = off;
   if (p->pack_ok) {
     const size_t n1 = static_cast<size_t>(std::max<int64_t>(N, 1));
     p->off_map = off;
@@ -195,17 +190,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
     off += align_up(n1 * sizeof(int32_t));
     p->off_bcnt = off;
     off += align_up(static_cast<size_t>(std::max<int64_t>(pack_block_count(N), 1)) * sizeof(int32_t));
-    p->off_xs = off;
-    off += align_up(static_cast<size_t>(chunk) * static_cast<size_t>(H) * e);
   }
-  // With W transposed, grad_X = dZ W has both operands k-major and runs on
-  // the logits' pipeline (11% faster than reading W n-major); it costs one
-  // copy of W per call and W's size in workspace, taken only when that is at
-  // most one chunk of logits (H <= chunk).
-  p->wt = g_transposed_head && is16(dtype) && H <= chunk;
-  p->ldw = round_up(V, 64);
-  p->off_wt = off;
-  if (p->wt) off += align_up(static_cast<size_t>(H) * static_cast<size_t>(p->ldw) * e);
   p->total = off;
   return true;
 }
@@ -296,19 +281,11 @@ int flce_workspace_parts(int64_t N, int64_t H, int64_t V, int dtype, int64_t chu
                          size_t* parts) {
   Plan p;
   if (parts == nullptr || !make_plan(N, H, V, dtype, chunk_rows, &p)) return FLCE_E_INVALID_ARG;
-  parts[0] = p.off_chunk;                                  // header + per-row losses
-  parts[1] = p.off_split - p.off_chunk;                    // chunk logits / dlogits
-  parts[2] = (p.pack_ok ? p.off_map : p.off_wt) - p.off_split;  // grad_X K-split partials
-  parts[3] = p.pack_ok ? p.off_xs - p.off_map : 0;         // packed-row lists
-  parts[4] = p.pack_ok ? p.off_wt - p.off_xs : 0;          // gathered hidden states
-  parts[5] = p.total - p.off_wt;                           // transposed head
+  parts[0] = p.off_chunk;                  // header + per-row losses
+  parts[1] = p.off_split - p.off_chunk;    // chunk logits / dlogits
+  parts[2] = p.off_map - p.off_split;      // grad_X K-split partials (and gathered rows)
+  parts[3] = p.total - p.off_map;          // packed-row lists
   return FLCE_OK;
-}
-
-int flce_set_transposed_head(int enable) {
-  const int was = g_transposed_head ? 1 : 0;
-  g_transposed_head = enable != 0;
-  return was;
 }
 
 int flce_set_row_packing(int enable) {
@@ -383,30 +360,16 @@ struct Packer {
   }
 };
 
-// The B operand of the grad_X product dZ_c W: the transposed head W^T
-// (k-major, written into the workspace once per call) when the plan holds
-// it, else W itself (n-major).
-void grad_x_head(const Plan& p, const void* W, int64_t H, char* ws, GemmDesc& g2) {
-  if (p.wt) {
-    g2.B = ws + p.off_wt; g2.ldb = p.ldw; g2.b_kmajor = true;
-  } else {
-    g2.B = W; g2.ldb = H; g2.b_kmajor = false;
-  }
-}
-int transpose_head(const Plan& p, const void* W, int64_t V, int64_t H, char* ws, hipStream_t s) {
-  if (!p.wt) return FLCE_OK;
-  LCE_TRY(timed(kKindOther, s, [&] { return launch_transpose16(W, V, H, ws + p.off_wt, p.ldw, s); }));
-  return FLCE_OK;
-}
-
 // The two gradient products of one chunk whose dlogits are in zbuf:
-//   grad_X rows = dZ_c W (stored, or added when accum_gx), against the
-//   plan's transposed head when it holds one, else W itself;
-//   grad_W = dZ_c^T X_c (stored on the first chunk, added after).
-// The last packed chunk's grad_X is split along K (its part-full tile rounds
-// are then half as long). grad_X goes through the split-K partial buffer
-// when it is split, or when a packed chunk adds to grad_X (the reduction then
-// adds each row to its original row). Either gradient may be null.
+//   grad_W = dZ_c^T X_c (stored on the first chunk, added after);
+//   grad_X rows = dZ_c W (stored, or added when accum_gx), W read as stored
+//   (n-major B operand).
+// grad_W runs first: it is the last reader of the chunk's gathered rows,
+// which share the split-K partial buffer that grad_X may write. The last
+// packed chunk's grad_X is split along K (its part-full tile rounds are then
+// half as long). grad_X goes through the split-K partial buffer when it is
+// split, or when a packed chunk adds to grad_X (the reduction then adds each
+// row to its original row). Either gradient may be null.
 int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_t V, void* zbuf,
                       const char* Xc, int64_t rows, int64_t r0, int64_t N, bool first,
                       const Packer& pkr, const RowPack& pk, void* grad_X, bool accum_gx,
@@ -417,8 +380,8 @@ int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_
   const bool pack = pkr.on;
   float* split_buf = reinterpret_cast<float*>(ws + p.off_split);
   auto gemm = [dtype](const GemmDesc& d, hipStream_t st) { return gemm_for(dtype, d, st); };
-  GemmDesc g3{};
   if (grad_W) {
+    GemmDesc g3{};
     g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
     g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
     g3.C = grad_W; g3.ldc = H;
@@ -427,11 +390,12 @@ int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_
     g3.k_splits = 1;
     scale_output(g3, gsc);
     pkr.limit(g3, 1, r0);
+    LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
   }
   if (grad_X) {
     GemmDesc g2{};
     g2.A = zbuf; g2.lda = p.ldz; g2.a_kmajor = true;
-    grad_x_head(p, W, H, ws, g2);
+    g2.B = W; g2.ldb = H; g2.b_kmajor = false;
     g2.M = rows; g2.N = H; g2.K = V;
     scale_output(g2, gsc);
     pkr.limit(g2, 0, r0);
@@ -454,7 +418,6 @@ int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_
                                     accum_gx, s, pk);
       }));
   }
-  if (grad_W) LCE_TRY(timed(kKindGradW, s, [&] { return gemm(g3, s); }));
   return FLCE_OK;
 }
 
@@ -495,10 +458,6 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
   const bool pack = pkr.on;
   const int32_t* ptgt = pkr.ptgt;
 
-  if (grad_X != nullptr && N > 0) {
-    st = transpose_head(p, W, V, H, ws, s);
-    if (st != FLCE_OK) return st;
-  }
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
@@ -989,10 +948,6 @@ static int shard_backward_impl(const void* X, const void* W_shard, const void* b
   st = pkr.setup(p, ws, hdr, targets, N, V_global, ignore_index, nullptr, grad_X,
                  H * static_cast<int64_t>(ge), s);
   if (st != FLCE_OK) return st;
-  if (grad_X != nullptr && N > 0) {
-    st = transpose_head(p, W_shard, V_local, H, ws, s);
-    if (st != FLCE_OK) return st;
-  }
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
@@ -1098,17 +1053,17 @@ static int jsd_impl(const void* X_s, const void* W_s, const void* X_t, const voi
   if (N == 0 && grad_W_s)
     LCE_TRY(timed(kKindOther, s, [&] { return launch_zero(grad_W_s, V * H_s, grad_dtype, s); }));
   // Packed rows (as in flce_chunks) when the teacher's gathered hidden states
-  // fit the split-K partial buffer, which is free until the grad_X product.
+  // fit the split-K partial buffer after the student's: the buffer is free
+  // from the gather until the grad_X product, and the teacher's rows are read
+  // only by the teacher's logits product.
   const size_t split_bytes = p.off_map - p.off_split;
-  const bool teacher_fits = static_cast<size_t>(p.chunk) * static_cast<size_t>(H_t) * e <= split_bytes;
+  const size_t xs_bytes = align_up(static_cast<size_t>(p.chunk) * static_cast<size_t>(H_s) * e);
+  const bool teacher_fits =
+      xs_bytes + static_cast<size_t>(p.chunk) * static_cast<size_t>(H_t) * e <= split_bytes;
   Packer pkr;
   st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows, grad_X_s,
                  H_s * static_cast<int64_t>(ge), s, teacher_fits);
   if (st != FLCE_OK) return st;
-  if (grad_X_s != nullptr && N > 0) {
-    st = transpose_head(p, W_s, V, H_s, ws, s);
-    if (st != FLCE_OK) return st;
-  }
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
@@ -1119,9 +1074,10 @@ static int jsd_impl(const void* X_s, const void* W_s, const void* X_t, const voi
     const char* Xt_c = static_cast<const char*>(X_t) + static_cast<size_t>(r0) * H_t * e;
     if (pkr.on) {
       LCE_TRY(timed(kKindOther, s, [&] {
-        return launch_gather_rows(X_t, H_t * static_cast<int64_t>(e), rows, pk, split_buf, s);
+        return launch_gather_rows(X_t, H_t * static_cast<int64_t>(e), rows, pk,
+                                  reinterpret_cast<char*>(split_buf) + xs_bytes, s);
       }));
-      Xt_c = reinterpret_cast<const char*>(split_buf);
+      Xt_c = reinterpret_cast<const char*>(split_buf) + xs_bytes;
     }
     GemmDesc gs{};
     gs.A = Xs_c; gs.lda = H_s; gs.a_kmajor = true;
@@ -1243,10 +1199,6 @@ static int dpo_impl(const void* X, const void* W, const int32_t* targets, int64_
   st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows, grad_X,
                  H * static_cast<int64_t>(ge), s);
   if (st != FLCE_OK) return st;
-  if (grad_X != nullptr && N > 0) {
-    st = transpose_head(p, W, V, H, ws, s);
-    if (st != FLCE_OK) return st;
-  }
   const int32_t* tg = pkr.on ? pkr.ptgt : targets;
   // Pass 1: the CE row losses of every row (= minus the token log-probabilities).
   const char* Xc = nullptr;

@@ -324,10 +324,6 @@ hipError_t launch_pack_rows(const int32_t* targets, int64_t n, int64_t V, int32_
 // of row_bytes bytes (a multiple of 16, 16-byte aligned).
 hipError_t launch_gather_rows(const void* src, int64_t row_bytes, int64_t rows, RowPack pk,
                               void* out, hipStream_t s);
-// out[h, v] = W[v, h] for a 16-bit [V, H] matrix; columns V..ldo of out are
-// zeros (ldo a multiple of 64, at least V).
-hipError_t launch_transpose16(const void* W, int64_t V, int64_t H, void* out, int64_t ldo,
-                              hipStream_t s);
 // Zeros the rows r of G ([n, row_bytes]) whose target is not packed.
 hipError_t launch_zero_dead_rows(const int32_t* targets, int64_t n, int64_t V, int32_t ign,
                                  void* G, int64_t row_bytes, hipStream_t s);

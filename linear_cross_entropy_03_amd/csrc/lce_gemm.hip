@@ -72,27 +72,11 @@ __device__ __forceinline__ bool apply_live(GemmDesc& d, int64_t& tiles_m, int64_
 }
 
 // ---------------------------------------------------------------------------
-// The four-stage pipeline (grad_X): 32-wide k stages in 4 LDS buffers filled
-// by direct HBM->LDS loads.
+// MFMA GEMMs for 16-bit inputs (bf16 / fp16, fp32 accumulation).
 //
-// K advances 32 at a time through 4 LDS stages of 32 KiB (A 16 KiB + B
-// 16 KiB). Each stage is filled by buffer_load_dwordx4 ... lds: the data never
+// Operand tiles reach LDS through buffer_load_dwordx4 ... lds: the data never
 // passes through registers, and rows past the operand's end and K-tails read
 // as zero through the buffer descriptor's range check instead of branches.
-// Loads run three stages ahead of the MFMAs. The four stage buffers are four
-// LDS objects and the main loop is unrolled by four, so the compiler sees
-// which buffer each direct load writes and each LDS read reads: it then waits
-// only for the loads a read depends on, and the loads can be scheduled
-// between the MFMAs like any other instruction (one direct load per four
-// MFMAs; the texture unit takes roughly 16-20 clocks per 1 KiB instruction, so
-// a burst of them would hold the issuing wave). One barrier per stage sits
-// between the stage's two 16-wide k steps, so the next stage's first
-// fragments are read from LDS while the current stage's second k step is on
-// the MFMA pipe.
-//
-// The 256x256 tile is split over kWM x kWN waves: 2 x 4 waves, two per SIMD,
-// 128x64 each, so one wave's MFMAs cover the other's waits.
-//
 // Operands that are k-contiguous in HBM are stored [row][k] and read with
 // ds_read_b128; m/n-contiguous operands are stored [k][mn] as loaded and read
 // with ds_read_b64_tr_b16, which hands each lane four consecutive k of one
@@ -106,10 +90,7 @@ __device__ __forceinline__ bool apply_live(GemmDesc& d, int64_t& tiles_m, int64_
 
 namespace mfma2 {
 
-constexpr int kBM = 256, kBK = 32;
-constexpr int kWM = 2;                        // waves along M (each 128 rows)
-constexpr int kOpElems = kBM * kBK;           // one operand, one stage: 8192 bf16
-constexpr int kStageElems = 2 * kOpElems;     // A then B
+constexpr int kBM = 256;                      // output tile: 256 x 256
 constexpr int kOOB = 0x7FFFFFF0;              // buffer offset that reads as zero
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -120,16 +101,11 @@ typedef __attribute__((address_space(3))) i16x4_t lds_v4;
 // uniform across a wave).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-__device__ __forceinline__ int kswz(int row) {
-  return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
-}
 __device__ __forceinline__ int mswz(int k) {
   const int i = k & 3;
   return ((i & 1) << 1) | ((i & 2) << 1) | ((i & 1) << 3);
 }
-// Element offset of (row, 8-wide k chunk kc) in a k-major stage tile [256][32].
-__device__ __forceinline__ int koff(int row, int kc) { return row * kBK + ((kc ^ kswz(row)) << 3); }
-// Element offset of (k, mn) in an mn-major stage tile [32][256].
+// Element offset of (k, mn) in an mn-major tile [k][256].
 __device__ __forceinline__ int moff(int k, int mn) {
   return k * kBM + (((mn >> 3) ^ mswz(k)) << 3) + (mn & 7);
 }
@@ -168,110 +144,6 @@ __device__ __forceinline__ void block_sync() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The four stage buffers are separate LDS objects: the compiler can then tell
-// the direct loads into one buffer from LDS reads of another, and waits only
-// for the loads that a read depends on.
-__shared__ __align__(16) uint16_t g_stage0[kStageElems];
-__shared__ __align__(16) uint16_t g_stage1[kStageElems];
-__shared__ __align__(16) uint16_t g_stage2[kStageElems];
-__shared__ __align__(16) uint16_t g_stage3[kStageElems];
-
-template <int kB>
-__device__ __forceinline__ uint16_t* stage_buf() {
-  if constexpr (kB == 0) return g_stage0;
-  else if constexpr (kB == 1) return g_stage1;
-  else if constexpr (kB == 2) return g_stage2;
-  else return g_stage3;
-}
-
-// One operand of the GEMM: issues this wave's share of a stage's direct loads
-// and reads MFMA fragments. `rows` is the extent along m (A) or n (B); ld
-// its row stride. kWaves waves share each stage's loads.
-template <bool kKMajor, int kWaves>
-struct Operand {
-  // k-major: 16 rows per instruction; mn-major: 2 k-rows per instruction.
-  static constexpr int kInstr = kKMajor ? kBM / 16 / kWaves : kBK / 2 / kWaves;
-  const uint16_t* P;
-  int64_t ld, rows, r0;     // r0: first m/n row of this tile
-  rsrc_t tile_rsrc;         // k-major: the tile's rows
-  int voff0[kInstr];        // k-major: per-lane byte offset of (row, chunk) at k = 0
-  int kc8[kInstr];          // k-major: per-lane chunk start (elements)
-  int moff0[kInstr];        // mn-major: per-lane byte offset inside a stage
-
-  __device__ __forceinline__ int first_row(int w, int t) const {   // k-major LDS row
-    return (w * kInstr + t) * 16;
-  }
-  __device__ __forceinline__ int first_k(int w, int t) const {     // mn-major LDS k-row
-    return (w * kInstr + t) * 2;
-  }
-
-  __device__ __forceinline__ void init(const uint16_t* P_, int64_t ld_, int64_t rows_, int64_t r0_) {
-    P = P_; ld = ld_; rows = rows_; r0 = r0_;
-    const int lane = threadIdx.x & 63, w = wave_id();
-    if constexpr (kKMajor) {
-      int64_t nrows = rows - r0;
-      if (nrows > kBM) nrows = kBM;
-      tile_rsrc = make_rsrc(P + r0 * ld, nrows * ld * 2);
-#pragma unroll
-      for (int t = 0; t < kInstr; ++t) {
-        const int row = first_row(w, t) + (lane >> 2);
-        const int kc = (lane & 3) ^ kswz(row);
-        kc8[t] = kc * 8;
-        voff0[t] = static_cast<int>(row * ld * 2) + kc * 16;
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < kInstr; ++t) {
-        const int k = first_k(w, t) + (lane >> 5);
-        const int c = (lane & 31) ^ mswz(k);
-        moff0[t] = static_cast<int>(k * ld * 2) + c * 16;
-      }
-    }
-  }
-
-  // This wave's direct loads of K range [k0, k0 + 32) (clipped to kend) into
-  // the stage tile `dst`.
-  __device__ __forceinline__ void issue(uint16_t* dst, int64_t k0, int64_t kend) const {
-    const int w = wave_id();
-    if constexpr (kKMajor) {
-      const int64_t klim = kend - k0;  // chunks with kc8 >= klim are K-tail
-#pragma unroll
-      for (int t = 0; t < kInstr; ++t) {
-        const int voff = kc8[t] < klim ? voff0[t] + static_cast<int>(k0 * 2) : kOOB;
-        dma16(tile_rsrc, dst + first_row(w, t) * kBK, voff);
-      }
-    } else {
-      int64_t nk = kend - k0;
-      if (nk > kBK) nk = kBK;
-      // From (k0, r0) to the end of row k0 + nk - 1.
-      const rsrc_t r = make_rsrc(P + k0 * ld + r0, (nk * ld - r0) * 2);
-#pragma unroll
-      for (int t = 0; t < kInstr; ++t) dma16(r, dst + first_k(w, t) * kBM, moff0[t]);
-    }
-  }
-
-  // Fragment for MFMA rows base..base+31 (lane%32) and k-half lane/32 of the
-  // 16-wide k step kk: 8 consecutive k values.
-  __device__ __forceinline__ bf16x8_t frag(const uint16_t* src, int base, int kk) const {
-    const int lane = threadIdx.x & 63;
-    if constexpr (kKMajor) {
-      // base is a multiple of 32 and the swizzle depends on row bits 1..3
-      // only, so base contributes a constant (immediate) offset.
-      return *reinterpret_cast<const bf16x8_t*>(src + base * kBK + koff(lane & 31, kk * 2 + (lane >> 5)));
-    } else {
-      const int i = (lane & 15) >> 2, q = lane & 3;
-      const int k = kk * 16 + (lane >> 5) * 8 + i;
-      const int mn = base + ((lane >> 4) & 1) * 16 + q * 4;
-      uint16_t* s = const_cast<uint16_t*>(src);
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s + moff(k, mn)));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s + moff(k + 4, mn)));
-      const short __attribute__((ext_vector_type(8))) v =
-          __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      return __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-};
-
 // A wave's fragments for one 16-wide k step: 4 blocks of 32 rows of A and
 // kFJ blocks of 32 columns of B.
 template <int kFJ>
@@ -279,91 +151,13 @@ struct Frags {
   bf16x8_t a[4], b[kFJ];
 };
 
-template <int kFJ, bool kAK, bool kBKm, int kW>
-__device__ __forceinline__ void load_frags(Frags<kFJ>& f, const Operand<kAK, kW>& A,
-                                           const Operand<kBKm, kW>& B, const uint16_t* stage,
-                                           int row0, int col0, int kk) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = A.frag(stage, row0 + i * 32, kk);
-#pragma unroll
-  for (int j = 0; j < kFJ; ++j) f.b[j] = B.frag(stage + kOpElems, col0 + j * 32, kk);
-}
-
-// One 16-wide k step: read the next fragments `nf` from LDS and run the
-// 4 x kFJ MFMAs on `f`; the scheduler is told to interleave the LDS reads one
-// per MFMA so neither pipe waits on a burst of the other.
-template <int kTy, int kHalf, int kFJ, bool kAK, bool kBKm, int kW>
-__device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][kFJ], const Frags<kFJ>& f,
-                                         Frags<kFJ>& nf, const Operand<kAK, kW>& A,
-                                         const Operand<kBKm, kW>& B, const uint16_t* src,
-                                         int row0, int col0, int kk, uint16_t* dst, int64_t k0,
-                                         int64_t kend) {
-  constexpr int kDma = kHalf == 0 ? Operand<kAK, kW>::kInstr : Operand<kBKm, kW>::kInstr;
-  if constexpr (kHalf == 0) A.issue(dst, k0, kend);
-  else B.issue(dst + kOpElems, k0, kend);
-  load_frags(nf, A, B, src, row0, col0, kk);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < kFJ; ++j)
-      // B first: each 32x32 result block is C^T, so a lane holds 4 consecutive n.
-      if constexpr (kTy == 1)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, f.b[j]),
-                                                           __builtin_bit_cast(f16x8_t, f.a[i]),
-                                                           acc[i][j], 0, 0, 0);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-  constexpr int kReads = (kAK ? 4 : 8) + (kBKm ? kFJ : 2 * kFJ);  // LDS reads per step
-#pragma unroll
-  for (int t = 0; t < 4 * kFJ; ++t) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    if (t < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    if (t % (4 * kFJ / kDma) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
-  }
-  if constexpr (kReads > 4 * kFJ) __builtin_amdgcn_sched_group_barrier(0x100, kReads - 4 * kFJ, 0);
-}
-
-// Stage s (buffer kB = s % 4): its second k step on the MFMA pipe while the
-// first fragments of stage s + 1 are read, with the loads of stage s + 3 into
-// buffer (s + 3) % 4 spread over both steps (A in the first, B in the
-// second). Buffer (s + 3) % 4 last held stage s - 1, whose reads all finished
-// before the previous barrier. Loads past the end of K read zeros, so every
-// stage issues the same number of loads.
-template <int kTy, int kB, int kFJ, bool kAK, bool kBKm, int kW>
-__device__ __forceinline__ void stage_iter(f32x16_t (&acc)[4][kFJ], Frags<kFJ>& f0, Frags<kFJ>& f1,
-                                           const Operand<kAK, kW>& A, const Operand<kBKm, kW>& B,
-                                           int row0, int col0, int64_t k0, int64_t kend) {
-  constexpr int kPerA = Operand<kAK, kW>::kInstr, kPer = kPerA + Operand<kBKm, kW>::kInstr;
-  uint16_t* dst = stage_buf<(kB + 3) & 3>();
-  mma_step<kTy, 0>(acc, f0, f1, A, B, stage_buf<kB>(), row0, col0, 1, dst, k0, kend);
-  // Stage s + 1 has landed once only the loads issued after it (stage s + 2
-  // and the A half of stage s + 3) are in flight. The count holds because the
-  // loop issues no other vector memory instruction: no register spills, which
-  // the launcher checks.
-  wait_vmcnt<kPer + kPerA>();
-  block_sync();
-  mma_step<kTy, 1>(acc, f1, f0, A, B, stage_buf<(kB + 1) & 3>(), row0, col0, 0, dst, k0, kend);
-}
-
 // Output through LDS. The MFMA result layout gives each lane 4 consecutive
 // columns of one row, so direct stores touch 32 rows per instruction with 8
-// or 16 bytes each. Each wave instead writes half of its 128 x 64 result
-// (64 rows) into its own LDS region and reads it back as whole row segments:
+// or 16 bytes each. Each wave instead takes its result 128 x 64 at a time and
+// writes half of that (64 rows) into its own LDS region and reads it back as whole row segments:
 // 8 lanes per 128-byte row (bf16) or 16 lanes per 256-byte row (fp32), so
 // every store instruction covers full cache lines. Slots are XOR-swizzled by
 // row to spread the column-wise writes over the banks.
-
-// This wave's region: kBytes each, packed into the 32 KiB stage buffers.
-template <int kBytes>
-__device__ __forceinline__ char* epi_region(int w) {
-  constexpr int kPerBuf = 2 * kOpElems * 2 / kBytes;  // waves per stage buffer
-  const int b = w / kPerBuf, o = (w % kPerBuf) * kBytes;
-  char* base = b == 0 ? reinterpret_cast<char*>(g_stage0)
-             : b == 1 ? reinterpret_cast<char*>(g_stage1)
-             : b == 2 ? reinterpret_cast<char*>(g_stage2)
-                      : reinterpret_cast<char*>(g_stage3);
-  return base + o;
-}
 
 // Output stores. With LCE_NT_STORES they are non-temporal: the outputs
 // (chunk logits, gradients) are not read again by this kernel, so they are
@@ -554,84 +348,6 @@ __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[4][kFJ], cons
   }
 }
 
-template <bool kAK, bool kBKm, int kEpi, int kWN, int kTy>
-__global__ __launch_bounds__(64 * kWM * kWN) __attribute__((amdgpu_waves_per_eu(kWN / 2, kWN / 2)))
-void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
-  constexpr int kWaves = kWM * kWN;
-  constexpr int kFJ = kBM / kWN / 32;  // 32-column MFMA blocks per wave
-  constexpr int kPer = Operand<kAK, kWaves>::kInstr + Operand<kBKm, kWaves>::kInstr;
-  constexpr bool kAcc = kEpi == kEpiAccumF32 || kEpi == kEpiAccum16;
-
-  // Whole workgroups leave here, before any barrier.
-  if (!apply_live(d, tiles_m, tiles_n, kBM, blockIdx.x)) return;
-  int64_t tm, tn;
-  int sp;
-  tiles::tile_of(blockIdx.x, tiles_m, tiles_n, d.k_splits, tm, tn, sp);
-  const int64_t m0 = tm * kBM, n0 = tn * kBM;
-  const int64_t kbeg = static_cast<int64_t>(sp) * k_per_split;
-  int64_t kend = kbeg + k_per_split;
-  if (kend > d.K) kend = d.K;
-  const int ksteps = kend > kbeg ? static_cast<int>((kend - kbeg + kBK - 1) / kBK) : 0;
-  if (kAcc && ksteps == 0) return;  // adds nothing
-
-  Operand<kAK, kWaves> opA;
-  Operand<kBKm, kWaves> opB;
-  opA.init(static_cast<const uint16_t*>(d.A), d.lda, d.M, m0);
-  opB.init(static_cast<const uint16_t*>(d.B), d.ldb, d.N, n0);
-
-  const int wave = wave_id();
-  const int wm = wave / kWN, wn = wave % kWN;
-  const int row0 = wm * (kBM / kWM), col0 = wn * (kBM / kWN);
-
-  f32x16_t acc[4][kFJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < kFJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // Pipeline: stage s lives in buffer s % 4. Stages 0..2 are loaded up front;
-  // during stage s the loads of stage s + 3 go into buffer (s + 3) % 4, whose
-  // last reader (stage s - 1) finished before the previous barrier. The
-  // barrier of stage s (between its two k steps) waits for stage s + 1.
-  if (ksteps > 0) {
-    opA.issue(stage_buf<0>(), kbeg, kend);
-    opB.issue(stage_buf<0>() + kOpElems, kbeg, kend);
-    opA.issue(stage_buf<1>(), kbeg + kBK, kend);
-    opB.issue(stage_buf<1>() + kOpElems, kbeg + kBK, kend);
-    opA.issue(stage_buf<2>(), kbeg + 2 * kBK, kend);
-    opB.issue(stage_buf<2>() + kOpElems, kbeg + 2 * kBK, kend);
-    wait_vmcnt<2 * kPer>();
-    block_sync();
-    Frags<kFJ> f0, f1;
-    load_frags(f0, opA, opB, stage_buf<0>(), row0, col0, 0);
-    // The buffer of stage s must be known at compile time, hence four stages
-    // per trip. The last stage's second step reads fragments of a stage past
-    // the end (zeros or stale, in bounds); they are never used.
-    int s = 0;
-    for (; s + 4 <= ksteps; s += 4) {
-      const int64_t k3 = kbeg + static_cast<int64_t>(s + 3) * kBK;
-      stage_iter<kTy, 0>(acc, f0, f1, opA, opB, row0, col0, k3, kend);
-      stage_iter<kTy, 1>(acc, f0, f1, opA, opB, row0, col0, k3 + kBK, kend);
-      stage_iter<kTy, 2>(acc, f0, f1, opA, opB, row0, col0, k3 + 2 * kBK, kend);
-      stage_iter<kTy, 3>(acc, f0, f1, opA, opB, row0, col0, k3 + 3 * kBK, kend);
-    }
-    const int64_t k3 = kbeg + static_cast<int64_t>(s + 3) * kBK;
-    if (s < ksteps) stage_iter<kTy, 0>(acc, f0, f1, opA, opB, row0, col0, k3, kend);
-    if (s + 1 < ksteps) stage_iter<kTy, 1>(acc, f0, f1, opA, opB, row0, col0, k3 + kBK, kend);
-    if (s + 2 < ksteps) stage_iter<kTy, 2>(acc, f0, f1, opA, opB, row0, col0, k3 + 2 * kBK, kend);
-    // Loads past the end are still in flight; they write this workgroup's LDS.
-    wait_vmcnt<0>();
-  }
-
-  // Every wave is done with the stage buffers; they now stage the output.
-  block_sync();
-  if constexpr (kEpi == kEpiLogits) epilogue_16<kTy, kFJ>(acc, d, m0, n0, row0, col0, epi_region<8192>(wave));
-  else epilogue_f32<kEpi, kTy, kFJ>(acc, d, m0, n0, sp, row0, col0, epi_region<8192>(wave));
-}
-
-
 // ---------------------------------------------------------------------------
 // The ring pipeline: 64-wide k steps through five LDS slots of 32 KiB.
 //
@@ -643,11 +359,12 @@ void k_gemm2(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) 
 // slots keep three operand loads (96 KiB) in flight while two are read, as
 // much as the four 32-wide stages. Loads go out in the order A_0, B_0, A_1,
 // B_1, ..., load j into slot j % 5, so step s reads A_s from slot 2s % 5 and
-// B_s from slot (2s + 1) % 5; the main loop is unrolled by five steps so that
-// every slot index is a compile-time constant (the same precise-wait argument
-// as for the four stage buffers). Used for logits (both operands k-major) and
-// grad_W (both mn-major); grad_X measured slower on it and keeps the four
-// stages.
+// B_s from slot (2s + 1) % 5. The five slots are five LDS objects and the main
+// loop is unrolled by five steps, so every slot index is a compile-time
+// constant: the compiler sees which slot each direct load writes and each LDS
+// read reads, waits only for the loads a read depends on, and the loads can
+// be scheduled between the MFMAs like any other instruction. Used for all
+// three products.
 //
 // k-major slots are [row][64] with the 16-byte chunk c of row r at position
 // c ^ rswz(r); mn-major slots are [k][256] with the mn-major swizzle above.
@@ -714,9 +431,13 @@ struct ROp<true, kW> {
       dma16(rsrc, dst + first_row(w, t) * kRK, voff);
     }
   }
-  __device__ __forceinline__ static bf16x8_t frag(const uint16_t* src, int base, int kk) {
+  int fbase;  // first row of fragment 0
+  __device__ __forceinline__ void frags(int base0) { fbase = base0; }
+  // Fragment f: rows fbase + 32 f + lane % 32, k-half lane / 32 of step kk.
+  __device__ __forceinline__ bf16x8_t frag(const uint16_t* src, int f, int kk) const {
     const int lane = threadIdx.x & 63, r = lane & 31, c = kk * 2 + (lane >> 5);
-    return *reinterpret_cast<const bf16x8_t*>(src + base * kRK + r * kRK + ((c ^ rswz(r)) << 3));
+    return *reinterpret_cast<const bf16x8_t*>(src + (fbase + f * 32) * kRK + r * kRK +
+                                              ((c ^ rswz(r)) << 3));
   }
 };
 
@@ -749,14 +470,31 @@ struct ROp<false, kW> {
 #pragma unroll
     for (int t = kFirst; t < kFirst + kCount; ++t) dma16(r, dst + first_k(w, t) * kBM, moff0[t]);
   }
-  __device__ __forceinline__ static bf16x8_t frag(const uint16_t* src, int base, int kk) {
+  // Byte offset of this lane's first read for fragment f (rows or columns
+  // base0 + 32 f) at kk = 0; the swizzle depends on k mod 4 only, so the
+  // other reads of a fragment are this offset plus a constant.
+  int foff[4];
+  __device__ __forceinline__ void frags(int base0) {
     const int lane = threadIdx.x & 63;
     const int i = (lane & 15) >> 2, q = lane & 3;
-    const int k = kk * 16 + (lane >> 5) * 8 + i;
-    const int mn = base + ((lane >> 4) & 1) * 16 + q * 4;
-    uint16_t* s = const_cast<uint16_t*>(src);
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s + moff(k, mn)));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s + moff(k + 4, mn)));
+    const int k = (lane >> 5) * 8 + i;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      int o = moff(k, base0 + f * 32 + ((lane >> 4) & 1) * 16 + q * 4) * 2;
+      // Opaque to the optimiser: each read's address stays "slot + offset +
+      // constant". Rebuilt from other reads' addresses, the transposed reads
+      // lost the LDS alias scopes that tell the wait-count pass they do not
+      // overlap the slot being filled, and every such read then waited for
+      // all outstanding direct loads (vmcnt(0)): 960 against 1420 TFLOP/s
+      // when the other operand is k-contiguous.
+      asm volatile("" : "+v"(o));
+      foff[f] = o;
+    }
+  }
+  __device__ __forceinline__ bf16x8_t frag(const uint16_t* src, int f, int kk) const {
+    const char* s = reinterpret_cast<const char*>(src) + foff[f] + kk * 16 * kBM * 2;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(s + 4 * kBM * 2));
     const short __attribute__((ext_vector_type(8))) v =
         __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8_t, v);
@@ -768,13 +506,14 @@ struct ROp<false, kW> {
 // interleaved as in mma_step.
 template <int kTy, int kDma, bool kAK, bool kBKm, int kW, int kFJ, typename Issue>
 __device__ __forceinline__ void sub(f32x16_t (&acc)[4][kFJ], const Frags<kFJ>& f, Frags<kFJ>& nf,
-                                    const uint16_t* srcA, const uint16_t* srcB, int row0, int col0,
-                                    int kk, Issue&& issue) {
+                                    const ROp<kAK, kW>& A, const ROp<kBKm, kW>& B,
+                                    const uint16_t* srcA, const uint16_t* srcB, int kk,
+                                    Issue&& issue) {
   issue();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) nf.a[i] = ROp<kAK, kW>::frag(srcA, row0 + i * 32, kk);
+  for (int i = 0; i < 4; ++i) nf.a[i] = A.frag(srcA, i, kk);
 #pragma unroll
-  for (int j = 0; j < kFJ; ++j) nf.b[j] = ROp<kBKm, kW>::frag(srcB, col0 + j * 32, kk);
+  for (int j = 0; j < kFJ; ++j) nf.b[j] = B.frag(srcB, j, kk);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -803,25 +542,25 @@ __device__ __forceinline__ void sub(f32x16_t (&acc)[4][kFJ], const Frags<kFJ>& f
 // step's slots, and the last sub-step issues B_{s+2} into the slot of A_s.
 template <int kTy, int kS, bool kAK, bool kBKm, int kW, int kFJ>
 __device__ __forceinline__ void step(f32x16_t (&acc)[4][kFJ], Frags<kFJ>& f0, Frags<kFJ>& f1,
-                                     const ROp<kAK, kW>& A, const ROp<kBKm, kW>& B, int row0,
-                                     int col0, int64_t k2, int64_t kend) {
+                                     const ROp<kAK, kW>& A, const ROp<kBKm, kW>& B, int64_t k2,
+                                     int64_t kend) {
   constexpr int sa = (2 * kS) % 5, sb = (2 * kS + 1) % 5, pb = (2 * kS + 4) % 5;
   constexpr int na = (2 * kS + 2) % 5, nb = (2 * kS + 3) % 5;
   constexpr int kI = ROp<kAK, kW>::kInstr, kH = kI / 2;
   static_assert(kI == ROp<kBKm, kW>::kInstr, "equal load counts per operand");
   const uint16_t* a = slot_buf<sa>();
   const uint16_t* b = slot_buf<sb>();
-  sub<kTy, kH, kAK, kBKm, kW>(acc, f0, f1, a, b, row0, col0, 1,
+  sub<kTy, kH, kAK, kBKm, kW>(acc, f0, f1, A, B, a, b, 1,
                               [&] { A.template issue<0, kH>(slot_buf<pb>(), k2, kend); });
-  sub<kTy, kH, kAK, kBKm, kW>(acc, f1, f0, a, b, row0, col0, 2,
+  sub<kTy, kH, kAK, kBKm, kW>(acc, f1, f0, A, B, a, b, 2,
                               [&] { A.template issue<kH, kH>(slot_buf<pb>(), k2, kend); });
-  sub<kTy, 0, kAK, kBKm, kW>(acc, f0, f1, a, b, row0, col0, 3, [] {});
-  // Only A_{s+2} was issued after B_{s+1}; as in the four-stage loop the
-  // count relies on there being no other vector memory instruction (no
-  // spills, checked by the launcher).
+  sub<kTy, 0, kAK, kBKm, kW>(acc, f0, f1, A, B, a, b, 3, [] {});
+  // Only A_{s+2} was issued after B_{s+1}; the count relies on there being
+  // no other vector memory instruction in the loop (no spills, checked by
+  // the launcher).
   wait_vmcnt<kI>();
   block_sync();
-  sub<kTy, kI, kAK, kBKm, kW>(acc, f1, f0, slot_buf<na>(), slot_buf<nb>(), row0, col0, 0,
+  sub<kTy, kI, kAK, kBKm, kW>(acc, f1, f0, A, B, slot_buf<na>(), slot_buf<nb>(), 0,
                               [&] { B.template issue<0, kI>(slot_buf<sa>(), k2, kend); });
 }
 
@@ -854,6 +593,8 @@ __device__ __forceinline__ void ring_tile(GemmDesc d, int64_t bid, int64_t tiles
   B.init(static_cast<const uint16_t*>(d.B), d.ldb, d.N, n0);
   const int wave = wave_id();
   const int row0 = (wave / (kW / 2)) * 128, col0 = (wave % (kW / 2)) * (kFJ * 32);
+  A.frags(row0);
+  B.frags(col0);
   f32x16_t acc[4][kFJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -873,23 +614,23 @@ __device__ __forceinline__ void ring_tile(GemmDesc d, int64_t bid, int64_t tiles
     block_sync();
     Frags<kFJ> f0, f1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f0.a[i] = ROp<kAK, kW>::frag(slot_buf<0>(), row0 + i * 32, 0);
+    for (int i = 0; i < 4; ++i) f0.a[i] = A.frag(slot_buf<0>(), i, 0);
 #pragma unroll
-    for (int j = 0; j < kFJ; ++j) f0.b[j] = ROp<kBKm, kW>::frag(slot_buf<1>(), col0 + j * 32, 0);
+    for (int j = 0; j < kFJ; ++j) f0.b[j] = B.frag(slot_buf<1>(), j, 0);
     int s = 0;
     for (; s + 5 <= ksteps; s += 5) {
       const int64_t k2 = kbeg + static_cast<int64_t>(s + 2) * kRK;
-      step<kTy, 0>(acc, f0, f1, A, B, row0, col0, k2, kend);
-      step<kTy, 1>(acc, f0, f1, A, B, row0, col0, k2 + kRK, kend);
-      step<kTy, 2>(acc, f0, f1, A, B, row0, col0, k2 + 2 * kRK, kend);
-      step<kTy, 3>(acc, f0, f1, A, B, row0, col0, k2 + 3 * kRK, kend);
-      step<kTy, 4>(acc, f0, f1, A, B, row0, col0, k2 + 4 * kRK, kend);
+      step<kTy, 0>(acc, f0, f1, A, B, k2, kend);
+      step<kTy, 1>(acc, f0, f1, A, B, k2 + kRK, kend);
+      step<kTy, 2>(acc, f0, f1, A, B, k2 + 2 * kRK, kend);
+      step<kTy, 3>(acc, f0, f1, A, B, k2 + 3 * kRK, kend);
+      step<kTy, 4>(acc, f0, f1, A, B, k2 + 4 * kRK, kend);
     }
     const int64_t k2 = kbeg + static_cast<int64_t>(s + 2) * kRK;
-    if (s < ksteps) step<kTy, 0>(acc, f0, f1, A, B, row0, col0, k2, kend);
-    if (s + 1 < ksteps) step<kTy, 1>(acc, f0, f1, A, B, row0, col0, k2 + kRK, kend);
-    if (s + 2 < ksteps) step<kTy, 2>(acc, f0, f1, A, B, row0, col0, k2 + 2 * kRK, kend);
-    if (s + 3 < ksteps) step<kTy, 3>(acc, f0, f1, A, B, row0, col0, k2 + 3 * kRK, kend);
+    if (s < ksteps) step<kTy, 0>(acc, f0, f1, A, B, k2, kend);
+    if (s + 1 < ksteps) step<kTy, 1>(acc, f0, f1, A, B, k2 + kRK, kend);
+    if (s + 2 < ksteps) step<kTy, 2>(acc, f0, f1, A, B, k2 + 2 * kRK, kend);
+    if (s + 3 < ksteps) step<kTy, 3>(acc, f0, f1, A, B, k2 + 3 * kRK, kend);
     wait_vmcnt<0>();
   }
   // Every wave is done with the slots; each wave stages its output through
@@ -915,32 +656,6 @@ void k_ring(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int64_t k_per_split) {
 }  // namespace ring
 }  // namespace mfma2
 
-template <bool kAK, bool kBKm, int kEpi, int kWN, int kTy>
-static hipError_t launch_mfma_kernel(const GemmDesc& d, hipStream_t s) {
-  using namespace mfma2;
-  const int64_t tiles_m = (d.M + kBM - 1) / kBM, tiles_n = (d.N + kBM - 1) / kBM;
-  const int splits = d.k_splits > 1 ? d.k_splits : 1;
-  int64_t k_per = (d.K + splits - 1) / splits;
-  k_per = (k_per + kBK - 1) / kBK * kBK;
-  const int64_t blocks = tiles_m * tiles_n * splits;
-  auto kern = k_gemm2<kAK, kBKm, kEpi, kWN, kTy>;
-  // Spill stores would be counted by the loop's explicit vmcnt waits.
-  static int spills = -1;
-  if (spills < 0) {
-    hipFuncAttributes fa;
-    const hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
-    if (e != hipSuccess) return e;
-    spills = fa.localSizeBytes != 0;
-  }
-  if (spills) return hipErrorInvalidDeviceFunction;
-  GemmDesc dd = d;
-  dd.k_splits = splits;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * kWM * kWN), 0, s, dd,
-                     tiles_m, tiles_n, k_per);
-  return hipGetLastError();
-}
-
-
 template <bool kAK, bool kBKm, int kEpi, int kTy, int kW>
 static hipError_t launch_ring(const GemmDesc& d, hipStream_t s) {
   using namespace mfma2;
@@ -949,7 +664,7 @@ static hipError_t launch_ring(const GemmDesc& d, hipStream_t s) {
   int64_t k_per = (d.K + splits - 1) / splits;
   k_per = (k_per + ring::kRK - 1) / ring::kRK * ring::kRK;
   auto kern = ring::k_ring<kAK, kBKm, kEpi, kTy, kW>;
-  // As for the four-stage kernel: spill stores would break the explicit waits.
+  // Spill stores would be counted by the loop's explicit vmcnt waits.
   static int spills = -1;
   if (spills < 0) {
     hipFuncAttributes fa;
@@ -967,26 +682,19 @@ static hipError_t launch_ring(const GemmDesc& d, hipStream_t s) {
 
 template <int kTy>
 static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
+  // The three layouts of the FLCE products: logits X W^T (both operands
+  // k-contiguous), grad_X dZ W (A k-contiguous, B n-contiguous) and grad_W
+  // dZ^T X (both m/n-contiguous).
   if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits)
     return launch_ring<true, true, kEpiLogits, kTy, 4>(d, s);
-  // grad_X against the transposed head (both operands k-major): the ring on
-  // 4 waves of 128 x 128, like the logits.
-  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiStoreF32)
-    return launch_ring<true, true, kEpiStoreF32, kTy, 4>(d, s);
-  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiAccumF32)
-    return launch_ring<true, true, kEpiAccumF32, kTy, 4>(d, s);
-  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiStore16)
-    return launch_ring<true, true, kEpiStore16, kTy, 4>(d, s);
-  if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiAccum16)
-    return launch_ring<true, true, kEpiAccum16, kTy, 4>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
-    return launch_mfma_kernel<true, false, kEpiStoreF32, 4, kTy>(d, s);
+    return launch_ring<true, false, kEpiStoreF32, kTy, 4>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccumF32)
-    return launch_mfma_kernel<true, false, kEpiAccumF32, 4, kTy>(d, s);
+    return launch_ring<true, false, kEpiAccumF32, kTy, 4>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStore16)
-    return launch_mfma_kernel<true, false, kEpiStore16, 4, kTy>(d, s);
+    return launch_ring<true, false, kEpiStore16, kTy, 4>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)
-    return launch_mfma_kernel<true, false, kEpiAccum16, 4, kTy>(d, s);
+    return launch_ring<true, false, kEpiAccum16, kTy, 4>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStore16)
     return launch_ring<false, false, kEpiStore16, kTy, 4>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)

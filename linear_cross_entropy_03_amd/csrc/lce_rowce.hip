@@ -1454,45 +1454,6 @@ hipError_t launch_gather_rows(const void* src, int64_t row_bytes, int64_t rows, 
   return hipGetLastError();
 }
 
-// out[h, v] = W[v, h] for v < V, 0 for V <= v < ldo (16-bit elements); 64 x 64
-// tiles through LDS, 16-byte loads and stores.
-__global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ W, int64_t V,
-                                                     int64_t H, uint16_t* __restrict__ out,
-                                                     int64_t ldo) {
-  __shared__ __align__(16) uint16_t tile[64][72];  // [v][h]
-  const int64_t vb = static_cast<int64_t>(blockIdx.x) * 64, hb = static_cast<int64_t>(blockIdx.y) * 64;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = t; i < 512; i += 256) {
-    const int r = i >> 3, c = i & 7;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (vb + r < V && hb + c * 8 < H) v = *reinterpret_cast<const uint4*>(W + (vb + r) * H + hb + c * 8);
-    *reinterpret_cast<uint4*>(&tile[r][c * 8]) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = t; i < 512; i += 256) {
-    const int hh = i >> 3, c = i & 7;
-    if (hb + hh >= H || vb + c * 8 >= ldo) continue;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = static_cast<uint32_t>(tile[c * 8 + 2 * e][hh]) |
-             (static_cast<uint32_t>(tile[c * 8 + 2 * e + 1][hh]) << 16);
-    *reinterpret_cast<uint4*>(out + (hb + hh) * ldo + vb + c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-hipError_t launch_transpose16(const void* W, int64_t V, int64_t H, void* out, int64_t ldo,
-                              hipStream_t s) {
-  if (V <= 0 || H <= 0) return hipSuccess;
-  if (H % 8 != 0 || ldo % 64 != 0 || ldo < V) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(ldo / 64), static_cast<unsigned>((H + 63) / 64));
-  hipLaunchKernelGGL(k_transpose16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(W), V, H,
-                     static_cast<uint16_t*>(out), ldo);
-  return hipGetLastError();
-}
-
 // Workgroups stride over the rows (the grid is capped, so any n launches).
 __global__ __launch_bounds__(256) void k_zero_dead_rows(const int32_t* __restrict__ t, int64_t n,
                                                         int64_t V, int32_t ign,

@@ -74,31 +74,28 @@ def test_workspace_queries_and_plan(B):
 
 def test_row_packing_switch_and_workspace(B):
     """The packing switch returns the previous setting and does not change the
-    workspace size; 16-bit plans hold the packing buffers (row map and packed
-    targets, 4 bytes per row each, the chunk's gathered rows, one split-K
-    partial at least, and the transposed head when H <= chunk), float32 plans
-    none of them."""
+    workspace size; 16-bit plans hold the packing lists (row map and packed
+    targets, 4 bytes per row each, plus block counts) and at least one split-K
+    partial of chunk x H float32, whose first half also takes the chunk's
+    gathered 16-bit rows; float32 plans hold neither."""
     was = B.flce_set_row_packing(False)
     try:
         assert B.flce_set_row_packing(True) is False
         assert B.flce_set_row_packing(True) is True
-        N, H, V, C = 4096, 512, 3000, 1024
-        on = B.flce_workspace_bytes(N, H, V, B.BF16, C)
-        B.flce_set_row_packing(False)
-        assert B.flce_workspace_bytes(N, H, V, B.BF16, C) == on
-        f32 = B.flce_workspace_bytes(N, H, V, B.F32, C)
+        N, H, V = 4096, 512, 3000
         ldz = (V + 7) // 8 * 8
-        assert f32 >= 256 + N * 4 + C * ldz * 4
-        assert f32 < 256 + N * 4 + C * ldz * 4 + 4 * 256
-        base16 = 256 + N * 4 + C * ldz * 2
-        # ... and, as H <= chunk, the transposed head W^T [H, round_up(V, 64)].
-        wt = H * ((V + 63) // 64 * 64) * 2
-        assert on >= base16 + C * H * 4 + 2 * N * 4 + C * H * 2 + wt
-        assert on < base16 + C * H * 4 + 2 * N * 4 + C * H * 2 + wt + 16 * 256
-        # A chunk shorter than H leaves the head untransposed.
-        short = B.flce_workspace_bytes(N, H, V, B.BF16, 256)
-        base = 256 + N * 4 + 256 * ldz * 2 + 256 * H * 4 + 2 * N * 4 + 256 * H * 2
-        assert base <= short < base + 16 * 256
+        for C in (1024, 256):
+            on = B.flce_workspace_bytes(N, H, V, B.BF16, C)
+            B.flce_set_row_packing(False)
+            assert B.flce_workspace_bytes(N, H, V, B.BF16, C) == on
+            B.flce_set_row_packing(True)
+            f32 = B.flce_workspace_bytes(N, H, V, B.F32, C)
+            assert 256 + N * 4 + C * ldz * 4 <= f32 < 256 + N * 4 + C * ldz * 4 + 4 * 256
+            base16 = 256 + N * 4 + C * ldz * 2 + C * H * 4 + 2 * N * 4
+            assert base16 <= on < base16 + 16 * 256
+            parts = B.flce_workspace_parts(N, H, V, B.BF16, C)
+            assert sum(parts.values()) == on
+            assert parts["split_partials"] >= C * H * 4 >= 2 * C * H * 2
     finally:
         B.flce_set_row_packing(was)
 

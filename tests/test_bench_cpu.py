@@ -14,7 +14,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 LOGITS = "void lce::mfma2::ring::k_ring<true, true, 0, 0>(lce::GemmDesc, long, long, long)"
-GRAD_X = "void lce::mfma2::k_gemm2<true, false, 1, 4, 0>(lce::GemmDesc, long, long, long)"
+GRAD_X = "void lce::mfma2::ring::k_ring<true, false, 1, 0, 4>(lce::GemmDesc, long, long, long)"
 ROW_CE = "void lce::k_row_ce_pf<unsigned short, 16>(unsigned short const*, long)"
 COPY = "__amd_rocclr_copyBuffer"
 
@@ -86,6 +86,8 @@ def test_kernel_classes_cover_the_launched_gemms():
         GRAD_X: "grad_x_gemm",
         "void lce::mfma2::ring::k_ring<false, false, 1, 0>(lce::GemmDesc, long, long, long)": "grad_w_gemm",
         "void lce::mfma2::ring::k_ring<false, false, 2, 0>(lce::GemmDesc, long, long, long)": "grad_w_gemm",
+        "void lce::mfma2::ring::k_ring<false, false, 4, 0, 4>(lce::GemmDesc, long, long, long)": "grad_w_gemm",
+        "void lce::mfma2::ring::k_ring<true, false, 3, 0, 4>(lce::GemmDesc, long, long, long)": "grad_x_gemm",
         ROW_CE: "row_ce",
     }
     for name, kind in names.items():
@@ -99,27 +101,20 @@ def test_kernel_classes_cover_the_launched_gemms():
     (256, 64, 1024, "f32", 0), (1000, 136, 4099, "bf16", 256)])
 def test_workspace_parts_and_the_one_chunk_bound(N, H, V, dtype, chunk):
     """The library's workspace regions sum to its workspace query and have the
-    documented sizes; the bench's bound (one chunk of logits + (N + V) x 16 +
-    split-K partials) then holds the workspace except for the transposed head
-    and the chunk's gathered hidden states, which the bench reports apart."""
+    documented sizes, and the whole workspace is within the bench's bound:
+    one chunk of logits + (N + V) x 16 bytes + the grad_X split-K partials
+    (which hold the gathered rows of a packed chunk)."""
     from linear_cross_entropy_03_amd import binding as B
     dt = B.BF16 if dtype == "bf16" else B.F32
     e = 2 if dtype == "bf16" else 4
     up = lambda x: (x + 255) // 256 * 256
-    for wt_on in (True, False):
-        was = B.flce_set_transposed_head(wt_on)
-        try:
-            c, s = B.flce_plan(N, H, V, dt, chunk)
-            ws = B.flce_workspace_bytes(N, H, V, dt, chunk)
-            parts = bench.scratch_parts(B, N, H, V, dt, chunk)
-        finally:
-            B.flce_set_transposed_head(was)
-        assert parts["workspace"] == ws
-        assert parts["chunk_logits"] == up(c * ((V + 7) // 8 * 8) * e)
-        has_wt = wt_on and e == 2 and H <= c
-        assert parts["transposed_head"] == (up(H * ((V + 63) // 64 * 64) * e) if has_wt else 0)
-        assert parts["gathered_rows"] == (up(c * H * e) if e == 2 else 0)
-        assert parts["rows"] <= 256 + up(4 * N) and parts["pack_lists"] <= 3 * up(4 * N) + 4096
-        bound = bench.survey_bound_bytes(parts, N, V)
-        rest = ws - parts["transposed_head"] - parts["gathered_rows"]
-        assert rest <= bound
+    c, s = B.flce_plan(N, H, V, dt, chunk)
+    ws = B.flce_workspace_bytes(N, H, V, dt, chunk)
+    parts = bench.scratch_parts(B, N, H, V, dt, chunk)
+    assert set(parts) == {"rows", "chunk_logits", "split_partials", "pack_lists", "workspace"}
+    assert parts["workspace"] == ws
+    assert parts["chunk_logits"] == up(c * ((V + 7) // 8 * 8) * e)
+    if e == 2:
+        assert parts["split_partials"] >= up(c * H * 4)      # room for the gathered rows too
+    assert parts["rows"] <= 256 + up(4 * N) and parts["pack_lists"] <= 3 * up(4 * N) + 4096
+    assert ws <= bench.survey_bound_bytes(parts, N, V)
