@@ -105,6 +105,12 @@ struct Plan {
   // grad_X product writes partials. pack_ok is false for float32 inputs.
   bool pack_ok;
   size_t off_map, off_ptgt, off_bcnt, off_xs;
+  // When the rest of the split-K partials holds it too: the gathered rows
+  // transposed, [H, ldt] (ldt = chunk rounded up to 64), the k-contiguous B
+  // operand of the grad_W product.
+  bool xt_ok;
+  int64_t ldt;
+  size_t off_xt;
   size_t total;
 };
 
@@ -181,6 +187,14 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
                     static_cast<size_t>(H) * sizeof(float));
   p->pack_ok = is16(dtype);
   p->off_xs = p->off_split;
+  {
+    const size_t split_bytes = off - p->off_split;
+    const size_t xs_bytes = align_up(static_cast<size_t>(chunk) * static_cast<size_t>(H) * e);
+    p->ldt = round_up(chunk, 64);
+    p->off_xt = p->off_split + xs_bytes;
+    p->xt_ok = p->pack_ok &&
+               xs_bytes + static_cast<size_t>(H) * static_cast<size_t>(p->ldt) * e <= split_bytes;
+  }
   p->off_map = p->off_ptgt = p->off_bcnt = off;
   if (p->pack_ok) {
     const size_t n1 = static_cast<size_t>(std::max<int64_t>(N, 1));
@@ -315,6 +329,9 @@ struct Packer {
   int32_t* map = nullptr;          // packed row -> original row [N]
   const int32_t* ptgt = nullptr;   // packed targets [N]
   char* xs = nullptr;              // the chunk's gathered hidden states [chunk, H]
+  char* xt = nullptr;              // ... and transposed [H, ldt] (when t_on)
+  int64_t ldt = 0;
+  bool t_on = false;
   const int32_t* live = nullptr;   // &hdr->n_packed
 
   // Lists the rows whose target is valid against V_valid, zeroes the other
@@ -322,12 +339,15 @@ struct Packer {
   // their grad_X rows of gx_row_bytes bytes.
   int setup(const Plan& p, char* ws, WsHeader* hdr, const int32_t* targets, int64_t N,
             int64_t V_valid, int32_t ign, float* loss_rows, void* grad_X, int64_t gx_row_bytes,
-            hipStream_t s, bool allow = true) {
+            hipStream_t s, bool allow = true, bool allow_t = true) {
     on = allow && g_row_packing && p.pack_ok && N > 0;
     if (!on) return FLCE_OK;
     map = reinterpret_cast<int32_t*>(ws + p.off_map);
     ptgt = reinterpret_cast<const int32_t*>(ws + p.off_ptgt);
     xs = ws + p.off_xs;
+    t_on = allow_t && p.xt_ok;
+    xt = ws + p.off_xt;
+    ldt = p.ldt;
     live = &hdr->n_packed;
     LCE_TRY(timed(kKindOther, s, [&] {
       return launch_pack_rows(targets, N, V_valid, ign, map, const_cast<int32_t*>(ptgt),
@@ -342,14 +362,23 @@ struct Packer {
   RowPack chunk(int64_t r0) const {
     return on ? RowPack{map + r0, live, r0} : RowPack{nullptr, nullptr, 0};
   }
-  // The chunk's rows of X: gathered when packed, else rows r0.. of X.
+  // The chunk's rows of X: gathered when packed, else rows r0.. of X. With
+  // Xt given and the plan holding it, also their transpose (*Xt, else null).
   int rows_of(const void* X, int64_t r0, int64_t rows, int64_t H, size_t e, hipStream_t s,
-              const char** Xc) const {
+              const char** Xc, const char** Xt = nullptr) const {
     *Xc = static_cast<const char*>(X) + static_cast<size_t>(r0) * H * e;
+    if (Xt) *Xt = nullptr;
     if (!on) return FLCE_OK;
-    LCE_TRY(timed(kKindOther, s, [&] {
-      return launch_gather_rows(X, H * static_cast<int64_t>(e), rows, chunk(r0), xs, s);
-    }));
+    if (Xt && t_on) {
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_gather_rows_t(X, H, rows, chunk(r0), xs, xt, ldt, s);
+      }));
+      *Xt = xt;
+    } else {
+      LCE_TRY(timed(kKindOther, s, [&] {
+        return launch_gather_rows(X, H * static_cast<int64_t>(e), rows, chunk(r0), xs, s);
+      }));
+    }
     *Xc = xs;
     return FLCE_OK;
   }
@@ -361,7 +390,8 @@ struct Packer {
 };
 
 // The two gradient products of one chunk whose dlogits are in zbuf:
-//   grad_W = dZ_c^T X_c (stored on the first chunk, added after);
+//   grad_W = dZ_c^T X_c (stored on the first chunk, added after), reading
+//   the transposed gathered rows Xt ([H, ldt], k-contiguous) when given;
 //   grad_X rows = dZ_c W (stored, or added when accum_gx), W read as stored
 //   (n-major B operand).
 // grad_W runs first: it is the last reader of the chunk's gathered rows,
@@ -371,7 +401,7 @@ struct Packer {
 // split, or when a packed chunk adds to grad_X (the reduction then adds each
 // row to its original row). Either gradient may be null.
 int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_t V, void* zbuf,
-                      const char* Xc, int64_t rows, int64_t r0, int64_t N, bool first,
+                      const char* Xc, const char* Xt, int64_t rows, int64_t r0, int64_t N, bool first,
                       const Packer& pkr, const RowPack& pk, void* grad_X, bool accum_gx,
                       void* grad_W, int grad_dtype, const GradScaling& gsc, char* ws,
                       hipStream_t s) {
@@ -383,7 +413,11 @@ int gradient_products(const Plan& p, int dtype, const void* W, int64_t H, int64_
   if (grad_W) {
     GemmDesc g3{};
     g3.A = zbuf; g3.lda = p.ldz; g3.a_kmajor = false;
-    g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
+    if (Xt) {
+      g3.B = Xt; g3.ldb = p.ldt; g3.b_kmajor = true;
+    } else {
+      g3.B = Xc; g3.ldb = H; g3.b_kmajor = false;
+    }
     g3.C = grad_W; g3.ldc = H;
     g3.M = V; g3.N = H; g3.K = rows;
     g3.epilogue = first ? (g16 ? kEpiStore16 : kEpiStoreF32) : (g16 ? kEpiAccum16 : kEpiAccumF32);
@@ -463,9 +497,10 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
     const bool first = r0 == 0;
     // Packed: chunk rows are packed rows r0.. (live up to hdr->n_packed).
     const RowPack pk = pkr.chunk(r0);
-    const char* Xc;
-    st = pkr.rows_of(X, r0, rows, H, e, s, &Xc);
+    const char *Xc, *Xt;
+    st = pkr.rows_of(X, r0, rows, H, e, s, &Xc, grad_W ? &Xt : nullptr);
     if (st != FLCE_OK) return st;
+    if (!grad_W) Xt = nullptr;
     auto live = [&](GemmDesc& d, int dim) { pkr.limit(d, dim, r0); };
 
     GemmDesc g1{};
@@ -490,7 +525,7 @@ int flce_chunks(const Plan& p, int dtype, const void* X, const void* W, const vo
                              gsc.out_scale, gsc.out_shift, s, pk);
       }));
 
-    st = gradient_products(p, dtype, W, H, V, zbuf, Xc, rows, r0, N, first, pkr, pk, grad_X,
+    st = gradient_products(p, dtype, W, H, V, zbuf, Xc, Xt, rows, r0, N, first, pkr, pk, grad_X,
                            accum_gx, grad_W, grad_dtype, gsc, ws, s);
     if (st != FLCE_OK) return st;
   }
@@ -952,9 +987,10 @@ static int shard_backward_impl(const void* X, const void* W_shard, const void* b
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
     const RowPack pk = pkr.chunk(r0);
-    const char* Xc;
-    st = pkr.rows_of(X, r0, rows, H, e, s, &Xc);
+    const char *Xc, *Xt;
+    st = pkr.rows_of(X, r0, rows, H, e, s, &Xc, grad_W_shard ? &Xt : nullptr);
     if (st != FLCE_OK) return st;
+    if (!grad_W_shard) Xt = nullptr;
 
     GemmDesc g1{};
     g1.A = Xc; g1.lda = H; g1.a_kmajor = true;
@@ -974,8 +1010,8 @@ static int shard_backward_impl(const void* X, const void* W_shard, const void* b
         return launch_colsum(dtype, zbuf, p.ldz, rows, V_local, grad_bias_shard, grad_dtype, !first,
                              gsc.out_scale, gsc.out_shift, s, pk);
       }));
-    st = gradient_products(p, dtype, W_shard, H, V_local, zbuf, Xc, rows, r0, N, first, pkr, pk,
-                           grad_X, false, grad_W_shard, grad_dtype, gsc, ws, s);
+    st = gradient_products(p, dtype, W_shard, H, V_local, zbuf, Xc, Xt, rows, r0, N, first, pkr,
+                           pk, grad_X, false, grad_W_shard, grad_dtype, gsc, ws, s);
     if (st != FLCE_OK) return st;
   }
   return FLCE_OK;
@@ -1061,8 +1097,10 @@ static int jsd_impl(const void* X_s, const void* W_s, const void* X_t, const voi
   const bool teacher_fits =
       xs_bytes + static_cast<size_t>(p.chunk) * static_cast<size_t>(H_t) * e <= split_bytes;
   Packer pkr;
+  // The teacher's rows take the partial buffer's second half, so the student's
+  // grad_W reads its gathered rows as they are (no transposed copy).
   st = pkr.setup(p, ws, hdr, targets, N, V, ignore_index, loss_rows, grad_X_s,
-                 H_s * static_cast<int64_t>(ge), s, teacher_fits);
+                 H_s * static_cast<int64_t>(ge), s, teacher_fits, false);
   if (st != FLCE_OK) return st;
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
@@ -1094,7 +1132,7 @@ static int jsd_impl(const void* X_s, const void* W_s, const void* X_t, const voi
                             (pkr.on ? pkr.ptgt : targets) + r0, ignore_index, hdr,
                             pkr.on ? loss_rows : loss_rows + r0, gsc.row_shift, s, pk);
     }));
-    st = gradient_products(p, dtype, W_s, H_s, V, zs, Xs_c, rows, r0, N, first, pkr, pk, grad_X_s,
+    st = gradient_products(p, dtype, W_s, H_s, V, zs, Xs_c, nullptr, rows, r0, N, first, pkr, pk, grad_X_s,
                            false, grad_W_s, grad_dtype, gsc, ws, s);
     if (st != FLCE_OK) return st;
   }
@@ -1175,9 +1213,12 @@ static int dpo_impl(const void* X, const void* W, const int32_t* targets, int64_
   // nothing to the log-probabilities or the gradients: both passes run over
   // the packed rows (as in flce_chunks).
   Packer pkr;
-  // Chunk rows (gathered when packed) and their logits.
-  auto logits = [&](int64_t r0, int64_t rows, const char** Xc) {
-    int r = pkr.rows_of(X, r0, rows, H, e, s, Xc);
+  // Chunk rows (gathered when packed; transposed too when grad_W is wanted,
+  // also in the first pass, whose rows the second reuses for a single chunk)
+  // and their logits.
+  auto logits = [&](int64_t r0, int64_t rows, const char** Xc, const char** Xt) {
+    int r = pkr.rows_of(X, r0, rows, H, e, s, Xc, grad_W ? Xt : nullptr);
+    if (!grad_W) *Xt = nullptr;
     if (r != FLCE_OK) return hipErrorUnknown;
     GemmDesc g1{};
     g1.A = *Xc;
@@ -1202,9 +1243,10 @@ static int dpo_impl(const void* X, const void* W, const int32_t* targets, int64_
   const int32_t* tg = pkr.on ? pkr.ptgt : targets;
   // Pass 1: the CE row losses of every row (= minus the token log-probabilities).
   const char* Xc = nullptr;
+  const char* Xt = nullptr;
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t rows = std::min(p.chunk, N - r0);
-    LCE_TRY(logits(r0, rows, &Xc));
+    LCE_TRY(logits(r0, rows, &Xc, &Xt));
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_row_ce(dtype, zbuf, p.ldz, nullptr, p.ldz, rows, V, p.ldz - V, tg + r0,
                            ignore_index, hdr, pkr.on ? loss_rows : loss_rows + r0, nullptr, 0, s,
@@ -1226,13 +1268,13 @@ static int dpo_impl(const void* X, const void* W, const int32_t* targets, int64_
     const int64_t rows = std::min(p.chunk, N - r0);
     const bool first = r0 == 0;
     const RowPack pk = pkr.chunk(r0);
-    if (!one_chunk) LCE_TRY(logits(r0, rows, &Xc));
+    if (!one_chunk) LCE_TRY(logits(r0, rows, &Xc, &Xt));
     LCE_TRY(timed(kKindRowCE, s, [&] {
       return launch_row_ce(dtype, zbuf, p.ldz, zbuf, p.ldz, rows, V, p.ldz - V, tg + r0,
                            ignore_index, hdr, pkr.on ? loss_rows : loss_rows + r0,
                            pkr.on ? row_scale : row_scale + r0, gsc.row_shift, s, pk);
     }));
-    st = gradient_products(p, dtype, W, H, V, zbuf, Xc, rows, r0, N, first, pkr, pk, grad_X, false,
+    st = gradient_products(p, dtype, W, H, V, zbuf, Xc, Xt, rows, r0, N, first, pkr, pk, grad_X, false,
                            grad_W, grad_dtype, gsc, ws, s);
     if (st != FLCE_OK) return st;
   }

@@ -324,6 +324,12 @@ hipError_t launch_pack_rows(const int32_t* targets, int64_t n, int64_t V, int32_
 // of row_bytes bytes (a multiple of 16, 16-byte aligned).
 hipError_t launch_gather_rows(const void* src, int64_t row_bytes, int64_t rows, RowPack pk,
                               void* out, hipStream_t s);
+// The same for 16-bit rows of H elements (H a multiple of 8), also writing
+// the transpose: out_t[h, r] = src[pk.map[r], h] ([H, ldt], ldt a multiple of
+// 64 and at least rows); columns r of the last 64-row tile past the live
+// count are zeros.
+hipError_t launch_gather_rows_t(const void* src, int64_t H, int64_t rows, RowPack pk, void* out,
+                                void* out_t, int64_t ldt, hipStream_t s);
 // Zeros the rows r of G ([n, row_bytes]) whose target is not packed.
 hipError_t launch_zero_dead_rows(const int32_t* targets, int64_t n, int64_t V, int32_t ign,
                                  void* G, int64_t row_bytes, hipStream_t s);

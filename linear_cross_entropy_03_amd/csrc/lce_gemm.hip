@@ -682,9 +682,10 @@ static hipError_t launch_ring(const GemmDesc& d, hipStream_t s) {
 
 template <int kTy>
 static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
-  // The three layouts of the FLCE products: logits X W^T (both operands
+  // The layouts of the FLCE products: logits X W^T (both operands
   // k-contiguous), grad_X dZ W (A k-contiguous, B n-contiguous) and grad_W
-  // dZ^T X (both m/n-contiguous).
+  // dZ^T X (A m-contiguous; B the transposed gathered rows, k-contiguous, or
+  // X itself, n-contiguous).
   if (d.a_kmajor && d.b_kmajor && d.epilogue == kEpiLogits)
     return launch_ring<true, true, kEpiLogits, kTy, 4>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStoreF32)
@@ -695,6 +696,14 @@ static hipError_t launch_mfma_ty(const GemmDesc& d, hipStream_t s) {
     return launch_ring<true, false, kEpiStore16, kTy, 4>(d, s);
   if (d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)
     return launch_ring<true, false, kEpiAccum16, kTy, 4>(d, s);
+  if (!d.a_kmajor && d.b_kmajor && d.epilogue == kEpiStore16)
+    return launch_ring<false, true, kEpiStore16, kTy, 4>(d, s);
+  if (!d.a_kmajor && d.b_kmajor && d.epilogue == kEpiAccum16)
+    return launch_ring<false, true, kEpiAccum16, kTy, 4>(d, s);
+  if (!d.a_kmajor && d.b_kmajor && d.epilogue == kEpiStoreF32)
+    return launch_ring<false, true, kEpiStoreF32, kTy, 4>(d, s);
+  if (!d.a_kmajor && d.b_kmajor && d.epilogue == kEpiAccumF32)
+    return launch_ring<false, true, kEpiAccumF32, kTy, 4>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiStore16)
     return launch_ring<false, false, kEpiStore16, kTy, 4>(d, s);
   if (!d.a_kmajor && !d.b_kmajor && d.epilogue == kEpiAccum16)

@@ -1454,6 +1454,53 @@ hipError_t launch_gather_rows(const void* src, int64_t row_bytes, int64_t rows, 
   return hipGetLastError();
 }
 
+// Tiles of 64 chunk rows x 64 columns (16-bit elements): the live rows are
+// read once, stored row-major to out ([rows, H]) and, through LDS, transposed
+// to out_t ([H, ldt], columns = chunk rows; the tile's rows past the live
+// count are written as zeros).
+__global__ __launch_bounds__(256) void k_gather_rows_t(const uint16_t* __restrict__ src, int64_t H,
+                                                       RowPack pk, uint16_t* __restrict__ out,
+                                                       uint16_t* __restrict__ out_t, int64_t ldt) {
+  __shared__ __align__(16) uint16_t tile[64][72];  // [row][column]
+  const int64_t live = static_cast<int64_t>(*pk.live) - pk.base;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64, h0 = static_cast<int64_t>(blockIdx.y) * 64;
+  if (r0 >= live) return;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = t; i < 512; i += 256) {
+    const int r = i >> 3, c = i & 7;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r0 + r < live && h0 + c * 8 < H) {
+      v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(pk.map[r0 + r]) * H + h0 + c * 8);
+      *reinterpret_cast<uint4*>(out + (r0 + r) * H + h0 + c * 8) = v;
+    }
+    *reinterpret_cast<uint4*>(&tile[r][c * 8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = t; i < 512; i += 256) {
+    const int hh = i >> 3, c = i & 7;
+    if (h0 + hh >= H) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = static_cast<uint32_t>(tile[c * 8 + 2 * e][hh]) |
+             (static_cast<uint32_t>(tile[c * 8 + 2 * e + 1][hh]) << 16);
+    *reinterpret_cast<uint4*>(out_t + (h0 + hh) * ldt + r0 + c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+hipError_t launch_gather_rows_t(const void* src, int64_t H, int64_t rows, RowPack pk, void* out,
+                                void* out_t, int64_t ldt, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (H % 8 != 0 || ldt % 64 != 0 || ldt < rows || pk.live == nullptr || pk.map == nullptr)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>((rows + 63) / 64), static_cast<unsigned>((H + 63) / 64));
+  hipLaunchKernelGGL(k_gather_rows_t, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), H, pk,
+                     static_cast<uint16_t*>(out), static_cast<uint16_t*>(out_t), ldt);
+  return hipGetLastError();
+}
+
 // Workgroups stride over the rows (the grid is capped, so any n launches).
 __global__ __launch_bounds__(256) void k_zero_dead_rows(const int32_t* __restrict__ t, int64_t n,
                                                         int64_t V, int32_t ign,
