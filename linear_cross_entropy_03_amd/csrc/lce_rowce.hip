@@ -26,11 +26,19 @@ __global__ __launch_bounds__(1024) void k_count_targets(const int32_t* __restric
   if (threadIdx.x == 0) { s_valid = 0; s_bad = 0; }
   __syncthreads();
   int valid = 0, bad = 0;
-  for (int64_t i = threadIdx.x; i < n; i += 1024) {
-    const int32_t y = t[i];
-    if (y == ign) continue;
+  auto count = [&](int32_t y) {
+    if (y == ign) return;
     if (y >= 0 && static_cast<int64_t>(y) < V) ++valid; else ++bad;
+  };
+  // 16-byte loads, several in flight per lane, then the unaligned rest.
+  const int64_t n4 = (reinterpret_cast<uintptr_t>(t) & 15u) == 0 ? n / 4 : 0;
+  const int4* t4 = reinterpret_cast<const int4*>(t);
+#pragma unroll 8
+  for (int64_t i = threadIdx.x; i < n4; i += 1024) {
+    const int4 v = t4[i];
+    count(v.x); count(v.y); count(v.z); count(v.w);
   }
+  for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += 1024) count(t[i]);
   atomicAdd(&s_valid, valid);  // integer sums: exact in any order
   atomicAdd(&s_bad, bad);
   __syncthreads();
@@ -1112,8 +1120,9 @@ hipError_t launch_shift_labels(const int32_t* labels, int64_t B, int64_t S, int3
 // ------------------------------------------------------------ loss reduce
 
 // Sum of per-row losses in float64, in a fixed order independent of how the
-// rows were chunked (lane-strided partial sums, a butterfly within each wave,
-// the 16 wave sums in wave order); mean divides by the valid-row count. One
+// rows were chunked (lane-strided partial sums over groups of 4 rows, a
+// butterfly within each wave, the 16 wave sums in wave order); mean divides
+// by the valid-row count. One
 // barrier: the launch is latency-bound, so the tree through LDS is kept short.
 __global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ rows, int64_t n,
                                                       const WsHeader* __restrict__ hdr,
@@ -1121,7 +1130,18 @@ __global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ 
   __shared__ double wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   double acc = 0.0;
-  for (int64_t i = tid; i < n; i += 1024) acc += static_cast<double>(rows[i]);
+  // 16-byte loads, several in flight per lane, then the unaligned rest.
+  const int64_t n4 = (reinterpret_cast<uintptr_t>(rows) & 15u) == 0 ? n / 4 : 0;
+  const float4* r4 = reinterpret_cast<const float4*>(rows);
+#pragma unroll 8
+  for (int64_t i = tid; i < n4; i += 1024) {
+    const float4 v = r4[i];
+    acc += static_cast<double>(v.x);
+    acc += static_cast<double>(v.y);
+    acc += static_cast<double>(v.z);
+    acc += static_cast<double>(v.w);
+  }
+  for (int64_t i = n4 * 4 + tid; i < n; i += 1024) acc += static_cast<double>(rows[i]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
   if (lane == 0) wsum[w] = acc;
@@ -1262,12 +1282,68 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   Elem<TO>::store(out + ro * ld_out + c, acc);
 }
 
+// The same, kVec consecutive columns per lane (one 16-byte output vector; the
+// same additions in the same order, so the results are identical).
+template <typename TO>
+__global__ __launch_bounds__(256) void k_splitk_reduce_v(const float* __restrict__ parts, int splits,
+                                                         int64_t stride, int64_t rows, int64_t cols,
+                                                         int64_t ld_out, TO* __restrict__ out,
+                                                         int accumulate, RowPack pk) {
+  constexpr int kV = Elem<TO>::kVec;
+  if (pk.live != nullptr) {
+    const int64_t n = static_cast<int64_t>(*pk.live) - pk.base;
+    if (n < rows) rows = n;
+  }
+  const int64_t cv = cols / kV;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows * cv) return;
+  const int64_t r = i / cv, c = (i - r * cv) * kV;
+  float acc[kV];
+#pragma unroll
+  for (int q = 0; q < kV; q += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(parts + r * cols + c + q);
+    acc[q] = v.x; acc[q + 1] = v.y; acc[q + 2] = v.z; acc[q + 3] = v.w;
+  }
+  for (int sp = 1; sp < splits; ++sp) {
+#pragma unroll
+    for (int q = 0; q < kV; q += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(parts + sp * stride + r * cols + c + q);
+      acc[q] += v.x; acc[q + 1] += v.y; acc[q + 2] += v.z; acc[q + 3] += v.w;
+    }
+  }
+  const int64_t ro = pk.map != nullptr ? static_cast<int64_t>(pk.map[r]) : r;
+  uint4* o = reinterpret_cast<uint4*>(out + ro * ld_out + c);
+  if (accumulate) {
+    float old[kV];
+    Elem<TO>::unpack(*o, old);
+#pragma unroll
+    for (int q = 0; q < kV; ++q) acc[q] += old[q];
+  }
+  *o = Elem<TO>::pack(acc);
+}
+
 hipError_t launch_splitk_reduce(const float* parts, int splits, int64_t split_stride, int64_t rows,
                                 int64_t cols, int64_t ld_out, void* out, int out_dtype,
                                 bool accumulate, hipStream_t s, RowPack pk) {
+  const int acc = accumulate ? 1 : 0;
+  const int kv = out_dtype == 0 ? 4 : 8;
+  if (cols % kv == 0 && ld_out % kv == 0 && split_stride % 4 == 0 &&
+      (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (reinterpret_cast<uintptr_t>(parts) & 15u) == 0) {
+    const int64_t nv = rows * (cols / kv);
+    const dim3 grid(static_cast<unsigned>((nv + 255) / 256));
+    if (out_dtype == 1)
+      hipLaunchKernelGGL(k_splitk_reduce_v<uint16_t>, grid, dim3(256), 0, s, parts, splits,
+                         split_stride, rows, cols, ld_out, static_cast<uint16_t*>(out), acc, pk);
+    else if (out_dtype == 2)
+      hipLaunchKernelGGL(k_splitk_reduce_v<Half>, grid, dim3(256), 0, s, parts, splits,
+                         split_stride, rows, cols, ld_out, static_cast<Half*>(out), acc, pk);
+    else
+      hipLaunchKernelGGL(k_splitk_reduce_v<float>, grid, dim3(256), 0, s, parts, splits,
+                         split_stride, rows, cols, ld_out, static_cast<float*>(out), acc, pk);
+    return hipGetLastError();
+  }
   const int64_t n = rows * cols;
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
-  const int acc = accumulate ? 1 : 0;
   if (out_dtype == 1)
     hipLaunchKernelGGL(k_splitk_reduce<uint16_t>, grid, dim3(256), 0, s, parts, splits, split_stride,
                        rows, cols, ld_out, static_cast<uint16_t*>(out), acc, pk);
