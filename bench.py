@@ -139,7 +139,7 @@ def cpu_baseline(inp, cfg, target_s):
 KERNEL_KINDS = {  # kernel-name fragment -> kind reported by the timing hooks
     "k_ring<true, true, 0": "logits_gemm",     # X W^T (both operands k-contiguous)
     "k_ring<true, false": "grad_x_gemm",       # dZ W
-    "k_ring<false, false": "grad_w_gemm",      # dZ^T X
+    "k_ring<false, ": "grad_w_gemm",           # dZ^T X (X transposed, or as stored)
     "k_row_ce": "row_ce",
 }
 

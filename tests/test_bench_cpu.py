@@ -87,6 +87,7 @@ def test_kernel_classes_cover_the_launched_gemms():
         "void lce::mfma2::ring::k_ring<false, false, 1, 0>(lce::GemmDesc, long, long, long)": "grad_w_gemm",
         "void lce::mfma2::ring::k_ring<false, false, 2, 0>(lce::GemmDesc, long, long, long)": "grad_w_gemm",
         "void lce::mfma2::ring::k_ring<false, false, 4, 0, 4>(lce::GemmDesc, long, long, long)": "grad_w_gemm",
+        "void lce::mfma2::ring::k_ring<false, true, 2, 0, 4>(lce::GemmDesc, long, long, long)": "grad_w_gemm",
         "void lce::mfma2::ring::k_ring<true, false, 3, 0, 4>(lce::GemmDesc, long, long, long)": "grad_x_gemm",
         ROW_CE: "row_ce",
     }
