@@ -192,7 +192,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows, P
     const size_t xs_bytes = align_up(static_cast<size_t>(chunk) * static_cast<size_t>(H) * e);
     p->ldt = round_up(chunk, 64);
     p->off_xt = p->off_split + xs_bytes;
-    p->xt_ok = p->pack_ok &&
+    p->xt_ok = p->pack_ok && p->ldt < kMax16Stride &&
                xs_bytes + static_cast<size_t>(H) * static_cast<size_t>(p->ldt) * e <= split_bytes;
   }
   p->off_map = p->off_ptgt = p->off_bcnt = off;

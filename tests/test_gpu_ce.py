@@ -97,6 +97,19 @@ def test_ce_bf16_ragged_and_streaming(B, V):
     check_max_rel(g, ref_g, TOL["bf16"]["grad"], "grad_logits")
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 262147), ("f32", 140003)])
+def test_ce_streaming_rows_in_place(B, dtype, V):
+    """Rows beyond the register-resident limit (two streaming passes in
+    batches of vectors), misaligned row starts, gradient over the logits."""
+    N = 40
+    inp = synth.make_ce_inputs(N, V, dtype, std=2.0, ignore_frac=0.1, seed=V % 997)
+    say("ce streaming in place", dtype, N, V)
+    loss, g, _, _ = _run_ce(B, inp, "mean", mode="inplace")
+    ref_loss, ref_g, _ = O.cross_entropy(inp["logits_f32"], inp["targets"], reduction="mean")
+    check_scalar(loss, ref_loss, TOL[dtype]["loss"])
+    check_max_rel(g, ref_g, TOL[dtype]["grad"], "grad_logits")
+
+
 @pytest.mark.parametrize("V", [1003, 300001])
 def test_ce_f16(B, V):
     """Half-precision logits: register-resident and streaming rows."""
