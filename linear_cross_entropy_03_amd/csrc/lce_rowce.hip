@@ -74,15 +74,6 @@ __device__ __forceinline__ RowSplit split_row(const T* z, int64_t V) {
   return {head, nvec, head + nvec * kVec};
 }
 
-// Vectors per lane in flight in a streaming pass over a row too long for
-// registers.
-constexpr int kStream = 8;
-// The batched passes address the row through 32-bit buffer offsets,
-// including the last batch's lanes past its end.
-__device__ __forceinline__ bool stream_batched(int64_t nvec, int threads) {
-  return (nvec + static_cast<int64_t>(kStream) * threads) * 16 < (int64_t(1) << 31);
-}
-
 // Fold x into a running (max, sum of exp(x - max)) pair.
 __device__ __forceinline__ void online_push(float& m, float& s, float x) {
   const float mn = fmaxf(m, x);
@@ -132,6 +123,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
   const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo),
                                            static_cast<short>(0), n, 0x00020000);
+}
+
+// Vectors per lane in flight in a streaming pass over a row too long for
+// registers.
+constexpr int kStream = 8;
+// The batched passes address the row through 32-bit buffer offsets,
+// including the last batch's lanes past its end.
+__device__ __forceinline__ bool stream_batched(int64_t nvec, int threads) {
+  return (nvec + static_cast<int64_t>(kStream) * threads) * 16 < (int64_t(1) << 31);
+}
+
+// f(vi, v) for every 16-byte vector vi < nvec of one row (zv), lane-strided
+// (vector j kThreads + tid of each batch goes to lane tid): kStream
+// range-checked loads per lane in flight before any is used. f may write
+// vector vi in place (it was loaded by the same lane).
+template <int kThreads, typename F>
+__device__ __forceinline__ void stream_row(const uint4* zv, int64_t nvec, F&& f) {
+  const int tid = threadIdx.x;
+  const int64_t nbatch = stream_batched(nvec, kThreads) ? nvec : 0;
+  for (int64_t vi = nbatch + tid; vi < nvec; vi += kThreads) f(vi, zv[vi]);
+  if (nbatch == 0) return;
+  const __amdgpu_buffer_rsrc_t rv = row_rsrc(zv, nvec * 16);
+  for (int64_t b0 = 0; b0 < nbatch; b0 += kStream * kThreads) {
+    uint4 sb[kStream];
+#pragma unroll
+    for (int j = 0; j < kStream; ++j)
+      sb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rv, static_cast<int>((b0 + j * kThreads + tid) * 16), 0, 0));
+#pragma unroll
+    for (int j = 0; j < kStream; ++j) {
+      const int64_t vi = b0 + j * kThreads + tid;
+      if (vi < nvec) f(vi, sb[j]);
+    }
+  }
 }
 
 // One element's bits through a buffer descriptor (zero out of range).
@@ -285,31 +310,11 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
     s = ls;
   } else {
     if (sc.n > 0) count_partial<kThreads>(sc, targets, V, ign, t_first, cnt);
-    // Batches of kStream vectors per lane, all loads of a batch in flight
-    // before any is used (range-checked: zeros past the row, not folded in);
-    // rows beyond 32-bit buffer offsets take one vector at a time.
-    const __amdgpu_buffer_rsrc_t rv = row_rsrc(zv, rs.nvec * 16);
-    const int64_t nbatch = stream_batched(rs.nvec, kThreads) ? rs.nvec : 0;
-    for (int64_t vi = nbatch + tid; vi < rs.nvec; vi += kThreads) {
+    stream_row<kThreads>(zv, rs.nvec, [&](int64_t, const uint4& v) {
       float f[kVec];
-      E::unpack(zv[vi], f);
+      E::unpack(v, f);
       online_push_vec<kVec>(m, s, f);
-    }
-    for (int64_t b0 = 0; b0 < nbatch; b0 += kStream * kThreads) {
-      uint4 sb[kStream];
-#pragma unroll
-      for (int j = 0; j < kStream; ++j)
-        sb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rv, static_cast<int>((b0 + j * kThreads + tid) * 16), 0, 0));
-#pragma unroll
-      for (int j = 0; j < kStream; ++j) {
-        if (b0 + j * kThreads + tid < rs.nvec) {
-          float f[kVec];
-          E::unpack(sb[j], f);
-          online_push_vec<kVec>(m, s, f);
-        }
-      }
-    }
+    });
     if (tid < rs.head) online_push(m, s, E::load(z + tid));
     if (tid < V - rs.tail0) online_push(m, s, E::load(z + rs.tail0 + tid));
   }
@@ -369,35 +374,14 @@ __device__ __forceinline__ void row_ce_grad(const T* Z, int64_t ldz, T* G, int64
       }
     }
   } else {
-    const __amdgpu_buffer_rsrc_t rv = row_rsrc(zv, rs.nvec * 16);
-    const int64_t nbatch = stream_batched(rs.nvec, kThreads) ? rs.nvec : 0;
-    for (int64_t vi = nbatch + tid; vi < rs.nvec; vi += kThreads) {
+    stream_row<kThreads>(zv, rs.nvec, [&](int64_t vi, const uint4& v) {
       float f[kVec];
-      E::unpack(zv[vi], f);
+      E::unpack(v, f);
       const int64_t v0 = rs.head + vi * kVec;
 #pragma unroll
       for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
       store_grad_vec(gv + vi, E::pack(f), nt);
-    }
-    for (int64_t b0 = 0; b0 < nbatch; b0 += kStream * kThreads) {
-      uint4 sb[kStream];
-#pragma unroll
-      for (int j = 0; j < kStream; ++j)
-        sb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rv, static_cast<int>((b0 + j * kThreads + tid) * 16), 0, 0));
-#pragma unroll
-      for (int j = 0; j < kStream; ++j) {
-        const int64_t vi = b0 + j * kThreads + tid;
-        if (vi < rs.nvec) {
-          float f[kVec];
-          E::unpack(sb[j], f);
-          const int64_t v0 = rs.head + vi * kVec;
-#pragma unroll
-          for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
-          store_grad_vec(gv + vi, E::pack(f), nt);
-        }
-      }
-    }
+    });
   }
   if (tid < rs.head) E::store(g + tid, grad_of(E::load(z + tid), tid));
   if (tid < V - rs.tail0) {
@@ -756,11 +740,11 @@ __global__ __launch_bounds__(kThreads) void k_shard_stats(const T* __restrict__ 
     zt = E::load(&zt_bits);
   } else {
     if (sc.n > 0) count_partial<kThreads>(sc, targets, Vg, ign, t_first, cnt);
-    for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+    stream_row<kThreads>(zv, rs.nvec, [&](int64_t, const uint4& v) {
       float f[kVec];
-      E::unpack(zv[vi], f);
+      E::unpack(v, f);
       online_push_vec<kVec>(m, s, f);
-    }
+    });
     if (tid < rs.head) online_push(m, s, E::load(z + tid));
     if (tid < Vl - rs.tail0) online_push(m, s, E::load(z + rs.tail0 + tid));
     if (tid == 0 && here) zt = E::load(z + local);
@@ -865,14 +849,14 @@ __global__ __launch_bounds__(kThreads) void k_shard_grad(T* Z, int64_t ldz, int6
   };
   const RowSplit rs = split_row(z, Vl);
   uint4* zv = reinterpret_cast<uint4*>(z + rs.head);
-  for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+  stream_row<kThreads>(zv, rs.nvec, [&](int64_t vi, const uint4& v) {
     float f[kVec];
-    E::unpack(zv[vi], f);
+    E::unpack(v, f);
     const int64_t j0 = rs.head + vi * kVec;
 #pragma unroll
     for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], j0 + i);
     zv[vi] = E::pack(f);
-  }
+  });
   if (tid < rs.head) E::store(z + tid, grad_of(E::load(z + tid), tid));
   if (tid < Vl - rs.tail0) {
     const int64_t j = rs.tail0 + tid;
