@@ -6,8 +6,8 @@
 //   1. logits GEMM     Z_c = X_c W^T (+ b)        -> workspace chunk buffer
 //   2. row CE          loss rows; Z_c := dZ_c in place
 //   3. bias colsum     grad_bias (+)= column sums of dZ_c
-//   4. grad_X GEMM     grad_X[c rows] = dZ_c W
-//   5. grad_W GEMM     grad_W (+)= dZ_c^T X_c
+//   4. grad_W GEMM     grad_W (+)= dZ_c^T X_c
+//   5. grad_X GEMM     grad_X[c rows] = dZ_c W
 // followed by one deterministic loss reduction. Everything is enqueued on the
 // caller's stream; nothing is allocated.
 #include <hip/hip_runtime.h>

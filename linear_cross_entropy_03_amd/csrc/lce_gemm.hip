@@ -3,14 +3,14 @@
 // gradient and the accumulated head gradient):
 //   logits   Z_c  = X_c W^T (+ b)   A = X_c  (k-major)  B = W  (k-major)
 //   grad_X   dX_c = dZ_c W          A = dZ_c (k-major)  B = W  (n-major)
-//   grad_W   dW  += dZ_c^T X_c      A = dZ_c (m-major)  B = X_c (n-major)
+//   grad_W   dW  += dZ_c^T X_c      A = dZ_c (m-major)  B = X_c^T gathered
+//                                   (k-major), or X_c as stored (n-major)
 //
 // 16-bit path: v_mfma_f32_32x32x16_bf16 (or _f16 for IEEE half inputs, the
-// DeepSpeed vocab-parallel CE page's FP16 case) with fp32 accumulation, 256x256
-// tiles on 8 waves, operands staged in LDS by direct HBM->LDS loads. Two
-// pipelines (namespace mfma2): 32-wide k stages in four buffers (grad_X), and
-// 64-wide k steps through a ring of five single-operand slots (logits and
-// grad_W); see the comment at each.
+// DeepSpeed vocab-parallel CE page's FP16 case) with fp32 accumulation,
+// 256x256 tiles on 4 waves, operands staged in LDS by direct HBM->LDS loads,
+// K in 64-wide steps through a ring of five single-operand slots (namespace
+// mfma2::ring; see the comment there).
 // fp32 path: a plain LDS-tiled VALU kernel (namespace valu).
 #include "lce_common.h"
 
@@ -153,11 +153,12 @@ struct Frags {
 
 // Output through LDS. The MFMA result layout gives each lane 4 consecutive
 // columns of one row, so direct stores touch 32 rows per instruction with 8
-// or 16 bytes each. Each wave instead takes its result 128 x 64 at a time and
-// writes half of that (64 rows) into its own LDS region and reads it back as whole row segments:
-// 8 lanes per 128-byte row (bf16) or 16 lanes per 256-byte row (fp32), so
-// every store instruction covers full cache lines. Slots are XOR-swizzled by
-// row to spread the column-wise writes over the banks.
+// or 16 bytes each. Each wave instead takes its result 128 x 64 at a time,
+// writes part of that (64 rows for bf16, 32 for fp32) into its own LDS
+// region and reads it back as whole row segments: 8 lanes per 128-byte row
+// (bf16) or 16 lanes per 256-byte row (fp32), so every store instruction
+// covers full cache lines. Slots are XOR-swizzled by row to spread the
+// column-wise writes over the banks.
 
 // Output stores. With LCE_NT_STORES they are non-temporal: the outputs
 // (chunk logits, gradients) are not read again by this kernel, so they are
