@@ -605,13 +605,15 @@ def bench_grad16(torch, B, X, W, y, cfg, reps=5):
     return out
 
 
-def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=8192, reps=3):
+def bench_multihead(torch, B, X, W, y, cfg, K=5, n_rows=None, reps=3):
     """K LM heads over shared hidden states (the liger README's Medusa example:
-    5 heads) at the 8B head's shape on the first n_rows token rows. Head k's
-    weight is the workload's W rolled by 7k rows and its targets are the
-    targets shifted by k positions (a head predicting further ahead); all on
-    the device, no new host draws. GEMM work per call: K x 6 x n x H x V flop."""
-    N, H, V = n_rows, cfg["H"], cfg["V"]
+    5 heads) at the 8B head's shape, on all its token rows by default (the
+    headline step's rows, so each head's work matches one headline step).
+    Head k's weight is the workload's W rolled by 7k rows and its targets are
+    the targets shifted by k positions (a head predicting further ahead); all
+    on the device, no new host draws. GEMM work per call: K x 6 x n x H x V
+    flop."""
+    N, H, V = n_rows or cfg["N"], cfg["H"], cfg["V"]
     Xm = X[:N]
     Wk = torch.stack([torch.roll(W, shifts=7 * k, dims=0) for k in range(K)]).contiguous()
     yk = torch.stack([torch.roll(y[:N], shifts=-k) for k in range(K)]).contiguous()
