@@ -102,9 +102,10 @@ int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
  * per-row losses, [1] one chunk of logits / dlogits (chunk x round_up(V, 8)
  * elements), [2] the grad_X K-split partials (float32, S x chunk x H for the
  * largest split S used, at least one for 16-bit inputs; with row packing a
- * chunk's gathered hidden states, chunk x H 16-bit elements, share its first
- * half), [3] the packed-row lists (3 x N int32 and the pack kernels' block
- * counts; 0 for float32 inputs). The parts sum to flce_workspace_bytes.
+ * chunk's gathered hidden states, chunk x H 16-bit elements, and when they
+ * fit their transpose too, share it), [3] the packed-row lists (3 x N int32
+ * and the pack kernels' block counts; 0 for float32 inputs). The parts sum
+ * to flce_workspace_bytes.
  * parts must hold 4 entries. Returns FLCE_OK or FLCE_E_INVALID_ARG.
  */
 int flce_workspace_parts(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
