@@ -144,14 +144,25 @@ KERNEL_KINDS = {  # kernel-name fragment -> kind reported by the timing hooks
 }
 
 
+def code_tokens(text):
+    """C++ source without comments and with whitespace runs collapsed, so that
+    comment and layout edits do not count as kernel changes (string literals
+    in the HIP sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources; traffic figures are valid only for this hash."""
+    """Hash of the HIP sources' code (comments and layout ignored); traffic
+    figures are valid only for this hash."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_cross_entropy_03_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update((f + "\n" + code_tokens(fh.read())).encode())
     return h.hexdigest()[:16]
 
 

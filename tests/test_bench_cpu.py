@@ -79,6 +79,14 @@ def test_traffic_is_dropped_when_the_sources_change(tmp_path, monkeypatch):
     assert bench.load_traffic("unit") is None
 
 
+def test_source_hash_ignores_comments_and_layout():
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* no\n overflow */ }\n"
+    b = "int f(int x) {\n    return 2 * x;\n}"
+    c = "int f(int x) { return 3 * x; }"
+    assert bench.code_tokens(a) == bench.code_tokens(b)
+    assert bench.code_tokens(a) != bench.code_tokens(c)
+
+
 def test_kernel_classes_cover_the_launched_gemms():
     """Every GEMM and row kernel of the FLCE step maps to one class."""
     names = {
