@@ -742,3 +742,58 @@ def test_row_packing_over_a_thousand_pack_blocks(packing):
     Xs, Ws, _, ys = oracle_inputs(inp)
     ref_rows, _, _ = O.flce(Xs[rows], Ws, ys[rows], reduction="none", want_grads=False)
     check_max_rel(l1.cpu().numpy()[rows], ref_rows, TOL["bf16"]["loss"], "sampled row losses")
+
+
+def _guarded_workspace(n, guard=1 << 13):
+    """A workspace of exactly n bytes followed by `guard` bytes of 0x5A."""
+    import torch
+    buf = torch.full((n + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    return buf, buf[:n]
+
+
+def _guard_intact(buf, n):
+    import torch
+    torch.cuda.synchronize()
+    assert bool((buf[n:] == 0x5A).all()), "a call wrote past the workspace it was given"
+
+
+@pytest.mark.parametrize("chunk", [256, 160])
+def test_calls_stay_inside_the_workspace(B, chunk):
+    """Each FLCE-family call (FLCE, multi-head, distillation, DPO), given a
+    workspace of exactly its queried size, leaves the bytes after it alone and
+    still matches the oracle. Chunks of 256 rows hold the packed chunk's rows
+    and their transpose in the split-K partial buffer; chunks of 160 rows
+    (a transpose stride of 192) hold the rows only."""
+    import torch
+    N, H, V = 600, 136, 1000
+    inp = synth.make_flce_inputs(N, H, V, "bf16", bias_std=0.1, ignore_frac=0.1, seed=81)
+    X, W, b = (to_dev(inp[k], "bf16") for k in ("X", "W", "bias"))
+    y = to_dev(inp["targets"], "i32")
+    say("workspace bounds, chunk", chunk)
+    n = B.flce_workspace_bytes(N, H, V, B.BF16, chunk)
+    buf, ws = _guarded_workspace(n)
+    got = B.flce_forward_backward(X, W, y, bias=b, reduction="mean", chunk_rows=chunk,
+                                  grad_bias=True, workspace=ws)
+    _guard_intact(buf, n)
+    check_against_oracle(inp, "mean", tuple(None if t is None else to_host(t) for t in got))
+
+    K = 2
+    Wk = torch.stack([W, torch.roll(W, 3, dims=0)]).contiguous()
+    yk = torch.stack([y, torch.roll(y, -1)]).contiguous()
+    n = B.flce_multihead_workspace_bytes(N, H, V, K, B.BF16, chunk)
+    buf, ws = _guarded_workspace(n)
+    B.flce_multihead_forward_backward(X, Wk, yk, reduction="mean", chunk_rows=chunk, workspace=ws)
+    _guard_intact(buf, n)
+
+    n = B.flce_jsd_workspace_bytes(N, H, V, B.BF16, chunk)
+    buf, ws = _guarded_workspace(n)
+    B.flce_jsd_forward_backward(X, W, torch.roll(X, 1, dims=0).contiguous(), Wk[1], y,
+                                temperature=1.5, chunk_rows=chunk, workspace=ws)
+    _guard_intact(buf, n)
+
+    P, S = 2, N // 4
+    n = B.flce_dpo_workspace_bytes(P, S, H, V, B.BF16, chunk)
+    buf, ws = _guarded_workspace(n)
+    ref = torch.full((2 * P,), -float(S) * 7.0, device="cuda")
+    B.flce_dpo_forward_backward(X, W, y, P, S, ref, beta=0.2, chunk_rows=chunk, workspace=ws)
+    _guard_intact(buf, n)
