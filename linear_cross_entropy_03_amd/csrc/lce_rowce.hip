@@ -102,6 +102,53 @@ __device__ __forceinline__ void block_lse_parts(float m, float s, float* red0, f
   S = block_sum<kThreads>(mine, red1);
 }
 
+// The sum pass of the register-resident row kernels in base 2, one fma per
+// element: a lane with maximum m sums 2^(x log2e - m2), m2 = m log2e rounded
+// to float. Rounding is monotone, so the row's largest m2 is M log2e rounded
+// (M the row maximum), and 2^(x log2e - M2) = e^(x - M) 2^eps with
+// eps = M log2e - M2, which an fma gives exactly; the row's
+// lse = M + (log2 S - eps) ln 2 keeps M exact. No contraction here: m2 and
+// M2 must be the same rounded products the lanes used.
+__device__ __forceinline__ float lane_m2(float m) {
+#pragma clang fp contract(off)
+  return m * kLog2e;
+}
+template <int kThreads>
+__device__ __forceinline__ float block_lse2(float m, float s, float* red0, float* red1) {
+#pragma clang fp contract(off)
+  const float M = block_max<kThreads>(m, red0);
+  const float M2 = lane_m2(M);
+  const float mine = (m == -INFINITY) ? 0.0f : s * __builtin_amdgcn_exp2f(lane_m2(m) - M2);
+  const float S = block_sum<kThreads>(mine, red1);
+  const float eps = fmaf(M, kLog2e, -M2);
+  return M + (__builtin_amdgcn_logf(S) - eps) * kLn2;
+}
+
+// Gradient of one 16-byte vector of a row with a valid target:
+// c exp(x - lse) per element, and c (exp(x - lse) - 1) for the target when
+// it falls in this vector (rel = target - the vector's first column, in
+// [0, kVec)). Only the target's lane takes that branch, once per row, so
+// the other elements carry no per-element compare.
+template <typename T>
+__device__ __forceinline__ uint4 ce_grad_vec(const uint4& v, int64_t rel, float c, float lse) {
+  using E = Elem<T>;
+  constexpr int kVec = E::kVec;
+  float f[kVec], p[kVec];
+  E::unpack(v, f);
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    p[i] = __builtin_amdgcn_exp2f((f[i] - lse) * kLog2e);
+    f[i] = c * p[i];
+  }
+  if (static_cast<uint64_t>(rel) < static_cast<uint64_t>(kVec)) {
+    asm volatile("");  // a branch, not per-element selects
+#pragma unroll
+    for (int i = 0; i < kVec; ++i)
+      if (i == rel) f[i] = c * (p[i] - 1.0f);
+  }
+  return E::pack(f);
+}
+
 // Target count inside the row kernel, for calls of one launch over few rows:
 // every workgroup counts all n targets itself (n * 4 bytes from L2) and
 // workgroup 0 writes the header, which saves the separate count launch.
@@ -291,8 +338,10 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
     }
     if (tid < rs.head) lm = fmaxf(lm, E::load(z + tid));
     if (tid < V - rs.tail0) lm = fmaxf(lm, E::load(z + rs.tail0 + tid));
+    // Base-2 sum against the lane maximum (block_lse2).
     float ls = 0.0f;
     if (lm != -INFINITY) {
+      const float nm2 = -lane_m2(lm);
 #pragma unroll
       for (int j = 0; j < kRes; ++j) {
         const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
@@ -300,11 +349,11 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
           float f[kVec];
           E::unpack(buf[j], f);
 #pragma unroll
-          for (int i = 0; i < kVec; ++i) ls += __builtin_amdgcn_exp2f((f[i] - lm) * kLog2e);
+          for (int i = 0; i < kVec; ++i) ls += __builtin_amdgcn_exp2f(fmaf(f[i], kLog2e, nm2));
         }
       }
-      if (tid < rs.head) ls += __builtin_amdgcn_exp2f((E::load(z + tid) - lm) * kLog2e);
-      if (tid < V - rs.tail0) ls += __builtin_amdgcn_exp2f((E::load(z + rs.tail0 + tid) - lm) * kLog2e);
+      if (tid < rs.head) ls += __builtin_amdgcn_exp2f(fmaf(E::load(z + tid), kLog2e, nm2));
+      if (tid < V - rs.tail0) ls += __builtin_amdgcn_exp2f(fmaf(E::load(z + rs.tail0 + tid), kLog2e, nm2));
     }
     m = lm;
     s = ls;
@@ -320,9 +369,14 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   }
 
   // The reduction's barriers also publish the per-wave counts.
-  float M, S;
-  block_lse_parts<kThreads>(m, s, red0, red1, M, S);
-  const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
+  float lse;
+  if constexpr (kRes > 0) {
+    lse = block_lse2<kThreads>(m, s, red0, red1);
+  } else {
+    float M, S;
+    block_lse_parts<kThreads>(m, s, red0, red1, M, S);
+    lse = M + __builtin_amdgcn_logf(S) * kLn2;
+  }
   if (sc.n > 0) self_scale = count_finish<kThreads>(sc, cnt);
   if constexpr (kRes > 0) zt = E::load(&zt_bits);
   // Loss and per-row factor belong to the original row (packed chunks).
@@ -360,27 +414,29 @@ __device__ __forceinline__ void row_ce_grad(const T* Z, int64_t ldz, T* G, int64
     const float p = __builtin_amdgcn_exp2f((x - lse) * kLog2e);
     return c * (v == y ? p - 1.0f : p);
   };
-  if constexpr (kRes > 0) {
+  // The target's position relative to vector vi's first column.
+  const int64_t rel0 = static_cast<int64_t>(y) - rs.head;
+  if (!valid) {
+    // The whole row (uniform branch): zeros.
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (kRes > 0) {
+#pragma unroll
+      for (int j = 0; j < kRes; ++j) {
+        const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
+        if (vi < rs.nvec) store_grad_vec(gv + vi, zero, nt);
+      }
+    } else {
+      for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) store_grad_vec(gv + vi, zero, nt);
+    }
+  } else if constexpr (kRes > 0) {
 #pragma unroll
     for (int j = 0; j < kRes; ++j) {
       const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
-      if (vi < rs.nvec) {
-        float f[kVec];
-        E::unpack(buf[j], f);
-        const int64_t v0 = rs.head + vi * kVec;
-#pragma unroll
-        for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
-        store_grad_vec(gv + vi, E::pack(f), nt);
-      }
+      if (vi < rs.nvec) store_grad_vec(gv + vi, ce_grad_vec<T>(buf[j], rel0 - vi * kVec, c, lse), nt);
     }
   } else {
     stream_row<kThreads>(zv, rs.nvec, [&](int64_t vi, const uint4& v) {
-      float f[kVec];
-      E::unpack(v, f);
-      const int64_t v0 = rs.head + vi * kVec;
-#pragma unroll
-      for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
-      store_grad_vec(gv + vi, E::pack(f), nt);
+      store_grad_vec(gv + vi, ce_grad_vec<T>(v, rel0 - vi * kVec, c, lse), nt);
     });
   }
   if (tid < rs.head) E::store(g + tid, grad_of(E::load(z + tid), tid));
@@ -482,23 +538,23 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
     }
     if (tid < head) lm = fmaxf(lm, E::load(z + tid));
     if (tid < Vi - tail0) lm = fmaxf(lm, E::load(z + tail0 + tid));
+    // Base-2 sum against the lane maximum (block_lse2).
     float ls = 0.0f;
     if (lm != -INFINITY) {
+      const float nm2 = -lane_m2(lm);
 #pragma unroll
       for (int j = 0; j < kRes; ++j) {
         if (j * kThreads + tid < nvec) {
           float f[kVec];
           E::unpack(buf[j], f);
 #pragma unroll
-          for (int i = 0; i < kVec; ++i) ls += __builtin_amdgcn_exp2f((f[i] - lm) * kLog2e);
+          for (int i = 0; i < kVec; ++i) ls += __builtin_amdgcn_exp2f(fmaf(f[i], kLog2e, nm2));
         }
       }
-      if (tid < head) ls += __builtin_amdgcn_exp2f((E::load(z + tid) - lm) * kLog2e);
-      if (tid < Vi - tail0) ls += __builtin_amdgcn_exp2f((E::load(z + tail0 + tid) - lm) * kLog2e);
+      if (tid < head) ls += __builtin_amdgcn_exp2f(fmaf(E::load(z + tid), kLog2e, nm2));
+      if (tid < Vi - tail0) ls += __builtin_amdgcn_exp2f(fmaf(E::load(z + tail0 + tid), kLog2e, nm2));
     }
-    float M, S;
-    block_lse_parts<kThreads>(lm, ls, red0, red1, M, S);
-    const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
+    const float lse = block_lse2<kThreads>(lm, ls, red0, red1);
     const int64_t orow = pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row;
     if (tid == 0) loss_rows[orow] = valid ? (lse - zt) : 0.0f;
 
@@ -510,19 +566,23 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
       T* g = G + row * ldg;
       uint4* gv = reinterpret_cast<uint4*>(g + head);
       auto grad_of = [&](float x, int v) -> float {
+        if (!valid) return 0.0f;
         const float p = __builtin_amdgcn_exp2f((x - lse) * kLog2e);
         return c * (v == yt ? p - 1.0f : p);
       };
+      if (!valid) {
+        // The whole row (uniform branch): zeros.
 #pragma unroll
-      for (int j = 0; j < kRes; ++j) {
-        const int vi = j * kThreads + tid;
-        if (vi < nvec) {
-          float f[kVec];
-          E::unpack(buf[j], f);
-          const int v0 = head + vi * kVec;
+        for (int j = 0; j < kRes; ++j) {
+          const int vi = j * kThreads + tid;
+          if (vi < nvec) gv[vi] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      } else {
+        const int rel0 = y - head;
 #pragma unroll
-          for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], v0 + i);
-          gv[vi] = E::pack(f);
+        for (int j = 0; j < kRes; ++j) {
+          const int vi = j * kThreads + tid;
+          if (vi < nvec) gv[vi] = ce_grad_vec<T>(buf[j], rel0 - vi * kVec, c, lse);
         }
       }
       if (tid < head) E::store(g + tid, grad_of(E::load(z + tid), tid));
@@ -851,14 +911,15 @@ __global__ __launch_bounds__(kThreads) void k_shard_grad(T* Z, int64_t ldz, int6
   };
   const RowSplit rs = split_row(z, Vl);
   uint4* zv = reinterpret_cast<uint4*>(z + rs.head);
-  stream_row<kThreads>(zv, rs.nvec, [&](int64_t vi, const uint4& v) {
-    float f[kVec];
-    E::unpack(v, f);
-    const int64_t j0 = rs.head + vi * kVec;
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) f[i] = grad_of(f[i], j0 + i);
-    zv[vi] = E::pack(f);
-  });
+  if (!valid) {
+    // The whole row (uniform branch): zeros.
+    for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) zv[vi] = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    const int64_t rel0 = jt - rs.head;  // outside every vector when the target is not here
+    stream_row<kThreads>(zv, rs.nvec, [&](int64_t vi, const uint4& v) {
+      zv[vi] = ce_grad_vec<T>(v, rel0 - vi * kVec, c, L);
+    });
+  }
   if (tid < rs.head) E::store(z + tid, grad_of(E::load(z + tid), tid));
   if (tid < Vl - rs.tail0) {
     const int64_t j = rs.tail0 + tid;
