@@ -113,6 +113,10 @@ __device__ __forceinline__ float lane_m2(float m) {
 #pragma clang fp contract(off)
   return m * kLog2e;
 }
+__device__ __forceinline__ float lane_m2_by(float m, float k) {
+#pragma clang fp contract(off)
+  return m * k;
+}
 template <int kThreads>
 __device__ __forceinline__ float block_lse2(float m, float s, float* red0, float* red1) {
 #pragma clang fp contract(off)
@@ -1015,52 +1019,74 @@ __global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t
   const uint4* sv = reinterpret_cast<const uint4*>(s + rs.head);
   const uint4* tv = reinterpret_cast<const uint4*>(t + rs.head);
 
-  // Pass 1: online (max, sum exp) of both tempered rows.
+  // Everything in base 2: u = x k with k = log2(e) / tau for a raw logit x,
+  // so 2^u = e^(x / tau).
+  const float k2 = lane_m2(inv_tau);
+
+  // Pass 1: per-lane online (max, sum of 2^(u - max)) of both rows; a lane's
+  // max is the rounded product of its largest raw logit, the shift its fmas
+  // subtract.
   float ms = -INFINITY, ss = 0.0f, mt = -INFINITY, st = 0.0f;
+  auto push = [&](float& m, float& sum, const float* x, int n) {
+    float vm = x[0];
+    for (int i = 1; i < n; ++i) vm = fmaxf(vm, x[i]);
+    const float mn = fmaxf(m, lane_m2_by(vm, k2));
+    float acc = m == -INFINITY ? 0.0f : sum * __builtin_amdgcn_exp2f(m - mn);
+    for (int i = 0; i < n; ++i) acc += __builtin_amdgcn_exp2f(fmaf(x[i], k2, -mn));
+    sum = acc;
+    m = mn;
+  };
   for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
     float a[kVec], b[kVec];
     E::unpack(sv[vi], a);
     E::unpack(tv[vi], b);
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) { a[i] *= inv_tau; b[i] *= inv_tau; }
-    online_push_vec<kVec>(ms, ss, a);
-    online_push_vec<kVec>(mt, st, b);
+    push(ms, ss, a, kVec);
+    push(mt, st, b, kVec);
   }
   auto scalar_at = [&](int64_t v, float& a, float& b) {
-    a = E::load(s + v) * inv_tau;
-    b = E::load(t + v) * inv_tau;
+    a = E::load(s + v);
+    b = E::load(t + v);
   };
-  if (tid < rs.head) { float a, b; scalar_at(tid, a, b); online_push(ms, ss, a); online_push(mt, st, b); }
+  if (tid < rs.head) { float a, b; scalar_at(tid, a, b); push(ms, ss, &a, 1); push(mt, st, &b, 1); }
   if (tid < V - rs.tail0) {
     float a, b;
     scalar_at(rs.tail0 + tid, a, b);
-    online_push(ms, ss, a);
-    online_push(mt, st, b);
+    push(ms, ss, &a, 1);
+    push(mt, st, &b, 1);
   }
-  float Ms, Ss, Mt, St;
-  block_lse_parts<kThreads>(ms, ss, red0, red1, Ms, Ss);
-  __syncthreads();
-  block_lse_parts<kThreads>(mt, st, red0, red1, Mt, St);
-  const float lse_s = Ms + __builtin_amdgcn_logf(Ss) * kLn2;
-  const float lse_t = Mt + __builtin_amdgcn_logf(St) * kLn2;
-
-  // Per element: the log-probabilities, ln M (log-sum-exp of two, so it
-  // cannot underflow), the loss terms and sum(e^ls g).
-  auto terms = [&](float a, float b, float& lp, float& lm) {
-    lp = a - lse_s;
-    const float lq = b - lse_t;
-    const float mx = fmaxf(lp, lq);
-    lm = mx + __builtin_amdgcn_logf(0.5f * (__builtin_amdgcn_exp2f((lp - mx) * kLog2e) +
-                                            __builtin_amdgcn_exp2f((lq - mx) * kLog2e))) * kLn2;
-    return lq;
+  // Row log-sum-exps of u (base 2).
+  auto lse2_of = [&](float m, float sum) {
+    const float M = block_max<kThreads>(m, red0);
+    const float mine = m == -INFINITY ? 0.0f : sum * __builtin_amdgcn_exp2f(m - M);
+    return M + __builtin_amdgcn_logf(block_sum<kThreads>(mine, red1));
   };
+  const float ls2 = lse2_of(ms, ss);
+  __syncthreads();
+  const float lt2 = lse2_of(mt, st);
+
+  // Per element, in base 2: P = log2 p, Q = log2 q (the tempered log-softmax
+  // of each row over ln 2), LM = log2((p + q) / 2) = max(P, Q) +
+  // log2((1 + 2^-|P - Q|) / 2), which cannot underflow; p and q come from
+  // 2^max(P, Q) and 2^-|P - Q|: two exponentials and one logarithm per
+  // element. Returns dP = P - LM (and dQ, p, q); ln p - ln m = dP ln 2.
+  struct Terms { float p, q, dp, dq; };
+  auto terms = [&](float a, float b) -> Terms {
+    const float P = fmaf(a, k2, -ls2), Q = fmaf(b, k2, -lt2);
+    const float hi = fmaxf(P, Q);
+    const float e = __builtin_amdgcn_exp2f(fminf(P, Q) - hi);
+    const float x = __builtin_amdgcn_exp2f(hi);
+    const float lm = hi + __builtin_amdgcn_logf(fmaf(0.5f, e, 0.5f));
+    const bool pq = P >= Q;
+    return {pq ? x : x * e, pq ? x * e : x, P - lm, Q - lm};
+  };
+  // loss = 1/2 sum(p (ln p - ln m) + q (ln q - ln m)), sum(p g) with
+  // g = 1/2 (ln p - ln m): both summed here without their 1/2 ln 2.
   float loss = 0.0f, gbar = 0.0f;
   auto accumulate = [&](float a, float b) {
-    float lp, lm;
-    const float lq = terms(a, b, lp, lm);
-    const float p = __builtin_amdgcn_exp2f(lp * kLog2e), q = __builtin_amdgcn_exp2f(lq * kLog2e);
-    loss += 0.5f * (p * (lp - lm) + q * (lq - lm));
-    gbar += p * 0.5f * (lp - lm);
+    const Terms r = terms(a, b);
+    const float pd = r.p * r.dp;
+    loss += pd + r.q * r.dq;
+    gbar += pd;
   };
   // Pass 2.
   for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
@@ -1068,42 +1094,49 @@ __global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t
     E::unpack(sv[vi], a);
     E::unpack(tv[vi], b);
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) accumulate(a[i] * inv_tau, b[i] * inv_tau);
+    for (int i = 0; i < kVec; ++i) accumulate(a[i], b[i]);
   }
   if (tid < rs.head) { float a, b; scalar_at(tid, a, b); accumulate(a, b); }
   if (tid < V - rs.tail0) { float a, b; scalar_at(rs.tail0 + tid, a, b); accumulate(a, b); }
   __syncthreads();
-  const float L = block_sum<kThreads>(loss, red0);
-  const float Gb = block_sum<kThreads>(gbar, red1);
+  const float half_ln2 = 0.5f * kLn2;
+  const float L = half_ln2 * block_sum<kThreads>(loss, red0);
+  const float G2 = block_sum<kThreads>(gbar, red1);
   if (tid == 0) loss_rows[pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row] = valid ? L : 0.0f;
 
-  // Pass 3: the student gradient, in place.
-  const float c = !valid ? 0.0f
-                  : (grad_shift > 0 ? __builtin_ldexpf(1.0f, grad_shift) : hdr->scale) * inv_tau;
-  auto grad = [&](float a, float b) -> float {
-    float lp, lm;
-    terms(a, b, lp, lm);
-    return c * __builtin_amdgcn_exp2f(lp * kLog2e) * (0.5f * (lp - lm) - Gb);
-  };
+  // Pass 3: the student gradient, in place: c p (g - sum(p g)) with c the
+  // reduction scale over tau, = c ln2 / 2 p (dP - G2).
   uint4* svw = reinterpret_cast<uint4*>(s + rs.head);
-  for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
-    float a[kVec], b[kVec];
-    E::unpack(sv[vi], a);
-    E::unpack(tv[vi], b);
+  if (!valid) {
+    // The whole row (uniform branch): zeros.
+    for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) svw[vi] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid < rs.head) E::store(s + tid, 0.0f);
+    if (tid < V - rs.tail0) E::store(s + rs.tail0 + tid, 0.0f);
+  } else {
+    const float c = (grad_shift > 0 ? __builtin_ldexpf(1.0f, grad_shift) : hdr->scale) * inv_tau * half_ln2;
+    auto grad = [&](float a, float b) -> float {
+      const Terms r = terms(a, b);
+      return c * r.p * (r.dp - G2);
+    };
+    for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+      float a[kVec], b[kVec];
+      E::unpack(sv[vi], a);
+      E::unpack(tv[vi], b);
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) a[i] = valid ? grad(a[i] * inv_tau, b[i] * inv_tau) : 0.0f;
-    svw[vi] = E::pack(a);
-  }
-  // Scalar head and tail: each lane owns one element, read before it writes.
-  if (tid < rs.head) {
-    float a, b;
-    scalar_at(tid, a, b);
-    E::store(s + tid, valid ? grad(a, b) : 0.0f);
-  }
-  if (tid < V - rs.tail0) {
-    float a, b;
-    scalar_at(rs.tail0 + tid, a, b);
-    E::store(s + rs.tail0 + tid, valid ? grad(a, b) : 0.0f);
+      for (int i = 0; i < kVec; ++i) a[i] = grad(a[i], b[i]);
+      svw[vi] = E::pack(a);
+    }
+    // Scalar head and tail: each lane owns one element, read before it writes.
+    if (tid < rs.head) {
+      float a, b;
+      scalar_at(tid, a, b);
+      E::store(s + tid, grad(a, b));
+    }
+    if (tid < V - rs.tail0) {
+      float a, b;
+      scalar_at(rs.tail0 + tid, a, b);
+      E::store(s + rs.tail0 + tid, grad(a, b));
+    }
   }
   if (tid < pad_cols) E::store(s + V + tid, 0.0f);
 }
