@@ -129,26 +129,24 @@ __device__ __forceinline__ float block_lse2(float m, float s, float* red0, float
 }
 
 // Gradient of one 16-byte vector of a row with a valid target:
-// c exp(x - lse) per element, and c (exp(x - lse) - 1) for the target when
-// it falls in this vector (rel = target - the vector's first column, in
-// [0, kVec)). Only the target's lane takes that branch, once per row, so
-// the other elements carry no per-element compare.
+// c exp(x - lse) per element, and gt = c (exp(x_t - lse) - 1), computed once
+// per row from the target logit x_t, for the target when it falls in this
+// vector (rel = target - the vector's first column, in [0, kVec); |rel| <
+// 2^30 since V < 2^30). Only the target's lane takes that branch, once per
+// row, so the other elements carry no per-element compare.
 template <typename T>
-__device__ __forceinline__ uint4 ce_grad_vec(const uint4& v, int64_t rel, float c, float lse) {
+__device__ __forceinline__ uint4 ce_grad_vec(const uint4& v, int rel, float c, float lse, float gt) {
   using E = Elem<T>;
   constexpr int kVec = E::kVec;
-  float f[kVec], p[kVec];
+  float f[kVec];
   E::unpack(v, f);
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) {
-    p[i] = __builtin_amdgcn_exp2f((f[i] - lse) * kLog2e);
-    f[i] = c * p[i];
-  }
-  if (static_cast<uint64_t>(rel) < static_cast<uint64_t>(kVec)) {
+  for (int i = 0; i < kVec; ++i) f[i] = c * __builtin_amdgcn_exp2f((f[i] - lse) * kLog2e);
+  if (static_cast<unsigned>(rel) < static_cast<unsigned>(kVec)) {
     asm volatile("");  // a branch, not per-element selects
 #pragma unroll
     for (int i = 0; i < kVec; ++i)
-      if (i == rel) f[i] = c * (p[i] - 1.0f);
+      if (i == rel) f[i] = gt;
   }
   return E::pack(f);
 }
@@ -274,7 +272,7 @@ __device__ __forceinline__ void store_grad_vec(uint4* p, const uint4& v, int nt)
 template <typename T, int kThreads, int kRes>
 __device__ __forceinline__ void row_ce_grad(const T* Z, int64_t ldz, T* G, int64_t ldg, int64_t V,
                                             int64_t pad_cols, int64_t row, int32_t y, bool valid,
-                                            float lse, const RowSplit& rs, const uint4* buf,
+                                            float lse, float zt, const RowSplit& rs, const uint4* buf,
                                             const float* __restrict__ row_scale, int64_t orow,
                                             int grad_shift, float red_scale, int nt);
 
@@ -303,13 +301,14 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   const RowSplit rs = split_row(z, V);
   const uint4* zv = reinterpret_cast<const uint4*>(z + rs.head);
 
-  // The target logit is read before any lane can overwrite the row: the
-  // block reductions below end in __syncthreads, which waits for every load
-  // of the wave, and all writes come after them. In the register-resident
-  // path it is loaded after the row so the row's loads go out first.
+  // The target logit (every lane: the gradient needs it) is read before any
+  // lane can overwrite the row: the block reductions below end in
+  // __syncthreads, which waits for every load of the wave, and all writes
+  // come after them. In the register-resident path it is loaded after the
+  // row so the row's loads go out first.
   float zt = 0.0f;
   T zt_bits{};
-  if (kRes == 0 && tid == 0 && valid) zt = E::load(z + y);
+  if (kRes == 0 && valid) zt = E::load(z + y);
 
   float m = -INFINITY, s = 0.0f, self_scale = 0.0f;
   const int32_t t_first = (sc.n > 0 && tid < sc.n) ? targets[tid] : ign;
@@ -387,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
   const int64_t orow = pk.map != nullptr ? static_cast<int64_t>(pk.map[row]) : row;
   if (tid == 0) loss_rows[orow] = valid ? (lse - zt) : 0.0f;
   if (G != nullptr) row_ce_grad<T, kThreads, kRes>(Z, ldz, G, ldg, V, pad_cols, row, y, valid,
-                                                  lse, rs, buf, row_scale, orow, grad_shift,
+                                                  lse, zt, rs, buf, row_scale, orow, grad_shift,
                                                   sc.n > 0 ? self_scale : hdr->scale, sc.nt_grad);
 }
 
@@ -396,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void k_row_ce(const T* Z, int64_t ldz, T*
 template <typename T, int kThreads, int kRes>
 __device__ __forceinline__ void row_ce_grad(const T* Z, int64_t ldz, T* G, int64_t ldg, int64_t V,
                                             int64_t pad_cols, int64_t row, int32_t y, bool valid,
-                                            float lse, const RowSplit& rs, const uint4* buf,
+                                            float lse, float zt, const RowSplit& rs, const uint4* buf,
                                             const float* __restrict__ row_scale, int64_t orow,
                                             int grad_shift, float red_scale, int nt) {
   using E = Elem<T>;
@@ -418,29 +417,26 @@ __device__ __forceinline__ void row_ce_grad(const T* Z, int64_t ldz, T* G, int64
     const float p = __builtin_amdgcn_exp2f((x - lse) * kLog2e);
     return c * (v == y ? p - 1.0f : p);
   };
-  // The target's position relative to vector vi's first column.
-  const int64_t rel0 = static_cast<int64_t>(y) - rs.head;
+  // The target's position relative to vector vi's first column, and its
+  // gradient (valid rows only, where 0 <= y < V).
+  const int rel0 = valid ? y - static_cast<int>(rs.head) : 0;
+  const float gt = c * (__builtin_amdgcn_exp2f((zt - lse) * kLog2e) - 1.0f);
   if (!valid) {
-    // The whole row (uniform branch): zeros.
+    // The whole row (uniform branch): zeros. A plain strided loop, so that
+    // no per-vector index of the register-resident loop below is kept live
+    // for this rare case.
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (kRes > 0) {
-#pragma unroll
-      for (int j = 0; j < kRes; ++j) {
-        const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
-        if (vi < rs.nvec) store_grad_vec(gv + vi, zero, nt);
-      }
-    } else {
-      for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) store_grad_vec(gv + vi, zero, nt);
-    }
+    for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) store_grad_vec(gv + vi, zero, nt);
   } else if constexpr (kRes > 0) {
 #pragma unroll
     for (int j = 0; j < kRes; ++j) {
       const int64_t vi = static_cast<int64_t>(j) * kThreads + tid;
-      if (vi < rs.nvec) store_grad_vec(gv + vi, ce_grad_vec<T>(buf[j], rel0 - vi * kVec, c, lse), nt);
+      if (vi < rs.nvec)
+        store_grad_vec(gv + vi, ce_grad_vec<T>(buf[j], rel0 - static_cast<int>(vi) * kVec, c, lse, gt), nt);
     }
   } else {
     stream_row<kThreads>(zv, rs.nvec, [&](int64_t vi, const uint4& v) {
-      store_grad_vec(gv + vi, ce_grad_vec<T>(v, rel0 - vi * kVec, c, lse), nt);
+      store_grad_vec(gv + vi, ce_grad_vec<T>(v, static_cast<int>(rel0 - vi * kVec), c, lse, gt), nt);
     });
   }
   if (tid < rs.head) E::store(g + tid, grad_of(E::load(z + tid), tid));
@@ -514,7 +510,7 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
     const int nvec = static_cast<int>(rs.nvec), head = static_cast<int>(rs.head);
     const int tail0 = static_cast<int>(rs.tail0), Vi = static_cast<int>(V);
     float zt = 0.0f;
-    if (tid == 0 && valid) zt = E::load(z + y);  // before any lane overwrites the row
+    if (valid) zt = E::load(z + y);  // every lane, before any lane overwrites the row
 
     uint4 buf[kRes];
     {
@@ -576,17 +572,14 @@ __global__ __launch_bounds__(pf::kThreads) void k_row_ce_pf(const T* Z, int64_t 
       };
       if (!valid) {
         // The whole row (uniform branch): zeros.
-#pragma unroll
-        for (int j = 0; j < kRes; ++j) {
-          const int vi = j * kThreads + tid;
-          if (vi < nvec) gv[vi] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int vi = tid; vi < nvec; vi += kThreads) gv[vi] = make_uint4(0u, 0u, 0u, 0u);
       } else {
         const int rel0 = y - head;
+        const float gt = c * (__builtin_amdgcn_exp2f((zt - lse) * kLog2e) - 1.0f);
 #pragma unroll
         for (int j = 0; j < kRes; ++j) {
           const int vi = j * kThreads + tid;
-          if (vi < nvec) gv[vi] = ce_grad_vec<T>(buf[j], rel0 - vi * kVec, c, lse);
+          if (vi < nvec) gv[vi] = ce_grad_vec<T>(buf[j], rel0 - vi * kVec, c, lse, gt);
         }
       }
       if (tid < head) E::store(g + tid, grad_of(E::load(z + tid), tid));
@@ -919,9 +912,18 @@ __global__ __launch_bounds__(kThreads) void k_shard_grad(T* Z, int64_t ldz, int6
     // The whole row (uniform branch): zeros.
     for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) zv[vi] = make_uint4(0u, 0u, 0u, 0u);
   } else {
-    const int64_t rel0 = jt - rs.head;  // outside every vector when the target is not here
+    // The target's gradient, from its logit when the target is in this shard:
+    // every lane reads it, and the barrier keeps those reads ahead of the
+    // lanes' writes (a workgroup's memory operations issue in order on its
+    // CU). rel0 falls outside every vector when the target is not here
+    // (|jt| < 2^30).
+    const bool here = jt >= 0 && jt < Vl;
+    const float zt = here ? E::load(z + jt) : 0.0f;
+    __syncthreads();
+    const float gt = c * (__builtin_amdgcn_exp2f((zt - L) * kLog2e) - 1.0f);
+    const int64_t rel0 = jt - rs.head;
     stream_row<kThreads>(zv, rs.nvec, [&](int64_t vi, const uint4& v) {
-      zv[vi] = ce_grad_vec<T>(v, rel0 - vi * kVec, c, L);
+      zv[vi] = ce_grad_vec<T>(v, static_cast<int>(rel0 - vi * kVec), c, L, gt);
     });
   }
   if (tid < rs.head) E::store(z + tid, grad_of(E::load(z + tid), tid));
