@@ -292,3 +292,59 @@ def test_dpo_argument_errors(B):
     assert dpo(ref=None) == B.E_INVALID_ARG
     assert dpo(pl=24) == B.E_UNSUPPORTED
     assert dpo(wsb=B.flce_workspace_bytes(12, 8, 10)) == B.E_WORKSPACE
+
+
+def _device_code_objects(lib_path, tmp_path):
+    """The gfx950 code objects inside the library's offload bundles (one per
+    compiled HIP source), from its .hip_fatbin section."""
+    import shutil
+    import struct
+    import subprocess
+    objcopy = shutil.which("llvm-objcopy", path="/opt/rocm/llvm/bin")
+    if objcopy is None:
+        pytest.skip("llvm-objcopy not available")
+    fat = tmp_path / "fatbin.bin"
+    subprocess.run([objcopy, f"--dump-section=.hip_fatbin={fat}", lib_path, str(tmp_path / "lib.tmp")],
+                   check=True, capture_output=True)
+    data = fat.read_bytes()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    out, pos = [], 0
+    while (i := data.find(magic, pos)) >= 0:
+        (n,) = struct.unpack_from("<Q", data, i + len(magic))
+        off = i + len(magic) + 8
+        for _ in range(n):
+            e_off, e_size, t_size = struct.unpack_from("<QQQ", data, off)
+            off += 24
+            triple = data[off:off + t_size].decode()
+            off += t_size
+            if triple.endswith("gfx950"):
+                out.append(data[i + e_off:i + e_off + e_size])
+        pos = i + 1
+    return out
+
+
+def test_no_kernel_uses_scratch(tmp_path):
+    """Every kernel of the library keeps its state in registers and LDS: a
+    private segment would mean register spills to scratch memory, which the
+    row kernels would run through on every element (the ring GEMM's launcher
+    refuses such a build at run time as well). Reads the AMDGPU kernel
+    metadata of the library's own device code."""
+    import shutil
+    import subprocess
+    readelf = shutil.which("llvm-readelf", path="/opt/rocm/llvm/bin")
+    if readelf is None:
+        pytest.skip("llvm-readelf not available")
+    kernels, spilled = 0, []
+    for k, co in enumerate(_device_code_objects(LIB_PATH, tmp_path)):
+        path = tmp_path / f"co{k}.o"
+        path.write_bytes(co)
+        notes = subprocess.run([readelf, "--notes", str(path)], check=True, capture_output=True,
+                               text=True).stdout
+        priv = [int(l.split(":", 1)[1]) for l in notes.splitlines()
+                if l.strip().startswith(".private_segment_fixed_size:")]
+        syms = [l.split(":", 1)[1].strip() for l in notes.splitlines() if l.strip().startswith(".symbol:")]
+        assert len(priv) == len(syms)
+        kernels += len(syms)
+        spilled += [s for s, p in zip(syms, priv) if p != 0]
+    assert kernels >= 100, kernels
+    assert not spilled, spilled
