@@ -186,15 +186,21 @@ __device__ __forceinline__ bool stream_batched(int64_t nvec, int threads) {
 // f(vi, v) for every 16-byte vector vi < nvec of one row (zv), lane-strided
 // (vector j kThreads + tid of each batch goes to lane tid): kStream
 // range-checked loads per lane in flight before any is used. f may write
-// vector vi in place (it was loaded by the same lane).
-template <int kThreads, typename F>
+// vector vi in place (it was loaded by the same lane). kRev walks the
+// batches from the row's end: a pass right after a forward pass over the
+// same row then starts on the bytes fetched last, the likeliest to be still
+// in the L2 and the last-level cache.
+template <int kThreads, bool kRev = false, typename F>
 __device__ __forceinline__ void stream_row(const uint4* zv, int64_t nvec, F&& f) {
   const int tid = threadIdx.x;
   const int64_t nbatch = stream_batched(nvec, kThreads) ? nvec : 0;
   for (int64_t vi = nbatch + tid; vi < nvec; vi += kThreads) f(vi, zv[vi]);
   if (nbatch == 0) return;
   const __amdgpu_buffer_rsrc_t rv = row_rsrc(zv, nvec * 16);
-  for (int64_t b0 = 0; b0 < nbatch; b0 += kStream * kThreads) {
+  constexpr int64_t kBatch = static_cast<int64_t>(kStream) * kThreads;
+  const int64_t last = (nbatch - 1) / kBatch * kBatch;
+  for (int64_t i = 0; i <= last; i += kBatch) {
+    const int64_t b0 = kRev ? last - i : i;
     uint4 sb[kStream];
 #pragma unroll
     for (int j = 0; j < kStream; ++j)
@@ -435,7 +441,7 @@ __device__ __forceinline__ void row_ce_grad(const T* Z, int64_t ldz, T* G, int64
         store_grad_vec(gv + vi, ce_grad_vec<T>(buf[j], rel0 - static_cast<int>(vi) * kVec, c, lse, gt), nt);
     }
   } else {
-    stream_row<kThreads>(zv, rs.nvec, [&](int64_t vi, const uint4& v) {
+    stream_row<kThreads, true>(zv, rs.nvec, [&](int64_t vi, const uint4& v) {
       store_grad_vec(gv + vi, ce_grad_vec<T>(v, static_cast<int>(rel0 - vi * kVec), c, lse, gt), nt);
     });
   }
@@ -1090,8 +1096,11 @@ __global__ __launch_bounds__(kThreads) void k_row_jsd(T* S, const T* Tt, int64_t
     loss += pd + r.q * r.dq;
     gbar += pd;
   };
-  // Pass 2.
-  for (int64_t vi = tid; vi < rs.nvec; vi += kThreads) {
+  // Pass 2, from the row's end: it starts on the bytes pass 1 fetched last
+  // (the likeliest to be still cached), and pass 3 then starts on the bytes
+  // this pass fetched last.
+  for (int64_t vi = rs.nvec > tid ? tid + (rs.nvec - 1 - tid) / kThreads * kThreads : -1; vi >= 0;
+       vi -= kThreads) {
     float a[kVec], b[kVec];
     E::unpack(sv[vi], a);
     E::unpack(tv[vi], b);
