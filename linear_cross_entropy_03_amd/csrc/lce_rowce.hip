@@ -685,11 +685,121 @@ hipError_t launch_row_ce(int dtype, const void* Z, int64_t ldz, void* G, int64_t
                       row_scale, grad_shift, SelfCount{0, 0, nullptr, 0}, pk, s);
 }
 
+// Standalone calls (one launch, the targets counted here): two register-
+// resident rows per workgroup. Both rows' loads go out before either is
+// used, so the first row's reductions and gradient stores run while the
+// second row is still arriving. The targets the count needs are loaded
+// before the rows (loads complete in order: a target load issued after the
+// rows would wait for both).
+template <typename T, int kThreads, int kRes>
+__global__ __launch_bounds__(kThreads) void k_row_ce_pair(const T* Z, T* G, int64_t rows, int64_t V,
+                                                          const int32_t* __restrict__ targets,
+                                                          int32_t ign, float* __restrict__ loss_rows,
+                                                          SelfCount sc) {
+  using E = Elem<T>;
+  constexpr int kVec = E::kVec;
+  constexpr int kCnt = 4;  // targets per lane for the count: 4 x 512 = the self-count limit
+  __shared__ float red0[kThreads / 64], red1[kThreads / 64];
+  __shared__ float cnt[2][kThreads / 64];
+  const int tid = threadIdx.x;
+  int32_t tc[kCnt];
+#pragma unroll
+  for (int k = 0; k < kCnt; ++k) tc[k] = tid + k * kThreads < sc.n ? targets[tid + k * kThreads] : ign;
+  const int64_t r0 = 2 * static_cast<int64_t>(blockIdx.x);
+  const bool two = r0 + 1 < rows;
+  const int32_t y0 = targets[r0], y1 = two ? targets[r0 + 1] : ign;
+  const bool v0 = y0 != ign && y0 >= 0 && static_cast<int64_t>(y0) < V;
+  const bool v1 = two && y1 != ign && y1 >= 0 && static_cast<int64_t>(y1) < V;
+  const T* z0 = Z + r0 * V;
+  const T* z1 = z0 + V;
+  const RowSplit rs0 = split_row(z0, V), rs1 = split_row(z1, V);
+  uint4 b0[kRes], b1[kRes];
+  T t0{}, t1{};
+  {
+    const __amdgpu_buffer_rsrc_t a = row_rsrc(z0 + rs0.head, rs0.nvec * 16);
+#pragma unroll
+    for (int j = 0; j < kRes; ++j)
+      b0[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a, (j * kThreads + tid) * 16, 0, 0));
+    t0 = load_elem_bits<T>(row_rsrc(z0, V * static_cast<int64_t>(sizeof(T))),
+                           v0 ? static_cast<int>(y0 * sizeof(T)) : 0x7FFFFFF0);
+    const __amdgpu_buffer_rsrc_t b = row_rsrc(z1 + rs1.head, two ? rs1.nvec * 16 : 0);
+#pragma unroll
+    for (int j = 0; j < kRes; ++j)
+      b1[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b, (j * kThreads + tid) * 16, 0, 0));
+    t1 = load_elem_bits<T>(row_rsrc(z1, two ? V * static_cast<int64_t>(sizeof(T)) : 0),
+                           v1 ? static_cast<int>(y1 * sizeof(T)) : 0x7FFFFFF0);
+  }
+  {
+    int valid = 0, bad = 0;
+#pragma unroll
+    for (int k = 0; k < kCnt; ++k) {
+      const int32_t y = tc[k];
+      if (y != ign) {
+        if (y >= 0 && static_cast<int64_t>(y) < V) ++valid; else ++bad;
+      }
+    }
+    const float fv = wave_sum(static_cast<float>(valid)), fb = wave_sum(static_cast<float>(bad));
+    if ((tid & 63) == 0) {
+      cnt[0][tid >> 6] = fv;
+      cnt[1][tid >> 6] = fb;
+    }
+  }
+  float scale = 0.0f;
+  auto row = [&](const T* z, int64_t r, int32_t y, bool valid, const RowSplit& rs,
+                 const uint4 (&buf)[kRes], T tb, bool first) {
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRes; ++j) {
+      if (static_cast<int64_t>(j) * kThreads + tid < rs.nvec) {
+        float f[kVec];
+        E::unpack(buf[j], f);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) lm = fmaxf(lm, f[i]);
+      }
+    }
+    if (tid < rs.head) lm = fmaxf(lm, E::load(z + tid));
+    if (tid < V - rs.tail0) lm = fmaxf(lm, E::load(z + rs.tail0 + tid));
+    float ls = 0.0f;
+    if (lm != -INFINITY) {
+      const float nm2 = -lane_m2(lm);
+#pragma unroll
+      for (int j = 0; j < kRes; ++j) {
+        if (static_cast<int64_t>(j) * kThreads + tid < rs.nvec) {
+          float f[kVec];
+          E::unpack(buf[j], f);
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) ls += __builtin_amdgcn_exp2f(fmaf(f[i], kLog2e, nm2));
+        }
+      }
+      if (tid < rs.head) ls += __builtin_amdgcn_exp2f(fmaf(E::load(z + tid), kLog2e, nm2));
+      if (tid < V - rs.tail0) ls += __builtin_amdgcn_exp2f(fmaf(E::load(z + rs.tail0 + tid), kLog2e, nm2));
+    }
+    // The first row's barriers also publish the per-wave counts.
+    const float lse = block_lse2<kThreads>(lm, ls, red0, red1);
+    if (first) scale = count_finish<kThreads>(sc, cnt);
+    const float zt = E::load(&tb);
+    if (tid == 0) loss_rows[r] = valid ? (lse - zt) : 0.0f;
+    if (G != nullptr)
+      row_ce_grad<T, kThreads, kRes>(Z, V, G, V, V, 0, r, y, valid, lse, zt, rs, buf, nullptr, r, 0,
+                                     scale, sc.nt_grad);
+  };
+  row(z0, r0, y0, v0, rs0, b0, t0, true);
+  if (two) {
+    __syncthreads();  // red0 / red1 are reused
+    row(z1, r0 + 1, y1, v1, rs1, b1, t1, false);
+  }
+}
+
 // Standalone calls of rows of up to 8192 16-byte vectors: 512-lane
-// workgroups (kRes = vectors per lane). At 8 vectors per lane (the [1024,
-// 32768] bf16 shard) a workgroup needs 70 VGPRs per lane and three fit a CU;
-// 256-lane workgroups of 16 vectors (four per CU, every row of the shard
-// resident at once) measured slower (33-34 against 32-33 us per call).
+// workgroups. Rows of up to 4096 vectors (the [1024, 32768] bf16 shard: 8
+// per lane) go two to a workgroup (k_row_ce_pair: 114 VGPRs, two workgroups
+// and so every row of the shard resident per CU; the first row's reductions
+// and stores overlap the second row's loads): 26.5-26.9 against 28.5-29.0 us
+// for the kernel alone with one row per workgroup (70 VGPRs, three
+// workgroups per CU). Earlier, one row per workgroup: 256-lane workgroups of
+// 16 vectors (four per CU) measured slower than 512 lanes (33-34 against
+// 32-33 us per call), and so did 512 lanes held to 64 VGPRs for four
+// workgroups per CU (30.6-31.2 against 27.7-28.3 us for the kernel).
 template <typename T>
 static bool row_ce_512(const void* Z, void* G, int64_t rows, int64_t V, const int32_t* targets,
                        int32_t ign, const WsHeader* hdr, float* loss_rows, SelfCount sc,
@@ -698,16 +808,23 @@ static bool row_ce_512(const void* Z, void* G, int64_t rows, int64_t V, const in
   const int64_t nvec = (V + kVec - 1) / kVec;
   const T* z = static_cast<const T*>(Z);
   T* g = static_cast<T*>(G);
-  const dim3 grid(static_cast<unsigned>(rows)), block(512);
+  const dim3 block(512);
+  if (sc.n > 4 * 512) return false;  // the pair kernel holds 4 targets per lane for the count
+  if (nvec <= 8 * 512) {
+    const dim3 grid(static_cast<unsigned>((rows + 1) / 2));
+    if (nvec <= 4 * 512)
+      hipLaunchKernelGGL((k_row_ce_pair<T, 512, 4>), grid, block, 0, s, z, g, rows, V, targets, ign,
+                         loss_rows, sc);
+    else
+      hipLaunchKernelGGL((k_row_ce_pair<T, 512, 8>), grid, block, 0, s, z, g, rows, V, targets, ign,
+                         loss_rows, sc);
+    return true;
+  }
+  if (nvec > 16 * 512) return false;
   const RowPack pk{nullptr, nullptr, 0};
-#define LCE_ROW_CE512(R)                                                                        \
-  hipLaunchKernelGGL((k_row_ce<T, 512, R>), grid, block, 0, s, z, V, g, V, V, int64_t(0), targets, \
-                     ign, hdr, loss_rows, static_cast<const float*>(nullptr), 0, sc, pk)
-  if (nvec <= 4 * 512) LCE_ROW_CE512(4);
-  else if (nvec <= 8 * 512) LCE_ROW_CE512(8);
-  else if (nvec <= 16 * 512) LCE_ROW_CE512(16);
-  else return false;
-#undef LCE_ROW_CE512
+  hipLaunchKernelGGL((k_row_ce<T, 512, 16>), dim3(static_cast<unsigned>(rows)), block, 0, s, z, V, g,
+                     V, V, int64_t(0), targets, ign, hdr, loss_rows, static_cast<const float*>(nullptr),
+                     0, sc, pk);
   return true;
 }
 
