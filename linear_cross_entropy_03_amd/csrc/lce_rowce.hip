@@ -1387,6 +1387,15 @@ __global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ 
                                                       int reduction, float* __restrict__ out) {
   __shared__ double wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The count, read before the rows through a vector load so that its
+  // latency overlaps theirs: read where it is used it added a dependent load
+  // after the sum, and a scalar load at the top would be waited for before
+  // the rows' loads go out (scalar loads return out of order, so the first
+  // use of the kernel arguments waits for all of them).
+  const int n_valid = reduction == 2
+      ? __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(
+            row_rsrc(hdr, sizeof(WsHeader)), static_cast<int>(offsetof(WsHeader, n_valid)), 0, 0))
+      : 0;
   double acc = 0.0;
   // 16-byte loads, several in flight per lane, then the unaligned rest.
   const int64_t n4 = (reinterpret_cast<uintptr_t>(rows) & 15u) == 0 ? n / 4 : 0;
@@ -1408,7 +1417,7 @@ __global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ 
     double total = 0.0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) total += wsum[k];
-    if (reduction == 2) total = hdr->n_valid > 0 ? total / static_cast<double>(hdr->n_valid) : 0.0;
+    if (reduction == 2) total = n_valid > 0 ? total / static_cast<double>(n_valid) : 0.0;
     out[0] = static_cast<float>(total);
   }
 }
