@@ -271,7 +271,7 @@ def hooked_pass(torch, B, call, reps):
     B.flce_timing_enable(False)
 
 
-def bench_ce(torch, B, reps=40):
+def bench_ce(torch, B, reps=200):
     """Standalone CE over bf16 logits [1024, 32768] (one vocabulary shard,
     std 2, 5% ignored), gradient to a separate buffer, mean reduction. Eight
     buffer sets (1 GiB) are rotated so the 256 MB Infinity Cache cannot hold
