@@ -122,6 +122,44 @@ def test_ce_f16(B, V):
     check_max_rel(g, ref_g, TOL["f16"]["grad"], "grad_logits")
 
 
+@pytest.mark.parametrize("dtype,N,V,mode,reduction", [
+    ("bf16", 1023, 16389, "out", "mean"),      # odd rows (a last workgroup with one row), misaligned rows
+    ("f16", 2047, 16384, "inplace", "none"),   # 4 vectors per lane, every target counted in-kernel
+    ("bf16", 2048, 32768, "inplace", "sum")])  # the self-count limit, 8 vectors per lane
+def test_ce_two_rows_per_workgroup(B, dtype, N, V, mode, reduction):
+    """Standalone calls of up to 2048 rows of 16384-32768 16-bit logits run
+    two rows per workgroup: odd row counts, rows that do not start on 16
+    bytes, bad targets in the last two rows (one of them alone in its
+    workgroup when N is odd) and ignored rows, in place and out of place,
+    against the oracle; the device error report sees the bad targets."""
+    import torch
+    inp = synth.make_ce_inputs(N, V, dtype, std=2.0, ignore_frac=0.1, seed=N + V)
+    y = inp["targets"].copy()
+    y[N - 1] = V
+    y[N - 2] = -7
+    inp = dict(inp, targets=y)
+    ws = torch.zeros(B.ce_workspace_bytes(N, V), dtype=torch.uint8, device="cuda")
+    logits = to_dev(inp["logits"], dtype)
+    say("ce two rows per workgroup", dtype, N, V, mode, reduction)
+    g_arg = logits if mode == "inplace" else True
+    loss, g = B.ce_forward_backward(logits, to_dev(y, "i32"), reduction=reduction, grad_logits=g_arg,
+                                    workspace=ws)
+    assert B.flce_check_device_error(ws) == B.E_TARGET
+    ref_loss, ref_g, info = O.cross_entropy(inp["logits_f32"], y, reduction=reduction)
+    assert info["n_bad"] == 2
+    t = TOL[dtype]
+    if reduction == "none":
+        l = to_host(loss)
+        assert l[N - 1] == 0.0 and l[N - 2] == 0.0
+        check_max_rel(l, ref_loss, t["loss"], "loss rows")
+    else:
+        check_scalar(to_host(loss), ref_loss, t["loss"])
+    gh = to_host(g)
+    assert np.all(gh[N - 1] == 0.0) and np.all(gh[N - 2] == 0.0)
+    assert np.all(gh[y == -100] == 0.0)
+    check_max_rel(gh, ref_g, t["grad"], "grad")
+
+
 def test_ce_all_ignored_and_empty(B):
     import torch
     inp = synth.make_ce_inputs(16, 100, "f32", ignore_frac=1.0)
