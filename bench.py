@@ -577,7 +577,7 @@ def scratch_parts(B, N, H, V, dt, chunk_rows=0):
     return parts
 
 
-def survey_bound_bytes(parts, N, V):
+def one_chunk_bound_bytes(parts, N, V):
     """Peak extra memory allowed for one call: one chunk of logits, O((N + V)
     x 16) bytes of per-row and per-vocabulary scratch, and the split-K partials
     of the grad_X product."""
@@ -785,7 +785,7 @@ def measure_flce(torch, B, cfg, inp, dev, steps, warmup, chunk_rows=0, packing=T
     kernels = kernel_table(B, n_live, H, V, e, hook_steps, hooked_ms)
     step_flops = 6.0 * n_live * H * V
     extra = peak - io_bytes
-    bound = survey_bound_bytes(parts, N, V)
+    bound = one_chunk_bound_bytes(parts, N, V)
     out = {
         "N": N, "H": H, "V": V, "reduction": cfg["reduction"], "bias": bias is not None,
         "chunk_rows": chunk, "dx_splits": splits, "row_packing": packing,
@@ -841,7 +841,7 @@ def main():
         summarise_counters(args.workload, args.counters_from)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
 
     import torch

@@ -126,4 +126,4 @@ def test_workspace_parts_and_the_one_chunk_bound(N, H, V, dtype, chunk):
     if e == 2:
         assert parts["split_partials"] >= up(c * H * 4)      # room for the gathered rows too
     assert parts["rows"] <= 256 + up(4 * N) and parts["pack_lists"] <= 3 * up(4 * N) + 4096
-    assert ws <= bench.survey_bound_bytes(parts, N, V)
+    assert ws <= bench.one_chunk_bound_bytes(parts, N, V)
